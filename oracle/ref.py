@@ -1,0 +1,324 @@
+"""CPU oracle for the KVA projector and its attention-layer KV-cache write.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports, calls or links
+this module; only the tests, the smoke check and the CPU-baseline leg of the
+benchmark do.  It is written to be read against the pages, not to be fast:
+plain NumPy in float64, one library matmul per Linear, no fusion, no blocking.
+
+Sources (titles of the pages the method is described on):
+  [KVA]  "Qwen3.8-27B-KVA: late-layer KV approximation" (model card)
+  [MLA]  "Qwen3.8-27B-MLA" (model card; used only for the base model's
+         attention geometry and rotary frequency law)
+
+What the oracle computes, in the pages' order ([KVA] "What the hell?"):
+  residual of layer 31 -> RMSNorm -> Linear(5120 -> d) -> 3 x causal
+  transformer block -> RMSNorm -> one Linear head per late layer,
+with attention confined to the block (ubatch) of at most 1024 consecutive
+tokens a call is split into, so nothing depends on prompt length.
+
+Readings where the pages leave a step open are listed with each function.
+Every function here is pinned by tests against the pages' printed values,
+library special cases, closed forms, invariants or brute force, except the
+points marked "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# --------------------------------------------------------------------------
+# stored formats -> float64
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit pattern = upper 16 bits of an IEEE binary32 value."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def f16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """IEEE binary16 bit patterns -> float64 (subnormals included)."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+Q8_0_BLOCK = 32
+Q8_0_BYTES = 34      # fp16 scale + 32 int8 codes
+Q4_0_BYTES = 18      # fp16 scale + 32 4-bit codes
+
+
+def dequant_q8_0(packed: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """q8_0 (ggml's 8-bit block format, named on [KVA] "Projector quantization
+    and flash-attn"): each run of 32 consecutive inputs of a weight row is one
+    block holding a fp16 scale d and 32 int8 codes q; the weight is d * q.
+    The product of a fp16 value and an int8 has at most 11 + 8 significant
+    bits, so float64 (and float32) hold it exactly."""
+    nb = cols // Q8_0_BLOCK
+    blk = np.asarray(packed, dtype=np.uint8).reshape(rows, nb, Q8_0_BYTES)
+    d = f16_bits_to_f64(np.ascontiguousarray(blk[:, :, 0:2]).view(np.uint16)[:, :, 0])
+    q = np.ascontiguousarray(blk[:, :, 2:]).view(np.int8).astype(np.float64)
+    return (d[:, :, None] * q).reshape(rows, cols)
+
+
+def weight_f64(w: np.ndarray, dtype: str, out_dim: int, in_dim: int) -> np.ndarray:
+    """A stored Linear weight [out][in] as float64 values."""
+    if dtype == "f32":
+        return np.asarray(w, dtype=np.float32).astype(np.float64).reshape(out_dim, in_dim)
+    if dtype == "bf16":
+        return bf16_bits_to_f64(w).reshape(out_dim, in_dim)
+    if dtype == "q8_0":
+        return dequant_q8_0(w, out_dim, in_dim)
+    raise ValueError(dtype)
+
+
+# --------------------------------------------------------------------------
+# float64 -> bf16 (single rounding, nearest even)
+
+
+def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float64 values once to the nearest bf16 (ties to even) and return
+    the bit patterns.  bf16 keeps 8 significant bits and binary32's exponent
+    range; below 2^-126 the spacing stays 2^-133 (subnormals)."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros(x.shape, dtype=np.float64)
+    fin = np.isfinite(x) & (x != 0)
+    m, e = np.frexp(x[fin])                  # x = m * 2^e, 0.5 <= |m| < 1
+    ulp_exp = np.maximum(e - 8, -133)        # 8 significant bits
+    ulp = np.ldexp(1.0, ulp_exp)
+    r = np.rint(x[fin] / ulp) * ulp          # rint rounds half to even
+    out[fin] = r
+    out[~fin] = x[~fin]
+    with np.errstate(over="ignore"):
+        f = out.astype(np.float32)           # exact: r has <= 8 significant bits
+    big = np.abs(out) >= 2.0 ** 128          # rounded past the largest bf16
+    f[big] = np.copysign(np.inf, out[big])
+    bits = (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    bits[np.isnan(x)] = 0x7FC0
+    return bits
+
+
+# --------------------------------------------------------------------------
+# building blocks
+
+
+def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm over the last axis: x / sqrt(mean(x^2) + eps) times the stored
+    gain.  [KVA] "What the hell?" names RMSNorm without its epsilon; eps sits
+    inside the square root and is 1e-6 (reading)."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(g, dtype=np.float64)
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    return x / (1.0 + np.exp(-x))
+
+
+def causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                     n_heads: int, head_dim: int) -> np.ndarray:
+    """Multi-head causal self-attention over ONE block of tokens.
+
+    q, k, v: [T, n_heads*head_dim]; head j owns columns [j*head_dim, (j+1)*head_dim).
+    Scores are q.k / sqrt(head_dim); key j > query i is excluded before the
+    softmax (its weight is exactly zero).  No position encoding is applied:
+    the card lists none for the projector and the parameter totals leave no
+    room for a learned one (reading).  Returns [T, n_heads*head_dim]."""
+    T = q.shape[0]
+    out = np.empty((T, n_heads * head_dim), dtype=np.float64)
+    allowed = np.tril(np.ones((T, T), dtype=bool))
+    for h in range(n_heads):
+        c = slice(h * head_dim, (h + 1) * head_dim)
+        s = (q[:, c] @ k[:, c].T) / math.sqrt(head_dim)
+        s = np.where(allowed, s, -np.inf)
+        s = s - np.max(s, axis=1, keepdims=True)
+        p = np.exp(s)
+        p = p / np.sum(p, axis=1, keepdims=True)
+        out[:, c] = p @ v[:, c]
+    return out
+
+
+# --------------------------------------------------------------------------
+# the projector
+
+
+def prepare(cfg: dict, weights: dict) -> dict:
+    """float64 copies of the trunk weights (heads are converted on use)."""
+    dt = cfg["weight_dtype"]
+    d, f, n_in = cfg["d_model"], cfg["d_ffn"], cfg["n_in"]
+    hd = cfg["n_heads"] * cfg["head_dim"]
+    p = {"in_norm": weights["in_norm"].astype(np.float64),
+         "in_proj": weight_f64(weights["in_proj"], dt, d, n_in),
+         "out_norm": weights["out_norm"].astype(np.float64), "blocks": []}
+    for b in weights["blocks"]:
+        p["blocks"].append({
+            "attn_norm": b["attn_norm"].astype(np.float64),
+            "wq": weight_f64(b["wq"], dt, hd, d), "wk": weight_f64(b["wk"], dt, hd, d),
+            "wv": weight_f64(b["wv"], dt, hd, d), "wo": weight_f64(b["wo"], dt, d, hd),
+            "ffn_norm": b["ffn_norm"].astype(np.float64),
+            "w_gate": weight_f64(b["w_gate"], dt, f, d), "w_up": weight_f64(b["w_up"], dt, f, d),
+            "w_down": weight_f64(b["w_down"], dt, d, f)})
+    p["_raw"] = weights
+    return p
+
+
+def block_forward(h: np.ndarray, b: dict, cfg: dict) -> np.ndarray:
+    """One causal transformer block, pre-norm ([KVA] "What the hell?" and the
+    r2/r3 table: attention of 128-wide heads, then a SwiGLU FFN; the
+    parameter totals fix full multi-head Q/K/V/O and three FFN matrices).
+    Reading: RMSNorm before each sub-layer, residual adds, no trunk biases,
+    SwiGLU = silu(gate) * up, then down."""
+    eps = cfg["eps"]
+    a = rmsnorm(h, b["attn_norm"], eps)
+    q, k, v = a @ b["wq"].T, a @ b["wk"].T, a @ b["wv"].T
+    o = causal_attention(q, k, v, cfg["n_heads"], cfg["head_dim"])
+    h = h + o @ b["wo"].T
+    a = rmsnorm(h, b["ffn_norm"], eps)
+    act = silu(a @ b["w_gate"].T) * (a @ b["w_up"].T)
+    return h + act @ b["w_down"].T
+
+
+def block_ranges(n_tokens: int, attn_block: int):
+    """Consecutive attention blocks of `attn_block` tokens from token 0 of the
+    call; the last one may be shorter ([KVA] "What the hell?": the blocks
+    attend only within the ubatch they are given; the card's evaluation uses
+    1536-token prompts, i.e. a full ubatch and a 512-token remainder)."""
+    return [(s, min(s + attn_block, n_tokens)) for s in range(0, n_tokens, attn_block)]
+
+
+def trunk(cfg: dict, prep: dict, x: np.ndarray) -> np.ndarray:
+    """Final-normed trunk output z [T, d] for residuals x [T, n_in]."""
+    x = np.asarray(x, dtype=np.float64)
+    z = np.empty((x.shape[0], cfg["d_model"]), dtype=np.float64)
+    for s, e in block_ranges(x.shape[0], cfg["attn_block"]):
+        u = rmsnorm(x[s:e], prep["in_norm"], cfg["eps"])
+        h = u @ prep["in_proj"].T
+        for b in prep["blocks"]:
+            h = block_forward(h, b, cfg)
+        z[s:e] = rmsnorm(h, prep["out_norm"], cfg["eps"])
+    return z
+
+
+def head_weight(cfg: dict, prep: dict, i: int) -> np.ndarray:
+    h = cfg["heads"][i]
+    return weight_f64(prep["_raw"]["heads"][i]["w"], cfg["weight_dtype"], h["out_dim"], cfg["d_model"])
+
+
+def heads(cfg: dict, prep: dict, z: np.ndarray, which=None, cols=None) -> dict:
+    """Y_i = z W_i^T + b_i for each requested head i ([KVA] "What the hell?":
+    one Linear head per late layer; the table there gives each head's output
+    layout: gated DeltaNet qkv | a | b, attention k | v; drafter heads
+    kva.res.N / kva.final from the r2/r3 table).  The per-head bias is a
+    reading: it is the only choice whose parameter totals round to the card's.
+    `cols[i]`, if given, selects output columns of head i."""
+    which = range(len(cfg["heads"])) if which is None else which
+    out = {}
+    for i in which:
+        W = head_weight(cfg, prep, i)
+        b = prep["_raw"]["heads"][i]["b"]
+        if cols is not None and i in cols:
+            c = np.asarray(cols[i])
+            W = W[c]
+            b = None if b is None else b[c]
+        y = z @ W.T
+        if b is not None:
+            y = y + np.asarray(b, dtype=np.float64)
+        out[i] = y
+    return out
+
+
+def project(cfg: dict, weights_or_prep: dict, x: np.ndarray, which=None, cols=None) -> dict:
+    """The whole projector: per-head outputs {head index: [T, out_dim]} float64."""
+    prep = weights_or_prep if "_raw" in weights_or_prep else prepare(cfg, weights_or_prep)
+    z = trunk(cfg, prep, x)
+    return heads(cfg, prep, z, which, cols)
+
+
+# --------------------------------------------------------------------------
+# parameter accounting ([KVA] r2/r3 table; "Projector quantization")
+
+
+def param_count(cfg: dict, head_bias: bool | None = None) -> dict:
+    d, f, n_in = cfg["d_model"], cfg["d_ffn"], cfg["n_in"]
+    hd = cfg["n_heads"] * cfg["head_dim"]
+    bias = cfg["has_head_bias"] if head_bias is None else head_bias
+    nb = cfg["n_blocks"]
+    trunk_w = n_in * d + nb * (3 * hd * d + hd * d + 3 * d * f)
+    trunk_g = n_in + nb * 2 * d + d
+    mix = [h for h in cfg["heads"] if h["kind"] != "draft"]
+    dra = [h for h in cfg["heads"] if h["kind"] == "draft"]
+    mixer = sum(h["out_dim"] * (d + (1 if bias else 0)) for h in mix)
+    drafter = sum(h["out_dim"] * (d + (1 if bias else 0)) for h in dra)
+    return {"trunk": trunk_w + trunk_g, "trunk_linear": trunk_w, "mixer": mixer,
+            "drafter": drafter, "total": trunk_w + trunk_g + mixer + drafter,
+            "linear": trunk_w + sum(h["out_dim"] * d for h in cfg["heads"])}
+
+
+def quantized_file_bytes(cfg: dict, bytes_per_block: int, block: int = 32) -> int:
+    """Size of the projector with every Linear weight in a 32-element block
+    format and norm gains / head biases kept as fp32."""
+    pc = param_count(cfg)
+    lin = pc["linear"]
+    other = pc["total"] - lin
+    assert lin % block == 0
+    return lin // block * bytes_per_block + 4 * other
+
+
+# --------------------------------------------------------------------------
+# attention-layer KV-cache write ([KVA] "What the hell?": after projection the
+# engine applies k_norm and RoPE and writes the KV cache for the attention
+# layers; geometry and rotary law from [MLA] "What this is")
+
+
+def rope_inv_freq(n_rot: int, base: float) -> np.ndarray:
+    """Angular speed of rotary pair j: base^(-2j / n_rot), j < n_rot / 2."""
+    j = np.arange(n_rot // 2, dtype=np.float64)
+    return base ** (-2.0 * j / n_rot)
+
+
+def rope_rotate(x: np.ndarray, pos: np.ndarray, n_rot: int, base: float) -> np.ndarray:
+    """Rotate the first n_rot dims of x [T, ..., D] by position.  Pair j is
+    (x[j], x[j + n_rot/2]) (rotate-half pairing: a reading; parity unpinned,
+    the pages do not fix the pairing) turned by pos * inv_freq[j]; dims from
+    n_rot on pass through."""
+    x = np.array(x, dtype=np.float64, copy=True)
+    half = n_rot // 2
+    th = np.asarray(pos, dtype=np.float64)[:, None] * rope_inv_freq(n_rot, base)[None, :]
+    shape = (x.shape[0],) + (1,) * (x.ndim - 2) + (half,)
+    c, s = np.cos(th).reshape(shape), np.sin(th).reshape(shape)
+    a, b = x[..., :half].copy(), x[..., half:n_rot].copy()
+    x[..., :half] = a * c - b * s
+    x[..., half:n_rot] = a * s + b * c
+    return x
+
+
+def kv_write_values(kv: np.ndarray, gain: np.ndarray, pos0: int, n_kv_heads: int = 4,
+                    head_dim: int = 256, n_rot: int = 64, base: float = 1.0e7,
+                    eps: float = 1e-6):
+    """float64 K and V rows [T, n_kv_heads, head_dim] as they go into the cache.
+
+    kv: [T, 2 * n_kv_heads * head_dim], the attention head's k | v prediction
+    (pre-k_norm, pre-RoPE).  K: RMSNorm per KV head over its head_dim values
+    times the layer's k_norm gain, then RoPE at absolute position pos0 + t.
+    V is stored as predicted (no norm, no rotation)."""
+    kv = np.asarray(kv, dtype=np.float64)
+    T = kv.shape[0]
+    w = n_kv_heads * head_dim
+    k = kv[:, :w].reshape(T, n_kv_heads, head_dim)
+    v = kv[:, w:2 * w].reshape(T, n_kv_heads, head_dim)
+    k = rmsnorm(k, gain, eps)
+    k = rope_rotate(k, pos0 + np.arange(T), n_rot, base)
+    return k, v
+
+
+def kv_write(kv, gain, pos0, page_table, k_pool, v_pool, page_size: int = 256, **kw):
+    """Write bf16 K and V into paged pools [n_pages][page_size][n_kv_heads][head_dim]
+    (bit patterns, updated in place): token at position p goes to page
+    page_table[p // page_size], slot p % page_size."""
+    k, v = kv_write_values(kv, gain, pos0, **kw)
+    kb, vb = f64_to_bf16_bits(k), f64_to_bf16_bits(v)
+    for t in range(kb.shape[0]):
+        p = pos0 + t
+        pg, sl = int(page_table[p // page_size]), p % page_size
+        k_pool[pg, sl] = kb[t]
+        v_pool[pg, sl] = vb[t]
+    return k_pool, v_pool
