@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark of the KVA projector forward pass on one MI355X.
+
+One step = one call of kva_project_ubatch on one 1024-token ubatch of the r2
+projector (d 2560, 3 blocks, 20 heads, SwiGLU 7040, 24 DeltaNet + 8
+attention heads: 264,448 outputs per token), inputs already resident in HBM.
+Prints ONE JSON line.  `value` is projected tokens/s; the r3 projector
+(d 3072, + 4 drafter heads) is timed the same way and reported under "r3".
+
+The roofline entry is for the dominant kernel, the grouped head GEMM
+(about 72% of the algorithmic FLOPs): its device time is taken with HIP
+event pairs that the library records around it on the launch stream during
+the timed steps (kva_profile_enable); its work is 2 * n * N_heads * d FLOP.
+The CPU baseline is the float64 NumPy oracle on one r2 ubatch.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+
+METRIC = "projector tokens/s per 1024-token ubatch (r2,r3 bf16) + % bf16 MFMA peak"
+PEAK_TFLOPS = 2516.6        # MI355X dense bf16/fp16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+HBM_GBS = 8000.0
+STAGE_HEADS = 7
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "heads_gemm_r2_traffic.json")
+
+
+def flops(cfg: dict, n: int) -> dict:
+    """Algorithmic FLOPs of one call on n tokens: 2*M*N*K per GEMM plus the
+    causal half of attention (4 * head_dim * H * B(B+1)/2 per block)."""
+    d, F, n_in = cfg["d_model"], cfg["d_ffn"], cfg["n_in"]
+    H, hd = cfg["n_heads"], cfg["head_dim"]
+    nb = cfg["n_blocks"]
+    B = cfg["attn_block"]
+    blocks = [min(B, n - s) for s in range(0, n, B)]
+    f = {
+        "gemm_in": 2.0 * n * d * n_in,
+        "gemm_qkv": nb * 2.0 * n * 3 * H * hd * d,
+        "attn": nb * sum(4.0 * hd * H * b * (b + 1) / 2 for b in blocks),
+        "gemm_o": nb * 2.0 * n * d * H * hd,
+        "gemm_gateup": nb * 2.0 * n * 2 * F * d,
+        "gemm_down": nb * 2.0 * n * d * F,
+        "gemm_heads": 2.0 * n * sum(h["out_dim"] for h in cfg["heads"]) * d,
+    }
+    f["total"] = sum(f.values())
+    return f
+
+
+def src_hash() -> str:
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "learned_kv_approximation_amd", "csrc", "kva_gemm.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_bytes():
+    """Measured HBM bytes per head-GEMM launch (rocprofv3 FETCH_SIZE + WRITE_SIZE,
+    scaled by a copy-kernel calibration), if taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kva_gemm_src_sha256_16") != src_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def time_config(name: str, steps: int, warmup: int, n_tokens: int = 1024):
+    import torch
+
+    import learned_kv_approximation_amd as kva
+
+    cfg = synth.config(name)
+    t0 = time.time()
+    w = synth.make_weights(cfg)
+    x = synth.make_input(cfg, n_tokens=n_tokens)
+    print(f"[bench] {name}: weights generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    proj = kva.Projector(cfg, w, max_tokens=n_tokens)
+    del w
+    xd = torch.from_numpy(x).cuda()
+    outs = proj.alloc_outputs(n_tokens)
+    for _ in range(warmup):
+        proj.project(xd, outs)
+    torch.cuda.synchronize()
+
+    kva.kva_profile_enable(proj.ctx, 1 << STAGE_HEADS)
+    kva.kva_profile_read(proj.ctx)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    evs[0].record()
+    for k in range(steps):
+        proj.project(xd, outs)
+        evs[k + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per = [evs[k].elapsed_time(evs[k + 1]) for k in range(steps)]
+    total_ms = evs[0].elapsed_time(evs[-1])
+    heads = kva.kva_profile_read(proj.ctx)["gemm_heads"]
+
+    # per-stage breakdown, a separate set of steps with every stage bracketed
+    kva.kva_profile_enable(proj.ctx, (1 << len(kva.STAGES)) - 1)
+    n_prof = max(3, steps // 4)
+    for _ in range(n_prof):
+        proj.project(xd, outs)
+    torch.cuda.synchronize()
+    stages = kva.kva_profile_read(proj.ctx)
+    kva.kva_profile_enable(proj.ctx, 0)
+    proj.close()
+    del outs, xd
+    torch.cuda.empty_cache()
+    f = flops(cfg, n_tokens)
+    ms = total_ms / steps
+    res = {
+        "tokens_per_s": n_tokens / (ms / 1e3),
+        "ms_per_step": ms,
+        "ms_median": float(np.median(per)),
+        "ms_p10": float(np.percentile(per, 10)),
+        "ms_p90": float(np.percentile(per, 90)),
+        "wall_s": wall,
+        "tflop_per_step": f["total"] / 1e12,
+        "pct_mfma_peak": 100.0 * f["total"] / (ms / 1e3) / (PEAK_TFLOPS * 1e12),
+        "heads_gemm_ms": heads[1] / max(heads[0], 1),
+        "heads_gemm_tflop": f["gemm_heads"] / 1e12,
+        "stages_ms_per_step": {k: v[1] / n_prof for k, v in stages.items()},
+        "stage_tflops": {k: (f[k] / 1e12) / (v[1] / n_prof / 1e3) if v[1] > 0 and k in f else None
+                         for k, v in stages.items()},
+    }
+    return res
+
+
+def cpu_baseline(budget_tokens: int = 1024):
+    """The oracle, as it stands, on one r2 ubatch (all heads)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    cfg = synth.config("r2")
+    w = synth.make_weights(cfg)
+    x = synth.make_input(cfg, n_tokens=budget_tokens)
+    t0 = time.perf_counter()
+    oracle.project(cfg, w, x)
+    dt = time.perf_counter() - t0
+    return {"value": budget_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"r2, one {budget_tokens}-token ubatch, all 32 heads, float64 NumPy (BLAS threads={threads}), "
+                      f"{dt:.1f} s incl. weight conversion",
+            "cpu_model": _cpu_model()}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-r3", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(multi-GPU runs are not part of this benchmark).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import learned_kv_approximation_amd as kva
+    kva.lib()   # fails loudly if libkva.so is missing
+
+    r2 = time_config("r2", args.steps, args.warmup)
+    print(f"[bench] r2: {r2['tokens_per_s']:.0f} tok/s, {r2['pct_mfma_peak']:.1f}% peak", file=sys.stderr, flush=True)
+    r3 = None
+    if not args.no_r3:
+        r3 = time_config("r3", args.steps, args.warmup)
+        print(f"[bench] r3: {r3['tokens_per_s']:.0f} tok/s, {r3['pct_mfma_peak']:.1f}% peak", file=sys.stderr,
+              flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline()
+        print(f"[bench] cpu oracle: {cpu['value']:.1f} tok/s", file=sys.stderr, flush=True)
+
+    achieved = r2["heads_gemm_tflop"] / (r2["heads_gemm_ms"] / 1e3)
+    out = {
+        "metric": METRIC,
+        "value": round(r2["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r2["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 heads + fp16 trunk MFMA, fp32 accumulate",
+        "data": "synthetic (seeded N(0,1/fan_in) bf16 weights, N(0,1) residuals at RMS 4)",
+        "config": {"workload": "r2 KVA projector forward, one 1024-token ubatch: 5120 -> d 2560, 3 blocks "
+                               "(20 heads x 128, SwiGLU 7040), 24 DeltaNet heads (10240+48+48) + 8 attention "
+                               "heads (1024+1024)",
+                   "tokens_per_step": 1024, "tflop_per_step": round(r2["tflop_per_step"], 5)},
+        "pct_mfma_peak": round(r2["pct_mfma_peak"], 2),
+        "ms_median": round(r2["ms_median"], 4), "ms_p10": round(r2["ms_p10"], 4), "ms_p90": round(r2["ms_p90"], 4),
+        "roofline": {"bound": "mfma", "kernel": "gemm_nt<256,256,bf16,heads>",
+                     "achieved": round(achieved, 1), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic_bytes(),
+                     "launch_ms": round(r2["heads_gemm_ms"], 4),
+                     "flop_per_launch": r2["heads_gemm_tflop"] * 1e12},
+        "stages_ms_per_step": {k: round(v, 4) for k, v in r2["stages_ms_per_step"].items()},
+        "stage_tflops": {k: (round(v, 1) if v else None) for k, v in r2["stage_tflops"].items()},
+        "cpu_baseline": cpu,
+    }
+    if r3 is not None:
+        out["r3"] = {"tokens_per_s": round(r3["tokens_per_s"], 1), "ms_per_step": round(r3["ms_per_step"], 4),
+                     "pct_mfma_peak": round(r3["pct_mfma_peak"], 2), "tflop_per_step": round(r3["tflop_per_step"], 5),
+                     "heads_gemm_ms": round(r3["heads_gemm_ms"], 4),
+                     "stages_ms_per_step": {k: round(v, 4) for k, v in r3["stages_ms_per_step"].items()}}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

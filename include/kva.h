@@ -1,0 +1,262 @@
+/*
+ * kva.h -- C ABI of the KVA projector library for AMD Instinct MI355X (gfx950).
+ *
+ * The KVA projector ("Qwen3.8-27B-KVA: late-layer KV approximation", model
+ * card, section "What the hell?") maps the layer-31 residual of every prompt
+ * token (5120 wide) to the token-mixer inputs of the 32 late layers of the
+ * base model:
+ *
+ *   RMSNorm -> Linear(5120 -> d) -> 3 x [causal transformer block]
+ *           -> RMSNorm -> one Linear head per late layer
+ *
+ * where each block is pre-norm multi-head causal attention (heads of 128)
+ * followed by a SwiGLU FFN, and attention never crosses the 1024-token ubatch
+ * (here: "attention block") the tokens were given in.  Per the card's table
+ * of predicted inputs, a gated-DeltaNet layer receives in_proj_qkv | in_proj_a
+ * | in_proj_b (10240 + 48 + 48 values per token) and a full-attention layer
+ * receives k_proj | v_proj before k_norm and RoPE (1024 + 1024).  The r3
+ * variant adds drafter heads (kva.res.34, kva.res.48, kva.res.62, kva.final,
+ * r2/r3 table) that read the same final-normed trunk state.
+ *
+ * Conventions for every entry point:
+ *  - Sizes are element counts; matrices are row-major; a Linear weight is
+ *    stored [out][in] (row o holds the weights of output o).
+ *  - "device" pointers are HIP device memory on the context's device,
+ *    "host" pointers are ordinary CPU memory.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Compute
+ *    entry points validate their arguments on the host, enqueue work on
+ *    `stream` and return without synchronising.  Buffers passed to them must
+ *    stay valid until the stream has passed the call.
+ *  - Every call returns a kva_status; nothing aborts or throws across the
+ *    ABI.  kva_last_error() gives a human-readable detail for the calling
+ *    thread's most recent failure.  Device faults surface asynchronously at
+ *    the caller's next synchronisation of the stream.
+ *  - A context is used by one stream at a time (calls on one context must be
+ *    serialised by the caller).
+ */
+#ifndef KVA_H
+#define KVA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KVA_OK = 0,
+    KVA_ERR_ARG = 1,          /* NULL pointer or invalid enum value          */
+    KVA_ERR_SHAPE = 2,        /* unsupported or inconsistent dimensions      */
+    KVA_ERR_DTYPE = 3,        /* unsupported storage type                    */
+    KVA_ERR_OOM = 4,          /* device or host allocation failed            */
+    KVA_ERR_RANGE = 5,        /* a weight does not fit the compute type      */
+    KVA_ERR_UNSUPPORTED = 6,  /* valid request this build does not implement */
+    KVA_ERR_HIP = 7           /* a HIP runtime call or kernel launch failed  */
+} kva_status;
+
+typedef enum {
+    KVA_DTYPE_F32 = 0,   /* IEEE binary32                                        */
+    KVA_DTYPE_BF16 = 1,  /* bfloat16 bit patterns (uint16)                       */
+    KVA_DTYPE_Q8_0 = 2   /* blocks of 32 inputs: fp16 scale d, then 32 int8 q;   */
+                         /* weight = d * q; 34 bytes per block, blocks run along */
+                         /* the `in` axis of each row                            */
+} kva_dtype;
+
+typedef enum {
+    KVA_HEAD_DELTANET = 0,  /* gated-DeltaNet layer: qkv | a | b               */
+    KVA_HEAD_ATTN = 1,      /* full-attention layer: k | v (pre k_norm/RoPE)  */
+    KVA_HEAD_DRAFT = 2      /* drafter residual kva.res.N or kva.final        */
+} kva_head_kind;
+
+/* One output head (one late layer, or one drafter). */
+typedef struct {
+    int32_t kind;     /* kva_head_kind (informational; all heads are Linear+bias) */
+    int32_t layer;    /* base-model layer the head feeds (informational)          */
+    int32_t out_dim;  /* outputs per token, e.g. 10336, 2048 or 5120              */
+} kva_head_desc;
+
+/* Projector shape.  Field meanings follow the card's r2/r3 table:
+ * r2 = {5120, 2560, 3, 20, 128, 7040}, r3 = {5120, 3072, 3, 24, 128, 8448}. */
+typedef struct {
+    int32_t n_in;          /* residual width, 5120 for the base model            */
+    int32_t d_model;       /* trunk width d                                      */
+    int32_t n_blocks;      /* transformer blocks (3)                             */
+    int32_t n_heads;       /* attention heads per block; n_heads*head_dim==d     */
+    int32_t head_dim;      /* must be 128                                        */
+    int32_t d_ffn;         /* SwiGLU hidden width                                */
+    int32_t attn_block;    /* tokens per causal attention block (1024)           */
+    int32_t max_tokens;    /* largest n_tokens a call may pass                   */
+    float eps;             /* RMSNorm epsilon (inside the square root), 1e-6     */
+    int32_t weight_dtype;  /* kva_dtype of every Linear weight                   */
+    int32_t has_head_bias; /* 1: each head has an fp32 bias of out_dim values    */
+    int32_t n_out_heads;   /* number of entries in out_heads (1..64)             */
+    const kva_head_desc* out_heads; /* host array, copied by kva_create          */
+} kva_config;
+
+/* Weights of one transformer block (host pointers, weight_dtype storage). */
+typedef struct {
+    const float* attn_norm;  /* [d] fp32 gain                                   */
+    const void* wq;          /* [d][d]   (n_heads*head_dim rows)                */
+    const void* wk;          /* [d][d]                                           */
+    const void* wv;          /* [d][d]                                           */
+    const void* wo;          /* [d][d]                                           */
+    const float* ffn_norm;   /* [d] fp32 gain                                   */
+    const void* w_gate;      /* [d_ffn][d]                                       */
+    const void* w_up;        /* [d_ffn][d]                                       */
+    const void* w_down;      /* [d][d_ffn]                                       */
+} kva_block_weights;
+
+/* All projector weights, as HOST pointers.  kva_create copies (and repacks)
+ * them into memory the context owns; the caller may free them afterwards. */
+typedef struct {
+    const float* in_norm;              /* [n_in] fp32 gain                      */
+    const void* in_proj;               /* [d][n_in]                             */
+    const kva_block_weights* blocks;   /* n_blocks entries                      */
+    const float* out_norm;             /* [d] fp32 gain                         */
+    const void* const* head_w;         /* n_out_heads pointers, [out_dim][d]    */
+    const float* const* head_b;        /* n_out_heads pointers to [out_dim]     */
+                                       /* fp32, or NULL when !has_head_bias     */
+} kva_weights;
+
+typedef struct kva_ctx kva_ctx;
+
+typedef struct {
+    uint64_t calls;         /* successful kva_project_ubatch calls              */
+    uint64_t tokens;        /* tokens projected by them                         */
+    uint64_t blocks;        /* attention blocks processed                       */
+    uint64_t weight_bytes;  /* device bytes held for weights                    */
+    uint64_t scratch_bytes; /* device bytes held for activations                */
+} kva_stats;
+
+/* Checks a config on the host only (no device is touched): dimensions
+ * positive and consistent, head_dim == 128, n_heads*head_dim == d_model,
+ * n_in, d_model and d_ffn multiples of 64, attn_block a positive multiple of
+ * 64, 1 <= n_out_heads <= 64, every out_dim positive, weight_dtype known.
+ * Returns KVA_OK, KVA_ERR_ARG, KVA_ERR_SHAPE or KVA_ERR_DTYPE. */
+kva_status kva_validate_config(const kva_config* cfg);
+
+/* Creates a projector on HIP device `device`: validates `cfg`, allocates the
+ * weight arena and scratch for cfg->max_tokens tokens, converts and uploads
+ * the weights.  Trunk weights are converted to fp16 for the MFMA path
+ * (KVA_ERR_RANGE if a weight is outside fp16's finite range); head weights
+ * are kept as bf16 (fp32 weights are rounded to nearest even).  The call is
+ * synchronous.  On success *out owns all device memory it allocated; on
+ * failure *out is NULL and nothing is leaked. */
+kva_status kva_create(const kva_config* cfg, const kva_weights* w, int device, kva_ctx** out);
+
+/* The hot path: projects n_tokens residual rows.
+ *   x        device, [n_tokens][n_in] fp32 (layer-31 residuals)
+ *   head_out host array of n_out_heads DEVICE pointers; head i receives
+ *            [n_tokens][out_dim_i] fp32, row-major, columns in the head's
+ *            segment order (qkv|a|b, k|v, or the drafter's 5120).
+ * Tokens [0, n_tokens) are split into consecutive attention blocks of
+ * attn_block tokens starting at token 0; the last block may be shorter.
+ * Attention is causal within a block and never crosses blocks, so a block's
+ * outputs are bitwise identical whether it is passed alone or inside a longer
+ * call.  1 <= n_tokens <= max_tokens (else KVA_ERR_SHAPE).  Output buffers
+ * must not alias x or each other.  Asynchronous on `stream`. */
+kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n_tokens,
+                              float* const* head_out, void* stream);
+
+/* Synchronises the context's device, frees everything it owns.  NULL-safe. */
+kva_status kva_destroy(kva_ctx* ctx);
+
+/* Paged KV cache of one full-attention layer of the base model
+ * ("Qwen3.8-27B-MLA" card, "What this is": 4 KV heads of 256 dims, 64 of
+ * which are rotary).  Pools are device arrays of bf16 bit patterns laid out
+ * [n_pages][page_size][n_kv_heads][head_dim]; page_table is a device int32
+ * array mapping logical page (position / page_size) to a physical page. */
+typedef struct {
+    uint16_t* k_pool;
+    uint16_t* v_pool;
+    const int32_t* page_table;
+    int32_t page_size;     /* 256                                        */
+    int32_t n_pages;       /* physical pages in each pool                */
+    int32_t n_logical;     /* entries in page_table                      */
+    int32_t n_kv_heads;    /* 4                                          */
+    int32_t head_dim;      /* 256                                        */
+    int32_t n_rot;         /* rotary dims at the start of each KV head   */
+    double rope_base;      /* 1e7                                        */
+    float eps;             /* k_norm epsilon, 1e-6                       */
+} kva_paged_kv;
+
+/* The attention-layer state update that follows the projection ("What the
+ * hell?": k_norm + RoPE + KV-cache writes for the attention layers).  For
+ * token t at absolute position p = pos0 + t:
+ *   k = kv[t][0 : n_kv_heads*head_dim] viewed [n_kv_heads][head_dim];
+ *   each KV head: RMSNorm (eps inside the root) times k_gain[head_dim];
+ *   RoPE on dims [0, n_rot): pair (j, j + n_rot/2) turned by
+ *     p * rope_base^(-2j/n_rot) (the angle is reduced in double precision);
+ *   v = kv[t][n_kv_heads*head_dim : 2*n_kv_heads*head_dim] unchanged;
+ *   both rounded to bf16 (nearest even) and stored at
+ *     pool[page_table[p / page_size]][p % page_size].
+ *   kv      device fp32, row t at kv + t*ld_kv (ld_kv >= 2*n_kv_heads*head_dim)
+ *   k_gain  device fp32 [head_dim]
+ * Positions past n_logical*page_size, page entries outside [0, n_pages) are
+ * the caller's responsibility for page entries (KVA_ERR_SHAPE is returned
+ * when pos0 + n_tokens exceeds n_logical * page_size).  Asynchronous. */
+kva_status kva_attn_kv_write(const float* kv, int64_t ld_kv, int32_t n_tokens, int64_t pos0,
+                             const float* k_gain, const kva_paged_kv* cache, void* stream);
+
+/* Test hook: dequantises n_blocks q8_0 blocks (device, 34 bytes each) to
+ * fp32 (device, 32*n_blocks values) with the same device routine the q8_0
+ * GEMM uses: out = float(d) * q, exact, fp16 subnormal scales honoured. */
+kva_status kva_debug_dequant_q8_0(const void* blocks, int64_t n_blocks, float* out, void* stream);
+
+/* Test hook: copies the final-normed trunk state z of the most recent
+ * kva_project_ubatch call ([n_tokens][d_model] bf16 bit patterns, the head
+ * GEMM's A operand) to device buffer `dst`.  Asynchronous on `stream`. */
+kva_status kva_debug_copy_z(kva_ctx* ctx, uint16_t* dst, int32_t n_tokens, void* stream);
+
+/* Test hook (host only, no device): the packed column order of the head
+ * GEMM for `cfg`.  Head outputs are packed into 256-column tiles: first the
+ * out_dim / 256 full tiles of every head in head order, then one tail
+ * segment gathering every head's last out_dim % 256 columns (padded to a
+ * multiple of 256).  For packed column c, col_head[c] is the head (-1 for
+ * padding) and col_index[c] the column inside that head.  *n_cols receives the
+ * packed width; nothing is written past `capacity` entries (KVA_ERR_SHAPE if
+ * capacity is too small). */
+kva_status kva_debug_head_plan(const kva_config* cfg, int32_t* n_cols, int32_t* col_head,
+                               int32_t* col_index, int64_t capacity);
+
+/* Test hook (host only): the conversion kva_create applies to trunk weights,
+ * src_dtype (KVA_DTYPE_F32 or KVA_DTYPE_BF16) -> fp16 bit patterns, rounding
+ * to nearest even.  KVA_ERR_RANGE if a finite value rounds past fp16's
+ * largest finite value (dst is still fully written, with infinities). */
+kva_status kva_debug_host_to_f16(const void* src, int32_t src_dtype, int64_t n, uint16_t* dst);
+
+/* Stages of one projection, for kva_profile_*. */
+typedef enum {
+    KVA_STAGE_NORM = 0,        /* RMSNorm + cast kernels (input, 2 per block, final) */
+    KVA_STAGE_GEMM_IN = 1,     /* Linear n_in -> d                                    */
+    KVA_STAGE_GEMM_QKV = 2,    /* Q|K|V projection                                    */
+    KVA_STAGE_ATTN = 3,        /* block-causal attention                               */
+    KVA_STAGE_GEMM_O = 4,      /* output projection + residual                         */
+    KVA_STAGE_GEMM_GATEUP = 5, /* gate/up + SwiGLU                                     */
+    KVA_STAGE_GEMM_DOWN = 6,   /* down projection + residual                           */
+    KVA_STAGE_GEMM_HEADS = 7,  /* all heads + bias + per-head scatter                  */
+    KVA_N_STAGES = 8
+} kva_stage;
+
+typedef struct {
+    int32_t launches;   /* kernel launches timed since the last read            */
+    double total_ms;    /* their summed device time (HIP event pairs)           */
+} kva_stage_time;
+
+/* Benchmark support: while bit s of stage_mask is set, kva_project_ubatch
+ * records a HIP event pair on its stream around every launch of stage s.
+ * 0 disables recording.  Recording adds no synchronisation. */
+kva_status kva_profile_enable(kva_ctx* ctx, uint32_t stage_mask);
+
+/* Waits for the recorded events, writes per-stage totals to out[KVA_N_STAGES]
+ * and clears them. */
+kva_status kva_profile_read(kva_ctx* ctx, kva_stage_time* out);
+
+kva_status kva_get_stats(const kva_ctx* ctx, kva_stats* out);
+const char* kva_status_str(kva_status s);
+const char* kva_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVA_H */

@@ -1,0 +1,287 @@
+"""Python binding of libkva.so, the MI355X (gfx950) KVA projector library.
+
+Thin ctypes marshalling over the C ABI declared in include/kva.h: the
+functions below carry the C names and take plain integers for device
+pointers and the HIP stream.  Every step of the projection runs in the HIP
+kernels of libkva.so; there is no Python or CPU fallback.  If the library has
+not been built, loading it raises KvaError.
+
+`Projector` is a convenience wrapper that fills the C structs from a config
+dict and NumPy weights (see the `synth` package for their layout) and takes
+torch tensors for device memory and the current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkva.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "kva.h")
+
+c_i32, c_i64, c_f32, c_f64, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
+
+KVA_OK, KVA_ERR_ARG, KVA_ERR_SHAPE, KVA_ERR_DTYPE = 0, 1, 2, 3
+KVA_ERR_OOM, KVA_ERR_RANGE, KVA_ERR_UNSUPPORTED, KVA_ERR_HIP = 4, 5, 6, 7
+DTYPES = {"f32": 0, "bf16": 1, "q8_0": 2}
+KINDS = {"deltanet": 0, "attn": 1, "draft": 2}
+
+
+class kva_head_desc(ctypes.Structure):
+    _fields_ = [("kind", c_i32), ("layer", c_i32), ("out_dim", c_i32)]
+
+
+class kva_config(ctypes.Structure):
+    _fields_ = [("n_in", c_i32), ("d_model", c_i32), ("n_blocks", c_i32), ("n_heads", c_i32),
+                ("head_dim", c_i32), ("d_ffn", c_i32), ("attn_block", c_i32), ("max_tokens", c_i32),
+                ("eps", c_f32), ("weight_dtype", c_i32), ("has_head_bias", c_i32),
+                ("n_out_heads", c_i32), ("out_heads", ctypes.POINTER(kva_head_desc))]
+
+
+class kva_block_weights(ctypes.Structure):
+    _fields_ = [("attn_norm", c_vp), ("wq", c_vp), ("wk", c_vp), ("wv", c_vp), ("wo", c_vp),
+                ("ffn_norm", c_vp), ("w_gate", c_vp), ("w_up", c_vp), ("w_down", c_vp)]
+
+
+class kva_weights(ctypes.Structure):
+    _fields_ = [("in_norm", c_vp), ("in_proj", c_vp), ("blocks", ctypes.POINTER(kva_block_weights)),
+                ("out_norm", c_vp), ("head_w", ctypes.POINTER(c_vp)), ("head_b", ctypes.POINTER(c_vp))]
+
+
+class kva_stats(ctypes.Structure):
+    _fields_ = [("calls", ctypes.c_uint64), ("tokens", ctypes.c_uint64), ("blocks", ctypes.c_uint64),
+                ("weight_bytes", ctypes.c_uint64), ("scratch_bytes", ctypes.c_uint64)]
+
+
+class kva_stage_time(ctypes.Structure):
+    _fields_ = [("launches", c_i32), ("total_ms", c_f64)]
+
+
+STAGES = ["norm", "gemm_in", "gemm_qkv", "attn", "gemm_o", "gemm_gateup", "gemm_down", "gemm_heads"]
+
+
+class kva_paged_kv(ctypes.Structure):
+    _fields_ = [("k_pool", c_vp), ("v_pool", c_vp), ("page_table", c_vp), ("page_size", c_i32),
+                ("n_pages", c_i32), ("n_logical", c_i32), ("n_kv_heads", c_i32), ("head_dim", c_i32),
+                ("n_rot", c_i32), ("rope_base", c_f64), ("eps", c_f32)]
+
+
+class KvaError(RuntimeError):
+    def __init__(self, status: int, where: str = ""):
+        self.status = status
+        name = _lib.kva_status_str(status).decode() if _lib is not None else str(status)
+        detail = _lib.kva_last_error().decode() if _lib is not None else ""
+        super().__init__(f"{where}: {name}: {detail}" if where else f"{name}: {detail}")
+
+
+_lib = None
+
+_SIGS = {
+    "kva_validate_config": (c_i32, [ctypes.POINTER(kva_config)]),
+    "kva_create": (c_i32, [ctypes.POINTER(kva_config), ctypes.POINTER(kva_weights), c_i32, ctypes.POINTER(c_vp)]),
+    "kva_project_ubatch": (c_i32, [c_vp, c_vp, c_i32, ctypes.POINTER(c_vp), c_vp]),
+    "kva_destroy": (c_i32, [c_vp]),
+    "kva_attn_kv_write": (c_i32, [c_vp, c_i64, c_i32, c_i64, c_vp, ctypes.POINTER(kva_paged_kv), c_vp]),
+    "kva_debug_dequant_q8_0": (c_i32, [c_vp, c_i64, c_vp, c_vp]),
+    "kva_debug_copy_z": (c_i32, [c_vp, c_vp, c_i32, c_vp]),
+    "kva_debug_head_plan": (c_i32, [ctypes.POINTER(kva_config), ctypes.POINTER(c_i32), c_vp, c_vp, c_i64]),
+    "kva_debug_host_to_f16": (c_i32, [c_vp, c_i32, c_i64, c_vp]),
+    "kva_get_stats": (c_i32, [c_vp, ctypes.POINTER(kva_stats)]),
+    "kva_profile_enable": (c_i32, [c_vp, ctypes.c_uint32]),
+    "kva_profile_read": (c_i32, [c_vp, ctypes.POINTER(kva_stage_time)]),
+    "kva_status_str": (ctypes.c_char_p, [c_i32]),
+    "kva_last_error": (ctypes.c_char_p, []),
+}
+
+
+def lib():
+    """Load libkva.so once (raises KvaError-like RuntimeError if it is missing)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def header_exports() -> list:
+    """Names of the functions include/kva.h declares."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kva_\w+)\s*\(", text, re.M)))
+
+
+def _check(status: int, where: str):
+    if status != KVA_OK:
+        raise KvaError(status, where)
+
+
+# ------------------------------------------------------------------ C-named entry points
+
+def kva_validate_config(cfg: kva_config) -> int:
+    return lib().kva_validate_config(ctypes.byref(cfg))
+
+
+def kva_create(cfg: kva_config, weights: kva_weights, device: int = 0) -> int:
+    out = c_vp()
+    _check(lib().kva_create(ctypes.byref(cfg), ctypes.byref(weights), device, ctypes.byref(out)), "kva_create")
+    return out.value
+
+
+def kva_project_ubatch(ctx: int, x_ptr: int, n_tokens: int, head_out_ptrs, stream: int = 0) -> None:
+    arr = (c_vp * len(head_out_ptrs))(*head_out_ptrs)
+    _check(lib().kva_project_ubatch(ctx, x_ptr, n_tokens, arr, stream), "kva_project_ubatch")
+
+
+def kva_destroy(ctx: int) -> None:
+    _check(lib().kva_destroy(ctx), "kva_destroy")
+
+
+def kva_attn_kv_write(kv_ptr: int, ld_kv: int, n_tokens: int, pos0: int, k_gain_ptr: int,
+                      cache: kva_paged_kv, stream: int = 0) -> None:
+    _check(lib().kva_attn_kv_write(kv_ptr, ld_kv, n_tokens, pos0, k_gain_ptr, ctypes.byref(cache), stream),
+           "kva_attn_kv_write")
+
+
+def kva_debug_dequant_q8_0(blocks_ptr: int, n_blocks: int, out_ptr: int, stream: int = 0) -> None:
+    _check(lib().kva_debug_dequant_q8_0(blocks_ptr, n_blocks, out_ptr, stream), "kva_debug_dequant_q8_0")
+
+
+def kva_debug_copy_z(ctx: int, dst_ptr: int, n_tokens: int, stream: int = 0) -> None:
+    _check(lib().kva_debug_copy_z(ctx, dst_ptr, n_tokens, stream), "kva_debug_copy_z")
+
+
+def kva_debug_head_plan(cfg: kva_config):
+    import numpy as np
+    n = c_i32()
+    _check(lib().kva_debug_head_plan(ctypes.byref(cfg), ctypes.byref(n), None, None, 0), "kva_debug_head_plan")
+    head = np.empty(n.value, dtype=np.int32)
+    idx = np.empty(n.value, dtype=np.int32)
+    _check(lib().kva_debug_head_plan(ctypes.byref(cfg), ctypes.byref(n), head.ctypes.data, idx.ctypes.data,
+                                     n.value), "kva_debug_head_plan")
+    return head, idx
+
+
+def kva_debug_host_to_f16(src, src_dtype: str):
+    """Host conversion used for trunk weights; returns (status, fp16 bits)."""
+    import numpy as np
+    src = np.ascontiguousarray(src)
+    dst = np.empty(src.size, dtype=np.uint16)
+    st = lib().kva_debug_host_to_f16(src.ctypes.data, DTYPES[src_dtype], src.size, dst.ctypes.data)
+    return st, dst.reshape(src.shape)
+
+
+def kva_get_stats(ctx: int) -> dict:
+    s = kva_stats()
+    _check(lib().kva_get_stats(ctx, ctypes.byref(s)), "kva_get_stats")
+    return {k: getattr(s, k) for k, _ in kva_stats._fields_}
+
+
+def kva_profile_enable(ctx: int, stage_mask: int) -> None:
+    _check(lib().kva_profile_enable(ctx, stage_mask), "kva_profile_enable")
+
+
+def kva_profile_read(ctx: int) -> dict:
+    """{stage name: (launches, total_ms)} since the last read (waits for the events)."""
+    arr = (kva_stage_time * len(STAGES))()
+    _check(lib().kva_profile_read(ctx, arr), "kva_profile_read")
+    return {STAGES[i]: (arr[i].launches, arr[i].total_ms) for i in range(len(STAGES))}
+
+
+# ------------------------------------------------------------------ struct builders
+
+def make_config(cfg: dict, max_tokens: int | None = None):
+    """kva_config for a config dict (synth.config layout).  Returns (struct, keepalive)."""
+    heads = (kva_head_desc * len(cfg["heads"]))(
+        *[kva_head_desc(KINDS[h["kind"]], h["layer"], h["out_dim"]) for h in cfg["heads"]])
+    c = kva_config(cfg["n_in"], cfg["d_model"], cfg["n_blocks"], cfg["n_heads"], cfg["head_dim"],
+                   cfg["d_ffn"], cfg["attn_block"], int(max_tokens or cfg["n_tokens"]), cfg["eps"],
+                   DTYPES[cfg["weight_dtype"]], 1 if cfg["has_head_bias"] else 0, len(cfg["heads"]),
+                   ctypes.cast(heads, ctypes.POINTER(kva_head_desc)))
+    return c, heads
+
+
+def make_weights(cfg: dict, w: dict):
+    """kva_weights pointing at host NumPy arrays.  Returns (struct, keepalive)."""
+    import numpy as np
+    keep = []
+
+    def p(a):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a)
+        keep.append(a)
+        return a.ctypes.data
+
+    blocks = (kva_block_weights * len(w["blocks"]))(*[
+        kva_block_weights(p(b["attn_norm"]), p(b["wq"]), p(b["wk"]), p(b["wv"]), p(b["wo"]),
+                          p(b["ffn_norm"]), p(b["w_gate"]), p(b["w_up"]), p(b["w_down"]))
+        for b in w["blocks"]])
+    hw = (c_vp * len(w["heads"]))(*[p(h["w"]) for h in w["heads"]])
+    hb = (c_vp * len(w["heads"]))(*[p(h["b"]) for h in w["heads"]]) if cfg["has_head_bias"] else None
+    keep += [blocks, hw, hb]
+    s = kva_weights(p(w["in_norm"]), p(w["in_proj"]), ctypes.cast(blocks, ctypes.POINTER(kva_block_weights)),
+                    p(w["out_norm"]), ctypes.cast(hw, ctypes.POINTER(c_vp)),
+                    ctypes.cast(hb, ctypes.POINTER(c_vp)) if hb is not None else None)
+    return s, keep
+
+
+def current_stream() -> int:
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+class Projector:
+    """Owns a kva_ctx built from a config dict and NumPy weights."""
+
+    def __init__(self, cfg: dict, weights: dict, max_tokens: int | None = None, device: int = 0):
+        self.cfg = cfg
+        self.max_tokens = int(max_tokens or cfg["n_tokens"])
+        c, self._keep_c = make_config(cfg, self.max_tokens)
+        w, keep_w = make_weights(cfg, weights)
+        self._c = c
+        self.ctx = kva_create(c, w, device)
+        del keep_w
+
+    def alloc_outputs(self, n_tokens: int, device="cuda"):
+        import torch
+        return [torch.empty((n_tokens, h["out_dim"]), dtype=torch.float32, device=device)
+                for h in self.cfg["heads"]]
+
+    def project(self, x, outs=None, stream: int | None = None):
+        """x: [n, n_in] fp32 cuda tensor.  Returns the per-head fp32 outputs."""
+        assert x.is_cuda and x.dtype.is_floating_point and x.dtype.itemsize == 4 and x.is_contiguous()
+        n = x.shape[0]
+        assert x.shape[1] == self.cfg["n_in"]
+        if outs is None:
+            outs = self.alloc_outputs(n, x.device)
+        for o, h in zip(outs, self.cfg["heads"]):
+            assert o.is_contiguous() and o.shape[0] >= n and o.shape[1] == h["out_dim"]
+        kva_project_ubatch(self.ctx, x.data_ptr(), n, [o.data_ptr() for o in outs],
+                           current_stream() if stream is None else stream)
+        return outs
+
+    def copy_z(self, n_tokens: int):
+        import torch
+        z = torch.empty((n_tokens, self.cfg["d_model"]), dtype=torch.int16, device="cuda")
+        kva_debug_copy_z(self.ctx, z.data_ptr(), n_tokens, current_stream())
+        return z
+
+    def stats(self) -> dict:
+        return kva_get_stats(self.ctx)
+
+    def close(self):
+        if getattr(self, "ctx", None):
+            kva_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

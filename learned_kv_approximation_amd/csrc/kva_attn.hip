@@ -1,0 +1,239 @@
+// Block-causal multi-head attention for the projector's transformer blocks.
+//
+// The projector's blocks attend only within the ubatch (attention block) the
+// tokens arrive in, causally ("Qwen3.8-27B-KVA" model card, "What the hell?"
+// and the r2/r3 table: heads of 128, causal within 1024-token blocks).  For
+// query i of head h in block [s, e):  o_i = sum_{s<=j<=i} softmax_j(q_i.k_j/sqrt(128)) v_j.
+//
+// One workgroup = 2 waves = 64 queries of one head; each wave owns 32
+// queries.  K and V of 64 keys at a time are staged in LDS (double-buffered,
+// the next tile is fetched into registers while the current one is used).
+// Per key tile a wave computes S^T = K Q^T with 32x32x16 MFMAs, so each lane
+// holds the scores of ONE query (column lane%32) for 32 keys: the online
+// softmax (running max m, running sum l, fp32) is per lane plus one exchange
+// with lane^32.  O^T += V^T P^T then takes P straight from registers: V is
+// produced transposed (vt[c][t]) by the QKV GEMM, and the key rows of the K
+// tile are stored in LDS in the order that makes each lane's 8 P values 8
+// consecutive keys, so one 16-byte LDS read fetches the matching V^T chunk.
+// Keys after the query, and keys at or past n_tokens, get probability 0
+// (their scores are replaced by -inf before the max; V past n_tokens is
+// zeroed so 0 * V stays 0).
+#include "kva_internal.h"
+
+namespace kva {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int HD = 128;     // head dim
+constexpr int QT = 64;      // queries per workgroup
+constexpr int KT = 64;      // keys per tile
+constexpr int kThreads = 128;
+
+__device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// LDS row rho of the K tile holds key perm(rho) of the tile: bits 2 and 3 of
+// the index are swapped (an involution).
+__device__ __forceinline__ int perm(int rho) {
+    return (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);
+}
+
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+}
+
+__global__ void __launch_bounds__(kThreads) attn_fwd(const uint16_t* __restrict__ qk, int64_t ld_qk,
+                                                      int32_t k_off, const uint16_t* __restrict__ vt,
+                                                      int64_t ld_vt, uint16_t* __restrict__ o,
+                                                      int64_t ld_o, int32_t n, int32_t attn_block) {
+    __shared__ __attribute__((aligned(16))) uint16_t sK[2][KT * HD];   // [rho][128], chunk-swizzled
+    __shared__ __attribute__((aligned(16))) uint16_t sV[2][HD * KT];   // [d][64],   chunk-swizzled
+
+    const int h = blockIdx.y;
+    const int qt = gridDim.x - 1 - blockIdx.x;        // longest key ranges first
+    const int q0 = qt * QT;
+    const int bs = (q0 / attn_block) * attn_block;    // start of this block
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 5;
+    const int myq = q0 + wave * 32 + (lane & 31);
+    const int kv_end = min(q0 + QT, n);
+    const int ntiles = (kv_end - bs + KT - 1) / KT;
+
+    // Q fragments (B operand of S^T = K Q^T): 8 consecutive dims per lane per 16-dim step
+    u32x4 qf[HD / 16];
+    {
+        const uint16_t* qr = qk + (int64_t)min(myq, n - 1) * ld_qk + h * HD + g * 8;
+#pragma unroll
+        for (int ks = 0; ks < HD / 16; ++ks) qf[ks] = *(const u32x4*)(qr + ks * 16);
+    }
+
+    // tile loader: 1024 K chunks and 1024 V^T chunks of 16 bytes, 8 of each per thread
+    u32x4 rk[8], rv[8];
+    auto gload = [&](int kv0) {
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int id = tid + p * kThreads;
+            const int rho = id >> 4, c = id & 15;
+            const int kv = min(kv0 + perm(rho), n - 1);
+            rk[p] = *(const u32x4*)(qk + (int64_t)kv * ld_qk + k_off + h * HD + c * 8);
+        }
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int id = tid + p * kThreads;
+            const int d = id >> 3, c = id & 7;
+            const int t0 = kv0 + c * 8;
+            u32x4 v = *(const u32x4*)(vt + (int64_t)(h * HD + d) * ld_vt + t0);
+            if (t0 + 8 > n) {           // zero V of keys past the end (0 * V must stay 0)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (t0 + 2 * e >= n) v[e] &= 0xFFFF0000u;
+                    if (t0 + 2 * e + 1 >= n) v[e] &= 0x0000FFFFu;
+                }
+            }
+            rv[p] = v;
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int id = tid + p * kThreads;
+            const int rho = id >> 4, c = id & 15;
+            *(u32x4*)(&sK[buf][rho * HD + ((c ^ (rho & 15)) << 3)]) = rk[p];
+        }
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int id = tid + p * kThreads;
+            const int d = id >> 3, c = id & 7;
+            const int sw = (d & 7) ^ ((d >> 3) & 1);
+            *(u32x4*)(&sV[buf][d * KT + ((c ^ sw) << 3)]) = rv[p];
+        }
+    };
+
+    const float scale = 0.12751743082459868f;   // log2(e) / sqrt(128)
+    float m_i = -INFINITY, l_i = 0.0f;
+    f32x16 oacc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
+
+    gload(bs);
+    sstore(0);
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+        const int buf = t & 1;
+        const int kv0 = bs + t * KT;
+        if (t + 1 < ntiles) gload(kv0 + KT);
+
+        // S^T[rho][q] for rho in [0,64): two 32-key MFMA tiles
+        f32x16 s[2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[st][r] = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < HD / 16; ++ks) {
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const int rho = st * 32 + (lane & 31);
+                const int c = ks * 2 + g;
+                const u32x4 a = *(const u32x4*)(&sK[buf][rho * HD + ((c ^ (rho & 15)) << 3)]);
+                s[st] = mfma(a, qf[ks], s[st]);
+            }
+        }
+
+        // mask, scale, running max.  Element (st, r) is LDS row
+        // rho = 32 st + 8 (r/4) + 4 g + r%4, i.e. key kv0 + perm(rho).
+        float mx = m_i;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int rho = st * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                const int kv = kv0 + perm(rho);
+                float v = s[st][r] * scale;
+                if (kv > myq || kv >= n) v = -INFINITY;
+                s[st][r] = v;
+                mx = fmaxf(mx, v);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float alpha = exp2f(m_i - mx);
+        m_i = mx;
+        l_i *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+
+        // P^T fragments: MFMA m covers keys [16m, 16m+16) of the tile; lane holds
+        // keys 16m + 8g + 0..7 = registers 8(m%2)..8(m%2)+7 of s[m/2]
+        u32x4 pf[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                p[e] = exp2f(s[m >> 1][8 * (m & 1) + e] - mx);
+                l_i += p[e];
+            }
+            pf[m][0] = pack_f16(p[0], p[1]);
+            pf[m][1] = pack_f16(p[2], p[3]);
+            pf[m][2] = pack_f16(p[4], p[5]);
+            pf[m][3] = pack_f16(p[6], p[7]);
+        }
+
+        // O^T[d][q] += V^T[d][kv] P^T[kv][q]
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            const int d = dt * 32 + (lane & 31);
+            const int sw = (d & 7) ^ ((d >> 3) & 1);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int c = 2 * m + g;
+                const u32x4 a = *(const u32x4*)(&sV[buf][d * KT + ((c ^ sw) << 3)]);
+                oacc[dt] = mfma(a, pf[m], oacc[dt]);
+            }
+        }
+
+        if (t + 1 < ntiles) sstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    const float l_tot = l_i + __shfl_xor(l_i, 32);
+    const float inv = 1.0f / l_tot;
+    if (myq < n) {
+        uint16_t* orow = o + (int64_t)myq * ld_o + h * HD;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                // rows d = 32 dt + 8 q + 4 g + 0..3 of O^T, all for this lane's query
+                u32x2 pk;
+                pk[0] = pack_f16(oacc[dt][4 * q + 0] * inv, oacc[dt][4 * q + 1] * inv);
+                pk[1] = pack_f16(oacc[dt][4 * q + 2] * inv, oacc[dt][4 * q + 3] * inv);
+                *(u32x2*)(orow + dt * 32 + 8 * q + 4 * g) = pk;
+            }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attention(const uint16_t* qk, int64_t ld_qk, int32_t k_off, const uint16_t* vt,
+                            int64_t ld_vt, uint16_t* o, int64_t ld_o, int32_t n, int32_t n_heads,
+                            int32_t attn_block, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    if (attn_block % QT) return hipErrorInvalidValue;
+    dim3 grid((n + QT - 1) / QT, n_heads);
+    hipLaunchKernelGGL(attn_fwd, grid, dim3(kThreads), 0, s, qk, ld_qk, k_off, vt, ld_vt, o, ld_o, n,
+                       attn_block);
+    return hipGetLastError();
+}
+
+}  // namespace kva

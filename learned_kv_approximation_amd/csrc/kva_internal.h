@@ -1,0 +1,104 @@
+// Internal declarations shared by the runtime (kva_runtime.hip) and the
+// kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kva {
+
+constexpr int kMaxHeads = 64;
+// Column tile of the head GEMM.  Head outputs are packed so that every tile
+// belongs to one head, except the "tail" tiles that gather the out_dim % 256
+// remainders of all heads (e.g. the 24 DeltaNet a|b pairs, 24 * 96 columns).
+constexpr int kHeadTileN = 256;
+// Activation scratch is allocated with rows rounded up to this, so GEMM A
+// tiles never need a row clamp (rows >= n_tokens are computed and dropped).
+constexpr int kRowPad = 256;
+// Weight rows are padded with zeros to a multiple of this.
+constexpr int kColPad = 256;
+
+struct HeadOut {
+    float* ptr[kMaxHeads];
+    int32_t ld[kMaxHeads];
+};
+
+enum EpiKind : int {
+    EPI_STORE_F32 = 0,  // out_f32[m][n] = acc
+    EPI_ADD_F32 = 1,    // out_f32[m][n] += acc   (residual stream)
+    EPI_QKV = 2,        // n < n_split: out16[m][n] = fp16(acc); else vt[n - n_split][m] = fp16(acc)
+    EPI_SWIGLU = 3,     // gate/up interleaved per 32 columns: out16[m][f] = fp16(silu(g) * u)
+    EPI_HEADS = 4       // bias add, scatter to per-head fp32 outputs
+};
+
+struct EpiArgs {
+    float* out_f32 = nullptr;
+    int64_t ld_f32 = 0;
+    uint16_t* out16 = nullptr;
+    int64_t ld16 = 0;
+    uint16_t* vt = nullptr;
+    int64_t ld_vt = 0;
+    int32_t n_split = 0;
+    int32_t n_real = 0;                 // real (unpadded) columns of the product
+    const int32_t* tile_head = nullptr; // per 256-column tile: head, or -1 for a tail tile
+    const int32_t* tile_col0 = nullptr; // per tile: first destination column in that head
+    const int32_t* tail_head = nullptr; // per tail column: head, or -1 for padding
+    const int32_t* tail_col = nullptr;  // per tail column: destination column
+    int32_t tail_start = 0;             // first packed column of the tail segment
+    const float* bias = nullptr;        // [n_pad] packed bias, or nullptr
+    HeadOut heads;
+};
+
+// C[M][N] = A[M][K] * B[N][K]^T with 16-bit operands and fp32 accumulation.
+struct GemmArgs {
+    const uint16_t* A = nullptr;
+    int64_t lda = 0;
+    const uint16_t* B = nullptr;
+    int64_t ldb = 0;
+    int32_t M = 0;       // rows of A that are real (stores are masked to M)
+    int32_t N = 0;       // columns, a multiple of the tile width (weights are padded)
+    int32_t K = 0;       // multiple of 64
+    EpiArgs epi;
+};
+
+enum GemmOperand : int { OPD_F16 = 0, OPD_BF16 = 1 };
+enum GemmTile : int { TILE_256x256 = 0, TILE_128x128 = 1 };
+
+hipError_t launch_gemm(GemmOperand opd, GemmTile tile, EpiKind epi, const GemmArgs& args,
+                       hipStream_t stream);
+
+// out[r][c] = 16-bit(x[r][c] / sqrt(mean_c x[r][c]^2 + eps) * g[c]); fp16 or bf16.
+hipError_t launch_rmsnorm_cast(const float* x, int64_t ldx, const float* g, int32_t rows,
+                               int32_t cols, float eps, uint16_t* out, int64_t ldo, bool bf16,
+                               hipStream_t stream);
+
+// Block-causal multi-head attention with heads of 128.
+//   qk: [n][ld_qk] fp16, Q of head h at columns [h*128, h*128+128), K at k_off + h*128
+//   vt: [n_heads*128][ld_vt] fp16, V transposed (vt[c][t])
+//   o : [n][ld_o] fp16
+hipError_t launch_attention(const uint16_t* qk, int64_t ld_qk, int32_t k_off, const uint16_t* vt,
+                            int64_t ld_vt, uint16_t* o, int64_t ld_o, int32_t n_tokens,
+                            int32_t n_heads, int32_t attn_block, hipStream_t stream);
+
+struct KvWriteArgs {
+    const float* kv;
+    int64_t ld_kv;
+    int32_t n_tokens;
+    int64_t pos0;
+    const float* k_gain;
+    uint16_t* k_pool;
+    uint16_t* v_pool;
+    const int32_t* page_table;
+    int32_t page_size;
+    int32_t n_pages;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t n_rot;
+    float eps;
+    double inv_freq[64];   // rope_base^(-2j/n_rot), computed on the host in double
+};
+hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
+
+hipError_t launch_dequant_q8_0(const void* blocks, int64_t n_blocks, float* out, hipStream_t stream);
+
+}  // namespace kva

@@ -1,0 +1,156 @@
+// Row-wise kernels: RMSNorm (fused with the 16-bit cast that feeds the next
+// MFMA GEMM), the attention-layer KV-cache write (k_norm + partial RoPE +
+// paged bf16 store) and the q8_0 dequantisation test hook.
+#include "kva_internal.h"
+
+namespace kva {
+namespace {
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+__device__ __forceinline__ uint16_t to_bits(float v, bool bf16) {
+    return bf16 ? __builtin_bit_cast(uint16_t, static_cast<__bf16>(v))
+                : __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+}
+
+// RMSNorm ("Qwen3.8-27B-KVA" model card, "What the hell?": the projector's
+// input norm, the two pre-norms of each block and the final norm):
+// y = x / sqrt(mean(x^2) + eps) * g.  One workgroup per row; fixed
+// reduction order, so a row's result never depends on other rows.
+template <bool BF16>
+__global__ void __launch_bounds__(256) rmsnorm_cast(const float* __restrict__ x, int64_t ldx,
+                                                    const float* __restrict__ gain, int32_t cols,
+                                                    float eps, uint16_t* __restrict__ out,
+                                                    int64_t ldo) {
+    __shared__ float part[4];
+    const int row = blockIdx.x, tid = threadIdx.x;
+    const float* xr = x + (int64_t)row * ldx;
+    float ss = 0.0f;
+    for (int c = tid * 4; c < cols; c += 1024) {
+        const float4 v = *(const float4*)(xr + c);
+        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) part[tid >> 6] = ss;
+    __syncthreads();
+    const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+    const float r = 1.0f / sqrtf(tot / (float)cols + eps);
+    uint16_t* orow = out + (int64_t)row * ldo;
+    for (int c = tid * 4; c < cols; c += 1024) {
+        const float4 v = *(const float4*)(xr + c);
+        const float4 gg = *(const float4*)(gain + c);
+        ushort4 o;
+        o.x = to_bits(v.x * r * gg.x, BF16);
+        o.y = to_bits(v.y * r * gg.y, BF16);
+        o.z = to_bits(v.z * r * gg.z, BF16);
+        o.w = to_bits(v.w * r * gg.w, BF16);
+        *(ushort4*)(orow + c) = o;
+    }
+}
+
+// KV-cache write for one full-attention layer ("Qwen3.8-27B-KVA" card, "What
+// the hell?": after projection the engine applies k_norm and RoPE and writes
+// the KV cache; geometry from the "Qwen3.8-27B-MLA" card, "What this is":
+// 4 KV heads of 256 dims with 64 rotary dims each).  One wave per (token, KV
+// head): lane l holds dims 4l..4l+3 of k and of v.  The rotary pair
+// (j, j + n_rot/2) of lane l < n_rot/8 lives in lane l + n_rot/8.
+// The angle p * inv_freq[j] is formed and reduced modulo 2 pi in double
+// (p reaches 65535 and more: an fp32 product would be off by several 1e-3 rad).
+__global__ void __launch_bounds__(256) kv_write_kernel(KvWriteArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int kvh = threadIdx.x >> 6;           // 4 waves = 4 KV heads (head_dim 256)
+    const int t = blockIdx.x;
+    const int64_t p = a.pos0 + t;
+    const int pg = a.page_table[p / a.page_size];
+    if (pg < 0 || pg >= a.n_pages) return;
+    const int slot = (int)(p % a.page_size);
+    const float* kr = a.kv + (int64_t)t * a.ld_kv + kvh * a.head_dim;
+    const float* vr = kr + a.n_kv_heads * a.head_dim;
+    const int d0 = lane * 4;
+
+    float4 k = *(const float4*)(kr + d0);
+    const float4 v = *(const float4*)(vr + d0);
+    const float ss = wave_sum(k.x * k.x + k.y * k.y + k.z * k.z + k.w * k.w);
+    const float r = 1.0f / sqrtf(ss / (float)a.head_dim + a.eps);
+    const float4 gg = *(const float4*)(a.k_gain + d0);
+    k.x *= r * gg.x; k.y *= r * gg.y; k.z *= r * gg.z; k.w *= r * gg.w;
+
+    const int half_lanes = a.n_rot / 8;         // lanes holding the first half of the rotary dims
+    const float4 other = make_float4(__shfl_xor(k.x, half_lanes), __shfl_xor(k.y, half_lanes),
+                                     __shfl_xor(k.z, half_lanes), __shfl_xor(k.w, half_lanes));
+    if (lane < 2 * half_lanes) {
+        const bool first = lane < half_lanes;
+        const int j0 = (first ? lane : lane - half_lanes) * 4;
+        float kk[4] = {k.x, k.y, k.z, k.w};
+        const float oo[4] = {other.x, other.y, other.z, other.w};
+        const double two_pi = 6.283185307179586476925286766559;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            double th = (double)p * a.inv_freq[j0 + e];
+            th -= two_pi * floor(th / two_pi);
+            float sn, cs;
+            sincosf((float)th, &sn, &cs);
+            // first half: x' = x cos - y sin ; second half: y' = x sin + y cos
+            kk[e] = first ? (kk[e] * cs - oo[e] * sn) : (oo[e] * sn + kk[e] * cs);
+        }
+        k = make_float4(kk[0], kk[1], kk[2], kk[3]);
+    }
+    const int64_t base = (((int64_t)pg * a.page_size + slot) * a.n_kv_heads + kvh) * a.head_dim + d0;
+    ushort4 ko, vo;
+    ko.x = to_bits(k.x, true); ko.y = to_bits(k.y, true); ko.z = to_bits(k.z, true); ko.w = to_bits(k.w, true);
+    vo.x = to_bits(v.x, true); vo.y = to_bits(v.y, true); vo.z = to_bits(v.z, true); vo.w = to_bits(v.w, true);
+    *(ushort4*)(a.k_pool + base) = ko;
+    *(ushort4*)(a.v_pool + base) = vo;
+}
+
+// q8_0 block -> 32 fp32 weights, d * q exactly (the fp16 scale converts
+// exactly to fp32, subnormals included; the product has <= 19 significant bits).
+__device__ __forceinline__ float q8_0_value(uint16_t d_bits, int8_t q) {
+    return (float)__builtin_bit_cast(_Float16, d_bits) * (float)q;
+}
+
+__global__ void dequant_q8_0_kernel(const uint8_t* __restrict__ blocks, int64_t n_blocks,
+                                    float* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // one value per thread
+    if (i >= n_blocks * 32) return;
+    const int64_t b = i >> 5;
+    const uint8_t* blk = blocks + b * 34;
+    const uint16_t d = (uint16_t)blk[0] | ((uint16_t)blk[1] << 8);
+    out[i] = q8_0_value(d, (int8_t)blk[2 + (i & 31)]);
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm_cast(const float* x, int64_t ldx, const float* g, int32_t rows,
+                               int32_t cols, float eps, uint16_t* out, int64_t ldo, bool bf16,
+                               hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    if (cols % 4) return hipErrorInvalidValue;
+    if (bf16)
+        hipLaunchKernelGGL(rmsnorm_cast<true>, dim3(rows), dim3(256), 0, s, x, ldx, g, cols, eps, out, ldo);
+    else
+        hipLaunchKernelGGL(rmsnorm_cast<false>, dim3(rows), dim3(256), 0, s, x, ldx, g, cols, eps, out, ldo);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t s) {
+    if (a.n_tokens <= 0) return hipSuccess;
+    if (a.head_dim != 256 || a.n_kv_heads != 4 || a.n_rot % 8 || a.n_rot > 64 || a.n_rot <= 0)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kv_write_kernel, dim3(a.n_tokens), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant_q8_0(const void* blocks, int64_t n_blocks, float* out, hipStream_t s) {
+    if (n_blocks <= 0) return hipSuccess;
+    const int64_t n = n_blocks * 32;
+    hipLaunchKernelGGL(dequant_q8_0_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       (const uint8_t*)blocks, n_blocks, out);
+    return hipGetLastError();
+}
+
+}  // namespace kva

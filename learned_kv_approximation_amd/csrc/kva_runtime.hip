@@ -1,0 +1,670 @@
+// Host runtime behind the C ABI in include/kva.h: config validation, weight
+// conversion and repacking, device memory, and the launch sequence of one
+// projection (the hot path).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kva.h"
+#include "kva_internal.h"
+
+using namespace kva;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kva_status fail(kva_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+#define HIP_TRY(expr)                                                                   \
+    do {                                                                                \
+        hipError_t e_ = (expr);                                                         \
+        if (e_ != hipSuccess)                                                           \
+            return fail(e_ == hipErrorOutOfMemory ? KVA_ERR_OOM : KVA_ERR_HIP, "%s: %s (%s:%d)", \
+                        #expr, hipGetErrorString(e_), __FILE__, __LINE__);              \
+    } while (0)
+
+int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+// ------------------------------------------------------------------ host number formats
+
+float bf16_to_f32(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+}
+
+// fp32 -> fp16, round to nearest even.  Sets *overflow when a finite input
+// rounds to infinity.
+uint16_t f32_to_f16(float f, bool* overflow) {
+    uint32_t x;
+    std::memcpy(&x, &f, 4);
+    const uint32_t sign = (x >> 16) & 0x8000u;
+    const uint32_t ax = x & 0x7FFFFFFFu;
+    if (ax >= 0x7F800000u) return (uint16_t)(sign | 0x7C00u | (ax > 0x7F800000u ? 0x200u : 0u));
+    if (ax >= 0x477FF000u) {            // >= 65520: rounds past 65504
+        *overflow = true;
+        return (uint16_t)(sign | 0x7C00u);
+    }
+    if (ax >= 0x38800000u) {            // >= 2^-14: normal fp16
+        const uint32_t mant = ax & 0x7FFFFFu;
+        uint32_t h = ((((ax >> 23) - 127u + 15u)) << 10) | (mant >> 13);
+        const uint32_t rem = mant & 0x1FFFu;
+        if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) ++h;
+        return (uint16_t)(sign | h);
+    }
+    if (ax <= 0x33000000u) return (uint16_t)sign;   // <= 2^-25 rounds to zero
+    const uint32_t mant = (ax & 0x7FFFFFu) | 0x800000u;
+    const int shift = 126 - (int)(ax >> 23);       // value / 2^-24 = mant >> shift
+    uint32_t h = mant >> shift;
+    const uint32_t rem = mant & ((1u << shift) - 1u), half = 1u << (shift - 1);
+    if (rem > half || (rem == half && (h & 1u))) ++h;
+    return (uint16_t)(sign | h);
+}
+
+uint16_t f32_to_bf16(float f) {
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+float load_f32(const void* src, int dtype, int64_t i) {
+    if (dtype == KVA_DTYPE_F32) return static_cast<const float*>(src)[i];
+    return bf16_to_f32(static_cast<const uint16_t*>(src)[i]);
+}
+
+// ------------------------------------------------------------------ head packing
+
+struct HeadPlan {
+    int64_t n_pad = 0;
+    int32_t tail_start = 0;
+    std::vector<int32_t> tile_head, tile_col0;   // per kHeadTileN tile
+    std::vector<int32_t> tail_head, tail_col;    // per tail column
+    std::vector<int32_t> col_head, col_index;    // per packed column
+};
+
+HeadPlan plan_heads(const kva_config& c) {
+    HeadPlan p;
+    for (int i = 0; i < c.n_out_heads; ++i) {
+        const int full = c.out_heads[i].out_dim / kHeadTileN;
+        for (int t = 0; t < full; ++t) {
+            p.tile_head.push_back(i);
+            p.tile_col0.push_back(t * kHeadTileN);
+        }
+    }
+    p.tail_start = (int32_t)p.tile_head.size() * kHeadTileN;
+    for (int i = 0; i < c.n_out_heads; ++i) {
+        const int od = c.out_heads[i].out_dim;
+        for (int col = od / kHeadTileN * kHeadTileN; col < od; ++col) {
+            p.tail_head.push_back(i);
+            p.tail_col.push_back(col);
+        }
+    }
+    const int64_t tail_pad = round_up((int64_t)p.tail_head.size(), kHeadTileN);
+    p.tail_head.resize(tail_pad, -1);
+    p.tail_col.resize(tail_pad, 0);
+    for (int64_t t = 0; t < tail_pad / kHeadTileN; ++t) {
+        p.tile_head.push_back(-1);
+        p.tile_col0.push_back(0);
+    }
+    if (p.tail_head.empty()) {   // keep the device arrays non-empty
+        p.tail_head.push_back(-1);
+        p.tail_col.push_back(0);
+    }
+    p.n_pad = (int64_t)p.tile_head.size() * kHeadTileN;
+    p.col_head.resize(p.n_pad);
+    p.col_index.resize(p.n_pad);
+    for (int64_t c2 = 0; c2 < p.tail_start; ++c2) {
+        p.col_head[c2] = p.tile_head[c2 / kHeadTileN];
+        p.col_index[c2] = p.tile_col0[c2 / kHeadTileN] + (int32_t)(c2 % kHeadTileN);
+    }
+    for (int64_t c2 = p.tail_start; c2 < p.n_pad; ++c2) {
+        p.col_head[c2] = p.tail_head[c2 - p.tail_start];
+        p.col_index[c2] = p.tail_col[c2 - p.tail_start];
+    }
+    return p;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ context
+
+struct kva_ctx {
+    kva_config cfg{};
+    std::vector<kva_head_desc> heads;
+    int device = 0;
+    std::vector<void*> allocs;
+    uint64_t weight_bytes = 0, scratch_bytes = 0;
+
+    // weights (device)
+    uint16_t* w_in = nullptr;
+    float* g_in = nullptr;
+    float* g_out = nullptr;
+    struct Blk {
+        float* g_attn;
+        float* g_ffn;
+        uint16_t* wqkv;   // [pad(3 hd)][d] fp16: rows wq | wk | wv
+        uint16_t* wo;     // [pad(d)][hd]
+        uint16_t* wgu;    // [pad(2 F)][d]: per 64 rows, 32 gate rows then the matching 32 up rows
+        uint16_t* wd;     // [pad(d)][F]
+    };
+    std::vector<Blk> blk;
+    uint16_t* w_heads = nullptr;   // [n_pad][d] bf16, packed column order
+    float* b_heads = nullptr;      // [n_pad]
+    int32_t* tile_head = nullptr;
+    int32_t* tile_col0 = nullptr;
+    int32_t* tail_head = nullptr;
+    int32_t* tail_col = nullptr;
+    int64_t n_pad_heads = 0;
+    int32_t tail_start = 0;
+
+    // scratch (device), rows padded to kRowPad
+    int64_t m_alloc = 0;
+    uint16_t* u16 = nullptr;    // [m][n_in]   fp16 normed input
+    float* h = nullptr;         // [m][d]      fp32 residual stream
+    uint16_t* a16 = nullptr;    // [m][d]      fp16 normed activations
+    uint16_t* qk16 = nullptr;   // [m][2 hd]   fp16 Q | K
+    uint16_t* vt16 = nullptr;   // [hd][m]     fp16 V transposed
+    uint16_t* o16 = nullptr;    // [m][hd]     fp16 attention output
+    uint16_t* act16 = nullptr;  // [m][F]      fp16 SwiGLU output
+    uint16_t* z16 = nullptr;    // [m][d]      bf16 final-normed trunk state
+
+    kva_stats stats{};
+
+    // kva_profile_*: event pairs recorded around the launches of selected stages
+    uint32_t prof_mask = 0;
+    struct Rec {
+        int stage;
+        hipEvent_t a, b;
+    };
+    std::vector<Rec> prof_pending;
+    std::vector<hipEvent_t> prof_free;
+    kva_stage_time prof_acc[KVA_N_STAGES]{};
+
+    hipEvent_t take_event() {
+        if (!prof_free.empty()) {
+            hipEvent_t e = prof_free.back();
+            prof_free.pop_back();
+            return e;
+        }
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        return e;
+    }
+
+    template <class T>
+    hipError_t alloc(T** p, size_t bytes, bool weight) {
+        void* q = nullptr;
+        hipError_t e = hipMalloc(&q, bytes);
+        if (e != hipSuccess) return e;
+        allocs.push_back(q);
+        (weight ? weight_bytes : scratch_bytes) += bytes;
+        *p = static_cast<T*>(q);
+        return hipSuccess;
+    }
+    ~kva_ctx() {
+        for (Rec& r : prof_pending) {
+            (void)hipEventDestroy(r.a);
+            (void)hipEventDestroy(r.b);
+        }
+        for (hipEvent_t e : prof_free) (void)hipEventDestroy(e);
+        for (void* p : allocs) (void)hipFree(p);
+    }
+};
+
+namespace {
+
+kva_status validate(const kva_config* c) {
+    if (!c) return fail(KVA_ERR_ARG, "config is NULL");
+    if (c->n_in <= 0 || c->d_model <= 0 || c->n_blocks <= 0 || c->n_heads <= 0 ||
+        c->head_dim <= 0 || c->d_ffn <= 0 || c->attn_block <= 0 || c->max_tokens <= 0)
+        return fail(KVA_ERR_SHAPE, "all dimensions must be positive");
+    if (c->head_dim != 128) return fail(KVA_ERR_SHAPE, "head_dim must be 128 (got %d)", c->head_dim);
+    if ((int64_t)c->n_heads * c->head_dim != c->d_model)
+        return fail(KVA_ERR_SHAPE, "n_heads*head_dim (%d) must equal d_model (%d)",
+                    c->n_heads * c->head_dim, c->d_model);
+    if (c->n_in % 64 || c->d_model % 64 || c->d_ffn % 64)
+        return fail(KVA_ERR_SHAPE, "n_in, d_model and d_ffn must be multiples of 64");
+    if (c->attn_block % 64) return fail(KVA_ERR_SHAPE, "attn_block must be a multiple of 64");
+    if (c->n_blocks > 64) return fail(KVA_ERR_SHAPE, "at most 64 transformer blocks");
+    if (c->max_tokens > (1 << 24)) return fail(KVA_ERR_SHAPE, "max_tokens above 2^24");
+    if (!(c->eps >= 0.0f) || !std::isfinite(c->eps)) return fail(KVA_ERR_ARG, "eps must be finite and >= 0");
+    if (c->weight_dtype != KVA_DTYPE_F32 && c->weight_dtype != KVA_DTYPE_BF16 &&
+        c->weight_dtype != KVA_DTYPE_Q8_0)
+        return fail(KVA_ERR_DTYPE, "unknown weight dtype %d", c->weight_dtype);
+    if (c->has_head_bias != 0 && c->has_head_bias != 1) return fail(KVA_ERR_ARG, "has_head_bias must be 0 or 1");
+    if (c->n_out_heads < 1 || c->n_out_heads > kMaxHeads)
+        return fail(KVA_ERR_SHAPE, "n_out_heads must be in [1, %d]", kMaxHeads);
+    if (!c->out_heads) return fail(KVA_ERR_ARG, "out_heads is NULL");
+    for (int i = 0; i < c->n_out_heads; ++i) {
+        const kva_head_desc& h = c->out_heads[i];
+        if (h.out_dim <= 0 || h.out_dim > (1 << 20)) return fail(KVA_ERR_SHAPE, "head %d: bad out_dim %d", i, h.out_dim);
+        if (h.kind < KVA_HEAD_DELTANET || h.kind > KVA_HEAD_DRAFT) return fail(KVA_ERR_ARG, "head %d: bad kind", i);
+    }
+    return KVA_OK;
+}
+
+// Converts a [rows][cols] weight (fp32 or bf16) to fp16 at dst.
+kva_status to_f16_rows(const void* src, int dtype, int64_t rows, int64_t cols, uint16_t* dst,
+                       const char* name) {
+    if (!src) return fail(KVA_ERR_ARG, "weight %s is NULL", name);
+    bool ovf = false;
+    const int64_t n = rows * cols;
+    for (int64_t i = 0; i < n; ++i) dst[i] = f32_to_f16(load_f32(src, dtype, i), &ovf);
+    if (ovf) return fail(KVA_ERR_RANGE, "weight %s has values outside the fp16 range", name);
+    return KVA_OK;
+}
+
+kva_status upload(kva_ctx* ctx, void* dst, const void* src, size_t bytes) {
+    HIP_TRY(hipMemcpy(dst, src, bytes, hipMemcpyHostToDevice));
+    return KVA_OK;
+}
+
+#define KVA_TRY(expr)                    \
+    do {                                 \
+        kva_status s_ = (expr);          \
+        if (s_ != KVA_OK) return s_;     \
+    } while (0)
+
+kva_status create_impl(const kva_config* cfg, const kva_weights* w, int device, kva_ctx* ctx) {
+    const kva_config& c = *cfg;
+    if (c.weight_dtype == KVA_DTYPE_Q8_0)
+        return fail(KVA_ERR_UNSUPPORTED, "q8_0 weights are not supported by this build yet");
+    const int dt = c.weight_dtype;
+    const int64_t d = c.d_model, F = c.d_ffn, n_in = c.n_in;
+    const int64_t hd = (int64_t)c.n_heads * c.head_dim;
+    HIP_TRY(hipSetDevice(device));
+    ctx->device = device;
+
+    // -------- trunk weights -> fp16
+    std::vector<uint16_t> stage;
+    auto put16 = [&](uint16_t** dstp, int64_t rows_pad, int64_t cols) -> kva_status {
+        HIP_TRY(ctx->alloc(dstp, (size_t)rows_pad * cols * 2, true));
+        return upload(ctx, *dstp, stage.data(), (size_t)rows_pad * cols * 2);
+    };
+    auto putf = [&](float** dstp, const float* src, int64_t n, const char* name) -> kva_status {
+        if (!src) return fail(KVA_ERR_ARG, "gain %s is NULL", name);
+        HIP_TRY(ctx->alloc(dstp, (size_t)n * 4, true));
+        return upload(ctx, *dstp, src, (size_t)n * 4);
+    };
+
+    KVA_TRY(putf(&ctx->g_in, w->in_norm, n_in, "in_norm"));
+    KVA_TRY(putf(&ctx->g_out, w->out_norm, d, "out_norm"));
+    stage.assign((size_t)round_up(d, kColPad) * n_in, 0);
+    KVA_TRY(to_f16_rows(w->in_proj, dt, d, n_in, stage.data(), "in_proj"));
+    KVA_TRY(put16(&ctx->w_in, round_up(d, kColPad), n_in));
+
+    if (!w->blocks) return fail(KVA_ERR_ARG, "blocks is NULL");
+    ctx->blk.resize(c.n_blocks);
+    std::vector<uint16_t> tmp;
+    for (int b = 0; b < c.n_blocks; ++b) {
+        const kva_block_weights& bw = w->blocks[b];
+        kva_ctx::Blk& B = ctx->blk[b];
+        KVA_TRY(putf(&B.g_attn, bw.attn_norm, d, "attn_norm"));
+        KVA_TRY(putf(&B.g_ffn, bw.ffn_norm, d, "ffn_norm"));
+        stage.assign((size_t)round_up(3 * hd, kColPad) * d, 0);
+        KVA_TRY(to_f16_rows(bw.wq, dt, hd, d, stage.data(), "wq"));
+        KVA_TRY(to_f16_rows(bw.wk, dt, hd, d, stage.data() + hd * d, "wk"));
+        KVA_TRY(to_f16_rows(bw.wv, dt, hd, d, stage.data() + 2 * hd * d, "wv"));
+        KVA_TRY(put16(&B.wqkv, round_up(3 * hd, kColPad), d));
+        stage.assign((size_t)round_up(d, kColPad) * hd, 0);
+        KVA_TRY(to_f16_rows(bw.wo, dt, d, hd, stage.data(), "wo"));
+        KVA_TRY(put16(&B.wo, round_up(d, kColPad), hd));
+        // gate/up interleaved in groups of 32 rows so one 64-column MFMA pair
+        // holds gate and up of the same 32 hidden units
+        stage.assign((size_t)round_up(2 * F, kColPad) * d, 0);
+        tmp.assign((size_t)F * d, 0);
+        KVA_TRY(to_f16_rows(bw.w_gate, dt, F, d, tmp.data(), "w_gate"));
+        for (int64_t f = 0; f < F; ++f)
+            std::memcpy(&stage[(size_t)((f / 32) * 64 + f % 32) * d], &tmp[(size_t)f * d], (size_t)d * 2);
+        KVA_TRY(to_f16_rows(bw.w_up, dt, F, d, tmp.data(), "w_up"));
+        for (int64_t f = 0; f < F; ++f)
+            std::memcpy(&stage[(size_t)((f / 32) * 64 + 32 + f % 32) * d], &tmp[(size_t)f * d], (size_t)d * 2);
+        KVA_TRY(put16(&B.wgu, round_up(2 * F, kColPad), d));
+        stage.assign((size_t)round_up(d, kColPad) * F, 0);
+        KVA_TRY(to_f16_rows(bw.w_down, dt, d, F, stage.data(), "w_down"));
+        KVA_TRY(put16(&B.wd, round_up(d, kColPad), F));
+    }
+
+    // -------- heads -> bf16, packed column order
+    if (!w->head_w) return fail(KVA_ERR_ARG, "head_w is NULL");
+    if (c.has_head_bias && !w->head_b) return fail(KVA_ERR_ARG, "head_b is NULL but has_head_bias is set");
+    HeadPlan plan = plan_heads(c);
+    ctx->n_pad_heads = plan.n_pad;
+    ctx->tail_start = plan.tail_start;
+    for (int i = 0; i < c.n_out_heads; ++i) {
+        if (!w->head_w[i]) return fail(KVA_ERR_ARG, "head_w[%d] is NULL", i);
+        if (c.has_head_bias && !w->head_b[i]) return fail(KVA_ERR_ARG, "head_b[%d] is NULL", i);
+    }
+    stage.assign((size_t)plan.n_pad * d, 0);
+    std::vector<float> bias((size_t)plan.n_pad, 0.0f);
+    for (int64_t col = 0; col < plan.n_pad; ++col) {
+        const int hh = plan.col_head[col];
+        if (hh < 0) continue;
+        const int64_t src_row = plan.col_index[col];
+        uint16_t* dst = &stage[(size_t)col * d];
+        if (dt == KVA_DTYPE_BF16) {
+            std::memcpy(dst, static_cast<const uint16_t*>(w->head_w[hh]) + src_row * d, (size_t)d * 2);
+        } else {
+            const float* s = static_cast<const float*>(w->head_w[hh]) + src_row * d;
+            for (int64_t k = 0; k < d; ++k) dst[k] = f32_to_bf16(s[k]);
+        }
+        if (c.has_head_bias) bias[col] = w->head_b[hh][src_row];
+    }
+    KVA_TRY(put16(&ctx->w_heads, plan.n_pad, d));
+    {
+        float* bb = nullptr;
+        HIP_TRY(ctx->alloc(&bb, (size_t)plan.n_pad * 4, true));
+        KVA_TRY(upload(ctx, bb, bias.data(), (size_t)plan.n_pad * 4));
+        ctx->b_heads = c.has_head_bias ? bb : nullptr;
+    }
+    auto puti = [&](int32_t** dstp, const std::vector<int32_t>& v) -> kva_status {
+        HIP_TRY(ctx->alloc(dstp, v.size() * 4, true));
+        return upload(ctx, *dstp, v.data(), v.size() * 4);
+    };
+    KVA_TRY(puti(&ctx->tile_head, plan.tile_head));
+    KVA_TRY(puti(&ctx->tile_col0, plan.tile_col0));
+    KVA_TRY(puti(&ctx->tail_head, plan.tail_head));
+    KVA_TRY(puti(&ctx->tail_col, plan.tail_col));
+
+    // -------- scratch
+    const int64_t m = round_up(c.max_tokens, kRowPad);
+    ctx->m_alloc = m;
+    HIP_TRY(ctx->alloc(&ctx->u16, (size_t)m * n_in * 2, false));
+    HIP_TRY(ctx->alloc(&ctx->h, (size_t)m * d * 4, false));
+    HIP_TRY(ctx->alloc(&ctx->a16, (size_t)m * d * 2, false));
+    HIP_TRY(ctx->alloc(&ctx->qk16, (size_t)m * 2 * hd * 2, false));
+    HIP_TRY(ctx->alloc(&ctx->vt16, (size_t)hd * m * 2, false));
+    HIP_TRY(ctx->alloc(&ctx->o16, (size_t)m * hd * 2, false));
+    HIP_TRY(ctx->alloc(&ctx->act16, (size_t)m * F * 2, false));
+    HIP_TRY(ctx->alloc(&ctx->z16, (size_t)m * d * 2, false));
+    // Scratch rows past n_tokens feed MFMA rows whose results are dropped; zero
+    // them once so they always hold finite values.
+    HIP_TRY(hipMemset(ctx->u16, 0, (size_t)m * n_in * 2));
+    HIP_TRY(hipMemset(ctx->h, 0, (size_t)m * d * 4));
+    HIP_TRY(hipMemset(ctx->a16, 0, (size_t)m * d * 2));
+    HIP_TRY(hipMemset(ctx->qk16, 0, (size_t)m * 2 * hd * 2));
+    HIP_TRY(hipMemset(ctx->vt16, 0, (size_t)hd * m * 2));
+    HIP_TRY(hipMemset(ctx->o16, 0, (size_t)m * hd * 2));
+    HIP_TRY(hipMemset(ctx->act16, 0, (size_t)m * F * 2));
+    HIP_TRY(hipMemset(ctx->z16, 0, (size_t)m * d * 2));
+    HIP_TRY(hipDeviceSynchronize());
+    return KVA_OK;
+}
+
+#define LAUNCH(expr)                                                                      \
+    do {                                                                                  \
+        hipError_t e_ = (expr);                                                           \
+        if (e_ != hipSuccess) return fail(KVA_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+    } while (0)
+
+// Launch of one stage of the projection, bracketed by an event pair when the
+// stage is selected for profiling.
+#define STAGE(stage, expr)                                                                \
+    do {                                                                                  \
+        hipEvent_t a_ = nullptr, b_ = nullptr;                                            \
+        if (ctx->prof_mask & (1u << (stage))) {                                           \
+            a_ = ctx->take_event();                                                       \
+            b_ = ctx->take_event();                                                       \
+            if (a_ && b_) HIP_TRY(hipEventRecord(a_, s));                                 \
+        }                                                                                 \
+        LAUNCH(expr);                                                                     \
+        if (a_ && b_) {                                                                   \
+            HIP_TRY(hipEventRecord(b_, s));                                               \
+            ctx->prof_pending.push_back({(stage), a_, b_});                               \
+        }                                                                                 \
+    } while (0)
+
+}  // namespace
+
+// ================================================================== C ABI
+
+extern "C" {
+
+kva_status kva_validate_config(const kva_config* cfg) { return validate(cfg); }
+
+kva_status kva_create(const kva_config* cfg, const kva_weights* w, int device, kva_ctx** out) {
+    if (!out) return fail(KVA_ERR_ARG, "out is NULL");
+    *out = nullptr;
+    KVA_TRY(validate(cfg));
+    if (!w) return fail(KVA_ERR_ARG, "weights are NULL");
+    kva_ctx* ctx = new (std::nothrow) kva_ctx();
+    if (!ctx) return fail(KVA_ERR_OOM, "host allocation failed");
+    ctx->cfg = *cfg;
+    ctx->heads.assign(cfg->out_heads, cfg->out_heads + cfg->n_out_heads);
+    ctx->cfg.out_heads = ctx->heads.data();
+    kva_status s;
+    try {
+        s = create_impl(&ctx->cfg, w, device, ctx);
+    } catch (const std::bad_alloc&) {
+        s = fail(KVA_ERR_OOM, "host allocation failed while repacking weights");
+    }
+    if (s != KVA_OK) {
+        delete ctx;
+        return s;
+    }
+    ctx->stats.weight_bytes = ctx->weight_bytes;
+    ctx->stats.scratch_bytes = ctx->scratch_bytes;
+    *out = ctx;
+    return KVA_OK;
+}
+
+kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n, float* const* head_out,
+                              void* stream) {
+    if (!ctx || !x || !head_out) return fail(KVA_ERR_ARG, "NULL argument");
+    const kva_config& c = ctx->cfg;
+    if (n < 1 || n > c.max_tokens)
+        return fail(KVA_ERR_SHAPE, "n_tokens %d outside [1, %d]", n, c.max_tokens);
+    HeadOut ho{};
+    for (int i = 0; i < c.n_out_heads; ++i) {
+        if (!head_out[i]) return fail(KVA_ERR_ARG, "head_out[%d] is NULL", i);
+        ho.ptr[i] = head_out[i];
+        ho.ld[i] = c.out_heads[i].out_dim;
+    }
+    HIP_TRY(hipSetDevice(ctx->device));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t d = c.d_model, F = c.d_ffn, n_in = c.n_in;
+    const int64_t hd = (int64_t)c.n_heads * c.head_dim;
+
+    STAGE(KVA_STAGE_NORM, launch_rmsnorm_cast(x, n_in, ctx->g_in, n, (int32_t)n_in, c.eps, ctx->u16, n_in, false, s));
+    {
+        GemmArgs g;
+        g.A = ctx->u16; g.lda = n_in; g.B = ctx->w_in; g.ldb = n_in;
+        g.M = n; g.N = (int32_t)round_up(d, kColPad); g.K = (int32_t)n_in;
+        g.epi.out_f32 = ctx->h; g.epi.ld_f32 = d; g.epi.n_real = (int32_t)d;
+        STAGE(KVA_STAGE_GEMM_IN, launch_gemm(OPD_F16, TILE_128x128, EPI_STORE_F32, g, s));
+    }
+    for (int b = 0; b < c.n_blocks; ++b) {
+        const kva_ctx::Blk& B = ctx->blk[b];
+        STAGE(KVA_STAGE_NORM, launch_rmsnorm_cast(ctx->h, d, B.g_attn, n, (int32_t)d, c.eps, ctx->a16, d, false, s));
+        {
+            GemmArgs g;
+            g.A = ctx->a16; g.lda = d; g.B = B.wqkv; g.ldb = d;
+            g.M = n; g.N = (int32_t)round_up(3 * hd, kColPad); g.K = (int32_t)d;
+            g.epi.out16 = ctx->qk16; g.epi.ld16 = 2 * hd;
+            g.epi.vt = ctx->vt16; g.epi.ld_vt = ctx->m_alloc; g.epi.n_split = (int32_t)(2 * hd);
+            g.epi.n_real = (int32_t)(3 * hd);
+            STAGE(KVA_STAGE_GEMM_QKV, launch_gemm(OPD_F16, TILE_128x128, EPI_QKV, g, s));
+        }
+        STAGE(KVA_STAGE_ATTN, launch_attention(ctx->qk16, 2 * hd, (int32_t)hd, ctx->vt16, ctx->m_alloc, ctx->o16, hd, n,
+                                c.n_heads, c.attn_block, s));
+        {
+            GemmArgs g;
+            g.A = ctx->o16; g.lda = hd; g.B = B.wo; g.ldb = hd;
+            g.M = n; g.N = (int32_t)round_up(d, kColPad); g.K = (int32_t)hd;
+            g.epi.out_f32 = ctx->h; g.epi.ld_f32 = d; g.epi.n_real = (int32_t)d;
+            STAGE(KVA_STAGE_GEMM_O, launch_gemm(OPD_F16, TILE_128x128, EPI_ADD_F32, g, s));
+        }
+        STAGE(KVA_STAGE_NORM, launch_rmsnorm_cast(ctx->h, d, B.g_ffn, n, (int32_t)d, c.eps, ctx->a16, d, false, s));
+        {
+            GemmArgs g;
+            g.A = ctx->a16; g.lda = d; g.B = B.wgu; g.ldb = d;
+            g.M = n; g.N = (int32_t)round_up(2 * F, kColPad); g.K = (int32_t)d;
+            g.epi.out16 = ctx->act16; g.epi.ld16 = F; g.epi.n_real = (int32_t)(2 * F);
+            STAGE(KVA_STAGE_GEMM_GATEUP, launch_gemm(OPD_F16, TILE_128x128, EPI_SWIGLU, g, s));
+        }
+        {
+            GemmArgs g;
+            g.A = ctx->act16; g.lda = F; g.B = B.wd; g.ldb = F;
+            g.M = n; g.N = (int32_t)round_up(d, kColPad); g.K = (int32_t)F;
+            g.epi.out_f32 = ctx->h; g.epi.ld_f32 = d; g.epi.n_real = (int32_t)d;
+            STAGE(KVA_STAGE_GEMM_DOWN, launch_gemm(OPD_F16, TILE_128x128, EPI_ADD_F32, g, s));
+        }
+    }
+    STAGE(KVA_STAGE_NORM, launch_rmsnorm_cast(ctx->h, d, ctx->g_out, n, (int32_t)d, c.eps, ctx->z16, d, true, s));
+    {
+        GemmArgs g;
+        g.A = ctx->z16; g.lda = d; g.B = ctx->w_heads; g.ldb = d;
+        g.M = n; g.N = (int32_t)ctx->n_pad_heads; g.K = (int32_t)d;
+        g.epi.n_real = (int32_t)ctx->n_pad_heads;
+        g.epi.tile_head = ctx->tile_head; g.epi.tile_col0 = ctx->tile_col0;
+        g.epi.tail_head = ctx->tail_head; g.epi.tail_col = ctx->tail_col;
+        g.epi.tail_start = ctx->tail_start; g.epi.bias = ctx->b_heads;
+        g.epi.heads = ho;
+        STAGE(KVA_STAGE_GEMM_HEADS, launch_gemm(OPD_BF16, TILE_256x256, EPI_HEADS, g, s));
+    }
+    ctx->stats.calls += 1;
+    ctx->stats.tokens += (uint64_t)n;
+    ctx->stats.blocks += (uint64_t)((n + c.attn_block - 1) / c.attn_block);
+    return KVA_OK;
+}
+
+kva_status kva_destroy(kva_ctx* ctx) {
+    if (!ctx) return KVA_OK;
+    kva_status s = KVA_OK;
+    if (hipSetDevice(ctx->device) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+        s = fail(KVA_ERR_HIP, "device synchronisation failed in kva_destroy");
+    delete ctx;
+    return s;
+}
+
+kva_status kva_attn_kv_write(const float* kv, int64_t ld_kv, int32_t n, int64_t pos0,
+                             const float* k_gain, const kva_paged_kv* cache, void* stream) {
+    if (!kv || !k_gain || !cache || !cache->k_pool || !cache->v_pool || !cache->page_table)
+        return fail(KVA_ERR_ARG, "NULL argument");
+    if (n < 0 || pos0 < 0) return fail(KVA_ERR_SHAPE, "negative n_tokens or pos0");
+    if (cache->n_kv_heads != 4 || cache->head_dim != 256)
+        return fail(KVA_ERR_UNSUPPORTED, "only 4 KV heads of 256 dims are supported");
+    if (cache->n_rot <= 0 || cache->n_rot > 64 || cache->n_rot % 8)
+        return fail(KVA_ERR_SHAPE, "n_rot must be a multiple of 8 in [8, 64]");
+    if (cache->page_size <= 0 || cache->n_pages <= 0 || cache->n_logical <= 0)
+        return fail(KVA_ERR_SHAPE, "page_size, n_pages and n_logical must be positive");
+    if (ld_kv < 2LL * cache->n_kv_heads * cache->head_dim || ld_kv % 4)
+        return fail(KVA_ERR_SHAPE, "ld_kv must be >= 2*n_kv_heads*head_dim and a multiple of 4");
+    if (pos0 + n > (int64_t)cache->n_logical * cache->page_size)
+        return fail(KVA_ERR_SHAPE, "positions past the page table");
+    if (!(cache->rope_base > 1.0) || !std::isfinite(cache->rope_base))
+        return fail(KVA_ERR_ARG, "rope_base must be > 1");
+    if (n == 0) return KVA_OK;
+    KvWriteArgs a{};
+    a.kv = kv; a.ld_kv = ld_kv; a.n_tokens = n; a.pos0 = pos0; a.k_gain = k_gain;
+    a.k_pool = cache->k_pool; a.v_pool = cache->v_pool; a.page_table = cache->page_table;
+    a.page_size = cache->page_size; a.n_pages = cache->n_pages; a.n_kv_heads = cache->n_kv_heads;
+    a.head_dim = cache->head_dim; a.n_rot = cache->n_rot; a.eps = cache->eps;
+    for (int j = 0; j < cache->n_rot / 2; ++j)
+        a.inv_freq[j] = std::pow(cache->rope_base, -2.0 * j / (double)cache->n_rot);
+    LAUNCH(launch_kv_write(a, static_cast<hipStream_t>(stream)));
+    return KVA_OK;
+}
+
+kva_status kva_debug_dequant_q8_0(const void* blocks, int64_t n_blocks, float* out, void* stream) {
+    if (!blocks || !out) return fail(KVA_ERR_ARG, "NULL argument");
+    if (n_blocks < 0) return fail(KVA_ERR_SHAPE, "negative n_blocks");
+    LAUNCH(launch_dequant_q8_0(blocks, n_blocks, out, static_cast<hipStream_t>(stream)));
+    return KVA_OK;
+}
+
+kva_status kva_debug_copy_z(kva_ctx* ctx, uint16_t* dst, int32_t n, void* stream) {
+    if (!ctx || !dst) return fail(KVA_ERR_ARG, "NULL argument");
+    if (n < 1 || n > ctx->cfg.max_tokens) return fail(KVA_ERR_SHAPE, "bad n_tokens");
+    HIP_TRY(hipMemcpyAsync(dst, ctx->z16, (size_t)n * ctx->cfg.d_model * 2, hipMemcpyDeviceToDevice,
+                           static_cast<hipStream_t>(stream)));
+    return KVA_OK;
+}
+
+kva_status kva_debug_head_plan(const kva_config* cfg, int32_t* n_cols, int32_t* col_head,
+                               int32_t* col_index, int64_t capacity) {
+    KVA_TRY(validate(cfg));
+    if (!n_cols) return fail(KVA_ERR_ARG, "n_cols is NULL");
+    HeadPlan p = plan_heads(*cfg);
+    *n_cols = (int32_t)p.n_pad;
+    if (!col_head && !col_index) return KVA_OK;
+    if (capacity < p.n_pad) return fail(KVA_ERR_SHAPE, "capacity %lld < %lld", (long long)capacity, (long long)p.n_pad);
+    for (int64_t i = 0; i < p.n_pad; ++i) {
+        if (col_head) col_head[i] = p.col_head[i];
+        if (col_index) col_index[i] = p.col_head[i] < 0 ? -1 : p.col_index[i];
+    }
+    return KVA_OK;
+}
+
+kva_status kva_debug_host_to_f16(const void* src, int32_t src_dtype, int64_t n, uint16_t* dst) {
+    if (!src || !dst) return fail(KVA_ERR_ARG, "NULL argument");
+    if (src_dtype != KVA_DTYPE_F32 && src_dtype != KVA_DTYPE_BF16) return fail(KVA_ERR_DTYPE, "bad dtype");
+    bool ovf = false;
+    for (int64_t i = 0; i < n; ++i) dst[i] = f32_to_f16(load_f32(src, src_dtype, i), &ovf);
+    return ovf ? fail(KVA_ERR_RANGE, "value outside the fp16 range") : KVA_OK;
+}
+
+kva_status kva_profile_enable(kva_ctx* ctx, uint32_t stage_mask) {
+    if (!ctx) return fail(KVA_ERR_ARG, "ctx is NULL");
+    ctx->prof_mask = stage_mask & ((1u << KVA_N_STAGES) - 1u);
+    return KVA_OK;
+}
+
+kva_status kva_profile_read(kva_ctx* ctx, kva_stage_time* out) {
+    if (!ctx || !out) return fail(KVA_ERR_ARG, "NULL argument");
+    HIP_TRY(hipSetDevice(ctx->device));
+    for (kva_ctx::Rec& r : ctx->prof_pending) {
+        HIP_TRY(hipEventSynchronize(r.b));
+        float ms = 0.0f;
+        HIP_TRY(hipEventElapsedTime(&ms, r.a, r.b));
+        ctx->prof_acc[r.stage].launches += 1;
+        ctx->prof_acc[r.stage].total_ms += ms;
+        ctx->prof_free.push_back(r.a);
+        ctx->prof_free.push_back(r.b);
+    }
+    ctx->prof_pending.clear();
+    for (int i = 0; i < KVA_N_STAGES; ++i) {
+        out[i] = ctx->prof_acc[i];
+        ctx->prof_acc[i] = kva_stage_time{};
+    }
+    return KVA_OK;
+}
+
+kva_status kva_get_stats(const kva_ctx* ctx, kva_stats* out) {
+    if (!ctx || !out) return fail(KVA_ERR_ARG, "NULL argument");
+    *out = ctx->stats;
+    return KVA_OK;
+}
+
+const char* kva_status_str(kva_status s) {
+    switch (s) {
+        case KVA_OK: return "KVA_OK";
+        case KVA_ERR_ARG: return "KVA_ERR_ARG";
+        case KVA_ERR_SHAPE: return "KVA_ERR_SHAPE";
+        case KVA_ERR_DTYPE: return "KVA_ERR_DTYPE";
+        case KVA_ERR_OOM: return "KVA_ERR_OOM";
+        case KVA_ERR_RANGE: return "KVA_ERR_RANGE";
+        case KVA_ERR_UNSUPPORTED: return "KVA_ERR_UNSUPPORTED";
+        case KVA_ERR_HIP: return "KVA_ERR_HIP";
+    }
+    return "KVA_ERR_UNKNOWN";
+}
+
+const char* kva_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

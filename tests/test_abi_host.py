@@ -1,0 +1,114 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/kva.h declares, validates configs, and its host-side
+weight conversion and head packing are right."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import learned_kv_approximation_amd as kva
+import synth
+
+
+def test_library_exports_every_declared_function():
+    names = kva.header_exports()
+    assert {"kva_create", "kva_project_ubatch", "kva_destroy", "kva_attn_kv_write"} <= set(names)
+    L = kva.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(kva._SIGS), "binding signatures out of step with the header"
+
+
+def test_status_strings_and_null_safety():
+    L = kva.lib()
+    for s in range(8):
+        assert L.kva_status_str(s).decode().startswith("KVA_")
+    assert kva.lib().kva_destroy(None) == kva.KVA_OK
+    assert L.kva_project_ubatch(None, None, 1, None, None) == kva.KVA_ERR_ARG
+    assert b"NULL" in L.kva_last_error()
+
+
+@pytest.mark.parametrize("name", ["tiny", "r2", "r3"])
+def test_validate_accepts_page_configs(name):
+    c, keep = kva.make_config(synth.config(name))
+    assert kva.kva_validate_config(c) == kva.KVA_OK
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 64, kva.KVA_ERR_SHAPE),
+    ("n_heads", 3, kva.KVA_ERR_SHAPE),
+    ("d_ffn", 7000, kva.KVA_ERR_SHAPE),
+    ("attn_block", 1000, kva.KVA_ERR_SHAPE),
+    ("max_tokens", 0, kva.KVA_ERR_SHAPE),
+    ("weight_dtype", 9, kva.KVA_ERR_DTYPE),
+    ("n_out_heads", 0, kva.KVA_ERR_SHAPE),
+    ("n_out_heads", 65, kva.KVA_ERR_SHAPE),
+    ("has_head_bias", 2, kva.KVA_ERR_ARG),
+])
+def test_validate_rejects(field, value, status):
+    c, keep = kva.make_config(synth.config("r2"))
+    setattr(c, field, value)
+    assert kva.kva_validate_config(c) == status
+    assert kva.lib().kva_last_error()
+
+
+def test_validate_rejects_bad_head():
+    cfg = synth.config("tiny")
+    cfg["heads"][1]["out_dim"] = 0
+    c, keep = kva.make_config(cfg)
+    assert kva.kva_validate_config(c) == kva.KVA_ERR_SHAPE
+
+
+@pytest.mark.parametrize("name", ["tiny", "r2", "r3"])
+def test_head_plan_is_a_tiled_bijection(name):
+    cfg = synth.config(name)
+    c, keep = kva.make_config(cfg)
+    head, idx = kva.kva_debug_head_plan(c)
+    assert head.size % 256 == 0
+    seen = set()
+    for h, i in zip(head.tolist(), idx.tolist()):
+        if h < 0:
+            continue
+        assert 0 <= i < cfg["heads"][h]["out_dim"]
+        seen.add((h, i))
+    assert len(seen) == sum(h["out_dim"] for h in cfg["heads"])
+    assert np.count_nonzero(head >= 0) == len(seen)
+    # every 256-column tile outside the tail belongs to a single head
+    tiles = head.reshape(-1, 256)
+    full = [t for t in tiles if np.all(t == t[0]) and t[0] >= 0]
+    assert len(full) == sum(h["out_dim"] // 256 for h in cfg["heads"])
+    if name == "r2":
+        assert head.size == 264448 + 0   # 24 * 96 a|b columns fill 9 tiles exactly
+
+
+def test_host_f16_conversion_matches_numpy():
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal(200000) * np.exp2(rng.integers(-30, 17, 200000))).astype(np.float32)
+    x = x[np.abs(x) < 65504]
+    st, got = kva.kva_debug_host_to_f16(x, "f32")
+    assert st == kva.KVA_OK
+    assert np.array_equal(got, x.astype(np.float16).view(np.uint16))
+    b = synth.f32_to_bf16_bits(x[np.abs(x) < 65280])   # bf16 rounding must stay finite in fp16
+    st, got = kva.kva_debug_host_to_f16(b, "bf16")
+    bf = (b.astype(np.uint32) << 16).view(np.float32)
+    assert st == kva.KVA_OK and np.array_equal(got, bf.astype(np.float16).view(np.uint16))
+    # ties and the overflow edge
+    edge = np.array([65504.0, 65519.99, 65520.0, -70000.0, 2.0 ** -25, 3 * 2.0 ** -26, 1.0 + 2 ** -11],
+                    dtype=np.float32)
+    st, got = kva.kva_debug_host_to_f16(edge, "f32")
+    assert st == kva.KVA_ERR_RANGE
+    with np.errstate(over="ignore"):
+        assert np.array_equal(got, edge.astype(np.float16).view(np.uint16))
+
+
+def test_create_without_device_fails_cleanly():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    cfg = synth.config("tiny")
+    w = synth.make_weights(cfg)
+    c, k1 = kva.make_config(cfg)
+    s, k2 = kva.make_weights(cfg, w)
+    out = ctypes.c_void_p()
+    st = kva.lib().kva_create(ctypes.byref(c), ctypes.byref(s), 0, ctypes.byref(out))
+    assert st in (kva.KVA_ERR_HIP, kva.KVA_ERR_OOM) and out.value is None

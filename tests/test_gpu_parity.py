@@ -1,0 +1,235 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Bar (per head): max|y_gpu - y_oracle| <= 2e-2 * RMS(y_oracle) for 16-bit
+weights, and bitwise equality for the block-structure invariants (a block's
+outputs do not depend on other blocks or on later tokens), the q8_0
+dequantisation hook, and determinism.  The KV-cache write must land within
+one bf16 ulp of the oracle's correctly rounded value.
+"""
+import numpy as np
+import pytest
+import torch
+
+import learned_kv_approximation_amd as kva
+import oracle
+import synth
+from oracle import ref
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _run(proj, x):
+    outs = proj.project(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    return [o.cpu().numpy() for o in outs]
+
+
+def _errs(got, want):
+    out = {}
+    for i, y in want.items():
+        g = got[i].astype(np.float64)
+        rms = np.sqrt(np.mean(y * y))
+        out[i] = (float(np.max(np.abs(g - y)) / rms), float(np.sqrt(np.mean((g - y) ** 2)) / rms))
+    return out
+
+
+def _check(cfg, got, want, tol=TOL, label=""):
+    errs = _errs(got, want)
+    worst = max(e[0] for e in errs.values())
+    print(f"{label} worst max|err|/rms {worst:.4e}; sigma max {max(e[1] for e in errs.values()):.4e}", flush=True)
+    bad = {cfg["heads"][i]["name"]: e for i, e in errs.items() if not e[0] <= tol}
+    assert not bad, bad
+
+
+# ------------------------------------------------------------------ tiny config
+
+@pytest.fixture(scope="module")
+def tiny():
+    cfg = synth.config("tiny")
+    return cfg, synth.make_weights(cfg)
+
+
+def test_tiny_parity(tiny):
+    cfg, w = tiny
+    x = synth.make_input(cfg)
+    proj = kva.Projector(cfg, w, max_tokens=64)
+    _check(cfg, _run(proj, x), oracle.project(cfg, w, x), label="tiny")
+    proj.close()
+
+
+def test_tiny_trunk_state_matches_oracle(tiny):
+    cfg, w = tiny
+    x = synth.make_input(cfg)
+    proj = kva.Projector(cfg, w, max_tokens=64)
+    _run(proj, x)
+    z = proj.copy_z(64).cpu().numpy().view(np.uint16)
+    zg = ref.bf16_bits_to_f64(z)
+    zr = ref.trunk(cfg, ref.prepare(cfg, w), x)
+    err = np.max(np.abs(zg - zr)) / np.sqrt(np.mean(zr ** 2))
+    print("tiny z max|err|/rms", err)
+    assert err < 2e-2
+    proj.close()
+
+
+@pytest.mark.parametrize("n", [1, 63, 65, 200])
+def test_tiny_ragged_blocks(tiny, n):
+    cfg, w = tiny
+    cfg = dict(cfg, attn_block=64)
+    x = synth.make_input(cfg, n_tokens=n, seed=11)
+    proj = kva.Projector(cfg, w, max_tokens=256)
+    _check(cfg, _run(proj, x), oracle.project(cfg, w, x), label=f"tiny n={n}")
+    proj.close()
+
+
+def test_tiny_bad_arguments(tiny):
+    cfg, w = tiny
+    proj = kva.Projector(cfg, w, max_tokens=64)
+    x = torch.zeros((65, cfg["n_in"]), device="cuda")
+    with pytest.raises(kva.KvaError):
+        proj.project(x, outs=proj.alloc_outputs(65))
+    with pytest.raises(kva.KvaError):
+        kva.kva_project_ubatch(proj.ctx, x.data_ptr(), 0, [o.data_ptr() for o in proj.alloc_outputs(1)])
+    proj.close()
+
+
+# ------------------------------------------------------------------ r2, one 1024-token ubatch
+
+@pytest.fixture(scope="module")
+def r2():
+    cfg = synth.config("r2")
+    w = synth.make_weights(cfg)
+    prep = ref.prepare(cfg, w)
+    return cfg, w, prep
+
+
+def test_r2_full_ubatch_parity(r2):
+    cfg, w, prep = r2
+    x = synth.make_input(cfg)
+    proj = kva.Projector(cfg, w, max_tokens=1536)
+    got = _run(proj, x)
+    want = ref.project(cfg, prep, x)
+    _check(cfg, got, want, label="r2 1024")
+    # determinism: a second call is bitwise identical
+    got2 = _run(proj, x)
+    assert all(np.array_equal(a, b) for a, b in zip(got, got2))
+    proj.close()
+
+
+def test_r2_partial_last_ubatch(r2):
+    cfg, w, prep = r2
+    x = synth.make_input(cfg, n_tokens=1536, seed=21)
+    proj = kva.Projector(cfg, w, max_tokens=1536)
+    got = _run(proj, x)
+    heads = [0, 3, 31]
+    want = ref.project(cfg, prep, x[1024:], which=heads)
+    _check(cfg, {i: got[i][1024:] for i in heads}, want, label="r2 tail 512")
+    first = _run(proj, np.ascontiguousarray(x[:1024]))
+    assert all(np.array_equal(got[i][:1024], first[i]) for i in range(len(got)))
+    proj.close()
+
+
+# ------------------------------------------------------------------ r3: blocks, causality
+
+@pytest.fixture(scope="module")
+def r3():
+    cfg = synth.config("r3")
+    return cfg, synth.make_weights(cfg)
+
+
+def test_r3_blocks_are_independent_and_causal(r3):
+    cfg, w = r3
+    x = synth.make_input(cfg, n_tokens=2048)
+    proj = kva.Projector(cfg, w, max_tokens=2048)
+    both = _run(proj, x)
+    b0 = _run(proj, np.ascontiguousarray(x[:1024]))
+    b1 = _run(proj, np.ascontiguousarray(x[1024:]))
+    for i in range(len(both)):
+        assert np.array_equal(both[i][:1024], b0[i]), i
+        assert np.array_equal(both[i][1024:], b1[i]), i
+    j = 1500
+    x2 = x.copy()
+    x2[j] *= np.float32(-1.5)
+    pert = _run(proj, x2)
+    for i in range(len(both)):
+        assert np.array_equal(both[i][:j], pert[i][:j]), i
+        assert not np.array_equal(both[i][j], pert[i][j]), i
+    proj.close()
+
+
+def test_r3_parity_sampled_heads(r3):
+    cfg, w = r3
+    x = synth.make_input(cfg, n_tokens=1024)
+    proj = kva.Projector(cfg, w, max_tokens=1024)
+    got = _run(proj, x)
+    heads = [0, 3, 32, 35]          # DeltaNet, attention, drafter res.34, kva.final
+    want = ref.project(cfg, ref.prepare(cfg, w), x, which=heads)
+    _check(cfg, got, want, label="r3 sampled heads")
+    proj.close()
+
+
+# ------------------------------------------------------------------ hooks and the KV-cache write
+
+def test_dequant_q8_0_bit_exact():
+    rng = np.random.default_rng(9)
+    nb = 4096
+    codes = rng.integers(-128, 128, size=(1, nb * 32), dtype=np.int8)
+    sc_bits = rng.integers(0, 0x7C00, size=nb).astype(np.uint16)          # every finite magnitude
+    sc_bits |= (rng.integers(0, 2, size=nb).astype(np.uint16) << 15)       # both signs
+    sc_bits[:64] = np.arange(64, dtype=np.uint16)                           # subnormals and +0
+    packed = synth.pack_q8_0(codes, sc_bits.view(np.float16).reshape(1, nb))
+    want = ref.dequant_q8_0(packed, 1, nb * 32).astype(np.float32).reshape(-1)
+    blocks = torch.from_numpy(packed.reshape(-1)).cuda()
+    out = torch.empty(nb * 32, dtype=torch.float32, device="cuda")
+    kva.kva_debug_dequant_q8_0(blocks.data_ptr(), nb, out.data_ptr(), kva.current_stream())
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+def _kv_cache(n_logical, n_pages):
+    kp = torch.full((n_pages, 256, 4, 256), -1, dtype=torch.int16, device="cuda")
+    vp = torch.full((n_pages, 256, 4, 256), -1, dtype=torch.int16, device="cuda")
+    return kp, vp
+
+
+@pytest.mark.parametrize("pos0,n", [(0, 600), (65536 - 700, 700)])
+def test_kv_write_within_one_bf16_ulp(pos0, n):
+    n_logical = (pos0 + n + 255) // 256
+    gains, ptab, n_pages = synth.make_kv_write_inputs(pos0 + n, n_layers=1)
+    kv = synth.make_kv_rows(n, scale=3.0)
+    kp, vp = _kv_cache(n_logical, n_pages)
+    ptab_d = torch.from_numpy(ptab).cuda()
+    cache = kva.kva_paged_kv(kp.data_ptr(), vp.data_ptr(), ptab_d.data_ptr(), 256, n_pages, len(ptab),
+                             4, 256, 64, 1.0e7, 1e-6)
+    kv_d = torch.from_numpy(kv).cuda()
+    g_d = torch.from_numpy(gains[0]).cuda()
+    kva.kva_attn_kv_write(kv_d.data_ptr(), kv.shape[1], n, pos0, g_d.data_ptr(), cache, kva.current_stream())
+    torch.cuda.synchronize()
+    kpn = kp.cpu().numpy().view(np.uint16)
+    vpn = vp.cpu().numpy().view(np.uint16)
+    k, v = ref.kv_write_values(kv, gains[0], pos0)
+    pos = pos0 + np.arange(n)
+    gk = kpn[ptab[pos // 256], pos % 256]
+    gv = vpn[ptab[pos // 256], pos % 256]
+    assert np.array_equal(gv, ref.f64_to_bf16_bits(v))            # V: a single rounding of fp32 data
+    # K: one bf16 ulp of the correctly rounded value, plus the fp32 rotation's
+    # absolute error (angle, sin/cos and products, relative to the rotary pair's
+    # norm): where a rotated value nearly cancels, that exceeds its own bf16 ulp.
+    dk = np.abs(ref.bf16_bits_to_f64(gk) - ref.bf16_bits_to_f64(ref.f64_to_bf16_bits(k)))
+    ulp = np.ldexp(1.0, np.frexp(np.abs(k))[1] - 8)
+    pair = np.zeros_like(k)
+    pn = np.sqrt(k[..., :32] ** 2 + k[..., 32:64] ** 2)
+    pair[..., :32], pair[..., 32:64] = pn, pn
+    bound = ulp + 2.0 ** -20 * pair
+    assert np.all(dk <= bound), float(np.max(dk / bound))
+    assert np.mean(dk == 0) > 0.98
+    # slots outside the written range keep the poison
+    used = np.zeros((n_pages, 256), dtype=bool)
+    used[ptab[pos // 256], pos % 256] = True
+    assert np.all(kpn[~used] == 0xFFFF) and np.all(vpn[~used] == 0xFFFF)
