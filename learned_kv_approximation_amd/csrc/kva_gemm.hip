@@ -7,10 +7,10 @@
 // operand layout of the 32x32x16 MFMA: each lane feeds 8 consecutive
 // K-values of one row of A and 8 consecutive K-values of one row of W.
 //
-// Structure (one workgroup = 4 waves in a 2x2 grid, one BM x BN tile):
-//  - K is walked in slabs of 64.  Each thread fetches 16-byte chunks of the
-//    next slab from global memory into registers while the waves run MFMAs
-//    on the current slab from LDS (double-buffered LDS, one barrier a slab).
+// Structure (one workgroup = a grid of waves, one BM x BN tile):
+//  - K is walked in slabs of 64.  The next slab is copied from global memory
+//    straight into the second LDS buffer (global_load_lds) while the waves run
+//    MFMAs on the current one (one barrier a slab).
 //  - LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk
 //    c ^ swz(r), so the 16 rows one ds_read_b128 phase touches land on
 //    distinct banks.
@@ -31,7 +31,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BK = 64;          // K per slab (16-bit elements): 128-byte LDS rows
-constexpr int kThreads = 256;
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
@@ -51,14 +50,27 @@ __device__ __forceinline__ uint16_t to_f16_bits(float v) {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* gbl_ptr_t;
+
 // Output element (lane, r) of a 32x32 MFMA tile sits at
 //   row = 8*(r/4) + 4*(lane/32) + r%4,  col = lane%32.
-template <int BM, int BN, bool BF16, int EPI>
-__global__ void __launch_bounds__(kThreads) gemm_nt(GemmArgs g) {
-    constexpr int WM = BM / 2, WN = BN / 2;
+//
+// A BM x BN tile is computed by WGM x WGN waves, each owning a
+// (BM/WGM) x (BN/WGN) sub-tile.  Slabs of 64 K-values are copied from global
+// memory straight into LDS (global_load_lds, 16 bytes per lane; one wave
+// instruction fills 8 consecutive 128-byte rows): no register staging, no
+// ds_write.  Lane L of such an instruction lands at row L/8, physical chunk
+// L%8, so it fetches the logical chunk (L%8) ^ swz(row) of that row.
+template <int BM, int BN, int WGM, int WGN, bool BF16, int EPI>
+__global__ void __launch_bounds__(64 * WGM * WGN) gemm_nt(GemmArgs g) {
+    constexpr int NW = WGM * WGN;
+    constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int MI = WM / 32, NI = WN / 32;
-    constexpr int AP = BM / 32, BP = BN / 32;   // 16-byte chunks per thread per slab
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * BK];
+    constexpr int AI = BM / (8 * NW), BI = BN / (8 * NW);   // wave load instructions per slab
+    static_assert(AI >= 1 && BI >= 1 && MI >= 1 && NI >= 1, "tile too small for the wave grid");
+    constexpr int STAGE = (BM + BN) * BK;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE];
 
     const int mt = (g.M + BM - 1) / BM;
     const int nt = g.N / BN;
@@ -68,34 +80,38 @@ __global__ void __launch_bounds__(kThreads) gemm_nt(GemmArgs g) {
     if (v >= total) return;
     const int tm = v % mt, tn = v / mt;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int lrow = tid >> 3, lch = tid & 7;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WGN, wn = wave % WGN;
 
-    const uint16_t* pa = g.A + (int64_t)(tm * BM + lrow) * g.lda + lch * 8;
-    const uint16_t* pb = g.B + (int64_t)(tn * BN + lrow) * g.ldb + lch * 8;
-    const int64_t stepa = 32 * g.lda, stepb = 32 * g.ldb;
-
-    u32x4 ra[AP], rb[BP];
-    auto gload = [&](int kt) {
+    // rows >= M of A are padding rows of the activation scratch: loaded, never stored
+    const uint16_t* Ab = g.A + (int64_t)tm * BM * g.lda;
+    const uint16_t* Bb = g.B + (int64_t)tn * BN * g.ldb;
+    int offa[AI], offb[BI];
+    {
+        const int rr = lane >> 3, pc = lane & 7;
 #pragma unroll
-        for (int p = 0; p < AP; ++p) ra[p] = *(const u32x4*)(pa + p * stepa + kt * BK);
-#pragma unroll
-        for (int p = 0; p < BP; ++p) rb[p] = *(const u32x4*)(pb + p * stepb + kt * BK);
-    };
-    auto sstore = [&](int buf) {
-        uint16_t* sa = smem + buf * BM * BK;
-        uint16_t* sb = smem + 2 * BM * BK + buf * BN * BK;
-#pragma unroll
-        for (int p = 0; p < AP; ++p) {
-            const int r = p * 32 + lrow;
-            *(u32x4*)(sa + r * BK + ((lch ^ swz(r)) << 3)) = ra[p];
+        for (int i = 0; i < AI; ++i) {
+            const int row = (i * NW + wave) * 8 + rr;
+            offa[i] = row * (int)g.lda + ((pc ^ swz(row)) << 3);
         }
 #pragma unroll
-        for (int p = 0; p < BP; ++p) {
-            const int r = p * 32 + lrow;
-            *(u32x4*)(sb + r * BK + ((lch ^ swz(r)) << 3)) = rb[p];
+        for (int i = 0; i < BI; ++i) {
+            const int row = (i * NW + wave) * 8 + rr;
+            offb[i] = row * (int)g.ldb + ((pc ^ swz(row)) << 3);
         }
+    }
+    auto issue = [&](int kt, int buf) {
+        uint16_t* sa = smem + buf * STAGE;
+        uint16_t* sb = sa + BM * BK;
+#pragma unroll
+        for (int i = 0; i < AI; ++i)
+            __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Ab + offa[i] + kt * BK),
+                                             (lds_ptr_t)(sa + (i * NW + wave) * 8 * BK), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < BI; ++i)
+            __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Bb + offb[i] + kt * BK),
+                                             (lds_ptr_t)(sb + (i * NW + wave) * 8 * BK), 16, 0, 0);
     };
 
     f32x16 acc[MI][NI];
@@ -107,15 +123,18 @@ __global__ void __launch_bounds__(kThreads) gemm_nt(GemmArgs g) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     const int nk = g.K / BK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
     const int frow = lane & 31, fk = lane >> 5;
+    issue(0, 0);
+    // global_load_lds completes through vmcnt: wait for it explicitly, then
+    // the barrier publishes the slab to every wave
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
-        const uint16_t* sa = smem + buf * BM * BK;
-        const uint16_t* sb = smem + 2 * BM * BK + buf * BN * BK;
+        // the other buffer was last read before the previous barrier: refill it
+        if (kt + 1 < nk) issue(kt + 1, buf ^ 1);
+        const uint16_t* sa = smem + buf * STAGE;
+        const uint16_t* sb = sa + BM * BK;
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
             const int c = ks * 2 + fk;
@@ -135,8 +154,8 @@ __global__ void __launch_bounds__(kThreads) gemm_nt(GemmArgs g) {
 #pragma unroll
                 for (int j = 0; j < NI; ++j) acc[i][j] = mfma32<BF16>(af[i], bfr[j], acc[i][j]);
         }
-        if (kt + 1 < nk) sstore(buf ^ 1);
-        __syncthreads();
+        __builtin_amdgcn_s_waitcnt(0);   // the next slab has landed
+        __syncthreads();                 // ... for all waves, and all are done with this one
     }
 
     // ------------------------------------------------------------ epilogue
@@ -239,13 +258,14 @@ __global__ void __launch_bounds__(kThreads) gemm_nt(GemmArgs g) {
     }
 }
 
-template <int BM, int BN, bool BF16, int EPI>
+template <int BM, int BN, int WGM, int WGN, bool BF16, int EPI>
 hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
+    if (a.N % BN) return hipErrorInvalidValue;
     const int mt = (a.M + BM - 1) / BM;
     const int nt = a.N / BN;
     const int total = mt * nt;
     const int grid = (total + 7) / 8 * 8;
-    hipLaunchKernelGGL((gemm_nt<BM, BN, BF16, EPI>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((gemm_nt<BM, BN, WGM, WGN, BF16, EPI>), dim3(grid), dim3(64 * WGM * WGN), 0, s, a);
     return hipGetLastError();
 }
 
@@ -254,18 +274,22 @@ hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
 hipError_t launch_gemm(GemmOperand opd, GemmTile tile, EpiKind epi, const GemmArgs& a,
                        hipStream_t s) {
     if (a.M <= 0) return hipSuccess;
-    if (a.K % BK != 0) return hipErrorInvalidValue;
-    if (opd == OPD_BF16 && tile == TILE_256x256 && epi == EPI_HEADS) {
-        if (a.N % 256) return hipErrorInvalidValue;
-        return launch_one<256, 256, true, EPI_HEADS>(a, s);
-    }
+    if (a.K % BK != 0 || a.K <= 0) return hipErrorInvalidValue;
+    if (opd == OPD_BF16 && tile == TILE_256x256 && epi == EPI_HEADS)
+        return launch_one<256, 256, 2, 4, true, EPI_HEADS>(a, s);
     if (opd == OPD_F16 && tile == TILE_128x128) {
-        if (a.N % 128) return hipErrorInvalidValue;
         switch (epi) {
-            case EPI_STORE_F32: return launch_one<128, 128, false, EPI_STORE_F32>(a, s);
-            case EPI_ADD_F32: return launch_one<128, 128, false, EPI_ADD_F32>(a, s);
-            case EPI_QKV: return launch_one<128, 128, false, EPI_QKV>(a, s);
-            case EPI_SWIGLU: return launch_one<128, 128, false, EPI_SWIGLU>(a, s);
+            case EPI_STORE_F32: return launch_one<128, 128, 2, 2, false, EPI_STORE_F32>(a, s);
+            case EPI_ADD_F32: return launch_one<128, 128, 2, 2, false, EPI_ADD_F32>(a, s);
+            case EPI_QKV: return launch_one<128, 128, 2, 2, false, EPI_QKV>(a, s);
+            case EPI_SWIGLU: return launch_one<128, 128, 2, 2, false, EPI_SWIGLU>(a, s);
+            default: break;
+        }
+    }
+    if (opd == OPD_F16 && tile == TILE_128x64) {
+        switch (epi) {
+            case EPI_STORE_F32: return launch_one<128, 64, 2, 2, false, EPI_STORE_F32>(a, s);
+            case EPI_ADD_F32: return launch_one<128, 64, 2, 2, false, EPI_ADD_F32>(a, s);
             default: break;
         }
     }

@@ -62,7 +62,8 @@ struct GemmArgs {
 };
 
 enum GemmOperand : int { OPD_F16 = 0, OPD_BF16 = 1 };
-enum GemmTile : int { TILE_256x256 = 0, TILE_128x128 = 1 };
+// 256x256: 8 waves (2 per SIMD); 128x128 and 128x64: 4 waves.
+enum GemmTile : int { TILE_256x256 = 0, TILE_128x128 = 1, TILE_128x64 = 2 };
 
 hipError_t launch_gemm(GemmOperand opd, GemmTile tile, EpiKind epi, const GemmArgs& args,
                        hipStream_t stream);

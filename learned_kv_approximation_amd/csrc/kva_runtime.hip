@@ -486,7 +486,7 @@ kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n, float* co
         g.A = ctx->u16; g.lda = n_in; g.B = ctx->w_in; g.ldb = n_in;
         g.M = n; g.N = (int32_t)round_up(d, kColPad); g.K = (int32_t)n_in;
         g.epi.out_f32 = ctx->h; g.epi.ld_f32 = d; g.epi.n_real = (int32_t)d;
-        STAGE(KVA_STAGE_GEMM_IN, launch_gemm(OPD_F16, TILE_128x128, EPI_STORE_F32, g, s));
+        STAGE(KVA_STAGE_GEMM_IN, launch_gemm(OPD_F16, TILE_128x64, EPI_STORE_F32, g, s));
     }
     for (int b = 0; b < c.n_blocks; ++b) {
         const kva_ctx::Blk& B = ctx->blk[b];
@@ -507,7 +507,7 @@ kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n, float* co
             g.A = ctx->o16; g.lda = hd; g.B = B.wo; g.ldb = hd;
             g.M = n; g.N = (int32_t)round_up(d, kColPad); g.K = (int32_t)hd;
             g.epi.out_f32 = ctx->h; g.epi.ld_f32 = d; g.epi.n_real = (int32_t)d;
-            STAGE(KVA_STAGE_GEMM_O, launch_gemm(OPD_F16, TILE_128x128, EPI_ADD_F32, g, s));
+            STAGE(KVA_STAGE_GEMM_O, launch_gemm(OPD_F16, TILE_128x64, EPI_ADD_F32, g, s));
         }
         STAGE(KVA_STAGE_NORM, launch_rmsnorm_cast(ctx->h, d, B.g_ffn, n, (int32_t)d, c.eps, ctx->a16, d, false, s));
         {
@@ -522,7 +522,7 @@ kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n, float* co
             g.A = ctx->act16; g.lda = F; g.B = B.wd; g.ldb = F;
             g.M = n; g.N = (int32_t)round_up(d, kColPad); g.K = (int32_t)F;
             g.epi.out_f32 = ctx->h; g.epi.ld_f32 = d; g.epi.n_real = (int32_t)d;
-            STAGE(KVA_STAGE_GEMM_DOWN, launch_gemm(OPD_F16, TILE_128x128, EPI_ADD_F32, g, s));
+            STAGE(KVA_STAGE_GEMM_DOWN, launch_gemm(OPD_F16, TILE_128x64, EPI_ADD_F32, g, s));
         }
     }
     STAGE(KVA_STAGE_NORM, launch_rmsnorm_cast(ctx->h, d, ctx->g_out, n, (int32_t)d, c.eps, ctx->z16, d, true, s));
