@@ -137,9 +137,12 @@ kva_status kva_validate_config(const kva_config* cfg);
 
 /* Creates a projector on HIP device `device`: validates `cfg`, allocates the
  * weight arena and scratch for cfg->max_tokens tokens, converts and uploads
- * the weights.  Trunk weights are converted to fp16 for the MFMA path
- * (KVA_ERR_RANGE if a weight is outside fp16's finite range); head weights
- * are kept as bf16 (fp32 weights are rounded to nearest even).  The call is
+ * the weights.  fp32/bf16 weights: trunk weights are converted to fp16 for
+ * the MFMA path (KVA_ERR_RANGE if a weight is outside fp16's finite range),
+ * head weights are kept as bf16 (fp32 ones rounded to nearest even).  q8_0
+ * weights are split losslessly into an int8 code plane and an fp16 scale
+ * plane; the GEMMs form each weight d*q on the fly (see
+ * kva_debug_dequant_q8_0) and run fp16 MFMA throughout.  The call is
  * synchronous.  On success *out owns all device memory it allocated; on
  * failure *out is NULL and nothing is leaked. */
 kva_status kva_create(const kva_config* cfg, const kva_weights* w, int device, kva_ctx** out);
@@ -200,12 +203,14 @@ kva_status kva_attn_kv_write(const float* kv, int64_t ld_kv, int32_t n_tokens, i
 
 /* Test hook: dequantises n_blocks q8_0 blocks (device, 34 bytes each) to
  * fp32 (device, 32*n_blocks values) with the same device routine the q8_0
- * GEMM uses: out = float(d) * q, exact, fp16 subnormal scales honoured. */
+ * GEMM uses: out = float(d) * q, exact, fp16 subnormal scales honoured.
+ * (The GEMM then rounds that value once to fp16 for the MFMA.) */
 kva_status kva_debug_dequant_q8_0(const void* blocks, int64_t n_blocks, float* out, void* stream);
 
 /* Test hook: copies the final-normed trunk state z of the most recent
- * kva_project_ubatch call ([n_tokens][d_model] bf16 bit patterns, the head
- * GEMM's A operand) to device buffer `dst`.  Asynchronous on `stream`. */
+ * kva_project_ubatch call ([n_tokens][d_model] 16-bit patterns, the head
+ * GEMM's A operand: bf16, or fp16 for q8_0 weights) to device buffer `dst`.
+ * Asynchronous on `stream`. */
 kva_status kva_debug_copy_z(kva_ctx* ctx, uint16_t* dst, int32_t n_tokens, void* stream);
 
 /* Test hook (host only, no device): the packed column order of the head

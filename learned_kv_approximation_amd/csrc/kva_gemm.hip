@@ -62,13 +62,16 @@ typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 // instruction fills 8 consecutive 128-byte rows): no register staging, no
 // ds_write.  Lane L of such an instruction lands at row L/8, physical chunk
 // L%8, so it fetches the logical chunk (L%8) ^ swz(row) of that row.
-template <int BM, int BN, int WGM, int WGN, bool BF16, int EPI>
+template <int BM, int BN, int WGM, int WGN, int OPD, int EPI>
 __global__ void __launch_bounds__(64 * WGM * WGN) gemm_nt(GemmArgs g) {
+    constexpr bool BF16 = OPD == OPD_BF16;
+    constexpr bool Q8 = OPD == OPD_Q8;
     constexpr int NW = WGM * WGN;
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int MI = WM / 32, NI = WN / 32;
-    constexpr int AI = BM / (8 * NW), BI = BN / (8 * NW);   // wave load instructions per slab
-    static_assert(AI >= 1 && BI >= 1 && MI >= 1 && NI >= 1, "tile too small for the wave grid");
+    constexpr int AI = BM / (8 * NW), BI = Q8 ? 0 : BN / (8 * NW);   // wave DMA instructions per slab
+    static_assert(AI >= 1 && (Q8 || BI >= 1) && MI >= 1 && NI >= 1, "tile too small for the wave grid");
+    static_assert(!Q8 || 64 * NW == 2 * BN, "q8_0 weights: two threads per weight row");
     constexpr int STAGE = (BM + BN) * BK;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE];
 
@@ -87,7 +90,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_nt(GemmArgs g) {
     // rows >= M of A are padding rows of the activation scratch: loaded, never stored
     const uint16_t* Ab = g.A + (int64_t)tm * BM * g.lda;
     const uint16_t* Bb = g.B + (int64_t)tn * BN * g.ldb;
-    int offa[AI], offb[BI];
+    int offa[AI], offb[BI > 0 ? BI : 1];
     {
         const int rr = lane >> 3, pc = lane & 7;
 #pragma unroll
@@ -114,6 +117,44 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_nt(GemmArgs g) {
                                              (lds_ptr_t)(sb + (i * NW + wave) * 8 * BK), 16, 0, 0);
     };
 
+    // q8_0 weights: thread t owns one 32-code block of weight row t/2 per slab
+    // (half t%2 of the slab's 64 K-values): codes and scale go through
+    // registers, d*q is rounded once to fp16 and written to LDS.
+    const int qrow = tid >> 1, qhalf = tid & 1;
+    const int kblocks = g.K / 32;
+    const int8_t* Bq = Q8 ? g.Bq + ((int64_t)tn * BN + qrow) * g.ldb + qhalf * 32 : nullptr;
+    const uint16_t* Bs = Q8 ? g.Bs + ((int64_t)tn * BN + qrow) * kblocks + qhalf : nullptr;
+    u32x4 qr0, qr1;
+    uint16_t qd = 0;
+    auto qload = [&](int kt) {
+        if constexpr (Q8) {
+            qr0 = *(const u32x4*)(Bq + kt * BK);
+            qr1 = *(const u32x4*)(Bq + kt * BK + 16);
+            qd = Bs[kt * 2];
+        }
+    };
+    auto qstore = [&](int buf) {
+        if constexpr (Q8) {
+            uint16_t* sb = smem + buf * STAGE + BM * BK + qrow * BK;
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) {
+                const u32x4& src = c4 < 2 ? qr0 : qr1;
+                const uint32_t w0 = src[(c4 & 1) * 2], w1 = src[(c4 & 1) * 2 + 1];
+                u32x4 o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t w = e < 2 ? w0 : w1;
+                    const int q0 = (int)(int8_t)(w >> (16 * (e & 1)));
+                    const int q1 = (int)(int8_t)(w >> (16 * (e & 1) + 8));
+                    o[e] = (uint32_t)to_f16_bits(q8_0_value(qd, q0)) |
+                           ((uint32_t)to_f16_bits(q8_0_value(qd, q1)) << 16);
+                }
+                const int c = qhalf * 4 + c4;
+                *(u32x4*)(sb + ((c ^ swz(qrow)) << 3)) = o;
+            }
+        }
+    };
+
     f32x16 acc[MI][NI];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -124,7 +165,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_nt(GemmArgs g) {
 
     const int nk = g.K / BK;
     const int frow = lane & 31, fk = lane >> 5;
+    qload(0);
     issue(0, 0);
+    qstore(0);
     // global_load_lds completes through vmcnt: wait for it explicitly, then
     // the barrier publishes the slab to every wave
     __builtin_amdgcn_s_waitcnt(0);
@@ -132,7 +175,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_nt(GemmArgs g) {
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
         // the other buffer was last read before the previous barrier: refill it
-        if (kt + 1 < nk) issue(kt + 1, buf ^ 1);
+        if (kt + 1 < nk) {
+            qload(kt + 1);
+            issue(kt + 1, buf ^ 1);
+        }
         const uint16_t* sa = smem + buf * STAGE;
         const uint16_t* sb = sa + BM * BK;
 #pragma unroll
@@ -154,6 +200,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_nt(GemmArgs g) {
 #pragma unroll
                 for (int j = 0; j < NI; ++j) acc[i][j] = mfma32<BF16>(af[i], bfr[j], acc[i][j]);
         }
+        if (kt + 1 < nk) qstore(buf ^ 1);
         __builtin_amdgcn_s_waitcnt(0);   // the next slab has landed
         __syncthreads();                 // ... for all waves, and all are done with this one
     }
@@ -258,14 +305,14 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_nt(GemmArgs g) {
     }
 }
 
-template <int BM, int BN, int WGM, int WGN, bool BF16, int EPI>
+template <int BM, int BN, int WGM, int WGN, int OPD, int EPI>
 hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
     if (a.N % BN) return hipErrorInvalidValue;
     const int mt = (a.M + BM - 1) / BM;
     const int nt = a.N / BN;
     const int total = mt * nt;
     const int grid = (total + 7) / 8 * 8;
-    hipLaunchKernelGGL((gemm_nt<BM, BN, WGM, WGN, BF16, EPI>), dim3(grid), dim3(64 * WGM * WGN), 0, s, a);
+    hipLaunchKernelGGL((gemm_nt<BM, BN, WGM, WGN, OPD, EPI>), dim3(grid), dim3(64 * WGM * WGN), 0, s, a);
     return hipGetLastError();
 }
 
@@ -275,21 +322,33 @@ hipError_t launch_gemm(GemmOperand opd, GemmTile tile, EpiKind epi, const GemmAr
                        hipStream_t s) {
     if (a.M <= 0) return hipSuccess;
     if (a.K % BK != 0 || a.K <= 0) return hipErrorInvalidValue;
-    if (opd == OPD_BF16 && tile == TILE_256x256 && epi == EPI_HEADS)
-        return launch_one<256, 256, 2, 4, true, EPI_HEADS>(a, s);
+    if (opd == OPD_Q8 && (!a.Bq || !a.Bs)) return hipErrorInvalidValue;
+    if (tile == TILE_256x256 && epi == EPI_HEADS) {
+        if (opd == OPD_BF16) return launch_one<256, 256, 2, 4, OPD_BF16, EPI_HEADS>(a, s);
+        if (opd == OPD_Q8) return launch_one<256, 256, 2, 4, OPD_Q8, EPI_HEADS>(a, s);
+    }
     if (opd == OPD_F16 && tile == TILE_128x128) {
         switch (epi) {
-            case EPI_STORE_F32: return launch_one<128, 128, 2, 2, false, EPI_STORE_F32>(a, s);
-            case EPI_ADD_F32: return launch_one<128, 128, 2, 2, false, EPI_ADD_F32>(a, s);
-            case EPI_QKV: return launch_one<128, 128, 2, 2, false, EPI_QKV>(a, s);
-            case EPI_SWIGLU: return launch_one<128, 128, 2, 2, false, EPI_SWIGLU>(a, s);
+            case EPI_STORE_F32: return launch_one<128, 128, 2, 2, OPD_F16, EPI_STORE_F32>(a, s);
+            case EPI_ADD_F32: return launch_one<128, 128, 2, 2, OPD_F16, EPI_ADD_F32>(a, s);
+            case EPI_QKV: return launch_one<128, 128, 2, 2, OPD_F16, EPI_QKV>(a, s);
+            case EPI_SWIGLU: return launch_one<128, 128, 2, 2, OPD_F16, EPI_SWIGLU>(a, s);
+            default: break;
+        }
+    }
+    if (opd == OPD_Q8 && tile == TILE_128x128) {
+        switch (epi) {
+            case EPI_STORE_F32: return launch_one<128, 128, 2, 2, OPD_Q8, EPI_STORE_F32>(a, s);
+            case EPI_ADD_F32: return launch_one<128, 128, 2, 2, OPD_Q8, EPI_ADD_F32>(a, s);
+            case EPI_QKV: return launch_one<128, 128, 2, 2, OPD_Q8, EPI_QKV>(a, s);
+            case EPI_SWIGLU: return launch_one<128, 128, 2, 2, OPD_Q8, EPI_SWIGLU>(a, s);
             default: break;
         }
     }
     if (opd == OPD_F16 && tile == TILE_128x64) {
         switch (epi) {
-            case EPI_STORE_F32: return launch_one<128, 64, 2, 2, false, EPI_STORE_F32>(a, s);
-            case EPI_ADD_F32: return launch_one<128, 64, 2, 2, false, EPI_ADD_F32>(a, s);
+            case EPI_STORE_F32: return launch_one<128, 64, 2, 2, OPD_F16, EPI_STORE_F32>(a, s);
+            case EPI_ADD_F32: return launch_one<128, 64, 2, 2, OPD_F16, EPI_ADD_F32>(a, s);
             default: break;
         }
     }

@@ -50,18 +50,31 @@ struct EpiArgs {
 };
 
 // C[M][N] = A[M][K] * B[N][K]^T with 16-bit operands and fp32 accumulation.
+// For OPD_Q8 the weight comes as int8 codes Bq[N][ldb] and one fp16 scale per
+// 32 codes, Bs[N][K/32]; the weight is d * q (see q8_0_value).
 struct GemmArgs {
     const uint16_t* A = nullptr;
     int64_t lda = 0;
     const uint16_t* B = nullptr;
     int64_t ldb = 0;
+    const int8_t* Bq = nullptr;
+    const uint16_t* Bs = nullptr;
     int32_t M = 0;       // rows of A that are real (stores are masked to M)
     int32_t N = 0;       // columns, a multiple of the tile width (weights are padded)
     int32_t K = 0;       // multiple of 64
     EpiArgs epi;
 };
 
-enum GemmOperand : int { OPD_F16 = 0, OPD_BF16 = 1 };
+// OPD_F16 / OPD_BF16: both operands 16-bit.  OPD_Q8: A fp16, B q8_0 planes,
+// fp16 MFMA on the weights d*q rounded once to fp16.
+enum GemmOperand : int { OPD_F16 = 0, OPD_BF16 = 1, OPD_Q8 = 2 };
+
+// One q8_0 weight: the fp16 block scale (bit pattern d_bits) times the int8
+// code, exactly (an 11-bit significand times an 8-bit integer fits fp32's 24
+// bits; fp16 subnormal scales convert exactly to fp32).
+__device__ __forceinline__ float q8_0_value(uint16_t d_bits, int q) {
+    return (float)__builtin_bit_cast(_Float16, d_bits) * (float)q;
+}
 // 256x256: 8 waves (2 per SIMD); 128x128 and 128x64: 4 waves.
 enum GemmTile : int { TILE_256x256 = 0, TILE_128x128 = 1, TILE_128x64 = 2 };
 

@@ -107,12 +107,6 @@ __global__ void __launch_bounds__(256) kv_write_kernel(KvWriteArgs a) {
     *(ushort4*)(a.v_pool + base) = vo;
 }
 
-// q8_0 block -> 32 fp32 weights, d * q exactly (the fp16 scale converts
-// exactly to fp32, subnormals included; the product has <= 19 significant bits).
-__device__ __forceinline__ float q8_0_value(uint16_t d_bits, int8_t q) {
-    return (float)__builtin_bit_cast(_Float16, d_bits) * (float)q;
-}
-
 __global__ void dequant_q8_0_kernel(const uint8_t* __restrict__ blocks, int64_t n_blocks,
                                     float* __restrict__ out) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // one value per thread
@@ -120,7 +114,7 @@ __global__ void dequant_q8_0_kernel(const uint8_t* __restrict__ blocks, int64_t 
     const int64_t b = i >> 5;
     const uint8_t* blk = blocks + b * 34;
     const uint16_t d = (uint16_t)blk[0] | ((uint16_t)blk[1] << 8);
-    out[i] = q8_0_value(d, (int8_t)blk[2 + (i & 31)]);
+    out[i] = q8_0_value(d, (int)(int8_t)blk[2 + (i & 31)]);   // shared with the q8_0 GEMM
 }
 
 }  // namespace

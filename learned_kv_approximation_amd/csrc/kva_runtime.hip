@@ -36,6 +36,12 @@ kva_status fail(kva_status s, const char* fmt, ...) {
                         #expr, hipGetErrorString(e_), __FILE__, __LINE__);              \
     } while (0)
 
+#define KVA_TRY(expr)                    \
+    do {                                 \
+        kva_status s_ = (expr);          \
+        if (s_ != KVA_OK) return s_;     \
+    } while (0)
+
 int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
 // ------------------------------------------------------------------ host number formats
@@ -150,20 +156,27 @@ struct kva_ctx {
     std::vector<void*> allocs;
     uint64_t weight_bytes = 0, scratch_bytes = 0;
 
-    // weights (device)
-    uint16_t* w_in = nullptr;
+    // weights (device).  A weight is either 16-bit values w16[rows][K] (fp16
+    // trunk, bf16 heads) or, for q8_0, codes q[rows][K] + fp16 scales sc[rows][K/32].
+    struct DevW {
+        uint16_t* w16 = nullptr;
+        int8_t* q = nullptr;
+        uint16_t* sc = nullptr;
+    };
+    bool q8 = false;
+    DevW w_in;
     float* g_in = nullptr;
     float* g_out = nullptr;
     struct Blk {
-        float* g_attn;
-        float* g_ffn;
-        uint16_t* wqkv;   // [pad(3 hd)][d] fp16: rows wq | wk | wv
-        uint16_t* wo;     // [pad(d)][hd]
-        uint16_t* wgu;    // [pad(2 F)][d]: per 64 rows, 32 gate rows then the matching 32 up rows
-        uint16_t* wd;     // [pad(d)][F]
+        float* g_attn = nullptr;
+        float* g_ffn = nullptr;
+        DevW wqkv;   // [pad(3 hd)][d]: rows wq | wk | wv
+        DevW wo;     // [pad(d)][hd]
+        DevW wgu;    // [pad(2 F)][d]: per 64 rows, 32 gate rows then the matching 32 up rows
+        DevW wd;     // [pad(d)][F]
     };
     std::vector<Blk> blk;
-    uint16_t* w_heads = nullptr;   // [n_pad][d] bf16, packed column order
+    DevW w_heads;                  // [n_pad][d], packed column order
     float* b_heads = nullptr;      // [n_pad]
     int32_t* tile_head = nullptr;
     int32_t* tile_col0 = nullptr;
@@ -181,7 +194,7 @@ struct kva_ctx {
     uint16_t* vt16 = nullptr;   // [hd][m]     fp16 V transposed
     uint16_t* o16 = nullptr;    // [m][hd]     fp16 attention output
     uint16_t* act16 = nullptr;  // [m][F]      fp16 SwiGLU output
-    uint16_t* z16 = nullptr;    // [m][d]      bf16 final-normed trunk state
+    uint16_t* z16 = nullptr;    // [m][d]      final-normed trunk state: bf16 (fp16 for q8_0)
 
     kva_stats stats{};
 
@@ -274,99 +287,156 @@ kva_status upload(kva_ctx* ctx, void* dst, const void* src, size_t bytes) {
     return KVA_OK;
 }
 
-#define KVA_TRY(expr)                    \
-    do {                                 \
-        kva_status s_ = (expr);          \
-        if (s_ != KVA_OK) return s_;     \
-    } while (0)
+// One destination row of a packed weight: row `row` of source tensor `src`,
+// or a zero row when src is NULL (padding).
+struct RowSrc {
+    const void* src;
+    int64_t row;
+};
+
+// Target layouts on the device.
+enum PackTarget { PACK_F16 = 0, PACK_BF16 = 1, PACK_Q8 = 2 };
+
+// Packs rows (each K wide, stored in `dtype`) into the compute layout and
+// uploads it: fp16 or bf16 values [rows][K], or for q8_0 an int8 code plane
+// [rows][K] plus an fp16 scale plane [rows][K/32] (the 34-byte blocks split
+// losslessly into aligned planes).
+kva_status pack_weight(kva_ctx* ctx, int dtype, int64_t K, const std::vector<RowSrc>& rows,
+                       PackTarget target, kva_ctx::DevW* out, const char* name) {
+    const int64_t n = (int64_t)rows.size();
+    for (const RowSrc& r : rows)
+        if (!r.src && r.row >= 0) return fail(KVA_ERR_ARG, "weight %s is NULL", name);
+    if (target == PACK_Q8) {
+        if (dtype != KVA_DTYPE_Q8_0) return fail(KVA_ERR_DTYPE, "q8_0 layout needs q8_0 weights (%s)", name);
+        const int64_t nb = K / 32;
+        std::vector<int8_t> q((size_t)(n * K), 0);
+        std::vector<uint16_t> sc((size_t)(n * nb), 0);
+        for (int64_t r = 0; r < n; ++r) {
+            if (!rows[r].src) continue;
+            const uint8_t* blk = static_cast<const uint8_t*>(rows[r].src) + rows[r].row * nb * 34;
+            for (int64_t b = 0; b < nb; ++b) {
+                sc[(size_t)(r * nb + b)] = (uint16_t)(blk[b * 34] | (blk[b * 34 + 1] << 8));
+                std::memcpy(&q[(size_t)(r * K + b * 32)], blk + b * 34 + 2, 32);
+            }
+        }
+        HIP_TRY(ctx->alloc(&out->q, q.size(), true));
+        HIP_TRY(ctx->alloc(&out->sc, sc.size() * 2, true));
+        KVA_TRY(upload(ctx, out->q, q.data(), q.size()));
+        return upload(ctx, out->sc, sc.data(), sc.size() * 2);
+    }
+    if (dtype != KVA_DTYPE_F32 && dtype != KVA_DTYPE_BF16)
+        return fail(KVA_ERR_DTYPE, "16-bit layout needs fp32 or bf16 weights (%s)", name);
+    std::vector<uint16_t> w((size_t)(n * K), 0);
+    bool ovf = false;
+    for (int64_t r = 0; r < n; ++r) {
+        if (!rows[r].src) continue;
+        uint16_t* dst = &w[(size_t)(r * K)];
+        const int64_t base = rows[r].row * K;
+        if (target == PACK_BF16 && dtype == KVA_DTYPE_BF16) {
+            std::memcpy(dst, static_cast<const uint16_t*>(rows[r].src) + base, (size_t)K * 2);
+        } else if (target == PACK_BF16) {
+            for (int64_t k = 0; k < K; ++k) dst[k] = f32_to_bf16(static_cast<const float*>(rows[r].src)[base + k]);
+        } else {
+            for (int64_t k = 0; k < K; ++k) dst[k] = f32_to_f16(load_f32(rows[r].src, dtype, base + k), &ovf);
+        }
+    }
+    if (ovf) return fail(KVA_ERR_RANGE, "weight %s has values outside the fp16 range", name);
+    HIP_TRY(ctx->alloc(&out->w16, w.size() * 2, true));
+    return upload(ctx, out->w16, w.data(), w.size() * 2);
+}
+
+// Rows [0, n) of one tensor, then zero rows up to a multiple of kColPad.
+void add_rows(std::vector<RowSrc>& v, const void* src, int64_t n) {
+    for (int64_t r = 0; r < n; ++r) v.push_back({src, r});
+}
+void pad_rows(std::vector<RowSrc>& v) {
+    while (v.size() % kColPad) v.push_back({nullptr, -1});
+}
 
 kva_status create_impl(const kva_config* cfg, const kva_weights* w, int device, kva_ctx* ctx) {
     const kva_config& c = *cfg;
-    if (c.weight_dtype == KVA_DTYPE_Q8_0)
-        return fail(KVA_ERR_UNSUPPORTED, "q8_0 weights are not supported by this build yet");
     const int dt = c.weight_dtype;
+    const bool q8 = dt == KVA_DTYPE_Q8_0;
+    if (q8 && (c.n_in % 32 || c.d_model % 32 || c.d_ffn % 32))
+        return fail(KVA_ERR_SHAPE, "q8_0 needs every Linear input width to be a multiple of 32");
     const int64_t d = c.d_model, F = c.d_ffn, n_in = c.n_in;
     const int64_t hd = (int64_t)c.n_heads * c.head_dim;
     HIP_TRY(hipSetDevice(device));
     ctx->device = device;
+    ctx->q8 = q8;
+    const PackTarget trunk_t = q8 ? PACK_Q8 : PACK_F16;
+    const PackTarget head_t = q8 ? PACK_Q8 : PACK_BF16;
 
-    // -------- trunk weights -> fp16
-    std::vector<uint16_t> stage;
-    auto put16 = [&](uint16_t** dstp, int64_t rows_pad, int64_t cols) -> kva_status {
-        HIP_TRY(ctx->alloc(dstp, (size_t)rows_pad * cols * 2, true));
-        return upload(ctx, *dstp, stage.data(), (size_t)rows_pad * cols * 2);
-    };
     auto putf = [&](float** dstp, const float* src, int64_t n, const char* name) -> kva_status {
         if (!src) return fail(KVA_ERR_ARG, "gain %s is NULL", name);
         HIP_TRY(ctx->alloc(dstp, (size_t)n * 4, true));
         return upload(ctx, *dstp, src, (size_t)n * 4);
     };
 
+    // -------- trunk
     KVA_TRY(putf(&ctx->g_in, w->in_norm, n_in, "in_norm"));
     KVA_TRY(putf(&ctx->g_out, w->out_norm, d, "out_norm"));
-    stage.assign((size_t)round_up(d, kColPad) * n_in, 0);
-    KVA_TRY(to_f16_rows(w->in_proj, dt, d, n_in, stage.data(), "in_proj"));
-    KVA_TRY(put16(&ctx->w_in, round_up(d, kColPad), n_in));
-
+    {
+        std::vector<RowSrc> rows;
+        add_rows(rows, w->in_proj, d);
+        pad_rows(rows);
+        KVA_TRY(pack_weight(ctx, dt, n_in, rows, trunk_t, &ctx->w_in, "in_proj"));
+    }
     if (!w->blocks) return fail(KVA_ERR_ARG, "blocks is NULL");
     ctx->blk.resize(c.n_blocks);
-    std::vector<uint16_t> tmp;
     for (int b = 0; b < c.n_blocks; ++b) {
         const kva_block_weights& bw = w->blocks[b];
         kva_ctx::Blk& B = ctx->blk[b];
         KVA_TRY(putf(&B.g_attn, bw.attn_norm, d, "attn_norm"));
         KVA_TRY(putf(&B.g_ffn, bw.ffn_norm, d, "ffn_norm"));
-        stage.assign((size_t)round_up(3 * hd, kColPad) * d, 0);
-        KVA_TRY(to_f16_rows(bw.wq, dt, hd, d, stage.data(), "wq"));
-        KVA_TRY(to_f16_rows(bw.wk, dt, hd, d, stage.data() + hd * d, "wk"));
-        KVA_TRY(to_f16_rows(bw.wv, dt, hd, d, stage.data() + 2 * hd * d, "wv"));
-        KVA_TRY(put16(&B.wqkv, round_up(3 * hd, kColPad), d));
-        stage.assign((size_t)round_up(d, kColPad) * hd, 0);
-        KVA_TRY(to_f16_rows(bw.wo, dt, d, hd, stage.data(), "wo"));
-        KVA_TRY(put16(&B.wo, round_up(d, kColPad), hd));
+        std::vector<RowSrc> rows;
+        add_rows(rows, bw.wq, hd);
+        add_rows(rows, bw.wk, hd);
+        add_rows(rows, bw.wv, hd);
+        pad_rows(rows);
+        KVA_TRY(pack_weight(ctx, dt, d, rows, trunk_t, &B.wqkv, "wq|wk|wv"));
+        rows.clear();
+        add_rows(rows, bw.wo, d);
+        pad_rows(rows);
+        KVA_TRY(pack_weight(ctx, dt, hd, rows, trunk_t, &B.wo, "wo"));
         // gate/up interleaved in groups of 32 rows so one 64-column MFMA pair
         // holds gate and up of the same 32 hidden units
-        stage.assign((size_t)round_up(2 * F, kColPad) * d, 0);
-        tmp.assign((size_t)F * d, 0);
-        KVA_TRY(to_f16_rows(bw.w_gate, dt, F, d, tmp.data(), "w_gate"));
-        for (int64_t f = 0; f < F; ++f)
-            std::memcpy(&stage[(size_t)((f / 32) * 64 + f % 32) * d], &tmp[(size_t)f * d], (size_t)d * 2);
-        KVA_TRY(to_f16_rows(bw.w_up, dt, F, d, tmp.data(), "w_up"));
-        for (int64_t f = 0; f < F; ++f)
-            std::memcpy(&stage[(size_t)((f / 32) * 64 + 32 + f % 32) * d], &tmp[(size_t)f * d], (size_t)d * 2);
-        KVA_TRY(put16(&B.wgu, round_up(2 * F, kColPad), d));
-        stage.assign((size_t)round_up(d, kColPad) * F, 0);
-        KVA_TRY(to_f16_rows(bw.w_down, dt, d, F, stage.data(), "w_down"));
-        KVA_TRY(put16(&B.wd, round_up(d, kColPad), F));
+        rows.clear();
+        for (int64_t pr = 0; pr < 2 * F; ++pr) {
+            const int64_t f = (pr / 64) * 32 + pr % 32;
+            rows.push_back({(pr % 64) < 32 ? bw.w_gate : bw.w_up, f});
+        }
+        pad_rows(rows);
+        KVA_TRY(pack_weight(ctx, dt, d, rows, trunk_t, &B.wgu, "w_gate|w_up"));
+        rows.clear();
+        add_rows(rows, bw.w_down, d);
+        pad_rows(rows);
+        KVA_TRY(pack_weight(ctx, dt, F, rows, trunk_t, &B.wd, "w_down"));
     }
 
-    // -------- heads -> bf16, packed column order
+    // -------- heads, packed column order
     if (!w->head_w) return fail(KVA_ERR_ARG, "head_w is NULL");
     if (c.has_head_bias && !w->head_b) return fail(KVA_ERR_ARG, "head_b is NULL but has_head_bias is set");
-    HeadPlan plan = plan_heads(c);
-    ctx->n_pad_heads = plan.n_pad;
-    ctx->tail_start = plan.tail_start;
     for (int i = 0; i < c.n_out_heads; ++i) {
         if (!w->head_w[i]) return fail(KVA_ERR_ARG, "head_w[%d] is NULL", i);
         if (c.has_head_bias && !w->head_b[i]) return fail(KVA_ERR_ARG, "head_b[%d] is NULL", i);
     }
-    stage.assign((size_t)plan.n_pad * d, 0);
-    std::vector<float> bias((size_t)plan.n_pad, 0.0f);
-    for (int64_t col = 0; col < plan.n_pad; ++col) {
-        const int hh = plan.col_head[col];
-        if (hh < 0) continue;
-        const int64_t src_row = plan.col_index[col];
-        uint16_t* dst = &stage[(size_t)col * d];
-        if (dt == KVA_DTYPE_BF16) {
-            std::memcpy(dst, static_cast<const uint16_t*>(w->head_w[hh]) + src_row * d, (size_t)d * 2);
-        } else {
-            const float* s = static_cast<const float*>(w->head_w[hh]) + src_row * d;
-            for (int64_t k = 0; k < d; ++k) dst[k] = f32_to_bf16(s[k]);
-        }
-        if (c.has_head_bias) bias[col] = w->head_b[hh][src_row];
-    }
-    KVA_TRY(put16(&ctx->w_heads, plan.n_pad, d));
+    HeadPlan plan = plan_heads(c);
+    ctx->n_pad_heads = plan.n_pad;
+    ctx->tail_start = plan.tail_start;
     {
+        std::vector<RowSrc> rows((size_t)plan.n_pad);
+        std::vector<float> bias((size_t)plan.n_pad, 0.0f);
+        for (int64_t col = 0; col < plan.n_pad; ++col) {
+            const int hh = plan.col_head[col];
+            if (hh < 0) {
+                rows[col] = {nullptr, -1};
+                continue;
+            }
+            rows[col] = {w->head_w[hh], plan.col_index[col]};
+            if (c.has_head_bias) bias[col] = w->head_b[hh][plan.col_index[col]];
+        }
+        KVA_TRY(pack_weight(ctx, dt, d, rows, head_t, &ctx->w_heads, "heads"));
         float* bb = nullptr;
         HIP_TRY(ctx->alloc(&bb, (size_t)plan.n_pad * 4, true));
         KVA_TRY(upload(ctx, bb, bias.data(), (size_t)plan.n_pad * 4));
@@ -404,6 +474,13 @@ kva_status create_impl(const kva_config* cfg, const kva_weights* w, int device, 
     HIP_TRY(hipMemset(ctx->z16, 0, (size_t)m * d * 2));
     HIP_TRY(hipDeviceSynchronize());
     return KVA_OK;
+}
+
+void set_b(GemmArgs& g, const kva_ctx::DevW& w, int64_t K) {
+    g.B = w.w16;
+    g.Bq = w.q;
+    g.Bs = w.sc;
+    g.ldb = K;
 }
 
 #define LAUNCH(expr)                                                                      \
@@ -479,63 +556,66 @@ kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n, float* co
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t d = c.d_model, F = c.d_ffn, n_in = c.n_in;
     const int64_t hd = (int64_t)c.n_heads * c.head_dim;
+    // trunk operand type and the tile of the narrow (N = d) GEMMs
+    const GemmOperand opd = ctx->q8 ? OPD_Q8 : OPD_F16;
+    const GemmTile small_n = ctx->q8 ? TILE_128x128 : TILE_128x64;
 
     STAGE(KVA_STAGE_NORM, launch_rmsnorm_cast(x, n_in, ctx->g_in, n, (int32_t)n_in, c.eps, ctx->u16, n_in, false, s));
     {
         GemmArgs g;
-        g.A = ctx->u16; g.lda = n_in; g.B = ctx->w_in; g.ldb = n_in;
+        g.A = ctx->u16; g.lda = n_in; set_b(g, ctx->w_in, n_in);
         g.M = n; g.N = (int32_t)round_up(d, kColPad); g.K = (int32_t)n_in;
         g.epi.out_f32 = ctx->h; g.epi.ld_f32 = d; g.epi.n_real = (int32_t)d;
-        STAGE(KVA_STAGE_GEMM_IN, launch_gemm(OPD_F16, TILE_128x64, EPI_STORE_F32, g, s));
+        STAGE(KVA_STAGE_GEMM_IN, launch_gemm(opd, small_n, EPI_STORE_F32, g, s));
     }
     for (int b = 0; b < c.n_blocks; ++b) {
         const kva_ctx::Blk& B = ctx->blk[b];
         STAGE(KVA_STAGE_NORM, launch_rmsnorm_cast(ctx->h, d, B.g_attn, n, (int32_t)d, c.eps, ctx->a16, d, false, s));
         {
             GemmArgs g;
-            g.A = ctx->a16; g.lda = d; g.B = B.wqkv; g.ldb = d;
+            g.A = ctx->a16; g.lda = d; set_b(g, B.wqkv, d);
             g.M = n; g.N = (int32_t)round_up(3 * hd, kColPad); g.K = (int32_t)d;
             g.epi.out16 = ctx->qk16; g.epi.ld16 = 2 * hd;
             g.epi.vt = ctx->vt16; g.epi.ld_vt = ctx->m_alloc; g.epi.n_split = (int32_t)(2 * hd);
             g.epi.n_real = (int32_t)(3 * hd);
-            STAGE(KVA_STAGE_GEMM_QKV, launch_gemm(OPD_F16, TILE_128x128, EPI_QKV, g, s));
+            STAGE(KVA_STAGE_GEMM_QKV, launch_gemm(opd, TILE_128x128, EPI_QKV, g, s));
         }
         STAGE(KVA_STAGE_ATTN, launch_attention(ctx->qk16, 2 * hd, (int32_t)hd, ctx->vt16, ctx->m_alloc, ctx->o16, hd, n,
                                 c.n_heads, c.attn_block, s));
         {
             GemmArgs g;
-            g.A = ctx->o16; g.lda = hd; g.B = B.wo; g.ldb = hd;
+            g.A = ctx->o16; g.lda = hd; set_b(g, B.wo, hd);
             g.M = n; g.N = (int32_t)round_up(d, kColPad); g.K = (int32_t)hd;
             g.epi.out_f32 = ctx->h; g.epi.ld_f32 = d; g.epi.n_real = (int32_t)d;
-            STAGE(KVA_STAGE_GEMM_O, launch_gemm(OPD_F16, TILE_128x64, EPI_ADD_F32, g, s));
+            STAGE(KVA_STAGE_GEMM_O, launch_gemm(opd, small_n, EPI_ADD_F32, g, s));
         }
         STAGE(KVA_STAGE_NORM, launch_rmsnorm_cast(ctx->h, d, B.g_ffn, n, (int32_t)d, c.eps, ctx->a16, d, false, s));
         {
             GemmArgs g;
-            g.A = ctx->a16; g.lda = d; g.B = B.wgu; g.ldb = d;
+            g.A = ctx->a16; g.lda = d; set_b(g, B.wgu, d);
             g.M = n; g.N = (int32_t)round_up(2 * F, kColPad); g.K = (int32_t)d;
             g.epi.out16 = ctx->act16; g.epi.ld16 = F; g.epi.n_real = (int32_t)(2 * F);
-            STAGE(KVA_STAGE_GEMM_GATEUP, launch_gemm(OPD_F16, TILE_128x128, EPI_SWIGLU, g, s));
+            STAGE(KVA_STAGE_GEMM_GATEUP, launch_gemm(opd, TILE_128x128, EPI_SWIGLU, g, s));
         }
         {
             GemmArgs g;
-            g.A = ctx->act16; g.lda = F; g.B = B.wd; g.ldb = F;
+            g.A = ctx->act16; g.lda = F; set_b(g, B.wd, F);
             g.M = n; g.N = (int32_t)round_up(d, kColPad); g.K = (int32_t)F;
             g.epi.out_f32 = ctx->h; g.epi.ld_f32 = d; g.epi.n_real = (int32_t)d;
-            STAGE(KVA_STAGE_GEMM_DOWN, launch_gemm(OPD_F16, TILE_128x64, EPI_ADD_F32, g, s));
+            STAGE(KVA_STAGE_GEMM_DOWN, launch_gemm(opd, small_n, EPI_ADD_F32, g, s));
         }
     }
-    STAGE(KVA_STAGE_NORM, launch_rmsnorm_cast(ctx->h, d, ctx->g_out, n, (int32_t)d, c.eps, ctx->z16, d, true, s));
+    STAGE(KVA_STAGE_NORM, launch_rmsnorm_cast(ctx->h, d, ctx->g_out, n, (int32_t)d, c.eps, ctx->z16, d, !ctx->q8, s));
     {
         GemmArgs g;
-        g.A = ctx->z16; g.lda = d; g.B = ctx->w_heads; g.ldb = d;
+        g.A = ctx->z16; g.lda = d; set_b(g, ctx->w_heads, d);
         g.M = n; g.N = (int32_t)ctx->n_pad_heads; g.K = (int32_t)d;
         g.epi.n_real = (int32_t)ctx->n_pad_heads;
         g.epi.tile_head = ctx->tile_head; g.epi.tile_col0 = ctx->tile_col0;
         g.epi.tail_head = ctx->tail_head; g.epi.tail_col = ctx->tail_col;
         g.epi.tail_start = ctx->tail_start; g.epi.bias = ctx->b_heads;
         g.epi.heads = ho;
-        STAGE(KVA_STAGE_GEMM_HEADS, launch_gemm(OPD_BF16, TILE_256x256, EPI_HEADS, g, s));
+        STAGE(KVA_STAGE_GEMM_HEADS, launch_gemm(ctx->q8 ? OPD_Q8 : OPD_BF16, TILE_256x256, EPI_HEADS, g, s));
     }
     ctx->stats.calls += 1;
     ctx->stats.tokens += (uint64_t)n;

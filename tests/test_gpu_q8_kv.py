@@ -1,0 +1,132 @@
+"""GPU parity for the q8_0 projector and the chained attention-layer KV-cache
+write at prompt scale (65536 tokens, processed in 8192-token calls as the
+benchmark does).  Oracle: float64 on the dequantised weights (d * q).
+
+Bars: q8_0 outputs max|err| <= 5e-2 * RMS per head; KV cache after the
+chained projection + k_norm + RoPE + bf16 store within the projector's bar
+(2e-2 * RMS) plus one bf16 rounding of the largest value (2^-9 * max|v|).
+"""
+import numpy as np
+import pytest
+import torch
+
+import learned_kv_approximation_amd as kva
+import oracle
+import synth
+from oracle import ref
+
+pytestmark = pytest.mark.gpu
+TOL_Q8 = 5e-2
+CHUNK = 8192
+N_PROMPT = 65536
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _err(g, y):
+    rms = np.sqrt(np.mean(y * y))
+    return float(np.max(np.abs(g.astype(np.float64) - y)) / rms)
+
+
+def _bf16_bar(y, tol=2e-2):
+    return tol + 2.0 ** -9 * float(np.max(np.abs(y)) / np.sqrt(np.mean(y * y)))
+
+
+def test_tiny_q8_0_parity():
+    cfg = synth.config("tiny", weight_dtype="q8_0")
+    w = synth.make_weights(cfg)
+    x = synth.make_input(cfg, n_tokens=100)
+    proj = kva.Projector(cfg, w, max_tokens=128)
+    outs = proj.project(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    want = oracle.project(cfg, w, x)
+    errs = [_err(o.cpu().numpy(), want[i]) for i, o in enumerate(outs)]
+    print("tiny q8_0 max|err|/rms per head", errs)
+    assert max(errs) <= TOL_Q8
+    proj.close()
+
+
+@pytest.fixture(scope="module")
+def r3q8():
+    cfg = synth.config("r3_q8_0")
+    w = synth.make_weights(cfg)
+    return cfg, w, ref.prepare(cfg, w)
+
+
+def test_r3_q8_0_prompt_in_chunks(r3q8):
+    """65536 tokens in 8 calls of 8192: sampled ubatches {0, 31, 63} against the
+    oracle, and ubatch 31 bitwise equal to a call on that ubatch alone."""
+    cfg, w, prep = r3q8
+    x = synth.make_input(cfg, n_tokens=N_PROMPT)
+    proj = kva.Projector(cfg, w, max_tokens=CHUNK)
+    outs = proj.alloc_outputs(CHUNK)
+    xd = torch.from_numpy(x).cuda()
+    heads = [0, 3, 35]
+    keep = {}
+    for c0 in range(0, N_PROMPT, CHUNK):
+        proj.project(xd[c0:c0 + CHUNK], outs)
+        for u in (0, 31, 63):
+            s = u * 1024
+            if c0 <= s < c0 + CHUNK:
+                keep[u] = [outs[i][s - c0:s - c0 + 1024].cpu().numpy() for i in range(len(outs))]
+    torch.cuda.synchronize()
+    for u in (0, 31, 63):
+        want = ref.project(cfg, prep, x[u * 1024:(u + 1) * 1024], which=heads)
+        errs = {cfg["heads"][i]["name"]: _err(keep[u][i], want[i]) for i in heads}
+        print(f"q8_0 ubatch {u}: {errs}", flush=True)
+        assert max(errs.values()) <= TOL_Q8
+    alone = proj.project(xd[31 * 1024:32 * 1024].contiguous())
+    torch.cuda.synchronize()
+    for i in range(len(alone)):
+        assert np.array_equal(alone[i].cpu().numpy(), keep[31][i]), i
+    proj.close()
+
+
+@pytest.fixture(scope="module")
+def r3bf16():
+    cfg = synth.config("r3_kv")
+    w = synth.make_weights(cfg)
+    return cfg, w, ref.prepare(cfg, w)
+
+
+def test_r3_projection_chained_into_paged_kv_cache(r3bf16):
+    """The r3 bf16 projector over a 65536-token prompt, each attention head's
+    k|v written through k_norm + RoPE into its layer's paged bf16 cache."""
+    cfg, w, prep = r3bf16
+    x = synth.make_input(cfg, n_tokens=N_PROMPT)
+    attn = [i for i, h in enumerate(cfg["heads"]) if h["kind"] == "attn"]
+    gains, ptab, n_pages = synth.make_kv_write_inputs(N_PROMPT, n_layers=len(attn), seed=cfg["seed"])
+    proj = kva.Projector(cfg, w, max_tokens=CHUNK)
+    outs = proj.alloc_outputs(CHUNK)
+    xd = torch.from_numpy(x).cuda()
+    ptab_d = torch.from_numpy(ptab).cuda()
+    gains_d = torch.from_numpy(gains).cuda()
+    pools = [(torch.full((n_pages, 256, 4, 256), -1, dtype=torch.int16, device="cuda"),
+              torch.full((n_pages, 256, 4, 256), -1, dtype=torch.int16, device="cuda")) for _ in attn]
+    caches = [kva.kva_paged_kv(kp.data_ptr(), vp.data_ptr(), ptab_d.data_ptr(), 256, n_pages, len(ptab),
+                               4, 256, 64, 1.0e7, 1e-6) for kp, vp in pools]
+    st = kva.current_stream()
+    for c0 in range(0, N_PROMPT, CHUNK):
+        proj.project(xd[c0:c0 + CHUNK], outs)
+        for li, hi in enumerate(attn):
+            kva.kva_attn_kv_write(outs[hi].data_ptr(), 2048, CHUNK, c0, gains_d[li].data_ptr(), caches[li], st)
+    torch.cuda.synchronize()
+    want = {u: ref.project(cfg, prep, x[u * 1024:(u + 1) * 1024], which=attn) for u in (0, 63)}
+    for li, hi in enumerate(attn):
+        kpn = pools[li][0].cpu().numpy().view(np.uint16)
+        vpn = pools[li][1].cpu().numpy().view(np.uint16)
+        for u in (0, 63):
+            pos = u * 1024 + np.arange(1024)
+            k, v = ref.kv_write_values(want[u][hi], gains[li], u * 1024)
+            ek = _err(ref.bf16_bits_to_f64(kpn[ptab[pos // 256], pos % 256]), k)
+            ev = _err(ref.bf16_bits_to_f64(vpn[ptab[pos // 256], pos % 256]), v)
+            print(f"kv layer {cfg['heads'][hi]['layer']} ubatch {u}: k {ek:.3e} v {ev:.3e}", flush=True)
+            assert ek <= _bf16_bar(k) and ev <= _bf16_bar(v), (u, li, ek, ev, _bf16_bar(k), _bf16_bar(v))
+    # every slot of every page was written (no poison left anywhere)
+    for kp, vp in pools:
+        assert not bool((kp == -1).all(dim=-1).any()) and not bool((vp == -1).all(dim=-1).any())
+    proj.close()
