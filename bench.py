@@ -77,7 +77,11 @@ def traffic_bytes():
     return t.get("bytes_per_launch")
 
 
-def time_config(name: str, steps: int, warmup: int, n_tokens: int = 1024):
+def time_config(name: str, steps: int, warmup: int, n_tokens: int = 1024, prompt: int = 0,
+                stages: bool = True):
+    """Times kva_project_ubatch on `n_tokens`-token calls of projector `name`.
+    With prompt > 0, one step is a whole prompt of `prompt` tokens processed
+    in consecutive n_tokens-token calls (output buffers reused per call)."""
     import torch
 
     import learned_kv_approximation_amd as kva
@@ -85,14 +89,21 @@ def time_config(name: str, steps: int, warmup: int, n_tokens: int = 1024):
     cfg = synth.config(name)
     t0 = time.time()
     w = synth.make_weights(cfg)
-    x = synth.make_input(cfg, n_tokens=n_tokens)
-    print(f"[bench] {name}: weights generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    total = prompt or n_tokens
+    x = synth.make_input(cfg, n_tokens=total)
+    print(f"[bench] {name}: inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     proj = kva.Projector(cfg, w, max_tokens=n_tokens)
     del w
     xd = torch.from_numpy(x).cuda()
+    del x
     outs = proj.alloc_outputs(n_tokens)
+
+    def step():
+        for c0 in range(0, total, n_tokens):
+            proj.project(xd[c0:c0 + n_tokens], outs)
+
     for _ in range(warmup):
-        proj.project(xd, outs)
+        step()
     torch.cuda.synchronize()
 
     kva.kva_profile_enable(proj.ctx, 1 << STAGE_HEADS)
@@ -102,7 +113,7 @@ def time_config(name: str, steps: int, warmup: int, n_tokens: int = 1024):
     wall0 = time.perf_counter()
     evs[0].record()
     for k in range(steps):
-        proj.project(xd, outs)
+        step()
         evs[k + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -110,35 +121,104 @@ def time_config(name: str, steps: int, warmup: int, n_tokens: int = 1024):
     total_ms = evs[0].elapsed_time(evs[-1])
     heads = kva.kva_profile_read(proj.ctx)["gemm_heads"]
 
-    # per-stage breakdown, a separate set of steps with every stage bracketed
-    kva.kva_profile_enable(proj.ctx, (1 << len(kva.STAGES)) - 1)
-    n_prof = max(3, steps // 4)
-    for _ in range(n_prof):
-        proj.project(xd, outs)
-    torch.cuda.synchronize()
-    stages = kva.kva_profile_read(proj.ctx)
+    stage_ms = {}
+    if stages:
+        # per-stage breakdown, a separate set of steps with every stage bracketed
+        kva.kva_profile_enable(proj.ctx, (1 << len(kva.STAGES)) - 1)
+        n_prof = max(3, steps // 4)
+        for _ in range(n_prof):
+            step()
+        torch.cuda.synchronize()
+        stage_ms = {k: v[1] / n_prof for k, v in kva.kva_profile_read(proj.ctx).items()}
     kva.kva_profile_enable(proj.ctx, 0)
     proj.close()
     del outs, xd
     torch.cuda.empty_cache()
     f = flops(cfg, n_tokens)
+    calls = total // n_tokens
     ms = total_ms / steps
+    sec = ms / 1e3
     res = {
-        "tokens_per_s": n_tokens / (ms / 1e3),
+        "tokens_per_s": total / sec,
         "ms_per_step": ms,
         "ms_median": float(np.median(per)),
         "ms_p10": float(np.percentile(per, 10)),
         "ms_p90": float(np.percentile(per, 90)),
         "wall_s": wall,
-        "tflop_per_step": f["total"] / 1e12,
-        "pct_mfma_peak": 100.0 * f["total"] / (ms / 1e3) / (PEAK_TFLOPS * 1e12),
+        "tflop_per_step": calls * f["total"] / 1e12,
+        "pct_mfma_peak": 100.0 * calls * f["total"] / sec / (PEAK_TFLOPS * 1e12),
         "heads_gemm_ms": heads[1] / max(heads[0], 1),
         "heads_gemm_tflop": f["gemm_heads"] / 1e12,
-        "stages_ms_per_step": {k: v[1] / n_prof for k, v in stages.items()},
-        "stage_tflops": {k: (f[k] / 1e12) / (v[1] / n_prof / 1e3) if v[1] > 0 and k in f else None
-                         for k, v in stages.items()},
+        "stages_ms_per_step": stage_ms,
+        "stage_tflops": {k: (calls * f[k] / 1e12) / (v / 1e3) if v > 0 and k in f else None
+                         for k, v in stage_ms.items()},
     }
     return res
+
+
+def time_kv_write(n_tokens: int = 65536, layers: int = 8, chunk: int = 8192, steps: int = 5):
+    """kva_attn_kv_write for every attention layer over an n_tokens prompt
+    (chunk tokens per call, as after each projection call).  Per token and
+    layer it reads 2048 fp32 (8 KiB) and writes 2 x 1024 bf16 (4 KiB)."""
+    import torch
+
+    import learned_kv_approximation_amd as kva
+
+    gains, ptab, n_pages = synth.make_kv_write_inputs(n_tokens, n_layers=layers)
+    kv = torch.from_numpy(synth.make_kv_rows(chunk, scale=3.0)).cuda()
+    g = torch.from_numpy(gains).cuda()
+    pt = torch.from_numpy(ptab).cuda()
+    pools = [(torch.empty((n_pages, 256, 4, 256), dtype=torch.int16, device="cuda"),
+              torch.empty((n_pages, 256, 4, 256), dtype=torch.int16, device="cuda")) for _ in range(layers)]
+    caches = [kva.kva_paged_kv(kp.data_ptr(), vp.data_ptr(), pt.data_ptr(), 256, n_pages, len(ptab),
+                               4, 256, 64, 1.0e7, 1e-6) for kp, vp in pools]
+    st = kva.current_stream()
+
+    def step():
+        for c0 in range(0, n_tokens, chunk):
+            for li in range(layers):
+                kva.kva_attn_kv_write(kv.data_ptr(), 2048, chunk, c0, g[li].data_ptr(), caches[li], st)
+
+    step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = n_tokens * layers * (2048 * 4 + 2 * 1024 * 2)
+    del pools
+    torch.cuda.empty_cache()
+    return {"tokens": n_tokens, "layers": layers, "ms": round(ms, 4), "bytes": nbytes,
+            "gb_s": round(nbytes / (ms / 1e3) / 1e9, 1), "frac_hbm": round(nbytes / (ms / 1e3) / 1e9 / HBM_GBS, 4),
+            "launches": (n_tokens // chunk) * layers}
+
+
+def traffic_probe():
+    """Kernels whose HBM counters calibrate the head GEMM's traffic: two r2
+    projections, then two copies of exactly COPY_BYTES (read COPY_BYTES,
+    write COPY_BYTES) with torch's device copy."""
+    import torch
+
+    import learned_kv_approximation_amd as kva
+    cfg = synth.config("r2")
+    proj = kva.Projector(cfg, synth.make_weights(cfg), max_tokens=1024)
+    xd = torch.from_numpy(synth.make_input(cfg)).cuda()
+    outs = proj.alloc_outputs(1024)
+    for _ in range(2):
+        proj.project(xd, outs)
+    torch.cuda.synchronize()
+    proj.close()
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+COPY_BYTES = 1 << 30
 
 
 def cpu_baseline(min_seconds: float = 10.0, max_reps: int = 8):
@@ -183,6 +263,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-r3", action="store_true")
+    ap.add_argument("--quick", action="store_true", help="r2 and r3 one-ubatch lines only")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run 2 r2 projections and 2 plain 1 GiB device copies, print nothing (for rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -194,14 +277,26 @@ def main():
         sys.exit(1)
     import learned_kv_approximation_amd as kva
     kva.lib()   # fails loudly if libkva.so is missing
+    if args.traffic_probe:
+        traffic_probe()
+        return
 
     r2 = time_config("r2", args.steps, args.warmup)
     print(f"[bench] r2: {r2['tokens_per_s']:.0f} tok/s, {r2['pct_mfma_peak']:.1f}% peak", file=sys.stderr, flush=True)
-    r3 = None
+    r3 = r3b = q8 = q8p = kvw = None
     if not args.no_r3:
         r3 = time_config("r3", args.steps, args.warmup)
         print(f"[bench] r3: {r3['tokens_per_s']:.0f} tok/s, {r3['pct_mfma_peak']:.1f}% peak", file=sys.stderr,
               flush=True)
+        if not args.quick:
+            r3b = time_config("r3", max(5, args.steps // 3), 2, n_tokens=8192, stages=False)
+            print(f"[bench] r3 8192: {r3b['tokens_per_s']:.0f} tok/s", file=sys.stderr, flush=True)
+            q8 = time_config("r3_q8_0", args.steps, args.warmup, stages=True)
+            print(f"[bench] r3 q8_0: {q8['tokens_per_s']:.0f} tok/s", file=sys.stderr, flush=True)
+            q8p = time_config("r3_q8_0", 3, 1, n_tokens=8192, prompt=65536, stages=False)
+            print(f"[bench] r3 q8_0 65536: {q8p['tokens_per_s']:.0f} tok/s", file=sys.stderr, flush=True)
+            kvw = time_kv_write()
+            print(f"[bench] kv write: {kvw['gb_s']} GB/s", file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline()
@@ -236,11 +331,21 @@ def main():
         "stage_tflops": {k: (round(v, 1) if v else None) for k, v in r2["stage_tflops"].items()},
         "cpu_baseline": cpu,
     }
+    def brief(r):
+        return {"tokens_per_s": round(r["tokens_per_s"], 1), "ms_per_step": round(r["ms_per_step"], 4),
+                "pct_mfma_peak": round(r["pct_mfma_peak"], 2), "tflop_per_step": round(r["tflop_per_step"], 5),
+                "heads_gemm_ms": round(r["heads_gemm_ms"], 4),
+                "stages_ms_per_step": {k: round(v, 4) for k, v in r["stages_ms_per_step"].items()}}
     if r3 is not None:
-        out["r3"] = {"tokens_per_s": round(r3["tokens_per_s"], 1), "ms_per_step": round(r3["ms_per_step"], 4),
-                     "pct_mfma_peak": round(r3["pct_mfma_peak"], 2), "tflop_per_step": round(r3["tflop_per_step"], 5),
-                     "heads_gemm_ms": round(r3["heads_gemm_ms"], 4),
-                     "stages_ms_per_step": {k: round(v, 4) for k, v in r3["stages_ms_per_step"].items()}}
+        out["r3"] = brief(r3)
+    if r3b is not None:
+        out["r3_8192_tokens_one_call"] = brief(r3b)
+    if q8 is not None:
+        out["r3_q8_0"] = brief(q8)
+    if q8p is not None:
+        out["r3_q8_0_prompt_65536"] = brief(q8p)
+    if kvw is not None:
+        out["kv_write_65536x8"] = kvw
     print(json.dumps(out), flush=True)
 
 
