@@ -77,11 +77,16 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_nt(GemmArgs g) {
 
     const int mt = (g.M + BM - 1) / BM;
     const int nt = g.N / BN;
-    const int total = mt * nt;
+    const int S = g.splits;
+    const int total = mt * nt * S;
     const int per_xcd = gridDim.x / 8;
     const int v = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     if (v >= total) return;
-    const int tm = v % mt, tn = v / mt;
+    // M-tiles fastest, then splits, then N-tiles: the tiles sharing a weight
+    // strip run back to back on one XCD
+    const int tm = v % mt;
+    const int split = (v / mt) % S;
+    const int tn = v / (mt * S);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -163,10 +168,12 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_nt(GemmArgs g) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const int nk = g.K / BK;
+    const int nk_all = g.K / BK;
+    const int kb = split * nk_all / S;                 // this split's slabs: [kb, kb + nk)
+    const int nk = (split + 1) * nk_all / S - kb;
     const int frow = lane & 31, fk = lane >> 5;
-    qload(0);
-    issue(0, 0);
+    qload(kb);
+    issue(kb, 0);
     qstore(0);
     // global_load_lds completes through vmcnt: wait for it explicitly, then
     // the barrier publishes the slab to every wave
@@ -176,8 +183,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_nt(GemmArgs g) {
         const int buf = kt & 1;
         // the other buffer was last read before the previous barrier: refill it
         if (kt + 1 < nk) {
-            qload(kt + 1);
-            issue(kt + 1, buf ^ 1);
+            qload(kb + kt + 1);
+            issue(kb + kt + 1, buf ^ 1);
         }
         const uint16_t* sa = smem + buf * STAGE;
         const uint16_t* sb = sa + BM * BK;
@@ -210,7 +217,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_nt(GemmArgs g) {
     const int col_base = tn * BN + wn * WN + (lane & 31);
     const EpiArgs& e = g.epi;
 
-    if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_ADD_F32) {
+    if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_ADD_F32 || EPI == EPI_PARTIAL) {
+        float* out = e.out_f32 + (EPI == EPI_PARTIAL ? (int64_t)split * g.split_stride : 0);
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
             const int col = col_base + j * 32;
@@ -221,7 +229,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_nt(GemmArgs g) {
                 for (int r = 0; r < 16; ++r) {
                     const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
                     if (row < g.M) {
-                        float* p = e.out_f32 + (int64_t)row * e.ld_f32 + col;
+                        float* p = out + (int64_t)row * e.ld_f32 + col;
                         if constexpr (EPI == EPI_ADD_F32) *p += acc[i][j][r];
                         else *p = acc[i][j][r];
                     }
@@ -308,9 +316,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_nt(GemmArgs g) {
 template <int BM, int BN, int WGM, int WGN, int OPD, int EPI>
 hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
     if (a.N % BN) return hipErrorInvalidValue;
+    if (a.splits < 1 || a.splits > a.K / BK || (a.splits > 1 && EPI != EPI_PARTIAL)) return hipErrorInvalidValue;
     const int mt = (a.M + BM - 1) / BM;
     const int nt = a.N / BN;
-    const int total = mt * nt;
+    const int total = mt * nt * a.splits;
     const int grid = (total + 7) / 8 * 8;
     hipLaunchKernelGGL((gemm_nt<BM, BN, WGM, WGN, OPD, EPI>), dim3(grid), dim3(64 * WGM * WGN), 0, s, a);
     return hipGetLastError();
@@ -318,41 +327,38 @@ hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
 
 }  // namespace
 
+// The instantiated (operand, tile, epilogue) combinations.
+#define KVA_GEMM_CASE(OPD_, TILE_, EPI_, BM_, BN_, WGM_, WGN_) \
+    if (opd == OPD_ && tile == TILE_ && epi == EPI_) return launch_one<BM_, BN_, WGM_, WGN_, OPD_, EPI_>(a, s);
+
 hipError_t launch_gemm(GemmOperand opd, GemmTile tile, EpiKind epi, const GemmArgs& a,
                        hipStream_t s) {
     if (a.M <= 0) return hipSuccess;
     if (a.K % BK != 0 || a.K <= 0) return hipErrorInvalidValue;
     if (opd == OPD_Q8 && (!a.Bq || !a.Bs)) return hipErrorInvalidValue;
-    if (tile == TILE_256x256 && epi == EPI_HEADS) {
-        if (opd == OPD_BF16) return launch_one<256, 256, 2, 4, OPD_BF16, EPI_HEADS>(a, s);
-        if (opd == OPD_Q8) return launch_one<256, 256, 2, 4, OPD_Q8, EPI_HEADS>(a, s);
-    }
-    if (opd == OPD_F16 && tile == TILE_128x128) {
-        switch (epi) {
-            case EPI_STORE_F32: return launch_one<128, 128, 2, 2, OPD_F16, EPI_STORE_F32>(a, s);
-            case EPI_ADD_F32: return launch_one<128, 128, 2, 2, OPD_F16, EPI_ADD_F32>(a, s);
-            case EPI_QKV: return launch_one<128, 128, 2, 2, OPD_F16, EPI_QKV>(a, s);
-            case EPI_SWIGLU: return launch_one<128, 128, 2, 2, OPD_F16, EPI_SWIGLU>(a, s);
-            default: break;
-        }
-    }
-    if (opd == OPD_Q8 && tile == TILE_128x128) {
-        switch (epi) {
-            case EPI_STORE_F32: return launch_one<128, 128, 2, 2, OPD_Q8, EPI_STORE_F32>(a, s);
-            case EPI_ADD_F32: return launch_one<128, 128, 2, 2, OPD_Q8, EPI_ADD_F32>(a, s);
-            case EPI_QKV: return launch_one<128, 128, 2, 2, OPD_Q8, EPI_QKV>(a, s);
-            case EPI_SWIGLU: return launch_one<128, 128, 2, 2, OPD_Q8, EPI_SWIGLU>(a, s);
-            default: break;
-        }
-    }
-    if (opd == OPD_F16 && tile == TILE_128x64) {
-        switch (epi) {
-            case EPI_STORE_F32: return launch_one<128, 64, 2, 2, OPD_F16, EPI_STORE_F32>(a, s);
-            case EPI_ADD_F32: return launch_one<128, 64, 2, 2, OPD_F16, EPI_ADD_F32>(a, s);
-            default: break;
-        }
-    }
+    KVA_GEMM_CASE(OPD_BF16, TILE_256x256, EPI_HEADS, 256, 256, 2, 4)
+    KVA_GEMM_CASE(OPD_Q8, TILE_256x256, EPI_HEADS, 256, 256, 2, 4)
+    KVA_GEMM_CASE(OPD_F16, TILE_256x256, EPI_PARTIAL, 256, 256, 2, 4)
+    KVA_GEMM_CASE(OPD_F16, TILE_256x256, EPI_SWIGLU, 256, 256, 2, 4)
+    KVA_GEMM_CASE(OPD_F16, TILE_256x256, EPI_QKV, 256, 256, 2, 4)
+    KVA_GEMM_CASE(OPD_Q8, TILE_256x256, EPI_PARTIAL, 256, 256, 2, 4)
+    KVA_GEMM_CASE(OPD_Q8, TILE_256x256, EPI_SWIGLU, 256, 256, 2, 4)
+    KVA_GEMM_CASE(OPD_Q8, TILE_256x256, EPI_QKV, 256, 256, 2, 4)
+    KVA_GEMM_CASE(OPD_F16, TILE_128x128, EPI_STORE_F32, 128, 128, 2, 2)
+    KVA_GEMM_CASE(OPD_F16, TILE_128x128, EPI_ADD_F32, 128, 128, 2, 2)
+    KVA_GEMM_CASE(OPD_F16, TILE_128x128, EPI_PARTIAL, 128, 128, 2, 2)
+    KVA_GEMM_CASE(OPD_F16, TILE_128x128, EPI_QKV, 128, 128, 2, 2)
+    KVA_GEMM_CASE(OPD_F16, TILE_128x128, EPI_SWIGLU, 128, 128, 2, 2)
+    KVA_GEMM_CASE(OPD_Q8, TILE_128x128, EPI_STORE_F32, 128, 128, 2, 2)
+    KVA_GEMM_CASE(OPD_Q8, TILE_128x128, EPI_ADD_F32, 128, 128, 2, 2)
+    KVA_GEMM_CASE(OPD_Q8, TILE_128x128, EPI_PARTIAL, 128, 128, 2, 2)
+    KVA_GEMM_CASE(OPD_Q8, TILE_128x128, EPI_QKV, 128, 128, 2, 2)
+    KVA_GEMM_CASE(OPD_Q8, TILE_128x128, EPI_SWIGLU, 128, 128, 2, 2)
+    KVA_GEMM_CASE(OPD_F16, TILE_128x64, EPI_STORE_F32, 128, 64, 2, 2)
+    KVA_GEMM_CASE(OPD_F16, TILE_128x64, EPI_ADD_F32, 128, 64, 2, 2)
+    KVA_GEMM_CASE(OPD_F16, TILE_128x64, EPI_PARTIAL, 128, 64, 2, 2)
     return hipErrorNotSupported;
 }
+#undef KVA_GEMM_CASE
 
 }  // namespace kva

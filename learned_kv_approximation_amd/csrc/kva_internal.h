@@ -28,7 +28,8 @@ enum EpiKind : int {
     EPI_ADD_F32 = 1,    // out_f32[m][n] += acc   (residual stream)
     EPI_QKV = 2,        // n < n_split: out16[m][n] = fp16(acc); else vt[n - n_split][m] = fp16(acc)
     EPI_SWIGLU = 3,     // gate/up interleaved per 32 columns: out16[m][f] = fp16(silu(g) * u)
-    EPI_HEADS = 4       // bias add, scatter to per-head fp32 outputs
+    EPI_HEADS = 4,      // bias add, scatter to per-head fp32 outputs
+    EPI_PARTIAL = 5     // split-K partial: out_f32[split * split_stride + m * ld_f32 + n] = acc
 };
 
 struct EpiArgs {
@@ -62,6 +63,12 @@ struct GemmArgs {
     int32_t M = 0;       // rows of A that are real (stores are masked to M)
     int32_t N = 0;       // columns, a multiple of the tile width (weights are padded)
     int32_t K = 0;       // multiple of 64
+    // Split-K: the K slabs are cut into `splits` consecutive ranges, one per
+    // workgroup; each range's partial product goes to its own buffer
+    // (EPI_PARTIAL).  The split count must depend only on (N, K), never on M,
+    // so a row's result never depends on how many rows a call holds.
+    int32_t splits = 1;
+    int64_t split_stride = 0;
     EpiArgs epi;
 };
 
@@ -80,6 +87,14 @@ enum GemmTile : int { TILE_256x256 = 0, TILE_128x128 = 1, TILE_128x64 = 2 };
 
 hipError_t launch_gemm(GemmOperand opd, GemmTile tile, EpiKind epi, const GemmArgs& args,
                        hipStream_t stream);
+
+// Folds split-K partials into the residual stream and normalises it:
+//   h[r][c] = (add ? h[r][c] : 0) + P_0[r][c] + P_1[r][c] + ... (this order),
+//   out[r][c] = 16-bit(h[r][c] / sqrt(mean_c h[r][c]^2 + eps) * g[c]).
+// P_s = partials + s * pstride, rows of ldp.
+hipError_t launch_fold_rmsnorm(float* h, int64_t ldh, bool add, const float* partials, int32_t splits,
+                               int64_t pstride, int64_t ldp, const float* g, int32_t rows, int32_t cols,
+                               float eps, uint16_t* out, int64_t ldo, bool bf16, hipStream_t stream);
 
 // out[r][c] = 16-bit(x[r][c] / sqrt(mean_c x[r][c]^2 + eps) * g[c]); fp16 or bf16.
 hipError_t launch_rmsnorm_cast(const float* x, int64_t ldx, const float* g, int32_t rows,

@@ -52,6 +52,48 @@ __global__ void __launch_bounds__(256) rmsnorm_cast(const float* __restrict__ x,
     }
 }
 
+// Split-K fold + RMSNorm: the residual update that follows a split GEMM,
+// fused with the norm that reads the updated residual.  The partials are
+// added in a fixed order, so the result is deterministic and independent of
+// how many rows the call has.
+template <bool BF16>
+__global__ void __launch_bounds__(256) fold_rmsnorm(float* __restrict__ h, int64_t ldh, int add,
+                                                    const float* __restrict__ partials, int32_t splits,
+                                                    int64_t pstride, int64_t ldp,
+                                                    const float* __restrict__ gain, int32_t cols, float eps,
+                                                    uint16_t* __restrict__ out, int64_t ldo) {
+    __shared__ float part[4];
+    const int row = blockIdx.x, tid = threadIdx.x;
+    float* hr = h + (int64_t)row * ldh;
+    const float* pr = partials + (int64_t)row * ldp;
+    float ss = 0.0f;
+    for (int c = tid * 4; c < cols; c += 1024) {
+        float4 v = add ? *(const float4*)(hr + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int sp = 0; sp < splits; ++sp) {
+            const float4 p = *(const float4*)(pr + sp * pstride + c);
+            v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
+        }
+        *(float4*)(hr + c) = v;
+        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) part[tid >> 6] = ss;
+    __syncthreads();
+    const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+    const float r = 1.0f / sqrtf(tot / (float)cols + eps);
+    uint16_t* orow = out + (int64_t)row * ldo;
+    for (int c = tid * 4; c < cols; c += 1024) {
+        const float4 v = *(const float4*)(hr + c);     // written above by this thread
+        const float4 gg = *(const float4*)(gain + c);
+        ushort4 o;
+        o.x = to_bits(v.x * r * gg.x, BF16);
+        o.y = to_bits(v.y * r * gg.y, BF16);
+        o.z = to_bits(v.z * r * gg.z, BF16);
+        o.w = to_bits(v.w * r * gg.w, BF16);
+        *(ushort4*)(orow + c) = o;
+    }
+}
+
 // KV-cache write for one full-attention layer ("Qwen3.8-27B-KVA" card, "What
 // the hell?": after projection the engine applies k_norm and RoPE and writes
 // the KV cache; geometry from the "Qwen3.8-27B-MLA" card, "What this is":
@@ -128,6 +170,20 @@ hipError_t launch_rmsnorm_cast(const float* x, int64_t ldx, const float* g, int3
         hipLaunchKernelGGL(rmsnorm_cast<true>, dim3(rows), dim3(256), 0, s, x, ldx, g, cols, eps, out, ldo);
     else
         hipLaunchKernelGGL(rmsnorm_cast<false>, dim3(rows), dim3(256), 0, s, x, ldx, g, cols, eps, out, ldo);
+    return hipGetLastError();
+}
+
+hipError_t launch_fold_rmsnorm(float* h, int64_t ldh, bool add, const float* partials, int32_t splits,
+                               int64_t pstride, int64_t ldp, const float* g, int32_t rows, int32_t cols,
+                               float eps, uint16_t* out, int64_t ldo, bool bf16, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    if (cols % 4 || splits < 1) return hipErrorInvalidValue;
+    if (bf16)
+        hipLaunchKernelGGL(fold_rmsnorm<true>, dim3(rows), dim3(256), 0, s, h, ldh, (int)add, partials, splits,
+                           pstride, ldp, g, cols, eps, out, ldo);
+    else
+        hipLaunchKernelGGL(fold_rmsnorm<false>, dim3(rows), dim3(256), 0, s, h, ldh, (int)add, partials, splits,
+                           pstride, ldp, g, cols, eps, out, ldo);
     return hipGetLastError();
 }
 

@@ -36,6 +36,12 @@ kva_status fail(kva_status s, const char* fmt, ...) {
                         #expr, hipGetErrorString(e_), __FILE__, __LINE__);              \
     } while (0)
 
+// Split count of the GEMMs whose N is the trunk width (input, O, down): with
+// only d = 2560-3072 columns they fill too few workgroups at 1024 tokens.
+// Fixed (it may depend on N and K, never on the token count): a row's
+// reduction order, hence its bits, must not depend on the call's size.
+constexpr int kSplitNarrow = 2;
+
 #define KVA_TRY(expr)                    \
     do {                                 \
         kva_status s_ = (expr);          \
@@ -195,6 +201,7 @@ struct kva_ctx {
     uint16_t* o16 = nullptr;    // [m][hd]     fp16 attention output
     uint16_t* act16 = nullptr;  // [m][F]      fp16 SwiGLU output
     uint16_t* z16 = nullptr;    // [m][d]      final-normed trunk state: bf16 (fp16 for q8_0)
+    float* ws = nullptr;        // [kSplitNarrow][m][d] split-K partials of the N = d GEMMs
 
     kva_stats stats{};
 
@@ -462,6 +469,7 @@ kva_status create_impl(const kva_config* cfg, const kva_weights* w, int device, 
     HIP_TRY(ctx->alloc(&ctx->o16, (size_t)m * hd * 2, false));
     HIP_TRY(ctx->alloc(&ctx->act16, (size_t)m * F * 2, false));
     HIP_TRY(ctx->alloc(&ctx->z16, (size_t)m * d * 2, false));
+    HIP_TRY(ctx->alloc(&ctx->ws, (size_t)kSplitNarrow * m * d * 4, false));
     // Scratch rows past n_tokens feed MFMA rows whose results are dropped; zero
     // them once so they always hold finite values.
     HIP_TRY(hipMemset(ctx->u16, 0, (size_t)m * n_in * 2));
@@ -474,6 +482,18 @@ kva_status create_impl(const kva_config* cfg, const kva_weights* w, int device, 
     HIP_TRY(hipMemset(ctx->z16, 0, (size_t)m * d * 2));
     HIP_TRY(hipDeviceSynchronize());
     return KVA_OK;
+}
+
+// Tile for an M x N GEMM with `splits` K-ranges: the one with the fewer
+// estimated rounds over the 256 CUs, a 256x256 tile doing the work of four
+// 128x128 tiles in about 1/1.3 of their time.  Tile shape never changes a
+// result's bits (same K order per output).
+GemmTile pick_tile(int64_t M, int64_t N, int splits) {
+    const int64_t t128 = ((M + 127) / 128) * (N / 128) * splits;
+    const int64_t t256 = ((M + 255) / 256) * (N / 256) * splits;
+    const double c128 = (double)((t128 + 255) / 256);
+    const double c256 = (double)((t256 + 255) / 256) * 4.0 / 1.3;
+    return (N % 256 == 0 && c256 < c128) ? TILE_256x256 : TILE_128x128;
 }
 
 void set_b(GemmArgs& g, const kva_ctx::DevW& w, int64_t K) {
@@ -558,19 +578,30 @@ kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n, float* co
     const int64_t hd = (int64_t)c.n_heads * c.head_dim;
     // trunk operand type and the tile of the narrow (N = d) GEMMs
     const GemmOperand opd = ctx->q8 ? OPD_Q8 : OPD_F16;
-    const GemmTile small_n = ctx->q8 ? TILE_128x128 : TILE_128x64;
+    const int64_t pstride = ctx->m_alloc * d;   // between split-K partial buffers
+    // The narrow GEMMs (N = d: input, O, down) write kSplitNarrow partials to
+    // ws; the next norm folds them into h in a fixed order.
+    auto narrow = [&](const uint16_t* A, int64_t K, const kva_ctx::DevW& W, int stage) -> kva_status {
+        GemmArgs g;
+        g.A = A; g.lda = K; set_b(g, W, K);
+        g.M = n; g.N = (int32_t)round_up(d, kColPad); g.K = (int32_t)K;
+        g.splits = kSplitNarrow; g.split_stride = pstride;
+        g.epi.out_f32 = ctx->ws; g.epi.ld_f32 = d; g.epi.n_real = (int32_t)d;
+        STAGE(stage, launch_gemm(opd, pick_tile(n, g.N, g.splits), EPI_PARTIAL, g, s));
+        return KVA_OK;
+    };
+    auto fold = [&](bool add, const float* gain, uint16_t* out, bool bf16) -> kva_status {
+        STAGE(KVA_STAGE_NORM, launch_fold_rmsnorm(ctx->h, d, add, ctx->ws, kSplitNarrow, pstride, d, gain, n,
+                                                  (int32_t)d, c.eps, out, d, bf16, s));
+        return KVA_OK;
+    };
 
     STAGE(KVA_STAGE_NORM, launch_rmsnorm_cast(x, n_in, ctx->g_in, n, (int32_t)n_in, c.eps, ctx->u16, n_in, false, s));
-    {
-        GemmArgs g;
-        g.A = ctx->u16; g.lda = n_in; set_b(g, ctx->w_in, n_in);
-        g.M = n; g.N = (int32_t)round_up(d, kColPad); g.K = (int32_t)n_in;
-        g.epi.out_f32 = ctx->h; g.epi.ld_f32 = d; g.epi.n_real = (int32_t)d;
-        STAGE(KVA_STAGE_GEMM_IN, launch_gemm(opd, small_n, EPI_STORE_F32, g, s));
-    }
+    KVA_TRY(narrow(ctx->u16, n_in, ctx->w_in, KVA_STAGE_GEMM_IN));
     for (int b = 0; b < c.n_blocks; ++b) {
         const kva_ctx::Blk& B = ctx->blk[b];
-        STAGE(KVA_STAGE_NORM, launch_rmsnorm_cast(ctx->h, d, B.g_attn, n, (int32_t)d, c.eps, ctx->a16, d, false, s));
+        // h = (b == 0 ? 0 : h) + input/down partials; a = attn_norm(h)
+        KVA_TRY(fold(b > 0, B.g_attn, ctx->a16, false));
         {
             GemmArgs g;
             g.A = ctx->a16; g.lda = d; set_b(g, B.wqkv, d);
@@ -578,34 +609,22 @@ kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n, float* co
             g.epi.out16 = ctx->qk16; g.epi.ld16 = 2 * hd;
             g.epi.vt = ctx->vt16; g.epi.ld_vt = ctx->m_alloc; g.epi.n_split = (int32_t)(2 * hd);
             g.epi.n_real = (int32_t)(3 * hd);
-            STAGE(KVA_STAGE_GEMM_QKV, launch_gemm(opd, TILE_128x128, EPI_QKV, g, s));
+            STAGE(KVA_STAGE_GEMM_QKV, launch_gemm(opd, pick_tile(n, g.N, 1), EPI_QKV, g, s));
         }
         STAGE(KVA_STAGE_ATTN, launch_attention(ctx->qk16, 2 * hd, (int32_t)hd, ctx->vt16, ctx->m_alloc, ctx->o16, hd, n,
                                 c.n_heads, c.attn_block, s));
-        {
-            GemmArgs g;
-            g.A = ctx->o16; g.lda = hd; set_b(g, B.wo, hd);
-            g.M = n; g.N = (int32_t)round_up(d, kColPad); g.K = (int32_t)hd;
-            g.epi.out_f32 = ctx->h; g.epi.ld_f32 = d; g.epi.n_real = (int32_t)d;
-            STAGE(KVA_STAGE_GEMM_O, launch_gemm(opd, small_n, EPI_ADD_F32, g, s));
-        }
-        STAGE(KVA_STAGE_NORM, launch_rmsnorm_cast(ctx->h, d, B.g_ffn, n, (int32_t)d, c.eps, ctx->a16, d, false, s));
+        KVA_TRY(narrow(ctx->o16, hd, B.wo, KVA_STAGE_GEMM_O));
+        KVA_TRY(fold(true, B.g_ffn, ctx->a16, false));           // h += O partials; a = ffn_norm(h)
         {
             GemmArgs g;
             g.A = ctx->a16; g.lda = d; set_b(g, B.wgu, d);
             g.M = n; g.N = (int32_t)round_up(2 * F, kColPad); g.K = (int32_t)d;
             g.epi.out16 = ctx->act16; g.epi.ld16 = F; g.epi.n_real = (int32_t)(2 * F);
-            STAGE(KVA_STAGE_GEMM_GATEUP, launch_gemm(opd, TILE_128x128, EPI_SWIGLU, g, s));
+            STAGE(KVA_STAGE_GEMM_GATEUP, launch_gemm(opd, pick_tile(n, g.N, 1), EPI_SWIGLU, g, s));
         }
-        {
-            GemmArgs g;
-            g.A = ctx->act16; g.lda = F; set_b(g, B.wd, F);
-            g.M = n; g.N = (int32_t)round_up(d, kColPad); g.K = (int32_t)F;
-            g.epi.out_f32 = ctx->h; g.epi.ld_f32 = d; g.epi.n_real = (int32_t)d;
-            STAGE(KVA_STAGE_GEMM_DOWN, launch_gemm(opd, small_n, EPI_ADD_F32, g, s));
-        }
+        KVA_TRY(narrow(ctx->act16, F, B.wd, KVA_STAGE_GEMM_DOWN));
     }
-    STAGE(KVA_STAGE_NORM, launch_rmsnorm_cast(ctx->h, d, ctx->g_out, n, (int32_t)d, c.eps, ctx->z16, d, !ctx->q8, s));
+    KVA_TRY(fold(true, ctx->g_out, ctx->z16, !ctx->q8));           // h += down partials; z = out_norm(h)
     {
         GemmArgs g;
         g.A = ctx->z16; g.lda = d; set_b(g, ctx->w_heads, d);
