@@ -5,9 +5,11 @@
 // and the r2/r3 table: heads of 128, causal within 1024-token blocks).  For
 // query i of head h in block [s, e):  o_i = sum_{s<=j<=i} softmax_j(q_i.k_j/sqrt(128)) v_j.
 //
-// One workgroup = 2 waves = 64 queries of one head; each wave owns 32
-// queries.  K and V of 64 keys at a time are staged in LDS (double-buffered,
-// the next tile is fetched into registers while the current one is used).
+// One workgroup = 64 queries of one head, its key range split between
+// groups of 2 waves (32 queries per wave); each group stages K and V of 64
+// keys at a time in LDS (the next tile is fetched into registers while the
+// current one is used) and the groups' partial softmax states are merged at
+// the end.
 // Per key tile a wave computes S^T = K Q^T with 32x32x16 MFMAs, so each lane
 // holds the scores of ONE query (column lane%32) for 32 keys: the online
 // softmax (running max m, running sum l, fp32) is per lane plus one exchange
@@ -31,7 +33,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int HD = 128;     // head dim
 constexpr int QT = 64;      // queries per workgroup
 constexpr int KT = 64;      // keys per tile
-constexpr int kThreads = 128;
+constexpr int kKeySplit = 2;   // key-range groups per workgroup
 
 __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
@@ -49,22 +51,43 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
            ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
 }
 
-__global__ void __launch_bounds__(kThreads) attn_fwd(const uint16_t* __restrict__ qk, int64_t ld_qk,
-                                                      int32_t k_off, const uint16_t* __restrict__ vt,
-                                                      int64_t ld_vt, uint16_t* __restrict__ o,
-                                                      int64_t ld_o, int32_t n, int32_t attn_block) {
-    __shared__ __attribute__((aligned(16))) uint16_t sK[2][KT * HD];   // [rho][128], chunk-swizzled
-    __shared__ __attribute__((aligned(16))) uint16_t sV[2][HD * KT];   // [d][64],   chunk-swizzled
+// One workgroup = 64 queries of one head, KS groups of 2 waves.  Group g
+// takes the key tiles t = g, g + KS, g + 2 KS, ... of the query tile's range,
+// so the longest chain of tiles a wave walks is ceil(tiles / KS).  Within a
+// group, wave w % 2 owns queries 32 (w % 2) .. +31.  Each group stages its
+// own K and V^T tile in LDS (prefetched into registers one tile ahead).  At
+// the end the groups' running (max, sum, O) are merged through LDS:
+//   m = max_g m_g,  l = sum_g l_g 2^(m_g - m),  O = sum_g O_g 2^(m_g - m) / l.
+template <int KS>
+__global__ void __launch_bounds__(128 * KS) attn_fwd(const uint16_t* __restrict__ qk, int64_t ld_qk,
+                                                     int32_t k_off, const uint16_t* __restrict__ vt,
+                                                     int64_t ld_vt, uint16_t* __restrict__ o,
+                                                     int64_t ld_o, int32_t n, int32_t n_heads,
+                                                     int32_t attn_block) {
+    constexpr int TILE = KT * HD;                       // elements of one K (or V^T) tile
+    __shared__ __attribute__((aligned(16))) uint16_t smem[KS * 2 * TILE];   // per group: K | V^T
 
-    const int h = blockIdx.y;
-    const int qt = gridDim.x - 1 - blockIdx.x;        // longest key ranges first
+    // Work items in descending order of key range over ALL heads and blocks:
+    // the r-th round of n_heads * n_blocks items holds local q-tile tpb-1-r.
+    const int tpb = attn_block / QT;                  // q-tiles per attention block
+    const int nblk = (n + attn_block - 1) / attn_block;
+    const int per_round = n_heads * nblk;
+    const int L = blockIdx.x;
+    const int lt = tpb - 1 - L / per_round;
+    const int h = (L % per_round) % n_heads;
+    const int qt = ((L % per_round) / n_heads) * tpb + lt;
     const int q0 = qt * QT;
+    if (q0 >= n) return;                              // past the ragged last block
     const int bs = (q0 / attn_block) * attn_block;    // start of this block
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int grp = wave >> 1, gtid = tid & 127;      // key-range group, thread within the group
     const int g = lane >> 5;
-    const int myq = q0 + wave * 32 + (lane & 31);
+    const int myq = q0 + (wave & 1) * 32 + (lane & 31);
     const int kv_end = min(q0 + QT, n);
     const int ntiles = (kv_end - bs + KT - 1) / KT;
+    const int iters = (ntiles + KS - 1) / KS;          // same for every wave (barriers)
+    uint16_t* sK = smem + grp * 2 * TILE;              // [rho][128], chunk-swizzled
+    uint16_t* sV = sK + TILE;                          // [d][64],   chunk-swizzled
 
     // Q fragments (B operand of S^T = K Q^T): 8 consecutive dims per lane per 16-dim step
     u32x4 qf[HD / 16];
@@ -74,23 +97,23 @@ __global__ void __launch_bounds__(kThreads) attn_fwd(const uint16_t* __restrict_
         for (int ks = 0; ks < HD / 16; ++ks) qf[ks] = *(const u32x4*)(qr + ks * 16);
     }
 
-    // tile loader: 1024 K chunks and 1024 V^T chunks of 16 bytes, 8 of each per thread
+    // tile loader of a group: 1024 K chunks and 1024 V^T chunks of 16 bytes, 8 of each per thread
     u32x4 rk[8], rv[8];
     auto gload = [&](int kv0) {
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
-            const int id = tid + p * kThreads;
+            const int id = gtid + p * 128;
             const int rho = id >> 4, c = id & 15;
             const int kv = min(kv0 + perm(rho), n - 1);
             rk[p] = *(const u32x4*)(qk + (int64_t)kv * ld_qk + k_off + h * HD + c * 8);
         }
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
-            const int id = tid + p * kThreads;
+            const int id = gtid + p * 128;
             const int d = id >> 3, c = id & 7;
             const int t0 = kv0 + c * 8;
             u32x4 v = *(const u32x4*)(vt + (int64_t)(h * HD + d) * ld_vt + t0);
-            if (t0 + 8 > n) {           // zero V of keys past the end (0 * V must stay 0)
+            if (kv0 + KT > n && t0 + 8 > n) {   // zero V of keys past the end (0 * V must stay 0)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     if (t0 + 2 * e >= n) v[e] &= 0xFFFF0000u;
@@ -100,19 +123,19 @@ __global__ void __launch_bounds__(kThreads) attn_fwd(const uint16_t* __restrict_
             rv[p] = v;
         }
     };
-    auto sstore = [&](int buf) {
+    auto sstore = [&]() {
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
-            const int id = tid + p * kThreads;
+            const int id = gtid + p * 128;
             const int rho = id >> 4, c = id & 15;
-            *(u32x4*)(&sK[buf][rho * HD + ((c ^ (rho & 15)) << 3)]) = rk[p];
+            *(u32x4*)(&sK[rho * HD + ((c ^ (rho & 15)) << 3)]) = rk[p];
         }
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
-            const int id = tid + p * kThreads;
+            const int id = gtid + p * 128;
             const int d = id >> 3, c = id & 7;
             const int sw = (d & 7) ^ ((d >> 3) & 1);
-            *(u32x4*)(&sV[buf][d * KT + ((c ^ sw) << 3)]) = rv[p];
+            *(u32x4*)(&sV[d * KT + ((c ^ sw) << 3)]) = rv[p];
         }
     };
 
@@ -124,13 +147,39 @@ __global__ void __launch_bounds__(kThreads) attn_fwd(const uint16_t* __restrict_
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
 
-    gload(bs);
-    sstore(0);
-    __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
+    if (grp < ntiles) gload(bs + grp * KT);
+    for (int it = 0; it < iters; ++it) {
+        const int t = grp + it * KS;                   // this group's tile, if t < ntiles
+        const bool have = t < ntiles;
+        __syncthreads();                               // the previous tile's LDS reads are done
+        if (have) sstore();
+        __syncthreads();
+        if (t + KS < ntiles) gload(bs + (t + KS) * KT);
+        if (!have) continue;
         const int kv0 = bs + t * KT;
-        if (t + 1 < ntiles) gload(kv0 + KT);
+
+        // All K and V^T fragments of the tile are read from LDS up front (V^T
+        // lands while the softmax runs), so the MFMAs never wait on LDS one
+        // fragment at a time.
+        u32x4 kf[2][HD / 16], vf[4][4];
+#pragma unroll
+        for (int ks = 0; ks < HD / 16; ++ks)
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const int rho = st * 32 + (lane & 31);
+                const int c = ks * 2 + g;
+                kf[st][ks] = *(const u32x4*)(&sK[rho * HD + ((c ^ (rho & 15)) << 3)]);
+            }
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            const int d = dt * 32 + (lane & 31);
+            const int sw = (d & 7) ^ ((d >> 3) & 1);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int c = 2 * m + g;
+                vf[dt][m] = *(const u32x4*)(&sV[d * KT + ((c ^ sw) << 3)]);
+            }
+        }
 
         // S^T[rho][q] for rho in [0,64): two 32-key MFMA tiles
         f32x16 s[2];
@@ -139,32 +188,44 @@ __global__ void __launch_bounds__(kThreads) attn_fwd(const uint16_t* __restrict_
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[st][r] = 0.0f;
 #pragma unroll
-        for (int ks = 0; ks < HD / 16; ++ks) {
+        for (int ks = 0; ks < HD / 16; ++ks)
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                const int rho = st * 32 + (lane & 31);
-                const int c = ks * 2 + g;
-                const u32x4 a = *(const u32x4*)(&sK[buf][rho * HD + ((c ^ (rho & 15)) << 3)]);
-                s[st] = mfma(a, qf[ks], s[st]);
-            }
-        }
+            for (int st = 0; st < 2; ++st) s[st] = mfma(kf[st][ks], qf[ks], s[st]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (HD / 16), 0);   // K fragment reads
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);              // V^T fragment reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * (HD / 16), 0);   // S MFMAs
 
         // mask, scale, running max.  Element (st, r) is LDS row
-        // rho = 32 st + 8 (r/4) + 4 g + r%4, i.e. key kv0 + perm(rho).
+        // rho = 32 st + 8 (r/4) + 4 g + r%4, i.e. key kv0 + perm(rho).  Only
+        // the diagonal tile and a tile reaching past n_tokens need the mask;
+        // the test is uniform across the wave.
         float mx = m_i;
+        const int wq0 = q0 + (wave & 1) * 32;          // lowest query of this wave
+        if (kv0 + KT - 1 > wq0 || kv0 + KT > n) {
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+            for (int st = 0; st < 2; ++st)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int rho = st * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                const int kv = kv0 + perm(rho);
-                float v = s[st][r] * scale;
-                if (kv > myq || kv >= n) v = -INFINITY;
-                s[st][r] = v;
-                mx = fmaxf(mx, v);
-            }
+                for (int r = 0; r < 16; ++r) {
+                    const int rho = st * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                    const int kv = kv0 + perm(rho);
+                    float v = s[st][r] * scale;
+                    if (kv > myq || kv >= n) v = -INFINITY;
+                    s[st][r] = v;
+                    mx = fmaxf(mx, v);
+                }
+        } else {
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    s[st][r] *= scale;
+                    mx = fmaxf(mx, s[st][r]);
+                }
+        }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float alpha = exp2f(m_i - mx);
+        // exponents are <= 0 here (and -inf for masked keys): the hardware
+        // exp2 is exact enough and flushing underflow to 0 is what softmax wants
+        const float alpha = __builtin_amdgcn_exp2f(m_i - mx);
         m_i = mx;
         l_i *= alpha;
 #pragma unroll
@@ -180,7 +241,7 @@ __global__ void __launch_bounds__(kThreads) attn_fwd(const uint16_t* __restrict_
             float p[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                p[e] = exp2f(s[m >> 1][8 * (m & 1) + e] - mx);
+                p[e] = __builtin_amdgcn_exp2f(s[m >> 1][8 * (m & 1) + e] - mx);
                 l_i += p[e];
             }
             pf[m][0] = pack_f16(p[0], p[1]);
@@ -191,23 +252,50 @@ __global__ void __launch_bounds__(kThreads) attn_fwd(const uint16_t* __restrict_
 
         // O^T[d][q] += V^T[d][kv] P^T[kv][q]
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-            const int d = dt * 32 + (lane & 31);
-            const int sw = (d & 7) ^ ((d >> 3) & 1);
+        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int c = 2 * m + g;
-                const u32x4 a = *(const u32x4*)(&sV[buf][d * KT + ((c ^ sw) << 3)]);
-                oacc[dt] = mfma(a, pf[m], oacc[dt]);
-            }
-        }
-
-        if (t + 1 < ntiles) sstore(buf ^ 1);
-        __syncthreads();
+            for (int m = 0; m < 4; ++m) oacc[dt] = mfma(vf[dt][m], pf[m], oacc[dt]);
     }
 
-    const float l_tot = l_i + __shfl_xor(l_i, 32);
-    const float inv = 1.0f / l_tot;
+    // ---- merge the KS groups (group 0 writes the output)
+    l_i += __shfl_xor(l_i, 32);                       // both halves of the keys of this query
+    if constexpr (KS > 1) {
+        float* xo = reinterpret_cast<float*>(smem);    // [KS-1][2 waves][64 + 64 + 64*64] floats
+        constexpr int REC = 64 * 66;
+        __syncthreads();                               // all LDS tile reads are done
+        if (grp > 0) {
+            float* rec = xo + ((grp - 1) * 2 + (wave & 1)) * REC;
+            rec[lane] = m_i;
+            rec[64 + lane] = l_i;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) rec[128 + (dt * 16 + r) * 64 + lane] = oacc[dt][r];
+        }
+        __syncthreads();
+        if (grp > 0) return;
+        float mt = m_i;
+#pragma unroll
+        for (int gg = 1; gg < KS; ++gg) mt = fmaxf(mt, xo[((gg - 1) * 2 + (wave & 1)) * REC + lane]);
+        const float a0 = __builtin_amdgcn_exp2f(m_i - mt);
+        l_i *= a0;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[dt][r] *= a0;
+#pragma unroll
+        for (int gg = 1; gg < KS; ++gg) {
+            const float* rec = xo + ((gg - 1) * 2 + (wave & 1)) * REC;
+            const float ag = __builtin_amdgcn_exp2f(rec[lane] - mt);   // 0 for a group that saw no key
+            l_i += rec[64 + lane] * ag;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[dt][r] += rec[128 + (dt * 16 + r) * 64 + lane] * ag;
+        }
+    }
+
+    const float inv = 1.0f / l_i;
     if (myq < n) {
         uint16_t* orow = o + (int64_t)myq * ld_o + h * HD;
 #pragma unroll
@@ -230,9 +318,10 @@ hipError_t launch_attention(const uint16_t* qk, int64_t ld_qk, int32_t k_off, co
                             int32_t attn_block, hipStream_t s) {
     if (n <= 0) return hipSuccess;
     if (attn_block % QT) return hipErrorInvalidValue;
-    dim3 grid((n + QT - 1) / QT, n_heads);
-    hipLaunchKernelGGL(attn_fwd, grid, dim3(kThreads), 0, s, qk, ld_qk, k_off, vt, ld_vt, o, ld_o, n,
-                       attn_block);
+    const int nblk = (n + attn_block - 1) / attn_block;
+    const dim3 grid(n_heads * nblk * (attn_block / QT));
+    hipLaunchKernelGGL(attn_fwd<kKeySplit>, grid, dim3(128 * kKeySplit), 0, s, qk, ld_qk, k_off, vt, ld_vt, o,
+                       ld_o, n, n_heads, attn_block);
     return hipGetLastError();
 }
 
