@@ -13,7 +13,9 @@
 //    MFMAs on the current one (one barrier a slab).
 //  - LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk
 //    c ^ swz(r), so the 16 rows one ds_read_b128 phase touches land on
-//    distinct banks.
+//    distinct banks.  Weights are repacked at create into the same layout,
+//    slab by slab (kWeightTileRows rows x 64 K-values contiguous), so every
+//    weight DMA instruction reads one contiguous kilobyte.
 //  - Workgroup ids are remapped so that the tiles of one weight strip (all
 //    M-tiles of an N-tile) run back to back on the same XCD and share its L2:
 //    the hardware deals workgroups to the 8 XCDs round-robin.
@@ -33,6 +35,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int BK = 64;          // K per slab (16-bit elements): 128-byte LDS rows
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+static_assert(kWeightTileRows % 256 == 0, "weight tiles must hold whole GEMM tiles");
 
 template <bool BF16>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
@@ -94,7 +97,12 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_nt(GemmArgs g) {
 
     // rows >= M of A are padding rows of the activation scratch: loaded, never stored
     const uint16_t* Ab = g.A + (int64_t)tm * BM * g.lda;
-    const uint16_t* Bb = g.B + (int64_t)tn * BN * g.ldb;
+    // 16-bit weights are stored tiled (see kWeightTileRows): the rows of this
+    // tile sit at row offset r0 of weight tile nb, and each 64-wide K slab of
+    // a weight tile is one contiguous, already swizzled block
+    const int nk_all = g.K / BK;
+    const int nb = (tn * BN) / kWeightTileRows, r0 = (tn * BN) % kWeightTileRows;
+    const uint16_t* Bb = g.B + ((int64_t)nb * nk_all * kWeightTileRows + r0) * BK;
     int offa[AI], offb[BI > 0 ? BI : 1];
     {
         const int rr = lane >> 3, pc = lane & 7;
@@ -104,10 +112,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_nt(GemmArgs g) {
             offa[i] = row * (int)g.lda + ((pc ^ swz(row)) << 3);
         }
 #pragma unroll
-        for (int i = 0; i < BI; ++i) {
-            const int row = (i * NW + wave) * 8 + rr;
-            offb[i] = row * (int)g.ldb + ((pc ^ swz(row)) << 3);
-        }
+        for (int i = 0; i < BI; ++i) offb[i] = (i * NW + wave) * 8 * BK + lane * 8;   // 1 KB, contiguous
     }
     auto issue = [&](int kt, int buf) {
         uint16_t* sa = smem + buf * STAGE;
@@ -118,7 +123,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_nt(GemmArgs g) {
                                              (lds_ptr_t)(sa + (i * NW + wave) * 8 * BK), 16, 0, 0);
 #pragma unroll
         for (int i = 0; i < BI; ++i)
-            __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Bb + offb[i] + kt * BK),
+            __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Bb + (int64_t)kt * kWeightTileRows * BK + offb[i]),
                                              (lds_ptr_t)(sb + (i * NW + wave) * 8 * BK), 16, 0, 0);
     };
 
@@ -168,7 +173,6 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_nt(GemmArgs g) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const int nk_all = g.K / BK;
     const int kb = split * nk_all / S;                 // this split's slabs: [kb, kb + nk)
     const int nk = (split + 1) * nk_all / S - kb;
     const int frow = lane & 31, fk = lane >> 5;

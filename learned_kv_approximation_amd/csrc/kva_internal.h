@@ -17,6 +17,18 @@ constexpr int kHeadTileN = 256;
 constexpr int kRowPad = 256;
 // Weight rows are padded with zeros to a multiple of this.
 constexpr int kColPad = 256;
+// 16-bit weights [rows][K] are stored tiled: for each group of
+// kWeightTileRows rows and each 64-wide K slab, one contiguous block of
+// kWeightTileRows x 64 values, row after row; within a row the 16-byte chunk
+// c (K-values 8c..8c+7) sits at chunk c ^ ((r & 7) ^ ((r >> 3) & 1)).  This is
+// exactly the LDS layout of a GEMM B tile.
+constexpr int kWeightTileRows = 256;
+inline int64_t weight_tiled_index(int64_t row, int64_t k, int64_t K) {
+    const int64_t nb = row / kWeightTileRows, r = row % kWeightTileRows, kt = k / 64;
+    const int64_t c = (k % 64) / 8, e = k % 8;
+    const int64_t sw = (r & 7) ^ ((r >> 3) & 1);
+    return ((nb * (K / 64) + kt) * kWeightTileRows + r) * 64 + ((c ^ sw) * 8) + e;
+}
 
 struct HeadOut {
     float* ptr[kMaxHeads];

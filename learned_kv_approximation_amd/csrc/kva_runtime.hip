@@ -162,8 +162,9 @@ struct kva_ctx {
     std::vector<void*> allocs;
     uint64_t weight_bytes = 0, scratch_bytes = 0;
 
-    // weights (device).  A weight is either 16-bit values w16[rows][K] (fp16
-    // trunk, bf16 heads) or, for q8_0, codes q[rows][K] + fp16 scales sc[rows][K/32].
+    // weights (device).  A weight is either 16-bit values w16 (fp16
+    // trunk, bf16 heads; tiled, see weight_tiled_index) or, for q8_0, codes
+    // q[rows][K] + fp16 scales sc[rows][K/32].
     struct DevW {
         uint16_t* w16 = nullptr;
         int8_t* q = nullptr;
@@ -305,7 +306,8 @@ struct RowSrc {
 enum PackTarget { PACK_F16 = 0, PACK_BF16 = 1, PACK_Q8 = 2 };
 
 // Packs rows (each K wide, stored in `dtype`) into the compute layout and
-// uploads it: fp16 or bf16 values [rows][K], or for q8_0 an int8 code plane
+// uploads it: fp16 or bf16 values in the tiled layout of weight_tiled_index,
+// or for q8_0 an int8 code plane
 // [rows][K] plus an fp16 scale plane [rows][K/32] (the 34-byte blocks split
 // losslessly into aligned planes).
 kva_status pack_weight(kva_ctx* ctx, int dtype, int64_t K, const std::vector<RowSrc>& rows,
@@ -348,8 +350,13 @@ kva_status pack_weight(kva_ctx* ctx, int dtype, int64_t K, const std::vector<Row
         }
     }
     if (ovf) return fail(KVA_ERR_RANGE, "weight %s has values outside the fp16 range", name);
-    HIP_TRY(ctx->alloc(&out->w16, w.size() * 2, true));
-    return upload(ctx, out->w16, w.data(), w.size() * 2);
+    if (n % kWeightTileRows || K % 64) return fail(KVA_ERR_SHAPE, "weight %s: bad padding", name);
+    std::vector<uint16_t> t(w.size());
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t k = 0; k < K; k += 8)    // 8 consecutive K-values stay together
+            std::memcpy(&t[(size_t)weight_tiled_index(r, k, K)], &w[(size_t)(r * K + k)], 16);
+    HIP_TRY(ctx->alloc(&out->w16, t.size() * 2, true));
+    return upload(ctx, out->w16, t.data(), t.size() * 2);
 }
 
 // Rows [0, n) of one tensor, then zero rows up to a multiple of kColPad.
