@@ -290,6 +290,49 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_nt(GemmArgs g) {
     } else if constexpr (EPI == EPI_HEADS) {
         static_assert(BN == kHeadTileN, "head packing assumes one head per column tile");
         const int th = e.tile_head[tn];
+        // A whole-head tile whose destination rows are 16-byte aligned goes out
+        // through LDS: each half of the tile (128 x 256 fp32 = the 128 KB of
+        // LDS) is transposed there and written as full 1 KB rows with 16-byte
+        // stores (a quarter of the store instructions of the direct path).
+        if constexpr (BM == 256 && WGM == 2 && WGN == 4) {
+            if (th >= 0 && (e.heads.ld[th] % 4) == 0 && ((uintptr_t)e.heads.ptr[th] % 16) == 0) {
+                float* lds = reinterpret_cast<float*>(smem);       // [128][256], rows rotated by 32 every 4 rows
+                float* dst0 = e.heads.ptr[th] + e.tile_col0[tn];
+                const int64_t ld = e.heads.ld[th];
+                const float* bias = e.bias ? e.bias + tn * BN : nullptr;
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    if (wm == half) {
+#pragma unroll
+                        for (int j = 0; j < NI; ++j)
+#pragma unroll
+                            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                                for (int r = 0; r < 16; ++r) {
+                                    const int lr = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                                    const int lc = wn * WN + j * 32 + (lane & 31);
+                                    lds[lr * BN + ((lc + 32 * ((lr >> 2) & 1)) & (BN - 1))] = acc[i][j][r];
+                                }
+                    }
+                    __syncthreads();
+                    // 128 rows x 64 chunks of 4 columns; one wave stores one full row
+#pragma unroll
+                    for (int q = 0; q < (128 * 64) / (64 * NW); ++q) {
+                        const int id = q * 64 * NW + tid;
+                        const int lr = id >> 6, c4 = (id & 63) * 4;
+                        const int row = tm * BM + half * 128 + lr;
+                        float4 v = *(const float4*)(lds + lr * BN + ((c4 + 32 * ((lr >> 2) & 1)) & (BN - 1)));
+                        if (bias) {
+                            const float4 b = *(const float4*)(bias + c4);
+                            v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
+                        }
+                        if (row < g.M) *(float4*)(dst0 + (int64_t)row * ld + c4) = v;
+                    }
+                    __syncthreads();
+                }
+                return;
+            }
+        }
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
             const int col = col_base + j * 32;
