@@ -23,6 +23,8 @@
 //    fp16 Q|K plus transposed V, SwiGLU, bias + per-head scatter).
 #include "kva_internal.h"
 
+#include <type_traits>
+
 namespace kva {
 namespace {
 
@@ -59,6 +61,161 @@ typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 // Output element (lane, r) of a 32x32 MFMA tile sits at
 //   row = 8*(r/4) + 4*(lane/32) + r%4,  col = lane%32.
 //
+// Fused epilogue of a BM x BN tile held as 32x32 MFMA accumulators by a
+// WGM x WGN grid of waves (acc[i][j]: the wave's i-th 32-row, j-th 32-column
+// block).  `smem` (at least 128 KB, free when called) is used by the head
+// epilogue to turn whole-head tiles into full-row stores.
+template <int BM, int BN, int WGM, int WGN, int EPI, int MI, int NI>
+__device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[MI][NI], int tm, int tn, int split,
+                                         uint16_t* smem) {
+    constexpr int NW = WGM * WGN;
+    constexpr int WM = BM / WGM, WN = BN / WGN;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int row_base = tm * BM + wm * WM + 4 * (lane >> 5);
+    const int col_base = tn * BN + wn * WN + (lane & 31);
+    const EpiArgs& e = g.epi;
+
+    if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_ADD_F32 || EPI == EPI_PARTIAL) {
+        float* out = e.out_f32 + (EPI == EPI_PARTIAL ? (int64_t)split * g.split_stride : 0);
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int col = col_base + j * 32;
+            if (col >= e.n_real) continue;
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
+                    if (row < g.M) {
+                        float* p = out + (int64_t)row * e.ld_f32 + col;
+                        if constexpr (EPI == EPI_ADD_F32) *p += acc[i][j][r];
+                        else *p = acc[i][j][r];
+                    }
+                }
+        }
+    } else if constexpr (EPI == EPI_QKV) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int col = col_base + j * 32;
+            if (col >= e.n_real) continue;
+            if (col < e.n_split) {
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
+                        if (row < g.M) e.out16[(int64_t)row * e.ld16 + col] = to_f16_bits(acc[i][j][r]);
+                    }
+            } else {
+                // V^T: the lane's 4 consecutive rows are 4 consecutive tokens
+                uint16_t* vt = e.vt + (int64_t)(col - e.n_split) * e.ld_vt;
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int row = row_base + i * 32 + 8 * q;
+                        if (row < g.M) {
+                            u32x2 pk;
+                            pk[0] = (uint32_t)to_f16_bits(acc[i][j][4 * q + 0]) |
+                                    ((uint32_t)to_f16_bits(acc[i][j][4 * q + 1]) << 16);
+                            pk[1] = (uint32_t)to_f16_bits(acc[i][j][4 * q + 2]) |
+                                    ((uint32_t)to_f16_bits(acc[i][j][4 * q + 3]) << 16);
+                            *(u32x2*)(vt + row) = pk;
+                        }
+                    }
+            }
+        }
+    } else if constexpr (EPI == EPI_SWIGLU) {
+        static_assert(NI % 2 == 0, "gate/up pairs need an even number of 32-column tiles");
+#pragma unroll
+        for (int j = 0; j < NI; j += 2) {
+            const int f = (tn * BN + wn * WN + j * 32) / 2 + (lane & 31);
+            if (2 * f >= e.n_real) continue;
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
+                    if (row < g.M)
+                        e.out16[(int64_t)row * e.ld16 + f] =
+                            to_f16_bits(silu(acc[i][j][r]) * acc[i][j + 1][r]);
+                }
+        }
+    } else if constexpr (EPI == EPI_HEADS) {
+        static_assert(BN == kHeadTileN, "head packing assumes one head per column tile");
+        const int th = e.tile_head[tn];
+        // A whole-head tile whose destination rows are 16-byte aligned goes out
+        // through LDS: each half of the tile (128 x 256 fp32 = the 128 KB of
+        // LDS) is transposed there and written as full 1 KB rows with 16-byte
+        // stores (a quarter of the store instructions of the direct path).
+        if constexpr (BM == 256 && WGM == 2 && WGN == 4) {
+            if (th >= 0 && (e.heads.ld[th] % 4) == 0 && ((uintptr_t)e.heads.ptr[th] % 16) == 0) {
+                float* lds = reinterpret_cast<float*>(smem);       // [128][256], rows rotated by 32 every 4 rows
+                float* dst0 = e.heads.ptr[th] + e.tile_col0[tn];
+                const int64_t ld = e.heads.ld[th];
+                const float* bias = e.bias ? e.bias + tn * BN : nullptr;
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    if (wm == half) {
+#pragma unroll
+                        for (int j = 0; j < NI; ++j)
+#pragma unroll
+                            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                                for (int r = 0; r < 16; ++r) {
+                                    const int lr = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                                    const int lc = wn * WN + j * 32 + (lane & 31);
+                                    lds[lr * BN + ((lc + 32 * ((lr >> 2) & 1)) & (BN - 1))] = acc[i][j][r];
+                                }
+                    }
+                    __syncthreads();
+                    // 128 rows x 64 chunks of 4 columns; one wave stores one full row
+#pragma unroll
+                    for (int q = 0; q < (128 * 64) / (64 * NW); ++q) {
+                        const int id = q * 64 * NW + tid;
+                        const int lr = id >> 6, c4 = (id & 63) * 4;
+                        const int row = tm * BM + half * 128 + lr;
+                        float4 v = *(const float4*)(lds + lr * BN + ((c4 + 32 * ((lr >> 2) & 1)) & (BN - 1)));
+                        if (bias) {
+                            const float4 b = *(const float4*)(bias + c4);
+                            v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
+                        }
+                        if (row < g.M) *(float4*)(dst0 + (int64_t)row * ld + c4) = v;
+                    }
+                    __syncthreads();
+                }
+                return;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int col = col_base + j * 32;
+            float* dst;
+            int64_t ld;
+            if (th >= 0) {
+                dst = e.heads.ptr[th] + e.tile_col0[tn] + (col - tn * BN);
+                ld = e.heads.ld[th];
+            } else {
+                const int c = col - e.tail_start;
+                const int h = e.tail_head[c];
+                if (h < 0) continue;
+                dst = e.heads.ptr[h] + e.tail_col[c];
+                ld = e.heads.ld[h];
+            }
+            const float b = e.bias ? e.bias[col] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
+                    if (row < g.M) dst[(int64_t)row * ld] = acc[i][j][r] + b;
+                }
+        }
+    }
+}
+
 // A BM x BN tile is computed by WGM x WGN waves, each owning a
 // (BM/WGM) x (BN/WGN) sub-tile.  Slabs of 64 K-values are copied from global
 // memory straight into LDS (global_load_lds, 16 bytes per lane; one wave
@@ -216,148 +373,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_nt(GemmArgs g) {
         __syncthreads();                 // ... for all waves, and all are done with this one
     }
 
-    // ------------------------------------------------------------ epilogue
-    const int row_base = tm * BM + wm * WM + 4 * (lane >> 5);
-    const int col_base = tn * BN + wn * WN + (lane & 31);
-    const EpiArgs& e = g.epi;
-
-    if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_ADD_F32 || EPI == EPI_PARTIAL) {
-        float* out = e.out_f32 + (EPI == EPI_PARTIAL ? (int64_t)split * g.split_stride : 0);
-#pragma unroll
-        for (int j = 0; j < NI; ++j) {
-            const int col = col_base + j * 32;
-            if (col >= e.n_real) continue;
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
-                    if (row < g.M) {
-                        float* p = out + (int64_t)row * e.ld_f32 + col;
-                        if constexpr (EPI == EPI_ADD_F32) *p += acc[i][j][r];
-                        else *p = acc[i][j][r];
-                    }
-                }
-        }
-    } else if constexpr (EPI == EPI_QKV) {
-#pragma unroll
-        for (int j = 0; j < NI; ++j) {
-            const int col = col_base + j * 32;
-            if (col >= e.n_real) continue;
-            if (col < e.n_split) {
-#pragma unroll
-                for (int i = 0; i < MI; ++i)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
-                        if (row < g.M) e.out16[(int64_t)row * e.ld16 + col] = to_f16_bits(acc[i][j][r]);
-                    }
-            } else {
-                // V^T: the lane's 4 consecutive rows are 4 consecutive tokens
-                uint16_t* vt = e.vt + (int64_t)(col - e.n_split) * e.ld_vt;
-#pragma unroll
-                for (int i = 0; i < MI; ++i)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int row = row_base + i * 32 + 8 * q;
-                        if (row < g.M) {
-                            u32x2 pk;
-                            pk[0] = (uint32_t)to_f16_bits(acc[i][j][4 * q + 0]) |
-                                    ((uint32_t)to_f16_bits(acc[i][j][4 * q + 1]) << 16);
-                            pk[1] = (uint32_t)to_f16_bits(acc[i][j][4 * q + 2]) |
-                                    ((uint32_t)to_f16_bits(acc[i][j][4 * q + 3]) << 16);
-                            *(u32x2*)(vt + row) = pk;
-                        }
-                    }
-            }
-        }
-    } else if constexpr (EPI == EPI_SWIGLU) {
-        static_assert(NI % 2 == 0, "gate/up pairs need an even number of 32-column tiles");
-#pragma unroll
-        for (int j = 0; j < NI; j += 2) {
-            const int f = (tn * BN + wn * WN + j * 32) / 2 + (lane & 31);
-            if (2 * f >= e.n_real) continue;
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
-                    if (row < g.M)
-                        e.out16[(int64_t)row * e.ld16 + f] =
-                            to_f16_bits(silu(acc[i][j][r]) * acc[i][j + 1][r]);
-                }
-        }
-    } else if constexpr (EPI == EPI_HEADS) {
-        static_assert(BN == kHeadTileN, "head packing assumes one head per column tile");
-        const int th = e.tile_head[tn];
-        // A whole-head tile whose destination rows are 16-byte aligned goes out
-        // through LDS: each half of the tile (128 x 256 fp32 = the 128 KB of
-        // LDS) is transposed there and written as full 1 KB rows with 16-byte
-        // stores (a quarter of the store instructions of the direct path).
-        if constexpr (BM == 256 && WGM == 2 && WGN == 4) {
-            if (th >= 0 && (e.heads.ld[th] % 4) == 0 && ((uintptr_t)e.heads.ptr[th] % 16) == 0) {
-                float* lds = reinterpret_cast<float*>(smem);       // [128][256], rows rotated by 32 every 4 rows
-                float* dst0 = e.heads.ptr[th] + e.tile_col0[tn];
-                const int64_t ld = e.heads.ld[th];
-                const float* bias = e.bias ? e.bias + tn * BN : nullptr;
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    if (wm == half) {
-#pragma unroll
-                        for (int j = 0; j < NI; ++j)
-#pragma unroll
-                            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                                for (int r = 0; r < 16; ++r) {
-                                    const int lr = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                                    const int lc = wn * WN + j * 32 + (lane & 31);
-                                    lds[lr * BN + ((lc + 32 * ((lr >> 2) & 1)) & (BN - 1))] = acc[i][j][r];
-                                }
-                    }
-                    __syncthreads();
-                    // 128 rows x 64 chunks of 4 columns; one wave stores one full row
-#pragma unroll
-                    for (int q = 0; q < (128 * 64) / (64 * NW); ++q) {
-                        const int id = q * 64 * NW + tid;
-                        const int lr = id >> 6, c4 = (id & 63) * 4;
-                        const int row = tm * BM + half * 128 + lr;
-                        float4 v = *(const float4*)(lds + lr * BN + ((c4 + 32 * ((lr >> 2) & 1)) & (BN - 1)));
-                        if (bias) {
-                            const float4 b = *(const float4*)(bias + c4);
-                            v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
-                        }
-                        if (row < g.M) *(float4*)(dst0 + (int64_t)row * ld + c4) = v;
-                    }
-                    __syncthreads();
-                }
-                return;
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < NI; ++j) {
-            const int col = col_base + j * 32;
-            float* dst;
-            int64_t ld;
-            if (th >= 0) {
-                dst = e.heads.ptr[th] + e.tile_col0[tn] + (col - tn * BN);
-                ld = e.heads.ld[th];
-            } else {
-                const int c = col - e.tail_start;
-                const int h = e.tail_head[c];
-                if (h < 0) continue;
-                dst = e.heads.ptr[h] + e.tail_col[c];
-                ld = e.heads.ld[h];
-            }
-            const float b = e.bias ? e.bias[col] : 0.0f;
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
-                    if (row < g.M) dst[(int64_t)row * ld] = acc[i][j][r] + b;
-                }
-        }
-    }
+    epilogue<BM, BN, WGM, WGN, EPI, MI, NI>(g, acc, tm, tn, split, smem);
 }
 
 template <int BM, int BN, int WGM, int WGN, int OPD, int EPI>
@@ -370,6 +386,127 @@ hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
     const int grid = (total + 7) / 8 * 8;
     hipLaunchKernelGGL((gemm_nt<BM, BN, WGM, WGN, OPD, EPI>), dim3(grid), dim3(64 * WGM * WGN), 0, s, a);
     return hipGetLastError();
+}
+
+
+// Four-stage variant for operands that are both stored in the tiled32_index
+// layout (the head GEMM: bf16 weights and z).  One 256x256 tile per
+// workgroup, 2 x 4 waves of 128 x 64.
+//  - K is walked in 32-wide slabs; a slab of A and of B is 2 x 16 KB, each
+//    contiguous in global memory, copied straight into LDS (1 KB per wave
+//    instruction).  Four LDS stages: three slabs are in flight while one is
+//    consumed, which covers the L2 latency at full MFMA rate.
+//  - The MFMA fragments are double-buffered in registers: the LDS reads of
+//    the next 16-wide K step are issued before the MFMAs of the current one,
+//    including across the slab barrier, so LDS latency hides behind MFMAs.
+//    The K order of the accumulation is the plain one (slab by slab, step by
+//    step), the same as gemm_nt's: both kernels give identical bits.
+//  - Each slab ends with one barrier: it publishes the next slab (every wave
+//    has waited for its own DMA of it) and frees the stage the DMA of the
+//    slab after next refills.
+template <int OPD, int EPI>
+__global__ void __launch_bounds__(512) gemm_t32(GemmArgs g) {
+    constexpr bool BF16 = OPD == OPD_BF16;
+    constexpr int BM = 256, BN = 256, WGM = 2, WGN = 4, NW = WGM * WGN, KB = 32, S = 4;
+    constexpr int WM = BM / WGM, WN = BN / WGN, MI = WM / 32, NI = WN / 32;
+    constexpr int AI = BM / (16 * NW), BI = BN / (16 * NW);   // DMA instructions per wave per slab
+    constexpr int L = AI + BI;
+    constexpr int STAGE = (BM + BN) * KB;
+    static_assert(S * STAGE * 2 >= 128 * 1024, "the head epilogue stages 128 KB through LDS");
+    static_assert((S - 2) * L < 16, "vmcnt immediate");
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[S * STAGE];
+
+    const int mt = (g.M + BM - 1) / BM;
+    const int nt = g.N / BN;
+    const int total = mt * nt;
+    const int per_xcd = gridDim.x / 8;
+    const int v = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (v >= total) return;
+    const int tm = v % mt, tn = v / mt;     // M-tiles of one weight strip back to back on one XCD
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int nk = g.K / KB;
+    // 256-row groups of both operands: slab kt of group t starts at (t*nk + kt) * 256 * KB
+    const uint16_t* Ab = g.A + (int64_t)tm * nk * BM * KB;
+    const uint16_t* Bb = g.B + (int64_t)tn * nk * BN * KB;
+    auto issue = [&](int kt, int st) {
+        uint16_t* sa = smem + st * STAGE;
+        uint16_t* sb = sa + BM * KB;
+        const int64_t o = (int64_t)kt * BM * KB;
+#pragma unroll
+        for (int i = 0; i < AI; ++i)
+            __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Ab + o + (i * NW + wave) * 16 * KB + lane * 8),
+                                             (lds_ptr_t)(sa + (i * NW + wave) * 16 * KB), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < BI; ++i)
+            __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Bb + o + (i * NW + wave) * 16 * KB + lane * 8),
+                                             (lds_ptr_t)(sb + (i * NW + wave) * 16 * KB), 16, 0, 0);
+    };
+    f32x16 acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    const int frow = lane & 31, fk = lane >> 5;
+    const int sw = ((frow >> 1) ^ (frow >> 3)) & 3;     // fragment rows differ by multiples of 32
+    int aoff[MI], boff[NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i) aoff[i] = (wm * WM + i * 32 + frow) * KB;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) boff[j] = BM * KB + (wn * WN + j * 32 + frow) * KB;
+    u32x4 fa0[MI], fb0[NI], fa1[MI], fb1[NI];
+    auto rd = [&](int st, int ks, u32x4* fa, u32x4* fb) {
+        const uint16_t* base = smem + st * STAGE;
+        const int c = ((ks * 2 + fk) ^ sw) << 3;
+#pragma unroll
+        for (int i = 0; i < MI; ++i) fa[i] = *(const u32x4*)(base + aoff[i] + c);
+#pragma unroll
+        for (int j = 0; j < NI; ++j) fb[j] = *(const u32x4*)(base + boff[j] + c);
+    };
+    auto mm = [&](const u32x4* fa, const u32x4* fb) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NI; ++j) acc[i][j] = mfma32<BF16>(fa[i], fb[j], acc[i][j]);
+    };
+    // vmcnt(n) with lgkmcnt / expcnt left alone
+    auto vm_wait = [](auto n) {
+        constexpr int N = decltype(n)::value;
+        __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+    };
+
+#pragma unroll
+    for (int p = 0; p < S - 1; ++p)
+        if (p < nk) issue(p, p);
+    if (nk >= S - 1) vm_wait(std::integral_constant<int, (S - 2) * L>{});
+    else vm_wait(std::integral_constant<int, 0>{});
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    rd(0, 0, fa0, fb0);
+    for (int kt = 0; kt < nk; ++kt) {
+        const bool more = kt + S - 1 < nk;
+        // the stage of slab kt-1 was released by the previous barrier
+        if (more) issue(kt + S - 1, (kt + S - 1) % S);
+        rd(kt % S, 1, fa1, fb1);
+        mm(fa0, fb0);
+        if (more) vm_wait(std::integral_constant<int, (S - 2) * L>{});   // slab kt+1 has landed
+        else vm_wait(std::integral_constant<int, 0>{});
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");           // slab kt fully read
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        __asm__ volatile("" ::: "memory");
+        // after the last slab this reads a stale stage (in bounds); the values are not used
+        rd((kt + 1) % S, 0, fa0, fb0);
+        mm(fa1, fb1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __syncthreads();    // every wave is done with LDS: the epilogue may reuse it
+    epilogue<BM, BN, WGM, WGN, EPI, MI, NI>(g, acc, tm, tn, 0, smem);
 }
 
 }  // namespace
@@ -407,5 +544,17 @@ hipError_t launch_gemm(GemmOperand opd, GemmTile tile, EpiKind epi, const GemmAr
     return hipErrorNotSupported;
 }
 #undef KVA_GEMM_CASE
+
+hipError_t launch_gemm_t32(GemmOperand opd, EpiKind epi, const GemmArgs& a, hipStream_t s) {
+    if (a.M <= 0) return hipSuccess;
+    if (a.K % 32 != 0 || a.K <= 0 || a.N % 256 || a.splits != 1) return hipErrorInvalidValue;
+    const int total = ((a.M + 255) / 256) * (a.N / 256);
+    const int grid = (total + 7) / 8 * 8;
+    if (opd == OPD_BF16 && epi == EPI_HEADS) {
+        hipLaunchKernelGGL((gemm_t32<OPD_BF16, EPI_HEADS>), dim3(grid), dim3(512), 0, s, a);
+        return hipGetLastError();
+    }
+    return hipErrorNotSupported;
+}
 
 }  // namespace kva

@@ -23,11 +23,20 @@ constexpr int kColPad = 256;
 // c (K-values 8c..8c+7) sits at chunk c ^ ((r & 7) ^ ((r >> 3) & 1)).  This is
 // exactly the LDS layout of a GEMM B tile.
 constexpr int kWeightTileRows = 256;
-inline int64_t weight_tiled_index(int64_t row, int64_t k, int64_t K) {
+__host__ __device__ inline int64_t weight_tiled_index(int64_t row, int64_t k, int64_t K) {
     const int64_t nb = row / kWeightTileRows, r = row % kWeightTileRows, kt = k / 64;
     const int64_t c = (k % 64) / 8, e = k % 8;
     const int64_t sw = (r & 7) ^ ((r >> 3) & 1);
     return ((nb * (K / 64) + kt) * kWeightTileRows + r) * 64 + ((c ^ sw) * 8) + e;
+}
+// The same idea with 32-wide K slabs (64-byte rows, 4 chunks), used by the
+// four-stage GEMM for both of its operands (head weights and the final-normed
+// activations z): chunk c of row r sits at chunk c ^ (((r >> 1) ^ (r >> 3)) & 3).
+__host__ __device__ inline int64_t tiled32_index(int64_t row, int64_t k, int64_t K) {
+    const int64_t nb = row / kWeightTileRows, r = row % kWeightTileRows, kt = k / 32;
+    const int64_t c = (k % 32) / 8, e = k % 8;
+    const int64_t sw = ((r >> 1) ^ (r >> 3)) & 3;
+    return ((nb * (K / 32) + kt) * kWeightTileRows + r) * 32 + ((c ^ sw) * 8) + e;
 }
 
 struct HeadOut {
@@ -100,13 +109,24 @@ enum GemmTile : int { TILE_256x256 = 0, TILE_128x128 = 1, TILE_128x64 = 2 };
 hipError_t launch_gemm(GemmOperand opd, GemmTile tile, EpiKind epi, const GemmArgs& args,
                        hipStream_t stream);
 
+// The same product with both operands in the tiled32_index layout (A rows
+// grouped by 256 like the weight rows; rows >= M of the last group are read
+// and dropped).  256x256 tiles, four LDS stages of 32-wide slabs.
+// 16-bit operands only (OPD_F16 / OPD_BF16); K a multiple of 32.
+hipError_t launch_gemm_t32(GemmOperand opd, EpiKind epi, const GemmArgs& args, hipStream_t stream);
+
 // Folds split-K partials into the residual stream and normalises it:
 //   h[r][c] = (add ? h[r][c] : 0) + P_0[r][c] + P_1[r][c] + ... (this order),
 //   out[r][c] = 16-bit(h[r][c] / sqrt(mean_c h[r][c]^2 + eps) * g[c]).
-// P_s = partials + s * pstride, rows of ldp.
+// P_s = partials + s * pstride, rows of ldp.  With out_t32 the output goes
+// to out[tiled32_index(r, c, cols)] instead (ldo unused; cols % 32 == 0).
 hipError_t launch_fold_rmsnorm(float* h, int64_t ldh, bool add, const float* partials, int32_t splits,
                                int64_t pstride, int64_t ldp, const float* g, int32_t rows, int32_t cols,
-                               float eps, uint16_t* out, int64_t ldo, bool bf16, hipStream_t stream);
+                               float eps, uint16_t* out, int64_t ldo, bool bf16, bool out_t32,
+                               hipStream_t stream);
+
+// dst[r][c] = src[tiled32_index(r, c, cols)] for r < rows (16-bit values).
+hipError_t launch_untile32(const uint16_t* src, uint16_t* dst, int32_t rows, int32_t cols, hipStream_t stream);
 
 // out[r][c] = 16-bit(x[r][c] / sqrt(mean_c x[r][c]^2 + eps) * g[c]); fp16 or bf16.
 hipError_t launch_rmsnorm_cast(const float* x, int64_t ldx, const float* g, int32_t rows,

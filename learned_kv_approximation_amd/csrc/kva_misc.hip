@@ -55,8 +55,9 @@ __global__ void __launch_bounds__(256) rmsnorm_cast(const float* __restrict__ x,
 // Split-K fold + RMSNorm: the residual update that follows a split GEMM,
 // fused with the norm that reads the updated residual.  The partials are
 // added in a fixed order, so the result is deterministic and independent of
-// how many rows the call has.
-template <bool BF16>
+// how many rows the call has.  T32: the output goes out in the tiled32_index
+// layout (4 consecutive columns stay within one 8-value chunk).
+template <bool BF16, bool T32>
 __global__ void __launch_bounds__(256) fold_rmsnorm(float* __restrict__ h, int64_t ldh, int add,
                                                     const float* __restrict__ partials, int32_t splits,
                                                     int64_t pstride, int64_t ldp,
@@ -90,8 +91,17 @@ __global__ void __launch_bounds__(256) fold_rmsnorm(float* __restrict__ h, int64
         o.y = to_bits(v.y * r * gg.y, BF16);
         o.z = to_bits(v.z * r * gg.z, BF16);
         o.w = to_bits(v.w * r * gg.w, BF16);
-        *(ushort4*)(orow + c) = o;
+        if constexpr (T32) *(ushort4*)(out + tiled32_index(row, c, cols)) = o;
+        else *(ushort4*)(orow + c) = o;
     }
+}
+
+// Inverse of the tiled32_index layout, one row per workgroup (test hook).
+__global__ void __launch_bounds__(256) untile32_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                                       int32_t cols) {
+    const int row = blockIdx.x;
+    for (int c = threadIdx.x * 4; c < cols; c += 1024)
+        *(ushort4*)(dst + (int64_t)row * cols + c) = *(const ushort4*)(src + tiled32_index(row, c, cols));
 }
 
 // KV-cache write for one full-attention layer ("Qwen3.8-27B-KVA" card, "What
@@ -175,15 +185,24 @@ hipError_t launch_rmsnorm_cast(const float* x, int64_t ldx, const float* g, int3
 
 hipError_t launch_fold_rmsnorm(float* h, int64_t ldh, bool add, const float* partials, int32_t splits,
                                int64_t pstride, int64_t ldp, const float* g, int32_t rows, int32_t cols,
-                               float eps, uint16_t* out, int64_t ldo, bool bf16, hipStream_t s) {
+                               float eps, uint16_t* out, int64_t ldo, bool bf16, bool out_t32, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
-    if (cols % 4 || splits < 1) return hipErrorInvalidValue;
-    if (bf16)
-        hipLaunchKernelGGL(fold_rmsnorm<true>, dim3(rows), dim3(256), 0, s, h, ldh, (int)add, partials, splits,
-                           pstride, ldp, g, cols, eps, out, ldo);
-    else
-        hipLaunchKernelGGL(fold_rmsnorm<false>, dim3(rows), dim3(256), 0, s, h, ldh, (int)add, partials, splits,
-                           pstride, ldp, g, cols, eps, out, ldo);
+    if (cols % 4 || splits < 1 || (out_t32 && cols % 32)) return hipErrorInvalidValue;
+#define KVA_FOLD(B_, T_)                                                                                  \
+    hipLaunchKernelGGL((fold_rmsnorm<B_, T_>), dim3(rows), dim3(256), 0, s, h, ldh, (int)add, partials, \
+                       splits, pstride, ldp, g, cols, eps, out, ldo)
+    if (bf16 && out_t32) KVA_FOLD(true, true);
+    else if (bf16) KVA_FOLD(true, false);
+    else if (out_t32) KVA_FOLD(false, true);
+    else KVA_FOLD(false, false);
+#undef KVA_FOLD
+    return hipGetLastError();
+}
+
+hipError_t launch_untile32(const uint16_t* src, uint16_t* dst, int32_t rows, int32_t cols, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    if (cols % 32) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(untile32_kernel, dim3(rows), dim3(256), 0, s, src, dst, cols);
     return hipGetLastError();
 }
 

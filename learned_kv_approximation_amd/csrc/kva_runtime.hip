@@ -162,9 +162,9 @@ struct kva_ctx {
     std::vector<void*> allocs;
     uint64_t weight_bytes = 0, scratch_bytes = 0;
 
-    // weights (device).  A weight is either 16-bit values w16 (fp16
-    // trunk, bf16 heads; tiled, see weight_tiled_index) or, for q8_0, codes
-    // q[rows][K] + fp16 scales sc[rows][K/32].
+    // weights (device).  A weight is either 16-bit values w16 (fp16 trunk
+    // tiled as in weight_tiled_index; bf16 heads tiled as in tiled32_index)
+    // or, for q8_0, codes q[rows][K] + fp16 scales sc[rows][K/32].
     struct DevW {
         uint16_t* w16 = nullptr;
         int8_t* q = nullptr;
@@ -303,11 +303,12 @@ struct RowSrc {
 };
 
 // Target layouts on the device.
-enum PackTarget { PACK_F16 = 0, PACK_BF16 = 1, PACK_Q8 = 2 };
+enum PackTarget { PACK_F16 = 0, PACK_BF16_T32 = 1, PACK_Q8 = 2 };
 
 // Packs rows (each K wide, stored in `dtype`) into the compute layout and
-// uploads it: fp16 or bf16 values in the tiled layout of weight_tiled_index,
-// or for q8_0 an int8 code plane
+// uploads it: fp16 values in the tiled layout of weight_tiled_index (64-wide
+// slabs), bf16 values in that of tiled32_index (32-wide slabs), or for q8_0
+// an int8 code plane
 // [rows][K] plus an fp16 scale plane [rows][K/32] (the 34-byte blocks split
 // losslessly into aligned planes).
 kva_status pack_weight(kva_ctx* ctx, int dtype, int64_t K, const std::vector<RowSrc>& rows,
@@ -341,9 +342,9 @@ kva_status pack_weight(kva_ctx* ctx, int dtype, int64_t K, const std::vector<Row
         if (!rows[r].src) continue;
         uint16_t* dst = &w[(size_t)(r * K)];
         const int64_t base = rows[r].row * K;
-        if (target == PACK_BF16 && dtype == KVA_DTYPE_BF16) {
+        if (target == PACK_BF16_T32 && dtype == KVA_DTYPE_BF16) {
             std::memcpy(dst, static_cast<const uint16_t*>(rows[r].src) + base, (size_t)K * 2);
-        } else if (target == PACK_BF16) {
+        } else if (target == PACK_BF16_T32) {
             for (int64_t k = 0; k < K; ++k) dst[k] = f32_to_bf16(static_cast<const float*>(rows[r].src)[base + k]);
         } else {
             for (int64_t k = 0; k < K; ++k) dst[k] = f32_to_f16(load_f32(rows[r].src, dtype, base + k), &ovf);
@@ -353,8 +354,10 @@ kva_status pack_weight(kva_ctx* ctx, int dtype, int64_t K, const std::vector<Row
     if (n % kWeightTileRows || K % 64) return fail(KVA_ERR_SHAPE, "weight %s: bad padding", name);
     std::vector<uint16_t> t(w.size());
     for (int64_t r = 0; r < n; ++r)
-        for (int64_t k = 0; k < K; k += 8)    // 8 consecutive K-values stay together
-            std::memcpy(&t[(size_t)weight_tiled_index(r, k, K)], &w[(size_t)(r * K + k)], 16);
+        for (int64_t k = 0; k < K; k += 8) {   // 8 consecutive K-values stay together
+            const int64_t at = target == PACK_BF16_T32 ? tiled32_index(r, k, K) : weight_tiled_index(r, k, K);
+            std::memcpy(&t[(size_t)at], &w[(size_t)(r * K + k)], 16);
+        }
     HIP_TRY(ctx->alloc(&out->w16, t.size() * 2, true));
     return upload(ctx, out->w16, t.data(), t.size() * 2);
 }
@@ -379,7 +382,7 @@ kva_status create_impl(const kva_config* cfg, const kva_weights* w, int device, 
     ctx->device = device;
     ctx->q8 = q8;
     const PackTarget trunk_t = q8 ? PACK_Q8 : PACK_F16;
-    const PackTarget head_t = q8 ? PACK_Q8 : PACK_BF16;
+    const PackTarget head_t = q8 ? PACK_Q8 : PACK_BF16_T32;
 
     auto putf = [&](float** dstp, const float* src, int64_t n, const char* name) -> kva_status {
         if (!src) return fail(KVA_ERR_ARG, "gain %s is NULL", name);
@@ -597,9 +600,9 @@ kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n, float* co
         STAGE(stage, launch_gemm(opd, pick_tile(n, g.N, g.splits), EPI_PARTIAL, g, s));
         return KVA_OK;
     };
-    auto fold = [&](bool add, const float* gain, uint16_t* out, bool bf16) -> kva_status {
+    auto fold = [&](bool add, const float* gain, uint16_t* out, bool bf16, bool t32) -> kva_status {
         STAGE(KVA_STAGE_NORM, launch_fold_rmsnorm(ctx->h, d, add, ctx->ws, kSplitNarrow, pstride, d, gain, n,
-                                                  (int32_t)d, c.eps, out, d, bf16, s));
+                                                  (int32_t)d, c.eps, out, d, bf16, t32, s));
         return KVA_OK;
     };
 
@@ -608,7 +611,7 @@ kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n, float* co
     for (int b = 0; b < c.n_blocks; ++b) {
         const kva_ctx::Blk& B = ctx->blk[b];
         // h = (b == 0 ? 0 : h) + input/down partials; a = attn_norm(h)
-        KVA_TRY(fold(b > 0, B.g_attn, ctx->a16, false));
+        KVA_TRY(fold(b > 0, B.g_attn, ctx->a16, false, false));
         {
             GemmArgs g;
             g.A = ctx->a16; g.lda = d; set_b(g, B.wqkv, d);
@@ -621,7 +624,7 @@ kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n, float* co
         STAGE(KVA_STAGE_ATTN, launch_attention(ctx->qk16, 2 * hd, (int32_t)hd, ctx->vt16, ctx->m_alloc, ctx->o16, hd, n,
                                 c.n_heads, c.attn_block, s));
         KVA_TRY(narrow(ctx->o16, hd, B.wo, KVA_STAGE_GEMM_O));
-        KVA_TRY(fold(true, B.g_ffn, ctx->a16, false));           // h += O partials; a = ffn_norm(h)
+        KVA_TRY(fold(true, B.g_ffn, ctx->a16, false, false));           // h += O partials; a = ffn_norm(h)
         {
             GemmArgs g;
             g.A = ctx->a16; g.lda = d; set_b(g, B.wgu, d);
@@ -631,7 +634,9 @@ kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n, float* co
         }
         KVA_TRY(narrow(ctx->act16, F, B.wd, KVA_STAGE_GEMM_DOWN));
     }
-    KVA_TRY(fold(true, ctx->g_out, ctx->z16, !ctx->q8));           // h += down partials; z = out_norm(h)
+    // h += down partials; z = out_norm(h): bf16 in the tiled32 layout of the
+    // four-stage head GEMM, or fp16 row-major for the q8_0 head GEMM
+    KVA_TRY(fold(true, ctx->g_out, ctx->z16, !ctx->q8, !ctx->q8));
     {
         GemmArgs g;
         g.A = ctx->z16; g.lda = d; set_b(g, ctx->w_heads, d);
@@ -641,7 +646,8 @@ kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n, float* co
         g.epi.tail_head = ctx->tail_head; g.epi.tail_col = ctx->tail_col;
         g.epi.tail_start = ctx->tail_start; g.epi.bias = ctx->b_heads;
         g.epi.heads = ho;
-        STAGE(KVA_STAGE_GEMM_HEADS, launch_gemm(ctx->q8 ? OPD_Q8 : OPD_BF16, TILE_256x256, EPI_HEADS, g, s));
+        if (ctx->q8) STAGE(KVA_STAGE_GEMM_HEADS, launch_gemm(OPD_Q8, TILE_256x256, EPI_HEADS, g, s));
+        else STAGE(KVA_STAGE_GEMM_HEADS, launch_gemm_t32(OPD_BF16, EPI_HEADS, g, s));
     }
     ctx->stats.calls += 1;
     ctx->stats.tokens += (uint64_t)n;
@@ -697,8 +703,12 @@ kva_status kva_debug_dequant_q8_0(const void* blocks, int64_t n_blocks, float* o
 kva_status kva_debug_copy_z(kva_ctx* ctx, uint16_t* dst, int32_t n, void* stream) {
     if (!ctx || !dst) return fail(KVA_ERR_ARG, "NULL argument");
     if (n < 1 || n > ctx->cfg.max_tokens) return fail(KVA_ERR_SHAPE, "bad n_tokens");
-    HIP_TRY(hipMemcpyAsync(dst, ctx->z16, (size_t)n * ctx->cfg.d_model * 2, hipMemcpyDeviceToDevice,
-                           static_cast<hipStream_t>(stream)));
+    if (ctx->q8) {
+        HIP_TRY(hipMemcpyAsync(dst, ctx->z16, (size_t)n * ctx->cfg.d_model * 2, hipMemcpyDeviceToDevice,
+                               static_cast<hipStream_t>(stream)));
+    } else {
+        LAUNCH(launch_untile32(ctx->z16, dst, n, ctx->cfg.d_model, static_cast<hipStream_t>(stream)));
+    }
     return KVA_OK;
 }
 
