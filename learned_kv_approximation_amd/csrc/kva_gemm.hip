@@ -7,20 +7,17 @@
 // operand layout of the 32x32x16 MFMA: each lane feeds 8 consecutive
 // K-values of one row of A and 8 consecutive K-values of one row of W.
 //
-// Structure (one workgroup = a grid of waves, one BM x BN tile):
-//  - K is walked in slabs of 64.  The next slab is copied from global memory
-//    straight into the second LDS buffer (global_load_lds) while the waves run
-//    MFMAs on the current one (one barrier a slab).
-//  - LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk
-//    c ^ swz(r), so the 16 rows one ds_read_b128 phase touches land on
-//    distinct banks.  Weights are repacked at create into the same layout,
-//    slab by slab (kWeightTileRows rows x 64 K-values contiguous), so every
-//    weight DMA instruction reads one contiguous kilobyte.
-//  - Workgroup ids are remapped so that the tiles of one weight strip (all
-//    M-tiles of an N-tile) run back to back on the same XCD and share its L2:
-//    the hardware deals workgroups to the 8 XCDs round-robin.
-//  - fp32 accumulation; the epilogue is fused (fp32 store / residual add,
-//    fp16 Q|K plus transposed V, SwiGLU, bias + per-head scatter).
+// Two kernels share the fused epilogues (fp32 split-K partial, fp16
+// Q|K plus transposed V, SwiGLU, bias + per-head scatter):
+//  - gemm_t32: 16-bit weights (fp16 trunk, bf16 heads).  Both operands are
+//    stored in the tiled32_index layout; four LDS stages of 32-wide slabs.
+//  - gemm_q8: q8_0 weights.  The activation (fp16, row-major) is copied into
+//    LDS directly; the weight half of each 64-wide slab goes through
+//    registers, where d*q is formed exactly and rounded once to fp16.
+// In both, workgroup ids are remapped so that the tiles of one weight strip
+// (all M-tiles of an N-tile) run back to back on the same XCD and share its
+// L2: the hardware deals workgroups to the 8 XCDs round-robin.  Accumulation
+// is fp32, over K in plain sequential order.
 #include "kva_internal.h"
 
 #include <type_traits>
@@ -34,10 +31,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BK = 64;          // K per slab (16-bit elements): 128-byte LDS rows
+constexpr int BK = 64;          // gemm_q8: K per slab (fp16 elements): 128-byte LDS rows
 
+// gemm_q8's LDS swizzle: the 16-byte chunk c of row r sits at chunk c ^ swz(r),
+// so the 16 rows one ds_read_b128 phase touches land on distinct banks.
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-static_assert(kWeightTileRows % 256 == 0, "weight tiles must hold whole GEMM tiles");
 
 template <bool BF16>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
@@ -77,8 +75,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[MI][NI
     const int col_base = tn * BN + wn * WN + (lane & 31);
     const EpiArgs& e = g.epi;
 
-    if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_ADD_F32 || EPI == EPI_PARTIAL) {
-        float* out = e.out_f32 + (EPI == EPI_PARTIAL ? (int64_t)split * g.split_stride : 0);
+    if constexpr (EPI == EPI_PARTIAL) {
+        float* out = e.out_f32 + (int64_t)split * g.split_stride;
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
             const int col = col_base + j * 32;
@@ -88,11 +86,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[MI][NI
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
-                    if (row < g.M) {
-                        float* p = out + (int64_t)row * e.ld_f32 + col;
-                        if constexpr (EPI == EPI_ADD_F32) *p += acc[i][j][r];
-                        else *p = acc[i][j][r];
-                    }
+                    if (row < g.M) out[(int64_t)row * e.ld_f32 + col] = acc[i][j][r];
                 }
         }
     } else if constexpr (EPI == EPI_QKV) {
@@ -138,9 +132,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[MI][NI
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
-                    if (row < g.M)
-                        e.out16[(int64_t)row * e.ld16 + f] =
-                            to_f16_bits(silu(acc[i][j][r]) * acc[i][j + 1][r]);
+                    if (row < g.M) {
+                        const int64_t at = e.out16_t32 ? tiled32_index(row, f, e.ld16) : (int64_t)row * e.ld16 + f;
+                        e.out16[at] = to_f16_bits(silu(acc[i][j][r]) * acc[i][j + 1][r]);
+                    }
                 }
         }
     } else if constexpr (EPI == EPI_HEADS) {
@@ -216,22 +211,20 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[MI][NI
     }
 }
 
-// A BM x BN tile is computed by WGM x WGN waves, each owning a
-// (BM/WGM) x (BN/WGN) sub-tile.  Slabs of 64 K-values are copied from global
-// memory straight into LDS (global_load_lds, 16 bytes per lane; one wave
-// instruction fills 8 consecutive 128-byte rows): no register staging, no
-// ds_write.  Lane L of such an instruction lands at row L/8, physical chunk
-// L%8, so it fetches the logical chunk (L%8) ^ swz(row) of that row.
-template <int BM, int BN, int WGM, int WGN, int OPD, int EPI>
-__global__ void __launch_bounds__(64 * WGM * WGN) gemm_nt(GemmArgs g) {
-    constexpr bool BF16 = OPD == OPD_BF16;
-    constexpr bool Q8 = OPD == OPD_Q8;
+// q8_0 weights.  A BM x BN tile is computed by WGM x WGN waves, each owning
+// a (BM/WGM) x (BN/WGN) sub-tile.  The activation half of each 64-wide slab
+// is copied from global memory straight into LDS (global_load_lds, 16 bytes
+// per lane; one wave instruction fills 8 consecutive 128-byte rows): lane L
+// lands at row L/8, physical chunk L%8, so it fetches the logical chunk
+// (L%8) ^ swz(row) of that row.  Two LDS buffers, one barrier a slab.
+template <int BM, int BN, int WGM, int WGN, int EPI>
+__global__ void __launch_bounds__(64 * WGM * WGN) gemm_q8(GemmArgs g) {
     constexpr int NW = WGM * WGN;
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int MI = WM / 32, NI = WN / 32;
-    constexpr int AI = BM / (8 * NW), BI = Q8 ? 0 : BN / (8 * NW);   // wave DMA instructions per slab
-    static_assert(AI >= 1 && (Q8 || BI >= 1) && MI >= 1 && NI >= 1, "tile too small for the wave grid");
-    static_assert(!Q8 || 64 * NW == 2 * BN, "q8_0 weights: two threads per weight row");
+    constexpr int AI = BM / (8 * NW);   // wave DMA instructions per slab
+    static_assert(AI >= 1 && MI >= 1 && NI >= 1, "tile too small for the wave grid");
+    static_assert(64 * NW == 2 * BN, "q8_0 weights: two threads per weight row");
     constexpr int STAGE = (BM + BN) * BK;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE];
 
@@ -254,13 +247,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_nt(GemmArgs g) {
 
     // rows >= M of A are padding rows of the activation scratch: loaded, never stored
     const uint16_t* Ab = g.A + (int64_t)tm * BM * g.lda;
-    // 16-bit weights are stored tiled (see kWeightTileRows): the rows of this
-    // tile sit at row offset r0 of weight tile nb, and each 64-wide K slab of
-    // a weight tile is one contiguous, already swizzled block
     const int nk_all = g.K / BK;
-    const int nb = (tn * BN) / kWeightTileRows, r0 = (tn * BN) % kWeightTileRows;
-    const uint16_t* Bb = g.B + ((int64_t)nb * nk_all * kWeightTileRows + r0) * BK;
-    int offa[AI], offb[BI > 0 ? BI : 1];
+    int offa[AI];
     {
         const int rr = lane >> 3, pc = lane & 7;
 #pragma unroll
@@ -268,20 +256,13 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_nt(GemmArgs g) {
             const int row = (i * NW + wave) * 8 + rr;
             offa[i] = row * (int)g.lda + ((pc ^ swz(row)) << 3);
         }
-#pragma unroll
-        for (int i = 0; i < BI; ++i) offb[i] = (i * NW + wave) * 8 * BK + lane * 8;   // 1 KB, contiguous
     }
     auto issue = [&](int kt, int buf) {
         uint16_t* sa = smem + buf * STAGE;
-        uint16_t* sb = sa + BM * BK;
 #pragma unroll
         for (int i = 0; i < AI; ++i)
             __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Ab + offa[i] + kt * BK),
                                              (lds_ptr_t)(sa + (i * NW + wave) * 8 * BK), 16, 0, 0);
-#pragma unroll
-        for (int i = 0; i < BI; ++i)
-            __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Bb + (int64_t)kt * kWeightTileRows * BK + offb[i]),
-                                             (lds_ptr_t)(sb + (i * NW + wave) * 8 * BK), 16, 0, 0);
     };
 
     // q8_0 weights: thread t owns one 32-code block of weight row t/2 per slab
@@ -289,36 +270,32 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_nt(GemmArgs g) {
     // registers, d*q is rounded once to fp16 and written to LDS.
     const int qrow = tid >> 1, qhalf = tid & 1;
     const int kblocks = g.K / 32;
-    const int8_t* Bq = Q8 ? g.Bq + ((int64_t)tn * BN + qrow) * g.ldb + qhalf * 32 : nullptr;
-    const uint16_t* Bs = Q8 ? g.Bs + ((int64_t)tn * BN + qrow) * kblocks + qhalf : nullptr;
+    const int8_t* Bq = g.Bq + ((int64_t)tn * BN + qrow) * g.ldb + qhalf * 32;
+    const uint16_t* Bs = g.Bs + ((int64_t)tn * BN + qrow) * kblocks + qhalf;
     u32x4 qr0, qr1;
     uint16_t qd = 0;
     auto qload = [&](int kt) {
-        if constexpr (Q8) {
-            qr0 = *(const u32x4*)(Bq + kt * BK);
-            qr1 = *(const u32x4*)(Bq + kt * BK + 16);
-            qd = Bs[kt * 2];
-        }
+        qr0 = *(const u32x4*)(Bq + kt * BK);
+        qr1 = *(const u32x4*)(Bq + kt * BK + 16);
+        qd = Bs[kt * 2];
     };
     auto qstore = [&](int buf) {
-        if constexpr (Q8) {
-            uint16_t* sb = smem + buf * STAGE + BM * BK + qrow * BK;
+        uint16_t* sb = smem + buf * STAGE + BM * BK + qrow * BK;
 #pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4) {
-                const u32x4& src = c4 < 2 ? qr0 : qr1;
-                const uint32_t w0 = src[(c4 & 1) * 2], w1 = src[(c4 & 1) * 2 + 1];
-                u32x4 o;
+        for (int c4 = 0; c4 < 4; ++c4) {
+            const u32x4& src = c4 < 2 ? qr0 : qr1;
+            const uint32_t w0 = src[(c4 & 1) * 2], w1 = src[(c4 & 1) * 2 + 1];
+            u32x4 o;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t w = e < 2 ? w0 : w1;
-                    const int q0 = (int)(int8_t)(w >> (16 * (e & 1)));
-                    const int q1 = (int)(int8_t)(w >> (16 * (e & 1) + 8));
-                    o[e] = (uint32_t)to_f16_bits(q8_0_value(qd, q0)) |
-                           ((uint32_t)to_f16_bits(q8_0_value(qd, q1)) << 16);
-                }
-                const int c = qhalf * 4 + c4;
-                *(u32x4*)(sb + ((c ^ swz(qrow)) << 3)) = o;
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t w = e < 2 ? w0 : w1;
+                const int q0 = (int)(int8_t)(w >> (16 * (e & 1)));
+                const int q1 = (int)(int8_t)(w >> (16 * (e & 1) + 8));
+                o[e] = (uint32_t)to_f16_bits(q8_0_value(qd, q0)) |
+                       ((uint32_t)to_f16_bits(q8_0_value(qd, q1)) << 16);
             }
+            const int c = qhalf * 4 + c4;
+            *(u32x4*)(sb + ((c ^ swz(qrow)) << 3)) = o;
         }
     };
 
@@ -366,7 +343,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_nt(GemmArgs g) {
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
-                for (int j = 0; j < NI; ++j) acc[i][j] = mfma32<BF16>(af[i], bfr[j], acc[i][j]);
+                for (int j = 0; j < NI; ++j) acc[i][j] = mfma32<false>(af[i], bfr[j], acc[i][j]);
         }
         if (kt + 1 < nk) qstore(buf ^ 1);
         __builtin_amdgcn_s_waitcnt(0);   // the next slab has landed
@@ -376,64 +353,79 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_nt(GemmArgs g) {
     epilogue<BM, BN, WGM, WGN, EPI, MI, NI>(g, acc, tm, tn, split, smem);
 }
 
-template <int BM, int BN, int WGM, int WGN, int OPD, int EPI>
-hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
+template <int BM, int BN, int WGM, int WGN, int EPI>
+hipError_t launch_q8(const GemmArgs& a, hipStream_t s) {
     if (a.N % BN) return hipErrorInvalidValue;
     if (a.splits < 1 || a.splits > a.K / BK || (a.splits > 1 && EPI != EPI_PARTIAL)) return hipErrorInvalidValue;
     const int mt = (a.M + BM - 1) / BM;
     const int nt = a.N / BN;
     const int total = mt * nt * a.splits;
     const int grid = (total + 7) / 8 * 8;
-    hipLaunchKernelGGL((gemm_nt<BM, BN, WGM, WGN, OPD, EPI>), dim3(grid), dim3(64 * WGM * WGN), 0, s, a);
+    hipLaunchKernelGGL((gemm_q8<BM, BN, WGM, WGN, EPI>), dim3(grid), dim3(64 * WGM * WGN), 0, s, a);
     return hipGetLastError();
 }
 
 
 // Four-stage variant for operands that are both stored in the tiled32_index
-// layout (the head GEMM: bf16 weights and z).  One 256x256 tile per
-// workgroup, 2 x 4 waves of 128 x 64.
-//  - K is walked in 32-wide slabs; a slab of A and of B is 2 x 16 KB, each
-//    contiguous in global memory, copied straight into LDS (1 KB per wave
-//    instruction).  Four LDS stages: three slabs are in flight while one is
-//    consumed, which covers the L2 latency at full MFMA rate.
+// layout (the head GEMM, and the trunk GEMMs when their weights are 16-bit).
+// BM x BN tiles (256x256 with 2 x 4 waves of 128 x 64, or 128x128 with 2 x 2
+// waves of 64 x 64, whose 64 KB of LDS lets two workgroups share a CU).
+//  - K is walked in 32-wide slabs; the A and the B half of a slab are each one
+//    contiguous block in global memory, copied straight into LDS (1 KB per
+//    wave instruction).  Four LDS stages: three slabs are in flight while one
+//    is consumed, which covers the L2 latency at full MFMA rate.
 //  - The MFMA fragments are double-buffered in registers: the LDS reads of
 //    the next 16-wide K step are issued before the MFMAs of the current one,
 //    including across the slab barrier, so LDS latency hides behind MFMAs.
 //    The K order of the accumulation is the plain one (slab by slab, step by
-//    step), the same as gemm_nt's: both kernels give identical bits.
+//    step) for every tile shape, so the tile choice never changes the bits.
 //  - Each slab ends with one barrier: it publishes the next slab (every wave
 //    has waited for its own DMA of it) and frees the stage the DMA of the
 //    slab after next refills.
-template <int OPD, int EPI>
-__global__ void __launch_bounds__(512) gemm_t32(GemmArgs g) {
+//  - Split-K (EPI_PARTIAL only): the slabs are cut into `splits` consecutive
+//    ranges, one per workgroup, each writing its own partial buffer.
+template <int BM, int BN, int WGM, int WGN, int OPD, int EPI>
+__global__ void __launch_bounds__(64 * WGM * WGN) gemm_t32(GemmArgs g) {
     constexpr bool BF16 = OPD == OPD_BF16;
-    constexpr int BM = 256, BN = 256, WGM = 2, WGN = 4, NW = WGM * WGN, KB = 32, S = 4;
+    constexpr int NW = WGM * WGN, KB = 32, S = 4;
     constexpr int WM = BM / WGM, WN = BN / WGN, MI = WM / 32, NI = WN / 32;
     constexpr int AI = BM / (16 * NW), BI = BN / (16 * NW);   // DMA instructions per wave per slab
     constexpr int L = AI + BI;
     constexpr int STAGE = (BM + BN) * KB;
-    static_assert(S * STAGE * 2 >= 128 * 1024, "the head epilogue stages 128 KB through LDS");
+    static_assert(AI >= 1 && BI >= 1, "tile too small for the wave grid");
+    static_assert(EPI != EPI_HEADS || S * STAGE * 2 >= 128 * 1024, "the head epilogue stages 128 KB through LDS");
     static_assert((S - 2) * L < 16, "vmcnt immediate");
+    static_assert(kWeightTileRows % BM == 0 && kWeightTileRows % BN == 0, "tiles inside 256-row groups");
     __shared__ __attribute__((aligned(1024))) uint16_t smem[S * STAGE];
 
     const int mt = (g.M + BM - 1) / BM;
     const int nt = g.N / BN;
-    const int total = mt * nt;
+    const int SP = g.splits;
+    const int total = mt * nt * SP;
     const int per_xcd = gridDim.x / 8;
     const int v = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     if (v >= total) return;
-    const int tm = v % mt, tn = v / mt;     // M-tiles of one weight strip back to back on one XCD
+    // M-tiles fastest, then splits, then N-tiles: the tiles sharing a weight
+    // strip run back to back on one XCD
+    const int tm = v % mt;
+    const int split = (v / mt) % SP;
+    const int tn = v / (mt * SP);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WGN, wn = wave % WGN;
-    const int nk = g.K / KB;
-    // 256-row groups of both operands: slab kt of group t starts at (t*nk + kt) * 256 * KB
-    const uint16_t* Ab = g.A + (int64_t)tm * nk * BM * KB;
-    const uint16_t* Bb = g.B + (int64_t)tn * nk * BN * KB;
+    const int nk_all = g.K / KB;
+    const int kb = split * nk_all / SP;                // this split's slabs: [kb, kb + nk)
+    const int nk = (split + 1) * nk_all / SP - kb;
+    // slab kt of the rows [r0, r0 + BM) of a 256-row group t starts at
+    // ((t * nk_all + kt) * 256 + r0) * KB
+    const uint16_t* Ab = g.A + (((int64_t)(tm * BM / kWeightTileRows) * nk_all + kb) * kWeightTileRows +
+                                (tm * BM) % kWeightTileRows) * KB;
+    const uint16_t* Bb = g.B + (((int64_t)(tn * BN / kWeightTileRows) * nk_all + kb) * kWeightTileRows +
+                                (tn * BN) % kWeightTileRows) * KB;
     auto issue = [&](int kt, int st) {
         uint16_t* sa = smem + st * STAGE;
         uint16_t* sb = sa + BM * KB;
-        const int64_t o = (int64_t)kt * BM * KB;
+        const int64_t o = (int64_t)kt * kWeightTileRows * KB;
 #pragma unroll
         for (int i = 0; i < AI; ++i)
             __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Ab + o + (i * NW + wave) * 16 * KB + lane * 8),
@@ -505,56 +497,56 @@ __global__ void __launch_bounds__(512) gemm_t32(GemmArgs g) {
         __builtin_amdgcn_sched_barrier(0);
     }
     __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __syncthreads();    // every wave is done with LDS: the epilogue may reuse it
-    epilogue<BM, BN, WGM, WGN, EPI, MI, NI>(g, acc, tm, tn, 0, smem);
+    if constexpr (EPI == EPI_HEADS) __syncthreads();    // the head epilogue reuses LDS
+    epilogue<BM, BN, WGM, WGN, EPI, MI, NI>(g, acc, tm, tn, split, smem);
+}
+
+template <int BM, int BN, int WGM, int WGN, int OPD, int EPI>
+hipError_t launch_t32(const GemmArgs& a, hipStream_t s) {
+    if (a.N % BN) return hipErrorInvalidValue;
+    if (a.splits < 1 || a.splits > a.K / 32 || (a.splits > 1 && EPI != EPI_PARTIAL)) return hipErrorInvalidValue;
+    const int total = ((a.M + BM - 1) / BM) * (a.N / BN) * a.splits;
+    const int grid = (total + 7) / 8 * 8;
+    hipLaunchKernelGGL((gemm_t32<BM, BN, WGM, WGN, OPD, EPI>), dim3(grid), dim3(64 * WGM * WGN), 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace
 
-// The instantiated (operand, tile, epilogue) combinations.
-#define KVA_GEMM_CASE(OPD_, TILE_, EPI_, BM_, BN_, WGM_, WGN_) \
-    if (opd == OPD_ && tile == TILE_ && epi == EPI_) return launch_one<BM_, BN_, WGM_, WGN_, OPD_, EPI_>(a, s);
+// The instantiated (tile, epilogue) combinations of each kernel.
+#define KVA_Q8_CASE(TILE_, EPI_, BM_, BN_, WGM_, WGN_) \
+    if (tile == TILE_ && epi == EPI_) return launch_q8<BM_, BN_, WGM_, WGN_, EPI_>(a, s);
 
-hipError_t launch_gemm(GemmOperand opd, GemmTile tile, EpiKind epi, const GemmArgs& a,
-                       hipStream_t s) {
+hipError_t launch_gemm_q8(GemmTile tile, EpiKind epi, const GemmArgs& a, hipStream_t s) {
     if (a.M <= 0) return hipSuccess;
     if (a.K % BK != 0 || a.K <= 0) return hipErrorInvalidValue;
-    if (opd == OPD_Q8 && (!a.Bq || !a.Bs)) return hipErrorInvalidValue;
-    KVA_GEMM_CASE(OPD_BF16, TILE_256x256, EPI_HEADS, 256, 256, 2, 4)
-    KVA_GEMM_CASE(OPD_Q8, TILE_256x256, EPI_HEADS, 256, 256, 2, 4)
-    KVA_GEMM_CASE(OPD_F16, TILE_256x256, EPI_PARTIAL, 256, 256, 2, 4)
-    KVA_GEMM_CASE(OPD_F16, TILE_256x256, EPI_SWIGLU, 256, 256, 2, 4)
-    KVA_GEMM_CASE(OPD_F16, TILE_256x256, EPI_QKV, 256, 256, 2, 4)
-    KVA_GEMM_CASE(OPD_Q8, TILE_256x256, EPI_PARTIAL, 256, 256, 2, 4)
-    KVA_GEMM_CASE(OPD_Q8, TILE_256x256, EPI_SWIGLU, 256, 256, 2, 4)
-    KVA_GEMM_CASE(OPD_Q8, TILE_256x256, EPI_QKV, 256, 256, 2, 4)
-    KVA_GEMM_CASE(OPD_F16, TILE_128x128, EPI_STORE_F32, 128, 128, 2, 2)
-    KVA_GEMM_CASE(OPD_F16, TILE_128x128, EPI_ADD_F32, 128, 128, 2, 2)
-    KVA_GEMM_CASE(OPD_F16, TILE_128x128, EPI_PARTIAL, 128, 128, 2, 2)
-    KVA_GEMM_CASE(OPD_F16, TILE_128x128, EPI_QKV, 128, 128, 2, 2)
-    KVA_GEMM_CASE(OPD_F16, TILE_128x128, EPI_SWIGLU, 128, 128, 2, 2)
-    KVA_GEMM_CASE(OPD_Q8, TILE_128x128, EPI_STORE_F32, 128, 128, 2, 2)
-    KVA_GEMM_CASE(OPD_Q8, TILE_128x128, EPI_ADD_F32, 128, 128, 2, 2)
-    KVA_GEMM_CASE(OPD_Q8, TILE_128x128, EPI_PARTIAL, 128, 128, 2, 2)
-    KVA_GEMM_CASE(OPD_Q8, TILE_128x128, EPI_QKV, 128, 128, 2, 2)
-    KVA_GEMM_CASE(OPD_Q8, TILE_128x128, EPI_SWIGLU, 128, 128, 2, 2)
-    KVA_GEMM_CASE(OPD_F16, TILE_128x64, EPI_STORE_F32, 128, 64, 2, 2)
-    KVA_GEMM_CASE(OPD_F16, TILE_128x64, EPI_ADD_F32, 128, 64, 2, 2)
-    KVA_GEMM_CASE(OPD_F16, TILE_128x64, EPI_PARTIAL, 128, 64, 2, 2)
+    if (!a.Bq || !a.Bs) return hipErrorInvalidValue;
+    KVA_Q8_CASE(TILE_256x256, EPI_HEADS, 256, 256, 2, 4)
+    KVA_Q8_CASE(TILE_256x256, EPI_PARTIAL, 256, 256, 2, 4)
+    KVA_Q8_CASE(TILE_256x256, EPI_SWIGLU, 256, 256, 2, 4)
+    KVA_Q8_CASE(TILE_256x256, EPI_QKV, 256, 256, 2, 4)
+    KVA_Q8_CASE(TILE_128x128, EPI_PARTIAL, 128, 128, 2, 2)
+    KVA_Q8_CASE(TILE_128x128, EPI_QKV, 128, 128, 2, 2)
+    KVA_Q8_CASE(TILE_128x128, EPI_SWIGLU, 128, 128, 2, 2)
     return hipErrorNotSupported;
 }
-#undef KVA_GEMM_CASE
+#undef KVA_Q8_CASE
 
-hipError_t launch_gemm_t32(GemmOperand opd, EpiKind epi, const GemmArgs& a, hipStream_t s) {
+#define KVA_T32_CASE(OPD_, TILE_, EPI_, BM_, BN_, WGM_, WGN_) \
+    if (opd == OPD_ && tile == TILE_ && epi == EPI_) return launch_t32<BM_, BN_, WGM_, WGN_, OPD_, EPI_>(a, s);
+
+hipError_t launch_gemm_t32(GemmOperand opd, GemmTile tile, EpiKind epi, const GemmArgs& a, hipStream_t s) {
     if (a.M <= 0) return hipSuccess;
-    if (a.K % 32 != 0 || a.K <= 0 || a.N % 256 || a.splits != 1) return hipErrorInvalidValue;
-    const int total = ((a.M + 255) / 256) * (a.N / 256);
-    const int grid = (total + 7) / 8 * 8;
-    if (opd == OPD_BF16 && epi == EPI_HEADS) {
-        hipLaunchKernelGGL((gemm_t32<OPD_BF16, EPI_HEADS>), dim3(grid), dim3(512), 0, s, a);
-        return hipGetLastError();
-    }
+    if (a.K % 32 != 0 || a.K <= 0) return hipErrorInvalidValue;
+    KVA_T32_CASE(OPD_BF16, TILE_256x256, EPI_HEADS, 256, 256, 2, 4)
+    KVA_T32_CASE(OPD_F16, TILE_256x256, EPI_PARTIAL, 256, 256, 2, 4)
+    KVA_T32_CASE(OPD_F16, TILE_256x256, EPI_QKV, 256, 256, 2, 4)
+    KVA_T32_CASE(OPD_F16, TILE_256x256, EPI_SWIGLU, 256, 256, 2, 4)
+    KVA_T32_CASE(OPD_F16, TILE_128x128, EPI_PARTIAL, 128, 128, 2, 2)
+    KVA_T32_CASE(OPD_F16, TILE_128x128, EPI_QKV, 128, 128, 2, 2)
+    KVA_T32_CASE(OPD_F16, TILE_128x128, EPI_SWIGLU, 128, 128, 2, 2)
     return hipErrorNotSupported;
 }
+#undef KVA_T32_CASE
 
 }  // namespace kva

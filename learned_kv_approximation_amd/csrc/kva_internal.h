@@ -17,21 +17,14 @@ constexpr int kHeadTileN = 256;
 constexpr int kRowPad = 256;
 // Weight rows are padded with zeros to a multiple of this.
 constexpr int kColPad = 256;
-// 16-bit weights [rows][K] are stored tiled: for each group of
-// kWeightTileRows rows and each 64-wide K slab, one contiguous block of
-// kWeightTileRows x 64 values, row after row; within a row the 16-byte chunk
-// c (K-values 8c..8c+7) sits at chunk c ^ ((r & 7) ^ ((r >> 3) & 1)).  This is
-// exactly the LDS layout of a GEMM B tile.
+// 16-bit GEMM operands [rows][K] (weights, and the activations that feed a
+// GEMM with 16-bit weights) are stored tiled: for each group of
+// kWeightTileRows rows and each 32-wide K slab, one contiguous block of
+// kWeightTileRows x 32 values, row after row (64-byte rows); within a row the
+// 16-byte chunk c (K-values 8c..8c+7) sits at chunk c ^ (((r >> 1) ^ (r >> 3)) & 3).
+// That is exactly the LDS layout of a gemm_t32 slab, so every operand DMA
+// instruction reads one contiguous kilobyte.
 constexpr int kWeightTileRows = 256;
-__host__ __device__ inline int64_t weight_tiled_index(int64_t row, int64_t k, int64_t K) {
-    const int64_t nb = row / kWeightTileRows, r = row % kWeightTileRows, kt = k / 64;
-    const int64_t c = (k % 64) / 8, e = k % 8;
-    const int64_t sw = (r & 7) ^ ((r >> 3) & 1);
-    return ((nb * (K / 64) + kt) * kWeightTileRows + r) * 64 + ((c ^ sw) * 8) + e;
-}
-// The same idea with 32-wide K slabs (64-byte rows, 4 chunks), used by the
-// four-stage GEMM for both of its operands (head weights and the final-normed
-// activations z): chunk c of row r sits at chunk c ^ (((r >> 1) ^ (r >> 3)) & 3).
 __host__ __device__ inline int64_t tiled32_index(int64_t row, int64_t k, int64_t K) {
     const int64_t nb = row / kWeightTileRows, r = row % kWeightTileRows, kt = k / 32;
     const int64_t c = (k % 32) / 8, e = k % 8;
@@ -45,8 +38,6 @@ struct HeadOut {
 };
 
 enum EpiKind : int {
-    EPI_STORE_F32 = 0,  // out_f32[m][n] = acc
-    EPI_ADD_F32 = 1,    // out_f32[m][n] += acc   (residual stream)
     EPI_QKV = 2,        // n < n_split: out16[m][n] = fp16(acc); else vt[n - n_split][m] = fp16(acc)
     EPI_SWIGLU = 3,     // gate/up interleaved per 32 columns: out16[m][f] = fp16(silu(g) * u)
     EPI_HEADS = 4,      // bias add, scatter to per-head fp32 outputs
@@ -60,6 +51,7 @@ struct EpiArgs {
     int64_t ld16 = 0;
     uint16_t* vt = nullptr;
     int64_t ld_vt = 0;
+    int32_t out16_t32 = 0;              // EPI_SWIGLU: out16 in the tiled32_index layout (K = ld16)
     int32_t n_split = 0;
     int32_t n_real = 0;                 // real (unpadded) columns of the product
     const int32_t* tile_head = nullptr; // per 256-column tile: head, or -1 for a tail tile
@@ -71,9 +63,10 @@ struct EpiArgs {
     HeadOut heads;
 };
 
-// C[M][N] = A[M][K] * B[N][K]^T with 16-bit operands and fp32 accumulation.
-// For OPD_Q8 the weight comes as int8 codes Bq[N][ldb] and one fp16 scale per
-// 32 codes, Bs[N][K/32]; the weight is d * q (see q8_0_value).
+// C[M][N] = A[M][K] * B[N][K]^T with 16-bit activations and fp32
+// accumulation.  16-bit weights: B (tiled32 layout, ldb unused).  q8_0
+// weights: int8 codes Bq[N][ldb] and one fp16 scale per 32 codes,
+// Bs[N][K/32]; the weight is d * q (see q8_0_value).
 struct GemmArgs {
     const uint16_t* A = nullptr;
     int64_t lda = 0;
@@ -83,7 +76,7 @@ struct GemmArgs {
     const uint16_t* Bs = nullptr;
     int32_t M = 0;       // rows of A that are real (stores are masked to M)
     int32_t N = 0;       // columns, a multiple of the tile width (weights are padded)
-    int32_t K = 0;       // multiple of 64
+    int32_t K = 0;       // multiple of 32 (gemm_t32) or 64 (gemm_q8)
     // Split-K: the K slabs are cut into `splits` consecutive ranges, one per
     // workgroup; each range's partial product goes to its own buffer
     // (EPI_PARTIAL).  The split count must depend only on (N, K), never on M,
@@ -93,9 +86,8 @@ struct GemmArgs {
     EpiArgs epi;
 };
 
-// OPD_F16 / OPD_BF16: both operands 16-bit.  OPD_Q8: A fp16, B q8_0 planes,
-// fp16 MFMA on the weights d*q rounded once to fp16.
-enum GemmOperand : int { OPD_F16 = 0, OPD_BF16 = 1, OPD_Q8 = 2 };
+// Operand type of gemm_t32: both operands fp16 or both bf16.
+enum GemmOperand : int { OPD_F16 = 0, OPD_BF16 = 1 };
 
 // One q8_0 weight: the fp16 block scale (bit pattern d_bits) times the int8
 // code, exactly (an 11-bit significand times an 8-bit integer fits fp32's 24
@@ -103,17 +95,19 @@ enum GemmOperand : int { OPD_F16 = 0, OPD_BF16 = 1, OPD_Q8 = 2 };
 __device__ __forceinline__ float q8_0_value(uint16_t d_bits, int q) {
     return (float)__builtin_bit_cast(_Float16, d_bits) * (float)q;
 }
-// 256x256: 8 waves (2 per SIMD); 128x128 and 128x64: 4 waves.
-enum GemmTile : int { TILE_256x256 = 0, TILE_128x128 = 1, TILE_128x64 = 2 };
+// 256x256: 8 waves (2 per SIMD); 128x128: 4 waves.
+enum GemmTile : int { TILE_256x256 = 0, TILE_128x128 = 1 };
 
-hipError_t launch_gemm(GemmOperand opd, GemmTile tile, EpiKind epi, const GemmArgs& args,
-                       hipStream_t stream);
+// q8_0 weights: A fp16 row-major (rows padded to the tile), fp16 MFMA on the
+// weights d*q rounded once to fp16; K a multiple of 64.
+hipError_t launch_gemm_q8(GemmTile tile, EpiKind epi, const GemmArgs& args, hipStream_t stream);
 
 // The same product with both operands in the tiled32_index layout (A rows
 // grouped by 256 like the weight rows; rows >= M of the last group are read
-// and dropped).  256x256 tiles, four LDS stages of 32-wide slabs.
+// and dropped).  Four LDS stages of 32-wide slabs; tiles 256x256 or 128x128.
 // 16-bit operands only (OPD_F16 / OPD_BF16); K a multiple of 32.
-hipError_t launch_gemm_t32(GemmOperand opd, EpiKind epi, const GemmArgs& args, hipStream_t stream);
+hipError_t launch_gemm_t32(GemmOperand opd, GemmTile tile, EpiKind epi, const GemmArgs& args,
+                           hipStream_t stream);
 
 // Folds split-K partials into the residual stream and normalises it:
 //   h[r][c] = (add ? h[r][c] : 0) + P_0[r][c] + P_1[r][c] + ... (this order),
@@ -129,17 +123,18 @@ hipError_t launch_fold_rmsnorm(float* h, int64_t ldh, bool add, const float* par
 hipError_t launch_untile32(const uint16_t* src, uint16_t* dst, int32_t rows, int32_t cols, hipStream_t stream);
 
 // out[r][c] = 16-bit(x[r][c] / sqrt(mean_c x[r][c]^2 + eps) * g[c]); fp16 or bf16.
+// With out_t32 the output goes to out[tiled32_index(r, c, cols)] (ldo unused).
 hipError_t launch_rmsnorm_cast(const float* x, int64_t ldx, const float* g, int32_t rows,
                                int32_t cols, float eps, uint16_t* out, int64_t ldo, bool bf16,
-                               hipStream_t stream);
+                               bool out_t32, hipStream_t stream);
 
 // Block-causal multi-head attention with heads of 128.
 //   qk: [n][ld_qk] fp16, Q of head h at columns [h*128, h*128+128), K at k_off + h*128
 //   vt: [n_heads*128][ld_vt] fp16, V transposed (vt[c][t])
-//   o : [n][ld_o] fp16
+//   o : [n][ld_o] fp16, or with o_t32 o[tiled32_index(t, c, ld_o)]
 hipError_t launch_attention(const uint16_t* qk, int64_t ld_qk, int32_t k_off, const uint16_t* vt,
                             int64_t ld_vt, uint16_t* o, int64_t ld_o, int32_t n_tokens,
-                            int32_t n_heads, int32_t attn_block, hipStream_t stream);
+                            int32_t n_heads, int32_t attn_block, bool o_t32, hipStream_t stream);
 
 struct KvWriteArgs {
     const float* kv;

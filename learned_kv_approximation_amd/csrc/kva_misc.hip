@@ -21,7 +21,7 @@ __device__ __forceinline__ uint16_t to_bits(float v, bool bf16) {
 // input norm, the two pre-norms of each block and the final norm):
 // y = x / sqrt(mean(x^2) + eps) * g.  One workgroup per row; fixed
 // reduction order, so a row's result never depends on other rows.
-template <bool BF16>
+template <bool BF16, bool T32>
 __global__ void __launch_bounds__(256) rmsnorm_cast(const float* __restrict__ x, int64_t ldx,
                                                     const float* __restrict__ gain, int32_t cols,
                                                     float eps, uint16_t* __restrict__ out,
@@ -48,7 +48,8 @@ __global__ void __launch_bounds__(256) rmsnorm_cast(const float* __restrict__ x,
         o.y = to_bits(v.y * r * gg.y, BF16);
         o.z = to_bits(v.z * r * gg.z, BF16);
         o.w = to_bits(v.w * r * gg.w, BF16);
-        *(ushort4*)(orow + c) = o;
+        if constexpr (T32) *(ushort4*)(out + tiled32_index(row, c, cols)) = o;
+        else *(ushort4*)(orow + c) = o;
     }
 }
 
@@ -173,13 +174,16 @@ __global__ void dequant_q8_0_kernel(const uint8_t* __restrict__ blocks, int64_t 
 
 hipError_t launch_rmsnorm_cast(const float* x, int64_t ldx, const float* g, int32_t rows,
                                int32_t cols, float eps, uint16_t* out, int64_t ldo, bool bf16,
-                               hipStream_t s) {
+                               bool out_t32, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
-    if (cols % 4) return hipErrorInvalidValue;
-    if (bf16)
-        hipLaunchKernelGGL(rmsnorm_cast<true>, dim3(rows), dim3(256), 0, s, x, ldx, g, cols, eps, out, ldo);
-    else
-        hipLaunchKernelGGL(rmsnorm_cast<false>, dim3(rows), dim3(256), 0, s, x, ldx, g, cols, eps, out, ldo);
+    if (cols % 4 || (out_t32 && cols % 32)) return hipErrorInvalidValue;
+#define KVA_NORM(B_, T_) \
+    hipLaunchKernelGGL((rmsnorm_cast<B_, T_>), dim3(rows), dim3(256), 0, s, x, ldx, g, cols, eps, out, ldo)
+    if (bf16 && out_t32) KVA_NORM(true, true);
+    else if (bf16) KVA_NORM(true, false);
+    else if (out_t32) KVA_NORM(false, true);
+    else KVA_NORM(false, false);
+#undef KVA_NORM
     return hipGetLastError();
 }
 

@@ -162,9 +162,11 @@ struct kva_ctx {
     std::vector<void*> allocs;
     uint64_t weight_bytes = 0, scratch_bytes = 0;
 
-    // weights (device).  A weight is either 16-bit values w16 (fp16 trunk
-    // tiled as in weight_tiled_index; bf16 heads tiled as in tiled32_index)
-    // or, for q8_0, codes q[rows][K] + fp16 scales sc[rows][K/32].
+    // weights (device).  A weight is either 16-bit values w16 (fp16 trunk,
+    // bf16 heads; tiled as in tiled32_index) or, for q8_0, codes q[rows][K] +
+    // fp16 scales sc[rows][K/32].  With 16-bit weights every GEMM operand is
+    // in the tiled32 layout (the activation producers write it so); with
+    // q8_0 the activations are row-major.
     struct DevW {
         uint16_t* w16 = nullptr;
         int8_t* q = nullptr;
@@ -303,12 +305,11 @@ struct RowSrc {
 };
 
 // Target layouts on the device.
-enum PackTarget { PACK_F16 = 0, PACK_BF16_T32 = 1, PACK_Q8 = 2 };
+enum PackTarget { PACK_F16_T32 = 0, PACK_BF16_T32 = 1, PACK_Q8 = 2 };
 
 // Packs rows (each K wide, stored in `dtype`) into the compute layout and
-// uploads it: fp16 values in the tiled layout of weight_tiled_index (64-wide
-// slabs), bf16 values in that of tiled32_index (32-wide slabs), or for q8_0
-// an int8 code plane
+// uploads it: fp16 or bf16 values in the tiled layout of tiled32_index
+// (32-wide slabs), or for q8_0 an int8 code plane
 // [rows][K] plus an fp16 scale plane [rows][K/32] (the 34-byte blocks split
 // losslessly into aligned planes).
 kva_status pack_weight(kva_ctx* ctx, int dtype, int64_t K, const std::vector<RowSrc>& rows,
@@ -351,13 +352,11 @@ kva_status pack_weight(kva_ctx* ctx, int dtype, int64_t K, const std::vector<Row
         }
     }
     if (ovf) return fail(KVA_ERR_RANGE, "weight %s has values outside the fp16 range", name);
-    if (n % kWeightTileRows || K % 64) return fail(KVA_ERR_SHAPE, "weight %s: bad padding", name);
+    if (n % kWeightTileRows || K % 32) return fail(KVA_ERR_SHAPE, "weight %s: bad padding", name);
     std::vector<uint16_t> t(w.size());
     for (int64_t r = 0; r < n; ++r)
-        for (int64_t k = 0; k < K; k += 8) {   // 8 consecutive K-values stay together
-            const int64_t at = target == PACK_BF16_T32 ? tiled32_index(r, k, K) : weight_tiled_index(r, k, K);
-            std::memcpy(&t[(size_t)at], &w[(size_t)(r * K + k)], 16);
-        }
+        for (int64_t k = 0; k < K; k += 8)    // 8 consecutive K-values stay together
+            std::memcpy(&t[(size_t)tiled32_index(r, k, K)], &w[(size_t)(r * K + k)], 16);
     HIP_TRY(ctx->alloc(&out->w16, t.size() * 2, true));
     return upload(ctx, out->w16, t.data(), t.size() * 2);
 }
@@ -381,7 +380,7 @@ kva_status create_impl(const kva_config* cfg, const kva_weights* w, int device, 
     HIP_TRY(hipSetDevice(device));
     ctx->device = device;
     ctx->q8 = q8;
-    const PackTarget trunk_t = q8 ? PACK_Q8 : PACK_F16;
+    const PackTarget trunk_t = q8 ? PACK_Q8 : PACK_F16_T32;
     const PackTarget head_t = q8 ? PACK_Q8 : PACK_BF16_T32;
 
     auto putf = [&](float** dstp, const float* src, int64_t n, const char* name) -> kva_status {
@@ -498,6 +497,17 @@ kva_status create_impl(const kva_config* cfg, const kva_weights* w, int device, 
 // estimated rounds over the 256 CUs, a 256x256 tile doing the work of four
 // 128x128 tiles in about 1/1.3 of their time.  Tile shape never changes a
 // result's bits (same K order per output).
+// Tile of a four-stage (tiled32) trunk GEMM: 256x256 runs one workgroup per
+// CU; 128x128 runs two per CU (64 KB of LDS each), each taking about 1.3 / 4
+// of a 256x256 tile's time when alone.
+GemmTile pick_tile_t32(int64_t M, int64_t N, int splits) {
+    const int64_t t128 = ((M + 127) / 128) * (N / 128) * splits;
+    const int64_t t256 = ((M + 255) / 256) * (N / 256) * splits;
+    const double c256 = (double)((t256 + 255) / 256);
+    const double c128 = (double)((t128 + 511) / 512) * 2.0 * 1.3 / 4.0;
+    return (N % 256 == 0 && c256 <= c128) ? TILE_256x256 : TILE_128x128;
+}
+
 GemmTile pick_tile(int64_t M, int64_t N, int splits) {
     const int64_t t128 = ((M + 127) / 128) * (N / 128) * splits;
     const int64_t t256 = ((M + 255) / 256) * (N / 256) * splits;
@@ -586,8 +596,12 @@ kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n, float* co
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t d = c.d_model, F = c.d_ffn, n_in = c.n_in;
     const int64_t hd = (int64_t)c.n_heads * c.head_dim;
-    // trunk operand type and the tile of the narrow (N = d) GEMMs
-    const GemmOperand opd = ctx->q8 ? OPD_Q8 : OPD_F16;
+    // t32: 16-bit weights, every trunk operand in the tiled32 layout
+    const bool t32 = !ctx->q8;
+    auto gemm = [&](EpiKind epi, const GemmArgs& g) -> hipError_t {
+        if (t32) return launch_gemm_t32(OPD_F16, pick_tile_t32(g.M, g.N, g.splits), epi, g, s);
+        return launch_gemm_q8(pick_tile(g.M, g.N, g.splits), epi, g, s);
+    };
     const int64_t pstride = ctx->m_alloc * d;   // between split-K partial buffers
     // The narrow GEMMs (N = d: input, O, down) write kSplitNarrow partials to
     // ws; the next norm folds them into h in a fixed order.
@@ -597,21 +611,22 @@ kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n, float* co
         g.M = n; g.N = (int32_t)round_up(d, kColPad); g.K = (int32_t)K;
         g.splits = kSplitNarrow; g.split_stride = pstride;
         g.epi.out_f32 = ctx->ws; g.epi.ld_f32 = d; g.epi.n_real = (int32_t)d;
-        STAGE(stage, launch_gemm(opd, pick_tile(n, g.N, g.splits), EPI_PARTIAL, g, s));
+        STAGE(stage, gemm(EPI_PARTIAL, g));
         return KVA_OK;
     };
-    auto fold = [&](bool add, const float* gain, uint16_t* out, bool bf16, bool t32) -> kva_status {
+    auto fold = [&](bool add, const float* gain, uint16_t* out, bool bf16) -> kva_status {
         STAGE(KVA_STAGE_NORM, launch_fold_rmsnorm(ctx->h, d, add, ctx->ws, kSplitNarrow, pstride, d, gain, n,
                                                   (int32_t)d, c.eps, out, d, bf16, t32, s));
         return KVA_OK;
     };
 
-    STAGE(KVA_STAGE_NORM, launch_rmsnorm_cast(x, n_in, ctx->g_in, n, (int32_t)n_in, c.eps, ctx->u16, n_in, false, s));
+    STAGE(KVA_STAGE_NORM,
+          launch_rmsnorm_cast(x, n_in, ctx->g_in, n, (int32_t)n_in, c.eps, ctx->u16, n_in, false, t32, s));
     KVA_TRY(narrow(ctx->u16, n_in, ctx->w_in, KVA_STAGE_GEMM_IN));
     for (int b = 0; b < c.n_blocks; ++b) {
         const kva_ctx::Blk& B = ctx->blk[b];
         // h = (b == 0 ? 0 : h) + input/down partials; a = attn_norm(h)
-        KVA_TRY(fold(b > 0, B.g_attn, ctx->a16, false, false));
+        KVA_TRY(fold(b > 0, B.g_attn, ctx->a16, false));
         {
             GemmArgs g;
             g.A = ctx->a16; g.lda = d; set_b(g, B.wqkv, d);
@@ -619,24 +634,25 @@ kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n, float* co
             g.epi.out16 = ctx->qk16; g.epi.ld16 = 2 * hd;
             g.epi.vt = ctx->vt16; g.epi.ld_vt = ctx->m_alloc; g.epi.n_split = (int32_t)(2 * hd);
             g.epi.n_real = (int32_t)(3 * hd);
-            STAGE(KVA_STAGE_GEMM_QKV, launch_gemm(opd, pick_tile(n, g.N, 1), EPI_QKV, g, s));
+            STAGE(KVA_STAGE_GEMM_QKV, gemm(EPI_QKV, g));
         }
         STAGE(KVA_STAGE_ATTN, launch_attention(ctx->qk16, 2 * hd, (int32_t)hd, ctx->vt16, ctx->m_alloc, ctx->o16, hd, n,
-                                c.n_heads, c.attn_block, s));
+                                               c.n_heads, c.attn_block, t32, s));
         KVA_TRY(narrow(ctx->o16, hd, B.wo, KVA_STAGE_GEMM_O));
-        KVA_TRY(fold(true, B.g_ffn, ctx->a16, false, false));           // h += O partials; a = ffn_norm(h)
+        KVA_TRY(fold(true, B.g_ffn, ctx->a16, false));           // h += O partials; a = ffn_norm(h)
         {
             GemmArgs g;
             g.A = ctx->a16; g.lda = d; set_b(g, B.wgu, d);
             g.M = n; g.N = (int32_t)round_up(2 * F, kColPad); g.K = (int32_t)d;
             g.epi.out16 = ctx->act16; g.epi.ld16 = F; g.epi.n_real = (int32_t)(2 * F);
-            STAGE(KVA_STAGE_GEMM_GATEUP, launch_gemm(opd, pick_tile(n, g.N, 1), EPI_SWIGLU, g, s));
+            g.epi.out16_t32 = t32;
+            STAGE(KVA_STAGE_GEMM_GATEUP, gemm(EPI_SWIGLU, g));
         }
         KVA_TRY(narrow(ctx->act16, F, B.wd, KVA_STAGE_GEMM_DOWN));
     }
     // h += down partials; z = out_norm(h): bf16 in the tiled32 layout of the
     // four-stage head GEMM, or fp16 row-major for the q8_0 head GEMM
-    KVA_TRY(fold(true, ctx->g_out, ctx->z16, !ctx->q8, !ctx->q8));
+    KVA_TRY(fold(true, ctx->g_out, ctx->z16, !ctx->q8));
     {
         GemmArgs g;
         g.A = ctx->z16; g.lda = d; set_b(g, ctx->w_heads, d);
@@ -646,8 +662,8 @@ kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n, float* co
         g.epi.tail_head = ctx->tail_head; g.epi.tail_col = ctx->tail_col;
         g.epi.tail_start = ctx->tail_start; g.epi.bias = ctx->b_heads;
         g.epi.heads = ho;
-        if (ctx->q8) STAGE(KVA_STAGE_GEMM_HEADS, launch_gemm(OPD_Q8, TILE_256x256, EPI_HEADS, g, s));
-        else STAGE(KVA_STAGE_GEMM_HEADS, launch_gemm_t32(OPD_BF16, EPI_HEADS, g, s));
+        if (ctx->q8) STAGE(KVA_STAGE_GEMM_HEADS, launch_gemm_q8(TILE_256x256, EPI_HEADS, g, s));
+        else STAGE(KVA_STAGE_GEMM_HEADS, launch_gemm_t32(OPD_BF16, TILE_256x256, EPI_HEADS, g, s));
     }
     ctx->stats.calls += 1;
     ctx->stats.tokens += (uint64_t)n;
