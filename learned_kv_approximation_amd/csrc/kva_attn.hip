@@ -58,9 +58,9 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
 // own K and V^T tile in LDS (prefetched into registers one tile ahead).  At
 // the end the groups' running (max, sum, O) are merged through LDS:
 //   m = max_g m_g,  l = sum_g l_g 2^(m_g - m),  O = sum_g O_g 2^(m_g - m) / l.
-// T32: O goes out in the tiled32_index layout of the next GEMM's A operand
-// (each 8-byte store is 4 consecutive columns inside one 8-value chunk).
-template <int KS, bool T32>
+// O goes out in the tiled32_index layout of the next GEMM's A operand (each
+// 8-byte store is 4 consecutive columns inside one 8-value chunk).
+template <int KS>
 __global__ void __launch_bounds__(128 * KS) attn_fwd(const uint16_t* __restrict__ qk, int64_t ld_qk,
                                                      int32_t k_off, const uint16_t* __restrict__ vt,
                                                      int64_t ld_vt, uint16_t* __restrict__ o,
@@ -299,7 +299,6 @@ __global__ void __launch_bounds__(128 * KS) attn_fwd(const uint16_t* __restrict_
 
     const float inv = 1.0f / l_i;
     if (myq < n) {
-        uint16_t* orow = o + (int64_t)myq * ld_o + h * HD;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -308,9 +307,7 @@ __global__ void __launch_bounds__(128 * KS) attn_fwd(const uint16_t* __restrict_
                 u32x2 pk;
                 pk[0] = pack_f16(oacc[dt][4 * q + 0] * inv, oacc[dt][4 * q + 1] * inv);
                 pk[1] = pack_f16(oacc[dt][4 * q + 2] * inv, oacc[dt][4 * q + 3] * inv);
-                const int col = dt * 32 + 8 * q + 4 * g;
-                if constexpr (T32) *(u32x2*)(o + tiled32_index(myq, h * HD + col, ld_o)) = pk;
-                else *(u32x2*)(orow + col) = pk;
+                *(u32x2*)(o + tiled32_index(myq, h * HD + dt * 32 + 8 * q + 4 * g, ld_o)) = pk;
             }
     }
 }
@@ -319,17 +316,13 @@ __global__ void __launch_bounds__(128 * KS) attn_fwd(const uint16_t* __restrict_
 
 hipError_t launch_attention(const uint16_t* qk, int64_t ld_qk, int32_t k_off, const uint16_t* vt,
                             int64_t ld_vt, uint16_t* o, int64_t ld_o, int32_t n, int32_t n_heads,
-                            int32_t attn_block, bool o_t32, hipStream_t s) {
+                            int32_t attn_block, hipStream_t s) {
     if (n <= 0) return hipSuccess;
-    if (attn_block % QT || (o_t32 && ld_o % 32)) return hipErrorInvalidValue;
+    if (attn_block % QT || ld_o % 32) return hipErrorInvalidValue;
     const int nblk = (n + attn_block - 1) / attn_block;
     const dim3 grid(n_heads * nblk * (attn_block / QT));
-    if (o_t32)
-        hipLaunchKernelGGL((attn_fwd<kKeySplit, true>), grid, dim3(128 * kKeySplit), 0, s, qk, ld_qk, k_off, vt,
-                           ld_vt, o, ld_o, n, n_heads, attn_block);
-    else
-        hipLaunchKernelGGL((attn_fwd<kKeySplit, false>), grid, dim3(128 * kKeySplit), 0, s, qk, ld_qk, k_off, vt,
-                           ld_vt, o, ld_o, n, n_heads, attn_block);
+    hipLaunchKernelGGL(attn_fwd<kKeySplit>, grid, dim3(128 * kKeySplit), 0, s, qk, ld_qk, k_off, vt, ld_vt, o,
+                       ld_o, n, n_heads, attn_block);
     return hipGetLastError();
 }
 

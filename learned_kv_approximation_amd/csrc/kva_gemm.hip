@@ -7,17 +7,15 @@
 // operand layout of the 32x32x16 MFMA: each lane feeds 8 consecutive
 // K-values of one row of A and 8 consecutive K-values of one row of W.
 //
-// Two kernels share the fused epilogues (fp32 split-K partial, fp16
-// Q|K plus transposed V, SwiGLU, bias + per-head scatter):
-//  - gemm_t32: 16-bit weights (fp16 trunk, bf16 heads).  Both operands are
-//    stored in the tiled32_index layout; four LDS stages of 32-wide slabs.
-//  - gemm_q8: q8_0 weights.  The activation (fp16, row-major) is copied into
-//    LDS directly; the weight half of each 64-wide slab goes through
-//    registers, where d*q is formed exactly and rounded once to fp16.
-// In both, workgroup ids are remapped so that the tiles of one weight strip
-// (all M-tiles of an N-tile) run back to back on the same XCD and share its
-// L2: the hardware deals workgroups to the 8 XCDs round-robin.  Accumulation
-// is fp32, over K in plain sequential order.
+// One kernel, gemm_t32, with fused epilogues (fp32 split-K partial, fp16
+// Q|K plus transposed V, SwiGLU, bias + per-head scatter).  Activations are
+// 16-bit in the tiled32_index layout; weights are 16-bit in the same layout
+// (fp16 trunk, bf16 heads) or q8_0 (int8 codes + fp16 scales, tiled the same
+// way, so a slab's weight bytes are half those of fp16).  Workgroup ids are
+// remapped so that the tiles of one weight strip (all M-tiles of an N-tile)
+// run back to back on the same XCD and share its L2: the hardware deals
+// workgroups to the 8 XCDs round-robin.  Accumulation is fp32, over K in
+// plain sequential order.
 #include "kva_internal.h"
 
 #include <type_traits>
@@ -31,11 +29,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BK = 64;          // gemm_q8: K per slab (fp16 elements): 128-byte LDS rows
-
-// gemm_q8's LDS swizzle: the 16-byte chunk c of row r sits at chunk c ^ swz(r),
-// so the 16 rows one ds_read_b128 phase touches land on distinct banks.
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 template <bool BF16>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
@@ -132,10 +125,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[MI][NI
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
-                    if (row < g.M) {
-                        const int64_t at = e.out16_t32 ? tiled32_index(row, f, e.ld16) : (int64_t)row * e.ld16 + f;
-                        e.out16[at] = to_f16_bits(silu(acc[i][j][r]) * acc[i][j + 1][r]);
-                    }
+                    if (row < g.M)
+                        e.out16[tiled32_index(row, f, e.ld16)] = to_f16_bits(silu(acc[i][j][r]) * acc[i][j + 1][r]);
                 }
         }
     } else if constexpr (EPI == EPI_HEADS) {
@@ -211,192 +202,76 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[MI][NI
     }
 }
 
-// q8_0 weights.  A BM x BN tile is computed by WGM x WGN waves, each owning
-// a (BM/WGM) x (BN/WGN) sub-tile.  The activation half of each 64-wide slab
-// is copied from global memory straight into LDS (global_load_lds, 16 bytes
-// per lane; one wave instruction fills 8 consecutive 128-byte rows): lane L
-// lands at row L/8, physical chunk L%8, so it fetches the logical chunk
-// (L%8) ^ swz(row) of that row.  Two LDS buffers, one barrier a slab.
-template <int BM, int BN, int WGM, int WGN, int EPI>
-__global__ void __launch_bounds__(64 * WGM * WGN) gemm_q8(GemmArgs g) {
-    constexpr int NW = WGM * WGN;
-    constexpr int WM = BM / WGM, WN = BN / WGN;
-    constexpr int MI = WM / 32, NI = WN / 32;
-    constexpr int AI = BM / (8 * NW);   // wave DMA instructions per slab
-    static_assert(AI >= 1 && MI >= 1 && NI >= 1, "tile too small for the wave grid");
-    static_assert(64 * NW == 2 * BN, "q8_0 weights: two threads per weight row");
-    constexpr int STAGE = (BM + BN) * BK;
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE];
-
-    const int mt = (g.M + BM - 1) / BM;
-    const int nt = g.N / BN;
-    const int S = g.splits;
-    const int total = mt * nt * S;
-    const int per_xcd = gridDim.x / 8;
-    const int v = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    if (v >= total) return;
-    // M-tiles fastest, then splits, then N-tiles: the tiles sharing a weight
-    // strip run back to back on one XCD
-    const int tm = v % mt;
-    const int split = (v / mt) % S;
-    const int tn = v / (mt * S);
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / WGN, wn = wave % WGN;
-
-    // rows >= M of A are padding rows of the activation scratch: loaded, never stored
-    const uint16_t* Ab = g.A + (int64_t)tm * BM * g.lda;
-    const int nk_all = g.K / BK;
-    int offa[AI];
-    {
-        const int rr = lane >> 3, pc = lane & 7;
-#pragma unroll
-        for (int i = 0; i < AI; ++i) {
-            const int row = (i * NW + wave) * 8 + rr;
-            offa[i] = row * (int)g.lda + ((pc ^ swz(row)) << 3);
-        }
-    }
-    auto issue = [&](int kt, int buf) {
-        uint16_t* sa = smem + buf * STAGE;
-#pragma unroll
-        for (int i = 0; i < AI; ++i)
-            __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Ab + offa[i] + kt * BK),
-                                             (lds_ptr_t)(sa + (i * NW + wave) * 8 * BK), 16, 0, 0);
-    };
-
-    // q8_0 weights: thread t owns one 32-code block of weight row t/2 per slab
-    // (half t%2 of the slab's 64 K-values): codes and scale go through
-    // registers, d*q is rounded once to fp16 and written to LDS.
-    const int qrow = tid >> 1, qhalf = tid & 1;
-    const int kblocks = g.K / 32;
-    const int8_t* Bq = g.Bq + ((int64_t)tn * BN + qrow) * g.ldb + qhalf * 32;
-    const uint16_t* Bs = g.Bs + ((int64_t)tn * BN + qrow) * kblocks + qhalf;
-    u32x4 qr0, qr1;
-    uint16_t qd = 0;
-    auto qload = [&](int kt) {
-        qr0 = *(const u32x4*)(Bq + kt * BK);
-        qr1 = *(const u32x4*)(Bq + kt * BK + 16);
-        qd = Bs[kt * 2];
-    };
-    auto qstore = [&](int buf) {
-        uint16_t* sb = smem + buf * STAGE + BM * BK + qrow * BK;
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-            const u32x4& src = c4 < 2 ? qr0 : qr1;
-            const uint32_t w0 = src[(c4 & 1) * 2], w1 = src[(c4 & 1) * 2 + 1];
-            u32x4 o;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t w = e < 2 ? w0 : w1;
-                const int q0 = (int)(int8_t)(w >> (16 * (e & 1)));
-                const int q1 = (int)(int8_t)(w >> (16 * (e & 1) + 8));
-                o[e] = (uint32_t)to_f16_bits(q8_0_value(qd, q0)) |
-                       ((uint32_t)to_f16_bits(q8_0_value(qd, q1)) << 16);
-            }
-            const int c = qhalf * 4 + c4;
-            *(u32x4*)(sb + ((c ^ swz(qrow)) << 3)) = o;
-        }
-    };
-
-    f32x16 acc[MI][NI];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NI; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    const int kb = split * nk_all / S;                 // this split's slabs: [kb, kb + nk)
-    const int nk = (split + 1) * nk_all / S - kb;
-    const int frow = lane & 31, fk = lane >> 5;
-    qload(kb);
-    issue(kb, 0);
-    qstore(0);
-    // global_load_lds completes through vmcnt: wait for it explicitly, then
-    // the barrier publishes the slab to every wave
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        // the other buffer was last read before the previous barrier: refill it
-        if (kt + 1 < nk) {
-            qload(kb + kt + 1);
-            issue(kb + kt + 1, buf ^ 1);
-        }
-        const uint16_t* sa = smem + buf * STAGE;
-        const uint16_t* sb = sa + BM * BK;
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            const int c = ks * 2 + fk;
-            u32x4 af[MI], bfr[NI];
-#pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                const int r = wm * WM + i * 32 + frow;
-                af[i] = *(const u32x4*)(sa + r * BK + ((c ^ swz(r)) << 3));
-            }
-#pragma unroll
-            for (int j = 0; j < NI; ++j) {
-                const int r = wn * WN + j * 32 + frow;
-                bfr[j] = *(const u32x4*)(sb + r * BK + ((c ^ swz(r)) << 3));
-            }
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int j = 0; j < NI; ++j) acc[i][j] = mfma32<false>(af[i], bfr[j], acc[i][j]);
-        }
-        if (kt + 1 < nk) qstore(buf ^ 1);
-        __builtin_amdgcn_s_waitcnt(0);   // the next slab has landed
-        __syncthreads();                 // ... for all waves, and all are done with this one
-    }
-
-    epilogue<BM, BN, WGM, WGN, EPI, MI, NI>(g, acc, tm, tn, split, smem);
-}
-
-template <int BM, int BN, int WGM, int WGN, int EPI>
-hipError_t launch_q8(const GemmArgs& a, hipStream_t s) {
-    if (a.N % BN) return hipErrorInvalidValue;
-    if (a.splits < 1 || a.splits > a.K / BK || (a.splits > 1 && EPI != EPI_PARTIAL)) return hipErrorInvalidValue;
-    const int mt = (a.M + BM - 1) / BM;
-    const int nt = a.N / BN;
-    const int total = mt * nt * a.splits;
-    const int grid = (total + 7) / 8 * 8;
-    hipLaunchKernelGGL((gemm_q8<BM, BN, WGM, WGN, EPI>), dim3(grid), dim3(64 * WGM * WGN), 0, s, a);
-    return hipGetLastError();
-}
-
-
-// Four-stage variant for operands that are both stored in the tiled32_index
-// layout (the head GEMM, and the trunk GEMMs when their weights are 16-bit).
-// BM x BN tiles (256x256 with 2 x 4 waves of 128 x 64, or 128x128 with 2 x 2
-// waves of 64 x 64, whose 64 KB of LDS lets two workgroups share a CU).
-//  - K is walked in 32-wide slabs; the A and the B half of a slab are each one
-//    contiguous block in global memory, copied straight into LDS (1 KB per
-//    wave instruction).  Four LDS stages: three slabs are in flight while one
-//    is consumed, which covers the L2 latency at full MFMA rate.
+// K is walked in 32-wide slabs through a ring of S LDS stages.
+//  - A slab's A rows and B rows are each one contiguous block in global
+//    memory (the tiled layouts), copied straight into LDS with
+//    global_load_lds (1 KB per wave instruction; the q8_0 scales 64 bytes).
+//    S - 1 slabs are in flight while one is consumed, which covers the L2
+//    latency at full MFMA rate.
 //  - The MFMA fragments are double-buffered in registers: the LDS reads of
 //    the next 16-wide K step are issued before the MFMAs of the current one,
 //    including across the slab barrier, so LDS latency hides behind MFMAs.
-//    The K order of the accumulation is the plain one (slab by slab, step by
+//    q8_0: a lane's weight fragment (8 codes of one row and that row's block
+//    scale) is read raw and turned into fp16 after the current MFMAs are
+//    issued: d*q is one correctly rounded fp16 multiply, which is exactly the
+//    fp32 product d*q (11 x 8 significant bits) rounded once to fp16.
+//  - The K order of the accumulation is the plain one (slab by slab, step by
 //    step) for every tile shape, so the tile choice never changes the bits.
 //  - Each slab ends with one barrier: it publishes the next slab (every wave
-//    has waited for its own DMA of it) and frees the stage the DMA of the
-//    slab after next refills.
+//    has waited for its own DMA of it) and frees the stage the next DMA
+//    refills.
 //  - Split-K (EPI_PARTIAL only): the slabs are cut into `splits` consecutive
 //    ranges, one per workgroup, each writing its own partial buffer.
+// Tiles: 256x256 with 2 x 4 waves of 128 x 64, or 128x128 (small enough in
+// LDS for two or three workgroups per CU) with 2 x 2 waves of 64 x 64, or for
+// q8_0 (except SwiGLU, whose gate/up pairs need two 32-column blocks a wave)
+// 1 x 4 waves of 128 x 32, so that each weight fragment is converted by one
+// wave only.
+template <int BM, int BN, int OPD, int EPI>
+struct T32Shape {
+    static constexpr bool Q8 = OPD == OPD_Q8;
+    static constexpr int KB = 32;
+    static constexpr int A_BYTES = BM * KB * 2;
+    static constexpr int B_BYTES = Q8 ? BN * KB : BN * KB * 2;      // codes or 16-bit values
+    static constexpr int S_BYTES = Q8 ? BN * 2 : 0;                 // q8_0 scales
+    static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+    // the head epilogue stages 128 KB through LDS
+    static constexpr int S = (EPI == EPI_HEADS) ? (128 * 1024 + STAGE - 1) / STAGE : 4;
+};
+
+// q8_0 weight fragment: codes (8 consecutive K-values of one row) and the
+// row's fp16 block scale -> the 8 fp16 weights RNE(d * q).
+__device__ __forceinline__ u32x4 q8_fragment(u32x2 codes, uint16_t d_bits) {
+    const _Float16 d = __builtin_bit_cast(_Float16, d_bits);
+    u32x4 out;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        const uint32_t w = codes[h >> 1] >> (16 * (h & 1));
+        const _Float16 lo = (_Float16)(int8_t)(w & 0xFF) * d;
+        const _Float16 hi = (_Float16)(int8_t)((w >> 8) & 0xFF) * d;
+        out[h] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    return out;
+}
+
 template <int BM, int BN, int WGM, int WGN, int OPD, int EPI>
 __global__ void __launch_bounds__(64 * WGM * WGN) gemm_t32(GemmArgs g) {
+    using Sh = T32Shape<BM, BN, OPD, EPI>;
     constexpr bool BF16 = OPD == OPD_BF16;
-    constexpr int NW = WGM * WGN, KB = 32, S = 4;
+    constexpr bool Q8 = Sh::Q8;
+    constexpr int NW = WGM * WGN, KB = Sh::KB, S = Sh::S;
     constexpr int WM = BM / WGM, WN = BN / WGN, MI = WM / 32, NI = WN / 32;
-    constexpr int AI = BM / (16 * NW), BI = BN / (16 * NW);   // DMA instructions per wave per slab
-    constexpr int L = AI + BI;
-    constexpr int STAGE = (BM + BN) * KB;
-    static_assert(AI >= 1 && BI >= 1, "tile too small for the wave grid");
-    static_assert(EPI != EPI_HEADS || S * STAGE * 2 >= 128 * 1024, "the head epilogue stages 128 KB through LDS");
-    static_assert((S - 2) * L < 16, "vmcnt immediate");
+    constexpr int AI = Sh::A_BYTES / (1024 * NW), BI = Sh::B_BYTES / (1024 * NW);   // DMA instrs / wave / slab
+    // q8_0 scales: every wave copies 64 bytes of them (16 lanes x 4 bytes),
+    // so that every wave issues the same number of DMA instructions a slab
+    constexpr int L = AI + BI + (Q8 ? 1 : 0);
+    static_assert(AI >= 1 && BI >= 1 && AI * 1024 * NW == Sh::A_BYTES && BI * 1024 * NW == Sh::B_BYTES,
+                  "tile too small for the wave grid");
+    static_assert(!Q8 || Sh::S_BYTES == NW * 64, "scale DMA split");
+    static_assert((S - 2) * L < 64, "vmcnt range");
+    static_assert(EPI != EPI_HEADS || S * Sh::STAGE >= 128 * 1024, "the head epilogue stages 128 KB through LDS");
     static_assert(kWeightTileRows % BM == 0 && kWeightTileRows % BN == 0, "tiles inside 256-row groups");
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[S * STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[S * Sh::STAGE];
 
     const int mt = (g.M + BM - 1) / BM;
     const int nt = g.N / BN;
@@ -416,25 +291,47 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_t32(GemmArgs g) {
     const int nk_all = g.K / KB;
     const int kb = split * nk_all / SP;                // this split's slabs: [kb, kb + nk)
     const int nk = (split + 1) * nk_all / SP - kb;
-    // slab kt of the rows [r0, r0 + BM) of a 256-row group t starts at
-    // ((t * nk_all + kt) * 256 + r0) * KB
-    const uint16_t* Ab = g.A + (((int64_t)(tm * BM / kWeightTileRows) * nk_all + kb) * kWeightTileRows +
-                                (tm * BM) % kWeightTileRows) * KB;
-    const uint16_t* Bb = g.B + (((int64_t)(tn * BN / kWeightTileRows) * nk_all + kb) * kWeightTileRows +
-                                (tn * BN) % kWeightTileRows) * KB;
+    // slab kt of the rows [r0, r0 + BM) of 256-row group t starts at element
+    // (t * nk_all + kt) * 256 * KB + r0 * KB (q8_0 codes: bytes, scales: (..) * 256 + r0)
+    const int64_t a_slab0 = ((int64_t)(tm * BM / kWeightTileRows) * nk_all + kb);
+    const int64_t b_slab0 = ((int64_t)(tn * BN / kWeightTileRows) * nk_all + kb);
+    const uint8_t* Ab = reinterpret_cast<const uint8_t*>(g.A) +
+                        (a_slab0 * kWeightTileRows + (tm * BM) % kWeightTileRows) * KB * 2;
+    const uint8_t* Bb = Q8 ? reinterpret_cast<const uint8_t*>(g.Bq) +
+                                 (b_slab0 * kWeightTileRows + (tn * BN) % kWeightTileRows) * KB
+                           : reinterpret_cast<const uint8_t*>(g.B) +
+                                 (b_slab0 * kWeightTileRows + (tn * BN) % kWeightTileRows) * KB * 2;
+    const uint8_t* Sb = Q8 ? reinterpret_cast<const uint8_t*>(g.Bs) +
+                                 (b_slab0 * kWeightTileRows + (tn * BN) % kWeightTileRows) * 2
+                           : nullptr;
+    constexpr int64_t A_SLAB = (int64_t)kWeightTileRows * KB * 2;              // bytes between slabs
+    constexpr int64_t B_SLAB = (int64_t)kWeightTileRows * KB * (Q8 ? 1 : 2);
+    constexpr int64_t S_SLAB = (int64_t)kWeightTileRows * 2;
     auto issue = [&](int kt, int st) {
-        uint16_t* sa = smem + st * STAGE;
-        uint16_t* sb = sa + BM * KB;
-        const int64_t o = (int64_t)kt * kWeightTileRows * KB;
+        uint8_t* sa = smem + st * Sh::STAGE;
+        uint8_t* sb = sa + Sh::A_BYTES;
 #pragma unroll
         for (int i = 0; i < AI; ++i)
-            __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Ab + o + (i * NW + wave) * 16 * KB + lane * 8),
-                                             (lds_ptr_t)(sa + (i * NW + wave) * 16 * KB), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Ab + kt * A_SLAB + (i * NW + wave) * 1024 + lane * 16),
+                                             (lds_ptr_t)(sa + (i * NW + wave) * 1024), 16, 0, 0);
 #pragma unroll
         for (int i = 0; i < BI; ++i)
-            __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Bb + o + (i * NW + wave) * 16 * KB + lane * 8),
-                                             (lds_ptr_t)(sb + (i * NW + wave) * 16 * KB), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Bb + kt * B_SLAB + (i * NW + wave) * 1024 + lane * 16),
+                                             (lds_ptr_t)(sb + (i * NW + wave) * 1024), 16, 0, 0);
+        if constexpr (Q8) {
+            if (lane < 16)
+                __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Sb + kt * S_SLAB + wave * 64 + lane * 4),
+                                                 (lds_ptr_t)(sb + Sh::B_BYTES + wave * 64), 4, 0, 0);
+        }
     };
+    // vmcnt(n) with lgkmcnt / expcnt left alone; lgkmcnt(0) alone.  (The
+    // builtin, unlike inline asm, is seen by the compiler's own wait
+    // insertion, which then knows which LDS reads have landed.)
+    auto vm_wait = [](auto n) {
+        constexpr int N = decltype(n)::value;
+        __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+    };
+    auto lds_wait = []() { __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14)); };
     f32x16 acc[MI][NI];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -444,30 +341,44 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_t32(GemmArgs g) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     const int frow = lane & 31, fk = lane >> 5;
     const int sw = ((frow >> 1) ^ (frow >> 3)) & 3;     // fragment rows differ by multiples of 32
+    const int swq = (frow >> 2) & 3;                    // q8_0 code chunk swizzle
     int aoff[MI], boff[NI];
 #pragma unroll
-    for (int i = 0; i < MI; ++i) aoff[i] = (wm * WM + i * 32 + frow) * KB;
+    for (int i = 0; i < MI; ++i) aoff[i] = (wm * WM + i * 32 + frow) * KB * 2;
 #pragma unroll
-    for (int j = 0; j < NI; ++j) boff[j] = BM * KB + (wn * WN + j * 32 + frow) * KB;
+    for (int j = 0; j < NI; ++j) boff[j] = Sh::A_BYTES + (wn * WN + j * 32 + frow) * KB * (Q8 ? 1 : 2);
+    // fragments: fa/fb ready for the MFMA; for q8_0, qc/qs hold the raw codes and scales
     u32x4 fa0[MI], fb0[NI], fa1[MI], fb1[NI];
-    auto rd = [&](int st, int ks, u32x4* fa, u32x4* fb) {
-        const uint16_t* base = smem + st * STAGE;
-        const int c = ((ks * 2 + fk) ^ sw) << 3;
+    u32x2 qc0[NI], qc1[NI];
+    uint16_t qs0[NI], qs1[NI];
+    auto rd = [&](int st, int ks, u32x4* fa, u32x4* fb, u32x2* qc, uint16_t* qs) {
+        const uint8_t* base = smem + st * Sh::STAGE;
+        const int c = ((ks * 2 + fk) ^ sw) << 4;
 #pragma unroll
         for (int i = 0; i < MI; ++i) fa[i] = *(const u32x4*)(base + aoff[i] + c);
+        if constexpr (Q8) {
+            const int cq = ((ks * 2 + fk) ^ swq) << 3;
 #pragma unroll
-        for (int j = 0; j < NI; ++j) fb[j] = *(const u32x4*)(base + boff[j] + c);
+            for (int j = 0; j < NI; ++j) {
+                qc[j] = *(const u32x2*)(base + boff[j] + cq);
+                qs[j] = *(const uint16_t*)(base + Sh::A_BYTES + Sh::B_BYTES + (wn * WN + j * 32 + frow) * 2);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NI; ++j) fb[j] = *(const u32x4*)(base + boff[j] + c);
+        }
+    };
+    auto cvt = [&](u32x4* fb, const u32x2* qc, const uint16_t* qs) {
+        if constexpr (Q8) {
+#pragma unroll
+            for (int j = 0; j < NI; ++j) fb[j] = q8_fragment(qc[j], qs[j]);
+        }
     };
     auto mm = [&](const u32x4* fa, const u32x4* fb) {
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < NI; ++j) acc[i][j] = mfma32<BF16>(fa[i], fb[j], acc[i][j]);
-    };
-    // vmcnt(n) with lgkmcnt / expcnt left alone
-    auto vm_wait = [](auto n) {
-        constexpr int N = decltype(n)::value;
-        __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
     };
 
 #pragma unroll
@@ -477,34 +388,67 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_t32(GemmArgs g) {
     else vm_wait(std::integral_constant<int, 0>{});
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
-    rd(0, 0, fa0, fb0);
-    for (int kt = 0; kt < nk; ++kt) {
-        const bool more = kt + S - 1 < nk;
+    rd(0, 0, fa0, fb0, qc0, qs0);
+    cvt(fb0, qc0, qs0);
+    lds_wait();
+    // Instruction order of one K step: the LDS reads of the next step first,
+    // then the current MFMAs (q8_0: with the conversion of the next
+    // fragments between their two halves; it waits for the reads, and the
+    // first MFMAs cover that latency).
+    auto order = [&]() {
+        if constexpr (Q8) {
+            __builtin_amdgcn_sched_group_barrier(0x100, MI + 2 * NI, 0);   // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x008, MI * NI / 2, 0);   // MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);            // VALU: conversion
+            __builtin_amdgcn_sched_group_barrier(0x008, MI * NI / 2, 0);   // MFMAs
+        } else {
+            // one LDS read after each of the first MFMAs
+#pragma unroll
+            for (int q = 0; q < MI + NI; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, MI * NI - (MI + NI), 0);
+        }
+    };
+    // one slab; MORE: a later slab is still to be issued (the drain of the
+    // last S - 1 slabs runs as its own loop so that neither loop branches)
+    auto slab = [&](int kt, auto more_c) {
+        constexpr bool MORE = decltype(more_c)::value;
         // the stage of slab kt-1 was released by the previous barrier
-        if (more) issue(kt + S - 1, (kt + S - 1) % S);
-        rd(kt % S, 1, fa1, fb1);
+        if constexpr (MORE) issue(kt + S - 1, (kt + S - 1) % S);
+        rd(kt % S, 1, fa1, fb1, qc1, qs1);
         mm(fa0, fb0);
-        if (more) vm_wait(std::integral_constant<int, (S - 2) * L>{});   // slab kt+1 has landed
+        cvt(fb1, qc1, qs1);
+        order();
+        __builtin_amdgcn_sched_barrier(0);      // the waits below stay after this step's MFMAs
+        if constexpr (MORE) vm_wait(std::integral_constant<int, (S - 2) * L>{});   // slab kt+1 has landed
         else vm_wait(std::integral_constant<int, 0>{});
-        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");           // slab kt fully read
+        lds_wait();                                                      // slab kt fully read
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         __asm__ volatile("" ::: "memory");
         // after the last slab this reads a stale stage (in bounds); the values are not used
-        rd((kt + 1) % S, 0, fa0, fb0);
+        rd((kt + 1) % S, 0, fa0, fb0, qc0, qs0);
         mm(fa1, fb1);
+        cvt(fb0, qc0, qs0);
+        order();
         __builtin_amdgcn_sched_barrier(0);
-    }
-    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        lds_wait();     // the next step's fragments: long landed, and now known to be
+    };
+    int kt = 0;
+    for (; kt + S - 1 < nk; ++kt) slab(kt, std::true_type{});
+    for (; kt < nk; ++kt) slab(kt, std::false_type{});
     if constexpr (EPI == EPI_HEADS) __syncthreads();    // the head epilogue reuses LDS
-    epilogue<BM, BN, WGM, WGN, EPI, MI, NI>(g, acc, tm, tn, split, smem);
+    epilogue<BM, BN, WGM, WGN, EPI, MI, NI>(g, acc, tm, tn, split, reinterpret_cast<uint16_t*>(smem));
 }
 
 template <int BM, int BN, int WGM, int WGN, int OPD, int EPI>
 hipError_t launch_t32(const GemmArgs& a, hipStream_t s) {
     if (a.N % BN) return hipErrorInvalidValue;
     if (a.splits < 1 || a.splits > a.K / 32 || (a.splits > 1 && EPI != EPI_PARTIAL)) return hipErrorInvalidValue;
+    if (OPD == OPD_Q8 ? (!a.Bq || !a.Bs) : !a.B) return hipErrorInvalidValue;
     const int total = ((a.M + BM - 1) / BM) * (a.N / BN) * a.splits;
     const int grid = (total + 7) / 8 * 8;
     hipLaunchKernelGGL((gemm_t32<BM, BN, WGM, WGN, OPD, EPI>), dim3(grid), dim3(64 * WGM * WGN), 0, s, a);
@@ -513,24 +457,7 @@ hipError_t launch_t32(const GemmArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// The instantiated (tile, epilogue) combinations of each kernel.
-#define KVA_Q8_CASE(TILE_, EPI_, BM_, BN_, WGM_, WGN_) \
-    if (tile == TILE_ && epi == EPI_) return launch_q8<BM_, BN_, WGM_, WGN_, EPI_>(a, s);
-
-hipError_t launch_gemm_q8(GemmTile tile, EpiKind epi, const GemmArgs& a, hipStream_t s) {
-    if (a.M <= 0) return hipSuccess;
-    if (a.K % BK != 0 || a.K <= 0) return hipErrorInvalidValue;
-    if (!a.Bq || !a.Bs) return hipErrorInvalidValue;
-    KVA_Q8_CASE(TILE_256x256, EPI_HEADS, 256, 256, 2, 4)
-    KVA_Q8_CASE(TILE_256x256, EPI_PARTIAL, 256, 256, 2, 4)
-    KVA_Q8_CASE(TILE_256x256, EPI_SWIGLU, 256, 256, 2, 4)
-    KVA_Q8_CASE(TILE_256x256, EPI_QKV, 256, 256, 2, 4)
-    KVA_Q8_CASE(TILE_128x128, EPI_PARTIAL, 128, 128, 2, 2)
-    KVA_Q8_CASE(TILE_128x128, EPI_QKV, 128, 128, 2, 2)
-    KVA_Q8_CASE(TILE_128x128, EPI_SWIGLU, 128, 128, 2, 2)
-    return hipErrorNotSupported;
-}
-#undef KVA_Q8_CASE
+// The instantiated (operand, tile, epilogue) combinations.
 
 #define KVA_T32_CASE(OPD_, TILE_, EPI_, BM_, BN_, WGM_, WGN_) \
     if (opd == OPD_ && tile == TILE_ && epi == EPI_) return launch_t32<BM_, BN_, WGM_, WGN_, OPD_, EPI_>(a, s);
@@ -545,6 +472,13 @@ hipError_t launch_gemm_t32(GemmOperand opd, GemmTile tile, EpiKind epi, const Ge
     KVA_T32_CASE(OPD_F16, TILE_128x128, EPI_PARTIAL, 128, 128, 2, 2)
     KVA_T32_CASE(OPD_F16, TILE_128x128, EPI_QKV, 128, 128, 2, 2)
     KVA_T32_CASE(OPD_F16, TILE_128x128, EPI_SWIGLU, 128, 128, 2, 2)
+    KVA_T32_CASE(OPD_Q8, TILE_256x256, EPI_HEADS, 256, 256, 2, 4)
+    KVA_T32_CASE(OPD_Q8, TILE_256x256, EPI_PARTIAL, 256, 256, 2, 4)
+    KVA_T32_CASE(OPD_Q8, TILE_256x256, EPI_QKV, 256, 256, 2, 4)
+    KVA_T32_CASE(OPD_Q8, TILE_256x256, EPI_SWIGLU, 256, 256, 2, 4)
+    KVA_T32_CASE(OPD_Q8, TILE_128x128, EPI_PARTIAL, 128, 128, 1, 4)
+    KVA_T32_CASE(OPD_Q8, TILE_128x128, EPI_QKV, 128, 128, 1, 4)
+    KVA_T32_CASE(OPD_Q8, TILE_128x128, EPI_SWIGLU, 128, 128, 2, 2)
     return hipErrorNotSupported;
 }
 #undef KVA_T32_CASE

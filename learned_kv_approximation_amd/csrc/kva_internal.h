@@ -31,6 +31,19 @@ __host__ __device__ inline int64_t tiled32_index(int64_t row, int64_t k, int64_t
     const int64_t sw = ((r >> 1) ^ (r >> 3)) & 3;
     return ((nb * (K / 32) + kt) * kWeightTileRows + r) * 32 + ((c ^ sw) * 8) + e;
 }
+// q8_0 weights [rows][K] use the same grouping: for each 256-row group and
+// each 32-wide K slab (exactly one q8_0 block per row), the int8 codes of the
+// 256 rows form one contiguous 8 KB block of 32-byte rows, the 8-byte chunk c
+// of row r at chunk c ^ ((r >> 2) & 3); the fp16 scales of the same rows form
+// one contiguous 512-byte block.
+__host__ __device__ inline int64_t q8_code_index(int64_t row, int64_t k, int64_t K) {
+    const int64_t nb = row / kWeightTileRows, r = row % kWeightTileRows, kt = k / 32;
+    const int64_t c = (k % 32) / 8, e = k % 8;
+    return ((nb * (K / 32) + kt) * kWeightTileRows + r) * 32 + ((c ^ ((r >> 2) & 3)) * 8) + e;
+}
+__host__ __device__ inline int64_t q8_scale_index(int64_t row, int64_t kblock, int64_t K) {
+    return ((row / kWeightTileRows) * (K / 32) + kblock) * kWeightTileRows + row % kWeightTileRows;
+}
 
 struct HeadOut {
     float* ptr[kMaxHeads];
@@ -39,7 +52,7 @@ struct HeadOut {
 
 enum EpiKind : int {
     EPI_QKV = 2,        // n < n_split: out16[m][n] = fp16(acc); else vt[n - n_split][m] = fp16(acc)
-    EPI_SWIGLU = 3,     // gate/up interleaved per 32 columns: out16[m][f] = fp16(silu(g) * u)
+    EPI_SWIGLU = 3,     // gate/up interleaved per 32 columns: out16[tiled32_index(m, f, ld16)] = fp16(silu(g) * u)
     EPI_HEADS = 4,      // bias add, scatter to per-head fp32 outputs
     EPI_PARTIAL = 5     // split-K partial: out_f32[split * split_stride + m * ld_f32 + n] = acc
 };
@@ -51,7 +64,6 @@ struct EpiArgs {
     int64_t ld16 = 0;
     uint16_t* vt = nullptr;
     int64_t ld_vt = 0;
-    int32_t out16_t32 = 0;              // EPI_SWIGLU: out16 in the tiled32_index layout (K = ld16)
     int32_t n_split = 0;
     int32_t n_real = 0;                 // real (unpadded) columns of the product
     const int32_t* tile_head = nullptr; // per 256-column tile: head, or -1 for a tail tile
@@ -63,20 +75,20 @@ struct EpiArgs {
     HeadOut heads;
 };
 
-// C[M][N] = A[M][K] * B[N][K]^T with 16-bit activations and fp32
-// accumulation.  16-bit weights: B (tiled32 layout, ldb unused).  q8_0
-// weights: int8 codes Bq[N][ldb] and one fp16 scale per 32 codes,
-// Bs[N][K/32]; the weight is d * q (see q8_0_value).
+// C[M][N] = A[M][K] * B[N][K]^T with 16-bit activations (tiled32 layout)
+// and fp32 accumulation.  16-bit weights: B (tiled32 layout).  q8_0 weights:
+// int8 codes Bq (q8_code_index layout) and one fp16 scale per 32 codes, Bs
+// (q8_scale_index layout); the weight is d * q (see q8_0_value), rounded
+// once to fp16 for the MFMA.
 struct GemmArgs {
     const uint16_t* A = nullptr;
     int64_t lda = 0;
     const uint16_t* B = nullptr;
-    int64_t ldb = 0;
     const int8_t* Bq = nullptr;
     const uint16_t* Bs = nullptr;
     int32_t M = 0;       // rows of A that are real (stores are masked to M)
     int32_t N = 0;       // columns, a multiple of the tile width (weights are padded)
-    int32_t K = 0;       // multiple of 32 (gemm_t32) or 64 (gemm_q8)
+    int32_t K = 0;       // multiple of 32
     // Split-K: the K slabs are cut into `splits` consecutive ranges, one per
     // workgroup; each range's partial product goes to its own buffer
     // (EPI_PARTIAL).  The split count must depend only on (N, K), never on M,
@@ -86,8 +98,9 @@ struct GemmArgs {
     EpiArgs epi;
 };
 
-// Operand type of gemm_t32: both operands fp16 or both bf16.
-enum GemmOperand : int { OPD_F16 = 0, OPD_BF16 = 1 };
+// Operand type: both operands fp16, both bf16, or fp16 activations with
+// q8_0 weights (fp16 MFMA on d*q rounded once to fp16).
+enum GemmOperand : int { OPD_F16 = 0, OPD_BF16 = 1, OPD_Q8 = 2 };
 
 // One q8_0 weight: the fp16 block scale (bit pattern d_bits) times the int8
 // code, exactly (an 11-bit significand times an 8-bit integer fits fp32's 24
@@ -98,43 +111,36 @@ __device__ __forceinline__ float q8_0_value(uint16_t d_bits, int q) {
 // 256x256: 8 waves (2 per SIMD); 128x128: 4 waves.
 enum GemmTile : int { TILE_256x256 = 0, TILE_128x128 = 1 };
 
-// q8_0 weights: A fp16 row-major (rows padded to the tile), fp16 MFMA on the
-// weights d*q rounded once to fp16; K a multiple of 64.
-hipError_t launch_gemm_q8(GemmTile tile, EpiKind epi, const GemmArgs& args, hipStream_t stream);
-
-// The same product with both operands in the tiled32_index layout (A rows
-// grouped by 256 like the weight rows; rows >= M of the last group are read
-// and dropped).  Four LDS stages of 32-wide slabs; tiles 256x256 or 128x128.
-// 16-bit operands only (OPD_F16 / OPD_BF16); K a multiple of 32.
+// The GEMM.  A rows are grouped by 256 like the weight rows (rows >= M of
+// the last group are read and dropped).  32-wide K slabs through a ring of
+// LDS stages; tiles 256x256 or 128x128.
 hipError_t launch_gemm_t32(GemmOperand opd, GemmTile tile, EpiKind epi, const GemmArgs& args,
                            hipStream_t stream);
 
 // Folds split-K partials into the residual stream and normalises it:
 //   h[r][c] = (add ? h[r][c] : 0) + P_0[r][c] + P_1[r][c] + ... (this order),
 //   out[r][c] = 16-bit(h[r][c] / sqrt(mean_c h[r][c]^2 + eps) * g[c]).
-// P_s = partials + s * pstride, rows of ldp.  With out_t32 the output goes
-// to out[tiled32_index(r, c, cols)] instead (ldo unused; cols % 32 == 0).
+// P_s = partials + s * pstride, rows of ldp.  out is in the tiled32_index
+// layout (K = cols; cols % 32 == 0).
 hipError_t launch_fold_rmsnorm(float* h, int64_t ldh, bool add, const float* partials, int32_t splits,
                                int64_t pstride, int64_t ldp, const float* g, int32_t rows, int32_t cols,
-                               float eps, uint16_t* out, int64_t ldo, bool bf16, bool out_t32,
-                               hipStream_t stream);
+                               float eps, uint16_t* out, bool bf16, hipStream_t stream);
 
 // dst[r][c] = src[tiled32_index(r, c, cols)] for r < rows (16-bit values).
 hipError_t launch_untile32(const uint16_t* src, uint16_t* dst, int32_t rows, int32_t cols, hipStream_t stream);
 
-// out[r][c] = 16-bit(x[r][c] / sqrt(mean_c x[r][c]^2 + eps) * g[c]); fp16 or bf16.
-// With out_t32 the output goes to out[tiled32_index(r, c, cols)] (ldo unused).
+// out[tiled32_index(r, c, cols)] = 16-bit(x[r][c] / sqrt(mean_c x[r][c]^2 + eps) * g[c]);
+// fp16 or bf16; cols % 32 == 0.
 hipError_t launch_rmsnorm_cast(const float* x, int64_t ldx, const float* g, int32_t rows,
-                               int32_t cols, float eps, uint16_t* out, int64_t ldo, bool bf16,
-                               bool out_t32, hipStream_t stream);
+                               int32_t cols, float eps, uint16_t* out, bool bf16, hipStream_t stream);
 
 // Block-causal multi-head attention with heads of 128.
 //   qk: [n][ld_qk] fp16, Q of head h at columns [h*128, h*128+128), K at k_off + h*128
 //   vt: [n_heads*128][ld_vt] fp16, V transposed (vt[c][t])
-//   o : [n][ld_o] fp16, or with o_t32 o[tiled32_index(t, c, ld_o)]
+//   o : fp16 at o[tiled32_index(t, c, ld_o)] (ld_o = n_heads*128, a multiple of 32)
 hipError_t launch_attention(const uint16_t* qk, int64_t ld_qk, int32_t k_off, const uint16_t* vt,
                             int64_t ld_vt, uint16_t* o, int64_t ld_o, int32_t n_tokens,
-                            int32_t n_heads, int32_t attn_block, bool o_t32, hipStream_t stream);
+                            int32_t n_heads, int32_t attn_block, hipStream_t stream);
 
 struct KvWriteArgs {
     const float* kv;

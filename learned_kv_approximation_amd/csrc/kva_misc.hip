@@ -21,11 +21,12 @@ __device__ __forceinline__ uint16_t to_bits(float v, bool bf16) {
 // input norm, the two pre-norms of each block and the final norm):
 // y = x / sqrt(mean(x^2) + eps) * g.  One workgroup per row; fixed
 // reduction order, so a row's result never depends on other rows.
-template <bool BF16, bool T32>
+// The output goes out in the tiled32_index layout of the next GEMM's A
+// operand (4 consecutive columns stay within one 8-value chunk).
+template <bool BF16>
 __global__ void __launch_bounds__(256) rmsnorm_cast(const float* __restrict__ x, int64_t ldx,
                                                     const float* __restrict__ gain, int32_t cols,
-                                                    float eps, uint16_t* __restrict__ out,
-                                                    int64_t ldo) {
+                                                    float eps, uint16_t* __restrict__ out) {
     __shared__ float part[4];
     const int row = blockIdx.x, tid = threadIdx.x;
     const float* xr = x + (int64_t)row * ldx;
@@ -39,7 +40,6 @@ __global__ void __launch_bounds__(256) rmsnorm_cast(const float* __restrict__ x,
     __syncthreads();
     const float tot = (part[0] + part[1]) + (part[2] + part[3]);
     const float r = 1.0f / sqrtf(tot / (float)cols + eps);
-    uint16_t* orow = out + (int64_t)row * ldo;
     for (int c = tid * 4; c < cols; c += 1024) {
         const float4 v = *(const float4*)(xr + c);
         const float4 gg = *(const float4*)(gain + c);
@@ -48,22 +48,21 @@ __global__ void __launch_bounds__(256) rmsnorm_cast(const float* __restrict__ x,
         o.y = to_bits(v.y * r * gg.y, BF16);
         o.z = to_bits(v.z * r * gg.z, BF16);
         o.w = to_bits(v.w * r * gg.w, BF16);
-        if constexpr (T32) *(ushort4*)(out + tiled32_index(row, c, cols)) = o;
-        else *(ushort4*)(orow + c) = o;
+        *(ushort4*)(out + tiled32_index(row, c, cols)) = o;
     }
 }
 
 // Split-K fold + RMSNorm: the residual update that follows a split GEMM,
 // fused with the norm that reads the updated residual.  The partials are
 // added in a fixed order, so the result is deterministic and independent of
-// how many rows the call has.  T32: the output goes out in the tiled32_index
-// layout (4 consecutive columns stay within one 8-value chunk).
-template <bool BF16, bool T32>
+// how many rows the call has.  The normalised output goes out in the
+// tiled32_index layout (4 consecutive columns stay within one 8-value chunk).
+template <bool BF16>
 __global__ void __launch_bounds__(256) fold_rmsnorm(float* __restrict__ h, int64_t ldh, int add,
                                                     const float* __restrict__ partials, int32_t splits,
                                                     int64_t pstride, int64_t ldp,
                                                     const float* __restrict__ gain, int32_t cols, float eps,
-                                                    uint16_t* __restrict__ out, int64_t ldo) {
+                                                    uint16_t* __restrict__ out) {
     __shared__ float part[4];
     const int row = blockIdx.x, tid = threadIdx.x;
     float* hr = h + (int64_t)row * ldh;
@@ -83,7 +82,6 @@ __global__ void __launch_bounds__(256) fold_rmsnorm(float* __restrict__ h, int64
     __syncthreads();
     const float tot = (part[0] + part[1]) + (part[2] + part[3]);
     const float r = 1.0f / sqrtf(tot / (float)cols + eps);
-    uint16_t* orow = out + (int64_t)row * ldo;
     for (int c = tid * 4; c < cols; c += 1024) {
         const float4 v = *(const float4*)(hr + c);     // written above by this thread
         const float4 gg = *(const float4*)(gain + c);
@@ -92,8 +90,7 @@ __global__ void __launch_bounds__(256) fold_rmsnorm(float* __restrict__ h, int64
         o.y = to_bits(v.y * r * gg.y, BF16);
         o.z = to_bits(v.z * r * gg.z, BF16);
         o.w = to_bits(v.w * r * gg.w, BF16);
-        if constexpr (T32) *(ushort4*)(out + tiled32_index(row, c, cols)) = o;
-        else *(ushort4*)(orow + c) = o;
+        *(ushort4*)(out + tiled32_index(row, c, cols)) = o;
     }
 }
 
@@ -173,33 +170,27 @@ __global__ void dequant_q8_0_kernel(const uint8_t* __restrict__ blocks, int64_t 
 }  // namespace
 
 hipError_t launch_rmsnorm_cast(const float* x, int64_t ldx, const float* g, int32_t rows,
-                               int32_t cols, float eps, uint16_t* out, int64_t ldo, bool bf16,
-                               bool out_t32, hipStream_t s) {
+                               int32_t cols, float eps, uint16_t* out, bool bf16, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
-    if (cols % 4 || (out_t32 && cols % 32)) return hipErrorInvalidValue;
-#define KVA_NORM(B_, T_) \
-    hipLaunchKernelGGL((rmsnorm_cast<B_, T_>), dim3(rows), dim3(256), 0, s, x, ldx, g, cols, eps, out, ldo)
-    if (bf16 && out_t32) KVA_NORM(true, true);
-    else if (bf16) KVA_NORM(true, false);
-    else if (out_t32) KVA_NORM(false, true);
-    else KVA_NORM(false, false);
-#undef KVA_NORM
+    if (cols % 32) return hipErrorInvalidValue;
+    if (bf16)
+        hipLaunchKernelGGL(rmsnorm_cast<true>, dim3(rows), dim3(256), 0, s, x, ldx, g, cols, eps, out);
+    else
+        hipLaunchKernelGGL(rmsnorm_cast<false>, dim3(rows), dim3(256), 0, s, x, ldx, g, cols, eps, out);
     return hipGetLastError();
 }
 
 hipError_t launch_fold_rmsnorm(float* h, int64_t ldh, bool add, const float* partials, int32_t splits,
                                int64_t pstride, int64_t ldp, const float* g, int32_t rows, int32_t cols,
-                               float eps, uint16_t* out, int64_t ldo, bool bf16, bool out_t32, hipStream_t s) {
+                               float eps, uint16_t* out, bool bf16, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
-    if (cols % 4 || splits < 1 || (out_t32 && cols % 32)) return hipErrorInvalidValue;
-#define KVA_FOLD(B_, T_)                                                                                  \
-    hipLaunchKernelGGL((fold_rmsnorm<B_, T_>), dim3(rows), dim3(256), 0, s, h, ldh, (int)add, partials, \
-                       splits, pstride, ldp, g, cols, eps, out, ldo)
-    if (bf16 && out_t32) KVA_FOLD(true, true);
-    else if (bf16) KVA_FOLD(true, false);
-    else if (out_t32) KVA_FOLD(false, true);
-    else KVA_FOLD(false, false);
-#undef KVA_FOLD
+    if (cols % 32 || splits < 1) return hipErrorInvalidValue;
+    if (bf16)
+        hipLaunchKernelGGL(fold_rmsnorm<true>, dim3(rows), dim3(256), 0, s, h, ldh, (int)add, partials, splits,
+                           pstride, ldp, g, cols, eps, out);
+    else
+        hipLaunchKernelGGL(fold_rmsnorm<false>, dim3(rows), dim3(256), 0, s, h, ldh, (int)add, partials, splits,
+                           pstride, ldp, g, cols, eps, out);
     return hipGetLastError();
 }
 

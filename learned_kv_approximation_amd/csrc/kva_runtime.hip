@@ -163,10 +163,10 @@ struct kva_ctx {
     uint64_t weight_bytes = 0, scratch_bytes = 0;
 
     // weights (device).  A weight is either 16-bit values w16 (fp16 trunk,
-    // bf16 heads; tiled as in tiled32_index) or, for q8_0, codes q[rows][K] +
-    // fp16 scales sc[rows][K/32].  With 16-bit weights every GEMM operand is
-    // in the tiled32 layout (the activation producers write it so); with
-    // q8_0 the activations are row-major.
+    // bf16 heads; tiled as in tiled32_index) or, for q8_0, int8 codes q and
+    // fp16 scales sc (tiled as in q8_code_index / q8_scale_index).  Every
+    // GEMM activation operand is in the tiled32 layout (its producer writes
+    // it so).
     struct DevW {
         uint16_t* w16 = nullptr;
         int8_t* q = nullptr;
@@ -309,9 +309,8 @@ enum PackTarget { PACK_F16_T32 = 0, PACK_BF16_T32 = 1, PACK_Q8 = 2 };
 
 // Packs rows (each K wide, stored in `dtype`) into the compute layout and
 // uploads it: fp16 or bf16 values in the tiled layout of tiled32_index
-// (32-wide slabs), or for q8_0 an int8 code plane
-// [rows][K] plus an fp16 scale plane [rows][K/32] (the 34-byte blocks split
-// losslessly into aligned planes).
+// (32-wide slabs), or for q8_0 the 34-byte blocks split losslessly into an
+// int8 code plane and an fp16 scale plane, tiled the same way.
 kva_status pack_weight(kva_ctx* ctx, int dtype, int64_t K, const std::vector<RowSrc>& rows,
                        PackTarget target, kva_ctx::DevW* out, const char* name) {
     const int64_t n = (int64_t)rows.size();
@@ -319,6 +318,7 @@ kva_status pack_weight(kva_ctx* ctx, int dtype, int64_t K, const std::vector<Row
         if (!r.src && r.row >= 0) return fail(KVA_ERR_ARG, "weight %s is NULL", name);
     if (target == PACK_Q8) {
         if (dtype != KVA_DTYPE_Q8_0) return fail(KVA_ERR_DTYPE, "q8_0 layout needs q8_0 weights (%s)", name);
+        if (n % kWeightTileRows || K % 32) return fail(KVA_ERR_SHAPE, "weight %s: bad padding", name);
         const int64_t nb = K / 32;
         std::vector<int8_t> q((size_t)(n * K), 0);
         std::vector<uint16_t> sc((size_t)(n * nb), 0);
@@ -326,8 +326,9 @@ kva_status pack_weight(kva_ctx* ctx, int dtype, int64_t K, const std::vector<Row
             if (!rows[r].src) continue;
             const uint8_t* blk = static_cast<const uint8_t*>(rows[r].src) + rows[r].row * nb * 34;
             for (int64_t b = 0; b < nb; ++b) {
-                sc[(size_t)(r * nb + b)] = (uint16_t)(blk[b * 34] | (blk[b * 34 + 1] << 8));
-                std::memcpy(&q[(size_t)(r * K + b * 32)], blk + b * 34 + 2, 32);
+                sc[(size_t)q8_scale_index(r, b, K)] = (uint16_t)(blk[b * 34] | (blk[b * 34 + 1] << 8));
+                for (int64_t c = 0; c < 32; c += 8)   // 8 consecutive codes stay together
+                    std::memcpy(&q[(size_t)q8_code_index(r, b * 32 + c, K)], blk + b * 34 + 2 + c, 8);
             }
         }
         HIP_TRY(ctx->alloc(&out->q, q.size(), true));
@@ -508,19 +509,11 @@ GemmTile pick_tile_t32(int64_t M, int64_t N, int splits) {
     return (N % 256 == 0 && c256 <= c128) ? TILE_256x256 : TILE_128x128;
 }
 
-GemmTile pick_tile(int64_t M, int64_t N, int splits) {
-    const int64_t t128 = ((M + 127) / 128) * (N / 128) * splits;
-    const int64_t t256 = ((M + 255) / 256) * (N / 256) * splits;
-    const double c128 = (double)((t128 + 255) / 256);
-    const double c256 = (double)((t256 + 255) / 256) * 4.0 / 1.3;
-    return (N % 256 == 0 && c256 < c128) ? TILE_256x256 : TILE_128x128;
-}
 
 void set_b(GemmArgs& g, const kva_ctx::DevW& w, int64_t K) {
     g.B = w.w16;
     g.Bq = w.q;
     g.Bs = w.sc;
-    g.ldb = K;
 }
 
 #define LAUNCH(expr)                                                                      \
@@ -596,11 +589,10 @@ kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n, float* co
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t d = c.d_model, F = c.d_ffn, n_in = c.n_in;
     const int64_t hd = (int64_t)c.n_heads * c.head_dim;
-    // t32: 16-bit weights, every trunk operand in the tiled32 layout
-    const bool t32 = !ctx->q8;
+    // every GEMM activation operand is written in the tiled32 layout
+    const GemmOperand opd = ctx->q8 ? OPD_Q8 : OPD_F16;
     auto gemm = [&](EpiKind epi, const GemmArgs& g) -> hipError_t {
-        if (t32) return launch_gemm_t32(OPD_F16, pick_tile_t32(g.M, g.N, g.splits), epi, g, s);
-        return launch_gemm_q8(pick_tile(g.M, g.N, g.splits), epi, g, s);
+        return launch_gemm_t32(opd, pick_tile_t32(g.M, g.N, g.splits), epi, g, s);
     };
     const int64_t pstride = ctx->m_alloc * d;   // between split-K partial buffers
     // The narrow GEMMs (N = d: input, O, down) write kSplitNarrow partials to
@@ -616,12 +608,12 @@ kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n, float* co
     };
     auto fold = [&](bool add, const float* gain, uint16_t* out, bool bf16) -> kva_status {
         STAGE(KVA_STAGE_NORM, launch_fold_rmsnorm(ctx->h, d, add, ctx->ws, kSplitNarrow, pstride, d, gain, n,
-                                                  (int32_t)d, c.eps, out, d, bf16, t32, s));
+                                                  (int32_t)d, c.eps, out, bf16, s));
         return KVA_OK;
     };
 
     STAGE(KVA_STAGE_NORM,
-          launch_rmsnorm_cast(x, n_in, ctx->g_in, n, (int32_t)n_in, c.eps, ctx->u16, n_in, false, t32, s));
+          launch_rmsnorm_cast(x, n_in, ctx->g_in, n, (int32_t)n_in, c.eps, ctx->u16, false, s));
     KVA_TRY(narrow(ctx->u16, n_in, ctx->w_in, KVA_STAGE_GEMM_IN));
     for (int b = 0; b < c.n_blocks; ++b) {
         const kva_ctx::Blk& B = ctx->blk[b];
@@ -637,7 +629,7 @@ kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n, float* co
             STAGE(KVA_STAGE_GEMM_QKV, gemm(EPI_QKV, g));
         }
         STAGE(KVA_STAGE_ATTN, launch_attention(ctx->qk16, 2 * hd, (int32_t)hd, ctx->vt16, ctx->m_alloc, ctx->o16, hd, n,
-                                               c.n_heads, c.attn_block, t32, s));
+                                               c.n_heads, c.attn_block, s));
         KVA_TRY(narrow(ctx->o16, hd, B.wo, KVA_STAGE_GEMM_O));
         KVA_TRY(fold(true, B.g_ffn, ctx->a16, false));           // h += O partials; a = ffn_norm(h)
         {
@@ -645,13 +637,11 @@ kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n, float* co
             g.A = ctx->a16; g.lda = d; set_b(g, B.wgu, d);
             g.M = n; g.N = (int32_t)round_up(2 * F, kColPad); g.K = (int32_t)d;
             g.epi.out16 = ctx->act16; g.epi.ld16 = F; g.epi.n_real = (int32_t)(2 * F);
-            g.epi.out16_t32 = t32;
             STAGE(KVA_STAGE_GEMM_GATEUP, gemm(EPI_SWIGLU, g));
         }
         KVA_TRY(narrow(ctx->act16, F, B.wd, KVA_STAGE_GEMM_DOWN));
     }
-    // h += down partials; z = out_norm(h): bf16 in the tiled32 layout of the
-    // four-stage head GEMM, or fp16 row-major for the q8_0 head GEMM
+    // h += down partials; z = out_norm(h), tiled: bf16, or fp16 for q8_0
     KVA_TRY(fold(true, ctx->g_out, ctx->z16, !ctx->q8));
     {
         GemmArgs g;
@@ -662,8 +652,7 @@ kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n, float* co
         g.epi.tail_head = ctx->tail_head; g.epi.tail_col = ctx->tail_col;
         g.epi.tail_start = ctx->tail_start; g.epi.bias = ctx->b_heads;
         g.epi.heads = ho;
-        if (ctx->q8) STAGE(KVA_STAGE_GEMM_HEADS, launch_gemm_q8(TILE_256x256, EPI_HEADS, g, s));
-        else STAGE(KVA_STAGE_GEMM_HEADS, launch_gemm_t32(OPD_BF16, TILE_256x256, EPI_HEADS, g, s));
+        STAGE(KVA_STAGE_GEMM_HEADS, launch_gemm_t32(ctx->q8 ? OPD_Q8 : OPD_BF16, TILE_256x256, EPI_HEADS, g, s));
     }
     ctx->stats.calls += 1;
     ctx->stats.tokens += (uint64_t)n;
@@ -719,12 +708,7 @@ kva_status kva_debug_dequant_q8_0(const void* blocks, int64_t n_blocks, float* o
 kva_status kva_debug_copy_z(kva_ctx* ctx, uint16_t* dst, int32_t n, void* stream) {
     if (!ctx || !dst) return fail(KVA_ERR_ARG, "NULL argument");
     if (n < 1 || n > ctx->cfg.max_tokens) return fail(KVA_ERR_SHAPE, "bad n_tokens");
-    if (ctx->q8) {
-        HIP_TRY(hipMemcpyAsync(dst, ctx->z16, (size_t)n * ctx->cfg.d_model * 2, hipMemcpyDeviceToDevice,
-                               static_cast<hipStream_t>(stream)));
-    } else {
-        LAUNCH(launch_untile32(ctx->z16, dst, n, ctx->cfg.d_model, static_cast<hipStream_t>(stream)));
-    }
+    LAUNCH(launch_untile32(ctx->z16, dst, n, ctx->cfg.d_model, static_cast<hipStream_t>(stream)));
     return KVA_OK;
 }
 
