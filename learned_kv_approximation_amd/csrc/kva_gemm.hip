@@ -130,8 +130,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[MI][NI
                 }
         }
     } else if constexpr (EPI == EPI_HEADS) {
-        static_assert(BN == kHeadTileN, "head packing assumes one head per column tile");
-        const int th = e.tile_head[tn];
+        static_assert(kHeadTileN % BN == 0, "a GEMM tile lies inside one packed 256-column tile");
+        const int t256 = tn * BN / kHeadTileN;          // packed tile holding this GEMM tile
+        const int th = e.tile_head[t256];
         // A whole-head tile whose destination rows are 16-byte aligned goes out
         // through LDS: each half of the tile (128 x 256 fp32 = the 128 KB of
         // LDS) is transposed there and written as full 1 KB rows with 16-byte
@@ -139,7 +140,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[MI][NI
         if constexpr (BM == 256 && WGM == 2 && WGN == 4) {
             if (th >= 0 && (e.heads.ld[th] % 4) == 0 && ((uintptr_t)e.heads.ptr[th] % 16) == 0) {
                 float* lds = reinterpret_cast<float*>(smem);       // [128][256], rows rotated by 32 every 4 rows
-                float* dst0 = e.heads.ptr[th] + e.tile_col0[tn];
+                float* dst0 = e.heads.ptr[th] + e.tile_col0[t256];
                 const int64_t ld = e.heads.ld[th];
                 const float* bias = e.bias ? e.bias + tn * BN : nullptr;
 #pragma unroll
@@ -181,7 +182,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[MI][NI
             float* dst;
             int64_t ld;
             if (th >= 0) {
-                dst = e.heads.ptr[th] + e.tile_col0[tn] + (col - tn * BN);
+                dst = e.heads.ptr[th] + e.tile_col0[t256] + (col - t256 * kHeadTileN);
                 ld = e.heads.ld[th];
             } else {
                 const int c = col - e.tail_start;
@@ -205,7 +206,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[MI][NI
 // K is walked in 32-wide slabs through a ring of S LDS stages.
 //  - A slab's A rows and B rows are each one contiguous block in global
 //    memory (the tiled layouts), copied straight into LDS with
-//    global_load_lds (1 KB per wave instruction; the q8_0 scales 64 bytes).
+//    global_load_lds (1 KB per wave instruction; the q8_0 scales a few
+//    dozen bytes per wave).
 //    S - 1 slabs are in flight while one is consumed, which covers the L2
 //    latency at full MFMA rate.
 //  - The MFMA fragments are double-buffered in registers: the LDS reads of
@@ -235,8 +237,10 @@ struct T32Shape {
     static constexpr int B_BYTES = Q8 ? BN * KB : BN * KB * 2;      // codes or 16-bit values
     static constexpr int S_BYTES = Q8 ? BN * 2 : 0;                 // q8_0 scales
     static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
-    // the head epilogue stages 128 KB through LDS
-    static constexpr int S = (EPI == EPI_HEADS) ? (128 * 1024 + STAGE - 1) / STAGE : 4;
+    // the head epilogue of a 256-row tile stages 128 KB through LDS
+    static constexpr bool LDS_EPI = EPI == EPI_HEADS && BM == 256;
+    static constexpr int S = LDS_EPI ? (128 * 1024 + STAGE - 1) / STAGE : 4;
+    static constexpr int BYTES = S * STAGE;
 };
 
 // q8_0 weight fragment: codes (8 consecutive K-values of one row) and the
@@ -254,37 +258,27 @@ __device__ __forceinline__ u32x4 q8_fragment(u32x2 codes, uint16_t d_bits) {
     return out;
 }
 
+// One BM x BN tile (M-tile tm, N-tile tn, K range of split `split`), with
+// `smem` at least T32Shape<..>::BYTES of LDS.
 template <int BM, int BN, int WGM, int WGN, int OPD, int EPI>
-__global__ void __launch_bounds__(64 * WGM * WGN) gemm_t32(GemmArgs g) {
+__device__ __forceinline__ void t32_tile(const GemmArgs& g, int tm, int tn, int split, uint8_t* smem) {
     using Sh = T32Shape<BM, BN, OPD, EPI>;
     constexpr bool BF16 = OPD == OPD_BF16;
     constexpr bool Q8 = Sh::Q8;
     constexpr int NW = WGM * WGN, KB = Sh::KB, S = Sh::S;
     constexpr int WM = BM / WGM, WN = BN / WGN, MI = WM / 32, NI = WN / 32;
     constexpr int AI = Sh::A_BYTES / (1024 * NW), BI = Sh::B_BYTES / (1024 * NW);   // DMA instrs / wave / slab
-    // q8_0 scales: every wave copies 64 bytes of them (16 lanes x 4 bytes),
-    // so that every wave issues the same number of DMA instructions a slab
+    // q8_0 scales: every wave copies an equal share of them (SL lanes x 4
+    // bytes), so that every wave issues the same number of DMA instructions
+    constexpr int SL = Sh::S_BYTES / (4 * NW);
     constexpr int L = AI + BI + (Q8 ? 1 : 0);
     static_assert(AI >= 1 && BI >= 1 && AI * 1024 * NW == Sh::A_BYTES && BI * 1024 * NW == Sh::B_BYTES,
                   "tile too small for the wave grid");
-    static_assert(!Q8 || Sh::S_BYTES == NW * 64, "scale DMA split");
+    static_assert(!Q8 || (SL >= 1 && SL <= 64 && SL * 4 * NW == Sh::S_BYTES), "scale DMA split");
     static_assert((S - 2) * L < 64, "vmcnt range");
-    static_assert(EPI != EPI_HEADS || S * Sh::STAGE >= 128 * 1024, "the head epilogue stages 128 KB through LDS");
+    static_assert(!Sh::LDS_EPI || Sh::BYTES >= 128 * 1024, "the head epilogue stages 128 KB through LDS");
     static_assert(kWeightTileRows % BM == 0 && kWeightTileRows % BN == 0, "tiles inside 256-row groups");
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[S * Sh::STAGE];
-
-    const int mt = (g.M + BM - 1) / BM;
-    const int nt = g.N / BN;
     const int SP = g.splits;
-    const int total = mt * nt * SP;
-    const int per_xcd = gridDim.x / 8;
-    const int v = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    if (v >= total) return;
-    // M-tiles fastest, then splits, then N-tiles: the tiles sharing a weight
-    // strip run back to back on one XCD
-    const int tm = v % mt;
-    const int split = (v / mt) % SP;
-    const int tn = v / (mt * SP);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WGN, wn = wave % WGN;
@@ -319,9 +313,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_t32(GemmArgs g) {
             __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Bb + kt * B_SLAB + (i * NW + wave) * 1024 + lane * 16),
                                              (lds_ptr_t)(sb + (i * NW + wave) * 1024), 16, 0, 0);
         if constexpr (Q8) {
-            if (lane < 16)
-                __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Sb + kt * S_SLAB + wave * 64 + lane * 4),
-                                                 (lds_ptr_t)(sb + Sh::B_BYTES + wave * 64), 4, 0, 0);
+            if (lane < SL)
+                __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Sb + kt * S_SLAB + wave * SL * 4 + lane * 4),
+                                                 (lds_ptr_t)(sb + Sh::B_BYTES + wave * SL * 4), 4, 0, 0);
         }
     };
     // vmcnt(n) with lgkmcnt / expcnt left alone; lgkmcnt(0) alone.  (The
@@ -440,8 +434,54 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_t32(GemmArgs g) {
     int kt = 0;
     for (; kt + S - 1 < nk; ++kt) slab(kt, std::true_type{});
     for (; kt < nk; ++kt) slab(kt, std::false_type{});
-    if constexpr (EPI == EPI_HEADS) __syncthreads();    // the head epilogue reuses LDS
+    if constexpr (Sh::LDS_EPI) __syncthreads();    // the head epilogue reuses LDS
     epilogue<BM, BN, WGM, WGN, EPI, MI, NI>(g, acc, tm, tn, split, reinterpret_cast<uint16_t*>(smem));
+}
+
+// Workgroup ids are dealt to the 8 XCDs round-robin; this remaps them so that
+// consecutive tile indices run on one XCD (count: the grid, a multiple of 8).
+__device__ __forceinline__ int xcd_remap(int bid, int count) { return (bid % 8) * (count / 8) + bid / 8; }
+
+template <int BM, int BN, int WGM, int WGN, int OPD, int EPI>
+__global__ void __launch_bounds__(64 * WGM * WGN) gemm_t32(GemmArgs g) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[T32Shape<BM, BN, OPD, EPI>::BYTES];
+    const int mt = (g.M + BM - 1) / BM;
+    const int nt = g.N / BN;
+    const int total = mt * nt * g.splits;
+    const int v = xcd_remap(blockIdx.x, gridDim.x);
+    if (v >= total) return;
+    // M-tiles fastest, then splits, then N-tiles: the tiles sharing a weight
+    // strip run back to back on one XCD
+    t32_tile<BM, BN, WGM, WGN, OPD, EPI>(g, v % mt, v / (mt * g.splits), (v / mt) % g.splits, smem);
+}
+
+// The head GEMM in one launch of two parts: the first n_big 256-column
+// N-tiles as 256x256 tiles (a whole number of rounds over the CUs), the
+// remaining columns as 128 x SBN tiles (a quarter or half of the work), so
+// that the last round is that much shorter.  Both tile shapes accumulate K
+// in the same order: the split point never changes the bits.  SBN: 128, or
+// 256 for q8_0 (whose 128-column weight slab is too small for 8 waves' DMA).
+template <int OPD>
+constexpr int kTailBN = OPD == OPD_Q8 ? 256 : 128;
+
+template <int OPD>
+__global__ void __launch_bounds__(512) gemm_t32_heads(GemmArgs g, int n_big, int grid_big) {
+    constexpr int SBN = kTailBN<OPD>;
+    using ShB = T32Shape<256, 256, OPD, EPI_HEADS>;
+    using ShS = T32Shape<128, SBN, OPD, EPI_HEADS>;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[ShB::BYTES > ShS::BYTES ? ShB::BYTES : ShS::BYTES];
+    if ((int)blockIdx.x < grid_big) {
+        const int mt = (g.M + 255) / 256;
+        const int v = xcd_remap(blockIdx.x, grid_big);
+        if (v >= mt * n_big) return;
+        t32_tile<256, 256, 2, 4, OPD, EPI_HEADS>(g, v % mt, v / mt, 0, smem);
+    } else {
+        const int mt = (g.M + 127) / 128;
+        const int tn0 = n_big * (256 / SBN);            // first SBN-column tile
+        const int v = xcd_remap(blockIdx.x - grid_big, gridDim.x - grid_big);
+        if (v >= mt * (g.N / SBN - tn0)) return;
+        t32_tile<128, SBN, 2, 4, OPD, EPI_HEADS>(g, v % mt, tn0 + v / mt, 0, smem);
+    }
 }
 
 template <int BM, int BN, int WGM, int WGN, int OPD, int EPI>
@@ -459,20 +499,40 @@ hipError_t launch_t32(const GemmArgs& a, hipStream_t s) {
 
 // The instantiated (operand, tile, epilogue) combinations.
 
+hipError_t launch_gemm_heads(GemmOperand opd, const GemmArgs& a, int n_cu, hipStream_t s) {
+    if (a.M <= 0) return hipSuccess;
+    if (a.K % 32 != 0 || a.K <= 0 || a.N % 256 || a.splits != 1) return hipErrorInvalidValue;
+    if (opd == OPD_Q8 ? (!a.Bq || !a.Bs) : !a.B) return hipErrorInvalidValue;
+    const int mt = (a.M + 255) / 256, nt = a.N / 256, total = mt * nt;
+    // whole rounds of 256x256 tiles; the rest of the columns in 128x128 tiles
+    // when that shortens the last round
+    int n_big = nt;
+    if (n_cu > 0 && total > n_cu && total % n_cu != 0) n_big = (total / n_cu) * n_cu / mt;
+    const int grid_big = (mt * n_big + 7) / 8 * 8;
+    const int sbn = opd == OPD_Q8 ? kTailBN<OPD_Q8> : kTailBN<OPD_BF16>;
+    const int n_small = ((a.M + 127) / 128) * ((a.N - 256 * n_big) / sbn);
+    const int grid = grid_big + (n_small + 7) / 8 * 8;
+    if (opd == OPD_BF16)
+        hipLaunchKernelGGL(gemm_t32_heads<OPD_BF16>, dim3(grid), dim3(512), 0, s, a, n_big, grid_big);
+    else if (opd == OPD_Q8)
+        hipLaunchKernelGGL(gemm_t32_heads<OPD_Q8>, dim3(grid), dim3(512), 0, s, a, n_big, grid_big);
+    else
+        return hipErrorNotSupported;
+    return hipGetLastError();
+}
+
 #define KVA_T32_CASE(OPD_, TILE_, EPI_, BM_, BN_, WGM_, WGN_) \
     if (opd == OPD_ && tile == TILE_ && epi == EPI_) return launch_t32<BM_, BN_, WGM_, WGN_, OPD_, EPI_>(a, s);
 
 hipError_t launch_gemm_t32(GemmOperand opd, GemmTile tile, EpiKind epi, const GemmArgs& a, hipStream_t s) {
     if (a.M <= 0) return hipSuccess;
     if (a.K % 32 != 0 || a.K <= 0) return hipErrorInvalidValue;
-    KVA_T32_CASE(OPD_BF16, TILE_256x256, EPI_HEADS, 256, 256, 2, 4)
     KVA_T32_CASE(OPD_F16, TILE_256x256, EPI_PARTIAL, 256, 256, 2, 4)
     KVA_T32_CASE(OPD_F16, TILE_256x256, EPI_QKV, 256, 256, 2, 4)
     KVA_T32_CASE(OPD_F16, TILE_256x256, EPI_SWIGLU, 256, 256, 2, 4)
     KVA_T32_CASE(OPD_F16, TILE_128x128, EPI_PARTIAL, 128, 128, 2, 2)
     KVA_T32_CASE(OPD_F16, TILE_128x128, EPI_QKV, 128, 128, 2, 2)
     KVA_T32_CASE(OPD_F16, TILE_128x128, EPI_SWIGLU, 128, 128, 2, 2)
-    KVA_T32_CASE(OPD_Q8, TILE_256x256, EPI_HEADS, 256, 256, 2, 4)
     KVA_T32_CASE(OPD_Q8, TILE_256x256, EPI_PARTIAL, 256, 256, 2, 4)
     KVA_T32_CASE(OPD_Q8, TILE_256x256, EPI_QKV, 256, 256, 2, 4)
     KVA_T32_CASE(OPD_Q8, TILE_256x256, EPI_SWIGLU, 256, 256, 2, 4)

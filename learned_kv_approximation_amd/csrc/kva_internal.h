@@ -117,6 +117,10 @@ enum GemmTile : int { TILE_256x256 = 0, TILE_128x128 = 1 };
 hipError_t launch_gemm_t32(GemmOperand opd, GemmTile tile, EpiKind epi, const GemmArgs& args,
                            hipStream_t stream);
 
+// The head GEMM (EPI_HEADS, no split): 256x256 tiles over a whole number of
+// rounds of n_cu workgroups, the remaining columns in smaller tiles (128 rows).
+hipError_t launch_gemm_heads(GemmOperand opd, const GemmArgs& args, int n_cu, hipStream_t stream);
+
 // Folds split-K partials into the residual stream and normalises it:
 //   h[r][c] = (add ? h[r][c] : 0) + P_0[r][c] + P_1[r][c] + ... (this order),
 //   out[r][c] = 16-bit(h[r][c] / sqrt(mean_c h[r][c]^2 + eps) * g[c]).

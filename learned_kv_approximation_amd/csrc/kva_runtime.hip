@@ -159,6 +159,7 @@ struct kva_ctx {
     kva_config cfg{};
     std::vector<kva_head_desc> heads;
     int device = 0;
+    int n_cu = 0;                  // compute units of the device (head GEMM round size)
     std::vector<void*> allocs;
     uint64_t weight_bytes = 0, scratch_bytes = 0;
 
@@ -380,6 +381,7 @@ kva_status create_impl(const kva_config* cfg, const kva_weights* w, int device, 
     const int64_t hd = (int64_t)c.n_heads * c.head_dim;
     HIP_TRY(hipSetDevice(device));
     ctx->device = device;
+    HIP_TRY(hipDeviceGetAttribute(&ctx->n_cu, hipDeviceAttributeMultiprocessorCount, device));
     ctx->q8 = q8;
     const PackTarget trunk_t = q8 ? PACK_Q8 : PACK_F16_T32;
     const PackTarget head_t = q8 ? PACK_Q8 : PACK_BF16_T32;
@@ -652,7 +654,7 @@ kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n, float* co
         g.epi.tail_head = ctx->tail_head; g.epi.tail_col = ctx->tail_col;
         g.epi.tail_start = ctx->tail_start; g.epi.bias = ctx->b_heads;
         g.epi.heads = ho;
-        STAGE(KVA_STAGE_GEMM_HEADS, launch_gemm_t32(ctx->q8 ? OPD_Q8 : OPD_BF16, TILE_256x256, EPI_HEADS, g, s));
+        STAGE(KVA_STAGE_GEMM_HEADS, launch_gemm_heads(ctx->q8 ? OPD_Q8 : OPD_BF16, g, ctx->n_cu, s));
     }
     ctx->stats.calls += 1;
     ctx->stats.tokens += (uint64_t)n;
