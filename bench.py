@@ -322,7 +322,7 @@ def main():
                    "tokens_per_step": 1024, "tflop_per_step": round(r2["tflop_per_step"], 5)},
         "pct_mfma_peak": round(r2["pct_mfma_peak"], 2),
         "ms_median": round(r2["ms_median"], 4), "ms_p10": round(r2["ms_p10"], 4), "ms_p90": round(r2["ms_p90"], 4),
-        "roofline": {"bound": "mfma", "kernel": "gemm_t32<bf16,heads>",
+        "roofline": {"bound": "mfma", "kernel": "gemm_t32_heads<bf16>",
                      "achieved": round(achieved, 1), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic_bytes(),
                      "launch_ms": round(r2["heads_gemm_ms"], 4),
