@@ -141,8 +141,8 @@ kva_status kva_validate_config(const kva_config* cfg);
  * the MFMA path (KVA_ERR_RANGE if a weight is outside fp16's finite range),
  * head weights are kept as bf16 (fp32 ones rounded to nearest even).  q8_0
  * weights are split losslessly into an int8 code plane and an fp16 scale
- * plane; the GEMMs form each weight d*q on the fly (see
- * kva_debug_dequant_q8_0) and run fp16 MFMA throughout.  The call is
+ * plane; the GEMMs form each weight as d*q rounded once to fp16 on the fly
+ * (see kva_debug_dequant_q8_0_f16) and run fp16 MFMA throughout.  The call is
  * synchronous.  On success *out owns all device memory it allocated; on
  * failure *out is NULL and nothing is leaked. */
 kva_status kva_create(const kva_config* cfg, const kva_weights* w, int device, kva_ctx** out);
@@ -201,11 +201,19 @@ typedef struct {
 kva_status kva_attn_kv_write(const float* kv, int64_t ld_kv, int32_t n_tokens, int64_t pos0,
                              const float* k_gain, const kva_paged_kv* cache, void* stream);
 
-/* Test hook: dequantises n_blocks q8_0 blocks (device, 34 bytes each) to
- * fp32 (device, 32*n_blocks values) with the same device routine the q8_0
- * GEMM uses: out = float(d) * q, exact, fp16 subnormal scales honoured.
- * (The GEMM then rounds that value once to fp16 for the MFMA.) */
+/* Test hook: dequantises n_blocks q8_0 blocks (device, 34 bytes each: fp16
+ * scale d, then 32 int8 codes q; format from [KVA] "Projector quantization and
+ * flash-attn") to fp32 (device, 32*n_blocks values): out = float(d) * q,
+ * exact, fp16 subnormal scales honoured.  Asynchronous on `stream`;
+ * KVA_ERR_ARG for NULL pointers, KVA_ERR_SHAPE for n_blocks < 0. */
 kva_status kva_debug_dequant_q8_0(const void* blocks, int64_t n_blocks, float* out, void* stream);
+
+/* Test hook: the weights the q8_0 GEMMs actually feed to the fp16 MFMA, made
+ * by the GEMMs' own device routine: for n_blocks q8_0 blocks (device, 34
+ * bytes each) writes 32*n_blocks fp16 bit patterns (device), each the exact
+ * product d * q rounded once to nearest-even binary16 (overflow to +-inf).
+ * Asynchronous on `stream`; errors as kva_debug_dequant_q8_0. */
+kva_status kva_debug_dequant_q8_0_f16(const void* blocks, int64_t n_blocks, uint16_t* out, void* stream);
 
 /* Test hook: copies the final-normed trunk state z of the most recent
  * kva_project_ubatch call ([n_tokens][d_model] 16-bit patterns, the head

@@ -84,6 +84,7 @@ _SIGS = {
     "kva_destroy": (c_i32, [c_vp]),
     "kva_attn_kv_write": (c_i32, [c_vp, c_i64, c_i32, c_i64, c_vp, ctypes.POINTER(kva_paged_kv), c_vp]),
     "kva_debug_dequant_q8_0": (c_i32, [c_vp, c_i64, c_vp, c_vp]),
+    "kva_debug_dequant_q8_0_f16": (c_i32, [c_vp, c_i64, c_vp, c_vp]),
     "kva_debug_copy_z": (c_i32, [c_vp, c_vp, c_i32, c_vp]),
     "kva_debug_head_plan": (c_i32, [ctypes.POINTER(kva_config), ctypes.POINTER(c_i32), c_vp, c_vp, c_i64]),
     "kva_debug_host_to_f16": (c_i32, [c_vp, c_i32, c_i64, c_vp]),
@@ -150,6 +151,10 @@ def kva_attn_kv_write(kv_ptr: int, ld_kv: int, n_tokens: int, pos0: int, k_gain_
 
 def kva_debug_dequant_q8_0(blocks_ptr: int, n_blocks: int, out_ptr: int, stream: int = 0) -> None:
     _check(lib().kva_debug_dequant_q8_0(blocks_ptr, n_blocks, out_ptr, stream), "kva_debug_dequant_q8_0")
+
+
+def kva_debug_dequant_q8_0_f16(blocks_ptr: int, n_blocks: int, out_ptr: int, stream: int = 0) -> None:
+    _check(lib().kva_debug_dequant_q8_0_f16(blocks_ptr, n_blocks, out_ptr, stream), "kva_debug_dequant_q8_0_f16")
 
 
 def kva_debug_copy_z(ctx: int, dst_ptr: int, n_tokens: int, stream: int = 0) -> None:

@@ -246,20 +246,14 @@ struct T32Shape {
 // q8_0 weight fragment: codes (8 consecutive K-values of one row) and the
 // row's fp16 block scale -> the 8 fp16 weights RNE(d * q).
 __device__ __forceinline__ u32x4 q8_fragment(u32x2 codes, uint16_t d_bits) {
-    const _Float16 d = __builtin_bit_cast(_Float16, d_bits);
+    uint32_t o[4];
+    q8_0_f16x8(codes[0], codes[1], d_bits, o);
     u32x4 out;
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-        const uint32_t w = codes[h >> 1] >> (16 * (h & 1));
-        const _Float16 lo = (_Float16)(int8_t)(w & 0xFF) * d;
-        const _Float16 hi = (_Float16)(int8_t)((w >> 8) & 0xFF) * d;
-        out[h] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-    }
+    for (int h = 0; h < 4; ++h) out[h] = o[h];
     return out;
 }
 
-// One BM x BN tile (M-tile tm, N-tile tn, K range of split `split`), with
-// `smem` at least T32Shape<..>::BYTES of LDS.
 template <int BM, int BN, int WGM, int WGN, int OPD, int EPI>
 __device__ __forceinline__ void t32_tile(const GemmArgs& g, int tm, int tn, int split, uint8_t* smem) {
     using Sh = T32Shape<BM, BN, OPD, EPI>;

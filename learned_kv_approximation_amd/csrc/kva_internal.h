@@ -108,6 +108,22 @@ enum GemmOperand : int { OPD_F16 = 0, OPD_BF16 = 1, OPD_Q8 = 2 };
 __device__ __forceinline__ float q8_0_value(uint16_t d_bits, int q) {
     return (float)__builtin_bit_cast(_Float16, d_bits) * (float)q;
 }
+
+// Eight q8_0 weights as the fp16 values the MFMA consumes: codes c0 (K-values
+// 0..3, one byte each, lowest first) and c1 (4..7) times the fp16 scale
+// d_bits, each product rounded once to nearest-even fp16 (one fp16 multiply
+// of two exact fp16 operands is correctly rounded, so this is q8_0_value
+// rounded once).  out[h] packs K-values 2h (low half) and 2h + 1.
+__device__ __forceinline__ void q8_0_f16x8(uint32_t c0, uint32_t c1, uint16_t d_bits, uint32_t out[4]) {
+    const _Float16 d = __builtin_bit_cast(_Float16, d_bits);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        const uint32_t w = (h < 2 ? c0 : c1) >> (16 * (h & 1));
+        const _Float16 lo = (_Float16)(int8_t)(w & 0xFF) * d;
+        const _Float16 hi = (_Float16)(int8_t)((w >> 8) & 0xFF) * d;
+        out[h] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+}
 // 256x256: 8 waves (2 per SIMD); 128x128: 4 waves.
 enum GemmTile : int { TILE_256x256 = 0, TILE_128x128 = 1 };
 
@@ -166,5 +182,6 @@ struct KvWriteArgs {
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
 
 hipError_t launch_dequant_q8_0(const void* blocks, int64_t n_blocks, float* out, hipStream_t stream);
+hipError_t launch_dequant_q8_0_f16(const void* blocks, int64_t n_blocks, uint16_t* out, hipStream_t stream);
 
 }  // namespace kva

@@ -707,6 +707,13 @@ kva_status kva_debug_dequant_q8_0(const void* blocks, int64_t n_blocks, float* o
     return KVA_OK;
 }
 
+kva_status kva_debug_dequant_q8_0_f16(const void* blocks, int64_t n_blocks, uint16_t* out, void* stream) {
+    if (!blocks || !out) return fail(KVA_ERR_ARG, "NULL argument");
+    if (n_blocks < 0) return fail(KVA_ERR_SHAPE, "negative n_blocks");
+    LAUNCH(launch_dequant_q8_0_f16(blocks, n_blocks, out, static_cast<hipStream_t>(stream)));
+    return KVA_OK;
+}
+
 kva_status kva_debug_copy_z(kva_ctx* ctx, uint16_t* dst, int32_t n, void* stream) {
     if (!ctx || !dst) return fail(KVA_ERR_ARG, "NULL argument");
     if (n < 1 || n > ctx->cfg.max_tokens) return fail(KVA_ERR_SHAPE, "bad n_tokens");

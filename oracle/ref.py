@@ -97,6 +97,33 @@ def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return bits
 
 
+def f64_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float64 values once to the nearest IEEE binary16 (ties to even)
+    and return the bit patterns.  binary16 keeps 11 significant bits; below
+    2^-14 the spacing stays 2^-24 (subnormals); a result past 65504 is an
+    infinity."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros(x.shape, dtype=np.float64)
+    fin = np.isfinite(x) & (x != 0)
+    m, e = np.frexp(x[fin])                  # x = m * 2^e, 0.5 <= |m| < 1
+    ulp = np.ldexp(1.0, np.maximum(e - 11, -24))
+    out[fin] = np.rint(x[fin] / ulp) * ulp   # rint rounds half to even
+    out[~fin] = x[~fin]
+    big = np.abs(out) > 65504.0              # rounded past the largest binary16
+    with np.errstate(over="ignore"):
+        h = out.astype(np.float16)           # exact: out has <= 11 significant bits
+    h[big] = np.copysign(np.inf, out[big]).astype(np.float16)
+    bits = h.view(np.uint16).copy()
+    bits[np.isnan(x)] = 0x7E00
+    return bits
+
+
+def dequant_q8_0_f16_bits(packed: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """The fp16 weights an fp16 MFMA path feeds on for q8_0 weights: the exact
+    product d * q (dequant_q8_0) rounded once to the nearest binary16."""
+    return f64_to_f16_bits(dequant_q8_0(packed, rows, cols))
+
+
 # --------------------------------------------------------------------------
 # building blocks
 

@@ -193,6 +193,26 @@ def test_dequant_q8_0_bit_exact():
     assert np.array_equal(out.cpu().numpy().view(np.uint32), want.view(np.uint32))
 
 
+def test_dequant_q8_0_f16_weights_bit_exact():
+    """The fp16 weights the q8_0 GEMMs use (their own device routine) equal the
+    exact d * q rounded once to nearest-even binary16, overflow included."""
+    rng = np.random.default_rng(10)
+    nb = 4096
+    codes = rng.integers(-128, 128, size=(1, nb * 32), dtype=np.int8)
+    sc_bits = rng.integers(0, 0x7C00, size=nb).astype(np.uint16)
+    sc_bits |= (rng.integers(0, 2, size=nb).astype(np.uint16) << 15)
+    sc_bits[:64] = np.arange(64, dtype=np.uint16)
+    packed = synth.pack_q8_0(codes, sc_bits.view(np.float16).reshape(1, nb))
+    want = ref.dequant_q8_0_f16_bits(packed, 1, nb * 32).reshape(-1)
+    assert (want == 0x7C00).any() and (want == 0xFC00).any() and (want & 0x7C00 == 0).any()
+    blocks = torch.from_numpy(packed.reshape(-1)).cuda()
+    out = torch.empty(nb * 32, dtype=torch.int16, device="cuda")
+    kva.kva_debug_dequant_q8_0_f16(blocks.data_ptr(), nb, out.data_ptr(), kva.current_stream())
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, want), np.flatnonzero(got != want)[:10]
+
+
 def _kv_cache(n_logical, n_pages):
     kp = torch.full((n_pages, 256, 4, 256), -1, dtype=torch.int16, device="cuda")
     vp = torch.full((n_pages, 256, 4, 256), -1, dtype=torch.int16, device="cuda")

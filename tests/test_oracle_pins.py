@@ -278,6 +278,42 @@ def test_q8_0_dequant_hand_blocks():
     assert np.array_equal(v[3], np.tile([65504.0, -65504.0], 16))
 
 
+def test_f16_rounding_hand_cases_and_torch():
+    # ties to even, subnormal spacing 2^-24, overflow past 65504, signed zero
+    cases = {1 + 2.0 ** -11: 0x3C00, 1 + 3 * 2.0 ** -11: 0x3C02, 2.0 ** -25: 0x0000,
+             3 * 2.0 ** -26: 0x0001, 65519.0: 0x7BFF, 65520.0: 0x7C00, -0.0: 0x8000,
+             -65536.0: 0xFC00, 2.0 ** -14: 0x0400, 1.0 / 3.0: 0x3555}
+    got = ref.f64_to_f16_bits(np.array(list(cases)))
+    assert [int(b) for b in got] == list(cases.values())
+    # against torch's conversion on float32 inputs across the whole range
+    rng = np.random.default_rng(6)
+    x32 = (rng.standard_normal(20000) * np.exp2(rng.integers(-30, 20, 20000))).astype(np.float32)
+    want = torch.from_numpy(x32).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ref.f64_to_f16_bits(x32.astype(np.float64)), want)
+    # float64 inputs: one of the two binary16 neighbours, the nearer one
+    x = rng.standard_normal(20000) * 64
+    v = ref.f16_bits_to_f64(ref.f64_to_f16_bits(x))
+    up = np.nextafter(x.astype(np.float16), np.float16(np.inf)).astype(np.float64)
+    dn = np.nextafter(x.astype(np.float16), np.float16(-np.inf)).astype(np.float64)
+    assert np.all(np.abs(v - x) <= np.minimum(np.abs(up - x), np.abs(dn - x)) + 0.0)
+
+
+def test_q8_0_f16_weights_hand_blocks():
+    # exact products stay exact; a halfway product rounds to even; overflow -> inf
+    scales = np.array([0.5, 2.0 ** -24, 1 + 2.0 ** -10, 65504.0], dtype=np.float16)
+    codes = np.zeros((4, 32), dtype=np.int8)
+    codes[0] = np.arange(-128, -96)
+    codes[1, :] = 3
+    codes[2, :] = 3
+    codes[3, 0], codes[3, 1], codes[3, 2] = 1, -1, 2
+    packed = synth.pack_q8_0(codes.reshape(1, 128), scales.reshape(1, 4))
+    b = ref.dequant_q8_0_f16_bits(packed, 1, 128).reshape(4, 32)
+    assert np.array_equal(ref.f16_bits_to_f64(b[0]), 0.5 * np.arange(-128, -96))
+    assert np.all(b[1] == 0x0003)                      # 3 * 2^-24, a subnormal, exact
+    assert np.all(b[2] == 0x4202)                      # 3 + 3*2^-10: halfway, to even 3 + 2^-8
+    assert (b[3, 0], b[3, 1], b[3, 2], b[3, 3]) == (0x7BFF, 0xFBFF, 0x7C00, 0x0000)
+
+
 def test_bf16_rounding_matches_torch_and_neighbours():
     rng = np.random.default_rng(5)
     x32 = (rng.standard_normal(20000) * np.exp2(rng.integers(-140, 100, 20000))).astype(np.float32)
