@@ -196,6 +196,79 @@ def time_kv_write(n_tokens: int = 65536, layers: int = 8, chunk: int = 8192, ste
             "launches": (n_tokens // chunk) * layers}
 
 
+def mfma_loop(n_iter: int = 4000, workgroups_per_cu: int = 4, reps: int = 10):
+    """The MFMA rate the device sustains with no memory traffic (the library's
+    kva_debug_mfma_loop): the achievable ceiling at the clock it runs at."""
+    import torch
+
+    import learned_kv_approximation_amd as kva
+
+    n_wg = torch.cuda.get_device_properties(0).multi_processor_count * workgroups_per_cu
+    sink = torch.empty(256 * n_wg, dtype=torch.float32, device="cuda")
+    st = kva.current_stream()
+    for _ in range(3):
+        kva.kva_debug_mfma_loop(n_iter, n_wg, sink.data_ptr(), st)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        kva.kva_debug_mfma_loop(n_iter, n_wg, sink.data_ptr(), st)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flop = n_wg * 4 * n_iter * 8 * 32768
+    tf = flop / (ms / 1e3) / 1e12
+    return {"tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_TFLOPS, 4), "ms": round(ms, 4),
+            "waves": n_wg * 4, "mfma_per_wave": n_iter * 8, "instr": "v_mfma_f32_32x32x16_bf16"}
+
+
+def linear_weight_params(cfg: dict) -> int:
+    """Weights of every Linear of the projector (what q8_0 stores in blocks)."""
+    d, F, hd = cfg["d_model"], cfg["d_ffn"], cfg["n_heads"] * cfg["head_dim"]
+    trunk = cfg["n_in"] * d + cfg["n_blocks"] * (3 * hd * d + d * hd + 2 * F * d + d * F)
+    return trunk + sum(h["out_dim"] for h in cfg["heads"]) * d
+
+
+def q8_m_sweep(ms=(16, 32, 64, 128, 256, 512, 1024), steps: int = 10, warmup: int = 3):
+    """The r3 q8_0 projector at M tokens per call: each call reads every weight
+    once, so below M of a few hundred the path is bound by weight bandwidth
+    (reported as GB/s of q8_0 weight bytes, 34 per 32 weights)."""
+    import torch
+
+    import learned_kv_approximation_amd as kva
+
+    cfg = synth.config("r3_q8_0")
+    w = synth.make_weights(cfg)
+    x = synth.make_input(cfg, n_tokens=max(ms))
+    proj = kva.Projector(cfg, w, max_tokens=max(ms))
+    del w
+    xd = torch.from_numpy(x).cuda()
+    outs = proj.alloc_outputs(max(ms))
+    wbytes = linear_weight_params(cfg) * 34 // 32
+    res = {}
+    for m in ms:
+        xm = xd[:m].contiguous()
+        for _ in range(warmup):
+            proj.project(xm, outs)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            proj.project(xm, outs)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / steps
+        f = flops(cfg, m)["total"]
+        res[str(m)] = {"ms": round(t, 4), "tokens_per_s": round(m / (t / 1e3), 1),
+                       "pct_mfma_peak": round(100.0 * f / (t / 1e3) / (PEAK_TFLOPS * 1e12), 2),
+                       "weight_gb_s": round(wbytes / (t / 1e3) / 1e9, 1),
+                       "frac_hbm": round(wbytes / (t / 1e3) / 1e9 / HBM_GBS, 4)}
+    proj.close()
+    del outs, xd
+    torch.cuda.empty_cache()
+    return {"weight_bytes": wbytes, "by_tokens_per_call": res}
+
+
 def traffic_probe():
     """Kernels whose HBM counters calibrate the head GEMM's traffic: two r2
     projections, then two copies of exactly COPY_BYTES (read COPY_BYTES,
@@ -225,9 +298,13 @@ def cpu_baseline(min_seconds: float = 10.0, max_reps: int = 8):
     """The oracle, as it stands, on whole r2 ubatches (1024 tokens, all 32 heads),
     repeated until about `min_seconds` of CPU work; tokens/s over all reps."""
     import oracle
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        if info:
+            blas = f"{info[0].get('internal_api', '?')} {info[0].get('version', '')}".strip()
     except Exception:
         threads = os.cpu_count() or 1
     cfg = synth.config("r2")
@@ -242,7 +319,8 @@ def cpu_baseline(min_seconds: float = 10.0, max_reps: int = 8):
     return {"value": 1024 * reps / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"r2, {reps} x one 1024-token ubatch (all 32 heads), float64 NumPy with "
                       f"{threads} BLAS threads, {dt:.1f} s",
-            "cpu_model": _cpu_model()}
+            "cpu_model": _cpu_model(), "blas": blas,
+            "affinity_cores": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
 
 
 def _cpu_model() -> str:
@@ -283,7 +361,7 @@ def main():
 
     r2 = time_config("r2", args.steps, args.warmup)
     print(f"[bench] r2: {r2['tokens_per_s']:.0f} tok/s, {r2['pct_mfma_peak']:.1f}% peak", file=sys.stderr, flush=True)
-    r3 = r3b = q8 = q8p = kvw = None
+    r3 = r3b = q8 = q8p = kvw = sweep = mloop = None
     if not args.no_r3:
         r3 = time_config("r3", args.steps, args.warmup)
         print(f"[bench] r3: {r3['tokens_per_s']:.0f} tok/s, {r3['pct_mfma_peak']:.1f}% peak", file=sys.stderr,
@@ -297,6 +375,13 @@ def main():
             print(f"[bench] r3 q8_0 65536: {q8p['tokens_per_s']:.0f} tok/s", file=sys.stderr, flush=True)
             kvw = time_kv_write()
             print(f"[bench] kv write: {kvw['gb_s']} GB/s", file=sys.stderr, flush=True)
+            sweep = q8_m_sweep()
+            print("[bench] q8_0 M sweep: " + ", ".join(f"{m}: {v['weight_gb_s']} GB/s"
+                                                        for m, v in sweep["by_tokens_per_call"].items()),
+                  file=sys.stderr, flush=True)
+    if not args.quick:
+        mloop = mfma_loop()
+        print(f"[bench] pure MFMA loop: {mloop['tflops']} TFLOP/s", file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline()
@@ -346,6 +431,10 @@ def main():
         out["r3_q8_0_prompt_65536"] = brief(q8p)
     if kvw is not None:
         out["kv_write_65536x8"] = kvw
+    if sweep is not None:
+        out["r3_q8_0_m_sweep"] = sweep
+    if mloop is not None:
+        out["mfma_loop"] = mloop
     print(json.dumps(out), flush=True)
 
 

@@ -215,6 +215,16 @@ kva_status kva_debug_dequant_q8_0(const void* blocks, int64_t n_blocks, float* o
  * Asynchronous on `stream`; errors as kva_debug_dequant_q8_0. */
 kva_status kva_debug_dequant_q8_0_f16(const void* blocks, int64_t n_blocks, uint16_t* out, void* stream);
 
+/* Measurement hook: a pure-MFMA loop with no memory traffic.  Launches
+ * n_workgroups workgroups of 4 waves; each wave issues n_iter x 8 independent
+ * bf16 v_mfma_f32_32x32x16 (32768 FLOP each), i.e.
+ * n_workgroups * 4 * n_iter * 8 * 32768 FLOP in all, and writes one float
+ * per thread to sink (device, 256 * n_workgroups floats) so the work is not
+ * dead.  Timing it gives the MFMA rate the device sustains at its current
+ * clock.  Asynchronous on `stream`; KVA_ERR_ARG for a NULL sink,
+ * KVA_ERR_SHAPE for non-positive counts. */
+kva_status kva_debug_mfma_loop(int32_t n_iter, int32_t n_workgroups, float* sink, void* stream);
+
 /* Test hook: copies the final-normed trunk state z of the most recent
  * kva_project_ubatch call ([n_tokens][d_model] 16-bit patterns, the head
  * GEMM's A operand: bf16, or fp16 for q8_0 weights) to device buffer `dst`.

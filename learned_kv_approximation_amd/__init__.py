@@ -85,6 +85,7 @@ _SIGS = {
     "kva_attn_kv_write": (c_i32, [c_vp, c_i64, c_i32, c_i64, c_vp, ctypes.POINTER(kva_paged_kv), c_vp]),
     "kva_debug_dequant_q8_0": (c_i32, [c_vp, c_i64, c_vp, c_vp]),
     "kva_debug_dequant_q8_0_f16": (c_i32, [c_vp, c_i64, c_vp, c_vp]),
+    "kva_debug_mfma_loop": (c_i32, [c_i32, c_i32, c_vp, c_vp]),
     "kva_debug_copy_z": (c_i32, [c_vp, c_vp, c_i32, c_vp]),
     "kva_debug_head_plan": (c_i32, [ctypes.POINTER(kva_config), ctypes.POINTER(c_i32), c_vp, c_vp, c_i64]),
     "kva_debug_host_to_f16": (c_i32, [c_vp, c_i32, c_i64, c_vp]),
@@ -151,6 +152,10 @@ def kva_attn_kv_write(kv_ptr: int, ld_kv: int, n_tokens: int, pos0: int, k_gain_
 
 def kva_debug_dequant_q8_0(blocks_ptr: int, n_blocks: int, out_ptr: int, stream: int = 0) -> None:
     _check(lib().kva_debug_dequant_q8_0(blocks_ptr, n_blocks, out_ptr, stream), "kva_debug_dequant_q8_0")
+
+
+def kva_debug_mfma_loop(n_iter: int, n_workgroups: int, sink_ptr: int, stream: int = 0) -> None:
+    _check(lib().kva_debug_mfma_loop(n_iter, n_workgroups, sink_ptr, stream), "kva_debug_mfma_loop")
 
 
 def kva_debug_dequant_q8_0_f16(blocks_ptr: int, n_blocks: int, out_ptr: int, stream: int = 0) -> None:

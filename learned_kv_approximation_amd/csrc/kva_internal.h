@@ -184,4 +184,7 @@ hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
 hipError_t launch_dequant_q8_0(const void* blocks, int64_t n_blocks, float* out, hipStream_t stream);
 hipError_t launch_dequant_q8_0_f16(const void* blocks, int64_t n_blocks, uint16_t* out, hipStream_t stream);
 
+// n_workgroups x 4 waves, each n_iter x 8 bf16 32x32x16 MFMAs; sink: 256 floats per workgroup.
+hipError_t launch_mfma_loop(int32_t n_iter, int32_t n_workgroups, float* sink, hipStream_t stream);
+
 }  // namespace kva

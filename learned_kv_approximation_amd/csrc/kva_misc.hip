@@ -187,7 +187,44 @@ __global__ void dequant_q8_0_f16_kernel(const uint8_t* __restrict__ blocks, int6
     }
 }
 
+// Pure MFMA loop: each wave runs n_iter rounds of 8 independent bf16
+// 32x32x16 MFMAs on register operands (no memory traffic), then folds its
+// accumulators into sink so nothing is dead.  Measures the MFMA rate the
+// device sustains at its current clock.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+__global__ void __launch_bounds__(256) mfma_loop_kernel(int32_t n_iter, float* __restrict__ sink) {
+    const int lane = threadIdx.x & 63;
+    bf16x8_t a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        a[e] = (__bf16)(1.0f + 0.001f * (float)((lane + e) & 7));
+        b[e] = (__bf16)(0.5f - 0.001f * (float)((lane * 3 + e) & 7));
+    }
+    f32x16_t acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+    for (int it = 0; it < n_iter; ++it) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+    }
+    float t = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t += acc[j][r];
+    sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = t;
+}
+
 }  // namespace
+
+hipError_t launch_mfma_loop(int32_t n_iter, int32_t n_workgroups, float* sink, hipStream_t s) {
+    if (n_iter <= 0 || n_workgroups <= 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(mfma_loop_kernel, dim3(n_workgroups), dim3(256), 0, s, n_iter, sink);
+    return hipGetLastError();
+}
 
 hipError_t launch_rmsnorm_cast(const float* x, int64_t ldx, const float* g, int32_t rows,
                                int32_t cols, float eps, uint16_t* out, bool bf16, hipStream_t s) {

@@ -714,6 +714,13 @@ kva_status kva_debug_dequant_q8_0_f16(const void* blocks, int64_t n_blocks, uint
     return KVA_OK;
 }
 
+kva_status kva_debug_mfma_loop(int32_t n_iter, int32_t n_workgroups, float* sink, void* stream) {
+    if (!sink) return fail(KVA_ERR_ARG, "NULL argument");
+    if (n_iter <= 0 || n_workgroups <= 0) return fail(KVA_ERR_SHAPE, "n_iter and n_workgroups must be positive");
+    LAUNCH(launch_mfma_loop(n_iter, n_workgroups, sink, static_cast<hipStream_t>(stream)));
+    return KVA_OK;
+}
+
 kva_status kva_debug_copy_z(kva_ctx* ctx, uint16_t* dst, int32_t n, void* stream) {
     if (!ctx || !dst) return fail(KVA_ERR_ARG, "NULL argument");
     if (n < 1 || n > ctx->cfg.max_tokens) return fail(KVA_ERR_SHAPE, "bad n_tokens");
