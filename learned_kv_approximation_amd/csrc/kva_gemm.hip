@@ -510,6 +510,18 @@ hipError_t launch_gemm_heads(GemmOperand opd, const GemmArgs& a, int n_cu, hipSt
     if (a.M <= 0) return hipSuccess;
     if (a.K % 32 != 0 || a.K <= 0 || a.N % 256 || a.splits != 1) return hipErrorInvalidValue;
     if (opd == OPD_Q8 ? (!a.Bq || !a.Bs) : !a.B) return hipErrorInvalidValue;
+    if (opd != OPD_BF16 && opd != OPD_Q8) return hipErrorNotSupported;
+    // Few rows: one M-tile of 64 or 128 rows, so that every weight strip is
+    // read once by a workgroup whose MFMA work matches the real rows (with
+    // 256-row tiles a short call would run a 256-row product on padding).
+    if (a.M <= 64) {
+        if (opd == OPD_BF16) return launch_t32<64, 256, 1, 4, OPD_BF16, EPI_HEADS>(a, s);
+        return launch_t32<64, 256, 1, 4, OPD_Q8, EPI_HEADS>(a, s);
+    }
+    if (a.M <= 128) {
+        if (opd == OPD_BF16) return launch_t32<128, 256, 2, 4, OPD_BF16, EPI_HEADS>(a, s);
+        return launch_t32<128, 256, 2, 4, OPD_Q8, EPI_HEADS>(a, s);
+    }
     const int mt = (a.M + 255) / 256, nt = a.N / 256, total = mt * nt;
     // whole rounds of 256x256 tiles; the rest of the columns in 128x128 tiles
     // when that shortens the last round

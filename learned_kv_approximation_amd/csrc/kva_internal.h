@@ -134,7 +134,8 @@ hipError_t launch_gemm_t32(GemmOperand opd, GemmTile tile, EpiKind epi, const Ge
                            hipStream_t stream);
 
 // The head GEMM (EPI_HEADS, no split): 256x256 tiles over a whole number of
-// rounds of n_cu workgroups, the remaining columns in smaller tiles (128 rows).
+// rounds of n_cu workgroups, the remaining columns in smaller tiles (128 rows);
+// calls of at most 128 rows use one M-tile of 64 or 128 rows.
 hipError_t launch_gemm_heads(GemmOperand opd, const GemmArgs& args, int n_cu, hipStream_t stream);
 
 // Folds split-K partials into the residual stream and normalises it:

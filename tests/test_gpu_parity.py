@@ -136,6 +136,24 @@ def test_r2_partial_last_ubatch(r2):
     proj.close()
 
 
+def test_r2_short_calls_bitwise_equal_to_full_ubatch(r2):
+    """Calls of 64, 100 and 300 tokens run other GEMM tiles (64-, 128- and
+    256-row head tiles, other trunk tiles) than a 1024-token call: the first
+    tokens of a block must still come out bit for bit the same (causality
+    makes them independent of the later tokens), and match the oracle."""
+    cfg, w, prep = r2
+    x = synth.make_input(cfg, n_tokens=1024, seed=22)
+    proj = kva.Projector(cfg, w, max_tokens=1024)
+    full = _run(proj, x)
+    for n in (64, 100, 300):
+        part = _run(proj, np.ascontiguousarray(x[:n]))
+        for i in range(len(part)):
+            assert np.array_equal(part[i], full[i][:n]), (n, i)
+    want = ref.project(cfg, prep, x[:64], which=[0, 31])
+    _check(cfg, {i: full[i][:64] for i in (0, 31)}, want, label="r2 first 64")
+    proj.close()
+
+
 # ------------------------------------------------------------------ r3: blocks, causality
 
 @pytest.fixture(scope="module")

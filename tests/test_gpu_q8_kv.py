@@ -86,6 +86,25 @@ def test_r3_q8_0_prompt_in_chunks(r3q8):
     proj.close()
 
 
+def test_r3_q8_0_short_call_bitwise_equal(r3q8):
+    """A 64-token call (one 64-row M-tile) and a 1024-token call give the same
+    bits for the first 64 tokens, within the q8_0 bar of the oracle."""
+    cfg, w, prep = r3q8
+    x = synth.make_input(cfg, n_tokens=1024)
+    proj = kva.Projector(cfg, w, max_tokens=1024)
+    xd = torch.from_numpy(x).cuda()
+    full = [o.cpu().numpy() for o in proj.project(xd)]
+    short = [o.cpu().numpy() for o in proj.project(xd[:64].contiguous())]
+    torch.cuda.synchronize()
+    for i in range(len(full)):
+        assert np.array_equal(short[i], full[i][:64]), i
+    want = ref.project(cfg, prep, x[:64], which=[0, 35])
+    errs = [_err(short[i], want[i]) for i in (0, 35)]
+    print("q8_0 64-token call max|err|/rms", errs)
+    assert max(errs) <= TOL_Q8
+    proj.close()
+
+
 @pytest.fixture(scope="module")
 def r3bf16():
     cfg = synth.config("r3_kv")
