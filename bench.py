@@ -361,7 +361,7 @@ def main():
 
     r2 = time_config("r2", args.steps, args.warmup)
     print(f"[bench] r2: {r2['tokens_per_s']:.0f} tok/s, {r2['pct_mfma_peak']:.1f}% peak", file=sys.stderr, flush=True)
-    r3 = r3b = q8 = q8p = kvw = sweep = mloop = None
+    r3 = r3b = q8 = q8p = q4 = kvw = sweep = mloop = None
     if not args.no_r3:
         r3 = time_config("r3", args.steps, args.warmup)
         print(f"[bench] r3: {r3['tokens_per_s']:.0f} tok/s, {r3['pct_mfma_peak']:.1f}% peak", file=sys.stderr,
@@ -373,6 +373,8 @@ def main():
             print(f"[bench] r3 q8_0: {q8['tokens_per_s']:.0f} tok/s", file=sys.stderr, flush=True)
             q8p = time_config("r3_q8_0", 3, 1, n_tokens=8192, prompt=65536, stages=False)
             print(f"[bench] r3 q8_0 65536: {q8p['tokens_per_s']:.0f} tok/s", file=sys.stderr, flush=True)
+            q4 = time_config("r3_q4_0", args.steps, args.warmup, stages=True)
+            print(f"[bench] r3 q4_0: {q4['tokens_per_s']:.0f} tok/s", file=sys.stderr, flush=True)
             kvw = time_kv_write()
             print(f"[bench] kv write: {kvw['gb_s']} GB/s", file=sys.stderr, flush=True)
             sweep = q8_m_sweep()
@@ -429,6 +431,8 @@ def main():
         out["r3_q8_0"] = brief(q8)
     if q8p is not None:
         out["r3_q8_0_prompt_65536"] = brief(q8p)
+    if q4 is not None:
+        out["r3_q4_0"] = brief(q4)
     if kvw is not None:
         out["kv_write_65536x8"] = kvw
     if sweep is not None:

@@ -57,9 +57,13 @@ typedef enum {
 typedef enum {
     KVA_DTYPE_F32 = 0,   /* IEEE binary32                                        */
     KVA_DTYPE_BF16 = 1,  /* bfloat16 bit patterns (uint16)                       */
-    KVA_DTYPE_Q8_0 = 2   /* blocks of 32 inputs: fp16 scale d, then 32 int8 q;   */
+    KVA_DTYPE_Q8_0 = 2,  /* blocks of 32 inputs: fp16 scale d, then 32 int8 q;   */
                          /* weight = d * q; 34 bytes per block, blocks run along */
                          /* the `in` axis of each row                            */
+    KVA_DTYPE_Q4_0 = 3   /* blocks of 32 inputs: fp16 scale d, then 16 bytes of  */
+                         /* 4-bit codes n (byte j: input j in the low nibble,   */
+                         /* input j+16 in the high one); weight = d * (n - 8);   */
+                         /* 18 bytes per block, blocks along `in`                */
 } kva_dtype;
 
 typedef enum {
@@ -142,7 +146,9 @@ kva_status kva_validate_config(const kva_config* cfg);
  * head weights are kept as bf16 (fp32 ones rounded to nearest even).  q8_0
  * weights are split losslessly into an int8 code plane and an fp16 scale
  * plane; the GEMMs form each weight as d*q rounded once to fp16 on the fly
- * (see kva_debug_dequant_q8_0_f16) and run fp16 MFMA throughout.  The call is
+ * (see kva_debug_dequant_q8_0_f16) and run fp16 MFMA throughout.  q4_0
+ * weights likewise: a 4-bit code plane and an fp16 scale plane, weights
+ * d*(n-8) rounded once to fp16 (kva_debug_dequant_q4_0_f16).  The call is
  * synchronous.  On success *out owns all device memory it allocated; on
  * failure *out is NULL and nothing is leaked. */
 kva_status kva_create(const kva_config* cfg, const kva_weights* w, int device, kva_ctx** out);
@@ -215,6 +221,12 @@ kva_status kva_debug_dequant_q8_0(const void* blocks, int64_t n_blocks, float* o
  * Asynchronous on `stream`; errors as kva_debug_dequant_q8_0. */
 kva_status kva_debug_dequant_q8_0_f16(const void* blocks, int64_t n_blocks, uint16_t* out, void* stream);
 
+/* Test hook: the same for q4_0 blocks (device, 18 bytes each; see
+ * KVA_DTYPE_Q4_0): 32*n_blocks fp16 bit patterns, each d * (n - 8) rounded
+ * once to nearest-even binary16, made by the q4_0 GEMMs' own device routine.
+ * Asynchronous on `stream`; errors as kva_debug_dequant_q8_0. */
+kva_status kva_debug_dequant_q4_0_f16(const void* blocks, int64_t n_blocks, uint16_t* out, void* stream);
+
 /* Measurement hook: a pure-MFMA loop with no memory traffic.  Launches
  * n_workgroups workgroups of 4 waves; each wave issues n_iter x 8 independent
  * bf16 v_mfma_f32_32x32x16 (32768 FLOP each), i.e.
@@ -227,7 +239,7 @@ kva_status kva_debug_mfma_loop(int32_t n_iter, int32_t n_workgroups, float* sink
 
 /* Test hook: copies the final-normed trunk state z of the most recent
  * kva_project_ubatch call ([n_tokens][d_model] 16-bit patterns, the head
- * GEMM's A operand: bf16, or fp16 for q8_0 weights) to device buffer `dst`.
+ * GEMM's A operand: bf16, or fp16 for q8_0 / q4_0 weights) to device buffer `dst`.
  * Asynchronous on `stream`. */
 kva_status kva_debug_copy_z(kva_ctx* ctx, uint16_t* dst, int32_t n_tokens, void* stream);
 

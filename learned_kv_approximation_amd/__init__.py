@@ -24,7 +24,7 @@ c_i32, c_i64, c_f32, c_f64, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_floa
 
 KVA_OK, KVA_ERR_ARG, KVA_ERR_SHAPE, KVA_ERR_DTYPE = 0, 1, 2, 3
 KVA_ERR_OOM, KVA_ERR_RANGE, KVA_ERR_UNSUPPORTED, KVA_ERR_HIP = 4, 5, 6, 7
-DTYPES = {"f32": 0, "bf16": 1, "q8_0": 2}
+DTYPES = {"f32": 0, "bf16": 1, "q8_0": 2, "q4_0": 3}
 KINDS = {"deltanet": 0, "attn": 1, "draft": 2}
 
 
@@ -85,6 +85,7 @@ _SIGS = {
     "kva_attn_kv_write": (c_i32, [c_vp, c_i64, c_i32, c_i64, c_vp, ctypes.POINTER(kva_paged_kv), c_vp]),
     "kva_debug_dequant_q8_0": (c_i32, [c_vp, c_i64, c_vp, c_vp]),
     "kva_debug_dequant_q8_0_f16": (c_i32, [c_vp, c_i64, c_vp, c_vp]),
+    "kva_debug_dequant_q4_0_f16": (c_i32, [c_vp, c_i64, c_vp, c_vp]),
     "kva_debug_mfma_loop": (c_i32, [c_i32, c_i32, c_vp, c_vp]),
     "kva_debug_copy_z": (c_i32, [c_vp, c_vp, c_i32, c_vp]),
     "kva_debug_head_plan": (c_i32, [ctypes.POINTER(kva_config), ctypes.POINTER(c_i32), c_vp, c_vp, c_i64]),
@@ -156,6 +157,10 @@ def kva_debug_dequant_q8_0(blocks_ptr: int, n_blocks: int, out_ptr: int, stream:
 
 def kva_debug_mfma_loop(n_iter: int, n_workgroups: int, sink_ptr: int, stream: int = 0) -> None:
     _check(lib().kva_debug_mfma_loop(n_iter, n_workgroups, sink_ptr, stream), "kva_debug_mfma_loop")
+
+
+def kva_debug_dequant_q4_0_f16(blocks_ptr: int, n_blocks: int, out_ptr: int, stream: int = 0) -> None:
+    _check(lib().kva_debug_dequant_q4_0_f16(blocks_ptr, n_blocks, out_ptr, stream), "kva_debug_dequant_q4_0_f16")
 
 
 def kva_debug_dequant_q8_0_f16(blocks_ptr: int, n_blocks: int, out_ptr: int, stream: int = 0) -> None:

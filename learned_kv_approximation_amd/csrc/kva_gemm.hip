@@ -232,10 +232,13 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[MI][NI
 template <int BM, int BN, int OPD, int EPI>
 struct T32Shape {
     static constexpr bool Q8 = OPD == OPD_Q8;
+    static constexpr bool Q4 = OPD == OPD_Q4;
+    static constexpr bool QW = Q8 || Q4;                            // block-quantised weights
     static constexpr int KB = 32;
     static constexpr int A_BYTES = BM * KB * 2;
-    static constexpr int B_BYTES = Q8 ? BN * KB : BN * KB * 2;      // codes or 16-bit values
-    static constexpr int S_BYTES = Q8 ? BN * 2 : 0;                 // q8_0 scales
+    static constexpr int B_ROW = Q8 ? KB : Q4 ? KB / 2 : KB * 2;    // weight bytes of a row per slab
+    static constexpr int B_BYTES = BN * B_ROW;
+    static constexpr int S_BYTES = QW ? BN * 2 : 0;                 // fp16 block scales
     static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
     // the head epilogue of a 256-row tile stages 128 KB through LDS
     static constexpr bool LDS_EPI = EPI == EPI_HEADS && BM == 256;
@@ -243,11 +246,13 @@ struct T32Shape {
     static constexpr int BYTES = S * STAGE;
 };
 
-// q8_0 weight fragment: codes (8 consecutive K-values of one row) and the
-// row's fp16 block scale -> the 8 fp16 weights RNE(d * q).
-__device__ __forceinline__ u32x4 q8_fragment(u32x2 codes, uint16_t d_bits) {
+// Quantised weight fragment: codes (8 consecutive K-values of one row; q4_0
+// uses the first dword) and the row's fp16 block scale -> 8 fp16 weights.
+template <bool Q4>
+__device__ __forceinline__ u32x4 q_fragment(u32x2 codes, uint16_t d_bits) {
     uint32_t o[4];
-    q8_0_f16x8(codes[0], codes[1], d_bits, o);
+    if constexpr (Q4) q4_0_f16x8(codes[0], d_bits, o);
+    else q8_0_f16x8(codes[0], codes[1], d_bits, o);
     u32x4 out;
 #pragma unroll
     for (int h = 0; h < 4; ++h) out[h] = o[h];
@@ -258,17 +263,21 @@ template <int BM, int BN, int WGM, int WGN, int OPD, int EPI>
 __device__ __forceinline__ void t32_tile(const GemmArgs& g, int tm, int tn, int split, uint8_t* smem) {
     using Sh = T32Shape<BM, BN, OPD, EPI>;
     constexpr bool BF16 = OPD == OPD_BF16;
-    constexpr bool Q8 = Sh::Q8;
+    constexpr bool Q4 = Sh::Q4;
+    constexpr bool QW = Sh::QW;          // block-quantised weights (q8_0 or q4_0)
     constexpr int NW = WGM * WGN, KB = Sh::KB, S = Sh::S;
     constexpr int WM = BM / WGM, WN = BN / WGN, MI = WM / 32, NI = WN / 32;
-    constexpr int AI = Sh::A_BYTES / (1024 * NW), BI = Sh::B_BYTES / (1024 * NW);   // DMA instrs / wave / slab
+    // DMA instructions per wave and slab: 16 bytes per lane, or 4 for a
+    // weight slab too small to give every wave a whole kilobyte (q4_0)
+    constexpr int BSZ = Sh::B_BYTES >= 1024 * NW ? 16 : 4;
+    constexpr int AI = Sh::A_BYTES / (1024 * NW), BI = Sh::B_BYTES / (64 * BSZ * NW);
     // q8_0 scales: every wave copies an equal share of them (SL lanes x 4
     // bytes), so that every wave issues the same number of DMA instructions
     constexpr int SL = Sh::S_BYTES / (4 * NW);
-    constexpr int L = AI + BI + (Q8 ? 1 : 0);
-    static_assert(AI >= 1 && BI >= 1 && AI * 1024 * NW == Sh::A_BYTES && BI * 1024 * NW == Sh::B_BYTES,
+    constexpr int L = AI + BI + (QW ? 1 : 0);
+    static_assert(AI >= 1 && BI >= 1 && AI * 1024 * NW == Sh::A_BYTES && BI * 64 * BSZ * NW == Sh::B_BYTES,
                   "tile too small for the wave grid");
-    static_assert(!Q8 || (SL >= 1 && SL <= 64 && SL * 4 * NW == Sh::S_BYTES), "scale DMA split");
+    static_assert(!QW || (SL >= 1 && SL <= 64 && SL * 4 * NW == Sh::S_BYTES), "scale DMA split");
     static_assert((S - 2) * L < 64, "vmcnt range");
     static_assert(!Sh::LDS_EPI || Sh::BYTES >= 128 * 1024, "the head epilogue stages 128 KB through LDS");
     static_assert(kWeightTileRows % BM == 0 && kWeightTileRows % BN == 0, "tiles inside 256-row groups");
@@ -285,15 +294,13 @@ __device__ __forceinline__ void t32_tile(const GemmArgs& g, int tm, int tn, int 
     const int64_t b_slab0 = ((int64_t)(tn * BN / kWeightTileRows) * nk_all + kb);
     const uint8_t* Ab = reinterpret_cast<const uint8_t*>(g.A) +
                         (a_slab0 * kWeightTileRows + (tm * BM) % kWeightTileRows) * KB * 2;
-    const uint8_t* Bb = Q8 ? reinterpret_cast<const uint8_t*>(g.Bq) +
-                                 (b_slab0 * kWeightTileRows + (tn * BN) % kWeightTileRows) * KB
-                           : reinterpret_cast<const uint8_t*>(g.B) +
-                                 (b_slab0 * kWeightTileRows + (tn * BN) % kWeightTileRows) * KB * 2;
-    const uint8_t* Sb = Q8 ? reinterpret_cast<const uint8_t*>(g.Bs) +
+    const uint8_t* Bb = (QW ? reinterpret_cast<const uint8_t*>(g.Bq) : reinterpret_cast<const uint8_t*>(g.B)) +
+                        (b_slab0 * kWeightTileRows + (tn * BN) % kWeightTileRows) * Sh::B_ROW;
+    const uint8_t* Sb = QW ? reinterpret_cast<const uint8_t*>(g.Bs) +
                                  (b_slab0 * kWeightTileRows + (tn * BN) % kWeightTileRows) * 2
                            : nullptr;
     constexpr int64_t A_SLAB = (int64_t)kWeightTileRows * KB * 2;              // bytes between slabs
-    constexpr int64_t B_SLAB = (int64_t)kWeightTileRows * KB * (Q8 ? 1 : 2);
+    constexpr int64_t B_SLAB = (int64_t)kWeightTileRows * Sh::B_ROW;
     constexpr int64_t S_SLAB = (int64_t)kWeightTileRows * 2;
     auto issue = [&](int kt, int st) {
         uint8_t* sa = smem + st * Sh::STAGE;
@@ -303,10 +310,13 @@ __device__ __forceinline__ void t32_tile(const GemmArgs& g, int tm, int tn, int 
             __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Ab + kt * A_SLAB + (i * NW + wave) * 1024 + lane * 16),
                                              (lds_ptr_t)(sa + (i * NW + wave) * 1024), 16, 0, 0);
 #pragma unroll
-        for (int i = 0; i < BI; ++i)
-            __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Bb + kt * B_SLAB + (i * NW + wave) * 1024 + lane * 16),
-                                             (lds_ptr_t)(sb + (i * NW + wave) * 1024), 16, 0, 0);
-        if constexpr (Q8) {
+        for (int i = 0; i < BI; ++i) {
+            const uint8_t* src = Bb + kt * B_SLAB + (i * NW + wave) * 64 * BSZ + lane * BSZ;
+            uint8_t* dst = sb + (i * NW + wave) * 64 * BSZ;
+            if constexpr (BSZ == 16) __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)dst, 16, 0, 0);
+            else __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)dst, 4, 0, 0);
+        }
+        if constexpr (QW) {
             if (lane < SL)
                 __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Sb + kt * S_SLAB + wave * SL * 4 + lane * 4),
                                                  (lds_ptr_t)(sb + Sh::B_BYTES + wave * SL * 4), 4, 0, 0);
@@ -329,12 +339,12 @@ __device__ __forceinline__ void t32_tile(const GemmArgs& g, int tm, int tn, int 
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     const int frow = lane & 31, fk = lane >> 5;
     const int sw = ((frow >> 1) ^ (frow >> 3)) & 3;     // fragment rows differ by multiples of 32
-    const int swq = (frow >> 2) & 3;                    // q8_0 code chunk swizzle
+    const int swq = Q4 ? (frow >> 3) & 3 : (frow >> 2) & 3;   // q4_0 / q8_0 code chunk swizzle
     int aoff[MI], boff[NI];
 #pragma unroll
     for (int i = 0; i < MI; ++i) aoff[i] = (wm * WM + i * 32 + frow) * KB * 2;
 #pragma unroll
-    for (int j = 0; j < NI; ++j) boff[j] = Sh::A_BYTES + (wn * WN + j * 32 + frow) * KB * (Q8 ? 1 : 2);
+    for (int j = 0; j < NI; ++j) boff[j] = Sh::A_BYTES + (wn * WN + j * 32 + frow) * Sh::B_ROW;
     // fragments: fa/fb ready for the MFMA; for q8_0, qc/qs hold the raw codes and scales
     u32x4 fa0[MI], fb0[NI], fa1[MI], fb1[NI];
     u32x2 qc0[NI], qc1[NI];
@@ -344,11 +354,12 @@ __device__ __forceinline__ void t32_tile(const GemmArgs& g, int tm, int tn, int 
         const int c = ((ks * 2 + fk) ^ sw) << 4;
 #pragma unroll
         for (int i = 0; i < MI; ++i) fa[i] = *(const u32x4*)(base + aoff[i] + c);
-        if constexpr (Q8) {
-            const int cq = ((ks * 2 + fk) ^ swq) << 3;
+        if constexpr (QW) {
+            const int cq = ((ks * 2 + fk) ^ swq) << (Q4 ? 2 : 3);
 #pragma unroll
             for (int j = 0; j < NI; ++j) {
-                qc[j] = *(const u32x2*)(base + boff[j] + cq);
+                if constexpr (Q4) qc[j] = u32x2{*(const uint32_t*)(base + boff[j] + cq), 0u};
+                else qc[j] = *(const u32x2*)(base + boff[j] + cq);
                 qs[j] = *(const uint16_t*)(base + Sh::A_BYTES + Sh::B_BYTES + (wn * WN + j * 32 + frow) * 2);
             }
         } else {
@@ -357,9 +368,9 @@ __device__ __forceinline__ void t32_tile(const GemmArgs& g, int tm, int tn, int 
         }
     };
     auto cvt = [&](u32x4* fb, const u32x2* qc, const uint16_t* qs) {
-        if constexpr (Q8) {
+        if constexpr (QW) {
 #pragma unroll
-            for (int j = 0; j < NI; ++j) fb[j] = q8_fragment(qc[j], qs[j]);
+            for (int j = 0; j < NI; ++j) fb[j] = q_fragment<Q4>(qc[j], qs[j]);
         }
     };
     auto mm = [&](const u32x4* fa, const u32x4* fb) {
@@ -384,7 +395,7 @@ __device__ __forceinline__ void t32_tile(const GemmArgs& g, int tm, int tn, int 
     // fragments between their two halves; it waits for the reads, and the
     // first MFMAs cover that latency).
     auto order = [&]() {
-        if constexpr (Q8) {
+        if constexpr (QW) {
             __builtin_amdgcn_sched_group_barrier(0x100, MI + 2 * NI, 0);   // LDS reads
             __builtin_amdgcn_sched_group_barrier(0x008, MI * NI / 2, 0);   // MFMAs
             __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);            // VALU: conversion
@@ -403,7 +414,7 @@ __device__ __forceinline__ void t32_tile(const GemmArgs& g, int tm, int tn, int 
     // the other wave of its SIMD (measured: q8_0 GEMMs 3-6% faster; the
     // 16-bit path is faster without it)
     auto prio = [](auto p) {
-        if constexpr (Q8) {
+        if constexpr (QW) {
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_setprio(decltype(p)::value);
         }
@@ -469,7 +480,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_t32(GemmArgs g) {
 // in the same order: the split point never changes the bits.  SBN: 128, or
 // 256 for q8_0 (whose 128-column weight slab is too small for 8 waves' DMA).
 template <int OPD>
-constexpr int kTailBN = OPD == OPD_Q8 ? 256 : 128;
+constexpr int kTailBN = OPD == OPD_Q8 ? 256 : 128;   // q4_0's 128-column slab fits 8 waves' DMA
 
 template <int OPD>
 __global__ void __launch_bounds__(512) gemm_t32_heads(GemmArgs g, int n_big, int grid_big) {
@@ -495,7 +506,7 @@ template <int BM, int BN, int WGM, int WGN, int OPD, int EPI>
 hipError_t launch_t32(const GemmArgs& a, hipStream_t s) {
     if (a.N % BN) return hipErrorInvalidValue;
     if (a.splits < 1 || a.splits > a.K / 32 || (a.splits > 1 && EPI != EPI_PARTIAL)) return hipErrorInvalidValue;
-    if (OPD == OPD_Q8 ? (!a.Bq || !a.Bs) : !a.B) return hipErrorInvalidValue;
+    if ((OPD == OPD_Q8 || OPD == OPD_Q4) ? (!a.Bq || !a.Bs) : !a.B) return hipErrorInvalidValue;
     const int total = ((a.M + BM - 1) / BM) * (a.N / BN) * a.splits;
     const int grid = (total + 7) / 8 * 8;
     hipLaunchKernelGGL((gemm_t32<BM, BN, WGM, WGN, OPD, EPI>), dim3(grid), dim3(64 * WGM * WGN), 0, s, a);
@@ -509,17 +520,19 @@ hipError_t launch_t32(const GemmArgs& a, hipStream_t s) {
 hipError_t launch_gemm_heads(GemmOperand opd, const GemmArgs& a, int n_cu, hipStream_t s) {
     if (a.M <= 0) return hipSuccess;
     if (a.K % 32 != 0 || a.K <= 0 || a.N % 256 || a.splits != 1) return hipErrorInvalidValue;
-    if (opd == OPD_Q8 ? (!a.Bq || !a.Bs) : !a.B) return hipErrorInvalidValue;
-    if (opd != OPD_BF16 && opd != OPD_Q8) return hipErrorNotSupported;
+    if ((opd == OPD_Q8 || opd == OPD_Q4) ? (!a.Bq || !a.Bs) : !a.B) return hipErrorInvalidValue;
+    if (opd != OPD_BF16 && opd != OPD_Q8 && opd != OPD_Q4) return hipErrorNotSupported;
     // Few rows: one M-tile of 64 or 128 rows, so that every weight strip is
     // read once by a workgroup whose MFMA work matches the real rows (with
     // 256-row tiles a short call would run a 256-row product on padding).
     if (a.M <= 64) {
         if (opd == OPD_BF16) return launch_t32<64, 256, 1, 4, OPD_BF16, EPI_HEADS>(a, s);
+        if (opd == OPD_Q4) return launch_t32<64, 256, 1, 4, OPD_Q4, EPI_HEADS>(a, s);
         return launch_t32<64, 256, 1, 4, OPD_Q8, EPI_HEADS>(a, s);
     }
     if (a.M <= 128) {
         if (opd == OPD_BF16) return launch_t32<128, 256, 2, 4, OPD_BF16, EPI_HEADS>(a, s);
+        if (opd == OPD_Q4) return launch_t32<128, 256, 2, 4, OPD_Q4, EPI_HEADS>(a, s);
         return launch_t32<128, 256, 2, 4, OPD_Q8, EPI_HEADS>(a, s);
     }
     const int mt = (a.M + 255) / 256, nt = a.N / 256, total = mt * nt;
@@ -528,13 +541,15 @@ hipError_t launch_gemm_heads(GemmOperand opd, const GemmArgs& a, int n_cu, hipSt
     int n_big = nt;
     if (n_cu > 0 && total > n_cu && total % n_cu != 0) n_big = (total / n_cu) * n_cu / mt;
     const int grid_big = (mt * n_big + 7) / 8 * 8;
-    const int sbn = opd == OPD_Q8 ? kTailBN<OPD_Q8> : kTailBN<OPD_BF16>;
+    const int sbn = opd == OPD_Q8 ? kTailBN<OPD_Q8> : opd == OPD_Q4 ? kTailBN<OPD_Q4> : kTailBN<OPD_BF16>;
     const int n_small = ((a.M + 127) / 128) * ((a.N - 256 * n_big) / sbn);
     const int grid = grid_big + (n_small + 7) / 8 * 8;
     if (opd == OPD_BF16)
         hipLaunchKernelGGL(gemm_t32_heads<OPD_BF16>, dim3(grid), dim3(512), 0, s, a, n_big, grid_big);
     else if (opd == OPD_Q8)
         hipLaunchKernelGGL(gemm_t32_heads<OPD_Q8>, dim3(grid), dim3(512), 0, s, a, n_big, grid_big);
+    else if (opd == OPD_Q4)
+        hipLaunchKernelGGL(gemm_t32_heads<OPD_Q4>, dim3(grid), dim3(512), 0, s, a, n_big, grid_big);
     else
         return hipErrorNotSupported;
     return hipGetLastError();
@@ -558,6 +573,12 @@ hipError_t launch_gemm_t32(GemmOperand opd, GemmTile tile, EpiKind epi, const Ge
     KVA_T32_CASE(OPD_Q8, TILE_128x128, EPI_PARTIAL, 128, 128, 1, 4)
     KVA_T32_CASE(OPD_Q8, TILE_128x128, EPI_QKV, 128, 128, 1, 4)
     KVA_T32_CASE(OPD_Q8, TILE_128x128, EPI_SWIGLU, 128, 128, 2, 2)
+    KVA_T32_CASE(OPD_Q4, TILE_256x256, EPI_PARTIAL, 256, 256, 2, 4)
+    KVA_T32_CASE(OPD_Q4, TILE_256x256, EPI_QKV, 256, 256, 2, 4)
+    KVA_T32_CASE(OPD_Q4, TILE_256x256, EPI_SWIGLU, 256, 256, 2, 4)
+    KVA_T32_CASE(OPD_Q4, TILE_128x128, EPI_PARTIAL, 128, 128, 1, 4)
+    KVA_T32_CASE(OPD_Q4, TILE_128x128, EPI_QKV, 128, 128, 1, 4)
+    KVA_T32_CASE(OPD_Q4, TILE_128x128, EPI_SWIGLU, 128, 128, 2, 2)
     return hipErrorNotSupported;
 }
 #undef KVA_T32_CASE

@@ -34,15 +34,46 @@ __host__ __device__ inline int64_t tiled32_index(int64_t row, int64_t k, int64_t
 // q8_0 weights [rows][K] use the same grouping: for each 256-row group and
 // each 32-wide K slab (exactly one q8_0 block per row), the int8 codes of the
 // 256 rows form one contiguous 8 KB block of 32-byte rows, the 8-byte chunk c
-// of row r at chunk c ^ ((r >> 2) & 3); the fp16 scales of the same rows form
-// one contiguous 512-byte block.
-__host__ __device__ inline int64_t q8_code_index(int64_t row, int64_t k, int64_t K) {
+// of row r (K-values 8c..8c+7, in q8_chunk_pack order) at chunk
+// c ^ ((r >> 2) & 3); the fp16 scales of the same rows form one contiguous
+// 512-byte block.  Returns the byte offset of the chunk holding K-value k.
+__host__ __device__ inline int64_t q8_code_chunk(int64_t row, int64_t k, int64_t K) {
     const int64_t nb = row / kWeightTileRows, r = row % kWeightTileRows, kt = k / 32;
-    const int64_t c = (k % 32) / 8, e = k % 8;
-    return ((nb * (K / 32) + kt) * kWeightTileRows + r) * 32 + ((c ^ ((r >> 2) & 3)) * 8) + e;
+    const int64_t c = (k % 32) / 8;
+    return ((nb * (K / 32) + kt) * kWeightTileRows + r) * 32 + ((c ^ ((r >> 2) & 3)) * 8);
+}
+// The 8-byte chunk of 8 int8 codes (q[e] = code of K-value 8c + e): each
+// 32-bit half holds codes 4j, 4j + 2, 4j + 1, 4j + 3 in its bytes 0..3, so
+// that one mask puts a pair of consecutive codes into the two 16-bit halves.
+__host__ __device__ inline void q8_chunk_pack(const int8_t q[8], uint32_t* c0, uint32_t* c1) {
+    uint32_t w[2];
+    for (int j = 0; j < 2; ++j)
+        w[j] = (uint32_t)(uint8_t)q[4 * j] | ((uint32_t)(uint8_t)q[4 * j + 2] << 8) |
+               ((uint32_t)(uint8_t)q[4 * j + 1] << 16) | ((uint32_t)(uint8_t)q[4 * j + 3] << 24);
+    *c0 = w[0];
+    *c1 = w[1];
 }
 __host__ __device__ inline int64_t q8_scale_index(int64_t row, int64_t kblock, int64_t K) {
     return ((row / kWeightTileRows) * (K / 32) + kblock) * kWeightTileRows + row % kWeightTileRows;
+}
+// q4_0 weights: per 256-row group and 32-wide slab, the codes of the 256
+// rows form one contiguous 4 KB block of 16-byte rows; the 32-bit chunk c of
+// row r (K-values 8c..8c+7) sits at chunk c ^ ((r >> 3) & 3), with K-value
+// 8c + 2h in bits 4h..4h+3 and 8c + 2h + 1 in bits 16+4h..16+4h+3 (h < 4),
+// so that one mask puts a pair of codes into the two 16-bit halves.  The
+// scales use q8_scale_index.  Returns the byte offset of the chunk holding
+// K-value k.
+__host__ __device__ inline int64_t q4_code_chunk(int64_t row, int64_t k, int64_t K) {
+    const int64_t nb = row / kWeightTileRows, r = row % kWeightTileRows, kt = k / 32;
+    const int64_t c = (k % 32) / 8;
+    return ((nb * (K / 32) + kt) * kWeightTileRows + r) * 16 + ((c ^ ((r >> 3) & 3)) * 4);
+}
+// The 32-bit chunk of 8 codes (n[e] = code of K-value 8c + e) in that order.
+__host__ __device__ inline uint32_t q4_chunk_pack(const uint8_t n[8]) {
+    uint32_t w = 0;
+    for (int h = 0; h < 4; ++h)
+        w |= ((uint32_t)(n[2 * h] & 0xF) << (4 * h)) | ((uint32_t)(n[2 * h + 1] & 0xF) << (16 + 4 * h));
+    return w;
 }
 
 struct HeadOut {
@@ -77,9 +108,10 @@ struct EpiArgs {
 
 // C[M][N] = A[M][K] * B[N][K]^T with 16-bit activations (tiled32 layout)
 // and fp32 accumulation.  16-bit weights: B (tiled32 layout).  q8_0 weights:
-// int8 codes Bq (q8_code_index layout) and one fp16 scale per 32 codes, Bs
+// int8 codes Bq (q8_code_chunk layout) and one fp16 scale per 32 codes, Bs
 // (q8_scale_index layout); the weight is d * q (see q8_0_value), rounded
-// once to fp16 for the MFMA.
+// once to fp16 for the MFMA.  q4_0 weights: codes in Bq (q4_code_byte
+// layout), scales in Bs as for q8_0.
 struct GemmArgs {
     const uint16_t* A = nullptr;
     int64_t lda = 0;
@@ -99,8 +131,8 @@ struct GemmArgs {
 };
 
 // Operand type: both operands fp16, both bf16, or fp16 activations with
-// q8_0 weights (fp16 MFMA on d*q rounded once to fp16).
-enum GemmOperand : int { OPD_F16 = 0, OPD_BF16 = 1, OPD_Q8 = 2 };
+// q8_0 / q4_0 weights (fp16 MFMA on the weights rounded once to fp16).
+enum GemmOperand : int { OPD_F16 = 0, OPD_BF16 = 1, OPD_Q8 = 2, OPD_Q4 = 3 };
 
 // One q8_0 weight: the fp16 block scale (bit pattern d_bits) times the int8
 // code, exactly (an 11-bit significand times an 8-bit integer fits fp32's 24
@@ -109,19 +141,42 @@ __device__ __forceinline__ float q8_0_value(uint16_t d_bits, int q) {
     return (float)__builtin_bit_cast(_Float16, d_bits) * (float)q;
 }
 
-// Eight q8_0 weights as the fp16 values the MFMA consumes: codes c0 (K-values
-// 0..3, one byte each, lowest first) and c1 (4..7) times the fp16 scale
-// d_bits, each product rounded once to nearest-even fp16 (one fp16 multiply
-// of two exact fp16 operands is correctly rounded, so this is q8_0_value
-// rounded once).  out[h] packs K-values 2h (low half) and 2h + 1.
-__device__ __forceinline__ void q8_0_f16x8(uint32_t c0, uint32_t c1, uint16_t d_bits, uint32_t out[4]) {
+// Eight q4_0 weights as the fp16 values the MFMA consumes: a chunk of 8
+// codes n (q4_chunk_pack order) times the fp16 scale d_bits as d * (n - 8),
+// rounded once to nearest-even fp16.  Each code pair goes into the mantissas
+// of two fp16 values 1024 + n (exact: the spacing there is 1), 1032 is
+// subtracted exactly, and one fp16 multiply (correctly rounded) applies d.
+// out[h] packs K-values 2h (low half) and 2h + 1.
+typedef _Float16 kva_half2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void q4_0_f16x8(uint32_t codes, uint16_t d_bits, uint32_t out[4]) {
     const _Float16 d = __builtin_bit_cast(_Float16, d_bits);
+    const kva_half2 dd = {d, d};
+    const kva_half2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-        const uint32_t w = (h < 2 ? c0 : c1) >> (16 * (h & 1));
-        const _Float16 lo = (_Float16)(int8_t)(w & 0xFF) * d;
-        const _Float16 hi = (_Float16)(int8_t)((w >> 8) & 0xFF) * d;
-        out[h] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        const uint32_t t = ((codes >> (4 * h)) & 0x000F000Fu) | 0x64006400u;   // 1024 + n, two halves
+        const kva_half2 v = (__builtin_bit_cast(kva_half2, t) - off) * dd;
+        out[h] = __builtin_bit_cast(uint32_t, v);
+    }
+}
+
+// Eight q8_0 weights as the fp16 values the MFMA consumes: a chunk of 8 int8
+// codes q (q8_chunk_pack order) times the fp16 scale d_bits, each product
+// rounded once to nearest-even fp16.  Each code pair goes into the mantissas
+// of two fp16 values 1024 + (q + 128) (bits 0x6400 | (q ^ 0x80); exact: the
+// spacing there is 1), 1152 is subtracted exactly, and one fp16 multiply
+// (correctly rounded, so this is q8_0_value rounded once) applies d.
+// out[h] packs K-values 2h (low half) and 2h + 1.
+__device__ __forceinline__ void q8_0_f16x8(uint32_t c0, uint32_t c1, uint16_t d_bits, uint32_t out[4]) {
+    const _Float16 d = __builtin_bit_cast(_Float16, d_bits);
+    const kva_half2 dd = {d, d};
+    const kva_half2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        const uint32_t w = (h < 2 ? c0 : c1) >> (8 * (h & 1));
+        const uint32_t t = (w & 0x00FF00FFu) ^ 0x64806480u;      // 1024 + (q ^ 0x80), two halves
+        const kva_half2 v = (__builtin_bit_cast(kva_half2, t) - off) * dd;
+        out[h] = __builtin_bit_cast(uint32_t, v);
     }
 }
 // 256x256: 8 waves (2 per SIMD); 128x128: 4 waves.
@@ -184,6 +239,7 @@ hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
 
 hipError_t launch_dequant_q8_0(const void* blocks, int64_t n_blocks, float* out, hipStream_t stream);
 hipError_t launch_dequant_q8_0_f16(const void* blocks, int64_t n_blocks, uint16_t* out, hipStream_t stream);
+hipError_t launch_dequant_q4_0_f16(const void* blocks, int64_t n_blocks, uint16_t* out, hipStream_t stream);
 
 // n_workgroups x 4 waves, each n_iter x 8 bf16 32x32x16 MFMAs; sink: 256 floats per workgroup.
 hipError_t launch_mfma_loop(int32_t n_iter, int32_t n_workgroups, float* sink, hipStream_t stream);

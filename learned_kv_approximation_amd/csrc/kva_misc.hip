@@ -174,12 +174,40 @@ __global__ void dequant_q8_0_f16_kernel(const uint8_t* __restrict__ blocks, int6
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // group of 8 values
     if (i >= n_blocks * 4) return;
     const uint8_t* blk = blocks + (i >> 2) * 34;
-    const uint8_t* c = blk + 2 + (i & 3) * 8;
+    const int8_t* c = reinterpret_cast<const int8_t*>(blk + 2 + (i & 3) * 8);
     const uint16_t d = (uint16_t)blk[0] | ((uint16_t)blk[1] << 8);
-    const uint32_t c0 = (uint32_t)c[0] | ((uint32_t)c[1] << 8) | ((uint32_t)c[2] << 16) | ((uint32_t)c[3] << 24);
-    const uint32_t c1 = (uint32_t)c[4] | ((uint32_t)c[5] << 8) | ((uint32_t)c[6] << 16) | ((uint32_t)c[7] << 24);
+    int8_t q[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = c[e];
+    uint32_t c0, c1;
+    q8_chunk_pack(q, &c0, &c1);
     uint32_t o[4];
     q8_0_f16x8(c0, c1, d, o);   // shared with the q8_0 GEMM
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        out[i * 8 + 2 * h] = (uint16_t)(o[h] & 0xFFFF);
+        out[i * 8 + 2 * h + 1] = (uint16_t)(o[h] >> 16);
+    }
+}
+
+// The fp16 weights of q4_0 blocks as the GEMM forms them (q4_0_f16x8), one
+// thread per 8 values: the 8 codes of K-values 8c..8c+7 are gathered from
+// the block's ggml order into the GEMM's chunk order first (test hook).
+__global__ void dequant_q4_0_f16_kernel(const uint8_t* __restrict__ blocks, int64_t n_blocks,
+                                        uint16_t* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // group of 8 values
+    if (i >= n_blocks * 4) return;
+    const uint8_t* blk = blocks + (i >> 2) * 18;
+    const int c = (int)(i & 3);
+    const uint16_t d = (uint16_t)blk[0] | ((uint16_t)blk[1] << 8);
+    uint8_t nn[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int k = 8 * c + e;                                 // input of the block
+        nn[e] = k < 16 ? (blk[2 + k] & 0xF) : (blk[2 + k - 16] >> 4);
+    }
+    uint32_t o[4];
+    q4_0_f16x8(q4_chunk_pack(nn), d, o);    // shared with the q4_0 GEMM
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
         out[i * 8 + 2 * h] = (uint16_t)(o[h] & 0xFFFF);
@@ -263,6 +291,14 @@ hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t s) {
     if (a.head_dim != 256 || a.n_kv_heads != 4 || a.n_rot % 8 || a.n_rot > 64 || a.n_rot <= 0)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(kv_write_kernel, dim3(a.n_tokens), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant_q4_0_f16(const void* blocks, int64_t n_blocks, uint16_t* out, hipStream_t s) {
+    if (n_blocks <= 0) return hipSuccess;
+    const int64_t n = n_blocks * 4;
+    hipLaunchKernelGGL(dequant_q4_0_f16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       (const uint8_t*)blocks, n_blocks, out);
     return hipGetLastError();
 }
 

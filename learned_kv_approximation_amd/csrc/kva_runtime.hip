@@ -165,7 +165,7 @@ struct kva_ctx {
 
     // weights (device).  A weight is either 16-bit values w16 (fp16 trunk,
     // bf16 heads; tiled as in tiled32_index) or, for q8_0, int8 codes q and
-    // fp16 scales sc (tiled as in q8_code_index / q8_scale_index).  Every
+    // fp16 scales sc (tiled as in q8_code_chunk / q8_scale_index).  Every
     // GEMM activation operand is in the tiled32 layout (its producer writes
     // it so).
     struct DevW {
@@ -173,7 +173,8 @@ struct kva_ctx {
         int8_t* q = nullptr;
         uint16_t* sc = nullptr;
     };
-    bool q8 = false;
+    bool q8 = false;               // block-quantised weights (q8_0 or q4_0): fp16 activations
+    bool q4 = false;               // ... and they are q4_0
     DevW w_in;
     float* g_in = nullptr;
     float* g_out = nullptr;
@@ -268,7 +269,7 @@ kva_status validate(const kva_config* c) {
     if (c->max_tokens > (1 << 24)) return fail(KVA_ERR_SHAPE, "max_tokens above 2^24");
     if (!(c->eps >= 0.0f) || !std::isfinite(c->eps)) return fail(KVA_ERR_ARG, "eps must be finite and >= 0");
     if (c->weight_dtype != KVA_DTYPE_F32 && c->weight_dtype != KVA_DTYPE_BF16 &&
-        c->weight_dtype != KVA_DTYPE_Q8_0)
+        c->weight_dtype != KVA_DTYPE_Q8_0 && c->weight_dtype != KVA_DTYPE_Q4_0)
         return fail(KVA_ERR_DTYPE, "unknown weight dtype %d", c->weight_dtype);
     if (c->has_head_bias != 0 && c->has_head_bias != 1) return fail(KVA_ERR_ARG, "has_head_bias must be 0 or 1");
     if (c->n_out_heads < 1 || c->n_out_heads > kMaxHeads)
@@ -306,7 +307,7 @@ struct RowSrc {
 };
 
 // Target layouts on the device.
-enum PackTarget { PACK_F16_T32 = 0, PACK_BF16_T32 = 1, PACK_Q8 = 2 };
+enum PackTarget { PACK_F16_T32 = 0, PACK_BF16_T32 = 1, PACK_Q8 = 2, PACK_Q4 = 3 };
 
 // Packs rows (each K wide, stored in `dtype`) into the compute layout and
 // uploads it: fp16 or bf16 values in the tiled layout of tiled32_index
@@ -317,6 +318,34 @@ kva_status pack_weight(kva_ctx* ctx, int dtype, int64_t K, const std::vector<Row
     const int64_t n = (int64_t)rows.size();
     for (const RowSrc& r : rows)
         if (!r.src && r.row >= 0) return fail(KVA_ERR_ARG, "weight %s is NULL", name);
+    if (target == PACK_Q4) {
+        if (dtype != KVA_DTYPE_Q4_0) return fail(KVA_ERR_DTYPE, "q4_0 layout needs q4_0 weights (%s)", name);
+        if (n % kWeightTileRows || K % 32) return fail(KVA_ERR_SHAPE, "weight %s: bad padding", name);
+        const int64_t nb = K / 32;
+        std::vector<uint8_t> q((size_t)(n * K / 2), 0x88);   // padding rows: codes 8 (and scale 0)
+        std::vector<uint16_t> sc((size_t)(n * nb), 0);
+        for (int64_t r = 0; r < n; ++r) {
+            if (!rows[r].src) continue;
+            const uint8_t* blk = static_cast<const uint8_t*>(rows[r].src) + rows[r].row * nb * 18;
+            for (int64_t b = 0; b < nb; ++b) {
+                const uint8_t* qs = blk + b * 18 + 2;
+                sc[(size_t)q8_scale_index(r, b, K)] = (uint16_t)(blk[b * 18] | (blk[b * 18 + 1] << 8));
+                for (int64_t c = 0; c < 4; ++c) {       // 8 inputs of the block per chunk
+                    uint8_t nn[8];
+                    for (int e = 0; e < 8; ++e) {
+                        const int k = (int)(8 * c) + e;
+                        nn[e] = k < 16 ? (qs[k] & 0xF) : (qs[k - 16] >> 4);
+                    }
+                    const uint32_t w = q4_chunk_pack(nn);
+                    std::memcpy(&q[(size_t)q4_code_chunk(r, b * 32 + 8 * c, K)], &w, 4);
+                }
+            }
+        }
+        HIP_TRY(ctx->alloc(&out->q, q.size(), true));
+        HIP_TRY(ctx->alloc(&out->sc, sc.size() * 2, true));
+        KVA_TRY(upload(ctx, out->q, q.data(), q.size()));
+        return upload(ctx, out->sc, sc.data(), sc.size() * 2);
+    }
     if (target == PACK_Q8) {
         if (dtype != KVA_DTYPE_Q8_0) return fail(KVA_ERR_DTYPE, "q8_0 layout needs q8_0 weights (%s)", name);
         if (n % kWeightTileRows || K % 32) return fail(KVA_ERR_SHAPE, "weight %s: bad padding", name);
@@ -328,8 +357,11 @@ kva_status pack_weight(kva_ctx* ctx, int dtype, int64_t K, const std::vector<Row
             const uint8_t* blk = static_cast<const uint8_t*>(rows[r].src) + rows[r].row * nb * 34;
             for (int64_t b = 0; b < nb; ++b) {
                 sc[(size_t)q8_scale_index(r, b, K)] = (uint16_t)(blk[b * 34] | (blk[b * 34 + 1] << 8));
-                for (int64_t c = 0; c < 32; c += 8)   // 8 consecutive codes stay together
-                    std::memcpy(&q[(size_t)q8_code_index(r, b * 32 + c, K)], blk + b * 34 + 2 + c, 8);
+                for (int64_t c = 0; c < 32; c += 8) {   // 8 consecutive codes form one chunk
+                    uint32_t w[2];
+                    q8_chunk_pack(reinterpret_cast<const int8_t*>(blk + b * 34 + 2 + c), &w[0], &w[1]);
+                    std::memcpy(&q[(size_t)q8_code_chunk(r, b * 32 + c, K)], w, 8);
+                }
             }
         }
         HIP_TRY(ctx->alloc(&out->q, q.size(), true));
@@ -374,17 +406,19 @@ void pad_rows(std::vector<RowSrc>& v) {
 kva_status create_impl(const kva_config* cfg, const kva_weights* w, int device, kva_ctx* ctx) {
     const kva_config& c = *cfg;
     const int dt = c.weight_dtype;
-    const bool q8 = dt == KVA_DTYPE_Q8_0;
+    const bool q4 = dt == KVA_DTYPE_Q4_0;
+    const bool q8 = dt == KVA_DTYPE_Q8_0 || q4;
     if (q8 && (c.n_in % 32 || c.d_model % 32 || c.d_ffn % 32))
-        return fail(KVA_ERR_SHAPE, "q8_0 needs every Linear input width to be a multiple of 32");
+        return fail(KVA_ERR_SHAPE, "q8_0 / q4_0 need every Linear input width to be a multiple of 32");
     const int64_t d = c.d_model, F = c.d_ffn, n_in = c.n_in;
     const int64_t hd = (int64_t)c.n_heads * c.head_dim;
     HIP_TRY(hipSetDevice(device));
     ctx->device = device;
     HIP_TRY(hipDeviceGetAttribute(&ctx->n_cu, hipDeviceAttributeMultiprocessorCount, device));
     ctx->q8 = q8;
-    const PackTarget trunk_t = q8 ? PACK_Q8 : PACK_F16_T32;
-    const PackTarget head_t = q8 ? PACK_Q8 : PACK_BF16_T32;
+    ctx->q4 = q4;
+    const PackTarget trunk_t = q4 ? PACK_Q4 : q8 ? PACK_Q8 : PACK_F16_T32;
+    const PackTarget head_t = q4 ? PACK_Q4 : q8 ? PACK_Q8 : PACK_BF16_T32;
 
     auto putf = [&](float** dstp, const float* src, int64_t n, const char* name) -> kva_status {
         if (!src) return fail(KVA_ERR_ARG, "gain %s is NULL", name);
@@ -592,7 +626,7 @@ kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n, float* co
     const int64_t d = c.d_model, F = c.d_ffn, n_in = c.n_in;
     const int64_t hd = (int64_t)c.n_heads * c.head_dim;
     // every GEMM activation operand is written in the tiled32 layout
-    const GemmOperand opd = ctx->q8 ? OPD_Q8 : OPD_F16;
+    const GemmOperand opd = ctx->q4 ? OPD_Q4 : ctx->q8 ? OPD_Q8 : OPD_F16;
     auto gemm = [&](EpiKind epi, const GemmArgs& g) -> hipError_t {
         return launch_gemm_t32(opd, pick_tile_t32(g.M, g.N, g.splits), epi, g, s);
     };
@@ -654,7 +688,7 @@ kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n, float* co
         g.epi.tail_head = ctx->tail_head; g.epi.tail_col = ctx->tail_col;
         g.epi.tail_start = ctx->tail_start; g.epi.bias = ctx->b_heads;
         g.epi.heads = ho;
-        STAGE(KVA_STAGE_GEMM_HEADS, launch_gemm_heads(ctx->q8 ? OPD_Q8 : OPD_BF16, g, ctx->n_cu, s));
+        STAGE(KVA_STAGE_GEMM_HEADS, launch_gemm_heads(ctx->q8 ? opd : OPD_BF16, g, ctx->n_cu, s));
     }
     ctx->stats.calls += 1;
     ctx->stats.tokens += (uint64_t)n;
@@ -704,6 +738,13 @@ kva_status kva_debug_dequant_q8_0(const void* blocks, int64_t n_blocks, float* o
     if (!blocks || !out) return fail(KVA_ERR_ARG, "NULL argument");
     if (n_blocks < 0) return fail(KVA_ERR_SHAPE, "negative n_blocks");
     LAUNCH(launch_dequant_q8_0(blocks, n_blocks, out, static_cast<hipStream_t>(stream)));
+    return KVA_OK;
+}
+
+kva_status kva_debug_dequant_q4_0_f16(const void* blocks, int64_t n_blocks, uint16_t* out, void* stream) {
+    if (!blocks || !out) return fail(KVA_ERR_ARG, "NULL argument");
+    if (n_blocks < 0) return fail(KVA_ERR_SHAPE, "negative n_blocks");
+    LAUNCH(launch_dequant_q4_0_f16(blocks, n_blocks, out, static_cast<hipStream_t>(stream)));
     return KVA_OK;
 }
 

@@ -60,6 +60,22 @@ def dequant_q8_0(packed: np.ndarray, rows: int, cols: int) -> np.ndarray:
     return (d[:, :, None] * q).reshape(rows, cols)
 
 
+def dequant_q4_0(packed: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """q4_0 (ggml's 4-bit block format, the card's smaller projector file on
+    [KVA] "Projector quantization and flash-attn"): each run of 32 inputs is
+    one 18-byte block, a fp16 scale d then 16 bytes of 4-bit codes n; the
+    weight is d * (n - 8).  The pages fix only the block size (the 525 MB
+    file); the code order (byte j: input j in the low nibble, input j + 16
+    in the high nibble) and the offset 8 are ggml's.  d * (n - 8) has at
+    most 11 + 4 significant bits: exact in float64."""
+    nb = cols // Q8_0_BLOCK
+    blk = np.asarray(packed, dtype=np.uint8).reshape(rows, nb, Q4_0_BYTES)
+    d = f16_bits_to_f64(np.ascontiguousarray(blk[:, :, 0:2]).view(np.uint16)[:, :, 0])
+    qs = blk[:, :, 2:].astype(np.int64)
+    n = np.concatenate([qs & 0xF, qs >> 4], axis=2).astype(np.float64)   # inputs 0..15, then 16..31
+    return (d[:, :, None] * (n - 8.0)).reshape(rows, cols)
+
+
 def weight_f64(w: np.ndarray, dtype: str, out_dim: int, in_dim: int) -> np.ndarray:
     """A stored Linear weight [out][in] as float64 values."""
     if dtype == "f32":
@@ -68,6 +84,8 @@ def weight_f64(w: np.ndarray, dtype: str, out_dim: int, in_dim: int) -> np.ndarr
         return bf16_bits_to_f64(w).reshape(out_dim, in_dim)
     if dtype == "q8_0":
         return dequant_q8_0(w, out_dim, in_dim)
+    if dtype == "q4_0":
+        return dequant_q4_0(w, out_dim, in_dim)
     raise ValueError(dtype)
 
 
@@ -116,6 +134,11 @@ def f64_to_f16_bits(x: np.ndarray) -> np.ndarray:
     bits = h.view(np.uint16).copy()
     bits[np.isnan(x)] = 0x7E00
     return bits
+
+
+def dequant_q4_0_f16_bits(packed: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """q4_0 weights d * (n - 8) rounded once to the nearest binary16."""
+    return f64_to_f16_bits(dequant_q4_0(packed, rows, cols))
 
 
 def dequant_q8_0_f16_bits(packed: np.ndarray, rows: int, cols: int) -> np.ndarray:

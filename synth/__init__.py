@@ -16,7 +16,9 @@ Distributions: weights N(0, 1/fan_in) rounded once to the stored dtype; norm
 gains 1 + 0.02 N(0, 1); head biases N(0, 1/fan_in); residuals N(0, 1) per
 element, rescaled per token to an RMS of 4 for the full-size projectors.
 q8_0 weights: int8 codes uniform in [-127, 127] and one fp16 scale per block of
-32 inputs, |N(0, 1)| / (127 sqrt(fan_in)).
+32 inputs, |N(0, 1)| / (127 sqrt(fan_in)).  q4_0 weights (the card's other
+projector quantisation): 4-bit codes uniform in [0, 15] and one fp16 scale
+per block of 32 inputs, |N(0, 1)| / (8 sqrt(fan_in)).
 """
 from __future__ import annotations
 
@@ -84,6 +86,8 @@ _CONFIGS = {
 _CONFIGS["r3_q8_0"] = dict(copy.deepcopy(_CONFIGS["r3"]), weight_dtype="q8_0", seed=3,
                            n_tokens=65536)
 _CONFIGS["r3_kv"] = dict(copy.deepcopy(_CONFIGS["r3"]), seed=4, n_tokens=65536)
+_CONFIGS["r3_q4_0"] = dict(copy.deepcopy(_CONFIGS["r3"]), weight_dtype="q4_0", seed=5,
+                           n_tokens=8192)
 
 
 def config(name: str, **overrides) -> dict:
@@ -126,6 +130,23 @@ def pack_q8_0(codes: np.ndarray, scales_f16: np.ndarray) -> np.ndarray:
     return out.reshape(rows, nb * Q8_0_BYTES)
 
 
+Q4_0_BYTES = 2 + 16      # fp16 scale followed by 32 4-bit codes
+
+
+def pack_q4_0(codes: np.ndarray, scales_f16: np.ndarray) -> np.ndarray:
+    """Pack 4-bit codes [rows, cols] (values 0..15) and fp16 scales
+    [rows, cols/32] into 18-byte blocks: little-endian fp16 scale, then 16
+    bytes whose byte j holds code j in its low nibble and code j + 16 in its
+    high nibble (the ggml q4_0 layout)."""
+    rows, cols = codes.shape
+    nb = cols // Q8_0_BLOCK
+    c = np.asarray(codes, dtype=np.uint8).reshape(rows, nb, Q8_0_BLOCK)
+    out = np.empty((rows, nb, Q4_0_BYTES), dtype=np.uint8)
+    out[:, :, 0:2] = np.ascontiguousarray(scales_f16, dtype=np.float16).view(np.uint8).reshape(rows, nb, 2)
+    out[:, :, 2:] = (c[:, :, :16] & 0xF) | ((c[:, :, 16:] & 0xF) << 4)
+    return out.reshape(rows, nb * Q4_0_BYTES)
+
+
 # ---------------------------------------------------------------- weights
 
 def _linear(rng, out_dim, in_dim, dtype):
@@ -135,6 +156,12 @@ def _linear(rng, out_dim, in_dim, dtype):
         sc = np.abs(rng.standard_normal((out_dim, in_dim // Q8_0_BLOCK), dtype=np.float32))
         sc = (sc.astype(np.float64) / (127.0 * math.sqrt(in_dim))).astype(np.float16)
         return pack_q8_0(codes, sc)
+    if dtype == "q4_0":
+        assert in_dim % Q8_0_BLOCK == 0
+        codes = rng.integers(0, 16, size=(out_dim, in_dim), dtype=np.uint8)
+        sc = np.abs(rng.standard_normal((out_dim, in_dim // Q8_0_BLOCK), dtype=np.float32))
+        sc = (sc.astype(np.float64) / (8.0 * math.sqrt(in_dim))).astype(np.float16)
+        return pack_q4_0(codes, sc)
     w = rng.standard_normal((out_dim, in_dim), dtype=np.float32)
     w *= np.float32(1.0 / math.sqrt(in_dim))
     if dtype == "f32":

@@ -1,6 +1,8 @@
-"""GPU parity for the q8_0 projector and the chained attention-layer KV-cache
-write at prompt scale (65536 tokens, processed in 8192-token calls as the
-benchmark does).  Oracle: float64 on the dequantised weights (d * q).
+"""GPU parity for the q8_0 and q4_0 projectors and the chained
+attention-layer KV-cache write at prompt scale (65536 tokens, processed in
+8192-token calls as the benchmark does).  Oracle: float64 on the dequantised
+weights (d * q, d * (n - 8)).  q4_0 is held to the q8_0 bar (the pages give
+no bar of their own for it).
 
 Bars: q8_0 outputs max|err| <= 5e-2 * RMS per head; KV cache after the
 chained projection + k_norm + RoPE + bf16 store within the projector's bar
@@ -102,6 +104,56 @@ def test_r3_q8_0_short_call_bitwise_equal(r3q8):
     errs = [_err(short[i], want[i]) for i in (0, 35)]
     print("q8_0 64-token call max|err|/rms", errs)
     assert max(errs) <= TOL_Q8
+    proj.close()
+
+
+def test_dequant_q4_0_f16_weights_bit_exact():
+    """The fp16 weights the q4_0 GEMMs use equal d * (n - 8) rounded once to
+    nearest-even binary16, over every scale magnitude and both signs."""
+    rng = np.random.default_rng(13)
+    nb = 4096
+    codes = rng.integers(0, 16, size=(1, nb * 32), dtype=np.uint8)
+    sc_bits = rng.integers(0, 0x7C00, size=nb).astype(np.uint16)
+    sc_bits |= (rng.integers(0, 2, size=nb).astype(np.uint16) << 15)
+    sc_bits[:64] = np.arange(64, dtype=np.uint16)
+    packed = synth.pack_q4_0(codes, sc_bits.view(np.float16).reshape(1, nb))
+    want = ref.dequant_q4_0_f16_bits(packed, 1, nb * 32).reshape(-1)
+    blocks = torch.from_numpy(packed.reshape(-1)).cuda()
+    out = torch.empty(nb * 32, dtype=torch.int16, device="cuda")
+    kva.kva_debug_dequant_q4_0_f16(blocks.data_ptr(), nb, out.data_ptr(), kva.current_stream())
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, want), np.flatnonzero(got != want)[:10]
+
+
+@pytest.mark.parametrize("n", [40, 100, 300])
+def test_tiny_q4_0_parity(n):
+    cfg = synth.config("tiny", weight_dtype="q4_0")
+    w = synth.make_weights(cfg)
+    x = synth.make_input(cfg, n_tokens=n)
+    proj = kva.Projector(cfg, w, max_tokens=n)
+    outs = proj.project(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    want = oracle.project(cfg, w, x)
+    errs = [_err(o.cpu().numpy(), want[i]) for i, o in enumerate(outs)]
+    print(f"tiny q4_0 n={n} max|err|/rms per head", errs)
+    assert max(errs) <= TOL_Q8
+    proj.close()
+
+
+def test_r3_q4_0_ubatch_parity():
+    cfg = synth.config("r3_q4_0")
+    w = synth.make_weights(cfg)
+    prep = ref.prepare(cfg, w)
+    x = synth.make_input(cfg, n_tokens=1024)
+    proj = kva.Projector(cfg, w, max_tokens=1024)
+    outs = proj.project(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    heads = [0, 3, 35]
+    want = ref.project(cfg, prep, x, which=heads)
+    errs = {cfg["heads"][i]["name"]: _err(outs[i].cpu().numpy(), want[i]) for i in heads}
+    print("r3 q4_0 max|err|/rms", errs, flush=True)
+    assert max(errs.values()) <= TOL_Q8
     proj.close()
 
 

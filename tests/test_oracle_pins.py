@@ -314,6 +314,41 @@ def test_q8_0_f16_weights_hand_blocks():
     assert (b[3, 0], b[3, 1], b[3, 2], b[3, 3]) == (0x7BFF, 0xFBFF, 0x7C00, 0x0000)
 
 
+def test_q4_0_dequant_hand_blocks_and_brute_force():
+    # block 0: scale 0.5, codes 0..15 then 15..0; block 1: smallest subnormal
+    # scale; block 2: scale -0.0; block 3: largest fp16 with codes 0 and 15
+    scales = np.array([0.5, 2.0 ** -24, -0.0, 65504.0], dtype=np.float16)
+    codes = np.zeros((4, 32), dtype=np.uint8)
+    codes[0, :16], codes[0, 16:] = np.arange(16), np.arange(15, -1, -1)
+    codes[1] = np.arange(32) % 16
+    codes[2] = 9
+    codes[3, ::2], codes[3, 1::2] = 0, 15
+    packed = synth.pack_q4_0(codes.reshape(1, 128), scales.reshape(1, 4))
+    assert packed.shape == (1, 4 * 18)
+    v = ref.dequant_q4_0(packed, 1, 128).reshape(4, 32)
+    assert np.array_equal(v[0], 0.5 * (codes[0].astype(np.float64) - 8))
+    assert np.array_equal(v[1], (np.arange(32) % 16 - 8) * 2.0 ** -24)
+    assert np.all(v[2] == 0.0)
+    assert np.array_equal(v[3], np.tile([-8 * 65504.0, 7 * 65504.0], 16))
+    # byte j of a block: input j in the low nibble, input j + 16 in the high one
+    rng = np.random.default_rng(12)
+    raw = rng.integers(0, 256, size=(3, 5 * 18), dtype=np.uint8)
+    raw.reshape(3, 5, 18)[:, :, 0:2] = np.array([0.25], dtype=np.float16).view(np.uint8)   # finite scales
+    v = ref.dequant_q4_0(raw, 3, 160)
+    for r in range(3):
+        for b in range(5):
+            blk = raw[r, b * 18:(b + 1) * 18]
+            d = float(blk[:2].view(np.float16)[0])
+            for j in range(32):
+                byte = int(blk[2 + (j % 16)])
+                n = (byte & 15) if j < 16 else (byte >> 4)
+                assert v[r, b * 32 + j] == d * (n - 8)
+    # the fp16 weights: exact products stay exact; d * 7 may round
+    b = ref.dequant_q4_0_f16_bits(packed, 1, 128).reshape(4, 32)
+    assert np.array_equal(ref.f16_bits_to_f64(b[0]), 0.5 * (codes[0].astype(np.float64) - 8))
+    assert b[3, 0] == 0xFC00 and b[3, 1] == 0x7C00        # -8 * 65504 and 7 * 65504 overflow
+
+
 def test_bf16_rounding_matches_torch_and_neighbours():
     rng = np.random.default_rng(5)
     x32 = (rng.standard_normal(20000) * np.exp2(rng.integers(-140, 100, 20000))).astype(np.float32)
