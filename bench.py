@@ -196,6 +196,66 @@ def time_kv_write(n_tokens: int = 65536, layers: int = 8, chunk: int = 8192, ste
             "launches": (n_tokens // chunk) * layers}
 
 
+def time_prompt_kv(prompt: int = 65536, chunk: int = 8192, steps: int = 3, warmup: int = 1):
+    """The r3 bf16 projector over a `prompt`-token prompt in `chunk`-token
+    calls, with the attention-layer state update (k_norm + RoPE + paged bf16
+    KV write for the 8 attention heads): chained (kva_project_ubatch, then
+    kva_attn_kv_write per attention head) and fused into the head GEMM
+    (kva_project_ubatch_kv).  Both fill the same pools with the same bits."""
+    import torch
+
+    import learned_kv_approximation_amd as kva
+
+    cfg = synth.config("r3_kv")
+    w = synth.make_weights(cfg)
+    x = synth.make_input(cfg, n_tokens=prompt)
+    proj = kva.Projector(cfg, w, max_tokens=chunk)
+    del w
+    xd = torch.from_numpy(x).cuda()
+    del x
+    attn = [i for i, h in enumerate(cfg["heads"]) if h["kind"] == "attn"]
+    gains, ptab, n_pages = synth.make_kv_write_inputs(prompt, n_layers=len(attn), seed=cfg["seed"])
+    g = torch.from_numpy(gains).cuda()
+    pt = torch.from_numpy(ptab).cuda()
+    pools = [(torch.empty((n_pages, 256, 4, 256), dtype=torch.int16, device="cuda"),
+              torch.empty((n_pages, 256, 4, 256), dtype=torch.int16, device="cuda")) for _ in attn]
+    caches = [kva.kva_paged_kv(kp.data_ptr(), vp.data_ptr(), pt.data_ptr(), 256, n_pages, len(ptab),
+                               4, 256, 64, 1.0e7, 1e-6) for kp, vp in pools]
+    dests = [kva.kva_attn_dest(g[li].data_ptr(), caches[li]) for li in range(len(attn))]
+    outs = proj.alloc_outputs(chunk)
+    st = kva.current_stream()
+    ptrs = [0 if i in attn else o.data_ptr() for i, o in enumerate(outs)]
+
+    def chained():
+        for c0 in range(0, prompt, chunk):
+            proj.project(xd[c0:c0 + chunk], outs)
+            for li, hi in enumerate(attn):
+                kva.kva_attn_kv_write(outs[hi].data_ptr(), 2048, chunk, c0, g[li].data_ptr(), caches[li], st)
+
+    def fused():
+        for c0 in range(0, prompt, chunk):
+            kva.kva_project_ubatch_kv(proj.ctx, xd[c0:].data_ptr(), chunk, ptrs, c0, dests, st)
+
+    res = {"tokens": prompt, "tokens_per_call": chunk, "attention_layers": len(attn)}
+    for name, fn in (("chained", chained), ("fused", fused)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        res[name] = {"ms_per_prompt": round(ms, 3), "tokens_per_s": round(prompt / (ms / 1e3), 1)}
+    res["fused_speedup"] = round(res["chained"]["ms_per_prompt"] / res["fused"]["ms_per_prompt"], 4)
+    proj.close()
+    del pools, outs, xd
+    torch.cuda.empty_cache()
+    return res
+
+
 def mfma_loop(n_iter: int = 4000, workgroups_per_cu: int = 4, reps: int = 10):
     """The MFMA rate the device sustains with no memory traffic (the library's
     kva_debug_mfma_loop): the achievable ceiling at the clock it runs at."""
@@ -361,7 +421,7 @@ def main():
 
     r2 = time_config("r2", args.steps, args.warmup)
     print(f"[bench] r2: {r2['tokens_per_s']:.0f} tok/s, {r2['pct_mfma_peak']:.1f}% peak", file=sys.stderr, flush=True)
-    r3 = r3b = q8 = q8p = q4 = kvw = sweep = mloop = None
+    r3 = r3b = q8 = q8p = q4 = kvw = kvp = sweep = mloop = None
     if not args.no_r3:
         r3 = time_config("r3", args.steps, args.warmup)
         print(f"[bench] r3: {r3['tokens_per_s']:.0f} tok/s, {r3['pct_mfma_peak']:.1f}% peak", file=sys.stderr,
@@ -377,6 +437,9 @@ def main():
             print(f"[bench] r3 q4_0: {q4['tokens_per_s']:.0f} tok/s", file=sys.stderr, flush=True)
             kvw = time_kv_write()
             print(f"[bench] kv write: {kvw['gb_s']} GB/s", file=sys.stderr, flush=True)
+            kvp = time_prompt_kv()
+            print(f"[bench] r3 65536 + KV: chained {kvp['chained']['tokens_per_s']:.0f} tok/s, "
+                  f"fused {kvp['fused']['tokens_per_s']:.0f} tok/s", file=sys.stderr, flush=True)
             sweep = q8_m_sweep()
             print("[bench] q8_0 M sweep: " + ", ".join(f"{m}: {v['weight_gb_s']} GB/s"
                                                         for m, v in sweep["by_tokens_per_call"].items()),
@@ -435,6 +498,8 @@ def main():
         out["r3_q4_0"] = brief(q4)
     if kvw is not None:
         out["kv_write_65536x8"] = kvw
+    if kvp is not None:
+        out["r3_prompt_65536_with_kv"] = kvp
     if sweep is not None:
         out["r3_q8_0_m_sweep"] = sweep
     if mloop is not None:

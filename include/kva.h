@@ -207,6 +207,34 @@ typedef struct {
 kva_status kva_attn_kv_write(const float* kv, int64_t ld_kv, int32_t n_tokens, int64_t pos0,
                              const float* k_gain, const kva_paged_kv* cache, void* stream);
 
+/* One full-attention head's destination for kva_project_ubatch_kv. */
+typedef struct {
+    const float* k_gain;    /* device fp32 [head_dim], that layer's k_norm gain */
+    kva_paged_kv cache;     /* that layer's pools and page table                */
+} kva_attn_dest;
+
+/* kva_project_ubatch with the attention-layer state update fused into the
+ * head GEMM ("Qwen3.8-27B-KVA" card, "What the hell?": k_norm + RoPE + KV
+ * cache writes follow the projection).  Every head of kind KVA_HEAD_ATTN
+ * whose out_dim is 2 * 4 * 256 (k | v of 4 KV heads of 256 dims) is not
+ * written as fp32: its k and v go through exactly the arithmetic of
+ * kva_attn_kv_write, token t at position pos0 + t, into attn[a] (a = rank
+ * of that head among such heads, in head order).  The pools then hold the
+ * same bits as kva_project_ubatch followed by one kva_attn_kv_write per
+ * such head (kv = that head's output, ld_kv = 2048), without the fp32 k|v
+ * round trip through memory.
+ *   head_out  as for kva_project_ubatch; entries of the fused heads are
+ *             ignored and may be NULL
+ *   attn      host array of n_attn destinations (device pools, gains and
+ *             page tables); n_attn must equal the number of such heads
+ *             (KVA_ERR_SHAPE), at most 16; every cache must satisfy the
+ *             checks of kva_attn_kv_write and all must share n_rot,
+ *             rope_base and eps (KVA_ERR_UNSUPPORTED)
+ * Pools must not alias x, each other or the outputs.  Asynchronous. */
+kva_status kva_project_ubatch_kv(kva_ctx* ctx, const float* x, int32_t n_tokens,
+                                 float* const* head_out, int64_t pos0,
+                                 const kva_attn_dest* attn, int32_t n_attn, void* stream);
+
 /* Test hook: dequantises n_blocks q8_0 blocks (device, 34 bytes each: fp16
  * scale d, then 32 int8 codes q; format from [KVA] "Projector quantization and
  * flash-attn") to fp32 (device, 32*n_blocks values): out = float(d) * q,
@@ -245,9 +273,10 @@ kva_status kva_debug_copy_z(kva_ctx* ctx, uint16_t* dst, int32_t n_tokens, void*
 
 /* Test hook (host only, no device): the packed column order of the head
  * GEMM for `cfg`.  Head outputs are packed into 256-column tiles: first the
- * out_dim / 256 full tiles of every head in head order, then one tail
- * segment gathering every head's last out_dim % 256 columns (padded to a
- * multiple of 256).  For packed column c, col_head[c] is the head (-1 for
+ * 8 tiles of every full-attention head with out_dim 2048 (the heads
+ * kva_project_ubatch_kv fuses), then the out_dim / 256 full tiles of every
+ * other head, each group in head order, then one tail segment gathering
+ * every head's last out_dim % 256 columns (padded to a multiple of 256).  For packed column c, col_head[c] is the head (-1 for
  * padding) and col_index[c] the column inside that head.  *n_cols receives the
  * packed width; nothing is written past `capacity` entries (KVA_ERR_SHAPE if
  * capacity is too small). */

@@ -67,6 +67,10 @@ class kva_paged_kv(ctypes.Structure):
                 ("n_rot", c_i32), ("rope_base", c_f64), ("eps", c_f32)]
 
 
+class kva_attn_dest(ctypes.Structure):
+    _fields_ = [("k_gain", c_vp), ("cache", kva_paged_kv)]
+
+
 class KvaError(RuntimeError):
     def __init__(self, status: int, where: str = ""):
         self.status = status
@@ -81,6 +85,8 @@ _SIGS = {
     "kva_validate_config": (c_i32, [ctypes.POINTER(kva_config)]),
     "kva_create": (c_i32, [ctypes.POINTER(kva_config), ctypes.POINTER(kva_weights), c_i32, ctypes.POINTER(c_vp)]),
     "kva_project_ubatch": (c_i32, [c_vp, c_vp, c_i32, ctypes.POINTER(c_vp), c_vp]),
+    "kva_project_ubatch_kv": (c_i32, [c_vp, c_vp, c_i32, ctypes.POINTER(c_vp), c_i64,
+                                      ctypes.POINTER(kva_attn_dest), c_i32, c_vp]),
     "kva_destroy": (c_i32, [c_vp]),
     "kva_attn_kv_write": (c_i32, [c_vp, c_i64, c_i32, c_i64, c_vp, ctypes.POINTER(kva_paged_kv), c_vp]),
     "kva_debug_dequant_q8_0": (c_i32, [c_vp, c_i64, c_vp, c_vp]),
@@ -139,6 +145,15 @@ def kva_create(cfg: kva_config, weights: kva_weights, device: int = 0) -> int:
 def kva_project_ubatch(ctx: int, x_ptr: int, n_tokens: int, head_out_ptrs, stream: int = 0) -> None:
     arr = (c_vp * len(head_out_ptrs))(*head_out_ptrs)
     _check(lib().kva_project_ubatch(ctx, x_ptr, n_tokens, arr, stream), "kva_project_ubatch")
+
+
+def kva_project_ubatch_kv(ctx: int, x_ptr: int, n_tokens: int, head_out_ptrs, pos0: int, dests,
+                          stream: int = 0) -> None:
+    """dests: sequence of kva_attn_dest, one per fused attention head (head order)."""
+    arr = (c_vp * len(head_out_ptrs))(*head_out_ptrs)
+    d = (kva_attn_dest * max(1, len(dests)))(*dests)
+    _check(lib().kva_project_ubatch_kv(ctx, x_ptr, n_tokens, arr, pos0, d, len(dests), stream),
+           "kva_project_ubatch_kv")
 
 
 def kva_destroy(ctx: int) -> None:

@@ -17,6 +17,7 @@
 // workgroups to the 8 XCDs round-robin.  Accumulation is fp32, over K in
 // plain sequential order.
 #include "kva_internal.h"
+#include "kva_kv.h"
 
 #include <type_traits>
 
@@ -54,9 +55,9 @@ typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 //
 // Fused epilogue of a BM x BN tile held as 32x32 MFMA accumulators by a
 // WGM x WGN grid of waves (acc[i][j]: the wave's i-th 32-row, j-th 32-column
-// block).  `smem` (at least 128 KB, free when called) is used by the head
+// block).  `smem` (SMEM_BYTES, free when called) is used by the head
 // epilogue to turn whole-head tiles into full-row stores.
-template <int BM, int BN, int WGM, int WGN, int EPI, int MI, int NI>
+template <int BM, int BN, int WGM, int WGN, int EPI, int MI, int NI, int SMEM_BYTES>
 __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[MI][NI], int tm, int tn, int split,
                                          uint16_t* smem) {
     constexpr int NW = WGM * WGN;
@@ -133,49 +134,75 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[MI][NI
         static_assert(kHeadTileN % BN == 0, "a GEMM tile lies inside one packed 256-column tile");
         const int t256 = tn * BN / kHeadTileN;          // packed tile holding this GEMM tile
         const int th = e.tile_head[t256];
-        // A whole-head tile whose destination rows are 16-byte aligned goes out
-        // through LDS: each half of the tile (128 x 256 fp32 = the 128 KB of
-        // LDS) is transposed there and written as full 1 KB rows with 16-byte
-        // stores (a quarter of the store instructions of the direct path).
-        if constexpr (BM == 256 && WGM == 2 && WGN == 4) {
-            if (th >= 0 && (e.heads.ld[th] % 4) == 0 && ((uintptr_t)e.heads.ptr[th] % 16) == 0) {
-                float* lds = reinterpret_cast<float*>(smem);       // [128][256], rows rotated by 32 every 4 rows
-                float* dst0 = e.heads.ptr[th] + e.tile_col0[t256];
-                const int64_t ld = e.heads.ld[th];
+        // A whole-head tile goes out through LDS when it feeds the fused KV
+        // epilogue (k_norm needs a token's 256 columns in one wave), and for
+        // plain outputs of a 256-row tile whose destination rows are 16-byte
+        // aligned: CR rows x 256 fp32 at a time are transposed there and
+        // leave as full 1 KB rows, one row per wave and 4 columns per lane
+        // (a quarter of the store instructions of the direct path).
+        if constexpr (BN == kHeadTileN && WGN == 4) {
+            const int slot = (th >= 0 && e.kv_n > 0) ? e.kv_slot[th] : -1;
+            const bool plain = BM == 256 && WGM == 2 && th >= 0 && (e.heads.ld[th] % 4) == 0 &&
+                               ((uintptr_t)e.heads.ptr[th] % 16) == 0;
+            if (slot >= 0 || plain) {
+                constexpr int CR0 = (SMEM_BYTES / (BN * 4)) / 32 * 32;
+                constexpr int CR = CR0 < WM ? CR0 : WM;       // rows staged at a time
+                static_assert(CR >= 32 && WM % CR == 0 && CR % NW == 0, "epilogue staging");
+                float* lds = reinterpret_cast<float*>(smem);   // [CR][256], rows rotated by 32 every 4 rows
                 const float* bias = e.bias ? e.bias + tn * BN : nullptr;
+                const int part = e.tile_col0[t256] / kKvHeadDim;   // KV tile: 0..3 k, 4..7 v of that KV head
+                const bool is_k = part < kKvHeads;
+                const int kvh = is_k ? part : part - kKvHeads;
+                const KvPool* pool = slot >= 0 ? &e.kv_pool[slot] : nullptr;
+                float* dst0 = slot >= 0 ? nullptr : e.heads.ptr[th] + e.tile_col0[t256];
+                const int64_t ld = slot >= 0 ? 0 : e.heads.ld[th];
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    if (wm == half) {
+                for (int half = 0; half < WGM; ++half) {
 #pragma unroll
-                        for (int j = 0; j < NI; ++j)
+                    for (int c = 0; c < WM / CR; ++c) {
+                        if (wm == half) {
 #pragma unroll
-                            for (int i = 0; i < MI; ++i)
+                            for (int j = 0; j < NI; ++j)
 #pragma unroll
-                                for (int r = 0; r < 16; ++r) {
-                                    const int lr = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                                    const int lc = wn * WN + j * 32 + (lane & 31);
-                                    lds[lr * BN + ((lc + 32 * ((lr >> 2) & 1)) & (BN - 1))] = acc[i][j][r];
-                                }
-                    }
-                    __syncthreads();
-                    // 128 rows x 64 chunks of 4 columns; one wave stores one full row
+                                for (int ii = 0; ii < CR / 32; ++ii)
 #pragma unroll
-                    for (int q = 0; q < (128 * 64) / (64 * NW); ++q) {
-                        const int id = q * 64 * NW + tid;
-                        const int lr = id >> 6, c4 = (id & 63) * 4;
-                        const int row = tm * BM + half * 128 + lr;
-                        float4 v = *(const float4*)(lds + lr * BN + ((c4 + 32 * ((lr >> 2) & 1)) & (BN - 1)));
-                        if (bias) {
-                            const float4 b = *(const float4*)(bias + c4);
-                            v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
+                                    for (int r = 0; r < 16; ++r) {
+                                        const int lr = ii * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                                        const int lc = wn * WN + j * 32 + (lane & 31);
+                                        lds[lr * BN + ((lc + 32 * ((lr >> 2) & 1)) & (BN - 1))] =
+                                            acc[c * (CR / 32) + ii][j][r];
+                                    }
                         }
-                        if (row < g.M) *(float4*)(dst0 + (int64_t)row * ld + c4) = v;
+                        __syncthreads();
+                        // CR rows x 64 chunks of 4 columns; one wave takes one full row
+#pragma unroll
+                        for (int q = 0; q < CR / NW; ++q) {
+                            const int lr = q * NW + wave, c4 = lane * 4;
+                            const int row = tm * BM + half * WM + c * CR + lr;
+                            float4 v = *(const float4*)(lds + lr * BN + ((c4 + 32 * ((lr >> 2) & 1)) & (BN - 1)));
+                            if (bias) {
+                                const float4 b = *(const float4*)(bias + c4);
+                                v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
+                            }
+                            if (row >= g.M) continue;           // uniform over the wave
+                            if (slot < 0) {
+                                *(float4*)(dst0 + (int64_t)row * ld + c4) = v;
+                                continue;
+                            }
+                            const int64_t p = e.kv_pos0 + row;
+                            const int64_t off = kv_slot_offset(*pool, p, kvh, lane);
+                            if (is_k) v = kv_k_norm_rope(v, lane, p, pool->k_gain, e.kv_rope);
+                            if (off >= 0) kv_store_bf16((is_k ? pool->k_pool : pool->v_pool) + off, v);
+                        }
+                        __syncthreads();
                     }
-                    __syncthreads();
                 }
                 return;
             }
         }
+        // a KV head's tiles leave only through the staged path above (the
+        // launch keeps them 256 columns wide); never store them as fp32
+        if (th >= 0 && e.kv_n > 0 && e.kv_slot[th] >= 0) return;
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
             const int col = col_base + j * 32;
@@ -240,9 +267,10 @@ struct T32Shape {
     static constexpr int B_BYTES = BN * B_ROW;
     static constexpr int S_BYTES = QW ? BN * 2 : 0;                 // fp16 block scales
     static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
-    // the head epilogue of a 256-row tile stages 128 KB through LDS
-    static constexpr bool LDS_EPI = EPI == EPI_HEADS && BM == 256;
-    static constexpr int S = LDS_EPI ? (128 * 1024 + STAGE - 1) / STAGE : 4;
+    // the head epilogue stages whole 256-column tiles through LDS (128 KB at
+    // a time for a 256-row tile)
+    static constexpr bool LDS_EPI = EPI == EPI_HEADS && BN == kHeadTileN;
+    static constexpr int S = (LDS_EPI && BM == 256) ? (128 * 1024 + STAGE - 1) / STAGE : 4;
     static constexpr int BYTES = S * STAGE;
 };
 
@@ -279,7 +307,7 @@ __device__ __forceinline__ void t32_tile(const GemmArgs& g, int tm, int tn, int 
                   "tile too small for the wave grid");
     static_assert(!QW || (SL >= 1 && SL <= 64 && SL * 4 * NW == Sh::S_BYTES), "scale DMA split");
     static_assert((S - 2) * L < 64, "vmcnt range");
-    static_assert(!Sh::LDS_EPI || Sh::BYTES >= 128 * 1024, "the head epilogue stages 128 KB through LDS");
+    static_assert(!Sh::LDS_EPI || BM != 256 || Sh::BYTES >= 128 * 1024, "the head epilogue stages 128 KB through LDS");
     static_assert(kWeightTileRows % BM == 0 && kWeightTileRows % BN == 0, "tiles inside 256-row groups");
     const int SP = g.splits;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -453,7 +481,7 @@ __device__ __forceinline__ void t32_tile(const GemmArgs& g, int tm, int tn, int 
     for (; kt + S - 1 < nk; ++kt) slab(kt, std::true_type{});
     for (; kt < nk; ++kt) slab(kt, std::false_type{});
     if constexpr (Sh::LDS_EPI) __syncthreads();    // the head epilogue reuses LDS
-    epilogue<BM, BN, WGM, WGN, EPI, MI, NI>(g, acc, tm, tn, split, reinterpret_cast<uint16_t*>(smem));
+    epilogue<BM, BN, WGM, WGN, EPI, MI, NI, Sh::BYTES>(g, acc, tm, tn, split, reinterpret_cast<uint16_t*>(smem));
 }
 
 // Workgroup ids are dealt to the 8 XCDs round-robin; this remaps them so that
@@ -517,10 +545,11 @@ hipError_t launch_t32(const GemmArgs& a, hipStream_t s) {
 
 // The instantiated (operand, tile, epilogue) combinations.
 
-hipError_t launch_gemm_heads(GemmOperand opd, const GemmArgs& a, int n_cu, hipStream_t s) {
+hipError_t launch_gemm_heads(GemmOperand opd, const GemmArgs& a, int n_cu, int min_big, hipStream_t s) {
     if (a.M <= 0) return hipSuccess;
     if (a.K % 32 != 0 || a.K <= 0 || a.N % 256 || a.splits != 1) return hipErrorInvalidValue;
     if ((opd == OPD_Q8 || opd == OPD_Q4) ? (!a.Bq || !a.Bs) : !a.B) return hipErrorInvalidValue;
+    if (a.epi.kv_n > 0 && min_big * 256 > a.N) return hipErrorInvalidValue;
     if (opd != OPD_BF16 && opd != OPD_Q8 && opd != OPD_Q4) return hipErrorNotSupported;
     // Few rows: one M-tile of 64 or 128 rows, so that every weight strip is
     // read once by a workgroup whose MFMA work matches the real rows (with
@@ -540,6 +569,7 @@ hipError_t launch_gemm_heads(GemmOperand opd, const GemmArgs& a, int n_cu, hipSt
     // when that shortens the last round
     int n_big = nt;
     if (n_cu > 0 && total > n_cu && total % n_cu != 0) n_big = (total / n_cu) * n_cu / mt;
+    if (n_big < min_big) n_big = min_big < nt ? min_big : nt;
     const int grid_big = (mt * n_big + 7) / 8 * 8;
     const int sbn = opd == OPD_Q8 ? kTailBN<OPD_Q8> : opd == OPD_Q4 ? kTailBN<OPD_Q4> : kTailBN<OPD_BF16>;
     const int n_small = ((a.M + 127) / 128) * ((a.N - 256 * n_big) / sbn);

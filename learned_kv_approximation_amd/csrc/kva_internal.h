@@ -76,6 +76,28 @@ __host__ __device__ inline uint32_t q4_chunk_pack(const uint8_t n[8]) {
     return w;
 }
 
+// Attention-layer KV cache (4 KV heads of 256 dims per token).
+constexpr int kKvHeads = 4;
+constexpr int kKvHeadDim = 256;
+constexpr int kMaxAttnHeads = 16;
+
+// One attention layer's paged pools [n_pages][page_size][kKvHeads][kKvHeadDim]
+// bf16, its page table and its k_norm gain [kKvHeadDim].
+struct KvPool {
+    uint16_t* k_pool;
+    uint16_t* v_pool;
+    const int32_t* page_table;
+    const float* k_gain;
+    int32_t page_size;
+    int32_t n_pages;
+};
+
+struct KvRope {
+    int32_t n_rot;          // rotary dims at the start of each KV head (multiple of 8, <= 64)
+    float eps;              // k_norm epsilon
+    double inv_freq[32];    // rope_base^(-2j/n_rot), computed on the host in double
+};
+
 struct HeadOut {
     float* ptr[kMaxHeads];
     int32_t ld[kMaxHeads];
@@ -104,6 +126,15 @@ struct EpiArgs {
     int32_t tail_start = 0;             // first packed column of the tail segment
     const float* bias = nullptr;        // [n_pad] packed bias, or nullptr
     HeadOut heads;
+    // Fused attention-layer epilogue (EPI_HEADS): a head with kv_slot[h] >= 0
+    // is not written as fp32; its packed tiles (256 columns = one KV head of
+    // k, tiles 0..3, or of v, tiles 4..7) go through k_norm + RoPE (k) and
+    // bf16 rounding into kv_pool[kv_slot[h]], token m at position kv_pos0 + m.
+    int32_t kv_n = 0;                   // 0: no fused epilogue
+    int64_t kv_pos0 = 0;
+    int8_t kv_slot[kMaxHeads];
+    KvPool kv_pool[kMaxAttnHeads];
+    KvRope kv_rope;
 };
 
 // C[M][N] = A[M][K] * B[N][K]^T with 16-bit activations (tiled32 layout)
@@ -190,8 +221,10 @@ hipError_t launch_gemm_t32(GemmOperand opd, GemmTile tile, EpiKind epi, const Ge
 
 // The head GEMM (EPI_HEADS, no split): 256x256 tiles over a whole number of
 // rounds of n_cu workgroups, the remaining columns in smaller tiles (128 rows);
-// calls of at most 128 rows use one M-tile of 64 or 128 rows.
-hipError_t launch_gemm_heads(GemmOperand opd, const GemmArgs& args, int n_cu, hipStream_t stream);
+// calls of at most 128 rows use one M-tile of 64 or 128 rows.  The first
+// min_big 256-column tiles always run 256 columns wide (the fused KV epilogue
+// needs a KV head's 256 columns in one workgroup).
+hipError_t launch_gemm_heads(GemmOperand opd, const GemmArgs& args, int n_cu, int min_big, hipStream_t stream);
 
 // Folds split-K partials into the residual stream and normalises it:
 //   h[r][c] = (add ? h[r][c] : 0) + P_0[r][c] + P_1[r][c] + ... (this order),
@@ -219,21 +252,12 @@ hipError_t launch_attention(const uint16_t* qk, int64_t ld_qk, int32_t k_off, co
                             int32_t n_heads, int32_t attn_block, hipStream_t stream);
 
 struct KvWriteArgs {
-    const float* kv;
+    const float* kv;        // row t: k of the 4 KV heads, then v
     int64_t ld_kv;
     int32_t n_tokens;
     int64_t pos0;
-    const float* k_gain;
-    uint16_t* k_pool;
-    uint16_t* v_pool;
-    const int32_t* page_table;
-    int32_t page_size;
-    int32_t n_pages;
-    int32_t n_kv_heads;
-    int32_t head_dim;
-    int32_t n_rot;
-    float eps;
-    double inv_freq[64];   // rope_base^(-2j/n_rot), computed on the host in double
+    KvPool pool;
+    KvRope rope;
 };
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
 

@@ -2,6 +2,7 @@
 // MFMA GEMM), the attention-layer KV-cache write (k_norm + partial RoPE +
 // paged bf16 store) and the q8_0 dequantisation test hook.
 #include "kva_internal.h"
+#include "kva_kv.h"
 
 namespace kva {
 namespace {
@@ -102,59 +103,21 @@ __global__ void __launch_bounds__(256) untile32_kernel(const uint16_t* __restric
         *(ushort4*)(dst + (int64_t)row * cols + c) = *(const ushort4*)(src + tiled32_index(row, c, cols));
 }
 
-// KV-cache write for one full-attention layer ("Qwen3.8-27B-KVA" card, "What
-// the hell?": after projection the engine applies k_norm and RoPE and writes
-// the KV cache; geometry from the "Qwen3.8-27B-MLA" card, "What this is":
-// 4 KV heads of 256 dims with 64 rotary dims each).  One wave per (token, KV
-// head): lane l holds dims 4l..4l+3 of k and of v.  The rotary pair
-// (j, j + n_rot/2) of lane l < n_rot/8 lives in lane l + n_rot/8.
-// The angle p * inv_freq[j] is formed and reduced modulo 2 pi in double
-// (p reaches 65535 and more: an fp32 product would be off by several 1e-3 rad).
+// KV-cache write for one full-attention layer (the routines and their
+// sources are in kva_kv.h).  One wave per (token, KV head): lane l holds dims
+// 4l..4l+3 of k and of v.
 __global__ void __launch_bounds__(256) kv_write_kernel(KvWriteArgs a) {
     const int lane = threadIdx.x & 63;
-    const int kvh = threadIdx.x >> 6;           // 4 waves = 4 KV heads (head_dim 256)
+    const int kvh = threadIdx.x >> 6;           // 4 waves = 4 KV heads
     const int t = blockIdx.x;
     const int64_t p = a.pos0 + t;
-    const int pg = a.page_table[p / a.page_size];
-    if (pg < 0 || pg >= a.n_pages) return;
-    const int slot = (int)(p % a.page_size);
-    const float* kr = a.kv + (int64_t)t * a.ld_kv + kvh * a.head_dim;
-    const float* vr = kr + a.n_kv_heads * a.head_dim;
-    const int d0 = lane * 4;
-
-    float4 k = *(const float4*)(kr + d0);
-    const float4 v = *(const float4*)(vr + d0);
-    const float ss = wave_sum(k.x * k.x + k.y * k.y + k.z * k.z + k.w * k.w);
-    const float r = 1.0f / sqrtf(ss / (float)a.head_dim + a.eps);
-    const float4 gg = *(const float4*)(a.k_gain + d0);
-    k.x *= r * gg.x; k.y *= r * gg.y; k.z *= r * gg.z; k.w *= r * gg.w;
-
-    const int half_lanes = a.n_rot / 8;         // lanes holding the first half of the rotary dims
-    const float4 other = make_float4(__shfl_xor(k.x, half_lanes), __shfl_xor(k.y, half_lanes),
-                                     __shfl_xor(k.z, half_lanes), __shfl_xor(k.w, half_lanes));
-    if (lane < 2 * half_lanes) {
-        const bool first = lane < half_lanes;
-        const int j0 = (first ? lane : lane - half_lanes) * 4;
-        float kk[4] = {k.x, k.y, k.z, k.w};
-        const float oo[4] = {other.x, other.y, other.z, other.w};
-        const double two_pi = 6.283185307179586476925286766559;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            double th = (double)p * a.inv_freq[j0 + e];
-            th -= two_pi * floor(th / two_pi);
-            float sn, cs;
-            sincosf((float)th, &sn, &cs);
-            // first half: x' = x cos - y sin ; second half: y' = x sin + y cos
-            kk[e] = first ? (kk[e] * cs - oo[e] * sn) : (oo[e] * sn + kk[e] * cs);
-        }
-        k = make_float4(kk[0], kk[1], kk[2], kk[3]);
-    }
-    const int64_t base = (((int64_t)pg * a.page_size + slot) * a.n_kv_heads + kvh) * a.head_dim + d0;
-    ushort4 ko, vo;
-    ko.x = to_bits(k.x, true); ko.y = to_bits(k.y, true); ko.z = to_bits(k.z, true); ko.w = to_bits(k.w, true);
-    vo.x = to_bits(v.x, true); vo.y = to_bits(v.y, true); vo.z = to_bits(v.z, true); vo.w = to_bits(v.w, true);
-    *(ushort4*)(a.k_pool + base) = ko;
-    *(ushort4*)(a.v_pool + base) = vo;
+    const int64_t off = kv_slot_offset(a.pool, p, kvh, lane);
+    if (off < 0) return;
+    const float* kr = a.kv + (int64_t)t * a.ld_kv + kvh * kKvHeadDim;
+    const float* vr = kr + kKvHeads * kKvHeadDim;
+    const float4 k = kv_k_norm_rope(*(const float4*)(kr + lane * 4), lane, p, a.pool.k_gain, a.rope);
+    kv_store_bf16(a.pool.k_pool + off, k);
+    kv_store_bf16(a.pool.v_pool + off, *(const float4*)(vr + lane * 4));
 }
 
 __global__ void dequant_q8_0_kernel(const uint8_t* __restrict__ blocks, int64_t n_blocks,
@@ -288,8 +251,7 @@ hipError_t launch_untile32(const uint16_t* src, uint16_t* dst, int32_t rows, int
 
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t s) {
     if (a.n_tokens <= 0) return hipSuccess;
-    if (a.head_dim != 256 || a.n_kv_heads != 4 || a.n_rot % 8 || a.n_rot > 64 || a.n_rot <= 0)
-        return hipErrorInvalidValue;
+    if (a.rope.n_rot % 8 || a.rope.n_rot > 64 || a.rope.n_rot <= 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL(kv_write_kernel, dim3(a.n_tokens), dim3(256), 0, s, a);
     return hipGetLastError();
 }

@@ -104,14 +104,33 @@ float load_f32(const void* src, int dtype, int64_t i) {
 struct HeadPlan {
     int64_t n_pad = 0;
     int32_t tail_start = 0;
+    int32_t kv_tiles = 0;                        // leading tiles that belong to KV heads
+    std::vector<int32_t> kv_heads;               // KV heads in head order
     std::vector<int32_t> tile_head, tile_col0;   // per kHeadTileN tile
     std::vector<int32_t> tail_head, tail_col;    // per tail column
     std::vector<int32_t> col_head, col_index;    // per packed column
 };
 
+// A full-attention head whose output is k | v of kKvHeads heads of kKvHeadDim:
+// the fused KV epilogue can take it.
+bool is_kv_head(const kva_head_desc& h) {
+    return h.kind == KVA_HEAD_ATTN && h.out_dim == 2 * kKvHeads * kKvHeadDim;
+}
+
 HeadPlan plan_heads(const kva_config& c) {
     HeadPlan p;
+    // KV heads first, so their tiles always run as whole 256-column tiles
     for (int i = 0; i < c.n_out_heads; ++i) {
+        if (!is_kv_head(c.out_heads[i])) continue;
+        p.kv_heads.push_back(i);
+        for (int t = 0; t < c.out_heads[i].out_dim / kHeadTileN; ++t) {
+            p.tile_head.push_back(i);
+            p.tile_col0.push_back(t * kHeadTileN);
+        }
+    }
+    p.kv_tiles = (int32_t)p.tile_head.size();
+    for (int i = 0; i < c.n_out_heads; ++i) {
+        if (is_kv_head(c.out_heads[i])) continue;
         const int full = c.out_heads[i].out_dim / kHeadTileN;
         for (int t = 0; t < full; ++t) {
             p.tile_head.push_back(i);
@@ -195,6 +214,8 @@ struct kva_ctx {
     int32_t* tail_col = nullptr;
     int64_t n_pad_heads = 0;
     int32_t tail_start = 0;
+    int32_t kv_tiles = 0;             // leading packed tiles of the KV heads
+    std::vector<int32_t> kv_heads;    // heads the fused KV epilogue takes, in head order
 
     // scratch (device), rows padded to kRowPad
     int64_t m_alloc = 0;
@@ -477,6 +498,8 @@ kva_status create_impl(const kva_config* cfg, const kva_weights* w, int device, 
     HeadPlan plan = plan_heads(c);
     ctx->n_pad_heads = plan.n_pad;
     ctx->tail_start = plan.tail_start;
+    ctx->kv_tiles = plan.kv_tiles;
+    ctx->kv_heads = plan.kv_heads;
     {
         std::vector<RowSrc> rows((size_t)plan.n_pad);
         std::vector<float> bias((size_t)plan.n_pad, 0.0f);
@@ -609,16 +632,54 @@ kva_status kva_create(const kva_config* cfg, const kva_weights* w, int device, k
     return KVA_OK;
 }
 
-kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n, float* const* head_out,
-                              void* stream) {
+namespace {
+
+kva_status check_paged_kv(const kva_paged_kv* cache, const float* k_gain) {
+    if (!k_gain || !cache || !cache->k_pool || !cache->v_pool || !cache->page_table)
+        return fail(KVA_ERR_ARG, "NULL argument");
+    if (cache->n_kv_heads != kKvHeads || cache->head_dim != kKvHeadDim)
+        return fail(KVA_ERR_UNSUPPORTED, "only 4 KV heads of 256 dims are supported");
+    if (cache->n_rot <= 0 || cache->n_rot > 64 || cache->n_rot % 8)
+        return fail(KVA_ERR_SHAPE, "n_rot must be a multiple of 8 in [8, 64]");
+    if (cache->page_size <= 0 || cache->n_pages <= 0 || cache->n_logical <= 0)
+        return fail(KVA_ERR_SHAPE, "page_size, n_pages and n_logical must be positive");
+    if (!(cache->rope_base > 1.0) || !std::isfinite(cache->rope_base))
+        return fail(KVA_ERR_ARG, "rope_base must be > 1");
+    return KVA_OK;
+}
+
+KvPool make_pool(const kva_paged_kv* cache, const float* k_gain) {
+    KvPool p{};
+    p.k_pool = cache->k_pool; p.v_pool = cache->v_pool; p.page_table = cache->page_table;
+    p.k_gain = k_gain; p.page_size = cache->page_size; p.n_pages = cache->n_pages;
+    return p;
+}
+
+KvRope make_rope(const kva_paged_kv* cache) {
+    KvRope r{};
+    r.n_rot = cache->n_rot; r.eps = cache->eps;
+    for (int j = 0; j < cache->n_rot / 2; ++j)
+        r.inv_freq[j] = std::pow(cache->rope_base, -2.0 * j / (double)cache->n_rot);
+    return r;
+}
+
+}  // namespace
+
+namespace {
+
+// The projection; with `kv` set, the KV heads' tiles leave through the fused
+// KV epilogue instead of as fp32 outputs.
+kva_status project(kva_ctx* ctx, const float* x, int32_t n, float* const* head_out, const EpiArgs* kv,
+                   void* stream) {
     if (!ctx || !x || !head_out) return fail(KVA_ERR_ARG, "NULL argument");
     const kva_config& c = ctx->cfg;
     if (n < 1 || n > c.max_tokens)
         return fail(KVA_ERR_SHAPE, "n_tokens %d outside [1, %d]", n, c.max_tokens);
     HeadOut ho{};
     for (int i = 0; i < c.n_out_heads; ++i) {
-        if (!head_out[i]) return fail(KVA_ERR_ARG, "head_out[%d] is NULL", i);
-        ho.ptr[i] = head_out[i];
+        const bool fused = kv && kv->kv_slot[i] >= 0;
+        if (!head_out[i] && !fused) return fail(KVA_ERR_ARG, "head_out[%d] is NULL", i);
+        ho.ptr[i] = fused ? nullptr : head_out[i];
         ho.ld[i] = c.out_heads[i].out_dim;
     }
     HIP_TRY(hipSetDevice(ctx->device));
@@ -688,12 +749,54 @@ kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n, float* co
         g.epi.tail_head = ctx->tail_head; g.epi.tail_col = ctx->tail_col;
         g.epi.tail_start = ctx->tail_start; g.epi.bias = ctx->b_heads;
         g.epi.heads = ho;
-        STAGE(KVA_STAGE_GEMM_HEADS, launch_gemm_heads(ctx->q8 ? opd : OPD_BF16, g, ctx->n_cu, s));
+        if (kv) {
+            g.epi.kv_n = kv->kv_n;
+            g.epi.kv_pos0 = kv->kv_pos0;
+            std::memcpy(g.epi.kv_slot, kv->kv_slot, sizeof(g.epi.kv_slot));
+            std::memcpy(g.epi.kv_pool, kv->kv_pool, sizeof(g.epi.kv_pool));
+            g.epi.kv_rope = kv->kv_rope;
+        }
+        STAGE(KVA_STAGE_GEMM_HEADS, launch_gemm_heads(ctx->q8 ? opd : OPD_BF16, g, ctx->n_cu,
+                                                      kv ? ctx->kv_tiles : 0, s));
     }
     ctx->stats.calls += 1;
     ctx->stats.tokens += (uint64_t)n;
     ctx->stats.blocks += (uint64_t)((n + c.attn_block - 1) / c.attn_block);
     return KVA_OK;
+}
+
+}  // namespace
+
+kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n, float* const* head_out,
+                              void* stream) {
+    return project(ctx, x, n, head_out, nullptr, stream);
+}
+
+kva_status kva_project_ubatch_kv(kva_ctx* ctx, const float* x, int32_t n, float* const* head_out,
+                                 int64_t pos0, const kva_attn_dest* attn, int32_t n_attn, void* stream) {
+    if (!ctx || !attn) return fail(KVA_ERR_ARG, "NULL argument");
+    if (n_attn != (int32_t)ctx->kv_heads.size())
+        return fail(KVA_ERR_SHAPE, "n_attn %d, but the projector has %d attention heads of k|v 4 x 256",
+                    n_attn, (int)ctx->kv_heads.size());
+    if (n_attn > kMaxAttnHeads) return fail(KVA_ERR_UNSUPPORTED, "more than %d attention heads", kMaxAttnHeads);
+    if (pos0 < 0) return fail(KVA_ERR_SHAPE, "negative pos0");
+    EpiArgs kv{};
+    kv.kv_n = n_attn;
+    kv.kv_pos0 = pos0;
+    std::memset(kv.kv_slot, -1, sizeof(kv.kv_slot));
+    for (int a = 0; a < n_attn; ++a) {
+        const kva_paged_kv* cache = &attn[a].cache;
+        KVA_TRY(check_paged_kv(cache, attn[a].k_gain));
+        if (pos0 + n > (int64_t)cache->n_logical * cache->page_size)
+            return fail(KVA_ERR_SHAPE, "attention head %d: positions past the page table", a);
+        if (cache->n_rot != attn[0].cache.n_rot || cache->rope_base != attn[0].cache.rope_base ||
+            cache->eps != attn[0].cache.eps)
+            return fail(KVA_ERR_UNSUPPORTED, "attention heads must share n_rot, rope_base and eps");
+        kv.kv_slot[ctx->kv_heads[a]] = (int8_t)a;
+        kv.kv_pool[a] = make_pool(cache, attn[a].k_gain);
+    }
+    if (n_attn > 0) kv.kv_rope = make_rope(&attn[0].cache);
+    return project(ctx, x, n, head_out, n_attn > 0 ? &kv : nullptr, stream);
 }
 
 kva_status kva_destroy(kva_ctx* ctx) {
@@ -707,29 +810,18 @@ kva_status kva_destroy(kva_ctx* ctx) {
 
 kva_status kva_attn_kv_write(const float* kv, int64_t ld_kv, int32_t n, int64_t pos0,
                              const float* k_gain, const kva_paged_kv* cache, void* stream) {
-    if (!kv || !k_gain || !cache || !cache->k_pool || !cache->v_pool || !cache->page_table)
-        return fail(KVA_ERR_ARG, "NULL argument");
+    if (!kv) return fail(KVA_ERR_ARG, "NULL argument");
+    KVA_TRY(check_paged_kv(cache, k_gain));
     if (n < 0 || pos0 < 0) return fail(KVA_ERR_SHAPE, "negative n_tokens or pos0");
-    if (cache->n_kv_heads != 4 || cache->head_dim != 256)
-        return fail(KVA_ERR_UNSUPPORTED, "only 4 KV heads of 256 dims are supported");
-    if (cache->n_rot <= 0 || cache->n_rot > 64 || cache->n_rot % 8)
-        return fail(KVA_ERR_SHAPE, "n_rot must be a multiple of 8 in [8, 64]");
-    if (cache->page_size <= 0 || cache->n_pages <= 0 || cache->n_logical <= 0)
-        return fail(KVA_ERR_SHAPE, "page_size, n_pages and n_logical must be positive");
     if (ld_kv < 2LL * cache->n_kv_heads * cache->head_dim || ld_kv % 4)
         return fail(KVA_ERR_SHAPE, "ld_kv must be >= 2*n_kv_heads*head_dim and a multiple of 4");
     if (pos0 + n > (int64_t)cache->n_logical * cache->page_size)
         return fail(KVA_ERR_SHAPE, "positions past the page table");
-    if (!(cache->rope_base > 1.0) || !std::isfinite(cache->rope_base))
-        return fail(KVA_ERR_ARG, "rope_base must be > 1");
     if (n == 0) return KVA_OK;
     KvWriteArgs a{};
-    a.kv = kv; a.ld_kv = ld_kv; a.n_tokens = n; a.pos0 = pos0; a.k_gain = k_gain;
-    a.k_pool = cache->k_pool; a.v_pool = cache->v_pool; a.page_table = cache->page_table;
-    a.page_size = cache->page_size; a.n_pages = cache->n_pages; a.n_kv_heads = cache->n_kv_heads;
-    a.head_dim = cache->head_dim; a.n_rot = cache->n_rot; a.eps = cache->eps;
-    for (int j = 0; j < cache->n_rot / 2; ++j)
-        a.inv_freq[j] = std::pow(cache->rope_base, -2.0 * j / (double)cache->n_rot);
+    a.kv = kv; a.ld_kv = ld_kv; a.n_tokens = n; a.pos0 = pos0;
+    a.pool = make_pool(cache, k_gain);
+    a.rope = make_rope(cache);
     LAUNCH(launch_kv_write(a, static_cast<hipStream_t>(stream)));
     return KVA_OK;
 }

@@ -201,3 +201,29 @@ def test_r3_projection_chained_into_paged_kv_cache(r3bf16):
     for kp, vp in pools:
         assert not bool((kp == -1).all(dim=-1).any()) and not bool((vp == -1).all(dim=-1).any())
     proj.close()
+
+
+def _fused_r3(cfg, w, cases):
+    from test_gpu_fused_kv import fused_vs_chained
+    attn = [i for i, h in enumerate(cfg["heads"]) if h["kind"] == "attn"]
+    gains, ptab, n_pages = synth.make_kv_write_inputs(N_PROMPT, n_layers=len(attn), seed=cfg["seed"])
+    n_max = max(n for n, _ in cases)
+    x = synth.make_input(cfg, n_tokens=n_max)
+    proj = kva.Projector(cfg, w, max_tokens=n_max)
+    xd = torch.from_numpy(x).cuda()
+    gains_d = torch.from_numpy(gains).cuda()
+    for n, pos0 in cases:
+        fused_vs_chained(proj, cfg, xd, n, pos0, ptab, n_pages, gains_d)
+    proj.close()
+
+
+def test_r3_fused_kv_epilogue_equals_chained(r3bf16):
+    """kva_project_ubatch_kv on the r3 bf16 projector: pools bitwise equal to
+    the chained path (held to the oracle above), other heads bitwise equal."""
+    cfg, w, _ = r3bf16
+    _fused_r3(cfg, w, [(8192, 16384), (1000, 40007), (100, N_PROMPT - 100), (33, 5)])
+
+
+def test_r3_q8_0_fused_kv_epilogue_equals_chained(r3q8):
+    cfg, w, _ = r3q8
+    _fused_r3(cfg, w, [(1024, 7 * 1024), (64, 300)])
