@@ -201,9 +201,9 @@ typedef struct {
  *     pool[page_table[p / page_size]][p % page_size].
  *   kv      device fp32, row t at kv + t*ld_kv (ld_kv >= 2*n_kv_heads*head_dim)
  *   k_gain  device fp32 [head_dim]
- * Positions past n_logical*page_size, page entries outside [0, n_pages) are
- * the caller's responsibility for page entries (KVA_ERR_SHAPE is returned
- * when pos0 + n_tokens exceeds n_logical * page_size).  Asynchronous. */
+ * A token whose page-table entry lies outside [0, n_pages) is skipped
+ * (nothing is written for it).  KVA_ERR_SHAPE when pos0 + n_tokens exceeds
+ * n_logical * page_size or that product reaches 2^31.  Asynchronous. */
 kva_status kva_attn_kv_write(const float* kv, int64_t ld_kv, int32_t n_tokens, int64_t pos0,
                              const float* k_gain, const kva_paged_kv* cache, void* stream);
 

@@ -156,10 +156,15 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[MI][NI
                 const KvPool* pool = slot >= 0 ? &e.kv_pool[slot] : nullptr;
                 float* dst0 = slot >= 0 ? nullptr : e.heads.ptr[th] + e.tile_col0[t256];
                 const int64_t ld = slot >= 0 ? 0 : e.heads.ld[th];
+                constexpr int NC = WM / CR;                     // staging steps per wave row
+                KvLane kl{};
+                if (slot >= 0 && is_k) kl = kv_lane_setup(lane, pool->k_gain, e.kv_rope);
+                const int c4 = lane * 4;
+                const float4 b = bias ? *(const float4*)(bias + c4) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
                 for (int half = 0; half < WGM; ++half) {
 #pragma unroll
-                    for (int c = 0; c < WM / CR; ++c) {
+                    for (int c = 0; c < NC; ++c) {
                         if (wm == half) {
 #pragma unroll
                             for (int j = 0; j < NI; ++j)
@@ -175,24 +180,37 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[MI][NI
                         }
                         __syncthreads();
                         // CR rows x 64 chunks of 4 columns; one wave takes one full row
+                        const int row0 = tm * BM + half * WM + c * CR;
+                        if (slot < 0) {
 #pragma unroll
-                        for (int q = 0; q < CR / NW; ++q) {
-                            const int lr = q * NW + wave, c4 = lane * 4;
-                            const int row = tm * BM + half * WM + c * CR + lr;
-                            float4 v = *(const float4*)(lds + lr * BN + ((c4 + 32 * ((lr >> 2) & 1)) & (BN - 1)));
-                            if (bias) {
-                                const float4 b = *(const float4*)(bias + c4);
-                                v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
+                            for (int q = 0; q < CR / NW; ++q) {
+                                const int lr = q * NW + wave;
+                                float4 v = *(const float4*)(lds + lr * BN + ((c4 + 32 * ((lr >> 2) & 1)) & (BN - 1)));
+                                if (bias) { v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w; }
+                                if (row0 + lr < g.M) *(float4*)(dst0 + (int64_t)(row0 + lr) * ld + c4) = v;
                             }
-                            if (row >= g.M) continue;           // uniform over the wave
-                            if (slot < 0) {
-                                *(float4*)(dst0 + (int64_t)row * ld + c4) = v;
-                                continue;
+                        } else {
+                            // the physical pages of this wave's rows, one per lane,
+                            // fetched together before the row loop
+                            int my_pg = -1;
+                            if (lane < CR / NW && row0 + lane * NW + wave < g.M)
+                                my_pg = kv_page(*pool, e.kv_pos0 + row0 + lane * NW + wave);
+                            // not unrolled: the KV row code is large, and unrolled
+                            // copies of it would crowd the instruction cache
+#pragma unroll 1
+                            for (int q = 0; q < CR / NW; ++q) {
+                                const int lr = q * NW + wave;
+                                const int row = row0 + lr;
+                                if (row >= g.M) break;             // uniform over the wave; rows ascend
+                                float4 v = *(const float4*)(lds + lr * BN + ((c4 + 32 * ((lr >> 2) & 1)) & (BN - 1)));
+                                if (bias) { v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w; }
+                                const int64_t p = e.kv_pos0 + row;
+                                const int pg = __shfl(my_pg, q);
+                                if (is_k) v = kv_k_norm_rope(v, lane, p, kl, e.kv_rope.n_rot, e.kv_rope.eps);
+                                if (pg >= 0)
+                                    kv_store_bf16((is_k ? pool->k_pool : pool->v_pool) +
+                                                      kv_slot_offset(*pool, pg, p, kvh, lane), v);
                             }
-                            const int64_t p = e.kv_pos0 + row;
-                            const int64_t off = kv_slot_offset(*pool, p, kvh, lane);
-                            if (is_k) v = kv_k_norm_rope(v, lane, p, pool->k_gain, e.kv_rope);
-                            if (off >= 0) kv_store_bf16((is_k ? pool->k_pool : pool->v_pool) + off, v);
                         }
                         __syncthreads();
                     }

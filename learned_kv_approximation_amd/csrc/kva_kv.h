@@ -14,55 +14,108 @@ namespace kva {
 
 // Butterfly sum over the 64 lanes (fixed order; every lane gets the total).
 __device__ __forceinline__ float kv_wave_sum(float v) {
+#pragma clang fp contract(off)
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
     return v;
 }
 
+// Per-lane constants of the k path, loaded once and reused for every token:
+// the lane's 4 k_norm gains and, for lane j < n_rot/2, the frequency of
+// rotary pair j.
+struct KvLane {
+    float4 gain;
+    double inv_freq;
+};
+
+__device__ __forceinline__ KvLane kv_lane_setup(int lane, const float* __restrict__ gain, const KvRope& rope) {
+    KvLane L;
+    L.gain = *(const float4*)(gain + lane * 4);
+    L.inv_freq = lane < rope.n_rot / 2 ? rope.inv_freq[lane] : 0.0;
+    return L;
+}
+
+// sin and cos of an angle th >= 0 given in double (th below 2^40 or so):
+// the quadrant q = nearest integer of th / (pi/2) and the remainder
+// r = th - q*pi/2 (|r| <= pi/4) are formed in double, then the Taylor
+// polynomials of sin and cos at 0 (through r^9 and r^10; the first omitted
+// terms are below 2e-9 on |r| <= pi/4) are evaluated in fp32 and permuted and
+// negated by q mod 4.  Branch-free, a few dozen instructions; absolute error
+// about 1e-7 (an fp32 sincosf would also carry a large-argument path that a
+// compiler may evaluate on every call).
+__device__ __forceinline__ void kv_sincos(double th, float* sn, float* cs) {
+#pragma clang fp contract(off)
+    const double half_pi = 1.5707963267948966192313216916398;
+    const double q = rint(th * (1.0 / half_pi));
+    const float r = (float)(th - q * half_pi);
+    const float r2 = r * r;
+    const float s = r + r * r2 * (-1.0f / 6 + r2 * (1.0f / 120 + r2 * (-1.0f / 5040 + r2 * (1.0f / 362880))));
+    const float c = 1.0f + r2 * (-0.5f + r2 * (1.0f / 24 + r2 * (-1.0f / 720 + r2 * (1.0f / 40320 +
+                                                                            r2 * (-1.0f / 3628800)))));
+    const int qi = (int)((int64_t)q & 3);
+    const float sv = (qi & 1) ? c : s;          // sin(r + q pi/2): s, c, -s, -c
+    const float cv = (qi & 1) ? s : c;          // cos(r + q pi/2): c, -s, -c, s
+    *sn = (qi & 2) ? -sv : sv;
+    *cs = ((qi + 1) & 2) ? -cv : cv;
+}
+
 // k_norm then RoPE on one KV head of one token at absolute position p.
 //   k_norm: k / sqrt(mean(k^2) + eps) * gain (per KV head, 256 dims);
 //   RoPE: the pair (j, j + n_rot/2), j < n_rot/2, is turned by p * inv_freq[j].
-// The rotary pair of lane l < n_rot/8 lives in lane l + n_rot/8.  The angle is
-// formed and reduced modulo 2 pi in double (p reaches 65535 and more: an fp32
-// product would be off by several 1e-3 rad), then fp32 sincos.
+// The rotary pair of lane l < n_rot/8 lives in lane l + n_rot/8.  Each angle
+// is formed in double and reduced to a quarter turn there (kv_sincos): p
+// reaches 65535 and more, where an fp32 product would be off by several 1e-3
+// rad.
 // Must be called by all 64 lanes of a wave together.
-__device__ __forceinline__ float4 kv_k_norm_rope(float4 k, int lane, int64_t p, const float* __restrict__ gain,
-                                                 const KvRope& rope) {
+__device__ __forceinline__ float4 kv_k_norm_rope(float4 k, int lane, int64_t p, const KvLane& L,
+                                                 int n_rot, float eps) {
+    // No multiply-add contraction: whether the compiler fuses a product into
+    // an add may depend on the code around an inlined copy, and every caller
+    // must round exactly alike.
+#pragma clang fp contract(off)
     const float ss = kv_wave_sum(k.x * k.x + k.y * k.y + k.z * k.z + k.w * k.w);
-    const float r = 1.0f / sqrtf(ss / (float)kKvHeadDim + rope.eps);
-    const float4 gg = *(const float4*)(gain + lane * 4);
-    k.x *= r * gg.x; k.y *= r * gg.y; k.z *= r * gg.z; k.w *= r * gg.w;
+    const float r = 1.0f / sqrtf(ss / (float)kKvHeadDim + eps);
+    k.x *= r * L.gain.x; k.y *= r * L.gain.y; k.z *= r * L.gain.z; k.w *= r * L.gain.w;
 
-    const int half_lanes = rope.n_rot / 8;     // lanes holding the first half of the rotary dims
+    // lane j < n_rot/2 turns the angle of pair j; the lanes holding the
+    // pair's two values fetch it from there
+    float sj, cj;
+    kv_sincos((double)p * L.inv_freq, &sj, &cj);
+    const int half_lanes = n_rot / 8;          // lanes holding the first half of the rotary dims
     const float4 other = make_float4(__shfl_xor(k.x, half_lanes), __shfl_xor(k.y, half_lanes),
                                      __shfl_xor(k.z, half_lanes), __shfl_xor(k.w, half_lanes));
+    const int j0 = (lane < half_lanes ? lane : lane - half_lanes) * 4;
+    float sn[4], cs[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        sn[e] = __shfl(sj, j0 + e);
+        cs[e] = __shfl(cj, j0 + e);
+    }
     if (lane < 2 * half_lanes) {
         const bool first = lane < half_lanes;
-        const int j0 = (first ? lane : lane - half_lanes) * 4;
         float kk[4] = {k.x, k.y, k.z, k.w};
         const float oo[4] = {other.x, other.y, other.z, other.w};
-        const double two_pi = 6.283185307179586476925286766559;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            double th = (double)p * rope.inv_freq[j0 + e];
-            th -= two_pi * floor(th / two_pi);
-            float sn, cs;
-            sincosf((float)th, &sn, &cs);
+        for (int e = 0; e < 4; ++e)
             // first half: x' = x cos - y sin ; second half: y' = x sin + y cos
-            kk[e] = first ? (kk[e] * cs - oo[e] * sn) : (oo[e] * sn + kk[e] * cs);
-        }
+            kk[e] = first ? (kk[e] * cs[e] - oo[e] * sn[e]) : (oo[e] * sn[e] + kk[e] * cs[e]);
         k = make_float4(kk[0], kk[1], kk[2], kk[3]);
     }
     return k;
 }
 
-// Element offset of dims 4*lane.. of KV head kvh for position p in a pool
-// [n_pages][page_size][kKvHeads][kKvHeadDim], or -1 when the page-table entry
-// is outside [0, n_pages) (nothing is written for that token).
-__device__ __forceinline__ int64_t kv_slot_offset(const KvPool& c, int64_t p, int kvh, int lane) {
-    const int pg = c.page_table[p / c.page_size];
-    if (pg < 0 || pg >= c.n_pages) return -1;
-    const int slot = (int)(p % c.page_size);
+// Physical page of position p (positions are below 2^31, checked on the
+// host), or -1 when the page-table entry is outside [0, n_pages): nothing is
+// written for that token.
+__device__ __forceinline__ int kv_page(const KvPool& c, int64_t p) {
+    const int pg = c.page_table[(uint32_t)p / (uint32_t)c.page_size];
+    return (pg < 0 || pg >= c.n_pages) ? -1 : pg;
+}
+
+// Element offset of dims 4*lane.. of KV head kvh for position p on page pg in
+// a pool [n_pages][page_size][kKvHeads][kKvHeadDim].
+__device__ __forceinline__ int64_t kv_slot_offset(const KvPool& c, int pg, int64_t p, int kvh, int lane) {
+    const int slot = (int)((uint32_t)p % (uint32_t)c.page_size);
     return (((int64_t)pg * c.page_size + slot) * kKvHeads + kvh) * kKvHeadDim + lane * 4;
 }
 

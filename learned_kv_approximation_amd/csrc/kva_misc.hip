@@ -111,11 +111,13 @@ __global__ void __launch_bounds__(256) kv_write_kernel(KvWriteArgs a) {
     const int kvh = threadIdx.x >> 6;           // 4 waves = 4 KV heads
     const int t = blockIdx.x;
     const int64_t p = a.pos0 + t;
-    const int64_t off = kv_slot_offset(a.pool, p, kvh, lane);
-    if (off < 0) return;
+    const int pg = kv_page(a.pool, p);
+    if (pg < 0) return;
+    const int64_t off = kv_slot_offset(a.pool, pg, p, kvh, lane);
     const float* kr = a.kv + (int64_t)t * a.ld_kv + kvh * kKvHeadDim;
     const float* vr = kr + kKvHeads * kKvHeadDim;
-    const float4 k = kv_k_norm_rope(*(const float4*)(kr + lane * 4), lane, p, a.pool.k_gain, a.rope);
+    const KvLane L = kv_lane_setup(lane, a.pool.k_gain, a.rope);
+    const float4 k = kv_k_norm_rope(*(const float4*)(kr + lane * 4), lane, p, L, a.rope.n_rot, a.rope.eps);
     kv_store_bf16(a.pool.k_pool + off, k);
     kv_store_bf16(a.pool.v_pool + off, *(const float4*)(vr + lane * 4));
 }

@@ -645,6 +645,8 @@ kva_status check_paged_kv(const kva_paged_kv* cache, const float* k_gain) {
         return fail(KVA_ERR_SHAPE, "page_size, n_pages and n_logical must be positive");
     if (!(cache->rope_base > 1.0) || !std::isfinite(cache->rope_base))
         return fail(KVA_ERR_ARG, "rope_base must be > 1");
+    if ((int64_t)cache->n_logical * cache->page_size > INT32_MAX)
+        return fail(KVA_ERR_SHAPE, "n_logical * page_size must stay below 2^31 positions");
     return KVA_OK;
 }
 

@@ -75,8 +75,13 @@ def fused_vs_chained(proj, cfg, xd, n, pos0, ptab, n_pages, gains_d):
     kva.kva_project_ubatch_kv(proj.ctx, xd.data_ptr(), n, ptrs, pos0, dests, st)
     torch.cuda.synchronize()
     for li in range(len(attn)):
-        assert torch.equal(pa[li][0], pb[li][0]), ("k pool", li)
-        assert torch.equal(pa[li][1], pb[li][1]), ("v pool", li)
+        for part in (0, 1):
+            if not torch.equal(pa[li][part], pb[li][part]):
+                a_, b_ = pa[li][part].cpu().numpy(), pb[li][part].cpu().numpy()
+                bad = np.argwhere(a_ != b_)
+                print(f"layer {li} {'kv'[part]}: {len(bad)} differing values, first {bad[:8].tolist()}, "
+                      f"chained {a_[tuple(bad[:8].T)].tolist()} fused {b_[tuple(bad[:8].T)].tolist()}", flush=True)
+            assert torch.equal(pa[li][part], pb[li][part]), ("kv"[part] + " pool", li)
     for i, h in enumerate(cfg["heads"]):
         if i not in attn:
             assert torch.equal(outs_a[i], outs_b[i]), ("head", i)
