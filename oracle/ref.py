@@ -372,3 +372,101 @@ def kv_write(kv, gain, pos0, page_table, k_pool, v_pool, page_size: int = 256, *
         k_pool[pg, sl] = kb[t]
         v_pool[pg, sl] = vb[t]
     return k_pool, v_pool
+
+
+# --------------------------------------------------------------------------
+# quantised KV cache with a Hadamard rotation ([KVA] "Projector quantization
+# and flash-attn": q8_0 K and V caches work, and the engine rotates the
+# approximated K and V with the same Hadamard transform as the exact path).
+# Readings (the pages give no more than that sentence):
+#  - the rotation is the orthonormal Walsh-Hadamard transform of Sylvester
+#    order over each KV head's 256 dims, y = H x / 16 with
+#    H[i][j] = (-1)^popcount(i & j), applied to K after k_norm and RoPE and
+#    to V as predicted;
+#  - each KV head's 256 rotated values are then 8 q8_0 blocks of 32
+#    consecutive dims (ggml's block: fp16 scale d, 32 int8 codes q, value
+#    d * q), laid out [n_pages][page_size][n_kv_heads][8 x 34 bytes];
+#  - a block's quantisation is decided in binary32, the precision the rotated
+#    values exist in: d = amax / 127, q = round-half-away(y / d) (q = 0 when
+#    d = 0), clamped to [-127, 127]; the stored scale is d rounded once to
+#    fp16 (nearest even).
+
+
+def hadamard(n: int) -> np.ndarray:
+    """Sylvester-order Hadamard matrix of order n (a power of two) from its
+    definition H[i][j] = (-1)^(number of bits i and j share)."""
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    bits = np.bitwise_and(i, j)
+    parity = np.zeros_like(bits)
+    while np.any(bits):
+        parity ^= bits & 1
+        bits = bits >> 1
+    return np.where(parity == 1, -1.0, 1.0)
+
+
+def hadamard_rotate(x: np.ndarray) -> np.ndarray:
+    """y = H x / sqrt(n) along the last axis (H symmetric and H H = n I, so
+    this is an orthogonal involution)."""
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-1]
+    return x @ hadamard(n) / math.sqrt(n)
+
+
+def q8_0_quantize(y: np.ndarray):
+    """q8_0 blocks of the last axis (a multiple of 32), decided in binary32.
+    Returns (scale bits uint16 [..., nb], codes int8 [..., nb, 32])."""
+    y32 = np.asarray(y, dtype=np.float64).astype(np.float32)
+    blk = y32.reshape(y32.shape[:-1] + (y32.shape[-1] // Q8_0_BLOCK, Q8_0_BLOCK))
+    amax = np.max(np.abs(blk), axis=-1)
+    d = (amax / np.float32(127.0)).astype(np.float32)          # binary32 division
+    safe = np.where(d == 0, np.float32(1.0), d)
+    t = (blk / safe[..., None]).astype(np.float32)             # binary32 division
+    t64 = t.astype(np.float64)                                  # exact
+    q = np.sign(t64) * np.floor(np.abs(t64) + 0.5)              # half away from zero, exact in float64
+    q = np.clip(q, -127, 127)
+    q[d == 0] = 0
+    return f64_to_f16_bits(d.astype(np.float64)), q.astype(np.int8)
+
+
+def q8_0_block_bytes(d_bits: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """Pack scales [..., nb] and codes [..., nb, 32] into [..., nb * 34] bytes
+    (per block: the fp16 scale little-endian, then the 32 codes)."""
+    nb = d_bits.shape[-1]
+    out = np.zeros(d_bits.shape + (Q8_0_BYTES,), dtype=np.uint8)
+    out[..., 0] = (d_bits & 0xFF).astype(np.uint8)
+    out[..., 1] = (d_bits >> 8).astype(np.uint8)
+    out[..., 2:] = q.view(np.uint8)
+    return out.reshape(d_bits.shape[:-1] + (nb * Q8_0_BYTES,))
+
+
+def q8_0_block_values(row_bytes: np.ndarray) -> np.ndarray:
+    """Inverse of q8_0_block_bytes up to the values: [..., nb * 34] bytes ->
+    float64 [..., nb * 32], each fp16(d) * q exactly."""
+    b = np.asarray(row_bytes, dtype=np.uint8)
+    nb = b.shape[-1] // Q8_0_BYTES
+    blk = b.reshape(b.shape[:-1] + (nb, Q8_0_BYTES))
+    d = f16_bits_to_f64(np.ascontiguousarray(blk[..., 0:2]).view(np.uint16)[..., 0])
+    q = np.ascontiguousarray(blk[..., 2:]).view(np.int8).astype(np.float64)
+    return (d[..., None] * q).reshape(b.shape[:-1] + (nb * Q8_0_BLOCK,))
+
+
+def kv_write_q8_0_values(kv: np.ndarray, gain: np.ndarray, pos0: int, **kw):
+    """float64 rotated K and V [T, n_kv_heads, head_dim] as they are quantised
+    (k_norm and RoPE as in kv_write_values, then hadamard_rotate)."""
+    k, v = kv_write_values(kv, gain, pos0, **kw)
+    return hadamard_rotate(k), hadamard_rotate(v)
+
+
+def kv_write_q8_0(kv, gain, pos0, page_table, k_pool, v_pool, page_size: int = 256, **kw):
+    """Write q8_0 K and V rows into byte pools [n_pages][page_size][n_kv_heads]
+    [head_dim / 32 * 34] (updated in place), token at position p on page
+    page_table[p // page_size], slot p % page_size."""
+    k, v = kv_write_q8_0_values(kv, gain, pos0, **kw)
+    kb, vb = q8_0_block_bytes(*q8_0_quantize(k)), q8_0_block_bytes(*q8_0_quantize(v))
+    for t in range(kb.shape[0]):
+        p = pos0 + t
+        pg, sl = int(page_table[p // page_size]), p % page_size
+        k_pool[pg, sl] = kb[t]
+        v_pool[pg, sl] = vb[t]
+    return k_pool, v_pool

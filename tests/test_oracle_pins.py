@@ -433,6 +433,93 @@ def test_paged_write_gathers_back_and_fills_each_slot_once():
     assert np.all(kp[~used] == poison) and not np.any(np.all(kp[used] == poison, axis=-1))
 
 
+# ------------------------------------------------------------------ quantised KV cache (Hadamard + q8_0)
+
+def test_hadamard_is_scipys_sylvester_matrix_and_an_orthogonal_involution():
+    import scipy.linalg
+    for n in (2, 8, 32, 256):
+        H = ref.hadamard(n)
+        assert np.array_equal(H, scipy.linalg.hadamard(n))          # library special case
+        assert np.array_equal(H @ H.T, n * np.eye(n))
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((50, 4, 256))
+    y = ref.hadamard_rotate(x)
+    assert np.allclose(ref.hadamard_rotate(y), x, rtol=0, atol=1e-13)     # involution
+    assert np.allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-14)
+    # basis vectors: e_0 -> all 1/16, e_j -> row j of H / 16 (Sylvester order)
+    e = np.zeros(256)
+    e[0] = 1.0
+    assert np.array_equal(ref.hadamard_rotate(e), np.full(256, 1.0 / 16))
+    e[:] = 0
+    e[5] = 1.0
+    want = np.array([(-1.0) ** bin(i & 5).count("1") for i in range(256)]) / 16
+    assert np.array_equal(ref.hadamard_rotate(e), want)
+    # dot products survive the rotation (what lets attention use rotated K with rotated Q)
+    a, b = rng.standard_normal(256), rng.standard_normal(256)
+    assert abs(ref.hadamard_rotate(a) @ ref.hadamard_rotate(b) - a @ b) < 1e-12
+
+
+def test_q8_0_quantize_hand_blocks():
+    # amax 127 -> d = 1 exactly: the codes are the values rounded half away from zero
+    y = np.zeros(64)
+    y[:9] = [127, -127, 63.5, -63.5, 0.49, -2.5, 0.5, -0.5, 1.5]
+    y[32:35] = [-3.0, 1.5, 0.75]            # second block: amax 3, d = 3/127
+    d, q = ref.q8_0_quantize(y)
+    assert d[0] == 0x3C00                    # fp16 1.0
+    assert q[0, :9].tolist() == [127, -127, 64, -64, 0, -3, 1, -1, 2]
+    assert not q[0, 9:].any()
+    d1 = np.float32(3.0) / np.float32(127.0)
+    assert d[1] == ref.f64_to_f16_bits(np.array([float(d1)]))[0]
+    assert q[1, :3].tolist() == [-127, 64, 32]   # 1.5/d1 = 63.5 -> 64; 0.75/d1 = 31.75 -> 32
+    # an all-zero block has d = 0 and codes 0
+    d, q = ref.q8_0_quantize(np.zeros(32))
+    assert d[0] == 0 and not q.any()
+    # packing: scale little-endian, then the codes as bytes; values d*q back
+    d, q = ref.q8_0_quantize(y)
+    b = ref.q8_0_block_bytes(d, q)
+    assert b.shape == (68,) and b[0] == 0x00 and b[1] == 0x3C and b[2] == 127 and b[3] == 0x81
+    vals = ref.q8_0_block_values(b)
+    assert vals[0] == 127.0 and vals[3] == -64.0
+
+
+def test_q8_0_quantize_error_bound_and_extremes():
+    rng = np.random.default_rng(12)
+    y = rng.standard_normal((400, 256)) * np.exp2(rng.integers(-6, 6, (400, 1)))
+    d, q = ref.q8_0_quantize(y)
+    blk = y.reshape(400, 8, 32)
+    amax = np.abs(blk).max(-1)
+    # the block's largest magnitude always maps to +-127
+    assert np.all(np.abs(q).max(-1) == 127)
+    # |fp16(d) q - y| <= d/2 (rounding) + |fp16(d) - d| * 127 (scale storage) + fp32 slack
+    d32 = amax / 127.0
+    d16 = ref.f16_bits_to_f64(d)
+    err = np.abs(d16[..., None] * q - blk)
+    bound = 0.5 * d32 + np.abs(d16 - d32) * 127 + 1e-6 * amax
+    assert np.all(err <= bound[..., None])
+
+
+def test_q8_0_kv_write_layout_and_rotation():
+    n_tok = 300
+    gains, ptab, n_pages = synth.make_kv_write_inputs(n_tok, n_layers=1, n_pages=3)
+    kv = synth.make_kv_rows(n_tok)
+    kp = np.full((n_pages, 256, 4, 8 * 34), 0xFF, dtype=np.uint8)
+    vp = kp.copy()
+    ref.kv_write_q8_0(kv, gains[0], 10, ptab, kp, vp)
+    k, v = ref.kv_write_values(kv, gains[0], 10)
+    pos = 10 + np.arange(n_tok)
+    gk = ref.q8_0_block_values(kp[ptab[pos // 256], pos % 256])
+    gv = ref.q8_0_block_values(vp[ptab[pos // 256], pos % 256])
+    # rotating the dequantised rows back gives K and V within the q8_0 error
+    for got, want in ((gk, k), (gv, v)):
+        back = ref.hadamard_rotate(got)
+        rms = np.sqrt(np.mean(want * want))
+        assert np.max(np.abs(back - want)) / rms < 0.05
+        assert np.sqrt(np.mean((back - want) ** 2)) / rms < 0.01
+    used = np.zeros((n_pages, 256), dtype=bool)
+    used[ptab[pos // 256], pos % 256] = True
+    assert np.all(kp[~used] == 0xFF)
+
+
 # ------------------------------------------------------------------ planted mistakes
 
 def _mutants():
