@@ -156,10 +156,11 @@ def time_config(name: str, steps: int, warmup: int, n_tokens: int = 1024, prompt
     return res
 
 
-def time_kv_write(n_tokens: int = 65536, layers: int = 8, chunk: int = 8192, steps: int = 5):
+def time_kv_write(n_tokens: int = 65536, layers: int = 8, chunk: int = 8192, steps: int = 5, q8: bool = False):
     """kva_attn_kv_write for every attention layer over an n_tokens prompt
     (chunk tokens per call, as after each projection call).  Per token and
-    layer it reads 2048 fp32 (8 KiB) and writes 2 x 1024 bf16 (4 KiB)."""
+    layer it reads 2048 fp32 (8 KiB) and writes 2 x 1024 bf16 (4 KiB), or with
+    q8 the Hadamard-rotated q8_0 rows (2 x 4 x 272 bytes)."""
     import torch
 
     import learned_kv_approximation_amd as kva
@@ -168,10 +169,12 @@ def time_kv_write(n_tokens: int = 65536, layers: int = 8, chunk: int = 8192, ste
     kv = torch.from_numpy(synth.make_kv_rows(chunk, scale=3.0)).cuda()
     g = torch.from_numpy(gains).cuda()
     pt = torch.from_numpy(ptab).cuda()
-    pools = [(torch.empty((n_pages, 256, 4, 256), dtype=torch.int16, device="cuda"),
-              torch.empty((n_pages, 256, 4, 256), dtype=torch.int16, device="cuda")) for _ in range(layers)]
+    row_bytes = 272 if q8 else 512
+    pools = [(torch.empty((n_pages, 256, 4, row_bytes), dtype=torch.uint8, device="cuda"),
+              torch.empty((n_pages, 256, 4, row_bytes), dtype=torch.uint8, device="cuda")) for _ in range(layers)]
+    kv_type = kva.KVA_KV_Q8_0_HADAMARD if q8 else kva.KVA_KV_BF16
     caches = [kva.kva_paged_kv(kp.data_ptr(), vp.data_ptr(), pt.data_ptr(), 256, n_pages, len(ptab),
-                               4, 256, 64, 1.0e7, 1e-6) for kp, vp in pools]
+                               4, 256, 64, 1.0e7, 1e-6, kv_type) for kp, vp in pools]
     st = kva.current_stream()
 
     def step():
@@ -188,10 +191,11 @@ def time_kv_write(n_tokens: int = 65536, layers: int = 8, chunk: int = 8192, ste
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    nbytes = n_tokens * layers * (2048 * 4 + 2 * 1024 * 2)
+    nbytes = n_tokens * layers * (2048 * 4 + 2 * 4 * row_bytes)
     del pools
     torch.cuda.empty_cache()
-    return {"tokens": n_tokens, "layers": layers, "ms": round(ms, 4), "bytes": nbytes,
+    return {"tokens": n_tokens, "layers": layers, "cache": "q8_0 + Hadamard" if q8 else "bf16",
+            "ms": round(ms, 4), "bytes": nbytes,
             "gb_s": round(nbytes / (ms / 1e3) / 1e9, 1), "frac_hbm": round(nbytes / (ms / 1e3) / 1e9 / HBM_GBS, 4),
             "launches": (n_tokens // chunk) * layers}
 
@@ -421,7 +425,7 @@ def main():
 
     r2 = time_config("r2", args.steps, args.warmup)
     print(f"[bench] r2: {r2['tokens_per_s']:.0f} tok/s, {r2['pct_mfma_peak']:.1f}% peak", file=sys.stderr, flush=True)
-    r3 = r3b = q8 = q8p = q4 = kvw = kvp = sweep = mloop = None
+    r3 = r3b = q8 = q8p = q4 = kvw = kvw8 = kvp = sweep = mloop = None
     if not args.no_r3:
         r3 = time_config("r3", args.steps, args.warmup)
         print(f"[bench] r3: {r3['tokens_per_s']:.0f} tok/s, {r3['pct_mfma_peak']:.1f}% peak", file=sys.stderr,
@@ -437,6 +441,8 @@ def main():
             print(f"[bench] r3 q4_0: {q4['tokens_per_s']:.0f} tok/s", file=sys.stderr, flush=True)
             kvw = time_kv_write()
             print(f"[bench] kv write: {kvw['gb_s']} GB/s", file=sys.stderr, flush=True)
+            kvw8 = time_kv_write(q8=True)
+            print(f"[bench] kv write q8_0: {kvw8['gb_s']} GB/s", file=sys.stderr, flush=True)
             kvp = time_prompt_kv()
             print(f"[bench] r3 65536 + KV: chained {kvp['chained']['tokens_per_s']:.0f} tok/s, "
                   f"fused {kvp['fused']['tokens_per_s']:.0f} tok/s", file=sys.stderr, flush=True)
@@ -498,6 +504,8 @@ def main():
         out["r3_q4_0"] = brief(q4)
     if kvw is not None:
         out["kv_write_65536x8"] = kvw
+    if kvw8 is not None:
+        out["kv_write_q8_0_65536x8"] = kvw8
     if kvp is not None:
         out["r3_prompt_65536_with_kv"] = kvp
     if sweep is not None:

@@ -170,14 +170,34 @@ kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n_tokens,
 /* Synchronises the context's device, frees everything it owns.  NULL-safe. */
 kva_status kva_destroy(kva_ctx* ctx);
 
+/* Storage of a paged KV cache. */
+typedef enum {
+    KVA_KV_BF16 = 0,           /* rows of head_dim bf16 values                   */
+    KVA_KV_Q8_0_HADAMARD = 1   /* rows of head_dim/32 q8_0 blocks (34 bytes:     */
+                               /* fp16 scale d, 32 int8 codes q, value d*q) of   */
+                               /* the Hadamard-rotated values, see below         */
+} kva_kv_type;
+
 /* Paged KV cache of one full-attention layer of the base model
  * ("Qwen3.8-27B-MLA" card, "What this is": 4 KV heads of 256 dims, 64 of
- * which are rotary).  Pools are device arrays of bf16 bit patterns laid out
- * [n_pages][page_size][n_kv_heads][head_dim]; page_table is a device int32
- * array mapping logical page (position / page_size) to a physical page. */
+ * which are rotary).  Pools are device arrays laid out
+ * [n_pages][page_size][n_kv_heads][row], a row being one KV head of one token
+ * in the kv_type's format (bf16: 512 bytes; q8_0: 272 bytes, 2-byte aligned
+ * pools); page_table is a device int32 array mapping logical page
+ * (position / page_size) to a physical page.
+ *
+ * KVA_KV_Q8_0_HADAMARD ("Qwen3.8-27B-KVA" card, "Projector quantization and
+ * flash-attn": quantised q8_0 K/V caches, with the exact path's Hadamard
+ * rotation applied to the approximated K/V): each row is first rotated by the
+ * orthonormal Walsh-Hadamard transform of Sylvester order, y = H x / 16 with
+ * H[i][j] = (-1)^popcount(i & j) over the 256 dims (an orthogonal involution:
+ * a consumer rotates queries alike, or rotates y back), then stored as 8 q8_0
+ * blocks of 32 consecutive dims, decided in fp32: d = amax / 127,
+ * q = round-half-away(y / d) (0 when d = 0), clamped to [-127, 127], d stored
+ * rounded to fp16 (nearest even). */
 typedef struct {
-    uint16_t* k_pool;
-    uint16_t* v_pool;
+    void* k_pool;
+    void* v_pool;
     const int32_t* page_table;
     int32_t page_size;     /* 256                                        */
     int32_t n_pages;       /* physical pages in each pool                */
@@ -187,6 +207,7 @@ typedef struct {
     int32_t n_rot;         /* rotary dims at the start of each KV head   */
     double rope_base;      /* 1e7                                        */
     float eps;             /* k_norm epsilon, 1e-6                       */
+    int32_t kv_type;       /* kva_kv_type (KVA_ERR_DTYPE if unknown)     */
 } kva_paged_kv;
 
 /* The attention-layer state update that follows the projection ("What the
@@ -197,8 +218,8 @@ typedef struct {
  *   RoPE on dims [0, n_rot): pair (j, j + n_rot/2) turned by
  *     p * rope_base^(-2j/n_rot) (the angle is reduced in double precision);
  *   v = kv[t][n_kv_heads*head_dim : 2*n_kv_heads*head_dim] unchanged;
- *   both rounded to bf16 (nearest even) and stored at
- *     pool[page_table[p / page_size]][p % page_size].
+ *   both stored in the cache's kv_type (bf16 rounded to nearest even, or
+ *   Hadamard-rotated q8_0) at pool[page_table[p / page_size]][p % page_size].
  *   kv      device fp32, row t at kv + t*ld_kv (ld_kv >= 2*n_kv_heads*head_dim)
  *   k_gain  device fp32 [head_dim]
  * A token whose page-table entry lies outside [0, n_pages) is skipped

@@ -64,7 +64,10 @@ STAGES = ["norm", "gemm_in", "gemm_qkv", "attn", "gemm_o", "gemm_gateup", "gemm_
 class kva_paged_kv(ctypes.Structure):
     _fields_ = [("k_pool", c_vp), ("v_pool", c_vp), ("page_table", c_vp), ("page_size", c_i32),
                 ("n_pages", c_i32), ("n_logical", c_i32), ("n_kv_heads", c_i32), ("head_dim", c_i32),
-                ("n_rot", c_i32), ("rope_base", c_f64), ("eps", c_f32)]
+                ("n_rot", c_i32), ("rope_base", c_f64), ("eps", c_f32), ("kv_type", c_i32)]
+
+
+KVA_KV_BF16, KVA_KV_Q8_0_HADAMARD = 0, 1
 
 
 class kva_attn_dest(ctypes.Structure):

@@ -207,9 +207,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[MI][NI
                                 const int64_t p = e.kv_pos0 + row;
                                 const int pg = __shfl(my_pg, q);
                                 if (is_k) v = kv_k_norm_rope(v, lane, p, kl, e.kv_rope.n_rot, e.kv_rope.eps);
-                                if (pg >= 0)
-                                    kv_store_bf16((is_k ? pool->k_pool : pool->v_pool) +
-                                                      kv_slot_offset(*pool, pg, p, kvh, lane), v);
+                                if (pg >= 0) kv_store_row(*pool, is_k, kv_row_index(*pool, pg, p, kvh), lane, v);
                             }
                         }
                         __syncthreads();

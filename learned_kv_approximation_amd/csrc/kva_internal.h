@@ -81,15 +81,19 @@ constexpr int kKvHeads = 4;
 constexpr int kKvHeadDim = 256;
 constexpr int kMaxAttnHeads = 16;
 
-// One attention layer's paged pools [n_pages][page_size][kKvHeads][kKvHeadDim]
-// bf16, its page table and its k_norm gain [kKvHeadDim].
+// One attention layer's paged pools, its page table and its k_norm gain
+// [kKvHeadDim].  Pools are [n_pages][page_size][kKvHeads][row], a row being
+// kKvHeadDim bf16 values, or (q8 != 0) the Hadamard-rotated values as
+// kKvHeadDim / 32 q8_0 blocks of 34 bytes.
+constexpr int kKvQ8RowBytes = kKvHeadDim / 32 * 34;
 struct KvPool {
-    uint16_t* k_pool;
-    uint16_t* v_pool;
+    void* k_pool;
+    void* v_pool;
     const int32_t* page_table;
     const float* k_gain;
     int32_t page_size;
     int32_t n_pages;
+    int32_t q8;
 };
 
 struct KvRope {

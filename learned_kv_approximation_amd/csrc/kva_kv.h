@@ -112,11 +112,36 @@ __device__ __forceinline__ int kv_page(const KvPool& c, int64_t p) {
     return (pg < 0 || pg >= c.n_pages) ? -1 : pg;
 }
 
-// Element offset of dims 4*lane.. of KV head kvh for position p on page pg in
-// a pool [n_pages][page_size][kKvHeads][kKvHeadDim].
-__device__ __forceinline__ int64_t kv_slot_offset(const KvPool& c, int pg, int64_t p, int kvh, int lane) {
+// Row index (token slot and KV head) of position p on page pg in a pool
+// [n_pages][page_size][kKvHeads][row].
+__device__ __forceinline__ int64_t kv_row_index(const KvPool& c, int pg, int64_t p, int kvh) {
     const int slot = (int)((uint32_t)p % (uint32_t)c.page_size);
-    return (((int64_t)pg * c.page_size + slot) * kKvHeads + kvh) * kKvHeadDim + lane * 4;
+    return ((int64_t)pg * c.page_size + slot) * kKvHeads + kvh;
+}
+
+// Orthonormal Walsh-Hadamard transform of Sylvester order over the wave's
+// 256 values (lane l holds dims 4l..4l+3): y = H x / 16 with
+// H[i][j] = (-1)^popcount(i & j).  One butterfly stage per bit of the dim
+// index, (a, b) -> (a + b, a - b) on the pair that differs in that bit:
+// bits 0 and 1 inside the lane, bits 2..7 across lanes (lane bit 0..5).  The
+// quantised KV cache stores K and V rotated this way ([KVA] "Projector
+// quantization and flash-attn": the approximated K/V get the exact path's
+// Hadamard rotation).  Must be called by all 64 lanes of a wave together.
+__device__ __forceinline__ float4 kv_hadamard256(float4 x, int lane) {
+#pragma clang fp contract(off)
+    float a0 = x.x + x.y, a1 = x.x - x.y, a2 = x.z + x.w, a3 = x.z - x.w;
+    float b0 = a0 + a2, b1 = a1 + a3, b2 = a0 - a2, b3 = a1 - a3;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        const float o0 = __shfl_xor(b0, m), o1 = __shfl_xor(b1, m);
+        const float o2 = __shfl_xor(b2, m), o3 = __shfl_xor(b3, m);
+        const bool upper = lane & m;      // this lane holds the pair's second value
+        b0 = upper ? o0 - b0 : b0 + o0;
+        b1 = upper ? o1 - b1 : b1 + o1;
+        b2 = upper ? o2 - b2 : b2 + o2;
+        b3 = upper ? o3 - b3 : b3 + o3;
+    }
+    return make_float4(b0 * 0.0625f, b1 * 0.0625f, b2 * 0.0625f, b3 * 0.0625f);
 }
 
 // Round to bf16 (nearest even) and store 4 values.
@@ -127,6 +152,46 @@ __device__ __forceinline__ void kv_store_bf16(uint16_t* dst, float4 v) {
     o.z = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v.z));
     o.w = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v.w));
     *(ushort4*)dst = o;
+}
+
+// q8_0 (ggml's block: fp16 scale d, 32 int8 codes, value d * q) of the
+// wave's 256 values into one row of 8 blocks of 34 bytes.  Block b holds dims
+// 32b..32b+31, i.e. lanes 8b..8b+7.  The quantisation is decided in fp32:
+// d = amax / 127 and q = round-half-away(y / d) (correctly rounded
+// divisions; q = 0 when d = 0), clamped to [-127, 127]; d is stored rounded
+// to fp16 (nearest even).  Must be called by all 64 lanes of a wave together.
+__device__ __forceinline__ void kv_store_q8_0(uint8_t* row, float4 y, int lane) {
+#pragma clang fp contract(off)
+    float am = fmaxf(fmaxf(fabsf(y.x), fabsf(y.y)), fmaxf(fabsf(y.z), fabsf(y.w)));
+    am = fmaxf(am, __shfl_xor(am, 1));
+    am = fmaxf(am, __shfl_xor(am, 2));
+    am = fmaxf(am, __shfl_xor(am, 4));
+    const float d = am / 127.0f;
+    const float yy[4] = {y.x, y.y, y.z, y.w};
+    uint32_t packed = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float q = d != 0.0f ? roundf(yy[e] / d) : 0.0f;
+        q = fminf(fmaxf(q, -127.0f), 127.0f);
+        packed |= (uint32_t)(uint8_t)(int8_t)(int)q << (8 * e);
+    }
+    uint8_t* blk = row + (lane >> 3) * 34;
+    uint16_t* codes = reinterpret_cast<uint16_t*>(blk + 2 + (lane & 7) * 4);   // 2-byte aligned
+    codes[0] = (uint16_t)(packed & 0xFFFF);
+    codes[1] = (uint16_t)(packed >> 16);
+    if ((lane & 7) == 0)
+        *reinterpret_cast<uint16_t*>(blk) = __builtin_bit_cast(uint16_t, static_cast<_Float16>(d));
+}
+
+// Stores one KV head's 256 values of one token (k after k_norm and RoPE, or
+// v) at row `row` of the pool: bf16, or Hadamard-rotated q8_0.
+__device__ __forceinline__ void kv_store_row(const KvPool& c, bool is_k, int64_t row, int lane, float4 x) {
+    void* pool = is_k ? c.k_pool : c.v_pool;
+    if (c.q8) {
+        kv_store_q8_0(static_cast<uint8_t*>(pool) + row * kKvQ8RowBytes, kv_hadamard256(x, lane), lane);
+    } else {
+        kv_store_bf16(static_cast<uint16_t*>(pool) + row * kKvHeadDim + lane * 4, x);
+    }
 }
 
 }  // namespace kva

@@ -104,8 +104,8 @@ __global__ void __launch_bounds__(256) untile32_kernel(const uint16_t* __restric
 }
 
 // KV-cache write for one full-attention layer (the routines and their
-// sources are in kva_kv.h).  One wave per (token, KV head): lane l holds dims
-// 4l..4l+3 of k and of v.
+// sources are in kva_kv.h): bf16 rows, or Hadamard-rotated q8_0 rows.  One
+// wave per (token, KV head): lane l holds dims 4l..4l+3 of k and of v.
 __global__ void __launch_bounds__(256) kv_write_kernel(KvWriteArgs a) {
     const int lane = threadIdx.x & 63;
     const int kvh = threadIdx.x >> 6;           // 4 waves = 4 KV heads
@@ -113,13 +113,13 @@ __global__ void __launch_bounds__(256) kv_write_kernel(KvWriteArgs a) {
     const int64_t p = a.pos0 + t;
     const int pg = kv_page(a.pool, p);
     if (pg < 0) return;
-    const int64_t off = kv_slot_offset(a.pool, pg, p, kvh, lane);
+    const int64_t row = kv_row_index(a.pool, pg, p, kvh);
     const float* kr = a.kv + (int64_t)t * a.ld_kv + kvh * kKvHeadDim;
     const float* vr = kr + kKvHeads * kKvHeadDim;
     const KvLane L = kv_lane_setup(lane, a.pool.k_gain, a.rope);
     const float4 k = kv_k_norm_rope(*(const float4*)(kr + lane * 4), lane, p, L, a.rope.n_rot, a.rope.eps);
-    kv_store_bf16(a.pool.k_pool + off, k);
-    kv_store_bf16(a.pool.v_pool + off, *(const float4*)(vr + lane * 4));
+    kv_store_row(a.pool, true, row, lane, k);
+    kv_store_row(a.pool, false, row, lane, *(const float4*)(vr + lane * 4));
 }
 
 __global__ void dequant_q8_0_kernel(const uint8_t* __restrict__ blocks, int64_t n_blocks,

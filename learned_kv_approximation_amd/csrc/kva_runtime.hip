@@ -647,6 +647,11 @@ kva_status check_paged_kv(const kva_paged_kv* cache, const float* k_gain) {
         return fail(KVA_ERR_ARG, "rope_base must be > 1");
     if ((int64_t)cache->n_logical * cache->page_size > INT32_MAX)
         return fail(KVA_ERR_SHAPE, "n_logical * page_size must stay below 2^31 positions");
+    if (cache->kv_type != KVA_KV_BF16 && cache->kv_type != KVA_KV_Q8_0_HADAMARD)
+        return fail(KVA_ERR_DTYPE, "unknown kv_type %d", cache->kv_type);
+    if (cache->kv_type == KVA_KV_Q8_0_HADAMARD &&
+        (((uintptr_t)cache->k_pool | (uintptr_t)cache->v_pool) % 2))
+        return fail(KVA_ERR_ARG, "q8_0 pools must be 2-byte aligned");
     return KVA_OK;
 }
 
@@ -654,6 +659,7 @@ KvPool make_pool(const kva_paged_kv* cache, const float* k_gain) {
     KvPool p{};
     p.k_pool = cache->k_pool; p.v_pool = cache->v_pool; p.page_table = cache->page_table;
     p.k_gain = k_gain; p.page_size = cache->page_size; p.n_pages = cache->n_pages;
+    p.q8 = cache->kv_type == KVA_KV_Q8_0_HADAMARD;
     return p;
 }
 

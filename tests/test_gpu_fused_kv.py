@@ -46,25 +46,31 @@ def _small_cfg(weight_dtype):
     return synth.config("tiny", weight_dtype=weight_dtype, heads=heads, n_in=512)
 
 
-def _pools(n, n_pages):
-    return [(torch.full((n_pages, 256, 4, 256), -1, dtype=torch.int16, device="cuda"),
-             torch.full((n_pages, 256, 4, 256), -1, dtype=torch.int16, device="cuda")) for _ in range(n)]
+def _pools(n, n_pages, kv_type=kva.KVA_KV_BF16):
+    """Poisoned pools: bf16 rows of 0xFFFF, or q8_0 rows of 0xFF bytes."""
+    if kv_type == kva.KVA_KV_BF16:
+        shape, dt, poison = (n_pages, 256, 4, 256), torch.int16, -1
+    else:
+        shape, dt, poison = (n_pages, 256, 4, 272), torch.uint8, 0xFF
+    return [(torch.full(shape, poison, dtype=dt, device="cuda"),
+             torch.full(shape, poison, dtype=dt, device="cuda")) for _ in range(n)]
 
 
-def _caches(pools, ptab_d, n_logical, n_pages):
+def _caches(pools, ptab_d, n_logical, n_pages, kv_type=kva.KVA_KV_BF16):
     return [kva.kva_paged_kv(kp.data_ptr(), vp.data_ptr(), ptab_d.data_ptr(), 256, n_pages, n_logical,
-                             4, 256, 64, 1.0e7, 1e-6) for kp, vp in pools]
+                             4, 256, 64, 1.0e7, 1e-6, kv_type) for kp, vp in pools]
 
 
-def fused_vs_chained(proj, cfg, xd, n, pos0, ptab, n_pages, gains_d):
+def fused_vs_chained(proj, cfg, xd, n, pos0, ptab, n_pages, gains_d, kv_type=kva.KVA_KV_BF16):
     """Runs both paths on x[:n] at positions pos0.. and checks bitwise equality.
     Returns (fused pools, chained head outputs)."""
     attn = [i for i, h in enumerate(cfg["heads"]) if h["kind"] == "attn" and h["out_dim"] == KV_W]
     ptab_d = torch.from_numpy(ptab).cuda()
-    pa, pb = _pools(len(attn), n_pages), _pools(len(attn), n_pages)
-    ca, cb = _caches(pa, ptab_d, len(ptab), n_pages), _caches(pb, ptab_d, len(ptab), n_pages)
+    pa, pb = _pools(len(attn), n_pages, kv_type), _pools(len(attn), n_pages, kv_type)
+    ca = _caches(pa, ptab_d, len(ptab), n_pages, kv_type)
+    cb = _caches(pb, ptab_d, len(ptab), n_pages, kv_type)
     st = kva.current_stream()
-    print(f"fused vs chained: {cfg['name']} {cfg['weight_dtype']} n={n} pos0={pos0}", flush=True)
+    print(f"fused vs chained: {cfg['name']} {cfg['weight_dtype']} n={n} pos0={pos0} kv_type={kv_type}", flush=True)
     outs_a = proj.alloc_outputs(n)
     proj.project(xd[:n], outs_a)
     for li, hi in enumerate(attn):
@@ -89,9 +95,10 @@ def fused_vs_chained(proj, cfg, xd, n, pos0, ptab, n_pages, gains_d):
     pos = pos0 + np.arange(n)
     pages = ptab[pos // 256]
     ok = (pages >= 0) & (pages < n_pages)
+    poison = -1 if kv_type == kva.KVA_KV_BF16 else 0xFF
     for kp, vp in pb:
         kn = kp.cpu().numpy()
-        written = ~(kn == -1).all(axis=-1)          # [page][slot][kv head]
+        written = ~(kn == poison).all(axis=-1)      # [page][slot][kv head]
         want = np.zeros_like(written)
         want[pages[ok], pos[ok] % 256] = True
         assert np.array_equal(written, want)
@@ -131,6 +138,38 @@ def test_small_fused_kv_equals_chained_and_oracle(dtype):
                 tol = 5e-2 if dtype != "f32" else 2e-2
                 bar = tol + 2.0 ** -9 * np.max(np.abs(y)) / np.sqrt(np.mean(y * y))
                 print(f"  {dtype} n={n} head {hi} {name}: max|err|/rms {err:.3e} (bar {bar:.3e})", flush=True)
+                assert err <= bar
+    proj.close()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "q8_0"])
+def test_small_fused_q8_0_kv_equals_chained_and_oracle(dtype):
+    """The same with Hadamard-rotated q8_0 pools: fused bitwise equal to the
+    chained write, and the dequantised rows within the q8_0 bound of the
+    oracle (checked on the bf16-weight projector only, where the oracle's K
+    and V are within 2e-2 of the GPU's)."""
+    cfg = _small_cfg(dtype)
+    w = synth.make_weights(cfg)
+    n_max = 1200
+    x = synth.make_input(cfg, n_tokens=n_max)
+    proj = kva.Projector(cfg, w, max_tokens=n_max)
+    xd = torch.from_numpy(x).cuda()
+    gains, ptab, n_pages = synth.make_kv_write_inputs(8192, n_layers=2, seed=7)
+    gains_d = torch.from_numpy(gains).cuda()
+    for n, pos0 in [(40, 300), (100, 5000), (n_max, 1234)]:
+        pools, _ = fused_vs_chained(proj, cfg, xd, n, pos0, ptab, n_pages, gains_d, kva.KVA_KV_Q8_0_HADAMARD)
+        attn = [i for i, h in enumerate(cfg["heads"]) if h["kind"] == "attn"]
+        want = oracle.project(cfg, w, x[:n], which=attn)
+        pos = pos0 + np.arange(n)
+        for li, hi in enumerate(attn):
+            k, v = ref.kv_write_q8_0_values(want[hi], gains[li], pos0)
+            for part, y in ((0, k), (1, v)):
+                got = ref.q8_0_block_values(pools[li][part].cpu().numpy()[ptab[pos // 256], pos % 256])
+                err = np.max(np.abs(got - y)) / np.sqrt(np.mean(y * y))
+                tol = 5e-2 if dtype != "f32" else 2e-2
+                # projector bar + q8_0 step (half of amax/127, amax <= ~4.5 RMS for these rows)
+                bar = tol + 0.5 * np.max(np.abs(y)) / 127 / np.sqrt(np.mean(y * y)) * 1.1
+                print(f"  {dtype} n={n} head {hi} {'kv'[part]}: max|err|/rms {err:.3e} (bar {bar:.3e})", flush=True)
                 assert err <= bar
     proj.close()
 

@@ -272,3 +272,70 @@ def test_kv_write_parity(pos0, n):
     used = np.zeros((n_pages, 256), dtype=bool)
     used[ptab[pos // 256], pos % 256] = True
     assert np.all(kpn[~used] == 0xFFFF) and np.all(vpn[~used] == 0xFFFF)
+
+
+def _q8_rows_check(got_rows, want, where):
+    """got_rows [..., 272] q8_0 bytes vs float64 rotated values [..., 256].
+    Every dequantised value lies within the q8_0 bound of the float64 value
+    (half a step, the fp16 storage of the scale, and the fp32 arithmetic before
+    the decision); codes equal the oracle's except where the oracle's own
+    y / d sits within that fp32 slack of a rounding tie."""
+    gd = ref.q8_0_block_values(got_rows)
+    d_bits, q = ref.q8_0_quantize(want)
+    blk = want.reshape(want.shape[:-1] + (8, 32))
+    amax = np.abs(blk).max(-1)
+    d32 = amax / 127.0
+    d16 = ref.f16_bits_to_f64(d_bits)
+    slack = 2e-6 * amax                                 # fp32 Hadamard / norm / RoPE error, generous
+    bound = 0.5 * d32 + np.abs(d16 - d32) * 127 + slack
+    err = np.abs(gd.reshape(blk.shape) - blk)
+    assert np.all(err <= bound[..., None] * (1 + 1e-9)), (where, float(np.max(err / bound[..., None])))
+    gq = np.ascontiguousarray(got_rows.reshape(got_rows.shape[:-1] + (8, 34))[..., 2:]).view(np.int8)
+    diff = gq != q
+    t = blk / np.where(d32 == 0, 1, d32)[..., None]
+    near_tie = np.abs(np.abs(t - np.trunc(t)) - 0.5) < (slack / np.where(d32 == 0, 1, d32))[..., None] + 1e-4
+    assert np.all(~diff | near_tie), where
+    assert np.all(np.abs(gq.astype(int) - q.astype(int)) <= 1), where
+    return float(np.mean(diff))
+
+
+@pytest.mark.parametrize("integer", [True, False])
+def test_kv_write_q8_0_hadamard_parity(integer):
+    """Hadamard-rotated q8_0 KV write.  Integer-valued inputs make V's rotation
+    exact in fp32, so V's scales and codes must equal the oracle's bit for bit;
+    K (k_norm, RoPE) and real-valued inputs are held to the q8_0 bound."""
+    pos0, n = 1000, 700
+    n_logical = (pos0 + n + 255) // 256
+    gains, ptab, n_pages = synth.make_kv_write_inputs(pos0 + n, n_layers=1)
+    if integer:
+        rng = np.random.default_rng(21)
+        kv = np.round(rng.standard_normal((n, 2048)) * 20).astype(np.float32)
+        kv[7, 1024:1024 + 256] = 0.0                   # an all-zero V head: every block has d = 0, codes 0
+    else:
+        kv = synth.make_kv_rows(n, scale=3.0)
+    kp = torch.full((n_pages, 256, 4, 272), 0xFF, dtype=torch.uint8, device="cuda")
+    vp = torch.full((n_pages, 256, 4, 272), 0xFF, dtype=torch.uint8, device="cuda")
+    ptab_d = torch.from_numpy(ptab).cuda()
+    cache = kva.kva_paged_kv(kp.data_ptr(), vp.data_ptr(), ptab_d.data_ptr(), 256, n_pages, len(ptab),
+                             4, 256, 64, 1.0e7, 1e-6, kva.KVA_KV_Q8_0_HADAMARD)
+    kv_d = torch.from_numpy(kv).cuda()
+    g_d = torch.from_numpy(gains[0]).cuda()
+    print(f"q8_0 KV write: integer={integer} pos0={pos0} n={n}", flush=True)
+    kva.kva_attn_kv_write(kv_d.data_ptr(), kv.shape[1], n, pos0, g_d.data_ptr(), cache, kva.current_stream())
+    torch.cuda.synchronize()
+    kpn, vpn = kp.cpu().numpy(), vp.cpu().numpy()
+    k, v = ref.kv_write_q8_0_values(kv, gains[0], pos0)
+    pos = pos0 + np.arange(n)
+    gk = kpn[ptab[pos // 256], pos % 256]
+    gv = vpn[ptab[pos // 256], pos % 256]
+    if integer:
+        want_v = ref.q8_0_block_bytes(*ref.q8_0_quantize(v))
+        assert np.array_equal(gv, want_v)
+        assert not gv[7, 0].any()
+    fk = _q8_rows_check(gk, k, "k")
+    fv = _q8_rows_check(gv, v, "v")
+    print(f"  codes differing from the oracle's: k {fk:.2e}, v {fv:.2e}", flush=True)
+    assert fk < 1e-3 and fv < 1e-3
+    used = np.zeros((n_pages, 256), dtype=bool)
+    used[ptab[pos // 256], pos % 256] = True
+    assert np.all(kpn[~used] == 0xFF) and np.all(vpn[~used] == 0xFF)

@@ -203,7 +203,7 @@ def test_r3_projection_chained_into_paged_kv_cache(r3bf16):
     proj.close()
 
 
-def _fused_r3(cfg, w, cases):
+def _fused_r3(cfg, w, cases, kv_type=kva.KVA_KV_BF16):
     from test_gpu_fused_kv import fused_vs_chained
     attn = [i for i, h in enumerate(cfg["heads"]) if h["kind"] == "attn"]
     gains, ptab, n_pages = synth.make_kv_write_inputs(N_PROMPT, n_layers=len(attn), seed=cfg["seed"])
@@ -213,7 +213,7 @@ def _fused_r3(cfg, w, cases):
     xd = torch.from_numpy(x).cuda()
     gains_d = torch.from_numpy(gains).cuda()
     for n, pos0 in cases:
-        fused_vs_chained(proj, cfg, xd, n, pos0, ptab, n_pages, gains_d)
+        fused_vs_chained(proj, cfg, xd, n, pos0, ptab, n_pages, gains_d, kv_type)
     proj.close()
 
 
@@ -227,3 +227,9 @@ def test_r3_fused_kv_epilogue_equals_chained(r3bf16):
 def test_r3_q8_0_fused_kv_epilogue_equals_chained(r3q8):
     cfg, w, _ = r3q8
     _fused_r3(cfg, w, [(1024, 7 * 1024), (64, 300)])
+
+
+def test_r3_fused_q8_0_kv_cache_equals_chained(r3bf16):
+    """Hadamard-rotated q8_0 pools at r3 scale, fused vs chained."""
+    cfg, w, _ = r3bf16
+    _fused_r3(cfg, w, [(8192, 16384), (100, N_PROMPT - 100)], kv_type=kva.KVA_KV_Q8_0_HADAMARD)
