@@ -470,3 +470,102 @@ def kv_write_q8_0(kv, gain, pos0, page_table, k_pool, v_pool, page_size: int = 2
         k_pool[pg, sl] = kb[t]
         v_pool[pg, sl] = vb[t]
     return k_pool, v_pool
+
+
+# --------------------------------------------------------------------------
+# gated-DeltaNet state update ([KVA] "What the hell?": after projection the
+# engine runs, for the DeltaNet layers, conv + silu, l2-norm and the DeltaNet
+# scan over the approximated tokens; the table of predicted inputs gives
+# in_proj_qkv (q, k, v before conv/silu) 10240, in_proj_a 48, in_proj_b 48).
+# The pages name the steps but not their formulas.  Readings:
+#  - widths: 48 value heads (one a and one b per value head) of 128 dims
+#    (v = 6144), so q and k take 2048 each: 16 key heads of 128; value head h
+#    reads key head h // 3 (consecutive grouping); qkv order q | k | v;
+#  - conv: causal depthwise convolution of width 4 over the token axis on all
+#    10240 qkv channels, per-channel weights w[c][0..3] (w[c][3] multiplies
+#    the current token), no bias, the previous 3 tokens' raw qkv as the
+#    carried conv state (zeros at the start of a sequence); then SiLU;
+#  - l2-norm: k / sqrt(sum(k^2) + 1e-6) per key head (q likewise, but q only
+#    feeds the layer's output, which the update does not produce);
+#  - gates (the gated delta rule's Mamba-2-style decay): per value head and
+#    token, log-decay g = -exp(A_log) * softplus(a + dt_bias), decay
+#    alpha = exp(g), write strength beta = sigmoid(b);
+#  - gated delta rule on the state S [d_v][d_k] (S maps a key to a value):
+#    S_t = alpha_t * S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T;
+#  - the update's results are the state after the last token and the new
+#    conv state (the last 3 raw qkv rows); per-token outputs are not formed.
+# Parity for trained weights is unpinned (none of these formulas is on the
+# pages); the pins below check the functions against their definitions.
+
+DN_QKV, DN_NK, DN_NV, DN_HD, DN_CONV = 10240, 16, 48, 128, 4
+
+
+def causal_conv_silu(x: np.ndarray, w: np.ndarray, conv_state: np.ndarray):
+    """x [T, C] raw rows, w [C, W], conv_state [W-1, C] (oldest first).
+    Returns (silu(conv) [T, C], new conv state [W-1, C])."""
+    x = np.asarray(x, dtype=np.float64)
+    W = w.shape[1]
+    xp = np.concatenate([np.asarray(conv_state, dtype=np.float64), x], axis=0)
+    T = x.shape[0]
+    out = np.zeros_like(x)
+    for tau in range(W):
+        out += xp[tau:tau + T] * np.asarray(w, dtype=np.float64)[:, tau][None, :]
+    return silu(out), xp[T:].copy()
+
+
+def l2norm(x: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
+def softplus(x: np.ndarray) -> np.ndarray:
+    x = np.asarray(x, dtype=np.float64)
+    return np.logaddexp(0.0, x)
+
+
+def sigmoid(x: np.ndarray) -> np.ndarray:
+    """1 / (1 + exp(-x)), evaluated as exp(x) / (1 + exp(x)) for x < 0 so that
+    neither branch overflows or cancels."""
+    x = np.asarray(x, dtype=np.float64)
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def deltanet_prepare(mixer_in: np.ndarray, conv_w: np.ndarray, a_log: np.ndarray, dt_bias: np.ndarray,
+                     conv_state: np.ndarray, n_k: int = DN_NK, n_v: int = DN_NV, hd: int = DN_HD):
+    """From one DeltaNet head's predicted inputs [T, qkv | a | b] to the scan's
+    inputs: unit keys k [T, n_k, hd], values v [T, n_v, hd], decays alpha and
+    strengths beta [T, n_v], and the new conv state."""
+    m = np.asarray(mixer_in, dtype=np.float64)
+    qkv_w = 2 * n_k * hd + n_v * hd
+    act, new_conv = causal_conv_silu(m[:, :qkv_w], conv_w, conv_state)
+    T = m.shape[0]
+    k = l2norm(act[:, n_k * hd:2 * n_k * hd].reshape(T, n_k, hd))
+    v = act[:, 2 * n_k * hd:].reshape(T, n_v, hd)
+    a = m[:, qkv_w:qkv_w + n_v]
+    b = m[:, qkv_w + n_v:qkv_w + 2 * n_v]
+    g = -np.exp(np.asarray(a_log, dtype=np.float64))[None, :] * softplus(a + np.asarray(dt_bias)[None, :])
+    return k, v, np.exp(g), sigmoid(b), new_conv
+
+
+def gated_delta_scan(S0: np.ndarray, k: np.ndarray, v: np.ndarray, alpha: np.ndarray, beta: np.ndarray,
+                     group: int = 3) -> np.ndarray:
+    """S0 [n_v, dv, dk]; k [T, n_k, dk] (value head h reads key head h // group);
+    v [T, n_v, dv]; alpha, beta [T, n_v].  Token by token:
+    S <- alpha S (I - beta k k^T) + beta v k^T.  Returns the final state."""
+    S = np.array(S0, dtype=np.float64, copy=True)
+    kv_map = np.arange(S.shape[0]) // group
+    for t in range(k.shape[0]):
+        kk = k[t][kv_map]                                   # [n_v, dk]
+        Sk = np.einsum("hvk,hk->hv", S, kk)                 # S k
+        a, b = alpha[t][:, None, None], beta[t][:, None, None]
+        S = a * S - a * b * Sk[:, :, None] * kk[:, None, :] + b * v[t][:, :, None] * kk[:, None, :]
+    return S
+
+
+def deltanet_update(mixer_in, conv_w, a_log, dt_bias, conv_state, S0, n_k: int = DN_NK,
+                    n_v: int = DN_NV, hd: int = DN_HD):
+    """One DeltaNet layer's state update over the rows of mixer_in.
+    Returns (final state [n_v, hd, hd], new conv state [3, qkv])."""
+    k, v, alpha, beta, new_conv = deltanet_prepare(mixer_in, conv_w, a_log, dt_bias, conv_state, n_k, n_v, hd)
+    return gated_delta_scan(S0, k, v, alpha, beta, n_v // n_k), new_conv

@@ -252,3 +252,39 @@ def make_kv_rows(n_tokens: int, width: int = 2 * KV_HEADS * KV_HEAD_DIM, seed: i
     """Stand-alone f32 k|v rows [n_tokens, 2048] for exercising the cache write."""
     rng = np.random.default_rng(seed + 3000)
     return (rng.standard_normal((n_tokens, width), dtype=np.float32) * np.float32(scale))
+
+
+# ---------------------------------------------------------------- DeltaNet layer inputs
+
+DN_QKV, DN_HEADS_V, DN_HEAD_DIM, DN_CONV = 10240, 48, 128, 4
+
+
+def make_deltanet_params(n_layers: int, seed: int = 6):
+    """Per DeltaNet layer, the parameters the state update uses that the
+    projector does not produce, drawn like a freshly initialised layer:
+    depthwise conv weights [10240][4] ~ U(-1/2, 1/2); decay rates
+    A = exp(A_log) log-uniform in [0.01, 16]; dt_bias = softplus^-1(dt) with
+    dt log-uniform in [1e-3, 0.1].  fp32."""
+    rng = np.random.default_rng(seed + 4000)
+    conv_w = rng.uniform(-0.5, 0.5, (n_layers, DN_QKV, DN_CONV)).astype(np.float32)
+    a_log = rng.uniform(math.log(0.01), math.log(16.0), (n_layers, DN_HEADS_V)).astype(np.float32)
+    dt = np.exp(rng.uniform(math.log(1e-3), math.log(0.1), (n_layers, DN_HEADS_V)))
+    dt_bias = (dt + np.log(-np.expm1(-dt))).astype(np.float32)
+    return conv_w, a_log, dt_bias
+
+
+def make_deltanet_state(n_layers: int, seed: int = 6, scale: float = 0.05):
+    """Carried state before a ubatch: conv state [3][10240] (raw rows like the
+    projector's outputs) and recurrent states [48][128][128] ~ N(0, scale^2)."""
+    rng = np.random.default_rng(seed + 5000)
+    conv = rng.standard_normal((n_layers, DN_CONV - 1, DN_QKV), dtype=np.float32)
+    S = (rng.standard_normal((n_layers, DN_HEADS_V, DN_HEAD_DIM, DN_HEAD_DIM), dtype=np.float32)
+         * np.float32(scale))
+    return conv, S
+
+
+def make_deltanet_rows(n_tokens: int, seed: int = 6, width: int = DN_QKV + 2 * DN_HEADS_V) -> np.ndarray:
+    """Stand-alone DeltaNet head outputs [n_tokens][qkv | a | b] ~ N(0, 1), fp32
+    (the projector's outputs have unit scale)."""
+    rng = np.random.default_rng(seed + 6000)
+    return rng.standard_normal((n_tokens, width), dtype=np.float32)

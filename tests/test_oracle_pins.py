@@ -520,6 +520,106 @@ def test_q8_0_kv_write_layout_and_rotation():
     assert np.all(kp[~used] == 0xFF)
 
 
+# ------------------------------------------------------------------ gated-DeltaNet state update
+
+def test_deltanet_conv_matches_torch_conv1d():
+    rng = np.random.default_rng(31)
+    T, C = 9, 40
+    x = rng.standard_normal((T, C))
+    w = rng.standard_normal((C, 4))
+    st = rng.standard_normal((3, C))
+    got, new = ref.causal_conv_silu(x, w, st)
+    xp = torch.from_numpy(np.concatenate([st, x]).T[None])             # [1, C, T+3]
+    conv = F.conv1d(xp, torch.from_numpy(w)[:, None, :], groups=C)     # library special case
+    assert np.allclose(got, F.silu(conv)[0].T.numpy(), rtol=1e-13, atol=1e-13)
+    assert np.array_equal(new, x[-3:])
+    # fewer tokens than the window: the new state keeps older rows
+    got2, new2 = ref.causal_conv_silu(x[:2], w, st)
+    assert np.array_equal(new2, np.concatenate([st[2:], x[:2]]))
+
+
+def test_deltanet_gates_and_norm_match_torch():
+    rng = np.random.default_rng(32)
+    z = rng.standard_normal(1000) * 30
+    sp = F.softplus(torch.from_numpy(z)).numpy()        # torch returns x itself above x = 20
+    lo = z <= 20
+    assert np.allclose(ref.softplus(z[lo]), sp[lo], rtol=1e-13, atol=1e-300)
+    assert np.all(np.abs(ref.softplus(z[~lo]) - z[~lo]) <= np.exp(-z[~lo]) + 1e-14 * z[~lo])
+    assert np.allclose(ref.sigmoid(z), torch.sigmoid(torch.from_numpy(z)).numpy(), rtol=1e-13, atol=1e-300)
+    k = rng.standard_normal((20, 16, 128))
+    n = np.linalg.norm(ref.l2norm(k), axis=-1)
+    assert np.allclose(n, 1.0, atol=1e-9)
+    assert np.allclose(ref.l2norm(k), F.normalize(torch.from_numpy(k), dim=-1, eps=0).numpy(), rtol=1e-6)
+
+
+def _random_scan_inputs(rng, T, n_v=6, n_k=2, d=8):
+    k = ref.l2norm(rng.standard_normal((T, n_k, d)))
+    v = rng.standard_normal((T, n_v, d))
+    alpha = rng.uniform(0.5, 1.0, (T, n_v))
+    beta = rng.uniform(0.0, 1.0, (T, n_v))
+    S0 = rng.standard_normal((n_v, d, d))
+    return S0, k, v, alpha, beta
+
+
+def test_gated_delta_scan_equals_product_of_transitions():
+    """Closed form of the recurrence: S_T = S_0 M_1 ... M_T + sum_t beta_t v_t
+    k_t^T M_{t+1} ... M_T with M_t = alpha_t (I - beta_t k_t k_t^T), built by
+    explicit matrix products (value head h reads key head h // 3)."""
+    rng = np.random.default_rng(33)
+    T, d = 7, 8
+    S0, k, v, alpha, beta = _random_scan_inputs(rng, T, d=d)
+    got = ref.gated_delta_scan(S0, k, v, alpha, beta, group=3)
+    for h in range(6):
+        M = [alpha[t, h] * (np.eye(d) - beta[t, h] * np.outer(k[t, h // 3], k[t, h // 3])) for t in range(T)]
+        want = S0[h].copy()
+        for t in range(T):
+            want = want @ M[t]
+        for t in range(T):
+            tail = np.eye(d)
+            for s in range(t + 1, T):
+                tail = tail @ M[s]
+            want += beta[t, h] * np.outer(v[t, h], k[t, h // 3]) @ tail
+        assert np.allclose(got[h], want, rtol=1e-12, atol=1e-12)
+
+
+def test_gated_delta_scan_closed_cases():
+    rng = np.random.default_rng(34)
+    S0, k, v, alpha, beta = _random_scan_inputs(rng, 5)
+    # beta = 0: pure decay
+    got = ref.gated_delta_scan(S0, k, v, alpha, np.zeros_like(beta))
+    assert np.allclose(got, S0 * np.prod(alpha, axis=0)[:, None, None], rtol=1e-13)
+    # alpha = beta = 1 with orthonormal keys from a zero state: the state
+    # stores every association exactly, S k_i = v_i
+    d, n = 16, 10
+    Q, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    keys = Q[:n][:, None, :]                                 # [n, 1 key head, d]
+    vals = rng.standard_normal((n, 3, d))
+    S = ref.gated_delta_scan(np.zeros((3, d, d)), keys, vals, np.ones((n, 3)), np.ones((n, 3)))
+    for i in range(n):
+        assert np.allclose(S @ keys[i, 0], vals[i], atol=1e-12)
+    # one token: S_1 = alpha S_0 - alpha beta S_0 k k^T + beta v k^T
+    one = ref.gated_delta_scan(S0, k[:1], v[:1], alpha[:1], beta[:1])
+    kk = k[0][np.arange(6) // 3]
+    want = (alpha[0][:, None, None] * (S0 - beta[0][:, None, None] * np.einsum("hvk,hk,hj->hvj", S0, kk, kk))
+            + beta[0][:, None, None] * np.einsum("hv,hk->hvk", v[0], kk))
+    assert np.allclose(one, want, rtol=1e-13, atol=1e-13)
+
+
+def test_deltanet_update_splits_at_any_token():
+    """Carrying the conv state and the recurrent state across calls gives the
+    same result as one call (the update is a sequential recurrence)."""
+    conv_w, a_log, dt_bias = synth.make_deltanet_params(1)
+    conv0, S0 = synth.make_deltanet_state(1)
+    rows = synth.make_deltanet_rows(40)
+    S_all, c_all = ref.deltanet_update(rows, conv_w[0], a_log[0], dt_bias[0], conv0[0], S0[0])
+    S_a, c_a = ref.deltanet_update(rows[:17], conv_w[0], a_log[0], dt_bias[0], conv0[0], S0[0])
+    S_b, c_b = ref.deltanet_update(rows[17:], conv_w[0], a_log[0], dt_bias[0], c_a, S_a)
+    assert np.allclose(S_b, S_all, rtol=1e-12, atol=1e-14) and np.array_equal(c_b, c_all)
+    # widths: q | k | v = 2048 | 2048 | 6144 and a, b = 48 each
+    assert ref.DN_QKV == 2 * ref.DN_NK * ref.DN_HD + ref.DN_NV * ref.DN_HD == 10240
+    assert rows.shape[1] == 10240 + 48 + 48
+
+
 # ------------------------------------------------------------------ planted mistakes
 
 def _mutants():
