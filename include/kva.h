@@ -256,6 +256,48 @@ kva_status kva_project_ubatch_kv(kva_ctx* ctx, const float* x, int32_t n_tokens,
                                  float* const* head_out, int64_t pos0,
                                  const kva_attn_dest* attn, int32_t n_attn, void* stream);
 
+/* One gated-DeltaNet layer for kva_deltanet_update. */
+typedef struct {
+    const float* mixer_in;  /* device [n_tokens][ld_in]: the projector's output for
+                               this layer, q|k|v (raw, before conv) then a then b */
+    int64_t ld_in;          /* >= (2*n_k_heads + n_v_heads)*head_dim + 2*n_v_heads  */
+    const float* conv_w;    /* device [qkv channels][4], 16-byte aligned             */
+    const float* a_log;     /* device [n_v_heads]                                    */
+    const float* dt_bias;   /* device [n_v_heads]                                    */
+    float* conv_state;      /* device [3][qkv channels], in/out: raw rows of the 3
+                               tokens before the call, oldest first (zeros at the
+                               start of a sequence)                                  */
+    float* state;           /* device [n_v_heads][head_dim][head_dim] fp32, in/out:
+                               S[h][i][j] maps key dim j to value dim i             */
+} kva_deltanet_layer;
+
+/* The DeltaNet layers' state update after a projection ("Qwen3.8-27B-KVA"
+ * card, "What the hell?": conv + silu, l2-norm and the DeltaNet scan over the
+ * approximated tokens).  The card names the steps, not their formulas; this
+ * is the gated delta rule (Qwen3-Next-style gated DeltaNet layer):
+ *   qkv channels: q (n_k_heads*head_dim) | k (same) | v (n_v_heads*head_dim);
+ *   c = causal depthwise conv of width 4 over tokens (conv_w[ch][3] multiplies
+ *       the current token, [0] the token 3 back; rows before the call come
+ *       from conv_state), then SiLU;
+ *   k_h = c_k,h / sqrt(|c_k,h|^2 + 1e-6) per key head; v_h = c_v,h;
+ *   per value head h and token: alpha = exp(-exp(a_log[h]) *
+ *       softplus(a[h] + dt_bias[h])), beta = sigmoid(b[h]);
+ *   value head h reads key head h / (n_v_heads / n_k_heads), and
+ *   S_h <- alpha S_h (I - beta k k^T) + beta v k^T over the tokens in order.
+ * On return (on the stream) state holds S after the last token and
+ * conv_state the last 3 raw qkv rows of [old conv_state ; mixer_in rows].
+ * q's conv is not formed (the layer's output is not produced here).  An
+ * engine that runs the ubatch's last token exactly passes n_tokens - 1
+ * rows.  All layers share n_tokens and the head counts; any number of layers
+ * (launched 32 at a time).  head_dim must be 128 (KVA_ERR_UNSUPPORTED);
+ * KVA_ERR_SHAPE for inconsistent counts or a short ld_in; KVA_ERR_ARG for
+ * NULL or misaligned pointers.  Buffers of different layers must not alias.
+ * The scan runs in fp32 with the MFMA operands (unit keys, the chunk-start
+ * state and the chunk's corrections) rounded to fp16; the state stays fp32.
+ * Asynchronous on `stream`. */
+kva_status kva_deltanet_update(const kva_deltanet_layer* layers, int32_t n_layers, int32_t n_tokens,
+                               int32_t n_k_heads, int32_t n_v_heads, int32_t head_dim, void* stream);
+
 /* Test hook: dequantises n_blocks q8_0 blocks (device, 34 bytes each: fp16
  * scale d, then 32 int8 codes q; format from [KVA] "Projector quantization and
  * flash-attn") to fp32 (device, 32*n_blocks values): out = float(d) * q,

@@ -74,6 +74,11 @@ class kva_attn_dest(ctypes.Structure):
     _fields_ = [("k_gain", c_vp), ("cache", kva_paged_kv)]
 
 
+class kva_deltanet_layer(ctypes.Structure):
+    _fields_ = [("mixer_in", c_vp), ("ld_in", c_i64), ("conv_w", c_vp), ("a_log", c_vp), ("dt_bias", c_vp),
+                ("conv_state", c_vp), ("state", c_vp)]
+
+
 class KvaError(RuntimeError):
     def __init__(self, status: int, where: str = ""):
         self.status = status
@@ -91,6 +96,7 @@ _SIGS = {
     "kva_project_ubatch_kv": (c_i32, [c_vp, c_vp, c_i32, ctypes.POINTER(c_vp), c_i64,
                                       ctypes.POINTER(kva_attn_dest), c_i32, c_vp]),
     "kva_destroy": (c_i32, [c_vp]),
+    "kva_deltanet_update": (c_i32, [ctypes.POINTER(kva_deltanet_layer), c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
     "kva_attn_kv_write": (c_i32, [c_vp, c_i64, c_i32, c_i64, c_vp, ctypes.POINTER(kva_paged_kv), c_vp]),
     "kva_debug_dequant_q8_0": (c_i32, [c_vp, c_i64, c_vp, c_vp]),
     "kva_debug_dequant_q8_0_f16": (c_i32, [c_vp, c_i64, c_vp, c_vp]),
@@ -157,6 +163,14 @@ def kva_project_ubatch_kv(ctx: int, x_ptr: int, n_tokens: int, head_out_ptrs, po
     d = (kva_attn_dest * max(1, len(dests)))(*dests)
     _check(lib().kva_project_ubatch_kv(ctx, x_ptr, n_tokens, arr, pos0, d, len(dests), stream),
            "kva_project_ubatch_kv")
+
+
+def kva_deltanet_update(layers, n_tokens: int, n_k_heads: int = 16, n_v_heads: int = 48, head_dim: int = 128,
+                        stream: int = 0) -> None:
+    """layers: sequence of kva_deltanet_layer."""
+    arr = (kva_deltanet_layer * max(1, len(layers)))(*layers)
+    _check(lib().kva_deltanet_update(arr, len(layers), n_tokens, n_k_heads, n_v_heads, head_dim, stream),
+           "kva_deltanet_update")
 
 
 def kva_destroy(ctx: int) -> None:

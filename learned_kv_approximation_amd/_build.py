@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkva.so")
-SOURCES = ["kva_runtime.hip", "kva_gemm.hip", "kva_attn.hip", "kva_misc.hip"]
+SOURCES = ["kva_runtime.hip", "kva_gemm.hip", "kva_attn.hip", "kva_misc.hip", "kva_deltanet.hip"]
 ARCH = "gfx950"
 
 

@@ -265,6 +265,32 @@ struct KvWriteArgs {
 };
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
 
+// Gated-DeltaNet state update (kva_deltanet.hip).  Key and value heads of
+// kDnHeadDim, causal conv of width kDnConv; one launch takes up to
+// kMaxDnLayers layers.
+constexpr int kDnHeadDim = 128;
+constexpr int kDnConv = 4;
+constexpr int kMaxDnLayers = 32;
+
+struct DnLayer {
+    const float* x;          // [n_tokens][ld]: q|k|v raw, then a (n_v), then b (n_v)
+    int64_t ld;
+    const float* conv_w;     // [q|k|v channels][kDnConv], 16-byte aligned
+    const float* a_log;      // [n_v]
+    const float* dt_bias;    // [n_v]
+    float* conv_state;       // [kDnConv - 1][q|k|v channels], in/out
+    float* state;            // [n_v][kDnHeadDim (v)][kDnHeadDim (k)] fp32, in/out
+};
+
+struct DnArgs {
+    int32_t n_tokens;
+    int32_t n_layers;
+    int32_t n_k;             // key heads (q and k)
+    int32_t n_v;             // value heads, a multiple of n_k
+    DnLayer layer[kMaxDnLayers];
+};
+hipError_t launch_deltanet_update(const DnArgs& a, hipStream_t stream);
+
 hipError_t launch_dequant_q8_0(const void* blocks, int64_t n_blocks, float* out, hipStream_t stream);
 hipError_t launch_dequant_q8_0_f16(const void* blocks, int64_t n_blocks, uint16_t* out, hipStream_t stream);
 hipError_t launch_dequant_q4_0_f16(const void* blocks, int64_t n_blocks, uint16_t* out, hipStream_t stream);

@@ -834,6 +834,39 @@ kva_status kva_attn_kv_write(const float* kv, int64_t ld_kv, int32_t n, int64_t 
     return KVA_OK;
 }
 
+kva_status kva_deltanet_update(const kva_deltanet_layer* layers, int32_t n_layers, int32_t n_tokens,
+                               int32_t n_k_heads, int32_t n_v_heads, int32_t head_dim, void* stream) {
+    if (n_layers < 0 || n_tokens < 0) return fail(KVA_ERR_SHAPE, "negative n_layers or n_tokens");
+    if (n_layers == 0 || n_tokens == 0) return KVA_OK;
+    if (!layers) return fail(KVA_ERR_ARG, "NULL layers");
+    if (head_dim != kDnHeadDim) return fail(KVA_ERR_UNSUPPORTED, "head_dim must be %d", kDnHeadDim);
+    if (n_k_heads <= 0 || n_v_heads <= 0 || n_v_heads % n_k_heads)
+        return fail(KVA_ERR_SHAPE, "n_v_heads must be a positive multiple of n_k_heads");
+    const int64_t qkv = (int64_t)(2 * n_k_heads + n_v_heads) * head_dim;
+    for (int l = 0; l < n_layers; ++l) {
+        const kva_deltanet_layer& L = layers[l];
+        if (!L.mixer_in || !L.conv_w || !L.a_log || !L.dt_bias || !L.conv_state || !L.state)
+            return fail(KVA_ERR_ARG, "layer %d: NULL pointer", l);
+        if (L.ld_in < qkv + 2 * n_v_heads) return fail(KVA_ERR_SHAPE, "layer %d: ld_in too small", l);
+        if ((uintptr_t)L.conv_w % 16 || (uintptr_t)L.mixer_in % 4 || (uintptr_t)L.state % 4 ||
+            (uintptr_t)L.conv_state % 4)
+            return fail(KVA_ERR_ARG, "layer %d: misaligned pointer (conv_w needs 16 bytes)", l);
+    }
+    for (int l0 = 0; l0 < n_layers; l0 += kMaxDnLayers) {
+        DnArgs a{};
+        a.n_tokens = n_tokens;
+        a.n_layers = n_layers - l0 < kMaxDnLayers ? n_layers - l0 : kMaxDnLayers;
+        a.n_k = n_k_heads;
+        a.n_v = n_v_heads;
+        for (int l = 0; l < a.n_layers; ++l) {
+            const kva_deltanet_layer& L = layers[l0 + l];
+            a.layer[l] = DnLayer{L.mixer_in, L.ld_in, L.conv_w, L.a_log, L.dt_bias, L.conv_state, L.state};
+        }
+        LAUNCH(launch_deltanet_update(a, static_cast<hipStream_t>(stream)));
+    }
+    return KVA_OK;
+}
+
 kva_status kva_debug_dequant_q8_0(const void* blocks, int64_t n_blocks, float* out, void* stream) {
     if (!blocks || !out) return fail(KVA_ERR_ARG, "NULL argument");
     if (n_blocks < 0) return fail(KVA_ERR_SHAPE, "negative n_blocks");

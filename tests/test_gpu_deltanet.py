@@ -1,0 +1,153 @@
+"""GPU parity for the gated-DeltaNet state update (kva_deltanet_update)
+against the float64 oracle (oracle/ref.py: deltanet_update), on the same fp32
+inputs.
+
+Bars: the new conv state is a copy of input rows (bit-exact); the recurrent
+state must satisfy max|S_gpu - S_ref| <= 2e-2 * RMS(S_ref) per layer (the
+projector's own bar) and RMS(S_gpu - S_ref) <= 4e-3 * RMS(S_ref).  Where the
+error comes from: every MFMA operand (unit keys, the chunk-start state, the
+chunk's corrections) is rounded once to fp16 (relative error <= 2^-12 each);
+a chunk's update sums 32-128 such products with fp32 accumulation, and the
+state carries each chunk's rounding forward under the decay, so the RMS error
+grows roughly with the square root of the number of chunks that survive the
+decay (32 at 1024 tokens): ~2^-12 * sqrt(32) * a few ~ 1e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import learned_kv_approximation_amd as kva
+import synth
+from oracle import ref
+
+pytestmark = pytest.mark.gpu
+TOL_MAX, TOL_RMS = 2e-2, 4e-3
+LD = 10240 + 2 * 48
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _layers(rows, conv_w, a_log, dt_bias, conv, S):
+    """Device copies and the kva_deltanet_layer structs (one per layer)."""
+    dev = {k: [torch.from_numpy(np.ascontiguousarray(a[i])).cuda() for i in range(len(a))]
+           for k, a in (("x", rows), ("w", conv_w), ("al", a_log), ("dt", dt_bias), ("c", conv), ("S", S))}
+    ls = [kva.kva_deltanet_layer(dev["x"][i].data_ptr(), rows[i].shape[1], dev["w"][i].data_ptr(),
+                                 dev["al"][i].data_ptr(), dev["dt"][i].data_ptr(), dev["c"][i].data_ptr(),
+                                 dev["S"][i].data_ptr()) for i in range(len(rows))]
+    return ls, dev
+
+
+def _check_state(got, want, where):
+    rms = np.sqrt(np.mean(want * want))
+    err = got.astype(np.float64) - want
+    mx, sd = float(np.max(np.abs(err)) / rms), float(np.sqrt(np.mean(err * err)) / rms)
+    print(f"  {where}: state max|err|/rms {mx:.3e}, rms err/rms {sd:.3e}", flush=True)
+    assert mx <= TOL_MAX and sd <= TOL_RMS, (where, mx, sd)
+
+
+@pytest.mark.parametrize("T,n_layers", [(1, 2), (5, 2), (32, 2), (33, 2), (100, 2), (1024, 1)])
+def test_deltanet_update_matches_oracle(T, n_layers):
+    conv_w, a_log, dt_bias = synth.make_deltanet_params(n_layers)
+    conv, S = synth.make_deltanet_state(n_layers)
+    rows = [synth.make_deltanet_rows(T, seed=6 + i) for i in range(n_layers)]
+    print(f"deltanet T={T} layers={n_layers}", flush=True)
+    ls, dev = _layers(rows, conv_w, a_log, dt_bias, conv, S)
+    kva.kva_deltanet_update(ls, T, stream=kva.current_stream())
+    torch.cuda.synchronize()
+    for i in range(n_layers):
+        S_ref, c_ref = ref.deltanet_update(rows[i], conv_w[i], a_log[i], dt_bias[i], conv[i], S[i])
+        assert np.array_equal(dev["c"][i].cpu().numpy(), c_ref.astype(np.float32)), i
+        _check_state(dev["S"][i].cpu().numpy(), S_ref, f"layer {i}")
+
+
+def test_deltanet_update_split_calls():
+    """Two calls carrying the states (37 + 63 tokens) agree with the oracle's
+    single pass; the conv state after them is bitwise the single call's."""
+    conv_w, a_log, dt_bias = synth.make_deltanet_params(1)
+    conv, S = synth.make_deltanet_state(1)
+    rows = synth.make_deltanet_rows(100, seed=9)
+    ls, dev = _layers([rows[:37]], conv_w, a_log, dt_bias, conv, S)
+    kva.kva_deltanet_update(ls, 37, stream=kva.current_stream())
+    x2 = torch.from_numpy(np.ascontiguousarray(rows[37:])).cuda()
+    ls2 = [kva.kva_deltanet_layer(x2.data_ptr(), LD, dev["w"][0].data_ptr(), dev["al"][0].data_ptr(),
+                                  dev["dt"][0].data_ptr(), dev["c"][0].data_ptr(), dev["S"][0].data_ptr())]
+    kva.kva_deltanet_update(ls2, 63, stream=kva.current_stream())
+    torch.cuda.synchronize()
+    S_ref, c_ref = ref.deltanet_update(rows, conv_w[0], a_log[0], dt_bias[0], conv[0], S[0])
+    assert np.array_equal(dev["c"][0].cpu().numpy(), c_ref.astype(np.float32))
+    _check_state(dev["S"][0].cpu().numpy(), S_ref, "37 + 63")
+
+
+def test_deltanet_no_decay_stores_associations():
+    """Closed case through the whole GPU path: with no decay (exp(A_log) = 0
+    in fp32, so alpha = 1) and beta = 1 (sigmoid(40) rounds to 1 in fp32), the
+    delta rule makes the last token's association exact, S k_T = v_T, whatever
+    came before (|k_T| = 1).  The conv is the identity (weight 1 on the
+    current token) and SiLU is inverted on the host, so k and v are placed
+    directly (positive values, where SiLU is invertible)."""
+    T, n_k, n_v = 16, 16, 48
+    rng = np.random.default_rng(41)
+    keys = rng.uniform(0.01, 1.0, (T, 128))
+    keys = keys / np.linalg.norm(keys, axis=1, keepdims=True)
+    vals = rng.uniform(0.1, 1.0, (T, n_v, 128))
+
+    def silu_inv(y):
+        x = np.maximum(y, 1e-3) + 0.5
+        for _ in range(60):
+            s = 1 / (1 + np.exp(-x))
+            x = x - (x * s - y) / (s + x * s * (1 - s))
+        return x
+
+    rows = np.zeros((T, LD), dtype=np.float64)
+    for h in range(n_k):
+        rows[:, n_k * 128 + h * 128:n_k * 128 + (h + 1) * 128] = silu_inv(keys)
+    rows[:, 2 * n_k * 128:2 * n_k * 128 + n_v * 128] = silu_inv(vals).reshape(T, -1)
+    rows[:, 10240 + 48:] = 40.0                                # beta = sigmoid(40) = 1 in fp32
+    rows = rows.astype(np.float32)
+    conv_w = np.zeros((1, 10240, 4), np.float32)
+    conv_w[..., 3] = 1.0
+    a_log = np.full((1, 48), -1e4, np.float32)                 # exp(-1e4) = 0: alpha = 1
+    dt_bias = np.zeros((1, 48), np.float32)
+    conv = np.zeros((1, 3, 10240), np.float32)
+    S = np.zeros((1, 48, 128, 128), np.float32)
+    ls, dev = _layers([rows], conv_w, a_log, dt_bias, conv, S)
+    kva.kva_deltanet_update(ls, T, stream=kva.current_stream())
+    torch.cuda.synchronize()
+    got = dev["S"][0].cpu().numpy().astype(np.float64)
+    k_last = ref.l2norm(ref.silu(rows[-1, n_k * 128:n_k * 128 + 128].astype(np.float64)))
+    v_last = ref.silu(rows[-1, 2 * n_k * 128:2 * n_k * 128 + n_v * 128].astype(np.float64)).reshape(n_v, 128)
+    recall = got @ k_last
+    err = np.max(np.abs(recall - v_last)) / np.sqrt(np.mean(v_last ** 2))
+    print(f"  recall of the last association: max|err|/rms {err:.3e}", flush=True)
+    assert err < 5e-3
+    S_ref, _ = ref.deltanet_update(rows, conv_w[0], a_log[0], dt_bias[0], conv[0], S[0])
+    _check_state(got, S_ref, "no decay")
+
+
+def test_deltanet_argument_errors():
+    conv_w, a_log, dt_bias = synth.make_deltanet_params(1)
+    conv, S = synth.make_deltanet_state(1)
+    rows = [synth.make_deltanet_rows(8)]
+    ls, dev = _layers(rows, conv_w, a_log, dt_bias, conv, S)
+    st = kva.current_stream()
+    for kw, status in (({"n_k_heads": 5}, kva.KVA_ERR_SHAPE), ({"head_dim": 64}, kva.KVA_ERR_UNSUPPORTED)):
+        with pytest.raises(kva.KvaError) as e:
+            kva.kva_deltanet_update(ls, 8, stream=st, **kw)
+        assert e.value.status == status
+    bad = kva.kva_deltanet_layer(ls[0].mixer_in, LD - 1, ls[0].conv_w, ls[0].a_log, ls[0].dt_bias,
+                                 ls[0].conv_state, ls[0].state)
+    with pytest.raises(kva.KvaError) as e:
+        kva.kva_deltanet_update([bad], 8, stream=st)
+    assert e.value.status == kva.KVA_ERR_SHAPE
+    mis = kva.kva_deltanet_layer(ls[0].mixer_in, LD, ls[0].conv_w + 4, ls[0].a_log, ls[0].dt_bias,
+                                 ls[0].conv_state, ls[0].state)
+    with pytest.raises(kva.KvaError) as e:
+        kva.kva_deltanet_update([mis], 8, stream=st)
+    assert e.value.status == kva.KVA_ERR_ARG
+    kva.kva_deltanet_update(ls, 0, stream=st)                  # nothing to do
+    torch.cuda.synchronize()
+    assert np.array_equal(dev["S"][0].cpu().numpy(), S[0]) and np.array_equal(dev["c"][0].cpu().numpy(), conv[0])
