@@ -260,6 +260,44 @@ def time_prompt_kv(prompt: int = 65536, chunk: int = 8192, steps: int = 3, warmu
     return res
 
 
+def time_deltanet(n_tokens: int = 1024, layers: int = 24, steps: int = 10):
+    """kva_deltanet_update for the 24 DeltaNet layers of one 1024-token
+    ubatch (rows of qkv | a | b like the projector's DeltaNet heads, ~N(0,1)).
+    Algorithmic bytes per layer: the k, v, a, b columns of every row read once
+    (8288 fp32), the 128x128 fp32 states of the 48 value heads read and
+    written, the conv weights of k and v, and the new conv state (3 rows of
+    all 10240 channels read from the rows and written)."""
+    import torch
+
+    import learned_kv_approximation_amd as kva
+
+    conv_w, a_log, dt_bias = synth.make_deltanet_params(layers)
+    conv, S = synth.make_deltanet_state(layers)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    rows = [torch.randn((n_tokens, 10336), generator=g, device="cuda") for _ in range(layers)]
+    dev = [(torch.from_numpy(conv_w[l]).cuda(), torch.from_numpy(a_log[l]).cuda(), torch.from_numpy(dt_bias[l]).cuda(),
+            torch.from_numpy(conv[l]).cuda(), torch.from_numpy(S[l]).cuda()) for l in range(layers)]
+    ls = [kva.kva_deltanet_layer(rows[l].data_ptr(), 10336, *[t.data_ptr() for t in dev[l]]) for l in range(layers)]
+    st = kva.current_stream()
+    kva.kva_deltanet_update(ls, n_tokens, stream=st)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        kva.kva_deltanet_update(ls, n_tokens, stream=st)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    per_layer = (n_tokens * 8288 * 4 + 2 * 48 * 128 * 128 * 4 + 8192 * 16 + 2 * 3 * 10240 * 4)
+    nbytes = layers * per_layer
+    del rows, dev
+    torch.cuda.empty_cache()
+    return {"tokens": n_tokens, "layers": layers, "ms": round(ms, 4), "bytes": nbytes,
+            "gb_s": round(nbytes / (ms / 1e3) / 1e9, 1), "frac_hbm": round(nbytes / (ms / 1e3) / 1e9 / HBM_GBS, 4),
+            "tokens_per_s": round(n_tokens / (ms / 1e3), 1)}
+
+
 def mfma_loop(n_iter: int = 4000, workgroups_per_cu: int = 4, reps: int = 10):
     """The MFMA rate the device sustains with no memory traffic (the library's
     kva_debug_mfma_loop): the achievable ceiling at the clock it runs at."""
@@ -425,7 +463,7 @@ def main():
 
     r2 = time_config("r2", args.steps, args.warmup)
     print(f"[bench] r2: {r2['tokens_per_s']:.0f} tok/s, {r2['pct_mfma_peak']:.1f}% peak", file=sys.stderr, flush=True)
-    r3 = r3b = q8 = q8p = q4 = kvw = kvw8 = kvp = sweep = mloop = None
+    r3 = r3b = q8 = q8p = q4 = kvw = kvw8 = kvp = dnu = sweep = mloop = None
     if not args.no_r3:
         r3 = time_config("r3", args.steps, args.warmup)
         print(f"[bench] r3: {r3['tokens_per_s']:.0f} tok/s, {r3['pct_mfma_peak']:.1f}% peak", file=sys.stderr,
@@ -443,6 +481,9 @@ def main():
             print(f"[bench] kv write: {kvw['gb_s']} GB/s", file=sys.stderr, flush=True)
             kvw8 = time_kv_write(q8=True)
             print(f"[bench] kv write q8_0: {kvw8['gb_s']} GB/s", file=sys.stderr, flush=True)
+            dnu = time_deltanet()
+            print(f"[bench] deltanet update 24 layers x 1024: {dnu['ms']} ms, {dnu['gb_s']} GB/s",
+                  file=sys.stderr, flush=True)
             kvp = time_prompt_kv()
             print(f"[bench] r3 65536 + KV: chained {kvp['chained']['tokens_per_s']:.0f} tok/s, "
                   f"fused {kvp['fused']['tokens_per_s']:.0f} tok/s", file=sys.stderr, flush=True)
@@ -508,6 +549,8 @@ def main():
         out["kv_write_q8_0_65536x8"] = kvw8
     if kvp is not None:
         out["r3_prompt_65536_with_kv"] = kvp
+    if dnu is not None:
+        out["deltanet_update_24x1024"] = dnu
     if sweep is not None:
         out["r3_q8_0_m_sweep"] = sweep
     if mloop is not None:

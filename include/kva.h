@@ -30,7 +30,9 @@
  *  - Every call returns a kva_status; nothing aborts or throws across the
  *    ABI.  kva_last_error() gives a human-readable detail for the calling
  *    thread's most recent failure.  Device faults surface asynchronously at
- *    the caller's next synchronisation of the stream.
+ *    the caller's next synchronisation of the stream.  A HIP error left
+ *    pending on the thread by earlier work outside this library is cleared
+ *    (not reported) when a compute entry point starts.
  *  - A context is used by one stream at a time (calls on one context must be
  *    serialised by the caller).
  */
@@ -289,7 +291,8 @@ typedef struct {
  * q's conv is not formed (the layer's output is not produced here).  An
  * engine that runs the ubatch's last token exactly passes n_tokens - 1
  * rows.  All layers share n_tokens and the head counts; any number of layers
- * (launched 32 at a time).  head_dim must be 128 (KVA_ERR_UNSUPPORTED);
+ * (launched 32 at a time).  head_dim must be 128 and n_v_heads / n_k_heads
+ * at most 3 (KVA_ERR_UNSUPPORTED);
  * KVA_ERR_SHAPE for inconsistent counts or a short ld_in; KVA_ERR_ARG for
  * NULL or misaligned pointers.  Buffers of different layers must not alias.
  * The scan runs in fp32 with the MFMA operands (unit keys, the chunk-start

@@ -119,6 +119,13 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        # PyTorch ships its own HIP runtime under the same soname as the one
+        # libkva.so links: load torch first so that the process has one HIP
+        # runtime (the library loaded first would otherwise be torch's too).
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGS.items():
             f = getattr(L, name)

@@ -7,18 +7,18 @@
 //   alpha = exp(-exp(A_log) * softplus(a + dt_bias)), beta = sigmoid(b),
 //   S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T.
 //
-// One workgroup per (layer, value head) walks the tokens in chunks of C = 32
-// and keeps the 128 x 128 fp32 state in MFMA accumulators.  Within a chunk
+// One workgroup (8 waves) per (layer, key head) updates the value heads that
+// read that key head (up to 3), walking the tokens in chunks of C = 32 with
+// the 128 x 128 fp32 states in MFMA accumulators.  Within a chunk
 // (chunk-start state S0, gamma_t = alpha_1 ... alpha_t from the chunk start)
 // the recurrence unrolls to
 //   S_C = gamma_C S0 + sum_t (gamma_C / gamma_t) w_t k_t^T,
 //   (I + A) W = diag(beta) V - diag(beta gamma) K S0^T,
-//   A[t][i] = beta_t (gamma_t / gamma_i) (k_t . k_i) for i < t, else 0,
-// so W = U - Wk S0^T with [U | Wk] = (I + A)^-1 [diag(beta) V | diag(beta gamma) K].
-// The unit lower-triangular solve runs in fp32 by forward substitution, one
-// column of [U | Wk] per thread; K K^T, Wk S0^T and W^T K are 32x32x16 fp16
-// MFMAs with fp32 accumulation (keys are unit vectors; S0, Wk and W are
-// rounded to fp16 as MFMA operands only, the state itself stays fp32).
+//   A[t][i] = beta_t (gamma_t / gamma_i) (k_t . k_i) for i < t, else 0.
+// K K^T (shared by the heads), K S0^T and the state update W^T K are
+// 32x32x16 fp16 MFMAs with fp32 accumulation (unit keys, the chunk-start
+// state and W are rounded to fp16 as operands; the states stay fp32); the
+// unit lower-triangular solve for W runs in fp32, one value column per thread.
 #include "kva_internal.h"
 
 namespace kva {
@@ -29,20 +29,32 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kC = 32;                 // tokens per chunk
 constexpr int kD = kDnHeadDim;         // key and value head width
-constexpr int kRowH = kD + 8;          // fp16 row of 128 values, padded (272 B)
+constexpr int kG = 3;                  // value heads per key head a workgroup can take
 constexpr int kRowT = kC + 8;          // fp16 row of 32 values, padded (80 B)
+constexpr int kRowH = kD + 8;          // fp16 row of 128 values, padded (272 B)
+constexpr int kThreads = 512;
+constexpr int kTilesPerWave = 2 * kG;  // 16 state tiles per head over 8 waves
+
+// (K S0^T)^T and then W^T are kept [m][v][t] with 32 t per row (64 B) and
+// no padding; the four 16-byte chunks of row v are rotated by (v >> 1) & 3
+// so that the rows a lane group reads fall on different banks.
+__device__ __forceinline__ int wt_index(int v, int t) {
+    return v * kC + ((((t >> 3) ^ ((v >> 1) & 3)) << 3) | (t & 7));
+}
 
 struct DnSmem {
-    _Float16 s0h[kD][kRowH];           // chunk-start state S0 [v][k], fp16 operand
+    _Float16 s0h[kG][kD][kRowH];       // chunk-start states [m][v][k] (padded rows)
     _Float16 kht[kD][kRowT];           // unit keys transposed [k][t]
-    float af[kC][kC];                  // A [t][i]
-    float gcum[kC];                    // G_t = log gamma_t
-    float beta[kC];
+    _Float16 kh[kC][kRowH];            // unit keys [t][k]
+    float aft[kG][kC][kC];             // A transposed [m][i][t]
+    float gcum[kG][kC];                // G_t = log gamma_t
+    float beta[kG][kC];
+    float gam[kG][kC];                 // gamma_t
+    float sc[kG][kC];                  // gamma_C / gamma_t
     float rn[kC];                      // 1 / |k_t|
     union {
-        struct { float kr[kC][kD]; _Float16 kh[kC][kRowH]; } a;    // raw keys, unit keys [t][k]
-        struct { float uf[kC][kD]; _Float16 wkh[kC][kRowH]; } b;   // U [t][v], -Wk [t][k]
-        _Float16 wt[kD][kRowT];                                    // W^T scaled [v][t]
+        float kr[kC][kD];                          // raw keys [t][k]
+        _Float16 ks0[kG][kD * kC];                 // (K S0^T)^T, then W^T scaled, wt_index layout
     } r1;
 };
 
@@ -53,88 +65,120 @@ __device__ __forceinline__ f32x16 mma(f16x8 a, f16x8 b, f32x16 c) {
 // Row of element q of a 32x32 MFMA accumulator held by lane l (its column is l % 32).
 __device__ __forceinline__ int acc_row(int q, int lane) { return 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3); }
 
-__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + expf(-x)); }
+// SiLU with the hardware exponential and reciprocal (a few ulp; the values
+// feed fp16 MFMA operands and an fp32 solve whose own error is larger).
+__device__ __forceinline__ float silu_f(float x) { return __fdividef(x, 1.0f + __expf(-x)); }
 __device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))); }
 __device__ __forceinline__ float sigmoid_f(float x) {
     const float e = expf(-fabsf(x));
     return x >= 0.0f ? 1.0f / (1.0f + e) : e / (1.0f + e);
 }
 
-__global__ void __launch_bounds__(256) deltanet_scan(DnArgs g) {
+__global__ void __launch_bounds__(kThreads) deltanet_scan(DnArgs g) {
     __shared__ __attribute__((aligned(16))) DnSmem sm;
-    const int L = blockIdx.x / g.n_v, h = blockIdx.x % g.n_v;
+    const int L = blockIdx.x / g.n_k, kh = blockIdx.x % g.n_k;
     const DnLayer& ly = g.layer[L];
+    const int G = g.n_v / g.n_k;                      // value heads of this key head (<= kG)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int kh = h / (g.n_v / g.n_k);
     const int qkv = (2 * g.n_k + g.n_v) * kD;
-    const bool is_v = tid < kD;                       // waves 0-1: value channels, 2-3: key channels
-    const int j = tid & (kD - 1);
-    const int ch = is_v ? 2 * g.n_k * kD + h * kD + j : g.n_k * kD + kh * kD + j;
+    // threads [0, 128 G): value channel dv of head m; [384, 512): key channel
+    const bool is_k = tid >= kG * kD;
+    const bool is_v = tid < G * kD;
+    const int m = tid / kD, j = tid & (kD - 1);
+    const int hv = kh * G + m;                        // global value head of a value thread
+    const int ch = is_k ? g.n_k * kD + kh * kD + j : 2 * g.n_k * kD + hv * kD + j;
+    const bool active = is_k || is_v;
     const int T = g.n_tokens;
 
-    const float4 cw = *(const float4*)(ly.conv_w + (int64_t)ch * 4);
-    float xm3 = ly.conv_state[ch], xm2 = ly.conv_state[qkv + ch], xm1 = ly.conv_state[2 * qkv + ch];
-    const float decay_rate = expf(ly.a_log[h]);
-    const float dtb = ly.dt_bias[h];
+    float4 cw = make_float4(0.f, 0.f, 0.f, 0.f);
+    float xm3 = 0.f, xm2 = 0.f, xm1 = 0.f;
+    if (active) {
+        cw = *(const float4*)(ly.conv_w + (int64_t)ch * 4);
+        xm3 = ly.conv_state[ch]; xm2 = ly.conv_state[qkv + ch]; xm1 = ly.conv_state[2 * qkv + ch];
+    }
+    // gate lanes: wave m < G, lane r = token
+    const int gm = wave;
+    const bool gate_wave = gm < G;
+    const float decay_rate = gate_wave ? expf(ly.a_log[kh * G + gm]) : 0.f;
+    const float dtb = gate_wave ? ly.dt_bias[kh * G + gm] : 0.f;
 
-    // state: wave w holds rows v in [32w, 32w + 32), one accumulator per 32 keys
-    float* Sg = ly.state + (int64_t)h * kD * kD;
-    f32x16 S[4];
+    // states: tile tau = wave + 8 i (i < 2G): head tau / 16, rows 32 ((tau % 16) / 4), keys 32 (tau % 4)
+    f32x16 S[kTilesPerWave];
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt)
+    for (int i = 0; i < kTilesPerWave; ++i) {
+        const int tau = wave + 8 * i, hm = tau >> 4, rt = (tau & 15) >> 2, ct = tau & 3;
+        if (tau < 16 * G) {
+            const float* Sg = ly.state + (int64_t)(kh * G + hm) * kD * kD;
 #pragma unroll
-        for (int q = 0; q < 16; ++q)
-            S[jt][q] = Sg[(32 * wave + acc_row(q, lane)) * kD + 32 * jt + (lane & 31)];
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-        for (int q = 0; q < 16; ++q)
-            sm.s0h[32 * wave + acc_row(q, lane)][32 * jt + (lane & 31)] = (_Float16)S[jt][q];
+            for (int q = 0; q < 16; ++q) {
+                const int v = 32 * rt + acc_row(q, lane), k = 32 * ct + (lane & 31);
+                S[i][q] = Sg[v * kD + k];
+                sm.s0h[hm][v][k] = (_Float16)S[i][q];
+            }
+        }
+    }
 
+    __syncthreads();
     for (int t0 = 0; t0 < T; t0 += kC) {
         const int nv = T - t0 < kC ? T - t0 : kC;
-        // ---- conv + SiLU of this thread's channel over the chunk (zero past the end)
-        float xin[kC], val[kC];
+        // ---- conv + SiLU of this thread's channel (zero past the end); X holds
+        //      the values, then the right-hand side, then the solution.  Rows
+        //      past the end re-read the last row (values unused).
+        float X[kC];
+        float a_in = 0.f, b_in = 0.f;
+        if (active) {
 #pragma unroll
-        for (int r = 0; r < kC; ++r) xin[r] = r < nv ? ly.x[(int64_t)(t0 + r) * ly.ld + ch] : 0.0f;
+            for (int r = 0; r < kC; ++r) {
+                const int t = t0 + r < T ? t0 + r : T - 1;
+                X[r] = ly.x[(int64_t)t * ly.ld + ch];
+            }
+        }
+        if (gate_wave && lane < nv) {
+            const float* row = ly.x + (int64_t)(t0 + lane) * ly.ld;
+            a_in = row[qkv + kh * G + gm];
+            b_in = row[qkv + g.n_v + kh * G + gm];
+        }
 #pragma unroll
         for (int r = 0; r < kC; ++r) {
-            const float c = cw.x * xm3 + cw.y * xm2 + cw.z * xm1 + cw.w * xin[r];
-            val[r] = r < nv ? silu_f(c) : 0.0f;
-            xm3 = xm2; xm2 = xm1; xm1 = xin[r];
+            const float xr = X[r];
+            const float c = cw.x * xm3 + cw.y * xm2 + cw.z * xm1 + cw.w * xr;
+            X[r] = r < nv ? silu_f(c) : 0.0f;
+            xm3 = xm2; xm2 = xm1; xm1 = xr;
         }
-        if (!is_v) {
+        if (is_k) {
 #pragma unroll
-            for (int r = 0; r < kC; ++r) sm.r1.a.kr[r][j] = val[r];
+            for (int r = 0; r < kC; ++r) sm.r1.kr[r][j] = X[r];
         }
-        // ---- gates and their running log-decay (wave 0, lane r = token)
-        if (wave == 0) {
+        // ---- gates and their running log-decay
+        if (gate_wave) {
             float gl = 0.0f, be = 0.0f;
             if (lane < nv) {
-                const float* row = ly.x + (int64_t)(t0 + lane) * ly.ld;
-                gl = -decay_rate * softplus_f(row[qkv + h] + dtb);
-                be = sigmoid_f(row[qkv + g.n_v + h]);
+                gl = -decay_rate * softplus_f(a_in + dtb);
+                be = sigmoid_f(b_in);
             }
-            float G = gl;
+            float Gs = gl;
 #pragma unroll
             for (int o = 1; o < kC; o <<= 1) {
-                const float y = __shfl_up(G, o);
-                if ((lane & 31) >= o) G += y;
+                const float y = __shfl_up(Gs, o);
+                if ((lane & 31) >= o) Gs += y;
             }
+            const float GC = __shfl(Gs, kC - 1);
             if (lane < kC) {
-                sm.gcum[lane] = G;
-                sm.beta[lane] = be;
+                sm.gcum[gm][lane] = Gs;
+                sm.beta[gm][lane] = be;
+                sm.gam[gm][lane] = expf(Gs);
+                sm.sc[gm][lane] = expf(GC - Gs);
             }
         }
         __syncthreads();
         // ---- key norms: 8 threads per token
-        {
+        if (tid < 8 * kC) {
             const int r = tid >> 3, part = tid & 7;
             float ss = 0.0f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float v = sm.r1.a.kr[r][part * 16 + i];
+                const float v = sm.r1.kr[r][part * 16 + i];
                 ss += v * v;
             }
             ss += __shfl_xor(ss, 1);
@@ -143,99 +187,126 @@ __global__ void __launch_bounds__(256) deltanet_scan(DnArgs g) {
             if (part == 0) sm.rn[r] = 1.0f / sqrtf(ss + 1e-6f);
         }
         __syncthreads();
-        if (!is_v) {
+        if (is_k) {
 #pragma unroll
             for (int r = 0; r < kC; ++r) {
-                val[r] *= sm.rn[r];
-                const _Float16 hv = (_Float16)val[r];
-                sm.r1.a.kh[r][j] = hv;
-                sm.kht[j][r] = hv;
+                const _Float16 hv16 = (_Float16)(X[r] * sm.rn[r]);
+                sm.kh[r][j] = hv16;
+                sm.kht[j][r] = hv16;
             }
         }
         __syncthreads();
-        // ---- A = strictly lower (beta_t gamma_t / gamma_i k_t . k_i)   (wave 0)
-        if (wave == 0) {
+        // ---- MFMA phase: A_m from K K^T (wave 5 + m, which have one K S0^T tile
+        //      each below); (K S0_m^T)^T tiles (every wave)
+        if (wave >= 5 && wave - 5 < G) {
+            const int hm = wave - 5;
             f32x16 acc = {};
 #pragma unroll
             for (int ks = 0; ks < kD / 16; ++ks) {
-                const f16x8 a = *(const f16x8*)&sm.r1.a.kh[lane & 31][ks * 16 + (lane >> 5) * 8];
+                const f16x8 a = *(const f16x8*)&sm.kh[lane & 31][ks * 16 + (lane >> 5) * 8];
                 acc = mma(a, a, acc);
             }
             const int i = lane & 31;
+            const float gi = sm.gcum[hm][i];
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
                 const int t = acc_row(q, lane);
-                sm.af[t][i] = i < t ? sm.beta[t] * expf(sm.gcum[t] - sm.gcum[i]) * acc[q] : 0.0f;
+                sm.aft[hm][i][t] = i < t ? sm.beta[hm][t] * __expf(sm.gcum[hm][t] - gi) * acc[q] : 0.0f;
+            }
+        }
+        // tile u = wave + 8 i (u < 4 G): head u / 4, values 32 (u % 4); K = keys
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int u = wave + 8 * i;
+            if (u < 4 * G) {
+                const int hm = u >> 2, vt = u & 3;
+                f32x16 acc = {};
+#pragma unroll
+                for (int ks = 0; ks < kD / 16; ++ks) {
+                    const int k0 = ks * 16 + (lane >> 5) * 8;
+                    const f16x8 a = *(const f16x8*)&sm.kh[lane & 31][k0];
+                    const f16x8 b = *(const f16x8*)&sm.s0h[hm][32 * vt + (lane & 31)][k0];
+                    acc = mma(a, b, acc);
+                }
+#pragma unroll
+                for (int q = 0; q < 16; ++q)
+                    sm.r1.ks0[hm][wt_index(32 * vt + (lane & 31), acc_row(q, lane))] = (_Float16)acc[q];
             }
         }
         __syncthreads();
-        // ---- [U | Wk] = (I + A)^-1 [diag(beta) V | diag(beta gamma) K], one column per thread
-        float X[kC];
-#pragma unroll
-        for (int r = 0; r < kC; ++r) {
-            float s = sm.beta[r] * val[r];
-            if (!is_v) s *= expf(sm.gcum[r]);
-#pragma unroll
-            for (int i4 = 0; i4 < r; i4 += 4) {
-                const float4 a4 = *(const float4*)&sm.af[r][i4];
-                s -= a4.x * X[i4];
-                if (i4 + 1 < r) s -= a4.y * X[i4 + 1];
-                if (i4 + 2 < r) s -= a4.z * X[i4 + 2];
-                if (i4 + 3 < r) s -= a4.w * X[i4 + 3];
-            }
-            X[r] = s;
-        }
+        // ---- W_m = (I + A_m)^-1 (diag(beta) V - diag(beta gamma) K S0^T), one value
+        //      column per thread, in place, column by column
         if (is_v) {
+            _Float16* rowp = sm.r1.ks0[m];
 #pragma unroll
-            for (int r = 0; r < kC; ++r) sm.r1.b.uf[r][j] = X[r];
-        } else {
+            for (int r8 = 0; r8 < kC; r8 += 8) {
+                const f16x8 ks8 = *(const f16x8*)&rowp[wt_index(j, r8)];
 #pragma unroll
-            for (int r = 0; r < kC; ++r) sm.r1.b.wkh[r][j] = (_Float16)(-X[r]);
-        }
-        __syncthreads();
-        // ---- W = U - Wk S0^T: wave w takes values [32w, 32w + 32)
-        f32x16 W;
+                for (int e = 0; e < 8; ++e) {
+                    const int r = r8 + e;
+                    X[r] = sm.beta[m][r] * (X[r] - sm.gam[m][r] * (float)ks8[e]);
+                }
+            }
 #pragma unroll
-        for (int q = 0; q < 16; ++q) W[q] = sm.r1.b.uf[acc_row(q, lane)][32 * wave + (lane & 31)];
+            for (int i = 0; i < kC - 1; ++i) {
 #pragma unroll
-        for (int ks = 0; ks < kD / 16; ++ks) {
-            const f16x8 a = *(const f16x8*)&sm.r1.b.wkh[lane & 31][ks * 16 + (lane >> 5) * 8];
-            const f16x8 b = *(const f16x8*)&sm.s0h[32 * wave + (lane & 31)][ks * 16 + (lane >> 5) * 8];
-            W = mma(a, b, W);
-        }
-        __syncthreads();
-        const float GC = sm.gcum[kC - 1];
+                for (int r4 = (i + 1) & ~3; r4 < kC; r4 += 4) {
+                    const float4 a4 = *(const float4*)&sm.aft[m][i][r4];
+                    if (r4 + 0 > i) X[r4 + 0] -= a4.x * X[i];
+                    if (r4 + 1 > i) X[r4 + 1] -= a4.y * X[i];
+                    if (r4 + 2 > i) X[r4 + 2] -= a4.z * X[i];
+                    if (r4 + 3 > i) X[r4 + 3] -= a4.w * X[i];
+                }
+                if (i & 1) __builtin_amdgcn_sched_barrier(0);
+            }
+            // W^T scaled by gamma_C / gamma_t, over this thread's own row of ks0
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int t = acc_row(q, lane);
-            sm.r1.wt[32 * wave + (lane & 31)][t] = (_Float16)(W[q] * expf(GC - sm.gcum[t]));
-        }
-        __syncthreads();
-        // ---- S = gamma_C S0 + sum_t (gamma_C / gamma_t) w_t k_t^T
-        const float gC = expf(GC);
+            for (int r8 = 0; r8 < kC; r8 += 8) {
+                f16x8 w8;
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-#pragma unroll
-            for (int q = 0; q < 16; ++q) S[jt][q] *= gC;
-#pragma unroll
-            for (int s = 0; s < kC / 16; ++s) {
-                const f16x8 a = *(const f16x8*)&sm.r1.wt[32 * wave + (lane & 31)][s * 16 + (lane >> 5) * 8];
-                const f16x8 b = *(const f16x8*)&sm.kht[32 * jt + (lane & 31)][s * 16 + (lane >> 5) * 8];
-                S[jt] = mma(a, b, S[jt]);
+                for (int e = 0; e < 8; ++e) w8[e] = (_Float16)(X[r8 + e] * sm.sc[m][r8 + e]);
+                *(f16x8*)&rowp[wt_index(j, r8)] = w8;
             }
         }
+        __syncthreads();
+        // ---- S_m = gamma_C S0_m + sum_t (gamma_C / gamma_t) w_t k_t^T
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt)
+        for (int i = 0; i < kTilesPerWave; ++i) {
+            const int tau = wave + 8 * i, hm = tau >> 4, rt = (tau & 15) >> 2, ct = tau & 3;
+            if (tau < 16 * G) {
+                const float gC = sm.gam[hm][kC - 1];
 #pragma unroll
-            for (int q = 0; q < 16; ++q)
-                sm.s0h[32 * wave + acc_row(q, lane)][32 * jt + (lane & 31)] = (_Float16)S[jt][q];
+                for (int q = 0; q < 16; ++q) S[i][q] *= gC;
+#pragma unroll
+                for (int s = 0; s < kC / 16; ++s) {
+                    const int t8 = s * 16 + (lane >> 5) * 8;
+                    const f16x8 a = *(const f16x8*)&sm.r1.ks0[hm][wt_index(32 * rt + (lane & 31), t8)];
+                    const f16x8 b = *(const f16x8*)&sm.kht[32 * ct + (lane & 31)][t8];
+                    S[i] = mma(a, b, S[i]);
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kTilesPerWave; ++i) {
+            const int tau = wave + 8 * i, hm = tau >> 4, rt = (tau & 15) >> 2, ct = tau & 3;
+            if (tau < 16 * G) {
+#pragma unroll
+                for (int q = 0; q < 16; ++q)
+                    sm.s0h[hm][32 * rt + acc_row(q, lane)][32 * ct + (lane & 31)] = (_Float16)S[i][q];
+            }
+        }
         __syncthreads();
     }
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt)
+    for (int i = 0; i < kTilesPerWave; ++i) {
+        const int tau = wave + 8 * i, hm = tau >> 4, rt = (tau & 15) >> 2, ct = tau & 3;
+        if (tau < 16 * G) {
+            float* Sg = ly.state + (int64_t)(kh * G + hm) * kD * kD;
 #pragma unroll
-        for (int q = 0; q < 16; ++q)
-            Sg[(32 * wave + acc_row(q, lane)) * kD + 32 * jt + (lane & 31)] = S[jt][q];
+            for (int q = 0; q < 16; ++q) Sg[(32 * rt + acc_row(q, lane)) * kD + 32 * ct + (lane & 31)] = S[i][q];
+        }
+    }
 }
 
 // New conv state: the last (width - 1) rows of [old state ; the call's raw
@@ -262,8 +333,9 @@ __global__ void __launch_bounds__(256) deltanet_conv_state(DnArgs g) {
 
 hipError_t launch_deltanet_update(const DnArgs& a, hipStream_t s) {
     if (a.n_tokens <= 0 || a.n_layers <= 0) return hipSuccess;
-    if (a.n_layers > kMaxDnLayers || a.n_k <= 0 || a.n_v % a.n_k) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(deltanet_scan, dim3(a.n_layers * a.n_v), dim3(256), 0, s, a);
+    if (a.n_layers > kMaxDnLayers || a.n_k <= 0 || a.n_v % a.n_k || a.n_v / a.n_k > kG)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(deltanet_scan, dim3(a.n_layers * a.n_k), dim3(kThreads), 0, s, a);
     const int qkv = (2 * a.n_k + a.n_v) * kD;
     hipLaunchKernelGGL(deltanet_conv_state, dim3((qkv + 255) / 256, a.n_layers), dim3(256), 0, s, a);
     return hipGetLastError();

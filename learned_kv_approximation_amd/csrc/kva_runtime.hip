@@ -575,6 +575,10 @@ void set_b(GemmArgs& g, const kva_ctx::DevW& w, int64_t K) {
     g.Bs = w.sc;
 }
 
+// A HIP error left pending on this thread by earlier, unrelated work would be
+// returned by the hipGetLastError that follows our launches: clear it first.
+inline void clear_stale_error() { (void)hipGetLastError(); }
+
 #define LAUNCH(expr)                                                                      \
     do {                                                                                  \
         hipError_t e_ = (expr);                                                           \
@@ -679,6 +683,7 @@ namespace {
 // KV epilogue instead of as fp32 outputs.
 kva_status project(kva_ctx* ctx, const float* x, int32_t n, float* const* head_out, const EpiArgs* kv,
                    void* stream) {
+    clear_stale_error();
     if (!ctx || !x || !head_out) return fail(KVA_ERR_ARG, "NULL argument");
     const kva_config& c = ctx->cfg;
     if (n < 1 || n > c.max_tokens)
@@ -818,6 +823,7 @@ kva_status kva_destroy(kva_ctx* ctx) {
 
 kva_status kva_attn_kv_write(const float* kv, int64_t ld_kv, int32_t n, int64_t pos0,
                              const float* k_gain, const kva_paged_kv* cache, void* stream) {
+    clear_stale_error();
     if (!kv) return fail(KVA_ERR_ARG, "NULL argument");
     KVA_TRY(check_paged_kv(cache, k_gain));
     if (n < 0 || pos0 < 0) return fail(KVA_ERR_SHAPE, "negative n_tokens or pos0");
@@ -836,12 +842,15 @@ kva_status kva_attn_kv_write(const float* kv, int64_t ld_kv, int32_t n, int64_t 
 
 kva_status kva_deltanet_update(const kva_deltanet_layer* layers, int32_t n_layers, int32_t n_tokens,
                                int32_t n_k_heads, int32_t n_v_heads, int32_t head_dim, void* stream) {
+    clear_stale_error();
     if (n_layers < 0 || n_tokens < 0) return fail(KVA_ERR_SHAPE, "negative n_layers or n_tokens");
     if (n_layers == 0 || n_tokens == 0) return KVA_OK;
     if (!layers) return fail(KVA_ERR_ARG, "NULL layers");
     if (head_dim != kDnHeadDim) return fail(KVA_ERR_UNSUPPORTED, "head_dim must be %d", kDnHeadDim);
     if (n_k_heads <= 0 || n_v_heads <= 0 || n_v_heads % n_k_heads)
         return fail(KVA_ERR_SHAPE, "n_v_heads must be a positive multiple of n_k_heads");
+    if (n_v_heads / n_k_heads > 3)
+        return fail(KVA_ERR_UNSUPPORTED, "at most 3 value heads per key head are supported");
     const int64_t qkv = (int64_t)(2 * n_k_heads + n_v_heads) * head_dim;
     for (int l = 0; l < n_layers; ++l) {
         const kva_deltanet_layer& L = layers[l];
@@ -868,6 +877,7 @@ kva_status kva_deltanet_update(const kva_deltanet_layer* layers, int32_t n_layer
 }
 
 kva_status kva_debug_dequant_q8_0(const void* blocks, int64_t n_blocks, float* out, void* stream) {
+    clear_stale_error();
     if (!blocks || !out) return fail(KVA_ERR_ARG, "NULL argument");
     if (n_blocks < 0) return fail(KVA_ERR_SHAPE, "negative n_blocks");
     LAUNCH(launch_dequant_q8_0(blocks, n_blocks, out, static_cast<hipStream_t>(stream)));
@@ -875,6 +885,7 @@ kva_status kva_debug_dequant_q8_0(const void* blocks, int64_t n_blocks, float* o
 }
 
 kva_status kva_debug_dequant_q4_0_f16(const void* blocks, int64_t n_blocks, uint16_t* out, void* stream) {
+    clear_stale_error();
     if (!blocks || !out) return fail(KVA_ERR_ARG, "NULL argument");
     if (n_blocks < 0) return fail(KVA_ERR_SHAPE, "negative n_blocks");
     LAUNCH(launch_dequant_q4_0_f16(blocks, n_blocks, out, static_cast<hipStream_t>(stream)));
@@ -882,6 +893,7 @@ kva_status kva_debug_dequant_q4_0_f16(const void* blocks, int64_t n_blocks, uint
 }
 
 kva_status kva_debug_dequant_q8_0_f16(const void* blocks, int64_t n_blocks, uint16_t* out, void* stream) {
+    clear_stale_error();
     if (!blocks || !out) return fail(KVA_ERR_ARG, "NULL argument");
     if (n_blocks < 0) return fail(KVA_ERR_SHAPE, "negative n_blocks");
     LAUNCH(launch_dequant_q8_0_f16(blocks, n_blocks, out, static_cast<hipStream_t>(stream)));
@@ -889,6 +901,7 @@ kva_status kva_debug_dequant_q8_0_f16(const void* blocks, int64_t n_blocks, uint
 }
 
 kva_status kva_debug_mfma_loop(int32_t n_iter, int32_t n_workgroups, float* sink, void* stream) {
+    clear_stale_error();
     if (!sink) return fail(KVA_ERR_ARG, "NULL argument");
     if (n_iter <= 0 || n_workgroups <= 0) return fail(KVA_ERR_SHAPE, "n_iter and n_workgroups must be positive");
     LAUNCH(launch_mfma_loop(n_iter, n_workgroups, sink, static_cast<hipStream_t>(stream)));
@@ -896,6 +909,7 @@ kva_status kva_debug_mfma_loop(int32_t n_iter, int32_t n_workgroups, float* sink
 }
 
 kva_status kva_debug_copy_z(kva_ctx* ctx, uint16_t* dst, int32_t n, void* stream) {
+    clear_stale_error();
     if (!ctx || !dst) return fail(KVA_ERR_ARG, "NULL argument");
     if (n < 1 || n > ctx->cfg.max_tokens) return fail(KVA_ERR_SHAPE, "bad n_tokens");
     LAUNCH(launch_untile32(ctx->z16, dst, n, ctx->cfg.d_model, static_cast<hipStream_t>(stream)));

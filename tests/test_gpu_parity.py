@@ -339,3 +339,36 @@ def test_kv_write_q8_0_hadamard_parity(integer):
     used = np.zeros((n_pages, 256), dtype=bool)
     used[ptab[pos // 256], pos % 256] = True
     assert np.all(kpn[~used] == 0xFF) and np.all(vpn[~used] == 0xFF)
+
+
+def test_r2_projection_chained_into_deltanet_update(r2):
+    """The r2 projector's 24 DeltaNet heads feed kva_deltanet_update straight
+    from the head output buffers (rows of qkv | a | b); two sampled layers are
+    held to the oracle's update on the same fp32 rows (the DeltaNet bar of
+    test_gpu_deltanet.py)."""
+    cfg, w, _ = r2
+    x = synth.make_input(cfg, n_tokens=1024, seed=23)
+    proj = kva.Projector(cfg, w, max_tokens=1024)
+    outs = proj.project(torch.from_numpy(x).cuda())
+    dn = [i for i, h in enumerate(cfg["heads"]) if h["kind"] == "deltanet"]
+    assert len(dn) == 24
+    conv_w, a_log, dt_bias = synth.make_deltanet_params(len(dn))
+    conv, S = synth.make_deltanet_state(len(dn))
+    dev = [(torch.from_numpy(conv_w[l]).cuda(), torch.from_numpy(a_log[l]).cuda(),
+            torch.from_numpy(dt_bias[l]).cuda(), torch.from_numpy(conv[l]).cuda(), torch.from_numpy(S[l]).cuda())
+           for l in range(len(dn))]
+    layers = [kva.kva_deltanet_layer(outs[hi].data_ptr(), cfg["heads"][hi]["out_dim"], *[t.data_ptr() for t in d])
+              for hi, d in zip(dn, dev)]
+    kva.kva_deltanet_update(layers, 1024, stream=kva.current_stream())
+    torch.cuda.synchronize()
+    for l in (0, 23):
+        rows = outs[dn[l]].cpu().numpy()
+        S_ref, c_ref = ref.deltanet_update(rows, conv_w[l], a_log[l], dt_bias[l], conv[l], S[l])
+        got = dev[l][4].cpu().numpy().astype(np.float64)
+        rms = np.sqrt(np.mean(S_ref ** 2))
+        mx = np.max(np.abs(got - S_ref)) / rms
+        sd = np.sqrt(np.mean((got - S_ref) ** 2)) / rms
+        print(f"r2 layer {cfg['heads'][dn[l]]['layer']}: state max|err|/rms {mx:.3e} rms {sd:.3e}", flush=True)
+        assert mx <= 2e-2 and sd <= 4e-3
+        assert np.array_equal(dev[l][3].cpu().numpy(), c_ref.astype(np.float32))
+    proj.close()
