@@ -298,6 +298,47 @@ def time_deltanet(n_tokens: int = 1024, layers: int = 24, steps: int = 10):
             "tokens_per_s": round(n_tokens / (ms / 1e3), 1)}
 
 
+def time_map(start_layer: int = 12, n_layers: int = 64, n_in: int = 5120, n_tokens: int = 1024,
+             steps: int = 10, warmup: int = 3):
+    """The single-map projector: one bf16 map per later layer (start_layer+1 ..
+    n_layers-1) on the raw residual, 1024-token calls; one grouped GEMM of
+    2 * n_tokens * n_in * n_in * n_maps FLOP per call."""
+    import torch
+
+    import learned_kv_approximation_amd as kva
+
+    n_maps = synth.map_layers(start_layer, n_layers)
+    t0 = time.time()
+    maps, biases = synth.make_map_weights(n_in, n_maps, "bf16")
+    x = torch.from_numpy(synth.make_map_input(n_tokens, n_in)).cuda()
+    mp = kva.MapProjector(maps, biases, dtype="bf16", n_in=n_in, max_tokens=n_tokens)
+    del maps, biases
+    print(f"[bench] single-map projector: {n_maps} maps built in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    outs = mp.project(x)
+    for _ in range(warmup):
+        mp.project(x, outs)
+    torch.cuda.synchronize()
+    kva.kva_profile_enable(mp.ctx, 1 << STAGE_HEADS)
+    kva.kva_profile_read(mp.ctx)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        mp.project(x, outs)
+    e1.record()
+    torch.cuda.synchronize()
+    heads = kva.kva_profile_read(mp.ctx)["gemm_heads"]
+    kva.kva_profile_enable(mp.ctx, 0)
+    ms = e0.elapsed_time(e1) / steps
+    flop = 2.0 * n_tokens * n_in * n_in * n_maps
+    mp.close()
+    del outs, x
+    torch.cuda.empty_cache()
+    return {"start_layer": start_layer, "n_layers": n_layers, "maps": n_maps, "n_in": n_in, "tokens": n_tokens,
+            "ms": round(ms, 4), "tokens_per_s": round(n_tokens / (ms / 1e3), 1),
+            "tflop_per_call": round(flop / 1e12, 5), "pct_mfma_peak": round(100 * flop / (ms / 1e3) / (PEAK_TFLOPS * 1e12), 2),
+            "gemm_ms": round(heads[1] / max(heads[0], 1), 4)}
+
+
 def mfma_loop(n_iter: int = 4000, workgroups_per_cu: int = 4, reps: int = 10):
     """The MFMA rate the device sustains with no memory traffic (the library's
     kva_debug_mfma_loop): the achievable ceiling at the clock it runs at."""
@@ -463,7 +504,7 @@ def main():
 
     r2 = time_config("r2", args.steps, args.warmup)
     print(f"[bench] r2: {r2['tokens_per_s']:.0f} tok/s, {r2['pct_mfma_peak']:.1f}% peak", file=sys.stderr, flush=True)
-    r3 = r3b = q8 = q8p = q4 = kvw = kvw8 = kvp = dnu = sweep = mloop = None
+    r3 = r3b = q8 = q8p = q4 = kvw = kvw8 = kvp = dnu = p2 = sweep = mloop = None
     if not args.no_r3:
         r3 = time_config("r3", args.steps, args.warmup)
         print(f"[bench] r3: {r3['tokens_per_s']:.0f} tok/s, {r3['pct_mfma_peak']:.1f}% peak", file=sys.stderr,
@@ -484,6 +525,9 @@ def main():
             dnu = time_deltanet()
             print(f"[bench] deltanet update 24 layers x 1024: {dnu['ms']} ms, {dnu['gb_s']} GB/s",
                   file=sys.stderr, flush=True)
+            p2 = time_map()
+            print(f"[bench] single-map projector (start 12, 51 maps): {p2['tokens_per_s']:.0f} tok/s, "
+                  f"{p2['pct_mfma_peak']}% peak", file=sys.stderr, flush=True)
             kvp = time_prompt_kv()
             print(f"[bench] r3 65536 + KV: chained {kvp['chained']['tokens_per_s']:.0f} tok/s, "
                   f"fused {kvp['fused']['tokens_per_s']:.0f} tok/s", file=sys.stderr, flush=True)
@@ -551,6 +595,8 @@ def main():
         out["r3_prompt_65536_with_kv"] = kvp
     if dnu is not None:
         out["deltanet_update_24x1024"] = dnu
+    if p2 is not None:
+        out["single_map_projector_start12"] = p2
     if sweep is not None:
         out["r3_q8_0_m_sweep"] = sweep
     if mloop is not None:

@@ -180,6 +180,34 @@ typedef enum {
                                /* the Hadamard-rotated values, see below         */
 } kva_kv_type;
 
+/* The single-map projector of the R9V forum post ("R9V Update: Created and
+ * adopted KVA projections ...", first implementation): one dense linear map
+ * per later layer from the residual at a chosen start layer straight to that
+ * layer's input, y_l = W_l x + b_l, with no trunk (the post fits each map by
+ * ridge regression; here the maps are given).  The start layer only decides
+ * how many maps there are (the later layers).  A context made here holds the
+ * maps packed like kva_create's heads and runs them as one grouped GEMM:
+ *   n_in         residual width (a multiple of 32), also every map's width
+ *   n_maps       maps, 1..64 (e.g. 51 for start layer 12 of 64 layers)
+ *   weight_dtype KVA_DTYPE_F32 or _BF16 (rounded to bf16; the input x is
+ *                rounded to bf16 too), or _Q8_0 / _Q4_0 (weights d*q rounded
+ *                once to fp16, x to fp16)
+ *   w            host array of n_maps host pointers, [n_in (out)][n_in (in)]
+ *   b            host array of n_maps host pointers to fp32 [n_in], or NULL
+ *   max_tokens   largest n_tokens a call may pass
+ * Errors as kva_create (KVA_ERR_SHAPE / _DTYPE / _ARG / _OOM / _HIP).  Such a
+ * context works with kva_map_project, kva_profile_*, kva_get_stats and
+ * kva_destroy; kva_project_ubatch on it returns KVA_ERR_UNSUPPORTED. */
+kva_status kva_map_create(int32_t n_in, int32_t n_maps, int32_t weight_dtype, const void* const* w,
+                          const float* const* b, int32_t max_tokens, int device, kva_ctx** out);
+
+/* y_l = W_l x + b_l for the n_tokens rows of x (device fp32 [n_tokens][n_in]);
+ * out: host array of n_maps device pointers, map l writes fp32
+ * [n_tokens][n_in].  fp32 accumulation over n_in in a fixed order, so a row's
+ * results do not depend on the other rows of the call.  1 <= n_tokens <=
+ * max_tokens.  Asynchronous on `stream`. */
+kva_status kva_map_project(kva_ctx* ctx, const float* x, int32_t n_tokens, float* const* out, void* stream);
+
 /* Paged KV cache of one full-attention layer of the base model
  * ("Qwen3.8-27B-MLA" card, "What this is": 4 KV heads of 256 dims, 64 of
  * which are rotary).  Pools are device arrays laid out

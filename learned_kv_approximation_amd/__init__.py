@@ -96,6 +96,9 @@ _SIGS = {
     "kva_project_ubatch_kv": (c_i32, [c_vp, c_vp, c_i32, ctypes.POINTER(c_vp), c_i64,
                                       ctypes.POINTER(kva_attn_dest), c_i32, c_vp]),
     "kva_destroy": (c_i32, [c_vp]),
+    "kva_map_create": (c_i32, [c_i32, c_i32, c_i32, ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), c_i32, c_i32,
+                               ctypes.POINTER(c_vp)]),
+    "kva_map_project": (c_i32, [c_vp, c_vp, c_i32, ctypes.POINTER(c_vp), c_vp]),
     "kva_deltanet_update": (c_i32, [ctypes.POINTER(kva_deltanet_layer), c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
     "kva_attn_kv_write": (c_i32, [c_vp, c_i64, c_i32, c_i64, c_vp, ctypes.POINTER(kva_paged_kv), c_vp]),
     "kva_debug_dequant_q8_0": (c_i32, [c_vp, c_i64, c_vp, c_vp]),
@@ -178,6 +181,59 @@ def kva_deltanet_update(layers, n_tokens: int, n_k_heads: int = 16, n_v_heads: i
     arr = (kva_deltanet_layer * max(1, len(layers)))(*layers)
     _check(lib().kva_deltanet_update(arr, len(layers), n_tokens, n_k_heads, n_v_heads, head_dim, stream),
            "kva_deltanet_update")
+
+
+def kva_map_create(n_in: int, n_maps: int, weight_dtype: int, w_ptrs, b_ptrs, max_tokens: int,
+                   device: int = 0) -> int:
+    """w_ptrs / b_ptrs: host pointers (ints) per map; b_ptrs may be None."""
+    wa = (c_vp * n_maps)(*w_ptrs)
+    ba = (c_vp * n_maps)(*b_ptrs) if b_ptrs is not None else None
+    out = c_vp()
+    _check(lib().kva_map_create(n_in, n_maps, weight_dtype, wa, ba, max_tokens, device, ctypes.byref(out)),
+           "kva_map_create")
+    return out.value
+
+
+def kva_map_project(ctx: int, x_ptr: int, n_tokens: int, out_ptrs, stream: int = 0) -> None:
+    arr = (c_vp * len(out_ptrs))(*out_ptrs)
+    _check(lib().kva_map_project(ctx, x_ptr, n_tokens, arr, stream), "kva_map_project")
+
+
+class MapProjector:
+    """Owns a single-map context built from NumPy maps ([n_in][n_in] each, in
+    the storage format of `dtype`) and optional fp32 biases."""
+
+    def __init__(self, maps, biases=None, dtype: str = "bf16", n_in: int | None = None,
+                 max_tokens: int = 1024, device: int = 0):
+        import numpy as np
+        self.n_in = int(n_in if n_in is not None else maps[0].shape[-1])
+        self.n_maps = len(maps)
+        self._keep = [np.ascontiguousarray(m) for m in maps]
+        self._keep_b = [np.ascontiguousarray(b, dtype=np.float32) for b in biases] if biases is not None else None
+        self.ctx = kva_map_create(self.n_in, self.n_maps, DTYPES[dtype], [m.ctypes.data for m in self._keep],
+                                  [b.ctypes.data for b in self._keep_b] if self._keep_b is not None else None,
+                                  max_tokens, device)
+        del self._keep, self._keep_b
+
+    def project(self, x, outs=None, stream: int | None = None):
+        import torch
+        n = x.shape[0]
+        if outs is None:
+            outs = [torch.empty((n, self.n_in), dtype=torch.float32, device=x.device) for _ in range(self.n_maps)]
+        kva_map_project(self.ctx, x.data_ptr(), n, [o.data_ptr() for o in outs],
+                        current_stream() if stream is None else stream)
+        return outs
+
+    def close(self):
+        if getattr(self, "ctx", None):
+            kva_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def kva_destroy(ctx: int) -> None:

@@ -239,6 +239,11 @@ hipError_t launch_fold_rmsnorm(float* h, int64_t ldh, bool add, const float* par
                                int64_t pstride, int64_t ldp, const float* g, int32_t rows, int32_t cols,
                                float eps, uint16_t* out, bool bf16, hipStream_t stream);
 
+// out[tiled32_index(r, c, cols)] = 16-bit(x[r][c]) (fp16 or bf16, nearest
+// even); cols % 32 == 0.
+hipError_t launch_cast_tiled(const float* x, int64_t ldx, int32_t rows, int32_t cols, uint16_t* out, bool bf16,
+                             hipStream_t stream);
+
 // dst[r][c] = src[tiled32_index(r, c, cols)] for r < rows (16-bit values).
 hipError_t launch_untile32(const uint16_t* src, uint16_t* dst, int32_t rows, int32_t cols, hipStream_t stream);
 

@@ -53,6 +53,24 @@ __global__ void __launch_bounds__(256) rmsnorm_cast(const float* __restrict__ x,
     }
 }
 
+// Plain cast of fp32 rows to the 16-bit tiled32_index layout of a GEMM's A
+// operand (no norm), one workgroup per row: the single-map projector's input.
+template <bool BF16>
+__global__ void __launch_bounds__(256) cast_tiled(const float* __restrict__ x, int64_t ldx, int32_t cols,
+                                                  uint16_t* __restrict__ out) {
+    const int row = blockIdx.x;
+    const float* xr = x + (int64_t)row * ldx;
+    for (int c = threadIdx.x * 4; c < cols; c += 1024) {
+        const float4 v = *(const float4*)(xr + c);
+        ushort4 o;
+        o.x = to_bits(v.x, BF16);
+        o.y = to_bits(v.y, BF16);
+        o.z = to_bits(v.z, BF16);
+        o.w = to_bits(v.w, BF16);
+        *(ushort4*)(out + tiled32_index(row, c, cols)) = o;
+    }
+}
+
 // Split-K fold + RMSNorm: the residual update that follows a split GEMM,
 // fused with the norm that reads the updated residual.  The partials are
 // added in a fixed order, so the result is deterministic and independent of
@@ -227,6 +245,17 @@ hipError_t launch_rmsnorm_cast(const float* x, int64_t ldx, const float* g, int3
         hipLaunchKernelGGL(rmsnorm_cast<true>, dim3(rows), dim3(256), 0, s, x, ldx, g, cols, eps, out);
     else
         hipLaunchKernelGGL(rmsnorm_cast<false>, dim3(rows), dim3(256), 0, s, x, ldx, g, cols, eps, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_cast_tiled(const float* x, int64_t ldx, int32_t rows, int32_t cols, uint16_t* out, bool bf16,
+                             hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    if (cols % 32) return hipErrorInvalidValue;
+    if (bf16)
+        hipLaunchKernelGGL(cast_tiled<true>, dim3(rows), dim3(256), 0, s, x, ldx, cols, out);
+    else
+        hipLaunchKernelGGL(cast_tiled<false>, dim3(rows), dim3(256), 0, s, x, ldx, cols, out);
     return hipGetLastError();
 }
 

@@ -214,6 +214,7 @@ struct kva_ctx {
     int32_t* tail_col = nullptr;
     int64_t n_pad_heads = 0;
     int32_t tail_start = 0;
+    bool map_only = false;            // a single-map context (kva_map_create): heads on the raw input
     int32_t kv_tiles = 0;             // leading packed tiles of the KV heads
     std::vector<int32_t> kv_heads;    // heads the fused KV epilogue takes, in head order
 
@@ -424,6 +425,51 @@ void pad_rows(std::vector<RowSrc>& v) {
     while (v.size() % kColPad) v.push_back({nullptr, -1});
 }
 
+// The head weights and biases of config c (inputs d wide) in packed column
+// order (plan_heads), with the device tables of the packing.
+kva_status pack_heads(kva_ctx* ctx, const kva_config& c, const void* const* head_w, const float* const* head_b,
+                      int64_t d, PackTarget head_t) {
+    const int dt = c.weight_dtype;
+    if (!head_w) return fail(KVA_ERR_ARG, "head_w is NULL");
+    if (c.has_head_bias && !head_b) return fail(KVA_ERR_ARG, "head_b is NULL but has_head_bias is set");
+    for (int i = 0; i < c.n_out_heads; ++i) {
+        if (!head_w[i]) return fail(KVA_ERR_ARG, "head_w[%d] is NULL", i);
+        if (c.has_head_bias && !head_b[i]) return fail(KVA_ERR_ARG, "head_b[%d] is NULL", i);
+    }
+    HeadPlan plan = plan_heads(c);
+    ctx->n_pad_heads = plan.n_pad;
+    ctx->tail_start = plan.tail_start;
+    ctx->kv_tiles = plan.kv_tiles;
+    ctx->kv_heads = plan.kv_heads;
+    {
+        std::vector<RowSrc> rows((size_t)plan.n_pad);
+        std::vector<float> bias((size_t)plan.n_pad, 0.0f);
+        for (int64_t col = 0; col < plan.n_pad; ++col) {
+            const int hh = plan.col_head[col];
+            if (hh < 0) {
+                rows[col] = {nullptr, -1};
+                continue;
+            }
+            rows[col] = {head_w[hh], plan.col_index[col]};
+            if (c.has_head_bias) bias[col] = head_b[hh][plan.col_index[col]];
+        }
+        KVA_TRY(pack_weight(ctx, dt, d, rows, head_t, &ctx->w_heads, "heads"));
+        float* bb = nullptr;
+        HIP_TRY(ctx->alloc(&bb, (size_t)plan.n_pad * 4, true));
+        KVA_TRY(upload(ctx, bb, bias.data(), (size_t)plan.n_pad * 4));
+        ctx->b_heads = c.has_head_bias ? bb : nullptr;
+    }
+    auto puti = [&](int32_t** dstp, const std::vector<int32_t>& v) -> kva_status {
+        HIP_TRY(ctx->alloc(dstp, v.size() * 4, true));
+        return upload(ctx, *dstp, v.data(), v.size() * 4);
+    };
+    KVA_TRY(puti(&ctx->tile_head, plan.tile_head));
+    KVA_TRY(puti(&ctx->tile_col0, plan.tile_col0));
+    KVA_TRY(puti(&ctx->tail_head, plan.tail_head));
+    KVA_TRY(puti(&ctx->tail_col, plan.tail_col));
+    return KVA_OK;
+}
+
 kva_status create_impl(const kva_config* cfg, const kva_weights* w, int device, kva_ctx* ctx) {
     const kva_config& c = *cfg;
     const int dt = c.weight_dtype;
@@ -489,43 +535,7 @@ kva_status create_impl(const kva_config* cfg, const kva_weights* w, int device, 
     }
 
     // -------- heads, packed column order
-    if (!w->head_w) return fail(KVA_ERR_ARG, "head_w is NULL");
-    if (c.has_head_bias && !w->head_b) return fail(KVA_ERR_ARG, "head_b is NULL but has_head_bias is set");
-    for (int i = 0; i < c.n_out_heads; ++i) {
-        if (!w->head_w[i]) return fail(KVA_ERR_ARG, "head_w[%d] is NULL", i);
-        if (c.has_head_bias && !w->head_b[i]) return fail(KVA_ERR_ARG, "head_b[%d] is NULL", i);
-    }
-    HeadPlan plan = plan_heads(c);
-    ctx->n_pad_heads = plan.n_pad;
-    ctx->tail_start = plan.tail_start;
-    ctx->kv_tiles = plan.kv_tiles;
-    ctx->kv_heads = plan.kv_heads;
-    {
-        std::vector<RowSrc> rows((size_t)plan.n_pad);
-        std::vector<float> bias((size_t)plan.n_pad, 0.0f);
-        for (int64_t col = 0; col < plan.n_pad; ++col) {
-            const int hh = plan.col_head[col];
-            if (hh < 0) {
-                rows[col] = {nullptr, -1};
-                continue;
-            }
-            rows[col] = {w->head_w[hh], plan.col_index[col]};
-            if (c.has_head_bias) bias[col] = w->head_b[hh][plan.col_index[col]];
-        }
-        KVA_TRY(pack_weight(ctx, dt, d, rows, head_t, &ctx->w_heads, "heads"));
-        float* bb = nullptr;
-        HIP_TRY(ctx->alloc(&bb, (size_t)plan.n_pad * 4, true));
-        KVA_TRY(upload(ctx, bb, bias.data(), (size_t)plan.n_pad * 4));
-        ctx->b_heads = c.has_head_bias ? bb : nullptr;
-    }
-    auto puti = [&](int32_t** dstp, const std::vector<int32_t>& v) -> kva_status {
-        HIP_TRY(ctx->alloc(dstp, v.size() * 4, true));
-        return upload(ctx, *dstp, v.data(), v.size() * 4);
-    };
-    KVA_TRY(puti(&ctx->tile_head, plan.tile_head));
-    KVA_TRY(puti(&ctx->tile_col0, plan.tile_col0));
-    KVA_TRY(puti(&ctx->tail_head, plan.tail_head));
-    KVA_TRY(puti(&ctx->tail_col, plan.tail_col));
+    KVA_TRY(pack_heads(ctx, c, w->head_w, w->head_b, d, head_t));
 
     // -------- scratch
     const int64_t m = round_up(c.max_tokens, kRowPad);
@@ -685,6 +695,7 @@ kva_status project(kva_ctx* ctx, const float* x, int32_t n, float* const* head_o
                    void* stream) {
     clear_stale_error();
     if (!ctx || !x || !head_out) return fail(KVA_ERR_ARG, "NULL argument");
+    if (ctx->map_only) return fail(KVA_ERR_UNSUPPORTED, "a single-map context has no trunk: use kva_map_project");
     const kva_config& c = ctx->cfg;
     if (n < 1 || n > c.max_tokens)
         return fail(KVA_ERR_SHAPE, "n_tokens %d outside [1, %d]", n, c.max_tokens);
@@ -810,6 +821,89 @@ kva_status kva_project_ubatch_kv(kva_ctx* ctx, const float* x, int32_t n, float*
     }
     if (n_attn > 0) kv.kv_rope = make_rope(&attn[0].cache);
     return project(ctx, x, n, head_out, n_attn > 0 ? &kv : nullptr, stream);
+}
+
+kva_status kva_map_create(int32_t n_in, int32_t n_maps, int32_t weight_dtype, const void* const* w,
+                          const float* const* b, int32_t max_tokens, int device, kva_ctx** out) {
+    if (!out) return fail(KVA_ERR_ARG, "out is NULL");
+    *out = nullptr;
+    if (n_in < 32 || n_in % 32) return fail(KVA_ERR_SHAPE, "n_in must be a positive multiple of 32");
+    if (n_maps < 1 || n_maps > kMaxHeads) return fail(KVA_ERR_SHAPE, "n_maps outside [1, %d]", kMaxHeads);
+    if (max_tokens < 1) return fail(KVA_ERR_SHAPE, "max_tokens must be positive");
+    if (weight_dtype != KVA_DTYPE_F32 && weight_dtype != KVA_DTYPE_BF16 && weight_dtype != KVA_DTYPE_Q8_0 &&
+        weight_dtype != KVA_DTYPE_Q4_0)
+        return fail(KVA_ERR_DTYPE, "unknown weight_dtype %d", weight_dtype);
+    if (!w) return fail(KVA_ERR_ARG, "weights are NULL");
+    kva_ctx* ctx = new (std::nothrow) kva_ctx();
+    if (!ctx) return fail(KVA_ERR_OOM, "host allocation failed");
+    ctx->map_only = true;
+    kva_config& c = ctx->cfg;
+    c.n_in = n_in;
+    c.d_model = n_in;
+    c.max_tokens = max_tokens;
+    c.weight_dtype = weight_dtype;
+    c.has_head_bias = b ? 1 : 0;
+    c.n_out_heads = n_maps;
+    for (int i = 0; i < n_maps; ++i) ctx->heads.push_back(kva_head_desc{KVA_HEAD_DRAFT, i, n_in});
+    c.out_heads = ctx->heads.data();
+    kva_status st = KVA_OK;
+    try {
+        st = [&]() -> kva_status {
+            HIP_TRY(hipSetDevice(device));
+            ctx->device = device;
+            HIP_TRY(hipDeviceGetAttribute(&ctx->n_cu, hipDeviceAttributeMultiprocessorCount, device));
+            ctx->q4 = weight_dtype == KVA_DTYPE_Q4_0;
+            ctx->q8 = weight_dtype == KVA_DTYPE_Q8_0 || ctx->q4;
+            const PackTarget head_t = ctx->q4 ? PACK_Q4 : ctx->q8 ? PACK_Q8 : PACK_BF16_T32;
+            KVA_TRY(pack_heads(ctx, c, w, b, n_in, head_t));
+            const int64_t m = round_up(max_tokens, kRowPad);
+            ctx->m_alloc = m;
+            HIP_TRY(ctx->alloc(&ctx->z16, (size_t)m * n_in * 2, false));
+            HIP_TRY(hipMemset(ctx->z16, 0, (size_t)m * n_in * 2));
+            HIP_TRY(hipDeviceSynchronize());
+            return KVA_OK;
+        }();
+    } catch (const std::bad_alloc&) {
+        st = fail(KVA_ERR_OOM, "host allocation failed while repacking weights");
+    }
+    if (st != KVA_OK) {
+        delete ctx;
+        return st;
+    }
+    ctx->stats.weight_bytes = ctx->weight_bytes;
+    ctx->stats.scratch_bytes = ctx->scratch_bytes;
+    *out = ctx;
+    return KVA_OK;
+}
+
+kva_status kva_map_project(kva_ctx* ctx, const float* x, int32_t n, float* const* out, void* stream) {
+    clear_stale_error();
+    if (!ctx || !x || !out) return fail(KVA_ERR_ARG, "NULL argument");
+    if (!ctx->map_only) return fail(KVA_ERR_UNSUPPORTED, "not a single-map context (see kva_map_create)");
+    const kva_config& c = ctx->cfg;
+    if (n < 1 || n > c.max_tokens) return fail(KVA_ERR_SHAPE, "n_tokens %d outside [1, %d]", n, c.max_tokens);
+    HeadOut ho{};
+    for (int i = 0; i < c.n_out_heads; ++i) {
+        if (!out[i]) return fail(KVA_ERR_ARG, "out[%d] is NULL", i);
+        ho.ptr[i] = out[i];
+        ho.ld[i] = c.n_in;
+    }
+    HIP_TRY(hipSetDevice(ctx->device));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    STAGE(KVA_STAGE_NORM, launch_cast_tiled(x, c.n_in, n, c.n_in, ctx->z16, !ctx->q8, s));
+    GemmArgs g;
+    g.A = ctx->z16; g.lda = c.n_in; set_b(g, ctx->w_heads, c.n_in);
+    g.M = n; g.N = (int32_t)ctx->n_pad_heads; g.K = c.n_in;
+    g.epi.n_real = (int32_t)ctx->n_pad_heads;
+    g.epi.tile_head = ctx->tile_head; g.epi.tile_col0 = ctx->tile_col0;
+    g.epi.tail_head = ctx->tail_head; g.epi.tail_col = ctx->tail_col;
+    g.epi.tail_start = ctx->tail_start; g.epi.bias = ctx->b_heads;
+    g.epi.heads = ho;
+    const GemmOperand opd = ctx->q4 ? OPD_Q4 : ctx->q8 ? OPD_Q8 : OPD_BF16;
+    STAGE(KVA_STAGE_GEMM_HEADS, launch_gemm_heads(opd, g, ctx->n_cu, 0, s));
+    ctx->stats.calls += 1;
+    ctx->stats.tokens += (uint64_t)n;
+    return KVA_OK;
 }
 
 kva_status kva_destroy(kva_ctx* ctx) {

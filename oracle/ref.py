@@ -569,3 +569,26 @@ def deltanet_update(mixer_in, conv_w, a_log, dt_bias, conv_state, S0, n_k: int =
     Returns (final state [n_v, hd, hd], new conv state [3, qkv])."""
     k, v, alpha, beta, new_conv = deltanet_prepare(mixer_in, conv_w, a_log, dt_bias, conv_state, n_k, n_v, hd)
     return gated_delta_scan(S0, k, v, alpha, beta, n_v // n_k), new_conv
+
+
+# --------------------------------------------------------------------------
+# single-map projector (the R9V forum post, "R9V Update: Created and adopted
+# KVA projections ...": one full map per later layer, fitted by ridge
+# regression, from the start layer's residual straight to each later layer's
+# input; the start layer is variable).  Readings: each map is affine,
+# y_l = W_l x + b_l, with W_l square (the residual width on both sides); the
+# maps for a start layer s of an L-layer model are those of layers s+1..L-1.
+
+
+def map_project(x: np.ndarray, maps, biases=None, dtype: str = "f32") -> list:
+    """[x @ W_l^T + b_l] in float64 for every map (weights in their storage
+    format, decoded by weight_f64)."""
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[1]
+    out = []
+    for i, w in enumerate(maps):
+        y = x @ weight_f64(w, dtype, n, n).T
+        if biases is not None:
+            y = y + np.asarray(biases[i], dtype=np.float64)[None, :]
+        out.append(y)
+    return out

@@ -288,3 +288,31 @@ def make_deltanet_rows(n_tokens: int, seed: int = 6, width: int = DN_QKV + 2 * D
     (the projector's outputs have unit scale)."""
     rng = np.random.default_rng(seed + 6000)
     return rng.standard_normal((n_tokens, width), dtype=np.float32)
+
+
+# ---------------------------------------------------------------- single-map projector
+
+def map_layers(start_layer: int, n_layers: int = 64) -> int:
+    """Maps a start layer needs: one per later layer (start+1 .. n_layers-1)."""
+    return n_layers - 1 - start_layer
+
+
+def make_map_weights(n_in: int, n_maps: int, dtype: str = "bf16", seed: int = 8, bias: bool = True):
+    """n_maps square maps [n_in][n_in] ~ N(0, 1/n_in) in the storage format of
+    `dtype` (q8_0 / q4_0: random codes and scales of that scale), and fp32
+    biases ~ N(0, 1/n_in), drawn map by map from PCG64(seed + 7000)."""
+    rng = np.random.default_rng(seed + 7000)
+    maps, biases = [], []
+    for _ in range(n_maps):
+        maps.append(_linear(rng, n_in, n_in, dtype))
+        if bias:
+            biases.append((rng.standard_normal(n_in, dtype=np.float32) / np.float32(math.sqrt(n_in))))
+    return maps, (biases if bias else None)
+
+
+def make_map_input(n_tokens: int, n_in: int, seed: int = 8, rms: float = 4.0) -> np.ndarray:
+    """Start-layer residuals [n_tokens][n_in]: N(0, 1) rows rescaled to RMS `rms`."""
+    rng = np.random.default_rng(seed + 8000)
+    x = rng.standard_normal((n_tokens, n_in), dtype=np.float32).astype(np.float64)
+    x *= rms / np.sqrt(np.mean(x * x, axis=1, keepdims=True))
+    return x.astype(np.float32)

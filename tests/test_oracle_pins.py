@@ -620,6 +620,30 @@ def test_deltanet_update_splits_at_any_token():
     assert rows.shape[1] == 10240 + 48 + 48
 
 
+# ------------------------------------------------------------------ single-map projector
+
+def test_map_project_matches_torch_linear_and_closed_cases():
+    rng = np.random.default_rng(51)
+    n = 64
+    maps, biases = synth.make_map_weights(n, 3, "f32")
+    x = synth.make_map_input(10, n)
+    got = ref.map_project(x, maps, biases)
+    for i in range(3):                                            # library special case
+        want = F.linear(torch.from_numpy(x.astype(np.float64)), torch.from_numpy(maps[i].astype(np.float64)),
+                        torch.from_numpy(biases[i].astype(np.float64))).numpy()
+        assert np.allclose(got[i], want, rtol=1e-12, atol=1e-12)
+    # zero input gives the bias; the identity map gives the input back
+    z = ref.map_project(np.zeros((2, n)), maps, biases)
+    assert all(np.array_equal(z[i], np.tile(biases[i].astype(np.float64), (2, 1))) for i in range(3))
+    eye = ref.map_project(x, [np.eye(n, dtype=np.float32)])[0]
+    assert np.array_equal(eye, x.astype(np.float64))
+    # stored formats decode through the weight readers: a bf16 map equals its decoded values
+    wb = synth.make_map_weights(n, 1, "bf16", bias=False)[0][0]
+    assert np.allclose(ref.map_project(x, [wb], dtype="bf16")[0],
+                       x.astype(np.float64) @ ref.bf16_bits_to_f64(wb).reshape(n, n).T, rtol=1e-13)
+    assert synth.map_layers(12) == 51 and synth.map_layers(24) == 39
+
+
 # ------------------------------------------------------------------ planted mistakes
 
 def _mutants():
