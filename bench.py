@@ -485,6 +485,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-r3", action="store_true")
     ap.add_argument("--quick", action="store_true", help="r2 and r3 one-ubatch lines only")
+    ap.add_argument("--line", choices=["deltanet", "map", "kv_write", "kv_write_q8", "prompt_kv"],
+                    help="run one extra line alone and print its JSON (for profiling runs)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run 2 r2 projections and 2 plain 1 GiB device copies, print nothing (for rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -500,6 +502,11 @@ def main():
     kva.lib()   # fails loudly if libkva.so is missing
     if args.traffic_probe:
         traffic_probe()
+        return
+    if args.line:
+        fn = {"deltanet": time_deltanet, "map": time_map, "kv_write": time_kv_write,
+              "kv_write_q8": lambda: time_kv_write(q8=True), "prompt_kv": time_prompt_kv}[args.line]
+        print(json.dumps({"line": args.line, **fn()}), flush=True)
         return
 
     r2 = time_config("r2", args.steps, args.warmup)
