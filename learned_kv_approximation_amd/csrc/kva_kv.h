@@ -10,13 +10,42 @@
 #pragma once
 #include "kva_internal.h"
 
+#include <type_traits>
+
 namespace kva {
+
+// The value of lane (lane ^ M), M a power of two below 64, by the cheapest
+// route: DPP moves inside a row of 16 lanes (xor 1 and 2: quad permutes; xor
+// 4: half-row mirror then quad reverse, i -> 7 - (i ^ 3) = i ^ 4; xor 8: row
+// rotate by 8), a swizzle inside 32 lanes (xor 16), a permute across the
+// halves (xor 32).  Same pairing as __shfl_xor, so the same results.
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+    const int x = __builtin_bit_cast(int, v);
+    int r;
+    if constexpr (M == 1) r = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);       // quad_perm 1,0,3,2
+    else if constexpr (M == 2) r = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);  // quad_perm 2,3,0,1
+    else if constexpr (M == 4) {
+        const int h = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true);              // row_half_mirror
+        r = __builtin_amdgcn_mov_dpp(h, 0x1B, 0xF, 0xF, true);                         // quad_perm 3,2,1,0
+    } else if constexpr (M == 8) r = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, true); // row_ror 8
+    else if constexpr (M == 16) r = __builtin_amdgcn_ds_swizzle(x, (16 << 10) | 0x1F);  // bitmask: xor 16
+    else {
+        static_assert(M == 32, "lane_xor: mask");
+        return __shfl_xor(v, 32);
+    }
+    return __builtin_bit_cast(float, r);
+}
 
 // Butterfly sum over the 64 lanes (fixed order; every lane gets the total).
 __device__ __forceinline__ float kv_wave_sum(float v) {
 #pragma clang fp contract(off)
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    v += lane_xor<32>(v);
+    v += lane_xor<16>(v);
+    v += lane_xor<8>(v);
+    v += lane_xor<4>(v);
+    v += lane_xor<2>(v);
+    v += lane_xor<1>(v);
     return v;
 }
 
@@ -131,16 +160,22 @@ __device__ __forceinline__ float4 kv_hadamard256(float4 x, int lane) {
 #pragma clang fp contract(off)
     float a0 = x.x + x.y, a1 = x.x - x.y, a2 = x.z + x.w, a3 = x.z - x.w;
     float b0 = a0 + a2, b1 = a1 + a3, b2 = a0 - a2, b3 = a1 - a3;
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-        const float o0 = __shfl_xor(b0, m), o1 = __shfl_xor(b1, m);
-        const float o2 = __shfl_xor(b2, m), o3 = __shfl_xor(b3, m);
+    auto stage = [&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        const float o0 = lane_xor<m>(b0), o1 = lane_xor<m>(b1);
+        const float o2 = lane_xor<m>(b2), o3 = lane_xor<m>(b3);
         const bool upper = lane & m;      // this lane holds the pair's second value
         b0 = upper ? o0 - b0 : b0 + o0;
         b1 = upper ? o1 - b1 : b1 + o1;
         b2 = upper ? o2 - b2 : b2 + o2;
         b3 = upper ? o3 - b3 : b3 + o3;
-    }
+    };
+    stage(std::integral_constant<int, 1>{});
+    stage(std::integral_constant<int, 2>{});
+    stage(std::integral_constant<int, 4>{});
+    stage(std::integral_constant<int, 8>{});
+    stage(std::integral_constant<int, 16>{});
+    stage(std::integral_constant<int, 32>{});
     return make_float4(b0 * 0.0625f, b1 * 0.0625f, b2 * 0.0625f, b3 * 0.0625f);
 }
 
@@ -163,9 +198,9 @@ __device__ __forceinline__ void kv_store_bf16(uint16_t* dst, float4 v) {
 __device__ __forceinline__ void kv_store_q8_0(uint8_t* row, float4 y, int lane) {
 #pragma clang fp contract(off)
     float am = fmaxf(fmaxf(fabsf(y.x), fabsf(y.y)), fmaxf(fabsf(y.z), fabsf(y.w)));
-    am = fmaxf(am, __shfl_xor(am, 1));
-    am = fmaxf(am, __shfl_xor(am, 2));
-    am = fmaxf(am, __shfl_xor(am, 4));
+    am = fmaxf(am, lane_xor<1>(am));
+    am = fmaxf(am, lane_xor<2>(am));
+    am = fmaxf(am, lane_xor<4>(am));
     const float d = am / 127.0f;
     const float yy[4] = {y.x, y.y, y.z, y.w};
     uint32_t packed = 0;
