@@ -120,25 +120,31 @@ __global__ void __launch_bounds__(kThreads) deltanet_scan(DnArgs g) {
     }
 
     __syncthreads();
-    for (int t0 = 0; t0 < T; t0 += kC) {
-        const int nv = T - t0 < kC ? T - t0 : kC;
-        // ---- conv + SiLU of this thread's channel (zero past the end); X holds
-        //      the values, then the right-hand side, then the solution.  Rows
-        //      past the end re-read the last row (values unused).
-        float X[kC];
-        float a_in = 0.f, b_in = 0.f;
+    // X holds a chunk's raw rows, then (after conv + SiLU) its values, then the
+    // right-hand side and solution; once the solution is stored, the next
+    // chunk's raw rows are loaded into it, so the loads overlap the state
+    // update.  Rows past the end re-read the last row (values unused).
+    float X[kC];
+    float a_in = 0.f, b_in = 0.f;
+    auto fetch = [&](int c0) {
         if (active) {
 #pragma unroll
             for (int r = 0; r < kC; ++r) {
-                const int t = t0 + r < T ? t0 + r : T - 1;
+                const int t = c0 + r < T ? c0 + r : T - 1;
                 X[r] = ly.x[(int64_t)t * ly.ld + ch];
             }
         }
-        if (gate_wave && lane < nv) {
-            const float* row = ly.x + (int64_t)(t0 + lane) * ly.ld;
+        if (gate_wave && lane < kC) {
+            const int t = c0 + lane < T ? c0 + lane : T - 1;
+            const float* row = ly.x + (int64_t)t * ly.ld;
             a_in = row[qkv + kh * G + gm];
             b_in = row[qkv + g.n_v + kh * G + gm];
         }
+    };
+    fetch(0);
+    for (int t0 = 0; t0 < T; t0 += kC) {
+        const int nv = T - t0 < kC ? T - t0 : kC;
+        // ---- conv + SiLU of this thread's channel (zero past the end)
 #pragma unroll
         for (int r = 0; r < kC; ++r) {
             const float xr = X[r];
@@ -268,6 +274,7 @@ __global__ void __launch_bounds__(kThreads) deltanet_scan(DnArgs g) {
                 *(f16x8*)&rowp[wt_index(j, r8)] = w8;
             }
         }
+        if (t0 + kC < T) fetch(t0 + kC);
         __syncthreads();
         // ---- S_m = gamma_C S0_m + sum_t (gamma_C / gamma_t) w_t k_t^T
 #pragma unroll
