@@ -151,3 +151,39 @@ def test_deltanet_argument_errors():
     kva.kva_deltanet_update(ls, 0, stream=st)                  # nothing to do
     torch.cuda.synchronize()
     assert np.array_equal(dev["S"][0].cpu().numpy(), S[0]) and np.array_equal(dev["c"][0].cpu().numpy(), conv[0])
+
+
+@pytest.mark.parametrize("n_k", [48, 24])
+def test_deltanet_other_groupings(n_k):
+    """Value heads per key head 1 (48 key heads) and 2 (24): the same widths of
+    q and k per head, so the rows are (2 n_k + 48) x 128 + 96 wide."""
+    n_v, T = 48, 45
+    qkv = (2 * n_k + n_v) * 128
+    rng = np.random.default_rng(60 + n_k)
+    rows = rng.standard_normal((T, qkv + 2 * n_v), dtype=np.float32)
+    conv_w = rng.uniform(-0.5, 0.5, (1, qkv, 4)).astype(np.float32)
+    _, a_log, dt_bias = synth.make_deltanet_params(1)
+    conv = rng.standard_normal((1, 3, qkv), dtype=np.float32)
+    S = (rng.standard_normal((1, n_v, 128, 128), dtype=np.float32) * np.float32(0.05))
+    ls, dev = _layers([rows], conv_w, a_log, dt_bias, conv, S)
+    kva.kva_deltanet_update(ls, T, n_k_heads=n_k, n_v_heads=n_v, stream=kva.current_stream())
+    torch.cuda.synchronize()
+    S_ref, c_ref = ref.deltanet_update(rows, conv_w[0], a_log[0], dt_bias[0], conv[0], S[0], n_k=n_k, n_v=n_v)
+    assert np.array_equal(dev["c"][0].cpu().numpy(), c_ref.astype(np.float32))
+    _check_state(dev["S"][0].cpu().numpy(), S_ref, f"n_k={n_k}")
+
+
+def test_deltanet_many_layers_one_call():
+    """33 layers in one call (launched 32 + 1): every layer updated, each
+    against the oracle."""
+    L, T = 33, 7
+    conv_w, a_log, dt_bias = synth.make_deltanet_params(L)
+    conv, S = synth.make_deltanet_state(L)
+    rows = [synth.make_deltanet_rows(T, seed=100 + i) for i in range(L)]
+    ls, dev = _layers(rows, conv_w, a_log, dt_bias, conv, S)
+    kva.kva_deltanet_update(ls, T, stream=kva.current_stream())
+    torch.cuda.synchronize()
+    for i in (0, 31, 32):
+        S_ref, c_ref = ref.deltanet_update(rows[i], conv_w[i], a_log[i], dt_bias[i], conv[i], S[i])
+        assert np.array_equal(dev["c"][i].cpu().numpy(), c_ref.astype(np.float32)), i
+        _check_state(dev["S"][i].cpu().numpy(), S_ref, f"layer {i} of 33")
