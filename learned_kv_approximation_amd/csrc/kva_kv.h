@@ -20,21 +20,23 @@ namespace kva {
 // rotate by 8), a swizzle inside 32 lanes (xor 16), a permute across the
 // halves (xor 32).  Same pairing as __shfl_xor, so the same results.
 template <int M>
-__device__ __forceinline__ float lane_xor(float v) {
-    const int x = __builtin_bit_cast(int, v);
-    int r;
-    if constexpr (M == 1) r = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);       // quad_perm 1,0,3,2
-    else if constexpr (M == 2) r = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);  // quad_perm 2,3,0,1
+__device__ __forceinline__ int lane_xor_bits(int x) {
+    if constexpr (M == 1) return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);       // quad_perm 1,0,3,2
+    else if constexpr (M == 2) return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);  // quad_perm 2,3,0,1
     else if constexpr (M == 4) {
-        const int h = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true);              // row_half_mirror
-        r = __builtin_amdgcn_mov_dpp(h, 0x1B, 0xF, 0xF, true);                         // quad_perm 3,2,1,0
-    } else if constexpr (M == 8) r = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, true); // row_ror 8
-    else if constexpr (M == 16) r = __builtin_amdgcn_ds_swizzle(x, (16 << 10) | 0x1F);  // bitmask: xor 16
+        const int h = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true);                  // row_half_mirror
+        return __builtin_amdgcn_mov_dpp(h, 0x1B, 0xF, 0xF, true);                          // quad_perm 3,2,1,0
+    } else if constexpr (M == 8) return __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, true); // row_ror 8
+    else if constexpr (M == 16) return __builtin_amdgcn_ds_swizzle(x, (16 << 10) | 0x1F);  // bitmask: xor 16
     else {
         static_assert(M == 32, "lane_xor: mask");
-        return __shfl_xor(v, 32);
+        return __shfl_xor(x, 32);
     }
-    return __builtin_bit_cast(float, r);
+}
+
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+    return __builtin_bit_cast(float, lane_xor_bits<M>(__builtin_bit_cast(int, v)));
 }
 
 // Butterfly sum over the 64 lanes (fixed order; every lane gets the total).
@@ -191,22 +193,27 @@ __device__ __forceinline__ void kv_store_bf16(uint16_t* dst, float4 v) {
 
 // q8_0 (ggml's block: fp16 scale d, 32 int8 codes, value d * q) of the
 // wave's 256 values into one row of 8 blocks of 34 bytes.  Block b holds dims
-// 32b..32b+31, i.e. lanes 8b..8b+7.  The quantisation is decided in fp32:
-// d = amax / 127 and q = round-half-away(y / d) (correctly rounded
-// divisions; q = 0 when d = 0), clamped to [-127, 127]; d is stored rounded
-// to fp16 (nearest even).  Must be called by all 64 lanes of a wave together.
+// 32b..32b+31, i.e. lanes 8b..8b+7.  The quantisation is decided in fp32 by
+// ggml's q8_0 block rule: d = amax / 127, its reciprocal 1/d (both correctly
+// rounded divisions; 0 when d = 0), q = round-half-away(y * (1/d)), clamped
+// to [-127, 127]; d is stored rounded to fp16 (nearest even).  Must be called
+// by all 64 lanes of a wave together.
 __device__ __forceinline__ void kv_store_q8_0(uint8_t* row, float4 y, int lane) {
 #pragma clang fp contract(off)
-    float am = fmaxf(fmaxf(fabsf(y.x), fabsf(y.y)), fmaxf(fabsf(y.z), fabsf(y.w)));
-    am = fmaxf(am, lane_xor<1>(am));
-    am = fmaxf(am, lane_xor<2>(am));
-    am = fmaxf(am, lane_xor<4>(am));
-    const float d = am / 127.0f;
+    // block maximum of |y|: non-negative binary32 values order as their bit
+    // patterns, so the exchanges compare integers
+    const float am0 = fmaxf(fmaxf(fabsf(y.x), fabsf(y.y)), fmaxf(fabsf(y.z), fabsf(y.w)));
+    uint32_t ab = __builtin_bit_cast(uint32_t, am0);
+    ab = max(ab, (uint32_t)lane_xor_bits<1>((int)ab));
+    ab = max(ab, (uint32_t)lane_xor_bits<2>((int)ab));
+    ab = max(ab, (uint32_t)lane_xor_bits<4>((int)ab));
+    const float d = __builtin_bit_cast(float, ab) / 127.0f;
+    const float id = d != 0.0f ? 1.0f / d : 0.0f;
     const float yy[4] = {y.x, y.y, y.z, y.w};
     uint32_t packed = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        float q = d != 0.0f ? roundf(yy[e] / d) : 0.0f;
+        float q = roundf(yy[e] * id);
         q = fminf(fmaxf(q, -127.0f), 127.0f);
         packed |= (uint32_t)(uint8_t)(int8_t)(int)q << (8 * e);
     }

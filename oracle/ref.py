@@ -414,14 +414,19 @@ def hadamard_rotate(x: np.ndarray) -> np.ndarray:
 
 
 def q8_0_quantize(y: np.ndarray):
-    """q8_0 blocks of the last axis (a multiple of 32), decided in binary32.
-    Returns (scale bits uint16 [..., nb], codes int8 [..., nb, 32])."""
+    """q8_0 blocks of the last axis (a multiple of 32), decided in binary32,
+    by ggml's q8_0 block rule (the cache type the engine of [KVA] *Projector
+    quantization and flash-attn* writes): d = amax / 127, the reciprocal
+    1/d formed once per block, each code = round-half-away(y * (1/d)),
+    0 for an all-zero block.  Returns (scale bits uint16 [..., nb], codes
+    int8 [..., nb, 32])."""
     y32 = np.asarray(y, dtype=np.float64).astype(np.float32)
     blk = y32.reshape(y32.shape[:-1] + (y32.shape[-1] // Q8_0_BLOCK, Q8_0_BLOCK))
     amax = np.max(np.abs(blk), axis=-1)
     d = (amax / np.float32(127.0)).astype(np.float32)          # binary32 division
     safe = np.where(d == 0, np.float32(1.0), d)
-    t = (blk / safe[..., None]).astype(np.float32)             # binary32 division
+    inv = (np.float32(1.0) / safe).astype(np.float32)          # binary32 reciprocal
+    t = (blk * inv[..., None]).astype(np.float32)              # binary32 product
     t64 = t.astype(np.float64)                                  # exact
     q = np.sign(t64) * np.floor(np.abs(t64) + 0.5)              # half away from zero, exact in float64
     q = np.clip(q, -127, 127)

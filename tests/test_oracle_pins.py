@@ -471,6 +471,15 @@ def test_q8_0_quantize_hand_blocks():
     d1 = np.float32(3.0) / np.float32(127.0)
     assert d[1] == ref.f64_to_f16_bits(np.array([float(d1)]))[0]
     assert q[1, :3].tolist() == [-127, 64, 32]   # 1.5/d1 = 63.5 -> 64; 0.75/d1 = 31.75 -> 32
+    # the code is decided on y times the block's reciprocal, not on y / d: with
+    # amax 3 and y one ulp below fl32(2.5 d), y / d rounds to 2.5 but
+    # y * fl32(1/d) = 2.4999998 in binary32, so the code is 2, not 3
+    d3 = np.float32(3.0) / np.float32(127.0)
+    y2 = np.zeros(32, np.float32)
+    y2[0], y2[1] = 3.0, np.nextafter(np.float32(2.5) * d3, np.float32(0.0))
+    assert y2[1] / d3 == np.float32(2.5) and y2[1] * (np.float32(1.0) / d3) < np.float32(2.5)
+    _, q = ref.q8_0_quantize(y2.astype(np.float64))
+    assert q[0, :2].tolist() == [127, 2]
     # an all-zero block has d = 0 and codes 0
     d, q = ref.q8_0_quantize(np.zeros(32))
     assert d[0] == 0 and not q.any()
