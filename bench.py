@@ -166,7 +166,10 @@ def time_kv_write(n_tokens: int = 65536, layers: int = 8, chunk: int = 8192, ste
     import learned_kv_approximation_amd as kva
 
     gains, ptab, n_pages = synth.make_kv_write_inputs(n_tokens, n_layers=layers)
-    kv = torch.from_numpy(synth.make_kv_rows(chunk, scale=3.0)).cuda()
+    # one input buffer per layer (8 x 64 MiB at 8192 tokens per call), so that
+    # the reads are not served from the last-level cache
+    kv0 = torch.from_numpy(synth.make_kv_rows(chunk, scale=3.0)).cuda()
+    kvs = [kv0.clone() for _ in range(layers)]
     g = torch.from_numpy(gains).cuda()
     pt = torch.from_numpy(ptab).cuda()
     row_bytes = 272 if q8 else 512
@@ -180,7 +183,7 @@ def time_kv_write(n_tokens: int = 65536, layers: int = 8, chunk: int = 8192, ste
     def step():
         for c0 in range(0, n_tokens, chunk):
             for li in range(layers):
-                kva.kva_attn_kv_write(kv.data_ptr(), 2048, chunk, c0, g[li].data_ptr(), caches[li], st)
+                kva.kva_attn_kv_write(kvs[li].data_ptr(), 2048, chunk, c0, g[li].data_ptr(), caches[li], st)
 
     step()
     torch.cuda.synchronize()
@@ -192,7 +195,7 @@ def time_kv_write(n_tokens: int = 65536, layers: int = 8, chunk: int = 8192, ste
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     nbytes = n_tokens * layers * (2048 * 4 + 2 * 4 * row_bytes)
-    del pools
+    del pools, kvs
     torch.cuda.empty_cache()
     return {"tokens": n_tokens, "layers": layers, "cache": "q8_0 + Hadamard" if q8 else "bf16",
             "ms": round(ms, 4), "bytes": nbytes,

@@ -90,38 +90,52 @@ __device__ __forceinline__ void kv_sincos(double th, float* sn, float* cs) {
     *cs = ((qi + 1) & 2) ? -cv : cv;
 }
 
-// k_norm then RoPE on one KV head of one token at absolute position p.
+// Sine and cosine of the rotary angles of lane l's 4 dims at absolute
+// position p: lane j < n_rot/2 turns the angle of pair j (kv_sincos, formed in
+// double: p reaches 65535 and more, where an fp32 product would be off by
+// several 1e-3 rad) and the lanes holding the pair's two values fetch it
+// from there.  The same for every KV head of the token.  Must be called by
+// all 64 lanes of a wave together.
+struct KvAngles {
+    float sn[4], cs[4];
+};
+
+__device__ __forceinline__ KvAngles kv_rope_angles(int lane, int64_t p, const KvLane& L, int n_rot) {
+    float sj, cj;
+    kv_sincos((double)(int32_t)p * L.inv_freq, &sj, &cj);     // positions are below 2^31 (checked on the host)
+    const int half_lanes = n_rot / 8;          // lanes holding the first half of the rotary dims
+    const int j0 = (lane < half_lanes ? lane : lane - half_lanes) * 4;
+    KvAngles A;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        A.sn[e] = __shfl(sj, j0 + e);
+        A.cs[e] = __shfl(cj, j0 + e);
+    }
+    return A;
+}
+
+// k_norm then RoPE on one KV head of one token, with the token's angles.
 //   k_norm: k / sqrt(mean(k^2) + eps) * gain (per KV head, 256 dims);
 //   RoPE: the pair (j, j + n_rot/2), j < n_rot/2, is turned by p * inv_freq[j].
-// The rotary pair of lane l < n_rot/8 lives in lane l + n_rot/8.  Each angle
-// is formed in double and reduced to a quarter turn there (kv_sincos): p
-// reaches 65535 and more, where an fp32 product would be off by several 1e-3
-// rad.
+// The rotary pair of lane l < n_rot/8 lives in lane l + n_rot/8.
 // Must be called by all 64 lanes of a wave together.
-__device__ __forceinline__ float4 kv_k_norm_rope(float4 k, int lane, int64_t p, const KvLane& L,
+__device__ __forceinline__ float4 kv_k_norm_rope(float4 k, int lane, const KvAngles& A, const KvLane& L,
                                                  int n_rot, float eps) {
     // No multiply-add contraction: whether the compiler fuses a product into
     // an add may depend on the code around an inlined copy, and every caller
     // must round exactly alike.
 #pragma clang fp contract(off)
     const float ss = kv_wave_sum(k.x * k.x + k.y * k.y + k.z * k.z + k.w * k.w);
-    const float r = 1.0f / sqrtf(ss / (float)kKvHeadDim + eps);
+    const float r = __builtin_amdgcn_rsqf(ss / (float)kKvHeadDim + eps);   // hardware reciprocal square root (~1 ulp)
     k.x *= r * L.gain.x; k.y *= r * L.gain.y; k.z *= r * L.gain.z; k.w *= r * L.gain.w;
 
-    // lane j < n_rot/2 turns the angle of pair j; the lanes holding the
-    // pair's two values fetch it from there
-    float sj, cj;
-    kv_sincos((double)p * L.inv_freq, &sj, &cj);
-    const int half_lanes = n_rot / 8;          // lanes holding the first half of the rotary dims
-    const float4 other = make_float4(__shfl_xor(k.x, half_lanes), __shfl_xor(k.y, half_lanes),
-                                     __shfl_xor(k.z, half_lanes), __shfl_xor(k.w, half_lanes));
-    const int j0 = (lane < half_lanes ? lane : lane - half_lanes) * 4;
-    float sn[4], cs[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        sn[e] = __shfl(sj, j0 + e);
-        cs[e] = __shfl(cj, j0 + e);
-    }
+    const int half_lanes = n_rot / 8;
+    float4 other;
+    if (half_lanes == 8)        // 64 rotary dims: the partner is 8 lanes away inside a row of 16
+        other = make_float4(lane_xor<8>(k.x), lane_xor<8>(k.y), lane_xor<8>(k.z), lane_xor<8>(k.w));
+    else
+        other = make_float4(__shfl_xor(k.x, half_lanes), __shfl_xor(k.y, half_lanes),
+                            __shfl_xor(k.z, half_lanes), __shfl_xor(k.w, half_lanes));
     if (lane < 2 * half_lanes) {
         const bool first = lane < half_lanes;
         float kk[4] = {k.x, k.y, k.z, k.w};
@@ -129,10 +143,16 @@ __device__ __forceinline__ float4 kv_k_norm_rope(float4 k, int lane, int64_t p, 
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             // first half: x' = x cos - y sin ; second half: y' = x sin + y cos
-            kk[e] = first ? (kk[e] * cs[e] - oo[e] * sn[e]) : (oo[e] * sn[e] + kk[e] * cs[e]);
+            kk[e] = first ? (kk[e] * A.cs[e] - oo[e] * A.sn[e]) : (oo[e] * A.sn[e] + kk[e] * A.cs[e]);
         k = make_float4(kk[0], kk[1], kk[2], kk[3]);
     }
     return k;
+}
+
+// The same at absolute position p (angles formed here).
+__device__ __forceinline__ float4 kv_k_norm_rope(float4 k, int lane, int64_t p, const KvLane& L,
+                                                 int n_rot, float eps) {
+    return kv_k_norm_rope(k, lane, kv_rope_angles(lane, p, L, n_rot), L, n_rot, eps);
 }
 
 // Physical page of position p (positions are below 2^31, checked on the
@@ -158,27 +178,61 @@ __device__ __forceinline__ int64_t kv_row_index(const KvPool& c, int pg, int64_t
 // quantised KV cache stores K and V rotated this way ([KVA] "Projector
 // quantization and flash-attn": the approximated K/V get the exact path's
 // Hadamard rotation).  Must be called by all 64 lanes of a wave together.
+//
+// A cross-lane stage is one fused multiply-add per value, b <- b + c * o with
+// o the partner lane's value and c = -1 on the lane whose stage bit is set,
+// 1 on the other: that lane then holds b - o, the exact negation of the
+// butterfly's o - b (o * c is exact, so the sum is rounded once, and
+// rounding to nearest is symmetric).  Its partner differs from it only in
+// bits of later stages, so both carry the same sign and every later stage
+// stays a plain sum or difference; the sign of the result is
+// (-1)^popcount(lane), folded into the 1/16 scale.  The stages inside a row
+// of 16 lanes take the partner's value by DPP as the multiply-add's first
+// operand (one instruction per value; a DPP read needs two wait states after
+// the write of its source, which the s_nop gives for the first read and the
+// interleaving of the four values for the others).
 __device__ __forceinline__ float4 kv_hadamard256(float4 x, int lane) {
 #pragma clang fp contract(off)
-    float a0 = x.x + x.y, a1 = x.x - x.y, a2 = x.z + x.w, a3 = x.z - x.w;
+    const float a0 = x.x + x.y, a1 = x.x - x.y, a2 = x.z + x.w, a3 = x.z - x.w;
     float b0 = a0 + a2, b1 = a1 + a3, b2 = a0 - a2, b3 = a1 - a3;
-    auto stage = [&](auto mc) {
-        constexpr int m = decltype(mc)::value;
-        const float o0 = lane_xor<m>(b0), o1 = lane_xor<m>(b1);
-        const float o2 = lane_xor<m>(b2), o3 = lane_xor<m>(b3);
-        const bool upper = lane & m;      // this lane holds the pair's second value
-        b0 = upper ? o0 - b0 : b0 + o0;
-        b1 = upper ? o1 - b1 : b1 + o1;
-        b2 = upper ? o2 - b2 : b2 + o2;
-        b3 = upper ? o3 - b3 : b3 + o3;
-    };
-    stage(std::integral_constant<int, 1>{});
-    stage(std::integral_constant<int, 2>{});
-    stage(std::integral_constant<int, 4>{});
-    stage(std::integral_constant<int, 8>{});
-    stage(std::integral_constant<int, 16>{});
-    stage(std::integral_constant<int, 32>{});
-    return make_float4(b0 * 0.0625f, b1 * 0.0625f, b2 * 0.0625f, b3 * 0.0625f);
+    const float c1 = (lane & 1) ? -1.0f : 1.0f, c2 = (lane & 2) ? -1.0f : 1.0f;
+    const float c4 = (lane & 4) ? -1.0f : 1.0f, c8 = (lane & 8) ? -1.0f : 1.0f;
+    float t0, t1, t2, t3;
+    asm("s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %2, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %3, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %0, %9 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %9 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %2, %9 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %3, %9 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        // xor 4: half-row mirror, then the quad reversal as the DPP operand
+        "v_mov_b32_dpp %4, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "v_mov_b32_dpp %5, %1 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "v_mov_b32_dpp %6, %2 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "v_mov_b32_dpp %7, %3 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %10 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %10 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %10 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %10 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %0, %11 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %11 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %2, %11 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %3, %11 row_ror:8 row_mask:0xf bank_mask:0xf"
+        : "+v"(b0), "+v"(b1), "+v"(b2), "+v"(b3), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)
+        : "v"(c1), "v"(c2), "v"(c4), "v"(c8));
+    const float c16 = (lane & 16) ? -1.0f : 1.0f, c32 = (lane & 32) ? -1.0f : 1.0f;
+    b0 = __builtin_fmaf(lane_xor<16>(b0), c16, b0);
+    b1 = __builtin_fmaf(lane_xor<16>(b1), c16, b1);
+    b2 = __builtin_fmaf(lane_xor<16>(b2), c16, b2);
+    b3 = __builtin_fmaf(lane_xor<16>(b3), c16, b3);
+    b0 = __builtin_fmaf(lane_xor<32>(b0), c32, b0);
+    b1 = __builtin_fmaf(lane_xor<32>(b1), c32, b1);
+    b2 = __builtin_fmaf(lane_xor<32>(b2), c32, b2);
+    b3 = __builtin_fmaf(lane_xor<32>(b3), c32, b3);
+    const float sc = (__builtin_popcount(lane) & 1) ? -0.0625f : 0.0625f;
+    return make_float4(b0 * sc, b1 * sc, b2 * sc, b3 * sc);
 }
 
 // Round to bf16 (nearest even) and store 4 values.
@@ -210,12 +264,18 @@ __device__ __forceinline__ void kv_store_q8_0(uint8_t* row, float4 y, int lane) 
     const float d = __builtin_bit_cast(float, ab) / 127.0f;
     const float id = d != 0.0f ? 1.0f / d : 0.0f;
     const float yy[4] = {y.x, y.y, y.z, y.w};
+    // round half away from zero as trunc(t + copysign(h, t)), h the largest
+    // binary32 below 1/2: for |t| < 2^23 the sum rounds up to the next integer
+    // exactly when t's fraction is at least 1/2 (checked over every such
+    // binary32 value); the float-to-int conversion truncates
+    const float h = __builtin_bit_cast(float, 0x3EFFFFFFu);
     uint32_t packed = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        float q = roundf(yy[e] * id);
-        q = fminf(fmaxf(q, -127.0f), 127.0f);
-        packed |= (uint32_t)(uint8_t)(int8_t)(int)q << (8 * e);
+        const float t = yy[e] * id;
+        int q = (int)(t + copysignf(h, t));
+        q = min(max(q, -127), 127);
+        packed |= (uint32_t)(uint8_t)(int8_t)q << (8 * e);
     }
     uint8_t* blk = row + (lane >> 3) * 34;
     uint16_t* codes = reinterpret_cast<uint16_t*>(blk + 2 + (lane & 7) * 4);   // 2-byte aligned

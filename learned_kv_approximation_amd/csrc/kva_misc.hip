@@ -134,10 +134,11 @@ __global__ void __launch_bounds__(256) kv_write_kernel(KvWriteArgs a) {
     const int64_t row = kv_row_index(a.pool, pg, p, kvh);
     const float* kr = a.kv + (int64_t)t * a.ld_kv + kvh * kKvHeadDim;
     const float* vr = kr + kKvHeads * kKvHeadDim;
+    const float4 k0 = *(const float4*)(kr + lane * 4);
+    const float4 v0 = *(const float4*)(vr + lane * 4);
     const KvLane L = kv_lane_setup(lane, a.pool.k_gain, a.rope);
-    const float4 k = kv_k_norm_rope(*(const float4*)(kr + lane * 4), lane, p, L, a.rope.n_rot, a.rope.eps);
-    kv_store_row(a.pool, true, row, lane, k);
-    kv_store_row(a.pool, false, row, lane, *(const float4*)(vr + lane * 4));
+    kv_store_row(a.pool, true, row, lane, kv_k_norm_rope(k0, lane, p, L, a.rope.n_rot, a.rope.eps));
+    kv_store_row(a.pool, false, row, lane, v0);
 }
 
 __global__ void dequant_q8_0_kernel(const uint8_t* __restrict__ blocks, int64_t n_blocks,
