@@ -42,14 +42,15 @@ __host__ __device__ inline int64_t q8_code_chunk(int64_t row, int64_t k, int64_t
     const int64_t c = (k % 32) / 8;
     return ((nb * (K / 32) + kt) * kWeightTileRows + r) * 32 + ((c ^ ((r >> 2) & 3)) * 8);
 }
-// The 8-byte chunk of 8 int8 codes (q[e] = code of K-value 8c + e): each
-// 32-bit half holds codes 4j, 4j + 2, 4j + 1, 4j + 3 in its bytes 0..3, so
-// that one mask puts a pair of consecutive codes into the two 16-bit halves.
+// The 8-byte chunk of 8 int8 codes (q[e] = code of K-value 8c + e), each
+// stored as the unsigned byte q + 128 (q ^ 0x80): each 32-bit half holds
+// codes 4j, 4j + 2, 4j + 1, 4j + 3 in its bytes 0..3, so that one byte
+// permute puts a pair of consecutive codes into the two 16-bit halves.
 __host__ __device__ inline void q8_chunk_pack(const int8_t q[8], uint32_t* c0, uint32_t* c1) {
     uint32_t w[2];
     for (int j = 0; j < 2; ++j)
-        w[j] = (uint32_t)(uint8_t)q[4 * j] | ((uint32_t)(uint8_t)q[4 * j + 2] << 8) |
-               ((uint32_t)(uint8_t)q[4 * j + 1] << 16) | ((uint32_t)(uint8_t)q[4 * j + 3] << 24);
+        w[j] = (uint32_t)(uint8_t)(q[4 * j] ^ 0x80) | ((uint32_t)(uint8_t)(q[4 * j + 2] ^ 0x80) << 8) |
+               ((uint32_t)(uint8_t)(q[4 * j + 1] ^ 0x80) << 16) | ((uint32_t)(uint8_t)(q[4 * j + 3] ^ 0x80) << 24);
     *c0 = w[0];
     *c1 = w[1];
 }
@@ -195,12 +196,13 @@ __device__ __forceinline__ void q4_0_f16x8(uint32_t codes, uint16_t d_bits, uint
     }
 }
 
-// Eight q8_0 weights as the fp16 values the MFMA consumes: a chunk of 8 int8
-// codes q (q8_chunk_pack order) times the fp16 scale d_bits, each product
-// rounded once to nearest-even fp16.  Each code pair goes into the mantissas
-// of two fp16 values 1024 + (q + 128) (bits 0x6400 | (q ^ 0x80); exact: the
-// spacing there is 1), 1152 is subtracted exactly, and one fp16 multiply
-// (correctly rounded, so this is q8_0_value rounded once) applies d.
+// Eight q8_0 weights as the fp16 values the MFMA consumes: a chunk of 8
+// codes (q8_chunk_pack order and bias) times the fp16 scale d_bits, each
+// product rounded once to nearest-even fp16.  One byte permute puts a code
+// pair under the exponent byte 0x64, i.e. into the mantissas of two fp16
+// values 1024 + (q + 128) (exact: the spacing there is 1); 1152 is
+// subtracted exactly, and one fp16 multiply (correctly rounded, so this is
+// q8_0_value rounded once) applies d: three instructions per pair.
 // out[h] packs K-values 2h (low half) and 2h + 1.
 __device__ __forceinline__ void q8_0_f16x8(uint32_t c0, uint32_t c1, uint16_t d_bits, uint32_t out[4]) {
     const _Float16 d = __builtin_bit_cast(_Float16, d_bits);
@@ -208,8 +210,10 @@ __device__ __forceinline__ void q8_0_f16x8(uint32_t c0, uint32_t c1, uint16_t d_
     const kva_half2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-        const uint32_t w = (h < 2 ? c0 : c1) >> (8 * (h & 1));
-        const uint32_t t = (w & 0x00FF00FFu) ^ 0x64806480u;      // 1024 + (q ^ 0x80), two halves
+        // bytes 4..7 of the permute's input are the codes word, bytes 0..3 the
+        // exponent byte: result bytes (code 2 or 3, 0x64, code 0 or 1, 0x64)
+        const uint32_t sel = (h & 1) ? 0x00070005u : 0x00060004u;
+        const uint32_t t = __builtin_amdgcn_perm(h < 2 ? c0 : c1, 0x64646464u, sel);
         const kva_half2 v = (__builtin_bit_cast(kva_half2, t) - off) * dd;
         out[h] = __builtin_bit_cast(uint32_t, v);
     }
