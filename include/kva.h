@@ -222,9 +222,11 @@ kva_status kva_map_project(kva_ctx* ctx, const float* x, int32_t n_tokens, float
  * orthonormal Walsh-Hadamard transform of Sylvester order, y = H x / 16 with
  * H[i][j] = (-1)^popcount(i & j) over the 256 dims (an orthogonal involution:
  * a consumer rotates queries alike, or rotates y back), then stored as 8 q8_0
- * blocks of 32 consecutive dims, decided in fp32: d = amax / 127,
- * q = round-half-away(y / d) (0 when d = 0), clamped to [-127, 127], d stored
- * rounded to fp16 (nearest even). */
+ * blocks of 32 consecutive dims, decided in fp32 by ggml's q8_0 block rule:
+ * d = amax / 127, its reciprocal 1/d formed once (0 when d = 0),
+ * q = round-half-away(y * (1/d)), clamped to [-127, 127], d stored rounded
+ * to fp16 (nearest even).  The rotation itself is computed in fp32 (exact
+ * for integer-valued rows of moderate size). */
 typedef struct {
     void* k_pool;
     void* v_pool;
