@@ -219,7 +219,7 @@ __device__ __forceinline__ void q8_0_f16x8(uint32_t c0, uint32_t c1, uint16_t d_
     }
 }
 // 256x256: 8 waves (2 per SIMD); 128x128: 4 waves.
-enum GemmTile : int { TILE_256x256 = 0, TILE_128x128 = 1 };
+enum GemmTile : int { TILE_256x256 = 0, TILE_128x128 = 1, TILE_256x128 = 2 };
 
 // The GEMM.  A rows are grouped by 256 like the weight rows (rows >= M of
 // the last group are read and dropped).  32-wide K slabs through a ring of
