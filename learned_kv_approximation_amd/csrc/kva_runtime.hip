@@ -38,9 +38,15 @@ kva_status fail(kva_status s, const char* fmt, ...) {
 
 // Split count of the GEMMs whose N is the trunk width (input, O, down): with
 // only d = 2560-3072 columns they fill too few workgroups at 1024 tokens.
-// Fixed (it may depend on N and K, never on the token count): a row's
-// reduction order, hence its bits, must not depend on the call's size.
-constexpr int kSplitNarrow = 2;
+// Fixed per context (from d and max_tokens, never from a call's token count):
+// a row's reduction order, hence its bits, must not depend on the call's
+// size.  Three K-ranges when a context with 16-bit trunk weights takes at
+// most one 1024-token ubatch per call and the three ranges of its 256x128
+// tiles still fit one round over 256 CUs (d <= 2688); two otherwise (more
+// partials to fold cost more than they gain once the tiles fill the device).
+inline int split_narrow(int64_t d, int64_t max_tokens, bool f16_trunk) {
+    return (f16_trunk && max_tokens <= 1024 && d % 128 == 0 && 4 * (d / 128) * 3 <= 256) ? 3 : 2;
+}
 
 #define KVA_TRY(expr)                    \
     do {                                 \
@@ -228,7 +234,8 @@ struct kva_ctx {
     uint16_t* o16 = nullptr;    // [m][hd]     fp16 attention output
     uint16_t* act16 = nullptr;  // [m][F]      fp16 SwiGLU output
     uint16_t* z16 = nullptr;    // [m][d]      final-normed trunk state: bf16 (fp16 for q8_0)
-    float* ws = nullptr;        // [kSplitNarrow][m][d] split-K partials of the N = d GEMMs
+    float* ws = nullptr;        // [n_split][m][d] split-K partials of the N = d GEMMs
+    int n_split = 2;            // split count of the N = d GEMMs (split_narrow)
 
     kva_stats stats{};
 
@@ -548,7 +555,8 @@ kva_status create_impl(const kva_config* cfg, const kva_weights* w, int device, 
     HIP_TRY(ctx->alloc(&ctx->o16, (size_t)m * hd * 2, false));
     HIP_TRY(ctx->alloc(&ctx->act16, (size_t)m * F * 2, false));
     HIP_TRY(ctx->alloc(&ctx->z16, (size_t)m * d * 2, false));
-    HIP_TRY(ctx->alloc(&ctx->ws, (size_t)kSplitNarrow * m * d * 4, false));
+    ctx->n_split = split_narrow(d, c.max_tokens, !ctx->q8 && !ctx->q4);
+    HIP_TRY(ctx->alloc(&ctx->ws, (size_t)ctx->n_split * m * d * 4, false));
     // Scratch rows past n_tokens feed MFMA rows whose results are dropped; zero
     // them once so they always hold finite values.
     HIP_TRY(hipMemset(ctx->u16, 0, (size_t)m * n_in * 2));
@@ -724,19 +732,19 @@ kva_status project(kva_ctx* ctx, const float* x, int32_t n, float* const* head_o
         return launch_gemm_t32(opd, pick_tile_t32(g.M, g.N, g.splits, opd == OPD_F16), epi, g, s);
     };
     const int64_t pstride = ctx->m_alloc * d;   // between split-K partial buffers
-    // The narrow GEMMs (N = d: input, O, down) write kSplitNarrow partials to
-    // ws; the next norm folds them into h in a fixed order.
+    // The narrow GEMMs (N = d: input, O, down) write n_split partials to ws;
+    // the next norm folds them into h in a fixed order.
     auto narrow = [&](const uint16_t* A, int64_t K, const kva_ctx::DevW& W, int stage) -> kva_status {
         GemmArgs g;
         g.A = A; g.lda = K; set_b(g, W, K);
         g.M = n; g.N = (int32_t)round_up(d, kColPad); g.K = (int32_t)K;
-        g.splits = kSplitNarrow; g.split_stride = pstride;
+        g.splits = ctx->n_split; g.split_stride = pstride;
         g.epi.out_f32 = ctx->ws; g.epi.ld_f32 = d; g.epi.n_real = (int32_t)d;
         STAGE(stage, gemm(EPI_PARTIAL, g));
         return KVA_OK;
     };
     auto fold = [&](bool add, const float* gain, uint16_t* out, bool bf16) -> kva_status {
-        STAGE(KVA_STAGE_NORM, launch_fold_rmsnorm(ctx->h, d, add, ctx->ws, kSplitNarrow, pstride, d, gain, n,
+        STAGE(KVA_STAGE_NORM, launch_fold_rmsnorm(ctx->h, d, add, ctx->ws, ctx->n_split, pstride, d, gain, n,
                                                   (int32_t)d, c.eps, out, bf16, s));
         return KVA_OK;
     };
