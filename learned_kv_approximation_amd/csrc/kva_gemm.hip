@@ -520,7 +520,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_t32(GemmArgs g) {
 // The head GEMM in one launch of two parts: the first n_big 256-column
 // N-tiles as 256x256 tiles (a whole number of rounds over the CUs), the
 // remaining columns as 128 x SBN tiles (a quarter or half of the work), so
-// that the last round is that much shorter.  Both tile shapes accumulate K
+// that no round of 256x256 tiles is left partly empty.  Both tile shapes accumulate K
 // in the same order: the split point never changes the bits.  SBN: 128, or
 // 256 for q8_0 (whose 128-column weight slab is too small for 8 waves' DMA).
 template <int OPD>
@@ -532,15 +532,21 @@ __global__ void __launch_bounds__(512) gemm_t32_heads(GemmArgs g, int n_big, int
     using ShB = T32Shape<256, 256, OPD, EPI_HEADS>;
     using ShS = T32Shape<128, SBN, OPD, EPI_HEADS>;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[ShB::BYTES > ShS::BYTES ? ShB::BYTES : ShS::BYTES];
-    if ((int)blockIdx.x < grid_big) {
+    // The small tiles go first: the CUs that start with one finish it after
+    // about a third of a 256x256 tile and from then on run their 256x256
+    // tiles out of phase with the others, so that the tiles' epilogues (each
+    // writes 256 KB) are not all due at once (measured: 1.7% faster on r2,
+    // 3% on r3, than with the small tiles last).
+    const int grid_small = (int)gridDim.x - grid_big;
+    if ((int)blockIdx.x >= grid_small) {
         const int mt = (g.M + 255) / 256;
-        const int v = xcd_remap(blockIdx.x, grid_big);
+        const int v = xcd_remap(blockIdx.x - grid_small, grid_big);
         if (v >= mt * n_big) return;
         t32_tile<256, 256, 2, 4, OPD, EPI_HEADS>(g, v % mt, v / mt, 0, smem);
     } else {
         const int mt = (g.M + 127) / 128;
         const int tn0 = n_big * (256 / SBN);            // first SBN-column tile
-        const int v = xcd_remap(blockIdx.x - grid_big, gridDim.x - grid_big);
+        const int v = xcd_remap(blockIdx.x, grid_small);
         if (v >= mt * (g.N / SBN - tn0)) return;
         t32_tile<128, SBN, 2, 4, OPD, EPI_HEADS>(g, v % mt, tn0 + v / mt, 0, smem);
     }
