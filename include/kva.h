@@ -164,7 +164,10 @@ kva_status kva_create(const kva_config* cfg, const kva_weights* w, int device, k
  * attn_block tokens starting at token 0; the last block may be shorter.
  * Attention is causal within a block and never crosses blocks, so a block's
  * outputs are bitwise identical whether it is passed alone or inside a longer
- * call.  1 <= n_tokens <= max_tokens (else KVA_ERR_SHAPE).  Output buffers
+ * call on the same context.  (The K split of the trunk's d-wide GEMMs is
+ * fixed per context from d_model and max_tokens, so contexts created with a
+ * different max_tokens may differ in the last bits, within the tolerance.)
+ * 1 <= n_tokens <= max_tokens (else KVA_ERR_SHAPE).  Output buffers
  * must not alias x or each other.  Asynchronous on `stream`. */
 kva_status kva_project_ubatch(kva_ctx* ctx, const float* x, int32_t n_tokens,
                               float* const* head_out, void* stream);
