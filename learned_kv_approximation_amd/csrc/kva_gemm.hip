@@ -521,10 +521,11 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_t32(GemmArgs g) {
 // N-tiles as 256x256 tiles (a whole number of rounds over the CUs), the
 // remaining columns as 128 x SBN tiles (a quarter or half of the work), so
 // that no round of 256x256 tiles is left partly empty.  Both tile shapes accumulate K
-// in the same order: the split point never changes the bits.  SBN: 128, or
-// 256 for q8_0 (whose 128-column weight slab is too small for 8 waves' DMA).
+// in the same order: the split point never changes the bits.  SBN: 256 (a
+// half tile: q8_0's 128-column weight slab is too small for 8 waves' DMA,
+// and for bf16 it measured 0.5% faster than 128), 128 for q4_0.
 template <int OPD>
-constexpr int kTailBN = OPD == OPD_Q8 ? 256 : 128;   // q4_0's 128-column slab fits 8 waves' DMA
+constexpr int kTailBN = OPD == OPD_Q4 ? 128 : 256;
 
 template <int OPD>
 __global__ void __launch_bounds__(512) gemm_t32_heads(GemmArgs g, int n_big, int grid_big) {
@@ -533,8 +534,8 @@ __global__ void __launch_bounds__(512) gemm_t32_heads(GemmArgs g, int n_big, int
     using ShS = T32Shape<128, SBN, OPD, EPI_HEADS>;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[ShB::BYTES > ShS::BYTES ? ShB::BYTES : ShS::BYTES];
     // The small tiles go first: the CUs that start with one finish it after
-    // about a third of a 256x256 tile and from then on run their 256x256
-    // tiles out of phase with the others, so that the tiles' epilogues (each
+    // about half a 256x256 tile and from then on run their 256x256 tiles out
+    // of phase with the others, so that the tiles' epilogues (each
     // writes 256 KB) are not all due at once (measured: 1.7% faster on r2,
     // 3% on r3, than with the small tiles last).
     const int grid_small = (int)gridDim.x - grid_big;
