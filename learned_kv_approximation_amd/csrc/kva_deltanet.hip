@@ -46,7 +46,7 @@ struct DnSmem {
     _Float16 s0h[kG][kD][kRowH];       // chunk-start states [m][v][k] (padded rows)
     _Float16 kht[kD][kRowT];           // unit keys transposed [k][t]
     _Float16 kh[kC][kRowH];            // unit keys [t][k]
-    float aft[kG][kC][kC];             // A transposed [m][i][t]
+    float aft[kG][kC][kC + 4];         // A transposed [m][i][t] (rows padded: a lane per i writes a column)
     float gcum[kG][kC];                // G_t = log gamma_t
     float beta[kG][kC];
     float gam[kG][kC];                 // gamma_t
@@ -184,7 +184,9 @@ __global__ void __launch_bounds__(kThreads) deltanet_scan(DnArgs g) {
             float ss = 0.0f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float v = sm.r1.kr[r][part * 16 + i];
+                // element 8 ((i + r) % 16) + part: the 64 lanes of a wave
+                // (8 tokens x 8 parts) fall on 64 different banks
+                const float v = sm.r1.kr[r][((i + r) & 15) * 8 + part];
                 ss += v * v;
             }
             ss += __shfl_xor(ss, 1);
@@ -195,10 +197,14 @@ __global__ void __launch_bounds__(kThreads) deltanet_scan(DnArgs g) {
         __syncthreads();
         if (is_k) {
 #pragma unroll
-            for (int r = 0; r < kC; ++r) {
-                const _Float16 hv16 = (_Float16)(X[r] * sm.rn[r]);
-                sm.kh[r][j] = hv16;
-                sm.kht[j][r] = hv16;
+            for (int r8 = 0; r8 < kC; r8 += 8) {
+                f16x8 h8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    h8[e] = (_Float16)(X[r8 + e] * sm.rn[r8 + e]);
+                    sm.kh[r8 + e][j] = h8[e];
+                }
+                *(f16x8*)&sm.kht[j][r8] = h8;           // this channel's row, 16 bytes at a time
             }
         }
         __syncthreads();
