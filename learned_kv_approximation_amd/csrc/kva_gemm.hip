@@ -382,7 +382,7 @@ __device__ __forceinline__ void t32_tile(const GemmArgs& g, int tm, int tn, int 
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     const int frow = lane & 31, fk = lane >> 5;
-    const int sw = ((frow >> 1) ^ (frow >> 3)) & 3;     // fragment rows differ by multiples of 32
+    const int sw = tiled32_swizzle(frow);                // fragment rows differ by multiples of 32
     const int swq = Q4 ? (frow >> 3) & 3 : (frow >> 2) & 3;   // q4_0 / q8_0 code chunk swizzle
     int aoff[MI], boff[NI];
 #pragma unroll

@@ -21,14 +21,20 @@ constexpr int kColPad = 256;
 // GEMM with 16-bit weights) are stored tiled: for each group of
 // kWeightTileRows rows and each 32-wide K slab, one contiguous block of
 // kWeightTileRows x 32 values, row after row (64-byte rows); within a row the
-// 16-byte chunk c (K-values 8c..8c+7) sits at chunk c ^ (((r >> 1) ^ (r >> 3)) & 3).
+// 16-byte chunk c (K-values 8c..8c+7) sits at chunk c ^ tiled32_swizzle(r).
 // That is exactly the LDS layout of a gemm_t32 slab, so every operand DMA
 // instruction reads one contiguous kilobyte.
 constexpr int kWeightTileRows = 256;
+// The chunk rotation of row r: bits 2 and 3 of the row.  A wave's MFMA
+// fragment read (32 rows, 16 bytes each, two chunks per row across the two
+// lane halves) then falls on distinct LDS banks; the earlier rotation
+// ((r >> 1) ^ (r >> 3)) & 3 left every such read 2-way conflicted on gfx950
+// (measured with the SQ_LDS_BANK_CONFLICT counter).
+__host__ __device__ inline int tiled32_swizzle(int64_t r) { return (int)((r >> 2) & 3); }
 __host__ __device__ inline int64_t tiled32_index(int64_t row, int64_t k, int64_t K) {
     const int64_t nb = row / kWeightTileRows, r = row % kWeightTileRows, kt = k / 32;
     const int64_t c = (k % 32) / 8, e = k % 8;
-    const int64_t sw = ((r >> 1) ^ (r >> 3)) & 3;
+    const int64_t sw = tiled32_swizzle(r);
     return ((nb * (K / 32) + kt) * kWeightTileRows + r) * 32 + ((c ^ sw) * 8) + e;
 }
 // q8_0 weights [rows][K] use the same grouping: for each 256-row group and
