@@ -36,10 +36,11 @@ constexpr int kThreads = 512;
 constexpr int kTilesPerWave = 2 * kG;  // 16 state tiles per head over 8 waves
 
 // (K S0^T)^T and then W^T are kept [m][v][t] with 32 t per row (64 B) and
-// no padding; the four 16-byte chunks of row v are rotated by (v >> 1) & 3
-// so that the rows a lane group reads fall on different banks.
+// no padding; the four 16-byte chunks of row v are rotated by (v >> 2) & 3
+// so that a wave's 16-byte fragment reads (32 rows, two chunks per row) fall
+// on distinct banks (the rotation of the GEMM operand layout).
 __device__ __forceinline__ int wt_index(int v, int t) {
-    return v * kC + ((((t >> 3) ^ ((v >> 1) & 3)) << 3) | (t & 7));
+    return v * kC + ((((t >> 3) ^ ((v >> 2) & 3)) << 3) | (t & 7));
 }
 
 struct DnSmem {
