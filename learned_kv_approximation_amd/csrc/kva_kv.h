@@ -273,8 +273,9 @@ __device__ __forceinline__ void kv_store_q8_0(uint8_t* row, float4 y, int lane) 
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const float t = yy[e] * id;
-        int q = (int)(t + copysignf(h, t));
-        q = min(max(q, -127), 127);
+        // clamped before the conversion (a NaN becomes -127, never an
+        // out-of-range conversion); the same as clamping the integer
+        const int q = (int)fminf(fmaxf(t + copysignf(h, t), -127.0f), 127.0f);
         packed |= (uint32_t)(uint8_t)(int8_t)q << (8 * e);
     }
     uint8_t* blk = row + (lane >> 3) * 34;
