@@ -588,8 +588,8 @@ hipError_t launch_gemm_heads(GemmOperand opd, const GemmArgs& a, int n_cu, int m
         return launch_t32<128, 256, 2, 4, OPD_Q8, EPI_HEADS>(a, s);
     }
     const int mt = (a.M + 255) / 256, nt = a.N / 256, total = mt * nt;
-    // whole rounds of 256x256 tiles; the rest of the columns in 128x128 tiles
-    // when that shortens the last round
+    // whole rounds of 256x256 tiles; the rest of the columns in 128-row tiles
+    // (128 x kTailBN) when that shortens the last round
     int n_big = nt;
     if (n_cu > 0 && total > n_cu && total % n_cu != 0) n_big = (total / n_cu) * n_cu / mt;
     if (n_big < min_big) n_big = min_big < nt ? min_big : nt;
