@@ -300,7 +300,10 @@ __global__ void __launch_bounds__(kThreads) deltanet_scan(DnArgs g) {
                 }
             }
         }
-        __syncthreads();
+        // the fp16 copy of the new state for the next chunk's K S0^T (no
+        // barrier before it: this phase reads no s0h; the one after it keeps
+        // the next chunk's writes off ks0, kht and the gates until every
+        // wave is done here)
 #pragma unroll
         for (int i = 0; i < kTilesPerWave; ++i) {
             const int tau = wave + 8 * i, hm = tau >> 4, rt = (tau & 15) >> 2, ct = tau & 3;
