@@ -141,7 +141,6 @@ __global__ void __launch_bounds__(128 * KS) attn_fwd(const uint16_t* __restrict_
         }
     };
 
-    const float scale = 0.12751743082459868f;   // log2(e) / sqrt(128)
     float m_i = -INFINITY, l_i = 0.0f;
     f32x16 oacc[4];
 #pragma unroll
@@ -197,7 +196,7 @@ __global__ void __launch_bounds__(128 * KS) attn_fwd(const uint16_t* __restrict_
         __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);              // V^T fragment reads
         __builtin_amdgcn_sched_group_barrier(0x008, 2 * (HD / 16), 0);   // S MFMAs
 
-        // mask, scale, running max.  Element (st, r) is LDS row
+        // mask, running max.  Element (st, r) is LDS row
         // rho = 32 st + 8 (r/4) + 4 g + r%4, i.e. key kv0 + perm(rho).  Only
         // the diagonal tile and a tile reaching past n_tokens need the mask;
         // the test is uniform across the wave.
@@ -210,7 +209,7 @@ __global__ void __launch_bounds__(128 * KS) attn_fwd(const uint16_t* __restrict_
                 for (int r = 0; r < 16; ++r) {
                     const int rho = st * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
                     const int kv = kv0 + perm(rho);
-                    float v = s[st][r] * scale;
+                    float v = s[st][r];                 // Q came scaled by log2(e) / sqrt(128)
                     if (kv > myq || kv >= n) v = -INFINITY;
                     s[st][r] = v;
                     mx = fmaxf(mx, v);
@@ -219,10 +218,7 @@ __global__ void __launch_bounds__(128 * KS) attn_fwd(const uint16_t* __restrict_
 #pragma unroll
             for (int st = 0; st < 2; ++st)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    s[st][r] *= scale;
-                    mx = fmaxf(mx, s[st][r]);
-                }
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[st][r]);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         // exponents are <= 0 here (and -inf for masked keys): the hardware

@@ -89,12 +89,13 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[MI][NI
             const int col = col_base + j * 32;
             if (col >= e.n_real) continue;
             if (col < e.n_split) {
+                const float qs = col < e.n_split / 2 ? kAttnQScale : 1.0f;   // Q | K
 #pragma unroll
                 for (int i = 0; i < MI; ++i)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
-                        if (row < g.M) e.out16[(int64_t)row * e.ld16 + col] = to_f16_bits(acc[i][j][r]);
+                        if (row < g.M) e.out16[(int64_t)row * e.ld16 + col] = to_f16_bits(acc[i][j][r] * qs);
                     }
             } else {
                 // V^T: the lane's 4 consecutive rows are 4 consecutive tokens

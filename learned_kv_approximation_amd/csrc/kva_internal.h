@@ -25,6 +25,10 @@ constexpr int kColPad = 256;
 // That is exactly the LDS layout of a gemm_t32 slab, so every operand DMA
 // instruction reads one contiguous kilobyte.
 constexpr int kWeightTileRows = 256;
+// Attention's softmax works in base 2 on q.k / sqrt(128): the QKV GEMM
+// writes Q already multiplied by log2(e) / sqrt(128) (before its fp16
+// rounding), so the attention kernel exponentiates its scores directly.
+constexpr float kAttnQScale = 0.12751743082459868f;
 // The chunk rotation of row r: bits 2 and 3 of the row.  A wave's MFMA
 // fragment read (32 rows, 16 bytes each, two chunks per row across the two
 // lane halves) then falls on distinct LDS banks; the earlier rotation
