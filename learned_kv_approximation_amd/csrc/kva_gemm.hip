@@ -455,11 +455,12 @@ __device__ __forceinline__ void t32_tile(const GemmArgs& g, int tm, int tn, int 
             __builtin_amdgcn_sched_group_barrier(0x008, MI * NI - (MI + NI), 0);
         }
     };
-    // q8_0: the wave in its MFMA + conversion phase gets issue priority over
-    // the other wave of its SIMD (measured: q8_0 GEMMs 3-6% faster; the
-    // 16-bit path is faster without it)
+    // q8_0 / q4_0 trunk GEMMs: the wave in its MFMA + conversion phase gets
+    // issue priority over the other wave of its SIMD (measured: 3-6% faster;
+    // the 16-bit path is faster without it, and so is the q8_0 head GEMM, by
+    // 1.5%)
     auto prio = [](auto p) {
-        if constexpr (QW) {
+        if constexpr (QW && EPI != EPI_HEADS) {
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_setprio(decltype(p)::value);
         }
