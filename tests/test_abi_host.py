@@ -112,3 +112,31 @@ def test_create_without_device_fails_cleanly():
     out = ctypes.c_void_p()
     st = kva.lib().kva_create(ctypes.byref(c), ctypes.byref(s), 0, ctypes.byref(out))
     assert st in (kva.KVA_ERR_HIP, kva.KVA_ERR_OOM) and out.value is None
+
+
+def test_truncating_round_half_away_identity():
+    """The q8_0 KV kernels round t = y * (1/d) half away from zero as
+    trunc(t + copysign(pred(1/2), t)) in binary32 (one add, no roundf): check
+    that identity against an exact rounding on every binary32 value near the
+    half-integers of [-128, 128] (each k + 1/2 and 40 neighbours either side),
+    on the values just below 1/2, and on random draws."""
+    h = np.nextafter(np.float32(0.5), np.float32(0.0))
+    pts = []
+    for k in range(-128, 128):
+        c = np.float32(k + 0.5)
+        v = c
+        for _ in range(40):
+            v = np.nextafter(v, np.float32(-np.inf))
+            pts.append(v)
+        v = c
+        for _ in range(40):
+            v = np.nextafter(v, np.float32(np.inf))
+            pts.append(v)
+        pts.append(c)
+    x = np.concatenate([np.array(pts, np.float32),
+                        np.float32([h, -h, 0.0, -0.0, 1e-30, -1e-30, 0.25, 0.75]),
+                        np.random.default_rng(3).uniform(-128, 128, 200000).astype(np.float32)])
+    got = np.trunc((x + np.copysign(h, x)).astype(np.float32)).astype(np.float64)
+    xd = x.astype(np.float64)
+    want = np.sign(xd) * np.floor(np.abs(xd) + 0.5)       # exact in float64
+    assert np.array_equal(got, want)
