@@ -7,9 +7,9 @@
 //
 // One workgroup = 64 queries of one head, its key range split between
 // groups of 2 waves (32 queries per wave); each group stages K and V of 64
-// keys at a time in LDS (the next tile is fetched into registers while the
-// current one is used) and the groups' partial softmax states are merged at
-// the end.
+// keys at a time in LDS (copied by global_load_lds into a ring of two
+// stages, the next tile in flight while the current one is used) and the
+// groups' partial softmax states are merged at the end.
 // Per key tile a wave computes S^T = K Q^T with 32x32x16 MFMAs, so each lane
 // holds the scores of ONE query (column lane%32) for 32 keys: the online
 // softmax (running max m, running sum l, fp32) is per lane plus one exchange
@@ -29,11 +29,14 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
 constexpr int HD = 128;     // head dim
 constexpr int QT = 64;      // queries per workgroup
 constexpr int KT = 64;      // keys per tile
 constexpr int kKeySplit = 2;   // key-range groups per workgroup
+constexpr float kLazyShift = 8.0f;   // log2 units a score may exceed the softmax reference point by
 
 __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
@@ -55,7 +58,7 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
 // takes the key tiles t = g, g + KS, g + 2 KS, ... of the query tile's range,
 // so the longest chain of tiles a wave walks is ceil(tiles / KS).  Within a
 // group, wave w % 2 owns queries 32 (w % 2) .. +31.  Each group stages its
-// own K and V^T tile in LDS (prefetched into registers one tile ahead).  At
+// own K and V^T tiles in LDS (two stages, copied one tile ahead).  At
 // the end the groups' running (max, sum, O) are merged through LDS:
 //   m = max_g m_g,  l = sum_g l_g 2^(m_g - m),  O = sum_g O_g 2^(m_g - m) / l.
 // O goes out in the tiled32_index layout of the next GEMM's A operand (each
@@ -67,7 +70,8 @@ __global__ void __launch_bounds__(128 * KS) attn_fwd(const uint16_t* __restrict_
                                                      int64_t ld_o, int32_t n, int32_t n_heads,
                                                      int32_t attn_block) {
     constexpr int TILE = KT * HD;                       // elements of one K (or V^T) tile
-    __shared__ __attribute__((aligned(16))) uint16_t smem[KS * 2 * TILE];   // per group: K | V^T
+    constexpr int STAGE = 2 * TILE;                     // K | V^T
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[KS * 2 * STAGE];   // per group: two stages
 
     // Work items in descending order of key range over ALL heads and blocks:
     // the r-th round of n_heads * n_blocks items holds local q-tile tpb-1-r.
@@ -81,15 +85,15 @@ __global__ void __launch_bounds__(128 * KS) attn_fwd(const uint16_t* __restrict_
     const int q0 = qt * QT;
     if (q0 >= n) return;                              // past the ragged last block
     const int bs = (q0 / attn_block) * attn_block;    // start of this block
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int grp = wave >> 1, gtid = tid & 127;      // key-range group, thread within the group
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 1, gw = wave & 1;         // key-range group, wave within the group
     const int g = lane >> 5;
-    const int myq = q0 + (wave & 1) * 32 + (lane & 31);
+    const int myq = q0 + gw * 32 + (lane & 31);
     const int kv_end = min(q0 + QT, n);
     const int ntiles = (kv_end - bs + KT - 1) / KT;
     const int iters = (ntiles + KS - 1) / KS;          // same for every wave (barriers)
-    uint16_t* sK = smem + grp * 2 * TILE;              // [rho][128], chunk-swizzled
-    uint16_t* sV = sK + TILE;                          // [d][64],   chunk-swizzled
+    uint16_t* sG = smem + grp * 2 * STAGE;
 
     // Q fragments (B operand of S^T = K Q^T): 8 consecutive dims per lane per 16-dim step
     u32x4 qf[HD / 16];
@@ -99,46 +103,49 @@ __global__ void __launch_bounds__(128 * KS) attn_fwd(const uint16_t* __restrict_
         for (int ks = 0; ks < HD / 16; ++ks) qf[ks] = *(const u32x4*)(qr + ks * 16);
     }
 
-    // tile loader of a group: 1024 K chunks and 1024 V^T chunks of 16 bytes, 8 of each per thread
-    u32x4 rk[8], rv[8];
-    auto gload = [&](int kv0) {
+    // DMA of the group's tile at key kv0 into stage st: K as [rho][128] and
+    // V^T as [d][64], both chunk-swizzled, 1024 16-byte units each; LDS unit u
+    // comes from lane u % 64 of instruction u / 128 of wave (u / 64) % 2.  K
+    // rows past n_tokens repeat row n-1 (their scores are masked); V^T
+    // columns past n_tokens are read from the allocated padding and zeroed
+    // in registers after the LDS read.  Addresses: a block-relative base
+    // (uniform) plus 32-bit element offsets (the host checks they fit).
+    const uint16_t* kbase = qk + (int64_t)bs * ld_qk + k_off + h * HD;
+    const uint16_t* vbase = vt + (int64_t)(h * HD) * ld_vt + bs;
+    const int nrel = n - bs;                          // keys of this block present
+    int koff[8], voff[8];                             // tile-independent parts
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            const int id = gtid + p * 128;
-            const int rho = id >> 4, c = id & 15;
-            const int kv = min(kv0 + perm(rho), n - 1);
-            rk[p] = *(const u32x4*)(qk + (int64_t)kv * ld_qk + k_off + h * HD + c * 8);
-        }
+    for (int i = 0; i < 8; ++i) {
+        const int u = (2 * i + gw) * 64 + lane;
+        const int rho = u >> 4;
+        koff[i] = perm(rho);                          // key of LDS row rho, in the tile
+        voff[i] = (u >> 3) * (int)ld_vt + (((u & 7) ^ (((u >> 3) & 7) ^ ((u >> 6) & 1))) << 3);
+        koff[i] = koff[i] * (int)ld_qk + (((u & 15) ^ (rho & 15)) << 3);
+    }
+    auto issue = [&](int t, int st) {
+        uint16_t* sK = sG + st * STAGE;
+        uint16_t* sV = sK + TILE;
+        const int k0 = t * KT;                        // first key of the tile, block-relative
+        if (k0 + KT <= nrel) {
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            const int id = gtid + p * 128;
-            const int d = id >> 3, c = id & 7;
-            const int t0 = kv0 + c * 8;
-            u32x4 v = *(const u32x4*)(vt + (int64_t)(h * HD + d) * ld_vt + t0);
-            if (kv0 + KT > n && t0 + 8 > n) {   // zero V of keys past the end (0 * V must stay 0)
+            for (int i = 0; i < 8; ++i)
+                __builtin_amdgcn_global_load_lds((gbl_ptr_t)(kbase + k0 * (int)ld_qk + koff[i]),
+                                                 (lds_ptr_t)(sK + (2 * i + gw) * 512), 16, 0, 0);
+        } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (t0 + 2 * e >= n) v[e] &= 0xFFFF0000u;
-                    if (t0 + 2 * e + 1 >= n) v[e] &= 0x0000FFFFu;
-                }
+            for (int i = 0; i < 8; ++i) {
+                const int u = (2 * i + gw) * 64 + lane;
+                const int rho = u >> 4;
+                const int kv = min(k0 + perm(rho), nrel - 1);
+                __builtin_amdgcn_global_load_lds(
+                    (gbl_ptr_t)(kbase + kv * (int)ld_qk + (((u & 15) ^ (rho & 15)) << 3)),
+                    (lds_ptr_t)(sK + (2 * i + gw) * 512), 16, 0, 0);
             }
-            rv[p] = v;
-        }
-    };
-    auto sstore = [&]() {
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            const int id = gtid + p * 128;
-            const int rho = id >> 4, c = id & 15;
-            *(u32x4*)(&sK[rho * HD + ((c ^ (rho & 15)) << 3)]) = rk[p];
         }
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            const int id = gtid + p * 128;
-            const int d = id >> 3, c = id & 7;
-            const int sw = (d & 7) ^ ((d >> 3) & 1);
-            *(u32x4*)(&sV[d * KT + ((c ^ sw) << 3)]) = rv[p];
-        }
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_global_load_lds((gbl_ptr_t)(vbase + k0 + voff[i]),
+                                             (lds_ptr_t)(sV + (2 * i + gw) * 512), 16, 0, 0);
     };
 
     float m_i = -INFINITY, l_i = 0.0f;
@@ -148,39 +155,30 @@ __global__ void __launch_bounds__(128 * KS) attn_fwd(const uint16_t* __restrict_
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
 
-    if (grp < ntiles) gload(bs + grp * KT);
+    // Two stages per group: tile t + KS is copied while tile t is used.  One
+    // barrier per tile publishes tile t (every wave has waited for its own
+    // DMA of it) and frees the stage the next copy overwrites.
+    if (grp < ntiles) issue(grp, 0);
     for (int it = 0; it < iters; ++it) {
         const int t = grp + it * KS;                   // this group's tile, if t < ntiles
-        const bool have = t < ntiles;
-        __syncthreads();                               // the previous tile's LDS reads are done
-        if (have) sstore();
+        const int st = it & 1;
+        __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));   // vmcnt(0): own DMA of tile t landed
         __syncthreads();
-        if (t + KS < ntiles) gload(bs + (t + KS) * KT);
-        if (!have) continue;
+        if (t + KS < ntiles) issue(t + KS, st ^ 1);
+        if (t >= ntiles) continue;
         const int kv0 = bs + t * KT;
+        const uint16_t* sK = sG + st * STAGE;
+        const uint16_t* sV = sK + TILE;
 
-        // All K and V^T fragments of the tile are read from LDS up front (V^T
-        // lands while the softmax runs), so the MFMAs never wait on LDS one
-        // fragment at a time.
-        u32x4 kf[2][HD / 16], vf[4][4];
+        u32x4 kf[2][HD / 16];
 #pragma unroll
         for (int ks = 0; ks < HD / 16; ++ks)
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                const int rho = st * 32 + (lane & 31);
+            for (int st2 = 0; st2 < 2; ++st2) {
+                const int rho = st2 * 32 + (lane & 31);
                 const int c = ks * 2 + g;
-                kf[st][ks] = *(const u32x4*)(&sK[rho * HD + ((c ^ (rho & 15)) << 3)]);
+                kf[st2][ks] = *(const u32x4*)(&sK[rho * HD + ((c ^ (rho & 15)) << 3)]);
             }
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-            const int d = dt * 32 + (lane & 31);
-            const int sw = (d & 7) ^ ((d >> 3) & 1);
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int c = 2 * m + g;
-                vf[dt][m] = *(const u32x4*)(&sV[d * KT + ((c ^ sw) << 3)]);
-            }
-        }
 
         // S^T[rho][q] for rho in [0,64): two 32-key MFMA tiles
         f32x16 s[2];
@@ -191,10 +189,32 @@ __global__ void __launch_bounds__(128 * KS) attn_fwd(const uint16_t* __restrict_
 #pragma unroll
         for (int ks = 0; ks < HD / 16; ++ks)
 #pragma unroll
-            for (int st = 0; st < 2; ++st) s[st] = mfma(kf[st][ks], qf[ks], s[st]);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (HD / 16), 0);   // K fragment reads
-        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);              // V^T fragment reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * (HD / 16), 0);   // S MFMAs
+            for (int st2 = 0; st2 < 2; ++st2) s[st2] = mfma(kf[st2][ks], qf[ks], s[st2]);
+
+        // V^T fragments (A operand of O^T += V^T P^T), read while the S MFMAs run
+        u32x4 vf[4][4];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            const int d = dt * 32 + (lane & 31);
+            const int sw = (d & 7) ^ ((d >> 3) & 1);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int c = 2 * m + g;
+                vf[dt][m] = *(const u32x4*)(&sV[d * KT + ((c ^ sw) << 3)]);
+            }
+        }
+        if (kv0 + KT > n) {                            // zero V of keys past the end (0 * V must stay 0)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int t0 = kv0 + 16 * m + 8 * g;   // keys of vf[.][m]: t0 .. t0 + 7
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t keep = (t0 + 2 * e >= n ? 0u : 0x0000FFFFu) | (t0 + 2 * e + 1 >= n ? 0u : 0xFFFF0000u);
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt) vf[dt][m][e] &= keep;
+                }
+            }
+        }
 
         // mask, running max.  Element (st, r) is LDS row
         // rho = 32 st + 8 (r/4) + 4 g + r%4, i.e. key kv0 + perm(rho).  Only
@@ -221,15 +241,24 @@ __global__ void __launch_bounds__(128 * KS) attn_fwd(const uint16_t* __restrict_
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[st][r]);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        // exponents are <= 0 here (and -inf for masked keys): the hardware
-        // exp2 is exact enough and flushing underflow to 0 is what softmax wants
-        const float alpha = __builtin_amdgcn_exp2f(m_i - mx);
-        m_i = mx;
-        l_i *= alpha;
+        // The reference point m_i of l and O moves only when some query of
+        // the wave has a score more than kLazyShift above it (softmax is
+        // invariant to the shift, so this changes only roundings): the
+        // rescale of O then runs about once per wave instead of once per
+        // tile, and P = 2^(s - m_i) <= 2^kLazyShift stays far inside fp16.
+        // The first tile always sets m_i (it starts at -inf).  Exponents
+        // below are then <= kLazyShift (and -inf for masked keys): the
+        // hardware exp2 is exact enough, and flushing underflow to 0 is what
+        // softmax wants.
+        if (__builtin_amdgcn_ballot_w64(mx > m_i + kLazyShift) != 0) {
+            const float alpha = __builtin_amdgcn_exp2f(m_i - mx);
+            m_i = mx;
+            l_i *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+            for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+                for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+        }
 
         // P^T fragments: MFMA m covers keys [16m, 16m+16) of the tile; lane holds
         // keys 16m + 8g + 0..7 = registers 8(m%2)..8(m%2)+7 of s[m/2]
@@ -239,7 +268,7 @@ __global__ void __launch_bounds__(128 * KS) attn_fwd(const uint16_t* __restrict_
             float p[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                p[e] = __builtin_amdgcn_exp2f(s[m >> 1][8 * (m & 1) + e] - mx);
+                p[e] = __builtin_amdgcn_exp2f(s[m >> 1][8 * (m & 1) + e] - m_i);
                 l_i += p[e];
             }
             pf[m][0] = pack_f16(p[0], p[1]);
@@ -315,6 +344,9 @@ hipError_t launch_attention(const uint16_t* qk, int64_t ld_qk, int32_t k_off, co
                             int32_t attn_block, hipStream_t s) {
     if (n <= 0) return hipSuccess;
     if (attn_block % QT || ld_o % 32) return hipErrorInvalidValue;
+    // the kernel's per-lane offsets are 32-bit (block-relative for K)
+    if ((int64_t)HD * ld_vt + attn_block > INT32_MAX || (int64_t)(attn_block + KT) * ld_qk > INT32_MAX)
+        return hipErrorInvalidValue;
     const int nblk = (n + attn_block - 1) / attn_block;
     const dim3 grid(n_heads * nblk * (attn_block / QT));
     hipLaunchKernelGGL(attn_fwd<kKeySplit>, grid, dim3(128 * kKeySplit), 0, s, qk, ld_qk, k_off, vt, ld_vt, o,
