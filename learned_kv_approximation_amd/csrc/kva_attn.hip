@@ -34,8 +34,11 @@ typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
 constexpr int HD = 128;     // head dim
 constexpr int QT = 64;      // queries per workgroup
-constexpr int KT = 64;      // keys per tile
-constexpr int kKeySplit = 2;   // key-range groups per workgroup
+// Keys per tile and key-range groups per workgroup.  Also measured at 1024
+// tokens: 32-key tiles with 4 groups (8 waves, 2 per SIMD) 3% slower, with 2
+// groups 8% slower.
+constexpr int kKeyTile = 64;
+constexpr int kKeySplit = 2;
 constexpr float kLazyShift = 8.0f;   // log2 units a score may exceed the softmax reference point by
 
 __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
@@ -47,6 +50,15 @@ __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
 // the index are swapped (an involution).
 __device__ __forceinline__ int perm(int rho) {
     return (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);
+}
+
+// Chunk swizzle of the V^T tile ([d][KT], KT / 8 chunks of 16 bytes per
+// row): the 16 rows one half-wave reads at one chunk index land in 16
+// different 16-byte bank groups.
+template <int KT>
+__device__ __forceinline__ int vswz(int d) {
+    if constexpr (KT == 64) return (d & 7) ^ ((d >> 3) & 1);
+    else return (d >> 2) & 3;
 }
 
 __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
@@ -63,7 +75,7 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
 //   m = max_g m_g,  l = sum_g l_g 2^(m_g - m),  O = sum_g O_g 2^(m_g - m) / l.
 // O goes out in the tiled32_index layout of the next GEMM's A operand (each
 // 8-byte store is 4 consecutive columns inside one 8-value chunk).
-template <int KS>
+template <int KS, int KT>
 __global__ void __launch_bounds__(128 * KS) attn_fwd(const uint16_t* __restrict__ qk, int64_t ld_qk,
                                                      int32_t k_off, const uint16_t* __restrict__ vt,
                                                      int64_t ld_vt, uint16_t* __restrict__ o,
@@ -71,6 +83,11 @@ __global__ void __launch_bounds__(128 * KS) attn_fwd(const uint16_t* __restrict_
                                                      int32_t attn_block) {
     constexpr int TILE = KT * HD;                       // elements of one K (or V^T) tile
     constexpr int STAGE = 2 * TILE;                     // K | V^T
+    constexpr int NST = KT / 32;                        // 32-key S^T blocks per tile
+    constexpr int NM = KT / 16;                         // 16-key PV steps per tile
+    constexpr int NI = KT * 16 / 128;                   // DMA instructions per wave per operand
+    static_assert(KT == 32 || KT == 64, "key tile");
+    static_assert((KS - 1) * 2 * 64 * 66 * 4 <= KS * 2 * STAGE * 2, "merge records fit the tile stages");
     __shared__ __attribute__((aligned(1024))) uint16_t smem[KS * 2 * STAGE];   // per group: two stages
 
     // Work items in descending order of key range over ALL heads and blocks:
@@ -113,14 +130,13 @@ __global__ void __launch_bounds__(128 * KS) attn_fwd(const uint16_t* __restrict_
     const uint16_t* kbase = qk + (int64_t)bs * ld_qk + k_off + h * HD;
     const uint16_t* vbase = vt + (int64_t)(h * HD) * ld_vt + bs;
     const int nrel = n - bs;                          // keys of this block present
-    int koff[8], voff[8];                             // tile-independent parts
+    int koff[NI], voff[NI];                           // tile-independent parts
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NI; ++i) {
         const int u = (2 * i + gw) * 64 + lane;
-        const int rho = u >> 4;
-        koff[i] = perm(rho);                          // key of LDS row rho, in the tile
-        voff[i] = (u >> 3) * (int)ld_vt + (((u & 7) ^ (((u >> 3) & 7) ^ ((u >> 6) & 1))) << 3);
-        koff[i] = koff[i] * (int)ld_qk + (((u & 15) ^ (rho & 15)) << 3);
+        const int rho = u >> 4, d = u / (KT / 8);
+        koff[i] = perm(rho) * (int)ld_qk + (((u & 15) ^ (rho & 15)) << 3);
+        voff[i] = d * (int)ld_vt + (((u % (KT / 8)) ^ vswz<KT>(d)) << 3);
     }
     auto issue = [&](int t, int st) {
         uint16_t* sK = sG + st * STAGE;
@@ -128,12 +144,12 @@ __global__ void __launch_bounds__(128 * KS) attn_fwd(const uint16_t* __restrict_
         const int k0 = t * KT;                        // first key of the tile, block-relative
         if (k0 + KT <= nrel) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < NI; ++i)
                 __builtin_amdgcn_global_load_lds((gbl_ptr_t)(kbase + k0 * (int)ld_qk + koff[i]),
                                                  (lds_ptr_t)(sK + (2 * i + gw) * 512), 16, 0, 0);
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < NI; ++i) {
                 const int u = (2 * i + gw) * 64 + lane;
                 const int rho = u >> 4;
                 const int kv = min(k0 + perm(rho), nrel - 1);
@@ -143,7 +159,7 @@ __global__ void __launch_bounds__(128 * KS) attn_fwd(const uint16_t* __restrict_
             }
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < NI; ++i)
             __builtin_amdgcn_global_load_lds((gbl_ptr_t)(vbase + k0 + voff[i]),
                                              (lds_ptr_t)(sV + (2 * i + gw) * 512), 16, 0, 0);
     };
@@ -170,42 +186,42 @@ __global__ void __launch_bounds__(128 * KS) attn_fwd(const uint16_t* __restrict_
         const uint16_t* sK = sG + st * STAGE;
         const uint16_t* sV = sK + TILE;
 
-        u32x4 kf[2][HD / 16];
+        u32x4 kf[NST][HD / 16];
 #pragma unroll
         for (int ks = 0; ks < HD / 16; ++ks)
 #pragma unroll
-            for (int st2 = 0; st2 < 2; ++st2) {
+            for (int st2 = 0; st2 < NST; ++st2) {
                 const int rho = st2 * 32 + (lane & 31);
                 const int c = ks * 2 + g;
                 kf[st2][ks] = *(const u32x4*)(&sK[rho * HD + ((c ^ (rho & 15)) << 3)]);
             }
 
-        // S^T[rho][q] for rho in [0,64): two 32-key MFMA tiles
-        f32x16 s[2];
+        // S^T[rho][q] for rho in [0, KT): KT / 32 MFMA tiles of 32 keys
+        f32x16 s[NST];
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+        for (int st = 0; st < NST; ++st)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[st][r] = 0.0f;
 #pragma unroll
         for (int ks = 0; ks < HD / 16; ++ks)
 #pragma unroll
-            for (int st2 = 0; st2 < 2; ++st2) s[st2] = mfma(kf[st2][ks], qf[ks], s[st2]);
+            for (int st2 = 0; st2 < NST; ++st2) s[st2] = mfma(kf[st2][ks], qf[ks], s[st2]);
 
         // V^T fragments (A operand of O^T += V^T P^T), read while the S MFMAs run
-        u32x4 vf[4][4];
+        u32x4 vf[4][NM];
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
             const int d = dt * 32 + (lane & 31);
-            const int sw = (d & 7) ^ ((d >> 3) & 1);
+            const int sw = vswz<KT>(d);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
+            for (int m = 0; m < NM; ++m) {
                 const int c = 2 * m + g;
                 vf[dt][m] = *(const u32x4*)(&sV[d * KT + ((c ^ sw) << 3)]);
             }
         }
         if (kv0 + KT > n) {                            // zero V of keys past the end (0 * V must stay 0)
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
+            for (int m = 0; m < NM; ++m) {
                 const int t0 = kv0 + 16 * m + 8 * g;   // keys of vf[.][m]: t0 .. t0 + 7
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -224,7 +240,7 @@ __global__ void __launch_bounds__(128 * KS) attn_fwd(const uint16_t* __restrict_
         const int wq0 = q0 + (wave & 1) * 32;          // lowest query of this wave
         if (kv0 + KT - 1 > wq0 || kv0 + KT > n) {
 #pragma unroll
-            for (int st = 0; st < 2; ++st)
+            for (int st = 0; st < NST; ++st)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int rho = st * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
@@ -236,7 +252,7 @@ __global__ void __launch_bounds__(128 * KS) attn_fwd(const uint16_t* __restrict_
                 }
         } else {
 #pragma unroll
-            for (int st = 0; st < 2; ++st)
+            for (int st = 0; st < NST; ++st)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[st][r]);
         }
@@ -260,15 +276,20 @@ __global__ void __launch_bounds__(128 * KS) attn_fwd(const uint16_t* __restrict_
                 for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
         }
 
+        // A query that has seen only masked keys so far (a 32-key tile can lie
+        // wholly after the first half of the q-tile) keeps m_i = -inf; its P
+        // must be 0, not 2^(-inf + inf).
+        const float mref = m_i == -INFINITY ? 0.0f : m_i;
+
         // P^T fragments: MFMA m covers keys [16m, 16m+16) of the tile; lane holds
         // keys 16m + 8g + 0..7 = registers 8(m%2)..8(m%2)+7 of s[m/2]
-        u32x4 pf[4];
+        u32x4 pf[NM];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
+        for (int m = 0; m < NM; ++m) {
             float p[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                p[e] = __builtin_amdgcn_exp2f(s[m >> 1][8 * (m & 1) + e] - m_i);
+                p[e] = __builtin_amdgcn_exp2f(s[m >> 1][8 * (m & 1) + e] - mref);
                 l_i += p[e];
             }
             pf[m][0] = pack_f16(p[0], p[1]);
@@ -281,7 +302,7 @@ __global__ void __launch_bounds__(128 * KS) attn_fwd(const uint16_t* __restrict_
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-            for (int m = 0; m < 4; ++m) oacc[dt] = mfma(vf[dt][m], pf[m], oacc[dt]);
+            for (int m = 0; m < NM; ++m) oacc[dt] = mfma(vf[dt][m], pf[m], oacc[dt]);
     }
 
     // ---- merge the KS groups (group 0 writes the output)
@@ -345,11 +366,11 @@ hipError_t launch_attention(const uint16_t* qk, int64_t ld_qk, int32_t k_off, co
     if (n <= 0) return hipSuccess;
     if (attn_block % QT || ld_o % 32) return hipErrorInvalidValue;
     // the kernel's per-lane offsets are 32-bit (block-relative for K)
-    if ((int64_t)HD * ld_vt + attn_block > INT32_MAX || (int64_t)(attn_block + KT) * ld_qk > INT32_MAX)
+    if ((int64_t)HD * ld_vt + attn_block > INT32_MAX || (int64_t)(attn_block + kKeyTile) * ld_qk > INT32_MAX)
         return hipErrorInvalidValue;
     const int nblk = (n + attn_block - 1) / attn_block;
     const dim3 grid(n_heads * nblk * (attn_block / QT));
-    hipLaunchKernelGGL(attn_fwd<kKeySplit>, grid, dim3(128 * kKeySplit), 0, s, qk, ld_qk, k_off, vt, ld_vt, o,
+    hipLaunchKernelGGL((attn_fwd<kKeySplit, kKeyTile>), grid, dim3(128 * kKeySplit), 0, s, qk, ld_qk, k_off, vt, ld_vt, o,
                        ld_o, n, n_heads, attn_block);
     return hipGetLastError();
 }
