@@ -113,45 +113,109 @@ __global__ void __launch_bounds__(256) fold_rmsnorm(float* __restrict__ h, int64
     }
 }
 
-// The same with one float4 of the row per thread (cols / 4 threads, at most
-// 1024): every load of the row is in flight at once and the updated values
-// stay in registers for the normalisation.
-template <bool BF16>
+// The same with the row held in registers: V float4 per thread, thread t
+// owning columns 4 (t + i * blockDim.x) .. +3 for i < V (consecutive threads
+// read consecutive 16 bytes), and every load of the row (residual and
+// partials) issued before the first one is used.  Rows of up to 4096
+// columns in at most 512 threads (at 1024 tokens the whole grid is then
+// resident at once).
+constexpr int kMaxFoldSplits = 4;
+template <bool BF16, int V>
 __global__ void __launch_bounds__(1024) fold_rmsnorm_row(float* __restrict__ h, int64_t ldh, int add,
                                                          const float* __restrict__ partials, int32_t splits,
                                                          int64_t pstride, int64_t ldp,
                                                          const float* __restrict__ gain, int32_t cols, float eps,
                                                          uint16_t* __restrict__ out) {
     __shared__ float part[16];
-    const int row = blockIdx.x, tid = threadIdx.x, c = tid * 4;
-    const bool live = c < cols;
+    const int row = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
     float* hr = h + (int64_t)row * ldh;
     const float* pr = partials + (int64_t)row * ldp;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (live) {
-        if (add) v = *(const float4*)(hr + c);
-        for (int sp = 0; sp < splits; ++sp) {
-            const float4 p = *(const float4*)(pr + sp * pstride + c);
-            v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
-        }
-        *(float4*)(hr + c) = v;
+    float4 v[V], p[kMaxFoldSplits][V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int c = (tid + i * nt) * 4;
+        const bool live = c < cols;
+        v[i] = (live && add) ? *(const float4*)(hr + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int sp = 0; sp < kMaxFoldSplits; ++sp)
+            if (live && sp < splits) p[sp][i] = *(const float4*)(pr + sp * pstride + c);
     }
-    float ss = wave_sum(v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w);
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int c = (tid + i * nt) * 4;
+        if (c < cols) {
+#pragma unroll
+            for (int sp = 0; sp < kMaxFoldSplits; ++sp)
+                if (sp < splits) {
+                    v[i].x += p[sp][i].x; v[i].y += p[sp][i].y; v[i].z += p[sp][i].z; v[i].w += p[sp][i].w;
+                }
+            *(float4*)(hr + c) = v[i];
+        }
+        ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+    }
+    ss = wave_sum(ss);
     if ((tid & 63) == 0) part[tid >> 6] = ss;
     __syncthreads();
     float tot = 0.0f;
-    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += part[w];
+    for (int w = 0; w < (nt >> 6); ++w) tot += part[w];
     const float r = 1.0f / sqrtf(tot / (float)cols + eps);
-    if (live) {
-        const float4 gg = *(const float4*)(gain + c);
-        ushort4 o;
-        o.x = to_bits(v.x * r * gg.x, BF16);
-        o.y = to_bits(v.y * r * gg.y, BF16);
-        o.z = to_bits(v.z * r * gg.z, BF16);
-        o.w = to_bits(v.w * r * gg.w, BF16);
-        *(ushort4*)(out + tiled32_index(row, c, cols)) = o;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int c = (tid + i * nt) * 4;
+        if (c < cols) {
+            const float4 gg = *(const float4*)(gain + c);
+            ushort4 o;
+            o.x = to_bits(v[i].x * r * gg.x, BF16);
+            o.y = to_bits(v[i].y * r * gg.y, BF16);
+            o.z = to_bits(v[i].z * r * gg.z, BF16);
+            o.w = to_bits(v[i].w * r * gg.w, BF16);
+            *(ushort4*)(out + tiled32_index(row, c, cols)) = o;
+        }
     }
 }
+
+// rmsnorm_cast with the row held in registers (same thread-to-column map as
+// fold_rmsnorm_row): x is read once.
+template <bool BF16, int V>
+__global__ void __launch_bounds__(1024) rmsnorm_cast_row(const float* __restrict__ x, int64_t ldx,
+                                                         const float* __restrict__ gain, int32_t cols,
+                                                         float eps, uint16_t* __restrict__ out) {
+    __shared__ float part[16];
+    const int row = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
+    const float* xr = x + (int64_t)row * ldx;
+    float4 v[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int c = (tid + i * nt) * 4;
+        v[i] = c < cols ? *(const float4*)(xr + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) part[tid >> 6] = ss;
+    __syncthreads();
+    float tot = 0.0f;
+    for (int w = 0; w < (nt >> 6); ++w) tot += part[w];
+    const float r = 1.0f / sqrtf(tot / (float)cols + eps);
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int c = (tid + i * nt) * 4;
+        if (c < cols) {
+            const float4 gg = *(const float4*)(gain + c);
+            ushort4 o;
+            o.x = to_bits(v[i].x * r * gg.x, BF16);
+            o.y = to_bits(v[i].y * r * gg.y, BF16);
+            o.z = to_bits(v[i].z * r * gg.z, BF16);
+            o.w = to_bits(v[i].w * r * gg.w, BF16);
+            *(ushort4*)(out + tiled32_index(row, c, cols)) = o;
+        }
+    }
+}
+
+// Threads of a register-resident row kernel with V float4 per thread.
+inline unsigned row_threads(int32_t cols, int V) { return (unsigned)((cols / 4 / V + 63) / 64 * 64); }
 
 // Inverse of the tiled32_index layout, one row per workgroup (test hook).
 __global__ void __launch_bounds__(256) untile32_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
@@ -282,10 +346,19 @@ hipError_t launch_rmsnorm_cast(const float* x, int64_t ldx, const float* g, int3
                                int32_t cols, float eps, uint16_t* out, bool bf16, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
     if (cols % 32) return hipErrorInvalidValue;
-    if (bf16)
+    if (cols <= 2048) {
+        const dim3 t(row_threads(cols, 2));
+        if (bf16) hipLaunchKernelGGL((rmsnorm_cast_row<true, 2>), dim3(rows), t, 0, s, x, ldx, g, cols, eps, out);
+        else hipLaunchKernelGGL((rmsnorm_cast_row<false, 2>), dim3(rows), t, 0, s, x, ldx, g, cols, eps, out);
+    } else if (cols <= 8192) {
+        const dim3 t(row_threads(cols, 4));
+        if (bf16) hipLaunchKernelGGL((rmsnorm_cast_row<true, 4>), dim3(rows), t, 0, s, x, ldx, g, cols, eps, out);
+        else hipLaunchKernelGGL((rmsnorm_cast_row<false, 4>), dim3(rows), t, 0, s, x, ldx, g, cols, eps, out);
+    } else if (bf16) {
         hipLaunchKernelGGL(rmsnorm_cast<true>, dim3(rows), dim3(256), 0, s, x, ldx, g, cols, eps, out);
-    else
+    } else {
         hipLaunchKernelGGL(rmsnorm_cast<false>, dim3(rows), dim3(256), 0, s, x, ldx, g, cols, eps, out);
+    }
     return hipGetLastError();
 }
 
@@ -305,13 +378,20 @@ hipError_t launch_fold_rmsnorm(float* h, int64_t ldh, bool add, const float* par
                                float eps, uint16_t* out, bool bf16, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
     if (cols % 32 || splits < 1) return hipErrorInvalidValue;
-    if (cols <= 4096) {
-        const unsigned threads = (unsigned)((cols / 4 + 63) / 64 * 64);
-        if (bf16)
-            hipLaunchKernelGGL(fold_rmsnorm_row<true>, dim3(rows), dim3(threads), 0, s, h, ldh, (int)add, partials,
+    if (cols <= 4096 && splits <= kMaxFoldSplits) {
+        const bool two = cols > 1024;
+        const dim3 t(row_threads(cols, two ? 2 : 1));
+        if (bf16 && two)
+            hipLaunchKernelGGL((fold_rmsnorm_row<true, 2>), dim3(rows), t, 0, s, h, ldh, (int)add, partials,
+                               splits, pstride, ldp, g, cols, eps, out);
+        else if (two)
+            hipLaunchKernelGGL((fold_rmsnorm_row<false, 2>), dim3(rows), t, 0, s, h, ldh, (int)add, partials,
+                               splits, pstride, ldp, g, cols, eps, out);
+        else if (bf16)
+            hipLaunchKernelGGL((fold_rmsnorm_row<true, 1>), dim3(rows), t, 0, s, h, ldh, (int)add, partials,
                                splits, pstride, ldp, g, cols, eps, out);
         else
-            hipLaunchKernelGGL(fold_rmsnorm_row<false>, dim3(rows), dim3(threads), 0, s, h, ldh, (int)add, partials,
+            hipLaunchKernelGGL((fold_rmsnorm_row<false, 1>), dim3(rows), t, 0, s, h, ldh, (int)add, partials,
                                splits, pstride, ldp, g, cols, eps, out);
     } else if (bf16)
         hipLaunchKernelGGL(fold_rmsnorm<true>, dim3(rows), dim3(256), 0, s, h, ldh, (int)add, partials, splits,
