@@ -89,6 +89,39 @@ def test_tiny_ragged_blocks(tiny, n):
     proj.close()
 
 
+@pytest.mark.parametrize("scale", [1.0, 3.0])
+def test_tiny_long_block_peaked_scores(tiny, scale):
+    """1024 tokens in one attention block (16 key tiles per query tile) with
+    the Q and K weights scaled by `scale` (scores x scale^2).  At 3 the
+    running maximum of a query jumps by several units between key tiles, so
+    the softmax rescale of the output accumulators runs on non-empty state
+    (with unscaled weights it runs only on the first tile).
+
+    Bar at scale 1: the projector's (max|err| <= 2e-2 RMS).  At scale 3 the
+    scores are 9x the workload's, and the fp16 rounding of Q and K (relative
+    2^-11 each, so score errors of about |s| 2^-10) moves the weights of
+    nearly tied keys: a few tokens' outputs move by up to ~0.2 RMS whatever
+    the softmax does (measured 0.190 both with this kernel and with one that
+    rescales on every tile).  The bar there is the RMS error, <= 2e-2 RMS
+    (measured 8.3e-3): a rescale that dropped or misapplied the factor would
+    move every affected query by O(1)."""
+    cfg, w = tiny
+    cfg = dict(cfg, attn_block=1024)
+    w = dict(w, blocks=[dict(b, wq=b["wq"] * np.float32(scale), wk=b["wk"] * np.float32(scale))
+                        for b in w["blocks"]])
+    x = synth.make_input(cfg, n_tokens=1024, seed=12)
+    proj = kva.Projector(cfg, w, max_tokens=1024)
+    got, want = _run(proj, x), oracle.project(cfg, w, x)
+    proj.close()
+    if scale == 1.0:
+        _check(cfg, got, want, label="tiny 1024 tokens")
+        return
+    errs = _errs(got, want)
+    print(f"tiny 1024 tokens, qk scale {scale}: worst max|err|/rms {max(e[0] for e in errs.values()):.4e}; "
+          f"rms err/rms {max(e[1] for e in errs.values()):.4e}", flush=True)
+    assert all(e[1] <= 2e-2 for e in errs.values()), errs
+
+
 def test_tiny_bad_arguments(tiny):
     cfg, w = tiny
     proj = kva.Projector(cfg, w, max_tokens=64)
