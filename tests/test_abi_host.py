@@ -140,3 +140,21 @@ def test_truncating_round_half_away_identity():
     xd = x.astype(np.float64)
     want = np.sign(xd) * np.floor(np.abs(xd) + 0.5)       # exact in float64
     assert np.array_equal(got, want)
+
+
+def test_build_commands_keep_packed_fp32_off():
+    """Every HIP source is compiled for gfx950 with the packed fp32 VALU
+    feature disabled (the compiler would otherwise form packed adds and
+    multiplies from scalar float code); only the attention source asks for
+    VGPR-form MFMAs, and the link step names every object."""
+    from learned_kv_approximation_amd import _build
+    objs = []
+    for src in _build.SOURCES:
+        cmd = _build.compile_command(src, src + ".o")
+        assert "--offload-arch=gfx950" in cmd and "-O3" in cmd and "-c" in cmd
+        i = cmd.index("-packed-fp32-ops")
+        assert cmd[i - 3:i] == ["-Xclang", "-target-feature", "-Xclang"]
+        assert ("-amdgpu-mfma-vgpr-form" in cmd) == (src == "kva_attn.hip")
+        objs.append(src + ".o")
+    link = _build.link_command(objs, "lib.so")
+    assert "-shared" in link and all(o in link for o in objs) and link[-2:] == ["-o", "lib.so"]
