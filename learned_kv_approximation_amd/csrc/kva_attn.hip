@@ -365,8 +365,12 @@ hipError_t launch_attention(const uint16_t* qk, int64_t ld_qk, int32_t k_off, co
                             int32_t attn_block, hipStream_t s) {
     if (n <= 0) return hipSuccess;
     if (attn_block % QT || ld_o % 32) return hipErrorInvalidValue;
-    // the kernel's per-lane offsets are 32-bit (block-relative for K)
-    if ((int64_t)HD * ld_vt + attn_block > INT32_MAX || (int64_t)(attn_block + kKeyTile) * ld_qk > INT32_MAX)
+    // The kernel's per-lane element offsets are 32-bit: up to
+    // (HD - 1) ld_vt + attn_block + KT into V^T from the block's first
+    // column, up to (attn_block + KT) ld_qk into Q|K from the block's first
+    // row (max_tokens <= 2^24 keeps the first within range).
+    if ((int64_t)(HD - 1) * ld_vt + attn_block + kKeyTile > INT32_MAX ||
+        (int64_t)(attn_block + kKeyTile) * ld_qk > INT32_MAX)
         return hipErrorInvalidValue;
     const int nblk = (n + attn_block - 1) / attn_block;
     const dim3 grid(n_heads * nblk * (attn_block / QT));
