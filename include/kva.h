@@ -370,6 +370,15 @@ kva_status kva_debug_mfma_loop(int32_t n_iter, int32_t n_workgroups, float* sink
  * Asynchronous on `stream`. */
 kva_status kva_debug_copy_z(kva_ctx* ctx, uint16_t* dst, int32_t n_tokens, void* stream);
 
+/* Test hook: fills every byte of the context's activation scratch (the
+ * buffers kva_create sizes for max_tokens: normed input, residual stream,
+ * split-K partials, Q|K, V^T, attention output, SwiGLU output, z) with 0xFF,
+ * a NaN in fp32, fp16 and bf16 alike.  A following projection must give the
+ * same bits as on clean scratch: no kernel may read a scratch value that
+ * the same call did not write first, except where it discards the result.
+ * Asynchronous on `stream`; KVA_ERR_ARG for a NULL ctx. */
+kva_status kva_debug_poison_scratch(kva_ctx* ctx, void* stream);
+
 /* Test hook (host only, no device): the packed column order of the head
  * GEMM for `cfg`.  Head outputs are packed into 256-column tiles: first the
  * 8 tiles of every full-attention head with out_dim 2048 (the heads

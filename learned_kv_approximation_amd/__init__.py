@@ -106,6 +106,7 @@ _SIGS = {
     "kva_debug_dequant_q4_0_f16": (c_i32, [c_vp, c_i64, c_vp, c_vp]),
     "kva_debug_mfma_loop": (c_i32, [c_i32, c_i32, c_vp, c_vp]),
     "kva_debug_copy_z": (c_i32, [c_vp, c_vp, c_i32, c_vp]),
+    "kva_debug_poison_scratch": (c_i32, [c_vp, c_vp]),
     "kva_debug_head_plan": (c_i32, [ctypes.POINTER(kva_config), ctypes.POINTER(c_i32), c_vp, c_vp, c_i64]),
     "kva_debug_host_to_f16": (c_i32, [c_vp, c_i32, c_i64, c_vp]),
     "kva_get_stats": (c_i32, [c_vp, ctypes.POINTER(kva_stats)]),
@@ -264,6 +265,10 @@ def kva_debug_dequant_q8_0_f16(blocks_ptr: int, n_blocks: int, out_ptr: int, str
 
 def kva_debug_copy_z(ctx: int, dst_ptr: int, n_tokens: int, stream: int = 0) -> None:
     _check(lib().kva_debug_copy_z(ctx, dst_ptr, n_tokens, stream), "kva_debug_copy_z")
+
+
+def kva_debug_poison_scratch(ctx: int, stream: int = 0) -> None:
+    _check(lib().kva_debug_poison_scratch(ctx, stream), "kva_debug_poison_scratch")
 
 
 def kva_debug_head_plan(cfg: kva_config):

@@ -1,7 +1,9 @@
 // Host runtime behind the C ABI in include/kva.h: config validation, weight
 // conversion and repacking, device memory, and the launch sequence of one
 // projection (the hot path).
+#include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -63,6 +65,28 @@ float bf16_to_f32(uint16_t b) {
     float f;
     std::memcpy(&f, &u, 4);
     return f;
+}
+
+float f16_bits_to_f32(uint16_t h) {
+    const uint32_t sign = (uint32_t)(h & 0x8000u) << 16, e = (h >> 10) & 0x1Fu, m = h & 0x3FFu;
+    uint32_t u;
+    if (e == 0x1Fu) u = sign | 0x7F800000u | (m << 13);
+    else if (e != 0) u = sign | ((e + 112u) << 23) | (m << 13);
+    else {
+        float f = (float)m * 5.9604644775390625e-8f;     // m * 2^-24, exact
+        return (h & 0x8000u) ? -f : f;
+    }
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+}
+
+// A q8_0 / q4_0 block whose fp16 weights d * code (the GEMMs' operands,
+// d * code rounded once to fp16) would not all be finite: a non-finite
+// scale, or |d| * max|code| at or past 65520, which rounds to infinity.
+bool quant_block_out_of_range(uint16_t d_bits, int max_abs_code) {
+    const float d = f16_bits_to_f32(d_bits);
+    return !std::isfinite(d) || std::fabs(d) * (float)max_abs_code >= 65520.0f;
 }
 
 // fp32 -> fp16, round to nearest even.  Sets *overflow when a finite input
@@ -186,6 +210,7 @@ struct kva_ctx {
     int device = 0;
     int n_cu = 0;                  // compute units of the device (head GEMM round size)
     std::vector<void*> allocs;
+    std::vector<std::pair<void*, size_t>> scratch_regions;   // activation scratch (kva_debug_poison_scratch)
     uint64_t weight_bytes = 0, scratch_bytes = 0;
 
     // weights (device).  A weight is either 16-bit values w16 (fp16 trunk,
@@ -267,6 +292,7 @@ struct kva_ctx {
         if (e != hipSuccess) return e;
         allocs.push_back(q);
         (weight ? weight_bytes : scratch_bytes) += bytes;
+        if (!weight) scratch_regions.push_back({q, bytes});
         *p = static_cast<T*>(q);
         return hipSuccess;
     }
@@ -358,7 +384,16 @@ kva_status pack_weight(kva_ctx* ctx, int dtype, int64_t K, const std::vector<Row
             const uint8_t* blk = static_cast<const uint8_t*>(rows[r].src) + rows[r].row * nb * 18;
             for (int64_t b = 0; b < nb; ++b) {
                 const uint8_t* qs = blk + b * 18 + 2;
-                sc[(size_t)q8_scale_index(r, b, K)] = (uint16_t)(blk[b * 18] | (blk[b * 18 + 1] << 8));
+                const uint16_t d_bits = (uint16_t)(blk[b * 18] | (blk[b * 18 + 1] << 8));
+                int mx = 0;
+                for (int j = 0; j < 16; ++j) {
+                    const int lo = std::abs((qs[j] & 0xF) - 8), hi = std::abs((qs[j] >> 4) - 8);
+                    mx = std::max(mx, std::max(lo, hi));
+                }
+                if (quant_block_out_of_range(d_bits, mx))
+                    return fail(KVA_ERR_RANGE, "weight %s: q4_0 block (row %lld, block %lld) has a scale whose "
+                                "weights d*(n-8) are not finite in fp16", name, (long long)rows[r].row, (long long)b);
+                sc[(size_t)q8_scale_index(r, b, K)] = d_bits;
                 for (int64_t c = 0; c < 4; ++c) {       // 8 inputs of the block per chunk
                     uint8_t nn[8];
                     for (int e = 0; e < 8; ++e) {
@@ -385,7 +420,14 @@ kva_status pack_weight(kva_ctx* ctx, int dtype, int64_t K, const std::vector<Row
             if (!rows[r].src) continue;
             const uint8_t* blk = static_cast<const uint8_t*>(rows[r].src) + rows[r].row * nb * 34;
             for (int64_t b = 0; b < nb; ++b) {
-                sc[(size_t)q8_scale_index(r, b, K)] = (uint16_t)(blk[b * 34] | (blk[b * 34 + 1] << 8));
+                const uint16_t d_bits = (uint16_t)(blk[b * 34] | (blk[b * 34 + 1] << 8));
+                const int8_t* codes = reinterpret_cast<const int8_t*>(blk + b * 34 + 2);
+                int mx = 0;
+                for (int j = 0; j < 32; ++j) mx = std::max(mx, std::abs((int)codes[j]));
+                if (quant_block_out_of_range(d_bits, mx))
+                    return fail(KVA_ERR_RANGE, "weight %s: q8_0 block (row %lld, block %lld) has a scale whose "
+                                "weights d*q are not finite in fp16", name, (long long)rows[r].row, (long long)b);
+                sc[(size_t)q8_scale_index(r, b, K)] = d_bits;
                 for (int64_t c = 0; c < 32; c += 8) {   // 8 consecutive codes form one chunk
                     uint32_t w[2];
                     q8_chunk_pack(reinterpret_cast<const int8_t*>(blk + b * 34 + 2 + c), &w[0], &w[1]);
@@ -1023,6 +1065,15 @@ kva_status kva_debug_copy_z(kva_ctx* ctx, uint16_t* dst, int32_t n, void* stream
     if (!ctx || !dst) return fail(KVA_ERR_ARG, "NULL argument");
     if (n < 1 || n > ctx->cfg.max_tokens) return fail(KVA_ERR_SHAPE, "bad n_tokens");
     LAUNCH(launch_untile32(ctx->z16, dst, n, ctx->cfg.d_model, static_cast<hipStream_t>(stream)));
+    return KVA_OK;
+}
+
+kva_status kva_debug_poison_scratch(kva_ctx* ctx, void* stream) {
+    clear_stale_error();
+    if (!ctx) return fail(KVA_ERR_ARG, "NULL argument");
+    HIP_TRY(hipSetDevice(ctx->device));
+    for (const auto& r : ctx->scratch_regions)
+        HIP_TRY(hipMemsetAsync(r.first, 0xFF, r.second, static_cast<hipStream_t>(stream)));
     return KVA_OK;
 }
 

@@ -14,7 +14,7 @@ import torch
 import learned_kv_approximation_amd as kva
 import oracle
 import synth
-from oracle import ref
+from oracle import emu, ref
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -97,14 +97,16 @@ def test_tiny_long_block_peaked_scores(tiny, scale):
     the softmax rescale of the output accumulators runs on non-empty state
     (with unscaled weights it runs only on the first tile).
 
-    Bar at scale 1: the projector's (max|err| <= 2e-2 RMS).  At scale 3 the
-    scores are 9x the workload's, and the fp16 rounding of Q and K (relative
-    2^-11 each, so score errors of about |s| 2^-10) moves the weights of
-    nearly tied keys: a few tokens' outputs move by up to ~0.2 RMS whatever
-    the softmax does (measured 0.190 both with this kernel and with one that
-    rescales on every tile).  The bar there is the RMS error, <= 2e-2 RMS
-    (measured 8.3e-3): a rescale that dropped or misapplied the factor would
-    move every affected query by O(1)."""
+    Bar at scale 1: the projector's (max|err| <= 2e-2 RMS against the
+    oracle).  At scale 3 the storage roundings of a 16-bit path alone move a
+    few tokens by about 0.19 RMS from the float64 result: the rounding-point
+    emulator (oracle/emu.py, every intermediate the kernels store rounded
+    to its format, float64 arithmetic otherwise) shows 0.195 max / 8.4e-3
+    RMS on these inputs, and no single rounding point accounts for it.  So
+    at scale 3 the max bar applies against the emulator (2e-2 RMS: what is
+    left is accumulation order and fp32 arithmetic, which a rescale that
+    dropped or misapplied its factor would exceed by far), and the RMS
+    error against the oracle stays <= 2e-2."""
     cfg, w = tiny
     cfg = dict(cfg, attn_block=1024)
     w = dict(w, blocks=[dict(b, wq=b["wq"] * np.float32(scale), wk=b["wk"] * np.float32(scale))
@@ -113,13 +115,19 @@ def test_tiny_long_block_peaked_scores(tiny, scale):
     proj = kva.Projector(cfg, w, max_tokens=1024)
     got, want = _run(proj, x), oracle.project(cfg, w, x)
     proj.close()
+    emulated = emu.project(cfg, w, x)
+    ee = _errs(got, emulated)
+    print(f"tiny 1024 tokens, qk scale {scale}: vs emulator worst max|err|/rms {max(e[0] for e in ee.values()):.4e}",
+          flush=True)
     if scale == 1.0:
         _check(cfg, got, want, label="tiny 1024 tokens")
-        return
-    errs = _errs(got, want)
-    print(f"tiny 1024 tokens, qk scale {scale}: worst max|err|/rms {max(e[0] for e in errs.values()):.4e}; "
-          f"rms err/rms {max(e[1] for e in errs.values()):.4e}", flush=True)
-    assert all(e[1] <= 2e-2 for e in errs.values()), errs
+    else:
+        errs = _errs(got, want)
+        print(f"tiny 1024 tokens, qk scale {scale}: vs oracle worst max|err|/rms "
+              f"{max(e[0] for e in errs.values()):.4e}; rms err/rms {max(e[1] for e in errs.values()):.4e}",
+              flush=True)
+        assert all(e[1] <= 2e-2 for e in errs.values()), errs
+    _check(cfg, got, emulated, label=f"tiny 1024 tokens vs emulator, scale {scale}")
 
 
 def test_tiny_bad_arguments(tiny):
@@ -143,13 +151,23 @@ def r2():
     return cfg, w, prep
 
 
-def test_r2_full_ubatch_parity(r2):
+@pytest.fixture(scope="module")
+def r2_full(r2):
+    """One r2 ubatch and the oracle's outputs for all 32 heads (computed once)."""
     cfg, w, prep = r2
     x = synth.make_input(cfg)
-    proj = kva.Projector(cfg, w, max_tokens=1536)
+    return x, ref.project(cfg, prep, x)
+
+
+@pytest.mark.parametrize("max_tokens", [1024, 1536])
+def test_r2_full_ubatch_parity(r2, r2_full, max_tokens):
+    """All 32 heads, all 1024 tokens, in a context of max_tokens = 1024 (the
+    benchmark's: the N = d GEMMs split K three ways) and of 1536 (two ways)."""
+    cfg, w, _ = r2
+    x, want = r2_full
+    proj = kva.Projector(cfg, w, max_tokens=max_tokens)
     got = _run(proj, x)
-    want = ref.project(cfg, prep, x)
-    _check(cfg, got, want, label="r2 1024")
+    _check(cfg, got, want, label=f"r2 1024, max_tokens {max_tokens}")
     # determinism: a second call is bitwise identical
     got2 = _run(proj, x)
     assert all(np.array_equal(a, b) for a, b in zip(got, got2))
@@ -215,14 +233,40 @@ def test_r3_blocks_are_independent_and_causal(r3):
     proj.close()
 
 
-def test_r3_parity_sampled_heads(r3):
+def test_r3_parity_all_heads(r3):
+    """All 36 heads (24 DeltaNet, 8 attention, 4 drafters) of one ubatch."""
     cfg, w = r3
     x = synth.make_input(cfg, n_tokens=1024)
     proj = kva.Projector(cfg, w, max_tokens=1024)
     got = _run(proj, x)
-    heads = [0, 3, 32, 35]          # DeltaNet, attention, drafter res.34, kva.final
-    want = ref.project(cfg, ref.prepare(cfg, w), x, which=heads)
-    _check(cfg, got, want, label="r3 sampled heads")
+    want = ref.project(cfg, ref.prepare(cfg, w), x)
+    _check(cfg, got, want, label="r3 all heads")
+    proj.close()
+
+
+def test_r3_8192_tokens_in_one_call(r3):
+    """The r3 workload as configured: an 8192-token prompt in one call of a
+    max_tokens = 8192 context is 8 independent 1024-token blocks.  Each
+    block's outputs equal, bit for bit, a 1024-token call of the same
+    context on that block alone; blocks 0 and 7 match the oracle on all 36
+    heads (the oracle's block independence is pinned on the CPU)."""
+    cfg, w = r3
+    x = synth.make_input(cfg, n_tokens=8192)
+    proj = kva.Projector(cfg, w, max_tokens=8192)
+    full = proj.project(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    for b in range(8):
+        part = proj.project(torch.from_numpy(np.ascontiguousarray(x[b * 1024:(b + 1) * 1024])).cuda())
+        torch.cuda.synchronize()
+        for i in range(len(part)):
+            assert torch.equal(full[i][b * 1024:(b + 1) * 1024], part[i]), (b, i)
+        del part
+    prep = ref.prepare(cfg, w)
+    for b in (0, 7):
+        want = ref.project(cfg, prep, x[b * 1024:(b + 1) * 1024])
+        got = [o[b * 1024:(b + 1) * 1024].cpu().numpy() for o in full]
+        _check(cfg, got, want, label=f"r3 8192-token call, block {b}")
+    del full
     proj.close()
 
 

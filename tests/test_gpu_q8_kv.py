@@ -52,6 +52,35 @@ def test_tiny_q8_0_parity():
     proj.close()
 
 
+@pytest.mark.parametrize("dtype,d_bits,where", [("q8_0", 0x7BFF, "head"), ("q8_0", 0x7C00, "trunk"),
+                                                  ("q8_0", 0x7E00, "head"), ("q4_0", 0x7BFF, "trunk"),
+                                                  ("q4_0", 0xFC00, "head")])
+def test_quantised_scale_out_of_fp16_range_is_rejected(dtype, d_bits, where):
+    """A block whose fp16 weights d * code would overflow (65504 * 127 or
+    * 8) or whose scale is an infinity or NaN is refused at create with
+    KVA_ERR_RANGE, like an fp32 / bf16 weight outside fp16's range."""
+    cfg = synth.config("tiny", weight_dtype=dtype)
+    w = synth.make_weights(cfg)
+    bpb = 34 if dtype == "q8_0" else 18
+    if where == "head":
+        t = w["heads"][1]["w"].copy()
+        w = dict(w, heads=[dict(h) for h in w["heads"]])
+        w["heads"][1]["w"] = t
+    else:
+        t = w["blocks"][2]["w_down"].copy()
+        w = dict(w, blocks=[dict(b) for b in w["blocks"]])
+        w["blocks"][2]["w_down"] = t
+    flat = t.reshape(-1).view(np.uint8)
+    flat[5 * bpb:5 * bpb + 2] = np.array([d_bits], dtype=np.uint16).view(np.uint8)
+    if dtype == "q8_0":
+        flat[5 * bpb + 2] = 127                 # a code of magnitude 127 in that block
+    else:
+        flat[5 * bpb + 2] = 0x00                # code 0: n - 8 = -8
+    with pytest.raises(kva.KvaError) as e:
+        kva.Projector(cfg, w, max_tokens=64)
+    assert e.value.status == kva.KVA_ERR_RANGE, str(e.value)
+
+
 @pytest.fixture(scope="module")
 def r3q8():
     cfg = synth.config("r3_q8_0")

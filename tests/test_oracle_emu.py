@@ -1,0 +1,73 @@
+"""CPU: the rounding-point emulator (oracle/emu.py).
+
+With no rounding point it is the oracle (float64, same steps); each point
+only stores an intermediate in a 16-bit format.  On the 1024-token tiny
+block with Q and K weights scaled x3 (scores x9) the emulator reproduces the
+size of the GPU's deviation from the oracle (0.19 x RMS at most, 8e-3 RMS),
+and it takes every rounding point together to reach it: no single storage
+decision explains it, the peaked softmax amplifies them all.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import emu, ref
+
+
+def _errs(got, want):
+    mx, sd = 0.0, 0.0
+    for i, y in want.items():
+        rms = np.sqrt(np.mean(y * y))
+        d = got[i] - y
+        mx = max(mx, float(np.max(np.abs(d)) / rms))
+        sd = max(sd, float(np.sqrt(np.mean(d * d)) / rms))
+    return mx, sd
+
+
+def _peaked(scale, n_tokens=1024):
+    cfg = synth.config("tiny")
+    w = synth.make_weights(cfg)
+    cfg = dict(cfg, attn_block=1024)
+    w = dict(w, blocks=[dict(b, wq=b["wq"] * np.float32(scale), wk=b["wk"] * np.float32(scale))
+                        for b in w["blocks"]])
+    return cfg, w, synth.make_input(cfg, n_tokens=n_tokens, seed=12)
+
+
+def test_emulator_without_rounding_is_the_oracle():
+    cfg = synth.config("tiny")
+    w, x = synth.make_weights(cfg), synth.make_input(cfg)
+    mx, _ = _errs(emu.project(cfg, w, x, points=()), ref.project(cfg, w, x))
+    assert mx < 1e-10
+    # ragged blocks take the same block split as the oracle
+    cfg4 = dict(cfg, attn_block=16)
+    x = synth.make_input(cfg4, n_tokens=40, seed=3)
+    mx, _ = _errs(emu.project(cfg4, w, x, points=()), ref.project(cfg4, w, x))
+    assert mx < 1e-10
+
+
+def test_emulator_rounding_helpers():
+    x = np.array([1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, 65519.0, 65520.0, 2.0 ** -25, 3 * 2.0 ** -25])
+    assert list(emu.f16(x)) == [1.0, 1.0 + 2.0 ** -9, 65504.0, np.inf, 0.0, 2.0 ** -23]   # ties to even
+    y = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -3.0])
+    assert list(emu.bf16(y)) == [1.0, 1.0 + 2.0 ** -6, -3.0]
+    with pytest.raises(ValueError):
+        emu.project(synth.config("tiny"), None, None, points={"bogus"})
+
+
+@pytest.mark.parametrize("scale", [1.0, 3.0])
+def test_emulator_explains_peaked_score_error(scale):
+    cfg, w, x = _peaked(scale)
+    want = ref.project(cfg, w, x)
+    mx, sd = _errs(emu.project(cfg, w, x), want)
+    print(f"qk scale {scale}: emulated max|err|/rms {mx:.4e}, rms err/rms {sd:.4e}")
+    if scale == 1.0:
+        assert mx <= 2e-2 and sd <= 4e-3              # inside the projector's bar
+        return
+    # the GPU measured 0.190 / 8.3e-3 on these inputs; storage rounding alone gives the same size
+    assert 0.12 <= mx <= 0.3 and 4e-3 <= sd <= 1.5e-2
+    # no single point does it: the Q/K rounding alone stays far below
+    mq, _ = _errs(emu.project(cfg, w, x, points={"q", "kv"}), want)
+    assert mq < 0.5 * mx
+    # and without the Q/K rounding the others still do (amplification by the peaked softmax)
+    mo, _ = _errs(emu.project(cfg, w, x, points=emu.ALL_POINTS - {"q", "kv"}), want)
+    assert mo > 0.5 * mx

@@ -629,6 +629,125 @@ def test_deltanet_update_splits_at_any_token():
     assert rows.shape[1] == 10240 + 48 + 48
 
 
+def _prepare_by_loops(m, conv_w, a_log, dt_bias, conv_state, n_k, n_v, hd):
+    """The DeltaNet preparation written out element by element from its
+    definition (the readings in the oracle's DeltaNet section): columns
+    q | k | v | a | b; a width-4 causal depthwise conv over the raw q|k|v rows
+    (the carried rows first), SiLU, each key head divided by
+    sqrt(|k|^2 + 1e-6), value heads as they are, and per value head
+    alpha = exp(-exp(A_log) * ln(1 + e^(a + dt_bias))), beta = 1 / (1 + e^-b)."""
+    T = m.shape[0]
+    C = (2 * n_k + n_v) * hd
+    W = conv_w.shape[1]
+    rows = [list(map(float, r)) for r in conv_state] + [list(map(float, r[:C])) for r in m]
+    act = [[0.0] * C for _ in range(T)]
+    for t in range(T):
+        for c in range(C):
+            acc = 0.0
+            for tau in range(W):
+                acc += float(conv_w[c][tau]) * rows[t + tau][c]
+            act[t][c] = acc / (1.0 + math.exp(-acc))
+    k = np.zeros((T, n_k, hd))
+    v = np.zeros((T, n_v, hd))
+    alpha = np.zeros((T, n_v))
+    beta = np.zeros((T, n_v))
+    for t in range(T):
+        for j in range(n_k):
+            col0 = n_k * hd + j * hd
+            nrm = math.sqrt(sum(act[t][col0 + e] ** 2 for e in range(hd)) + 1e-6)
+            for e in range(hd):
+                k[t, j, e] = act[t][col0 + e] / nrm
+        for h in range(n_v):
+            for e in range(hd):
+                v[t, h, e] = act[t][2 * n_k * hd + h * hd + e]
+            a = float(m[t, C + h])
+            b = float(m[t, C + n_v + h])
+            alpha[t, h] = math.exp(-math.exp(float(a_log[h])) * math.log1p(math.exp(a + float(dt_bias[h]))))
+            beta[t, h] = 1.0 / (1.0 + math.exp(-b))
+    new_conv = np.array(rows[T:], dtype=np.float64)
+    return k, v, alpha, beta, new_conv
+
+
+def _small_deltanet_case(seed=71, T=6, n_k=2, n_v=6, hd=4):
+    rng = np.random.default_rng(seed)
+    C = (2 * n_k + n_v) * hd
+    m = rng.standard_normal((T, C + 2 * n_v)) * 2.0
+    conv_w = rng.standard_normal((C, 4)) * 0.5
+    a_log = rng.uniform(-2.0, 1.0, n_v)
+    dt_bias = rng.standard_normal(n_v)
+    conv_state = rng.standard_normal((3, C))
+    return m, conv_w, a_log, dt_bias, conv_state, n_k, n_v, hd
+
+
+def _prepare_deviation(fn, case):
+    got = fn(*case)
+    want = _prepare_by_loops(*case)
+    return max(float(np.max(np.abs(np.asarray(g, dtype=np.float64) - w))) for g, w in zip(got, want))
+
+
+def test_deltanet_prepare_matches_elementwise_definition():
+    """Slices (q | k | v | a | b), conv, norm and gates against the scalar
+    definition on a small layer (2 key heads, 6 value heads of 4 dims)."""
+    case = _small_deltanet_case()
+    assert _prepare_deviation(ref.deltanet_prepare, case) < 1e-12
+
+
+def test_deltanet_prepare_hand_values():
+    """Gates at hand-computable points: a + dt_bias = 0 makes softplus ln 2, so
+    alpha = 2^(-exp(A_log)): 1/2 at A_log = 0, 1/4 at A_log = ln 2; beta is
+    1/2 at b = 0 and 3/4 at b = ln 3.  With conv weights (0, 0, 0, 1) the
+    conv is the identity, so k is the l2-normed SiLU of the k columns alone
+    (q columns hold other values) and v the SiLU of the v columns."""
+    n_k, n_v, hd, T = 1, 2, 4, 2
+    C = (2 * n_k + n_v) * hd
+    m = np.zeros((T, C + 2 * n_v))
+    m[:, :hd] = 7.0                                          # q: must not leak into k
+    m[:, hd:2 * hd] = [[1.0, 2.0, 3.0, 4.0], [-1.0, 0.5, 0.0, 2.0]]
+    m[:, 2 * hd:C] = np.arange(T * n_v * hd).reshape(T, n_v * hd) / 10.0 - 1.0
+    dt_bias = np.array([0.3, -1.2])
+    m[:, C:C + n_v] = -dt_bias                               # a + dt_bias = 0
+    m[0, C + n_v:] = [0.0, math.log(3.0)]
+    m[1, C + n_v:] = [math.log(3.0), 0.0]
+    conv_w = np.tile([0.0, 0.0, 0.0, 1.0], (C, 1))
+    a_log = np.array([0.0, math.log(2.0)])
+    k, v, alpha, beta, new_conv = ref.deltanet_prepare(m, conv_w, a_log, dt_bias, np.zeros((3, C)), n_k, n_v, hd)
+    assert np.allclose(alpha, [[0.5, 0.25], [0.5, 0.25]], rtol=1e-14)
+    assert np.allclose(beta, [[0.5, 0.75], [0.75, 0.5]], rtol=1e-14)
+    silu = lambda z: z / (1.0 + np.exp(-z))
+    kk = silu(m[:, hd:2 * hd])
+    assert np.allclose(k[:, 0, :], kk / np.sqrt(np.sum(kk ** 2, axis=1, keepdims=True) + 1e-6), rtol=1e-14)
+    assert np.allclose(v.reshape(T, -1), silu(m[:, 2 * hd:C]), rtol=1e-14)
+    assert np.array_equal(new_conv[1:], m[:, :C]) and np.array_equal(new_conv[0], np.zeros(C))
+
+
+def _prep_swapped_ab(m, conv_w, a_log, dt_bias, conv_state, n_k, n_v, hd):
+    C = (2 * n_k + n_v) * hd
+    m2 = m.copy()
+    m2[:, C:C + n_v], m2[:, C + n_v:C + 2 * n_v] = m[:, C + n_v:C + 2 * n_v], m[:, C:C + n_v]
+    return ref.deltanet_prepare(m2, conv_w, a_log, dt_bias, conv_state, n_k, n_v, hd)
+
+
+def _prep_gate_sign(*case):
+    k, v, alpha, beta, c = ref.deltanet_prepare(*case)
+    return k, v, 1.0 / alpha, beta, c                       # exp(+exp(A_log) softplus(.))
+
+
+def _prep_k_from_q(m, conv_w, a_log, dt_bias, conv_state, n_k, n_v, hd):
+    m2, cs2, w2 = m.copy(), conv_state.copy(), conv_w.copy()
+    m2[:, n_k * hd:2 * n_k * hd] = m[:, :n_k * hd]
+    cs2[:, n_k * hd:2 * n_k * hd] = conv_state[:, :n_k * hd]
+    w2[n_k * hd:2 * n_k * hd] = conv_w[:n_k * hd]
+    k, v, alpha, beta, _ = ref.deltanet_prepare(m2, w2, a_log, dt_bias, cs2, n_k, n_v, hd)
+    return k, v, alpha, beta, ref.deltanet_prepare(m, conv_w, a_log, dt_bias, conv_state, n_k, n_v, hd)[4]
+
+
+@pytest.mark.parametrize("mutant", [_prep_swapped_ab, _prep_gate_sign, _prep_k_from_q])
+def test_deltanet_prepare_planted_mistakes_are_caught(mutant):
+    """a and b swapped, the sign of the log-decay flipped, k read from the q
+    columns: each moves some output far off the elementwise definition."""
+    assert _prepare_deviation(mutant, _small_deltanet_case()) > 1e-3
+
+
 # ------------------------------------------------------------------ single-map projector
 
 def test_map_project_matches_torch_linear_and_closed_cases():
