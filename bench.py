@@ -442,8 +442,11 @@ COPY_BYTES = 1 << 30
 
 def cpu_baseline(min_seconds: float = 10.0, max_reps: int = 8):
     """The oracle, as it stands, on whole r2 ubatches (1024 tokens, all 32 heads),
-    repeated until about `min_seconds` of CPU work; tokens/s over all reps."""
+    repeated until about `min_seconds` of CPU work; tokens/s over all reps.
+    Beside it (key "fp32"), the same steps in float32 NumPy (sgemm): the
+    oracle's algorithm without rounding points, timed the same way."""
     import oracle
+    from oracle import emu
     blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
@@ -462,11 +465,26 @@ def cpu_baseline(min_seconds: float = 10.0, max_reps: int = 8):
         oracle.project(cfg, prep, x)
         reps += 1
     dt = time.perf_counter() - t0
+    del prep
+    # float32: weight decode happens inside the call (it is part of emu.project),
+    # so time it separately and subtract it from the total
+    t1 = time.perf_counter()
+    emu.project(cfg, w, x[:1], points=(), arith=np.float32)
+    decode = time.perf_counter() - t1
+    r32, t2 = 0, time.perf_counter()
+    while r32 < max_reps and (r32 == 0 or time.perf_counter() - t2 < min_seconds / 2):
+        emu.project(cfg, w, x, points=(), arith=np.float32)
+        r32 += 1
+    dt32 = max(time.perf_counter() - t2 - r32 * decode, 1e-9)
     return {"value": 1024 * reps / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"r2, {reps} x one 1024-token ubatch (all 32 heads), float64 NumPy with "
                       f"{threads} BLAS threads, {dt:.1f} s",
             "cpu_model": _cpu_model(), "blas": blas,
-            "affinity_cores": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+            "affinity_cores": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
+            "fp32": {"value": 1024 * r32 / dt32, "unit": "tokens/s", "cores": int(threads),
+                     "sample": f"r2, {r32} x one 1024-token ubatch, the oracle's steps in float32 NumPy "
+                               f"(sgemm), {dt32:.1f} s after subtracting the weight decode "
+                               f"({decode:.1f} s per call)"}}
 
 
 def _cpu_model() -> str:

@@ -148,9 +148,13 @@ kva_status kva_validate_config(const kva_config* cfg);
  * head weights are kept as bf16 (fp32 ones rounded to nearest even).  q8_0
  * weights are split losslessly into an int8 code plane and an fp16 scale
  * plane; the GEMMs form each weight as d*q rounded once to fp16 on the fly
- * (see kva_debug_dequant_q8_0_f16) and run fp16 MFMA throughout.  q4_0
+ * (see kva_debug_dequant_q8_0_f16) and run fp16 MFMA throughout: the weight
+ * the product uses is fp16(d*q), within 2^-12 relative of d*q (2^-25
+ * absolute where d*q is below fp16's normal range), not d*q itself.  q4_0
  * weights likewise: a 4-bit code plane and an fp16 scale plane, weights
- * d*(n-8) rounded once to fp16 (kva_debug_dequant_q4_0_f16).  The call is
+ * d*(n-8) rounded once to fp16 (kva_debug_dequant_q4_0_f16).  KVA_ERR_RANGE
+ * if a q8_0 / q4_0 block's scale is not finite or d*code rounds past fp16's
+ * largest finite value (|d| * max|code| >= 65520).  The call is
  * synchronous.  On success *out owns all device memory it allocated; on
  * failure *out is NULL and nothing is leaked. */
 kva_status kva_create(const kva_config* cfg, const kva_weights* w, int device, kva_ctx** out);
@@ -219,9 +223,9 @@ kva_status kva_map_project(kva_ctx* ctx, const float* x, int32_t n_tokens, float
  * pools); page_table is a device int32 array mapping logical page
  * (position / page_size) to a physical page.
  *
- * KVA_KV_Q8_0_HADAMARD ("Qwen3.8-27B-KVA" card, "Projector quantization and
- * flash-attn": quantised q8_0 K/V caches, with the exact path's Hadamard
- * rotation applied to the approximated K/V): each row is first rotated by the
+ * KVA_KV_Q8_0_HADAMARD ("Qwen3.8-27B-KVA" card, "Other notes": q8_0 K/V
+ * caches are supported, and the approximated K/V are rotated by the same
+ * Hadamard transform as the exactly computed ones): each row is first rotated by the
  * orthonormal Walsh-Hadamard transform of Sylvester order, y = H x / 16 with
  * H[i][j] = (-1)^popcount(i & j) over the 256 dims (an orthogonal involution:
  * a consumer rotates queries alike, or rotates y back), then stored as 8 q8_0
@@ -337,7 +341,8 @@ kva_status kva_deltanet_update(const kva_deltanet_layer* layers, int32_t n_layer
 /* Test hook: dequantises n_blocks q8_0 blocks (device, 34 bytes each: fp16
  * scale d, then 32 int8 codes q; format from [KVA] "Projector quantization and
  * flash-attn") to fp32 (device, 32*n_blocks values): out = float(d) * q,
- * exact, fp16 subnormal scales honoured.  Asynchronous on `stream`;
+ * exact, fp16 subnormal scales honoured.  This is the format's value; the
+ * GEMMs do not run this routine (their operand is kva_debug_dequant_q8_0_f16).  Asynchronous on `stream`;
  * KVA_ERR_ARG for NULL pointers, KVA_ERR_SHAPE for n_blocks < 0. */
 kva_status kva_debug_dequant_q8_0(const void* blocks, int64_t n_blocks, float* out, void* stream);
 
@@ -390,6 +395,18 @@ kva_status kva_debug_poison_scratch(kva_ctx* ctx, void* stream);
  * capacity is too small). */
 kva_status kva_debug_head_plan(const kva_config* cfg, int32_t* n_cols, int32_t* col_head,
                                int32_t* col_index, int64_t capacity);
+
+/* Test hook (host only, no device): packs one weight [rows][K] (src, host,
+ * in src_dtype storage: fp32, bf16, or q8_0 / q4_0 blocks along K) the way
+ * kva_create lays it out in device memory, rows padded with zero rows to a
+ * multiple of 256.  target 0: fp16 values, 1: bf16 values (both in 32-wide K
+ * slabs of 256 rows, 16-byte chunk c of row r at c ^ ((r >> 2) & 3)); 2: q8_0
+ * code plane (out) and fp16 scale plane (scales); 3: q4_0 likewise.  out
+ * receives the values or codes (out_bytes capacity), scales the scales
+ * (n_scales capacity; quantised targets only).  Errors as kva_create's
+ * packing (KVA_ERR_DTYPE, _RANGE), KVA_ERR_SHAPE for short buffers. */
+kva_status kva_debug_pack_weight(const void* src, int32_t src_dtype, int32_t rows, int32_t K, int32_t target,
+                                 void* out, int64_t out_bytes, uint16_t* scales, int64_t n_scales);
 
 /* Test hook (host only): the conversion kva_create applies to trunk weights,
  * src_dtype (KVA_DTYPE_F32 or KVA_DTYPE_BF16) -> fp16 bit patterns, rounding

@@ -109,6 +109,7 @@ _SIGS = {
     "kva_debug_poison_scratch": (c_i32, [c_vp, c_vp]),
     "kva_debug_head_plan": (c_i32, [ctypes.POINTER(kva_config), ctypes.POINTER(c_i32), c_vp, c_vp, c_i64]),
     "kva_debug_host_to_f16": (c_i32, [c_vp, c_i32, c_i64, c_vp]),
+    "kva_debug_pack_weight": (c_i32, [c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_i64, c_vp, c_i64]),
     "kva_get_stats": (c_i32, [c_vp, ctypes.POINTER(kva_stats)]),
     "kva_profile_enable": (c_i32, [c_vp, ctypes.c_uint32]),
     "kva_profile_read": (c_i32, [c_vp, ctypes.POINTER(kva_stage_time)]),
@@ -289,6 +290,25 @@ def kva_debug_host_to_f16(src, src_dtype: str):
     dst = np.empty(src.size, dtype=np.uint16)
     st = lib().kva_debug_host_to_f16(src.ctypes.data, DTYPES[src_dtype], src.size, dst.ctypes.data)
     return st, dst.reshape(src.shape)
+
+
+PACK_TARGETS = {"f16": 0, "bf16": 1, "q8_0": 2, "q4_0": 3}
+
+
+def kva_debug_pack_weight(src, src_dtype: str, rows: int, K: int, target: str):
+    """Host packing of one weight as kva_create lays it out; returns
+    (status, values or codes as bytes, scales or None)."""
+    import numpy as np
+    src = np.ascontiguousarray(src)
+    rpad = (rows + 255) // 256 * 256
+    quant = target in ("q8_0", "q4_0")
+    nbytes = rpad * K * 2 if not quant else (rpad * K if target == "q8_0" else rpad * K // 2)
+    out = np.zeros(nbytes, dtype=np.uint8)
+    sc = np.zeros(rpad * (K // 32), dtype=np.uint16) if quant else None
+    st = lib().kva_debug_pack_weight(src.ctypes.data, DTYPES[src_dtype], rows, K, PACK_TARGETS[target],
+                                     out.ctypes.data, out.size, sc.ctypes.data if quant else None,
+                                     sc.size if quant else 0)
+    return st, out, sc
 
 
 def kva_get_stats(ctx: int) -> dict:

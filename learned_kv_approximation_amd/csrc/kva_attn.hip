@@ -1,7 +1,7 @@
 // Block-causal multi-head attention for the projector's transformer blocks.
 //
-// The projector's blocks attend only within the ubatch (attention block) the
-// tokens arrive in, causally ("Qwen3.8-27B-KVA" model card, "What the hell?"
+// Attention in the projector is causal and confined to the ubatch (attention
+// block) a token arrived in ("Qwen3.8-27B-KVA" model card, "What the hell?"
 // and the r2/r3 table: heads of 128, causal within 1024-token blocks).  For
 // query i of head h in block [s, e):  o_i = sum_{s<=j<=i} softmax_j(q_i.k_j/sqrt(128)) v_j.
 //

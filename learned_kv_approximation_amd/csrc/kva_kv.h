@@ -175,9 +175,9 @@ __device__ __forceinline__ int64_t kv_row_index(const KvPool& c, int pg, int64_t
 // H[i][j] = (-1)^popcount(i & j).  One butterfly stage per bit of the dim
 // index, (a, b) -> (a + b, a - b) on the pair that differs in that bit:
 // bits 0 and 1 inside the lane, bits 2..7 across lanes (lane bit 0..5).  The
-// quantised KV cache stores K and V rotated this way ([KVA] "Projector
-// quantization and flash-attn": the approximated K/V get the exact path's
-// Hadamard rotation).  Must be called by all 64 lanes of a wave together.
+// quantised KV cache stores K and V rotated this way ([KVA] "Other notes":
+// the approximated K/V are rotated by the same Hadamard transform as the
+// exactly computed ones).  Must be called by all 64 lanes of a wave together.
 //
 // A cross-lane stage is one fused multiply-add per value, b <- b + c * o with
 // o the partner lane's value and c = -1 on the lane whose stage bit is set,

@@ -364,21 +364,32 @@ struct RowSrc {
 // Target layouts on the device.
 enum PackTarget { PACK_F16_T32 = 0, PACK_BF16_T32 = 1, PACK_Q8 = 2, PACK_Q4 = 3 };
 
-// Packs rows (each K wide, stored in `dtype`) into the compute layout and
-// uploads it: fp16 or bf16 values in the tiled layout of tiled32_index
-// (32-wide slabs), or for q8_0 the 34-byte blocks split losslessly into an
-// int8 code plane and an fp16 scale plane, tiled the same way.
-kva_status pack_weight(kva_ctx* ctx, int dtype, int64_t K, const std::vector<RowSrc>& rows,
-                       PackTarget target, kva_ctx::DevW* out, const char* name) {
+// A weight in its device layout, still on the host: 16-bit values w16 in the
+// tiled32_index layout, or int8/4-bit codes q and fp16 scales sc (q8_0 /
+// q4_0 planes, q8_code_chunk / q4_code_chunk and q8_scale_index layouts).
+struct HostPacked {
+    std::vector<uint16_t> w16;
+    std::vector<uint8_t> q;
+    std::vector<uint16_t> sc;
+};
+
+// Packs rows (each K wide, stored in `dtype`) into the compute layout on the
+// host: fp16 or bf16 values in the tiled layout of tiled32_index (32-wide
+// slabs), or for q8_0 / q4_0 the blocks split losslessly into a code plane
+// and an fp16 scale plane, tiled the same way.  Host memory only.
+kva_status pack_host(int dtype, int64_t K, const std::vector<RowSrc>& rows, PackTarget target, HostPacked* out,
+                     const char* name) {
     const int64_t n = (int64_t)rows.size();
     for (const RowSrc& r : rows)
         if (!r.src && r.row >= 0) return fail(KVA_ERR_ARG, "weight %s is NULL", name);
+    if (n % kWeightTileRows || K % 32 || K <= 0) return fail(KVA_ERR_SHAPE, "weight %s: bad padding", name);
     if (target == PACK_Q4) {
         if (dtype != KVA_DTYPE_Q4_0) return fail(KVA_ERR_DTYPE, "q4_0 layout needs q4_0 weights (%s)", name);
-        if (n % kWeightTileRows || K % 32) return fail(KVA_ERR_SHAPE, "weight %s: bad padding", name);
         const int64_t nb = K / 32;
-        std::vector<uint8_t> q((size_t)(n * K / 2), 0x88);   // padding rows: codes 8 (and scale 0)
-        std::vector<uint16_t> sc((size_t)(n * nb), 0);
+        std::vector<uint8_t>& q = out->q;
+        std::vector<uint16_t>& sc = out->sc;
+        q.assign((size_t)(n * K / 2), 0x88);   // padding rows: codes 8 (and scale 0)
+        sc.assign((size_t)(n * nb), 0);
         for (int64_t r = 0; r < n; ++r) {
             if (!rows[r].src) continue;
             const uint8_t* blk = static_cast<const uint8_t*>(rows[r].src) + rows[r].row * nb * 18;
@@ -405,17 +416,15 @@ kva_status pack_weight(kva_ctx* ctx, int dtype, int64_t K, const std::vector<Row
                 }
             }
         }
-        HIP_TRY(ctx->alloc(&out->q, q.size(), true));
-        HIP_TRY(ctx->alloc(&out->sc, sc.size() * 2, true));
-        KVA_TRY(upload(ctx, out->q, q.data(), q.size()));
-        return upload(ctx, out->sc, sc.data(), sc.size() * 2);
+        return KVA_OK;
     }
     if (target == PACK_Q8) {
         if (dtype != KVA_DTYPE_Q8_0) return fail(KVA_ERR_DTYPE, "q8_0 layout needs q8_0 weights (%s)", name);
-        if (n % kWeightTileRows || K % 32) return fail(KVA_ERR_SHAPE, "weight %s: bad padding", name);
         const int64_t nb = K / 32;
-        std::vector<int8_t> q((size_t)(n * K), 0);
-        std::vector<uint16_t> sc((size_t)(n * nb), 0);
+        std::vector<uint8_t>& q = out->q;
+        std::vector<uint16_t>& sc = out->sc;
+        q.assign((size_t)(n * K), 0);
+        sc.assign((size_t)(n * nb), 0);
         for (int64_t r = 0; r < n; ++r) {
             if (!rows[r].src) continue;
             const uint8_t* blk = static_cast<const uint8_t*>(rows[r].src) + rows[r].row * nb * 34;
@@ -430,15 +439,12 @@ kva_status pack_weight(kva_ctx* ctx, int dtype, int64_t K, const std::vector<Row
                 sc[(size_t)q8_scale_index(r, b, K)] = d_bits;
                 for (int64_t c = 0; c < 32; c += 8) {   // 8 consecutive codes form one chunk
                     uint32_t w[2];
-                    q8_chunk_pack(reinterpret_cast<const int8_t*>(blk + b * 34 + 2 + c), &w[0], &w[1]);
+                    q8_chunk_pack(codes + c, &w[0], &w[1]);
                     std::memcpy(&q[(size_t)q8_code_chunk(r, b * 32 + c, K)], w, 8);
                 }
             }
         }
-        HIP_TRY(ctx->alloc(&out->q, q.size(), true));
-        HIP_TRY(ctx->alloc(&out->sc, sc.size() * 2, true));
-        KVA_TRY(upload(ctx, out->q, q.data(), q.size()));
-        return upload(ctx, out->sc, sc.data(), sc.size() * 2);
+        return KVA_OK;
     }
     if (dtype != KVA_DTYPE_F32 && dtype != KVA_DTYPE_BF16)
         return fail(KVA_ERR_DTYPE, "16-bit layout needs fp32 or bf16 weights (%s)", name);
@@ -457,13 +463,27 @@ kva_status pack_weight(kva_ctx* ctx, int dtype, int64_t K, const std::vector<Row
         }
     }
     if (ovf) return fail(KVA_ERR_RANGE, "weight %s has values outside the fp16 range", name);
-    if (n % kWeightTileRows || K % 32) return fail(KVA_ERR_SHAPE, "weight %s: bad padding", name);
-    std::vector<uint16_t> t(w.size());
+    std::vector<uint16_t>& t = out->w16;
+    t.assign(w.size(), 0);
     for (int64_t r = 0; r < n; ++r)
         for (int64_t k = 0; k < K; k += 8)    // 8 consecutive K-values stay together
             std::memcpy(&t[(size_t)tiled32_index(r, k, K)], &w[(size_t)(r * K + k)], 16);
-    HIP_TRY(ctx->alloc(&out->w16, t.size() * 2, true));
-    return upload(ctx, out->w16, t.data(), t.size() * 2);
+    return KVA_OK;
+}
+
+// pack_host, then upload into memory the context owns.
+kva_status pack_weight(kva_ctx* ctx, int dtype, int64_t K, const std::vector<RowSrc>& rows,
+                       PackTarget target, kva_ctx::DevW* out, const char* name) {
+    HostPacked hp;
+    KVA_TRY(pack_host(dtype, K, rows, target, &hp, name));
+    if (target == PACK_Q8 || target == PACK_Q4) {
+        HIP_TRY(ctx->alloc(&out->q, hp.q.size(), true));
+        HIP_TRY(ctx->alloc(&out->sc, hp.sc.size() * 2, true));
+        KVA_TRY(upload(ctx, out->q, hp.q.data(), hp.q.size()));
+        return upload(ctx, out->sc, hp.sc.data(), hp.sc.size() * 2);
+    }
+    HIP_TRY(ctx->alloc(&out->w16, hp.w16.size() * 2, true));
+    return upload(ctx, out->w16, hp.w16.data(), hp.w16.size() * 2);
 }
 
 // Rows [0, n) of one tensor, then zero rows up to a multiple of kColPad.
@@ -671,6 +691,7 @@ inline void clear_stale_error() { (void)hipGetLastError(); }
     } while (0)
 
 }  // namespace
+
 
 // ================================================================== C ABI
 
@@ -1088,6 +1109,32 @@ kva_status kva_debug_head_plan(const kva_config* cfg, int32_t* n_cols, int32_t* 
     for (int64_t i = 0; i < p.n_pad; ++i) {
         if (col_head) col_head[i] = p.col_head[i];
         if (col_index) col_index[i] = p.col_head[i] < 0 ? -1 : p.col_index[i];
+    }
+    return KVA_OK;
+}
+
+kva_status kva_debug_pack_weight(const void* src, int32_t src_dtype, int32_t rows, int32_t K, int32_t target,
+                                 void* out, int64_t out_bytes, uint16_t* scales, int64_t n_scales) {
+    if (!src || !out) return fail(KVA_ERR_ARG, "NULL argument");
+    if (rows <= 0 || K <= 0) return fail(KVA_ERR_SHAPE, "rows and K must be positive");
+    if (target < PACK_F16_T32 || target > PACK_Q4) return fail(KVA_ERR_ARG, "unknown target %d", target);
+    std::vector<RowSrc> rv;
+    for (int32_t r = 0; r < rows; ++r) rv.push_back({src, r});
+    while (rv.size() % kColPad) rv.push_back({nullptr, -1});
+    HostPacked hp;
+    try {
+        KVA_TRY(pack_host(src_dtype, K, rv, (PackTarget)target, &hp, "debug"));
+    } catch (const std::bad_alloc&) {
+        return fail(KVA_ERR_OOM, "host allocation failed");
+    }
+    const bool quant = target == PACK_Q8 || target == PACK_Q4;
+    const size_t bytes = quant ? hp.q.size() : hp.w16.size() * 2;
+    if ((uint64_t)out_bytes < bytes) return fail(KVA_ERR_SHAPE, "out needs %zu bytes", bytes);
+    std::memcpy(out, quant ? (const void*)hp.q.data() : (const void*)hp.w16.data(), bytes);
+    if (quant) {
+        if (!scales || n_scales < (int64_t)hp.sc.size())
+            return fail(KVA_ERR_SHAPE, "scales needs %zu entries", hp.sc.size());
+        std::memcpy(scales, hp.sc.data(), hp.sc.size() * 2);
     }
     return KVA_OK;
 }

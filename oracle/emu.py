@@ -24,9 +24,11 @@ time:
   act     silu(gate) * up                                    fp16
   z       final-norm output                                  bf16 (fp16 for q8_0/q4_0)
 
-The accumulations (GEMMs, softmax sums) stay float64, so a residual
-difference between this emulation and the GPU is accumulation order and
-fp32 rounding, not a storage decision.
+The accumulations (GEMMs, softmax sums) stay float64 by default, so a
+residual difference between this emulation and the GPU is accumulation
+order and fp32 rounding, not a storage decision.  With arith=np.float32 and
+no rounding point the same steps run in float32 NumPy (sgemm): the
+benchmark's float32 CPU baseline.
 """
 from __future__ import annotations
 
@@ -54,7 +56,16 @@ def bf16(x: np.ndarray) -> np.ndarray:
 
 
 def _r(points, name, fn, x):
-    return fn(x) if name in points else x
+    return fn(x).astype(x.dtype) if name in points else x
+
+
+def _rmsnorm(x, g, eps):
+    """ref.rmsnorm in the dtype of x."""
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * g
+
+
+def _silu(x):
+    return x / (1.0 + np.exp(-x))
 
 
 def attention_base2(q2: np.ndarray, k: np.ndarray, v: np.ndarray, n_heads: int, head_dim: int,
@@ -64,7 +75,7 @@ def attention_base2(q2: np.ndarray, k: np.ndarray, v: np.ndarray, n_heads: int, 
     With no rounding this equals ref.causal_attention(q, k, v) up to the
     float64 rounding of the rescaled scores."""
     T = q2.shape[0]
-    out = np.empty((T, n_heads * head_dim), dtype=np.float64)
+    out = np.empty((T, n_heads * head_dim), dtype=q2.dtype)
     allowed = np.tril(np.ones((T, T), dtype=bool))
     for h in range(n_heads):
         c = slice(h * head_dim, (h + 1) * head_dim)
@@ -75,11 +86,11 @@ def attention_base2(q2: np.ndarray, k: np.ndarray, v: np.ndarray, n_heads: int, 
     return out
 
 
-def project(cfg: dict, weights: dict, x: np.ndarray, points=ALL_POINTS, which=None) -> dict:
+def project(cfg: dict, weights: dict, x: np.ndarray, points=ALL_POINTS, which=None, arith=np.float64) -> dict:
     """Per-head outputs {head: [T, out_dim]} of the projector with the given
     rounding points applied (ALL_POINTS: every storage rounding of a 16-bit
     implementation; an empty set reproduces ref.project up to float64
-    rounding)."""
+    rounding), computed in `arith` (float64 or float32)."""
     points = frozenset(points)
     unknown = points - ALL_POINTS
     if unknown:
@@ -90,46 +101,49 @@ def project(cfg: dict, weights: dict, x: np.ndarray, points=ALL_POINTS, which=No
     H, hd = cfg["n_heads"], cfg["head_dim"]
     eps = cfg["eps"]
 
-    def wt(w, o, i):
-        return _r(points, "w", f16, ref.weight_f64(w, dt, o, i))
+    ar = np.dtype(arith)
 
-    x = np.asarray(x, dtype=np.float64)
-    g_in = weights["in_norm"].astype(np.float64)
+    def wt(w, o, i):
+        return _r(points, "w", f16, ref.weight_f64(w, dt, o, i)).astype(ar)
+
+    x = np.asarray(x, dtype=ar)
+    g_in = weights["in_norm"].astype(ar)
     w_in = wt(weights["in_proj"], d, n_in)
     blocks = []
     for b in weights["blocks"]:
         blocks.append({k: wt(b[k], *shape) for k, shape in
                        (("wq", (H * hd, d)), ("wk", (H * hd, d)), ("wv", (H * hd, d)), ("wo", (d, H * hd)),
                         ("w_gate", (f, d)), ("w_up", (f, d)), ("w_down", (d, f)))})
-        blocks[-1]["attn_norm"] = b["attn_norm"].astype(np.float64)
-        blocks[-1]["ffn_norm"] = b["ffn_norm"].astype(np.float64)
+        blocks[-1]["attn_norm"] = b["attn_norm"].astype(ar)
+        blocks[-1]["ffn_norm"] = b["ffn_norm"].astype(ar)
+    g_out = weights["out_norm"].astype(ar)
     z_round = f16 if quant else bf16
 
-    z = np.empty((x.shape[0], d), dtype=np.float64)
+    z = np.empty((x.shape[0], d), dtype=ar)
     for s, e in ref.block_ranges(x.shape[0], cfg["attn_block"]):
-        u = _r(points, "in", f16, ref.rmsnorm(x[s:e], g_in, eps))
+        u = _r(points, "in", f16, _rmsnorm(x[s:e], g_in, eps))
         h = u @ w_in.T
         for b in blocks:
-            a = _r(points, "a1", f16, ref.rmsnorm(h, b["attn_norm"], eps))
-            q2 = (a @ b["wq"].T) * (Q_SCALE_F32 if "q" in points else Q_SCALE)
+            a = _r(points, "a1", f16, _rmsnorm(h, b["attn_norm"], eps))
+            q2 = (a @ b["wq"].T) * ar.type(Q_SCALE_F32 if "q" in points else Q_SCALE)
             q2 = _r(points, "q", f16, q2)
             k = _r(points, "kv", f16, a @ b["wk"].T)
             v = _r(points, "kv", f16, a @ b["wv"].T)
             o = _r(points, "o", f16, attention_base2(q2, k, v, H, hd, points))
             h = h + o @ b["wo"].T
-            a = _r(points, "a2", f16, ref.rmsnorm(h, b["ffn_norm"], eps))
-            act = _r(points, "act", f16, ref.silu(a @ b["w_gate"].T) * (a @ b["w_up"].T))
+            a = _r(points, "a2", f16, _rmsnorm(h, b["ffn_norm"], eps))
+            act = _r(points, "act", f16, _silu(a @ b["w_gate"].T) * (a @ b["w_up"].T))
             h = h + act @ b["w_down"].T
-        z[s:e] = _r(points, "z", z_round, ref.rmsnorm(h, weights["out_norm"].astype(np.float64), eps))
+        z[s:e] = _r(points, "z", z_round, _rmsnorm(h, g_out, eps))
 
     out = {}
     which = range(len(cfg["heads"])) if which is None else which
     for i in which:
         hdesc = cfg["heads"][i]
         W = ref.weight_f64(weights["heads"][i]["w"], dt, hdesc["out_dim"], d)
-        W = _r(points, "wh", f16 if quant else bf16, W)
+        W = _r(points, "wh", f16 if quant else bf16, W).astype(ar)
         y = z @ W.T
         if weights["heads"][i]["b"] is not None:
-            y = y + np.asarray(weights["heads"][i]["b"], dtype=np.float64)
+            y = y + np.asarray(weights["heads"][i]["b"], dtype=ar)
         out[i] = y
     return out

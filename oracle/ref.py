@@ -229,9 +229,10 @@ def block_forward(h: np.ndarray, b: dict, cfg: dict) -> np.ndarray:
 
 def block_ranges(n_tokens: int, attn_block: int):
     """Consecutive attention blocks of `attn_block` tokens from token 0 of the
-    call; the last one may be shorter ([KVA] "What the hell?": the blocks
-    attend only within the ubatch they are given; the card's evaluation uses
-    1536-token prompts, i.e. a full ubatch and a 512-token remainder)."""
+    call; the last one may be shorter ([KVA] "What the hell?": attention in
+    the projector never looks past the ubatch a token arrived in; the card's
+    evaluation uses 1536-token prompts, i.e. a full ubatch and a 512-token
+    remainder)."""
     return [(s, min(s + attn_block, n_tokens)) for s in range(0, n_tokens, attn_block)]
 
 
@@ -375,9 +376,9 @@ def kv_write(kv, gain, pos0, page_table, k_pool, v_pool, page_size: int = 256, *
 
 
 # --------------------------------------------------------------------------
-# quantised KV cache with a Hadamard rotation ([KVA] "Projector quantization
-# and flash-attn": q8_0 K and V caches work, and the engine rotates the
-# approximated K and V with the same Hadamard transform as the exact path).
+# quantised KV cache with a Hadamard rotation ([KVA] "Other notes": q8_0 K and
+# V caches are supported, and the approximated K and V go through the same
+# Hadamard rotation as the exactly computed ones).
 # Readings (the pages give no more than that sentence):
 #  - the rotation is the orthonormal Walsh-Hadamard transform of Sylvester
 #    order over each KV head's 256 dims, y = H x / 16 with

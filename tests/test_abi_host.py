@@ -158,3 +158,84 @@ def test_build_commands_keep_packed_fp32_off():
         objs.append(src + ".o")
     link = _build.link_command(objs, "lib.so")
     assert "-shared" in link and all(o in link for o in objs) and link[-2:] == ["-o", "lib.so"]
+
+
+# ------------------------------------------------------------------ weight packing (host only)
+
+def _t32_index(r, k, K):
+    """Element index of (row r, K-value k) in the 16-bit device layout: 256-row
+    groups, 32-wide K slabs, 64-byte rows, 16-byte chunk c at c ^ ((r >> 2) & 3)."""
+    nb, rr, kt = r // 256, r % 256, k // 32
+    c, e = (k % 32) // 8, k % 8
+    return ((nb * (K // 32) + kt) * 256 + rr) * 32 + ((c ^ ((rr >> 2) & 3)) * 8) + e
+
+
+@pytest.mark.parametrize("target", ["f16", "bf16"])
+def test_pack_weight_16bit_layout(target):
+    rng = np.random.default_rng(61)
+    rows, K = 300, 96
+    w = (rng.standard_normal((rows, K)) * 0.1).astype(np.float32)
+    st, out, _ = kva.kva_debug_pack_weight(w, "f32", rows, K, target)
+    assert st == kva.KVA_OK
+    got = out.view(np.uint16)
+    want = (np.float16 if target == "f16" else None)
+    r, k = np.meshgrid(np.arange(512), np.arange(K), indexing="ij")
+    idx = _t32_index(r, k, K)
+    assert np.unique(idx).size == idx.size == got.size            # a permutation of the buffer
+    if target == "f16":
+        vals = np.zeros((512, K), dtype=np.float16)
+        vals[:rows] = w.astype(np.float16)
+        assert np.array_equal(got[idx], vals.view(np.uint16))
+    else:
+        bits = np.zeros((512, K), dtype=np.uint16)
+        bits[:rows] = synth.f32_to_bf16_bits(w)
+        assert np.array_equal(got[idx], bits)
+
+
+def test_pack_weight_q8_0_planes():
+    rng = np.random.default_rng(62)
+    rows, K = 260, 64
+    codes = rng.integers(-128, 128, size=(rows, K), dtype=np.int8)
+    sc = (np.abs(rng.standard_normal((rows, K // 32))) * 1e-3).astype(np.float16)
+    blocks = synth.pack_q8_0(codes, sc)
+    st, out, scales = kva.kva_debug_pack_weight(blocks, "q8_0", rows, K, "q8_0")
+    assert st == kva.KVA_OK
+    for r in (0, 1, 5, 37, 255, 256, 259, 300, 511):
+        for b in range(K // 32):
+            nb, rr = r // 256, r % 256
+            si = (nb * (K // 32) + b) * 256 + rr
+            want_d = sc[r, b].view(np.uint16) if r < rows else 0
+            assert scales[si] == want_d, (r, b)
+            for c in range(4):
+                off = ((nb * (K // 32) + b) * 256 + rr) * 32 + ((c ^ ((rr >> 2) & 3)) * 8)
+                chunk = out[off:off + 8]
+                q = codes[r, b * 32 + 8 * c: b * 32 + 8 * c + 8] if r < rows else np.zeros(8, np.int8)
+                biased = (q.view(np.uint8) ^ 0x80)
+                # each 32-bit half holds codes 4j, 4j+2, 4j+1, 4j+3 in its bytes
+                order = [0, 2, 1, 3, 4, 6, 5, 7]
+                assert np.array_equal(chunk, biased[order]) if r < rows else np.all(chunk == 0), (r, b, c)
+
+
+def test_pack_weight_q4_0_planes_and_range():
+    rng = np.random.default_rng(63)
+    rows, K = 256, 64
+    n = rng.integers(0, 16, size=(rows, K)).astype(np.uint8)
+    sc = (np.abs(rng.standard_normal((rows, K // 32))) * 1e-3).astype(np.float16)
+    blocks = synth.pack_q4_0(n, sc)
+    st, out, scales = kva.kva_debug_pack_weight(blocks, "q4_0", rows, K, "q4_0")
+    assert st == kva.KVA_OK
+    for r in (0, 3, 8, 100, 255):
+        for b in range(K // 32):
+            for c in range(4):
+                off = ((b) * 256 + r) * 16 + ((c ^ ((r >> 3) & 3)) * 4)
+                wv = int(out[off:off + 4].view(np.uint32)[0])
+                for e in range(8):
+                    h, hi = e // 2, e % 2
+                    got = (wv >> (16 * hi + 4 * h)) & 0xF
+                    assert got == n[r, b * 32 + 8 * c + e], (r, b, c, e)
+    # a scale whose weights overflow fp16 is refused
+    bad = blocks.copy().reshape(rows, -1)
+    bad[7, 0:2] = np.array([0x7BFF], dtype=np.uint16).view(np.uint8)
+    bad[7, 2] = 0x00                                  # code 0 -> n - 8 = -8
+    st, _, _ = kva.kva_debug_pack_weight(bad, "q4_0", rows, K, "q4_0")
+    assert st == kva.KVA_ERR_RANGE

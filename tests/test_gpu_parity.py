@@ -89,6 +89,20 @@ def test_tiny_ragged_blocks(tiny, n):
     proj.close()
 
 
+def _jitter_spread(cfg, w, x, base, trials=3, rel=1e-7):
+    """How far the emulator moves when its input moves by fp32-size noise:
+    the worst (max|diff|/rms, rms diff/rms) over `trials` relative jitters of
+    x by rel * N(0, 1)."""
+    rng = np.random.default_rng(1234)
+    mx, sd = 0.0, 0.0
+    for _ in range(trials):
+        xj = x.astype(np.float64) * (1.0 + rel * rng.standard_normal(x.shape))
+        e = _errs(emu.project(cfg, w, xj), base)
+        mx = max(mx, max(v[0] for v in e.values()))
+        sd = max(sd, max(v[1] for v in e.values()))
+    return mx, sd
+
+
 @pytest.mark.parametrize("scale", [1.0, 3.0])
 def test_tiny_long_block_peaked_scores(tiny, scale):
     """1024 tokens in one attention block (16 key tiles per query tile) with
@@ -98,15 +112,15 @@ def test_tiny_long_block_peaked_scores(tiny, scale):
     (with unscaled weights it runs only on the first tile).
 
     Bar at scale 1: the projector's (max|err| <= 2e-2 RMS against the
-    oracle).  At scale 3 the storage roundings of a 16-bit path alone move a
-    few tokens by about 0.19 RMS from the float64 result: the rounding-point
-    emulator (oracle/emu.py, every intermediate the kernels store rounded
-    to its format, float64 arithmetic otherwise) shows 0.195 max / 8.4e-3
-    RMS on these inputs, and no single rounding point accounts for it.  So
-    at scale 3 the max bar applies against the emulator (2e-2 RMS: what is
-    left is accumulation order and fp32 arithmetic, which a rescale that
-    dropped or misapplied its factor would exceed by far), and the RMS
-    error against the oracle stays <= 2e-2."""
+    oracle).  At scale 3 the block is numerically chaotic: the rounding-point
+    emulator (oracle/emu.py: every intermediate the kernels store rounded to
+    its format, float64 arithmetic otherwise) is 0.195 RMS away from the
+    oracle at most (the GPU: 0.190), and it moves by 0.03-0.04 RMS when its
+    input is jittered by 1e-7 relative, the size of fp32 arithmetic noise.
+    So at scale 3 the GPU is held to the emulator within 1.5x that measured
+    spread (max and RMS; a rescale that dropped or misapplied its factor
+    would move whole rows by O(1)), and to the oracle by the RMS error
+    (<= 2e-2)."""
     cfg, w = tiny
     cfg = dict(cfg, attn_block=1024)
     w = dict(w, blocks=[dict(b, wq=b["wq"] * np.float32(scale), wk=b["wk"] * np.float32(scale))
@@ -117,17 +131,19 @@ def test_tiny_long_block_peaked_scores(tiny, scale):
     proj.close()
     emulated = emu.project(cfg, w, x)
     ee = _errs(got, emulated)
-    print(f"tiny 1024 tokens, qk scale {scale}: vs emulator worst max|err|/rms {max(e[0] for e in ee.values()):.4e}",
-          flush=True)
+    gm, gs = max(e[0] for e in ee.values()), max(e[1] for e in ee.values())
+    print(f"tiny 1024 tokens, qk scale {scale}: vs emulator worst max|err|/rms {gm:.4e}, rms {gs:.4e}", flush=True)
     if scale == 1.0:
         _check(cfg, got, want, label="tiny 1024 tokens")
-    else:
-        errs = _errs(got, want)
-        print(f"tiny 1024 tokens, qk scale {scale}: vs oracle worst max|err|/rms "
-              f"{max(e[0] for e in errs.values()):.4e}; rms err/rms {max(e[1] for e in errs.values()):.4e}",
-              flush=True)
-        assert all(e[1] <= 2e-2 for e in errs.values()), errs
-    _check(cfg, got, emulated, label=f"tiny 1024 tokens vs emulator, scale {scale}")
+        _check(cfg, got, emulated, label="tiny 1024 tokens vs emulator")
+        return
+    errs = _errs(got, want)
+    print(f"tiny 1024 tokens, qk scale {scale}: vs oracle worst max|err|/rms "
+          f"{max(e[0] for e in errs.values()):.4e}; rms err/rms {max(e[1] for e in errs.values()):.4e}", flush=True)
+    assert all(e[1] <= 2e-2 for e in errs.values()), errs
+    sm, ss = _jitter_spread(cfg, w, x, emulated)
+    print(f"  emulator spread under 1e-7 input jitter: max {sm:.4e}, rms {ss:.4e}", flush=True)
+    assert gm <= max(TOL, 1.5 * sm) and gs <= 1.5 * ss, (gm, gs, sm, ss)
 
 
 def test_tiny_bad_arguments(tiny):
