@@ -215,6 +215,21 @@ kva_status kva_map_create(int32_t n_in, int32_t n_maps, int32_t weight_dtype, co
  * max_tokens.  Asynchronous on `stream`. */
 kva_status kva_map_project(kva_ctx* ctx, const float* x, int32_t n_tokens, float* const* out, void* stream);
 
+/* kva_map_project for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and the same results, bit for bit, but the residual's
+ * tiled 16-bit copy (round_up(n_tokens, 256) * n_in * 2 bytes) goes to a
+ * static device array of 16 MiB that the library holds on each device until
+ * the process ends, instead of the context's scratch.  The call allocates
+ * nothing (no hipMalloc, no events; kva_profile_* records nothing for it).
+ * Every call on one device shares that array: calls that overlap on one GPU
+ * (other streams, other threads, other contexts) race and must be ordered by
+ * the caller.  KVA_ERR_SHAPE if the copy would exceed 16 MiB (n_in = 5120:
+ * at most 1536 tokens) or n_tokens is outside [1, max_tokens]; otherwise
+ * errors as kva_map_project.  Asynchronous on `stream`. */
+kva_status kva_map_project_noalloc(kva_ctx* ctx, const float* x, int32_t n_tokens, float* const* out,
+                                   void* stream);
+
 /* Paged KV cache of one full-attention layer of the base model
  * ("Qwen3.8-27B-MLA" card, "What this is": 4 KV heads of 256 dims, 64 of
  * which are rotary).  Pools are device arrays laid out

@@ -99,6 +99,7 @@ _SIGS = {
     "kva_map_create": (c_i32, [c_i32, c_i32, c_i32, ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), c_i32, c_i32,
                                ctypes.POINTER(c_vp)]),
     "kva_map_project": (c_i32, [c_vp, c_vp, c_i32, ctypes.POINTER(c_vp), c_vp]),
+    "kva_map_project_noalloc": (c_i32, [c_vp, c_vp, c_i32, ctypes.POINTER(c_vp), c_vp]),
     "kva_deltanet_update": (c_i32, [ctypes.POINTER(kva_deltanet_layer), c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
     "kva_attn_kv_write": (c_i32, [c_vp, c_i64, c_i32, c_i64, c_vp, ctypes.POINTER(kva_paged_kv), c_vp]),
     "kva_debug_dequant_q8_0": (c_i32, [c_vp, c_i64, c_vp, c_vp]),
@@ -199,6 +200,11 @@ def kva_map_create(n_in: int, n_maps: int, weight_dtype: int, w_ptrs, b_ptrs, ma
 def kva_map_project(ctx: int, x_ptr: int, n_tokens: int, out_ptrs, stream: int = 0) -> None:
     arr = (c_vp * len(out_ptrs))(*out_ptrs)
     _check(lib().kva_map_project(ctx, x_ptr, n_tokens, arr, stream), "kva_map_project")
+
+
+def kva_map_project_noalloc(ctx: int, x_ptr: int, n_tokens: int, out_ptrs, stream: int = 0) -> None:
+    arr = (c_vp * len(out_ptrs))(*out_ptrs)
+    _check(lib().kva_map_project_noalloc(ctx, x_ptr, n_tokens, arr, stream), "kva_map_project_noalloc")
 
 
 class MapProjector:

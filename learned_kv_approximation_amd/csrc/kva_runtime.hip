@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -690,6 +691,77 @@ inline void clear_stale_error() { (void)hipGetLastError(); }
         }                                                                                 \
     } while (0)
 
+// ------------------------------------------------------------------ static scratch
+
+// Device memory of kva_map_project_noalloc: the tiled 16-bit copy of the
+// residual rows that feeds the maps' GEMM (round_up(n_tokens, 256) x n_in
+// values), for callers that cannot allocate.  One copy per device, held
+// until the process ends; every call on a device shares it.
+constexpr uint64_t kStaticScratchBytes = 16ull << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Resolves the device address of `scratch` on `device` (which must be
+// current) once; the host-side name of the array is not a device address.
+kva_status static_scratch_setup(int device) {
+    if (device < 0 || device >= kMaxDevices) return fail(KVA_ERR_UNSUPPORTED, "device index %d", device);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[device]) return KVA_OK;
+    void* p = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(KVA_ERR_HIP, "hipGetSymbolAddress gave NULL for the static scratch");
+    g_scratch_ptr[device] = p;
+    return KVA_OK;
+}
+
+void* static_scratch_ptr(int device) {
+    if (device < 0 || device >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    return g_scratch_ptr[device];
+}
+
+// The single-map projection with the residual's tiled copy at `a_buf`
+// (round_up(n, 256) x n_in 16-bit values).  `profile`: record the
+// kva_profile_* event pairs (kva_map_project_noalloc does not: creating an
+// event is a runtime allocation).
+kva_status map_project_impl(kva_ctx* ctx, const float* x, int32_t n, float* const* out, uint16_t* a_buf,
+                            bool profile, void* stream) {
+    const kva_config& c = ctx->cfg;
+    if (n < 1 || n > c.max_tokens) return fail(KVA_ERR_SHAPE, "n_tokens %d outside [1, %d]", n, c.max_tokens);
+    HeadOut ho{};
+    for (int i = 0; i < c.n_out_heads; ++i) {
+        if (!out[i]) return fail(KVA_ERR_ARG, "out[%d] is NULL", i);
+        ho.ptr[i] = out[i];
+        ho.ld[i] = c.n_in;
+    }
+    HIP_TRY(hipSetDevice(ctx->device));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint32_t saved_mask = ctx->prof_mask;
+    if (!profile) ctx->prof_mask = 0;
+    struct Restore {
+        kva_ctx* c;
+        uint32_t m;
+        ~Restore() { c->prof_mask = m; }
+    } restore{ctx, saved_mask};
+    STAGE(KVA_STAGE_NORM, launch_cast_tiled(x, c.n_in, n, c.n_in, a_buf, !ctx->q8, s));
+    GemmArgs g;
+    g.A = a_buf; g.lda = c.n_in; set_b(g, ctx->w_heads, c.n_in);
+    g.M = n; g.N = (int32_t)ctx->n_pad_heads; g.K = c.n_in;
+    g.epi.n_real = (int32_t)ctx->n_pad_heads;
+    g.epi.tile_head = ctx->tile_head; g.epi.tile_col0 = ctx->tile_col0;
+    g.epi.tail_head = ctx->tail_head; g.epi.tail_col = ctx->tail_col;
+    g.epi.tail_start = ctx->tail_start; g.epi.bias = ctx->b_heads;
+    g.epi.heads = ho;
+    const GemmOperand opd = ctx->q4 ? OPD_Q4 : ctx->q8 ? OPD_Q8 : OPD_BF16;
+    STAGE(KVA_STAGE_GEMM_HEADS, launch_gemm_heads(opd, g, ctx->n_cu, 0, s));
+    ctx->stats.calls += 1;
+    ctx->stats.tokens += (uint64_t)n;
+    return KVA_OK;
+}
+
 }  // namespace
 
 
@@ -931,6 +1003,7 @@ kva_status kva_map_create(int32_t n_in, int32_t n_maps, int32_t weight_dtype, co
             HIP_TRY(hipSetDevice(device));
             ctx->device = device;
             HIP_TRY(hipDeviceGetAttribute(&ctx->n_cu, hipDeviceAttributeMultiprocessorCount, device));
+            KVA_TRY(static_scratch_setup(device));
             ctx->q4 = weight_dtype == KVA_DTYPE_Q4_0;
             ctx->q8 = weight_dtype == KVA_DTYPE_Q8_0 || ctx->q4;
             const PackTarget head_t = ctx->q4 ? PACK_Q4 : ctx->q8 ? PACK_Q8 : PACK_BF16_T32;
@@ -959,30 +1032,23 @@ kva_status kva_map_project(kva_ctx* ctx, const float* x, int32_t n, float* const
     clear_stale_error();
     if (!ctx || !x || !out) return fail(KVA_ERR_ARG, "NULL argument");
     if (!ctx->map_only) return fail(KVA_ERR_UNSUPPORTED, "not a single-map context (see kva_map_create)");
-    const kva_config& c = ctx->cfg;
-    if (n < 1 || n > c.max_tokens) return fail(KVA_ERR_SHAPE, "n_tokens %d outside [1, %d]", n, c.max_tokens);
-    HeadOut ho{};
-    for (int i = 0; i < c.n_out_heads; ++i) {
-        if (!out[i]) return fail(KVA_ERR_ARG, "out[%d] is NULL", i);
-        ho.ptr[i] = out[i];
-        ho.ld[i] = c.n_in;
-    }
-    HIP_TRY(hipSetDevice(ctx->device));
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    STAGE(KVA_STAGE_NORM, launch_cast_tiled(x, c.n_in, n, c.n_in, ctx->z16, !ctx->q8, s));
-    GemmArgs g;
-    g.A = ctx->z16; g.lda = c.n_in; set_b(g, ctx->w_heads, c.n_in);
-    g.M = n; g.N = (int32_t)ctx->n_pad_heads; g.K = c.n_in;
-    g.epi.n_real = (int32_t)ctx->n_pad_heads;
-    g.epi.tile_head = ctx->tile_head; g.epi.tile_col0 = ctx->tile_col0;
-    g.epi.tail_head = ctx->tail_head; g.epi.tail_col = ctx->tail_col;
-    g.epi.tail_start = ctx->tail_start; g.epi.bias = ctx->b_heads;
-    g.epi.heads = ho;
-    const GemmOperand opd = ctx->q4 ? OPD_Q4 : ctx->q8 ? OPD_Q8 : OPD_BF16;
-    STAGE(KVA_STAGE_GEMM_HEADS, launch_gemm_heads(opd, g, ctx->n_cu, 0, s));
-    ctx->stats.calls += 1;
-    ctx->stats.tokens += (uint64_t)n;
-    return KVA_OK;
+    return map_project_impl(ctx, x, n, out, ctx->z16, true, stream);
+}
+
+kva_status kva_map_project_noalloc(kva_ctx* ctx, const float* x, int32_t n, float* const* out, void* stream) {
+    clear_stale_error();
+    if (!ctx || !x || !out) return fail(KVA_ERR_ARG, "NULL argument");
+    if (!ctx->map_only) return fail(KVA_ERR_UNSUPPORTED, "not a single-map context (see kva_map_create)");
+    if (n < 1 || n > ctx->cfg.max_tokens)
+        return fail(KVA_ERR_SHAPE, "n_tokens %d outside [1, %d]", n, ctx->cfg.max_tokens);
+    const uint64_t need = (uint64_t)round_up(n, kRowPad) * (uint64_t)ctx->cfg.n_in * 2u;
+    if (need > kStaticScratchBytes)
+        return fail(KVA_ERR_SHAPE, "n_tokens %d needs %llu bytes of the static scratch, which holds %llu", n,
+                    (unsigned long long)need, (unsigned long long)kStaticScratchBytes);
+    void* buf = static_scratch_ptr(ctx->device);
+    if (!buf) return fail(KVA_ERR_HIP, "the static scratch of device %d has no address (see kva_map_create)",
+                          ctx->device);
+    return map_project_impl(ctx, x, n, out, static_cast<uint16_t*>(buf), false, stream);
 }
 
 kva_status kva_destroy(kva_ctx* ctx) {
