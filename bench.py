@@ -487,6 +487,75 @@ def cpu_baseline(min_seconds: float = 10.0, max_reps: int = 8):
                                f"({decode:.1f} s per call)"}}
 
 
+def power_loop(seconds: float, interval: float = 0.5):
+    """Loops r2 projections (one 1024-token ubatch per call) for `seconds`
+    while a second thread samples `amd-smi metric -p -c --json` every
+    `interval` s; returns the socket power and clock samples."""
+    import subprocess
+    import threading
+
+    import torch
+
+    import learned_kv_approximation_amd as kva
+
+    cfg = synth.config("r2")
+    w = synth.make_weights(cfg)
+    proj = kva.Projector(cfg, w, max_tokens=1024)
+    del w
+    xd = torch.from_numpy(synth.make_input(cfg)).cuda()
+    outs = proj.alloc_outputs(1024)
+    for _ in range(5):
+        proj.project(xd, outs)
+    torch.cuda.synchronize()
+    kva.kva_profile_enable(proj.ctx, 1 << STAGE_HEADS)
+    kva.kva_profile_read(proj.ctx)
+    for _ in range(20):
+        proj.project(xd, outs)
+    heads = kva.kva_profile_read(proj.ctx)["gemm_heads"]
+    kva.kva_profile_enable(proj.ctx, 0)
+    samples, stop = [], [False]
+
+    def find(obj, key):
+        if isinstance(obj, dict):
+            for k, v in obj.items():
+                if k == key:
+                    yield v
+                yield from find(v, key)
+        elif isinstance(obj, list):
+            for v in obj:
+                yield from find(v, key)
+
+    def sampler():
+        while not stop[0]:
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True,
+                                   timeout=10)
+                d = json.loads(r.stdout)
+                pw = next((v.get("value") for v in find(d, "socket_power") if isinstance(v, dict)), None)
+                gfx = [v["clk"]["value"] for v in find(d, "gfx_0") if isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+                mem = [v["clk"]["value"] for v in find(d, "mem_0") if isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+                samples.append({"t": round(time.perf_counter() - t0, 2), "socket_power_w": pw,
+                                "gfx_mhz": gfx[0] if gfx else None, "mem_mhz": mem[0] if mem else None})
+            except Exception as ex:   # the tool is optional: report, do not fail the run
+                samples.append({"error": str(ex)[:200]})
+            time.sleep(interval)
+
+    t0 = time.perf_counter()
+    th = threading.Thread(target=sampler)
+    th.start()
+    calls = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(50):
+            proj.project(xd, outs)
+        torch.cuda.synchronize()
+        calls += 50
+    stop[0] = True
+    th.join()
+    proj.close()
+    return {"calls": calls, "seconds": round(time.perf_counter() - t0, 2),
+            "heads_gemm_ms": round(heads[1] / max(heads[0], 1), 4), "samples": samples}
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -508,6 +577,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="r2 and r3 one-ubatch lines only")
     ap.add_argument("--line", choices=["deltanet", "map", "kv_write", "kv_write_q8", "prompt_kv"],
                     help="run one extra line alone and print its JSON (for profiling runs)")
+    ap.add_argument("--power-loop", type=float, default=0.0, metavar="SECONDS",
+                    help="loop r2 projections for SECONDS while sampling socket power and clocks (amd-smi)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run 2 r2 projections and 2 plain 1 GiB device copies, print nothing (for rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -523,6 +594,9 @@ def main():
     kva.lib()   # fails loudly if libkva.so is missing
     if args.traffic_probe:
         traffic_probe()
+        return
+    if args.power_loop > 0:
+        print(json.dumps({"line": "power_loop", **power_loop(args.power_loop)}), flush=True)
         return
     if args.line:
         fn = {"deltanet": time_deltanet, "map": time_map, "kv_write": time_kv_write,

@@ -160,7 +160,7 @@ kva_status kva_validate_config(const kva_config* cfg);
 kva_status kva_create(const kva_config* cfg, const kva_weights* w, int device, kva_ctx** out);
 
 /* The hot path: projects n_tokens residual rows.
- *   x        device, [n_tokens][n_in] fp32 (layer-31 residuals)
+ *   x        device, [n_tokens][n_in] fp32 (layer-31 residuals), 16-byte aligned
  *   head_out host array of n_out_heads DEVICE pointers; head i receives
  *            [n_tokens][out_dim_i] fp32, row-major, columns in the head's
  *            segment order (qkv|a|b, k|v, or the drafter's 5120).
@@ -208,7 +208,8 @@ typedef enum {
 kva_status kva_map_create(int32_t n_in, int32_t n_maps, int32_t weight_dtype, const void* const* w,
                           const float* const* b, int32_t max_tokens, int device, kva_ctx** out);
 
-/* y_l = W_l x + b_l for the n_tokens rows of x (device fp32 [n_tokens][n_in]);
+/* y_l = W_l x + b_l for the n_tokens rows of x (device fp32 [n_tokens][n_in],
+ * 16-byte aligned; KVA_ERR_ARG otherwise);
  * out: host array of n_maps device pointers, map l writes fp32
  * [n_tokens][n_in].  fp32 accumulation over n_in in a fixed order, so a row's
  * results do not depend on the other rows of the call.  1 <= n_tokens <=

@@ -731,6 +731,7 @@ kva_status map_project_impl(kva_ctx* ctx, const float* x, int32_t n, float* cons
                             bool profile, void* stream) {
     const kva_config& c = ctx->cfg;
     if (n < 1 || n > c.max_tokens) return fail(KVA_ERR_SHAPE, "n_tokens %d outside [1, %d]", n, c.max_tokens);
+    if ((uintptr_t)x % 16) return fail(KVA_ERR_ARG, "x must be 16-byte aligned (rows are read 16 bytes at a time)");
     HeadOut ho{};
     for (int i = 0; i < c.n_out_heads; ++i) {
         if (!out[i]) return fail(KVA_ERR_ARG, "out[%d] is NULL", i);
@@ -850,6 +851,7 @@ kva_status project(kva_ctx* ctx, const float* x, int32_t n, float* const* head_o
     const kva_config& c = ctx->cfg;
     if (n < 1 || n > c.max_tokens)
         return fail(KVA_ERR_SHAPE, "n_tokens %d outside [1, %d]", n, c.max_tokens);
+    if ((uintptr_t)x % 16) return fail(KVA_ERR_ARG, "x must be 16-byte aligned (rows are read 16 bytes at a time)");
     HeadOut ho{};
     for (int i = 0; i < c.n_out_heads; ++i) {
         const bool fused = kv && kv->kv_slot[i] >= 0;

@@ -7,6 +7,8 @@ dequantisation hook, and determinism.  The KV-cache write must land within
 one bf16 ulp of the oracle's correctly rounded value plus the fp32
 rotation's absolute error (2^-20 of the rotary pair's norm); V bit-exact.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -154,6 +156,9 @@ def test_tiny_bad_arguments(tiny):
         proj.project(x, outs=proj.alloc_outputs(65))
     with pytest.raises(kva.KvaError):
         kva.kva_project_ubatch(proj.ctx, x.data_ptr(), 0, [o.data_ptr() for o in proj.alloc_outputs(1)])
+    with pytest.raises(kva.KvaError) as e:           # rows are read 16 bytes at a time
+        kva.kva_project_ubatch(proj.ctx, x.data_ptr() + 4, 1, [o.data_ptr() for o in proj.alloc_outputs(1)])
+    assert e.value.status == kva.KVA_ERR_ARG
     proj.close()
 
 
@@ -438,8 +443,8 @@ def test_kv_write_q8_0_hadamard_parity(integer):
 
 def test_r2_projection_chained_into_deltanet_update(r2):
     """The r2 projector's 24 DeltaNet heads feed kva_deltanet_update straight
-    from the head output buffers (rows of qkv | a | b); two sampled layers are
-    held to the oracle's update on the same fp32 rows (the DeltaNet bar of
+    from the head output buffers (rows of qkv | a | b); every layer is held to
+    the oracle's update on the same fp32 rows (the DeltaNet bar of
     test_gpu_deltanet.py)."""
     cfg, w, _ = r2
     x = synth.make_input(cfg, n_tokens=1024, seed=23)
@@ -456,9 +461,16 @@ def test_r2_projection_chained_into_deltanet_update(r2):
               for hi, d in zip(dn, dev)]
     kva.kva_deltanet_update(layers, 1024, stream=kva.current_stream())
     torch.cuda.synchronize()
-    for l in (0, 23):
-        rows = outs[dn[l]].cpu().numpy()
-        S_ref, c_ref = ref.deltanet_update(rows, conv_w[l], a_log[l], dt_bias[l], conv[l], S[l])
+    # the oracle's 24 sequential scans run in worker processes (spawned: the
+    # parent holds the GPU)
+    import concurrent.futures
+    import multiprocessing
+    rows_all = [outs[dn[l]].cpu().numpy() for l in range(len(dn))]
+    with concurrent.futures.ProcessPoolExecutor(max_workers=min(8, os.cpu_count() or 1),
+                                                mp_context=multiprocessing.get_context("spawn")) as ex:
+        refs = list(ex.map(ref.deltanet_update, rows_all, conv_w, a_log, dt_bias, conv, S))
+    for l in range(len(dn)):
+        S_ref, c_ref = refs[l]
         got = dev[l][4].cpu().numpy().astype(np.float64)
         rms = np.sqrt(np.mean(S_ref ** 2))
         mx = np.max(np.abs(got - S_ref)) / rms
