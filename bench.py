@@ -376,9 +376,10 @@ def linear_weight_params(cfg: dict) -> int:
 
 
 def q8_m_sweep(ms=(16, 32, 64, 128, 256, 512, 1024), steps: int = 10, warmup: int = 3):
-    """The r3 q8_0 projector at M tokens per call: each call reads every weight
-    once, so below M of a few hundred the path is bound by weight bandwidth
-    (reported as GB/s of q8_0 weight bytes, 34 per 32 weights)."""
+    """The r3 q8_0 projector at M tokens per call, each M in a context sized for
+    it: each call reads every weight once, so below M of a few hundred the
+    path is bound by weight bandwidth (reported as GB/s of q8_0 weight bytes,
+    34 per 32 weights, for the whole call and for the head GEMM alone)."""
     import torch
 
     import learned_kv_approximation_amd as kva
@@ -386,33 +387,43 @@ def q8_m_sweep(ms=(16, 32, 64, 128, 256, 512, 1024), steps: int = 10, warmup: in
     cfg = synth.config("r3_q8_0")
     w = synth.make_weights(cfg)
     x = synth.make_input(cfg, n_tokens=max(ms))
-    proj = kva.Projector(cfg, w, max_tokens=max(ms))
-    del w
     xd = torch.from_numpy(x).cuda()
-    outs = proj.alloc_outputs(max(ms))
     wbytes = linear_weight_params(cfg) * 34 // 32
+    head_bytes = sum(h["out_dim"] for h in cfg["heads"]) * cfg["d_model"] * 34 // 32
     res = {}
     for m in ms:
+        # a context sized for the call (max_tokens = M), as a caller that runs
+        # calls of this size would create
+        proj = kva.Projector(cfg, w, max_tokens=m)
+        outs = proj.alloc_outputs(m)
         xm = xd[:m].contiguous()
         for _ in range(warmup):
             proj.project(xm, outs)
         torch.cuda.synchronize()
+        kva.kva_profile_enable(proj.ctx, 1 << STAGE_HEADS)
+        kva.kva_profile_read(proj.ctx)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(steps):
             proj.project(xm, outs)
         e1.record()
         torch.cuda.synchronize()
+        hs = kva.kva_profile_read(proj.ctx)["gemm_heads"]
+        proj.close()
         t = e0.elapsed_time(e1) / steps
+        th = hs[1] / max(hs[0], 1)
         f = flops(cfg, m)["total"]
         res[str(m)] = {"ms": round(t, 4), "tokens_per_s": round(m / (t / 1e3), 1),
                        "pct_mfma_peak": round(100.0 * f / (t / 1e3) / (PEAK_TFLOPS * 1e12), 2),
                        "weight_gb_s": round(wbytes / (t / 1e3) / 1e9, 1),
-                       "frac_hbm": round(wbytes / (t / 1e3) / 1e9 / HBM_GBS, 4)}
-    proj.close()
+                       "frac_hbm": round(wbytes / (t / 1e3) / 1e9 / HBM_GBS, 4),
+                       "heads_gemm_ms": round(th, 4),
+                       "heads_weight_gb_s": round(head_bytes / (th / 1e3) / 1e9, 1),
+                       "heads_frac_hbm": round(head_bytes / (th / 1e3) / 1e9 / HBM_GBS, 4)}
+    del w
     del outs, xd
     torch.cuda.empty_cache()
-    return {"weight_bytes": wbytes, "by_tokens_per_call": res}
+    return {"weight_bytes": wbytes, "head_weight_bytes": head_bytes, "by_tokens_per_call": res}
 
 
 def traffic_probe():
@@ -634,7 +645,7 @@ def main():
             print(f"[bench] r3 65536 + KV: chained {kvp['chained']['tokens_per_s']:.0f} tok/s, "
                   f"fused {kvp['fused']['tokens_per_s']:.0f} tok/s", file=sys.stderr, flush=True)
             sweep = q8_m_sweep()
-            print("[bench] q8_0 M sweep: " + ", ".join(f"{m}: {v['weight_gb_s']} GB/s"
+            print("[bench] q8_0 M sweep: " + ", ".join(f"{m}: {v['weight_gb_s']} GB/s (heads {v['heads_weight_gb_s']})"
                                                         for m, v in sweep["by_tokens_per_call"].items()),
                   file=sys.stderr, flush=True)
     if not args.quick:

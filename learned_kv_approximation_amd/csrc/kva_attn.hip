@@ -257,18 +257,23 @@ __global__ void __launch_bounds__(128 * KS) attn_fwd(const uint16_t* __restrict_
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[st][r]);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        // The reference point m_i of l and O moves only when some query of
-        // the wave has a score more than kLazyShift above it (softmax is
-        // invariant to the shift, so this changes only roundings): the
-        // rescale of O then runs about once per wave instead of once per
-        // tile, and P = 2^(s - m_i) <= 2^kLazyShift stays far inside fp16.
-        // The first tile always sets m_i (it starts at -inf).  Exponents
+        // A query's reference point m_i of l and O moves only when one of
+        // its scores is more than kLazyShift above it (softmax is invariant
+        // to the shift, so this changes only roundings): the rescale of O
+        // then runs about once per wave instead of once per tile, and
+        // P = 2^(s - m_i) <= 2^kLazyShift stays far inside fp16.  The
+        // decision is per query; the wave runs the multiply when any of its
+        // queries moves, with the factor 1 (exact) for the others, so a
+        // query's result depends on its own scores alone and a block's
+        // first tokens come out bit for bit the same whatever follows them.
+        // The first unmasked tile sets m_i (it starts at -inf).  Exponents
         // below are then <= kLazyShift (and -inf for masked keys): the
         // hardware exp2 is exact enough, and flushing underflow to 0 is what
         // softmax wants.
-        if (__builtin_amdgcn_ballot_w64(mx > m_i + kLazyShift) != 0) {
-            const float alpha = __builtin_amdgcn_exp2f(m_i - mx);
-            m_i = mx;
+        const bool move = mx > m_i + kLazyShift;
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {
+            const float alpha = move ? __builtin_amdgcn_exp2f(m_i - mx) : 1.0f;
+            m_i = move ? mx : m_i;
             l_i *= alpha;
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt)

@@ -119,7 +119,7 @@ __global__ void __launch_bounds__(256) fold_rmsnorm(float* __restrict__ h, int64
 // partials) issued before the first one is used.  Rows of up to 4096
 // columns in at most 512 threads (at 1024 tokens the whole grid is then
 // resident at once).
-constexpr int kMaxFoldSplits = 4;
+constexpr int kMaxFoldSplits = 8;
 template <bool BF16, int V>
 __global__ void __launch_bounds__(1024) fold_rmsnorm_row(float* __restrict__ h, int64_t ldh, int add,
                                                          const float* __restrict__ partials, int32_t splits,

@@ -47,7 +47,11 @@ kva_status fail(kva_status s, const char* fmt, ...) {
 // most one 1024-token ubatch per call and the three ranges of its 256x128
 // tiles still fit one round over 256 CUs (d <= 2688); two otherwise (more
 // partials to fold cost more than they gain once the tiles fill the device).
+// Contexts of at most 128 tokens per call (one 128-row tile) read every
+// weight once per call and have few tiles: eight K-ranges, so that the
+// narrow GEMMs stream their weights from 8x as many workgroups.
 inline int split_narrow(int64_t d, int64_t max_tokens, bool f16_trunk) {
+    if (max_tokens <= 128) return 8;
     return (f16_trunk && max_tokens <= 1024 && d % 128 == 0 && 4 * (d / 128) * 3 <= 256) ? 3 : 2;
 }
 

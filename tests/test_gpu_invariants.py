@@ -9,6 +9,16 @@
   region (one shared allocation, heads back to back with gaps) survive, for
   full and ragged token counts, whole-head tiles and the tail tiles that
   gather the last out_dim % 256 columns of every head.
+- Causality inside a block: a block's first n tokens come out bit for bit
+  the same whatever the later tokens are (a call of n tokens against the
+  full block), also with peaked scores, where the softmax reference points
+  of the queries move between key tiles at different times.
+- Reach of a NaN: a NaN in the input of token j makes every output of the
+  tokens from j to the end of its block NaN and changes no bit of the other
+  blocks or of the tokens before j's 64-token query tile.  The earlier
+  tokens of that tile are not checked: the diagonal key tile multiplies
+  their zero softmax weights with V rows that include token j's, and
+  0 * NaN is NaN in the matrix cores.
 """
 import numpy as np
 import pytest
@@ -92,3 +102,47 @@ def test_head_outputs_stay_inside_their_regions(name, n):
     assert np.all(host[~inside] == SENTINEL), np.flatnonzero((host != SENTINEL) & ~inside)[:8]
     for i, (a, b) in enumerate(spans):
         assert not np.any(host[a:b] == SENTINEL), (i, int(np.sum(host[a:b] == SENTINEL)))
+
+
+def _peaked(cfg, w, scale):
+    return dict(w, blocks=[dict(b, wq=b["wq"] * np.float32(scale), wk=b["wk"] * np.float32(scale))
+                           for b in w["blocks"]])
+
+
+@pytest.mark.parametrize("scale", [1.0, 3.0])
+def test_block_prefix_does_not_depend_on_later_tokens(scale):
+    """One 1024-token attention block; with the Q and K weights scaled by 3
+    a query's running maximum jumps between key tiles, at different tiles
+    for different queries of one wave."""
+    cfg = dict(synth.config("tiny"), attn_block=1024)
+    w = _peaked(cfg, synth.make_weights(cfg), scale)
+    x = synth.make_input(cfg, n_tokens=1024, seed=34)
+    proj = kva.Projector(cfg, w, max_tokens=1024)
+    full = [o.cpu() for o in _run(proj, x)]
+    for n in (1, 5, 31, 32, 33, 47, 63, 64, 65, 100, 129, 511, 777, 1000, 1023):
+        part = _run(proj, np.ascontiguousarray(x[:n]))
+        for i, o in enumerate(part):
+            assert torch.equal(o.cpu(), full[i][:n]), (scale, n, i)
+    proj.close()
+
+
+@pytest.mark.parametrize("j", [0, 100, 300, 340, 511])
+def test_nan_reaches_only_later_tokens_of_its_block(j):
+    block = 256
+    cfg = dict(synth.config("tiny"), attn_block=block)
+    w = synth.make_weights(cfg)
+    x = synth.make_input(cfg, n_tokens=512, seed=35)
+    proj = kva.Projector(cfg, w, max_tokens=512)
+    clean = [o.cpu() for o in _run(proj, x)]
+    xn = x.copy()
+    xn[j, 7] = np.nan
+    dirty = [o.cpu() for o in _run(proj, xn)]
+    proj.close()
+    bs, be, ts = (j // block) * block, (j // block + 1) * block, (j // 64) * 64
+    for i, (a, b) in enumerate(zip(clean, dirty)):
+        assert torch.isfinite(a).all(), i
+        assert torch.isnan(b[j:be]).all(), (j, i)
+        assert torch.equal(a[:ts], b[:ts]), (j, i)
+        assert torch.equal(a[be:], b[be:]), (j, i)
+        assert torch.isfinite(b[:ts]).all() and torch.isfinite(b[be:]).all(), (j, i)
+    assert bs <= ts

@@ -208,6 +208,19 @@ def test_r2_partial_last_ubatch(r2):
     proj.close()
 
 
+@pytest.mark.parametrize("m", [16, 128])
+def test_r2_small_context_parity(r2, m):
+    """Contexts of at most 128 tokens per call split the GEMMs whose N is the
+    trunk width eight ways in K: all 32 heads against the oracle."""
+    cfg, w, prep = r2
+    x = synth.make_input(cfg, n_tokens=m, seed=23)
+    proj = kva.Projector(cfg, w, max_tokens=m)
+    got = _run(proj, x)
+    want = ref.project(cfg, prep, x)
+    _check(cfg, got, want, label=f"r2 context of {m} tokens")
+    proj.close()
+
+
 def test_r2_short_calls_bitwise_equal_to_full_ubatch(r2):
     """Calls of 64, 100 and 300 tokens run other GEMM tiles (64-, 128- and
     256-row head tiles, other trunk tiles) than a 1024-token call: the first

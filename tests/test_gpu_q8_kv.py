@@ -188,6 +188,25 @@ def test_r3_q4_0_ubatch_parity():
     proj.close()
 
 
+@pytest.mark.parametrize("m", [16, 128])
+def test_r3_q8_0_small_context_parity(m):
+    """A context of at most 128 tokens per call splits the GEMMs whose N is
+    the trunk width eight ways in K (the benchmark's per-M contexts)."""
+    cfg = synth.config("r3_q8_0")
+    w = synth.make_weights(cfg)
+    prep = ref.prepare(cfg, w)
+    x = synth.make_input(cfg, n_tokens=m, seed=24)
+    proj = kva.Projector(cfg, w, max_tokens=m)
+    outs = proj.project(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    heads = list(range(len(cfg["heads"])))
+    want = ref.project(cfg, prep, x, which=heads)
+    errs = {cfg["heads"][i]["name"]: _err(outs[i].cpu().numpy(), want[i]) for i in heads}
+    print(f"r3 q8_0 context of {m} tokens: max|err|/rms {max(errs.values()):.4e}", flush=True)
+    assert max(errs.values()) <= TOL_Q8
+    proj.close()
+
+
 @pytest.fixture(scope="module")
 def r3bf16():
     cfg = synth.config("r3_kv")
