@@ -375,6 +375,18 @@ kva_status kva_debug_dequant_q8_0_f16(const void* blocks, int64_t n_blocks, uint
  * Asynchronous on `stream`; errors as kva_debug_dequant_q8_0. */
 kva_status kva_debug_dequant_q4_0_f16(const void* blocks, int64_t n_blocks, uint16_t* out, void* stream);
 
+/* Test hook: the q8_0 block rule's scale and reciprocal as the KV-cache
+ * write forms them (d = amax / 127 and 1 / d by a multiply-add correction and
+ * a reciprocal Newton step instead of division; [KVA] "Other notes" for the
+ * Hadamard-rotated q8_0 cache, ggml's q8_0 rule for the block) against
+ * correctly rounded division, over all 2^32 binary32 patterns on the device.
+ * Adds to counts (device, 3 x uint64, the caller zeroes them): [0] patterns
+ * whose scale differs (-0 excluded), [1] patterns in [2^-126, 2^126) whose
+ * fast reciprocal differs, [2] patterns whose guarded reciprocal (0 for 0)
+ * differs; NaN matches any NaN.  Asynchronous on `stream` (a few ms);
+ * KVA_ERR_ARG for NULL counts. */
+kva_status kva_debug_check_q8_scale(unsigned long long* counts, void* stream);
+
 /* Measurement hook: a pure-MFMA loop with no memory traffic.  Launches
  * n_workgroups workgroups of 4 waves; each wave issues n_iter x 8 independent
  * bf16 v_mfma_f32_32x32x16 (32768 FLOP each), i.e.

@@ -106,6 +106,7 @@ _SIGS = {
     "kva_debug_dequant_q8_0_f16": (c_i32, [c_vp, c_i64, c_vp, c_vp]),
     "kva_debug_dequant_q4_0_f16": (c_i32, [c_vp, c_i64, c_vp, c_vp]),
     "kva_debug_mfma_loop": (c_i32, [c_i32, c_i32, c_vp, c_vp]),
+    "kva_debug_check_q8_scale": (c_i32, [c_vp, c_vp]),
     "kva_debug_copy_z": (c_i32, [c_vp, c_vp, c_i32, c_vp]),
     "kva_debug_poison_scratch": (c_i32, [c_vp, c_vp]),
     "kva_debug_head_plan": (c_i32, [ctypes.POINTER(kva_config), ctypes.POINTER(c_i32), c_vp, c_vp, c_i64]),
@@ -264,6 +265,10 @@ def kva_debug_mfma_loop(n_iter: int, n_workgroups: int, sink_ptr: int, stream: i
 
 def kva_debug_dequant_q4_0_f16(blocks_ptr: int, n_blocks: int, out_ptr: int, stream: int = 0) -> None:
     _check(lib().kva_debug_dequant_q4_0_f16(blocks_ptr, n_blocks, out_ptr, stream), "kva_debug_dequant_q4_0_f16")
+
+
+def kva_debug_check_q8_scale(counts_ptr: int, stream: int = 0) -> None:
+    _check(lib().kva_debug_check_q8_scale(counts_ptr, stream), "kva_debug_check_q8_scale")
 
 
 def kva_debug_dequant_q8_0_f16(blocks_ptr: int, n_blocks: int, out_ptr: int, stream: int = 0) -> None:

@@ -312,6 +312,7 @@ hipError_t launch_deltanet_update(const DnArgs& a, hipStream_t stream);
 
 hipError_t launch_dequant_q8_0(const void* blocks, int64_t n_blocks, float* out, hipStream_t stream);
 hipError_t launch_dequant_q8_0_f16(const void* blocks, int64_t n_blocks, uint16_t* out, hipStream_t stream);
+hipError_t launch_check_q8_scale(unsigned long long* counts, hipStream_t stream);
 hipError_t launch_dequant_q4_0_f16(const void* blocks, int64_t n_blocks, uint16_t* out, hipStream_t stream);
 
 // n_workgroups x 4 waves, each n_iter x 8 bf16 32x32x16 MFMAs; sink: 256 floats per workgroup.

@@ -245,6 +245,41 @@ __device__ __forceinline__ void kv_store_bf16(uint16_t* dst, float4 v) {
     *(ushort4*)dst = o;
 }
 
+// The q8_0 block rule's scale and its reciprocal from the block maximum
+// amax >= 0: d = amax / 127 and id = 1 / d (0 when d = 0), both the correctly
+// rounded binary32 results.  Without the division instruction sequence:
+//  - d: q0 = amax * RN(1/127), then one correction with the exact residual
+//    amax - 127 q0 (an fma), q0 + residual * RN(1/127) rounded once
+//    (Markstein's correction step); an infinite q0 passes through;
+//  - id, for 2^-126 <= d < 2^126 (d and 1/d normal): the hardware
+//    reciprocal y0, then one Newton step y0 + y0 (1 - d y0) with fma
+//    (Markstein's reciprocal iteration).
+// Both agree with correctly rounded division on every binary32 input they
+// are used for (d: every amax except -0; id: every d in that range);
+// kva_debug_check_q8_scale runs that comparison over all 2^32 patterns on
+// the device.  A wave in which some lane's d is outside the range (zero,
+// subnormal, infinite, NaN, or 2^126 and above, which d = amax / 127 never
+// reaches) takes the division instead, all lanes together.
+__device__ __forceinline__ float q8_scale_d(float amax) {
+#pragma clang fp contract(off)
+    const float q0 = amax * (1.0f / 127.0f);
+    const float d = __builtin_fmaf(__builtin_fmaf(-q0, 127.0f, amax), 1.0f / 127.0f, q0);
+    return __builtin_isinf(q0) ? q0 : d;
+}
+
+__device__ __forceinline__ bool q8_scale_fast_ok(float d) { return d >= 0x1p-126f && d < 0x1p126f; }
+
+__device__ __forceinline__ float q8_scale_inv_fast(float d) {
+    const float y0 = __builtin_amdgcn_rcpf(d);
+    return __builtin_fmaf(__builtin_fmaf(-d, y0, 1.0f), y0, y0);
+}
+
+// Must be called by all 64 lanes of a wave together.
+__device__ __forceinline__ float q8_scale_inv(float d) {
+    if (__builtin_amdgcn_ballot_w64(!q8_scale_fast_ok(d)) != 0) return d != 0.0f ? 1.0f / d : 0.0f;
+    return q8_scale_inv_fast(d);
+}
+
 // q8_0 (ggml's block: fp16 scale d, 32 int8 codes, value d * q) of the
 // wave's 256 values into one row of 8 blocks of 34 bytes.  Block b holds dims
 // 32b..32b+31, i.e. lanes 8b..8b+7.  The quantisation is decided in fp32 by
@@ -261,8 +296,8 @@ __device__ __forceinline__ void kv_store_q8_0(uint8_t* row, float4 y, int lane) 
     ab = max(ab, (uint32_t)lane_xor_bits<1>((int)ab));
     ab = max(ab, (uint32_t)lane_xor_bits<2>((int)ab));
     ab = max(ab, (uint32_t)lane_xor_bits<4>((int)ab));
-    const float d = __builtin_bit_cast(float, ab) / 127.0f;
-    const float id = d != 0.0f ? 1.0f / d : 0.0f;
+    const float d = q8_scale_d(__builtin_bit_cast(float, ab));
+    const float id = q8_scale_inv(d);
     const float yy[4] = {y.x, y.y, y.z, y.w};
     // round half away from zero as trunc(t + copysign(h, t)), h the largest
     // binary32 below 1/2: for |t| < 2^23 the sum rounds up to the next integer
@@ -288,13 +323,19 @@ __device__ __forceinline__ void kv_store_q8_0(uint8_t* row, float4 y, int lane) 
 
 // Stores one KV head's 256 values of one token (k after k_norm and RoPE, or
 // v) at row `row` of the pool: bf16, or Hadamard-rotated q8_0.
-__device__ __forceinline__ void kv_store_row(const KvPool& c, bool is_k, int64_t row, int lane, float4 x) {
+// Q8: the pool's format known at compile time.
+template <bool Q8>
+__device__ __forceinline__ void kv_store_row_as(const KvPool& c, bool is_k, int64_t row, int lane, float4 x) {
     void* pool = is_k ? c.k_pool : c.v_pool;
-    if (c.q8) {
+    if constexpr (Q8)
         kv_store_q8_0(static_cast<uint8_t*>(pool) + row * kKvQ8RowBytes, kv_hadamard256(x, lane), lane);
-    } else {
+    else
         kv_store_bf16(static_cast<uint16_t*>(pool) + row * kKvHeadDim + lane * 4, x);
-    }
+}
+
+__device__ __forceinline__ void kv_store_row(const KvPool& c, bool is_k, int64_t row, int lane, float4 x) {
+    if (c.q8) kv_store_row_as<true>(c, is_k, row, lane, x);
+    else kv_store_row_as<false>(c, is_k, row, lane, x);
 }
 
 }  // namespace kva

@@ -1145,6 +1145,13 @@ kva_status kva_debug_dequant_q8_0_f16(const void* blocks, int64_t n_blocks, uint
     return KVA_OK;
 }
 
+kva_status kva_debug_check_q8_scale(unsigned long long* counts, void* stream) {
+    clear_stale_error();
+    if (!counts) return fail(KVA_ERR_ARG, "NULL argument");
+    LAUNCH(launch_check_q8_scale(counts, static_cast<hipStream_t>(stream)));
+    return KVA_OK;
+}
+
 kva_status kva_debug_mfma_loop(int32_t n_iter, int32_t n_workgroups, float* sink, void* stream) {
     clear_stale_error();
     if (!sink) return fail(KVA_ERR_ARG, "NULL argument");

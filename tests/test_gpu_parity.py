@@ -412,6 +412,17 @@ def _q8_rows_check(got_rows, want, where):
     return float(np.mean(diff))
 
 
+def test_q8_scale_rule_is_correctly_rounded_division_for_every_binary32():
+    """The KV write forms the q8_0 block scale d = amax / 127 and its
+    reciprocal without the division sequence; the device routine it runs
+    must give the correctly rounded quotients on every input it is used for
+    (all 2^32 patterns; the guarded reciprocal everywhere)."""
+    counts = torch.zeros(3, dtype=torch.int64, device="cuda")
+    kva.kva_debug_check_q8_scale(counts.data_ptr(), kva.current_stream())
+    torch.cuda.synchronize()
+    assert counts.tolist() == [0, 0, 0]
+
+
 @pytest.mark.parametrize("integer", [True, False])
 def test_kv_write_q8_0_hadamard_parity(integer):
     """Hadamard-rotated q8_0 KV write.  Integer-valued inputs make V's rotation
