@@ -287,7 +287,9 @@ struct T32Shape {
     // the head epilogue stages whole 256-column tiles through LDS (128 KB at
     // a time for a 256-row tile)
     static constexpr bool LDS_EPI = EPI == EPI_HEADS && BN == kHeadTileN;
-    static constexpr int S = (LDS_EPI && BM == 256) ? (128 * 1024 + STAGE - 1) / STAGE : 4;
+    // 64-row tiles (calls of at most 64 rows) stream every weight once from
+    // few workgroups: a deeper ring keeps more slabs in flight
+    static constexpr int S = (LDS_EPI && BM == 256) ? (128 * 1024 + STAGE - 1) / STAGE : (BM == 64 && EPI != EPI_HEADS) ? 8 : 4;
     static constexpr int BYTES = S * STAGE;
 };
 
@@ -637,6 +639,15 @@ hipError_t launch_gemm_t32(GemmOperand opd, GemmTile tile, EpiKind epi, const Ge
     KVA_T32_CASE(OPD_Q4, TILE_128x128, EPI_PARTIAL, 128, 128, 1, 4)
     KVA_T32_CASE(OPD_Q4, TILE_128x128, EPI_QKV, 128, 128, 1, 4)
     KVA_T32_CASE(OPD_Q4, TILE_128x128, EPI_SWIGLU, 128, 128, 2, 2)
+    KVA_T32_CASE(OPD_F16, TILE_64xN, EPI_PARTIAL, 64, 64, 1, 2)
+    KVA_T32_CASE(OPD_F16, TILE_64xN, EPI_QKV, 64, 64, 1, 2)
+    KVA_T32_CASE(OPD_F16, TILE_64xN, EPI_SWIGLU, 64, 128, 1, 2)
+    KVA_T32_CASE(OPD_Q8, TILE_64xN, EPI_PARTIAL, 64, 64, 1, 2)
+    KVA_T32_CASE(OPD_Q8, TILE_64xN, EPI_QKV, 64, 64, 1, 2)
+    KVA_T32_CASE(OPD_Q8, TILE_64xN, EPI_SWIGLU, 64, 128, 1, 2)
+    KVA_T32_CASE(OPD_Q4, TILE_64xN, EPI_PARTIAL, 64, 64, 1, 2)
+    KVA_T32_CASE(OPD_Q4, TILE_64xN, EPI_QKV, 64, 64, 1, 2)
+    KVA_T32_CASE(OPD_Q4, TILE_64xN, EPI_SWIGLU, 64, 128, 1, 2)
     return hipErrorNotSupported;
 }
 #undef KVA_T32_CASE

@@ -651,6 +651,10 @@ kva_status create_impl(const kva_config* cfg, const kva_weights* w, int device, 
 // either alternative there).  Not when 256-row tiles pad more rows than
 // 128-row ones.
 GemmTile pick_tile_t32(int64_t M, int64_t N, int splits, bool wide_ok) {
+    // A call of at most 64 rows: 64-row tiles (no rows computed past the
+    // 64th) of 64 columns (128 for SwiGLU), so that a narrow call still
+    // spreads its weights over a hundred or more workgroups.
+    if (M <= 64 && N % 128 == 0) return TILE_64xN;
     const int64_t t128 = ((M + 127) / 128) * (N / 128) * splits;
     const int64_t t256 = ((M + 255) / 256) * (N / 256) * splits;
     const int64_t t21 = ((M + 255) / 256) * (N / 128) * splits;
