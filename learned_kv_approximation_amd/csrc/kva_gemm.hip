@@ -557,6 +557,156 @@ __global__ void __launch_bounds__(512) gemm_t32_heads(GemmArgs g, int n_big, int
     }
 }
 
+// Skinny GEMM: calls of at most 32 rows in contexts created for at most 32
+// tokens per call.  Such a call reads every weight once and does little
+// MFMA work per weight, so the tiled GEMM's LDS ring (a barrier per 32-wide
+// slab, every wave waiting on the slowest DMA) is the wrong shape for it.
+// Here the operands stream from global memory straight into the MFMA
+// fragments of each wave (P slabs in flight per wave in registers, no LDS,
+// no barrier in the K loop); the NWK waves of a workgroup share one block
+// of 32 * NB output columns and each takes one contiguous range of the K
+// slabs of the workgroup's split (blockIdx.y of g.splits, EPI_PARTIAL
+// only); at the end the waves' partial sums are added through LDS in a
+// fixed tree order (wave w + NWK/2 into w, halving) and wave 0 runs the
+// fused epilogue of the tiled GEMM on the 32 * MI rows.  The K order is
+// therefore not the tiled GEMM's; a context uses one kernel for all its
+// calls (chosen from max_tokens), so a row's bits never depend on the call.
+template <int MI, int NB, int NWK, int P, int OPD, int EPI>
+__global__ void __launch_bounds__(64 * NWK) gemm_skinny(GemmArgs g) {
+    constexpr bool QW = OPD == OPD_Q8 || OPD == OPD_Q4;
+    constexpr bool Q4 = OPD == OPD_Q4;
+    constexpr bool BF16 = OPD == OPD_BF16;
+    constexpr int NACC = MI * NB * 16;                    // accumulator floats per lane
+    __shared__ float red[NWK / 2][NACC][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tn = blockIdx.x, split = blockIdx.y;
+    const int64_t nk_all = g.K / 32;
+    const int64_t sb0 = split * nk_all / g.splits, nks = (split + 1) * nk_all / g.splits - sb0;
+    const int kb0 = (int)(sb0 + wave * nks / NWK), kb1 = (int)(sb0 + (wave + 1) * nks / NWK);
+    const int frow = lane & 31, fk = lane >> 5;
+    f32x16 acc[MI][NB];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    // per-lane element offsets of slab 0 (A rows 32 i + frow of the first
+    // 256-row group; weight rows n = tn * 32 NB + 32 j + frow), chunk 2 ks + fk
+    int64_t aoff[MI][2], boff[NB][2], soff[NB];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) aoff[i][ks] = tiled32_index(32 * i + frow, (2 * ks + fk) * 8, g.K);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        const int64_t n = (int64_t)tn * 32 * NB + 32 * j + frow;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int64_t k = (2 * ks + fk) * 8;
+            boff[j][ks] = Q4 ? q4_code_chunk(n, k, g.K) : OPD == OPD_Q8 ? q8_code_chunk(n, k, g.K)
+                                                                       : tiled32_index(n, k, g.K);
+        }
+        soff[j] = q8_scale_index(n, 0, g.K);
+    }
+    constexpr int64_t A_SLAB = (int64_t)kWeightTileRows * 32;                     // elements
+    constexpr int64_t B_SLAB = (int64_t)kWeightTileRows * (QW ? (Q4 ? 16 : 32) : 32);  // bytes (q) / elements
+    struct Buf {
+        u32x4 a[MI][2];
+        u32x4 b[NB][2];
+        u32x2 qc[NB][2];
+        uint16_t qs[NB];
+    };
+    Buf buf[P];
+    auto load = [&](Buf& f, int kt) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) f.a[i][ks] = *(const u32x4*)(g.A + aoff[i][ks] + kt * A_SLAB);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            if constexpr (QW) {
+                const uint8_t* q = reinterpret_cast<const uint8_t*>(g.Bq) + kt * B_SLAB;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    if constexpr (Q4) f.qc[j][ks] = u32x2{*(const uint32_t*)(q + boff[j][ks]), 0u};
+                    else f.qc[j][ks] = *(const u32x2*)(q + boff[j][ks]);
+                }
+                f.qs[j] = g.Bs[soff[j] + (int64_t)kt * kWeightTileRows];
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) f.b[j][ks] = *(const u32x4*)(g.B + boff[j][ks] + kt * B_SLAB);
+            }
+        }
+    };
+    auto compute = [&](Buf& f) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const u32x4 b = QW ? q_fragment<Q4>(f.qc[j][ks], f.qs[j]) : f.b[j][ks];
+#pragma unroll
+                for (int i = 0; i < MI; ++i) acc[i][j] = mfma32<BF16>(f.a[i][ks], b, acc[i][j]);
+            }
+        }
+    };
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+        if (kb0 + p < kb1) load(buf[p], kb0 + p);
+    for (int kt = kb0; kt < kb1; kt += P) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            if (kt + p < kb1) {                           // uniform over the wave
+                compute(buf[p]);
+                if (kt + p + P < kb1) load(buf[p], kt + p + P);
+            }
+        }
+    }
+    // tree sum of the waves' partials: (w + h) into w for h = NWK/2, NWK/4, .., 1
+#pragma unroll
+    for (int h = NWK / 2; h >= 1; h /= 2) {
+        if (wave >= h && wave < 2 * h) {
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) red[wave - h][(i * NB + j) * 16 + r][lane] = acc[i][j][r];
+        }
+        __syncthreads();
+        if (wave < h) {
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] += red[wave][(i * NB + j) * 16 + r][lane];
+        }
+        __syncthreads();
+    }
+    if (wave == 0) epilogue<32 * MI, 32 * NB, 1, 1, EPI, MI, NB, 0>(g, acc, 0, tn, split, nullptr);
+}
+
+// P: slabs in flight per wave (register buffers)
+template <int MI, int NB, int NWK, int P, int OPD, int EPI>
+hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
+    if (a.N % (32 * NB)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_skinny<MI, NB, NWK, P, OPD, EPI>), dim3(a.N / (32 * NB), a.splits), dim3(64 * NWK), 0, s,
+                       a);
+    return hipGetLastError();
+}
+
+template <int OPD>
+hipError_t launch_skinny_epi(EpiKind epi, const GemmArgs& a, hipStream_t s) {
+    // wave counts and depths measured best on r2 / r3 q8_0 16-token calls
+    if (epi == EPI_PARTIAL) return launch_skinny<1, 1, 8, 3, OPD, EPI_PARTIAL>(a, s);
+    if (a.splits != 1) return hipErrorInvalidValue;
+    if (epi == EPI_QKV) return launch_skinny<1, 1, 8, 3, OPD, EPI_QKV>(a, s);
+    if (epi == EPI_SWIGLU) return launch_skinny<1, 2, 4, 6, OPD, EPI_SWIGLU>(a, s);
+    return hipErrorNotSupported;
+}
+
 template <int BM, int BN, int WGM, int WGN, int OPD, int EPI>
 hipError_t launch_t32(const GemmArgs& a, hipStream_t s) {
     if (a.N % BN) return hipErrorInvalidValue;
@@ -610,6 +760,16 @@ hipError_t launch_gemm_heads(GemmOperand opd, const GemmArgs& a, int n_cu, int m
     else
         return hipErrorNotSupported;
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_skinny(GemmOperand opd, EpiKind epi, const GemmArgs& a, hipStream_t s) {
+    if (a.M <= 0) return hipSuccess;
+    if (a.M > 32 || a.K % 32 != 0 || a.K <= 0 || a.splits < 1 || a.splits > a.K / 32) return hipErrorInvalidValue;
+    if ((opd == OPD_Q8 || opd == OPD_Q4) ? (!a.Bq || !a.Bs) : !a.B) return hipErrorInvalidValue;
+    if (opd == OPD_F16) return launch_skinny_epi<OPD_F16>(epi, a, s);
+    if (opd == OPD_Q8) return launch_skinny_epi<OPD_Q8>(epi, a, s);
+    if (opd == OPD_Q4) return launch_skinny_epi<OPD_Q4>(epi, a, s);
+    return hipErrorNotSupported;
 }
 
 #define KVA_T32_CASE(OPD_, TILE_, EPI_, BM_, BN_, WGM_, WGN_) \

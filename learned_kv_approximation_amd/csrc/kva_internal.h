@@ -237,6 +237,10 @@ enum GemmTile : int { TILE_256x256 = 0, TILE_128x128 = 1, TILE_256x128 = 2, TILE
 // LDS stages; tiles 256x256 or 128x128.
 hipError_t launch_gemm_t32(GemmOperand opd, GemmTile tile, EpiKind epi, const GemmArgs& args,
                            hipStream_t stream);
+// The skinny GEMM for calls of at most 32 rows (contexts of at most 32
+// tokens per call use it for every trunk GEMM): K split over the waves of a
+// workgroup, no LDS ring; split-K across workgroups for EPI_PARTIAL only.
+hipError_t launch_gemm_skinny(GemmOperand opd, EpiKind epi, const GemmArgs& args, hipStream_t stream);
 
 // The head GEMM (EPI_HEADS, no split): 256x256 tiles over a whole number of
 // rounds of n_cu workgroups, the remaining columns in smaller tiles (128 rows);

@@ -39,6 +39,12 @@ kva_status fail(kva_status s, const char* fmt, ...) {
                         #expr, hipGetErrorString(e_), __FILE__, __LINE__);              \
     } while (0)
 
+// Contexts of at most this many tokens per call run every trunk GEMM on the
+// skinny kernel (K split over the waves of a workgroup; the N = d GEMMs
+// also over kSkinnySplits workgroups, folded like the tiled split-K).
+constexpr int kSkinnyTokens = 32;
+constexpr int kSkinnySplits = 4;   // split-K of their N = d GEMMs across workgroups
+
 // Split count of the GEMMs whose N is the trunk width (input, O, down): with
 // only d = 2560-3072 columns they fill too few workgroups at 1024 tokens.
 // Fixed per context (from d and max_tokens, never from a call's token count):
@@ -49,7 +55,8 @@ kva_status fail(kva_status s, const char* fmt, ...) {
 // partials to fold cost more than they gain once the tiles fill the device).
 // Contexts of at most 128 tokens per call (one 128-row tile) read every
 // weight once per call and have few tiles: eight K-ranges, so that the
-// narrow GEMMs stream their weights from 8x as many workgroups.
+// narrow GEMMs stream their weights from 8x as many workgroups (contexts of
+// at most kSkinnyTokens take kSkinnySplits on the skinny kernel).
 inline int split_narrow(int64_t d, int64_t max_tokens, bool f16_trunk) {
     if (max_tokens <= 128) return 8;
     return (f16_trunk && max_tokens <= 1024 && d % 128 == 0 && 4 * (d / 128) * 3 <= 256) ? 3 : 2;
@@ -266,6 +273,7 @@ struct kva_ctx {
     uint16_t* z16 = nullptr;    // [m][d]      final-normed trunk state: bf16 (fp16 for q8_0)
     float* ws = nullptr;        // [n_split][m][d] split-K partials of the N = d GEMMs
     int n_split = 2;            // split count of the N = d GEMMs (split_narrow)
+    bool skinny = false;        // every trunk GEMM on the skinny kernel (max_tokens <= kSkinnyTokens)
 
     kva_stats stats{};
 
@@ -622,7 +630,8 @@ kva_status create_impl(const kva_config* cfg, const kva_weights* w, int device, 
     HIP_TRY(ctx->alloc(&ctx->o16, (size_t)m * hd * 2, false));
     HIP_TRY(ctx->alloc(&ctx->act16, (size_t)m * F * 2, false));
     HIP_TRY(ctx->alloc(&ctx->z16, (size_t)m * d * 2, false));
-    ctx->n_split = split_narrow(d, c.max_tokens, !ctx->q8 && !ctx->q4);
+    ctx->skinny = c.max_tokens <= kSkinnyTokens;
+    ctx->n_split = ctx->skinny ? kSkinnySplits : split_narrow(d, c.max_tokens, !ctx->q8 && !ctx->q4);
     HIP_TRY(ctx->alloc(&ctx->ws, (size_t)ctx->n_split * m * d * 4, false));
     // Scratch rows past n_tokens feed MFMA rows whose results are dropped; zero
     // them once so they always hold finite values.
@@ -874,6 +883,7 @@ kva_status project(kva_ctx* ctx, const float* x, int32_t n, float* const* head_o
     // every GEMM activation operand is written in the tiled32 layout
     const GemmOperand opd = ctx->q4 ? OPD_Q4 : ctx->q8 ? OPD_Q8 : OPD_F16;
     auto gemm = [&](EpiKind epi, const GemmArgs& g) -> hipError_t {
+        if (ctx->skinny) return launch_gemm_skinny(opd, epi, g, s);
         return launch_gemm_t32(opd, pick_tile_t32(g.M, g.N, g.splits, opd == OPD_F16), epi, g, s);
     };
     const int64_t pstride = ctx->m_alloc * d;   // between split-K partial buffers

@@ -81,6 +81,26 @@ def test_tiny_trunk_state_matches_oracle(tiny):
     proj.close()
 
 
+@pytest.mark.parametrize("dtype", ["f32", "q8_0", "q4_0"])
+def test_tiny_skinny_context(dtype):
+    """A context of at most 32 tokens per call runs every trunk GEMM on the
+    skinny kernel (K split over the waves of a workgroup, the N = d GEMMs
+    also over 4 workgroups; half its waves get no K slab at the tiny
+    widths): oracle parity (the q8_0 / q4_0 bar for quantised weights) and
+    a call's rows bit for bit those of a longer call."""
+    cfg = synth.config("tiny", weight_dtype=dtype)
+    w = synth.make_weights(cfg)
+    proj = kva.Projector(cfg, w, max_tokens=32)
+    x = synth.make_input(cfg, n_tokens=32, seed=41)
+    full = _run(proj, x)
+    _check(cfg, full, oracle.project(cfg, w, x), tol=TOL if dtype == "f32" else 5e-2, label=f"tiny {dtype} skinny")
+    for n in (1, 17):
+        part = _run(proj, np.ascontiguousarray(x[:n]))
+        for i in range(len(part)):
+            assert np.array_equal(part[i], full[i][:n]), (dtype, n, i)
+    proj.close()
+
+
 @pytest.mark.parametrize("n", [1, 63, 65, 200])
 def test_tiny_ragged_blocks(tiny, n):
     cfg, w = tiny
