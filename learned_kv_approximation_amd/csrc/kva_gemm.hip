@@ -57,6 +57,19 @@ typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 // WGM x WGN grid of waves (acc[i][j]: the wave's i-th 32-row, j-th 32-column
 // block).  `smem` (SMEM_BYTES, free when called) is used by the head
 // epilogue to turn whole-head tiles into full-row stores.
+// A workgroup barrier for LDS hand-offs only: this wave's LDS accesses have
+// completed (lgkmcnt(0)) when it arrives, and there is no memory fence, so
+// the global stores already issued (the epilogue's output rows) keep
+// draining across it.  __syncthreads' release fence would wait for them
+// first, although no wave reads another wave's global writes here.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14));   // lgkmcnt(0); vmcnt, expcnt untouched
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    __asm__ volatile("" ::: "memory");
+}
+
 template <int BM, int BN, int WGM, int WGN, int EPI, int MI, int NI, int SMEM_BYTES>
 __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[MI][NI], int tm, int tn, int split,
                                          uint16_t* smem) {
@@ -179,16 +192,31 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[MI][NI
                                             acc[c * (CR / 32) + ii][j][r];
                                     }
                         }
-                        __syncthreads();
+                        lds_barrier();
                         // CR rows x 64 chunks of 4 columns; one wave takes one full row
                         const int row0 = tm * BM + half * WM + c * CR;
                         if (slot < 0) {
+                            // all of the wave's rows read first, then stored: each store
+                            // keeps its own source registers, so no store waits for the
+                            // previous one to have read its data (one register set
+                            // reused across the rows made every store wait for the one
+                            // before it to complete: 9.6 -> 7.8 us per 256x256 tile)
+                            float4 rv[CR / NW];
 #pragma unroll
                             for (int q = 0; q < CR / NW; ++q) {
                                 const int lr = q * NW + wave;
-                                float4 v = *(const float4*)(lds + lr * BN + ((c4 + 32 * ((lr >> 2) & 1)) & (BN - 1)));
-                                if (bias) { v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w; }
-                                if (row0 + lr < g.M) *(float4*)(dst0 + (int64_t)(row0 + lr) * ld + c4) = v;
+                                rv[q] = *(const float4*)(lds + lr * BN + ((c4 + 32 * ((lr >> 2) & 1)) & (BN - 1)));
+                            }
+                            if (bias) {
+#pragma unroll
+                                for (int q = 0; q < CR / NW; ++q) {
+                                    rv[q].x += b.x; rv[q].y += b.y; rv[q].z += b.z; rv[q].w += b.w;
+                                }
+                            }
+#pragma unroll
+                            for (int q = 0; q < CR / NW; ++q) {
+                                const int lr = q * NW + wave;
+                                if (row0 + lr < g.M) *(float4*)(dst0 + (int64_t)(row0 + lr) * ld + c4) = rv[q];
                             }
                         } else {
                             // the physical pages of this wave's rows, one per lane,
@@ -211,7 +239,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[MI][NI
                                 if (pg >= 0) kv_store_row(*pool, is_k, kv_row_index(*pool, pg, p, kvh), lane, v);
                             }
                         }
-                        __syncthreads();
+                        lds_barrier();
                     }
                 }
                 return;
