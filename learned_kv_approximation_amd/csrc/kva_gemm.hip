@@ -57,6 +57,9 @@ typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 // WGM x WGN grid of waves (acc[i][j]: the wave's i-th 32-row, j-th 32-column
 // block).  `smem` (SMEM_BYTES, free when called) is used by the head
 // epilogue to turn whole-head tiles into full-row stores.
+// Stores of rows past a call's M land here (one word per lane; never read).
+__device__ float g_discard[64];
+
 // A workgroup barrier for LDS hand-offs only: this wave's LDS accesses have
 // completed (lgkmcnt(0)) when it arrives, and there is no memory fence, so
 // the global stores already issued (the epilogue's output rows) keep
@@ -248,6 +251,18 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[MI][NI
         // a KV head's tiles leave only through the staged path above (the
         // launch keeps them 256 columns wide); never store them as fp32
         if (th >= 0 && e.kv_n > 0 && e.kv_slot[th] >= 0) return;
+        // The bias is added in place, so every store reads its own accumulator
+        // register (a sum in one reused temporary made each store wait for
+        // the previous one to complete).
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int col = col_base + j * 32;
+            const float b = e.bias ? e.bias[col] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] += b;
+        }
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
             const int col = col_base + j * 32;
@@ -263,13 +278,16 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[MI][NI
                 dst = e.heads.ptr[h] + e.tail_col[c];
                 ld = e.heads.ld[h];
             }
-            const float b = e.bias ? e.bias[col] : 0.0f;
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
+                    // rows past M go to a discard word instead of a branch per
+                    // store (a store under its own branch gets its sum formed
+                    // there, in one reused register, and waits for the last)
                     const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
-                    if (row < g.M) dst[(int64_t)row * ld] = acc[i][j][r] + b;
+                    float* p = row < g.M ? dst + (int64_t)row * ld : &g_discard[lane];
+                    *p = acc[i][j][r];
                 }
         }
     }
