@@ -378,8 +378,10 @@ def linear_weight_params(cfg: dict) -> int:
 def q8_m_sweep(ms=(16, 32, 64, 128, 256, 512, 1024), steps: int = 10, warmup: int = 3):
     """The r3 q8_0 projector at M tokens per call, each M in a context sized for
     it: each call reads every weight once, so below M of a few hundred the
-    path is bound by weight bandwidth (reported as GB/s of q8_0 weight bytes,
-    34 per 32 weights, for the whole call and for the head GEMM alone)."""
+    path is bound by weight bandwidth (reported as GB/s of the weight bytes a
+    call reads, for the whole call and for the head GEMM alone: q8_0's 34 per
+    32 weights, or 2 per weight where a context of more than 256 tokens per
+    call holds the weights expanded to fp16)."""
     import torch
 
     import learned_kv_approximation_amd as kva
@@ -388,10 +390,13 @@ def q8_m_sweep(ms=(16, 32, 64, 128, 256, 512, 1024), steps: int = 10, warmup: in
     w = synth.make_weights(cfg)
     x = synth.make_input(cfg, n_tokens=max(ms))
     xd = torch.from_numpy(x).cuda()
-    wbytes = linear_weight_params(cfg) * 34 // 32
-    head_bytes = sum(h["out_dim"] for h in cfg["heads"]) * cfg["d_model"] * 34 // 32
+    n_w = linear_weight_params(cfg)
+    n_head = sum(h["out_dim"] for h in cfg["heads"]) * cfg["d_model"]
     res = {}
     for m in ms:
+        expanded = m > 256
+        wbytes = n_w * 2 if expanded else n_w * 34 // 32
+        head_bytes = n_head * 2 if expanded else n_head * 34 // 32
         # a context sized for the call (max_tokens = M), as a caller that runs
         # calls of this size would create
         proj = kva.Projector(cfg, w, max_tokens=m)
@@ -413,7 +418,8 @@ def q8_m_sweep(ms=(16, 32, 64, 128, 256, 512, 1024), steps: int = 10, warmup: in
         t = e0.elapsed_time(e1) / steps
         th = hs[1] / max(hs[0], 1)
         f = flops(cfg, m)["total"]
-        res[str(m)] = {"ms": round(t, 4), "tokens_per_s": round(m / (t / 1e3), 1),
+        res[str(m)] = {"weights": "fp16" if expanded else "q8_0",
+                       "ms": round(t, 4), "tokens_per_s": round(m / (t / 1e3), 1),
                        "pct_mfma_peak": round(100.0 * f / (t / 1e3) / (PEAK_TFLOPS * 1e12), 2),
                        "weight_gb_s": round(wbytes / (t / 1e3) / 1e9, 1),
                        "frac_hbm": round(wbytes / (t / 1e3) / 1e9 / HBM_GBS, 4),
@@ -423,7 +429,8 @@ def q8_m_sweep(ms=(16, 32, 64, 128, 256, 512, 1024), steps: int = 10, warmup: in
     del w
     del outs, xd
     torch.cuda.empty_cache()
-    return {"weight_bytes": wbytes, "head_weight_bytes": head_bytes, "by_tokens_per_call": res}
+    return {"weight_bytes_q8_0": n_w * 34 // 32, "head_weight_bytes_q8_0": n_head * 34 // 32,
+            "by_tokens_per_call": res}
 
 
 def traffic_probe():

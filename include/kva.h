@@ -152,7 +152,13 @@ kva_status kva_validate_config(const kva_config* cfg);
  * the product uses is fp16(d*q), within 2^-12 relative of d*q (2^-25
  * absolute where d*q is below fp16's normal range), not d*q itself.  q4_0
  * weights likewise: a 4-bit code plane and an fp16 scale plane, weights
- * d*(n-8) rounded once to fp16 (kva_debug_dequant_q4_0_f16).  KVA_ERR_RANGE
+ * d*(n-8) rounded once to fp16 (kva_debug_dequant_q4_0_f16).  For
+ * cfg->max_tokens > 256 q8_0 / q4_0 weights are instead expanded at create
+ * into those same fp16 values, stored like fp16 weights (about twice the
+ * q8_0 bytes): at such call sizes the GEMMs are bound by MFMA issue, not by
+ * weight bytes, and the in-register conversion costs more than the extra
+ * reads.  Outputs are bit-identical to a code-plane context that splits K
+ * the same way.  KVA_ERR_RANGE
  * if a q8_0 / q4_0 block's scale is not finite or d*code rounds past fp16's
  * largest finite value (|d| * max|code| >= 65520).  The call is
  * synchronous.  On success *out owns all device memory it allocated; on
@@ -432,7 +438,9 @@ kva_status kva_debug_head_plan(const kva_config* cfg, int32_t* n_cols, int32_t* 
  * kva_create lays it out in device memory, rows padded with zero rows to a
  * multiple of 256.  target 0: fp16 values, 1: bf16 values (both in 32-wide K
  * slabs of 256 rows, 16-byte chunk c of row r at c ^ ((r >> 2) & 3)); 2: q8_0
- * code plane (out) and fp16 scale plane (scales); 3: q4_0 likewise.  out
+ * code plane (out) and fp16 scale plane (scales); 3: q4_0 likewise.  Target
+ * 0 also takes q8_0 / q4_0 blocks: each weight is expanded to fp16(d*code),
+ * the layout of a context with max_tokens > 256.  out
  * receives the values or codes (out_bytes capacity), scales the scales
  * (n_scales capacity; quantised targets only).  Errors as kva_create's
  * packing (KVA_ERR_DTYPE, _RANGE), KVA_ERR_SHAPE for short buffers. */

@@ -773,17 +773,19 @@ hipError_t launch_gemm_heads(GemmOperand opd, const GemmArgs& a, int n_cu, int m
     if (a.K % 32 != 0 || a.K <= 0 || a.N % 256 || a.splits != 1) return hipErrorInvalidValue;
     if ((opd == OPD_Q8 || opd == OPD_Q4) ? (!a.Bq || !a.Bs) : !a.B) return hipErrorInvalidValue;
     if (a.epi.kv_n > 0 && min_big * 256 > a.N) return hipErrorInvalidValue;
-    if (opd != OPD_BF16 && opd != OPD_Q8 && opd != OPD_Q4) return hipErrorNotSupported;
+    if (opd != OPD_BF16 && opd != OPD_F16 && opd != OPD_Q8 && opd != OPD_Q4) return hipErrorNotSupported;
     // Few rows: one M-tile of 64 or 128 rows, so that every weight strip is
     // read once by a workgroup whose MFMA work matches the real rows (with
     // 256-row tiles a short call would run a 256-row product on padding).
     if (a.M <= 64) {
         if (opd == OPD_BF16) return launch_t32<64, 256, 1, 4, OPD_BF16, EPI_HEADS>(a, s);
+        if (opd == OPD_F16) return launch_t32<64, 256, 1, 4, OPD_F16, EPI_HEADS>(a, s);
         if (opd == OPD_Q4) return launch_t32<64, 256, 1, 4, OPD_Q4, EPI_HEADS>(a, s);
         return launch_t32<64, 256, 1, 4, OPD_Q8, EPI_HEADS>(a, s);
     }
     if (a.M <= 128) {
         if (opd == OPD_BF16) return launch_t32<128, 256, 2, 4, OPD_BF16, EPI_HEADS>(a, s);
+        if (opd == OPD_F16) return launch_t32<128, 256, 2, 4, OPD_F16, EPI_HEADS>(a, s);
         if (opd == OPD_Q4) return launch_t32<128, 256, 2, 4, OPD_Q4, EPI_HEADS>(a, s);
         return launch_t32<128, 256, 2, 4, OPD_Q8, EPI_HEADS>(a, s);
     }
@@ -795,10 +797,13 @@ hipError_t launch_gemm_heads(GemmOperand opd, const GemmArgs& a, int n_cu, int m
     if (n_big < min_big) n_big = min_big < nt ? min_big : nt;
     const int grid_big = (mt * n_big + 7) / 8 * 8;
     const int sbn = opd == OPD_Q8 ? kTailBN<OPD_Q8> : opd == OPD_Q4 ? kTailBN<OPD_Q4> : kTailBN<OPD_BF16>;
+    static_assert(kTailBN<OPD_F16> == kTailBN<OPD_BF16>, "16-bit tail tiles");
     const int n_small = ((a.M + 127) / 128) * ((a.N - 256 * n_big) / sbn);
     const int grid = grid_big + (n_small + 7) / 8 * 8;
     if (opd == OPD_BF16)
         hipLaunchKernelGGL(gemm_t32_heads<OPD_BF16>, dim3(grid), dim3(512), 0, s, a, n_big, grid_big);
+    else if (opd == OPD_F16)
+        hipLaunchKernelGGL(gemm_t32_heads<OPD_F16>, dim3(grid), dim3(512), 0, s, a, n_big, grid_big);
     else if (opd == OPD_Q8)
         hipLaunchKernelGGL(gemm_t32_heads<OPD_Q8>, dim3(grid), dim3(512), 0, s, a, n_big, grid_big);
     else if (opd == OPD_Q4)

@@ -45,6 +45,14 @@ kva_status fail(kva_status s, const char* fmt, ...) {
 constexpr int kSkinnyTokens = 32;
 constexpr int kSkinnySplits = 4;   // split-K of their N = d GEMMs across workgroups
 
+// Contexts of more than this many tokens per call hold q8_0 / q4_0 weights
+// expanded to fp16 (the values the in-register dequantisation forms, so the
+// same bits): at those sizes the GEMMs are bound by MFMA issue and power,
+// not by weight bytes, and the conversion's VALU work cost 14-19% of the
+// head GEMM; smaller contexts keep the code and scale planes (half the
+// bytes) for their weight-bandwidth-bound calls.
+constexpr int kExpandTokens = 256;
+
 // Split count of the GEMMs whose N is the trunk width (input, O, down): with
 // only d = 2560-3072 columns they fill too few workgroups at 1024 tokens.
 // Fixed per context (from d and max_tokens, never from a call's token count):
@@ -237,6 +245,10 @@ struct kva_ctx {
     };
     bool q8 = false;               // block-quantised weights (q8_0 or q4_0): fp16 activations
     bool q4 = false;               // ... and they are q4_0
+    // GEMM operands: fp16 trunk / bf16 heads for fp32 and bf16 weights;
+    // the code and scale planes for q8_0 / q4_0, or, in contexts of more than
+    // kExpandTokens tokens per call, those weights expanded to fp16 at create
+    GemmOperand trunk_opd = OPD_F16, head_opd = OPD_BF16;
     DevW w_in;
     float* g_in = nullptr;
     float* g_out = nullptr;
@@ -459,15 +471,39 @@ kva_status pack_host(int dtype, int64_t K, const std::vector<RowSrc>& rows, Pack
         }
         return KVA_OK;
     }
-    if (dtype != KVA_DTYPE_F32 && dtype != KVA_DTYPE_BF16)
-        return fail(KVA_ERR_DTYPE, "16-bit layout needs fp32 or bf16 weights (%s)", name);
+    const bool quant = dtype == KVA_DTYPE_Q8_0 || dtype == KVA_DTYPE_Q4_0;
+    if (dtype != KVA_DTYPE_F32 && dtype != KVA_DTYPE_BF16 && !(quant && target == PACK_F16_T32))
+        return fail(KVA_ERR_DTYPE, "16-bit layout needs fp32 or bf16 weights, or q8_0 / q4_0 for fp16 (%s)", name);
     std::vector<uint16_t> w((size_t)(n * K), 0);
     bool ovf = false;
     for (int64_t r = 0; r < n; ++r) {
         if (!rows[r].src) continue;
         uint16_t* dst = &w[(size_t)(r * K)];
         const int64_t base = rows[r].row * K;
-        if (target == PACK_BF16_T32 && dtype == KVA_DTYPE_BF16) {
+        if (quant) {
+            // q8_0 / q4_0 blocks expanded to the fp16 weights the in-register
+            // dequantisation forms: d * code is exact in fp32 (11 x 8 bits),
+            // rounded once to fp16, so the GEMM multiplies the same values
+            const bool is4 = dtype == KVA_DTYPE_Q4_0;
+            const int bb = is4 ? 18 : 34;
+            const uint8_t* blk = static_cast<const uint8_t*>(rows[r].src) + rows[r].row * (K / 32) * bb;
+            for (int64_t b = 0; b < K / 32; ++b) {
+                const uint8_t* p = blk + b * bb;
+                const uint16_t d_bits = (uint16_t)(p[0] | (p[1] << 8));
+                int mx = 0;
+                int code[32];
+                for (int j = 0; j < 32; ++j) {
+                    code[j] = is4 ? (j < 16 ? (p[2 + j] & 0xF) : (p[2 + j - 16] >> 4)) - 8 : (int)(int8_t)p[2 + j];
+                    mx = std::max(mx, std::abs(code[j]));
+                }
+                if (quant_block_out_of_range(d_bits, mx))
+                    return fail(KVA_ERR_RANGE, "weight %s: %s block (row %lld, block %lld) has a scale whose "
+                                "weights are not finite in fp16", name, is4 ? "q4_0" : "q8_0",
+                                (long long)rows[r].row, (long long)b);
+                const float d = f16_bits_to_f32(d_bits);
+                for (int j = 0; j < 32; ++j) dst[b * 32 + j] = f32_to_f16(d * (float)code[j], &ovf);
+            }
+        } else if (target == PACK_BF16_T32 && dtype == KVA_DTYPE_BF16) {
             std::memcpy(dst, static_cast<const uint16_t*>(rows[r].src) + base, (size_t)K * 2);
         } else if (target == PACK_BF16_T32) {
             for (int64_t k = 0; k < K; ++k) dst[k] = f32_to_bf16(static_cast<const float*>(rows[r].src)[base + k]);
@@ -566,8 +602,11 @@ kva_status create_impl(const kva_config* cfg, const kva_weights* w, int device, 
     HIP_TRY(hipDeviceGetAttribute(&ctx->n_cu, hipDeviceAttributeMultiprocessorCount, device));
     ctx->q8 = q8;
     ctx->q4 = q4;
-    const PackTarget trunk_t = q4 ? PACK_Q4 : q8 ? PACK_Q8 : PACK_F16_T32;
-    const PackTarget head_t = q4 ? PACK_Q4 : q8 ? PACK_Q8 : PACK_BF16_T32;
+    const bool expand = q8 && c.max_tokens > kExpandTokens;
+    const PackTarget trunk_t = expand ? PACK_F16_T32 : q4 ? PACK_Q4 : q8 ? PACK_Q8 : PACK_F16_T32;
+    const PackTarget head_t = expand ? PACK_F16_T32 : q4 ? PACK_Q4 : q8 ? PACK_Q8 : PACK_BF16_T32;
+    ctx->trunk_opd = expand ? OPD_F16 : q4 ? OPD_Q4 : q8 ? OPD_Q8 : OPD_F16;
+    ctx->head_opd = expand ? OPD_F16 : q4 ? OPD_Q4 : q8 ? OPD_Q8 : OPD_BF16;
 
     auto putf = [&](float** dstp, const float* src, int64_t n, const char* name) -> kva_status {
         if (!src) return fail(KVA_ERR_ARG, "gain %s is NULL", name);
@@ -631,7 +670,7 @@ kva_status create_impl(const kva_config* cfg, const kva_weights* w, int device, 
     HIP_TRY(ctx->alloc(&ctx->act16, (size_t)m * F * 2, false));
     HIP_TRY(ctx->alloc(&ctx->z16, (size_t)m * d * 2, false));
     ctx->skinny = c.max_tokens <= kSkinnyTokens;
-    ctx->n_split = ctx->skinny ? kSkinnySplits : split_narrow(d, c.max_tokens, !ctx->q8 && !ctx->q4);
+    ctx->n_split = ctx->skinny ? kSkinnySplits : split_narrow(d, c.max_tokens, ctx->trunk_opd == OPD_F16);
     HIP_TRY(ctx->alloc(&ctx->ws, (size_t)ctx->n_split * m * d * 4, false));
     // Scratch rows past n_tokens feed MFMA rows whose results are dropped; zero
     // them once so they always hold finite values.
@@ -881,7 +920,7 @@ kva_status project(kva_ctx* ctx, const float* x, int32_t n, float* const* head_o
     const int64_t d = c.d_model, F = c.d_ffn, n_in = c.n_in;
     const int64_t hd = (int64_t)c.n_heads * c.head_dim;
     // every GEMM activation operand is written in the tiled32 layout
-    const GemmOperand opd = ctx->q4 ? OPD_Q4 : ctx->q8 ? OPD_Q8 : OPD_F16;
+    const GemmOperand opd = ctx->trunk_opd;
     auto gemm = [&](EpiKind epi, const GemmArgs& g) -> hipError_t {
         if (ctx->skinny) return launch_gemm_skinny(opd, epi, g, s);
         return launch_gemm_t32(opd, pick_tile_t32(g.M, g.N, g.splits, opd == OPD_F16), epi, g, s);
@@ -951,7 +990,7 @@ kva_status project(kva_ctx* ctx, const float* x, int32_t n, float* const* head_o
             std::memcpy(g.epi.kv_pool, kv->kv_pool, sizeof(g.epi.kv_pool));
             g.epi.kv_rope = kv->kv_rope;
         }
-        STAGE(KVA_STAGE_GEMM_HEADS, launch_gemm_heads(ctx->q8 ? opd : OPD_BF16, g, ctx->n_cu,
+        STAGE(KVA_STAGE_GEMM_HEADS, launch_gemm_heads(ctx->head_opd, g, ctx->n_cu,
                                                       kv ? ctx->kv_tiles : 0, s));
     }
     ctx->stats.calls += 1;

@@ -8,6 +8,7 @@ import pytest
 
 import learned_kv_approximation_amd as kva
 import synth
+from oracle import ref
 
 
 def test_library_exports_every_declared_function():
@@ -239,3 +240,34 @@ def test_pack_weight_q4_0_planes_and_range():
     bad[7, 2] = 0x00                                  # code 0 -> n - 8 = -8
     st, _, _ = kva.kva_debug_pack_weight(bad, "q4_0", rows, K, "q4_0")
     assert st == kva.KVA_ERR_RANGE
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
+def test_pack_weight_quantised_expanded_to_fp16(fmt):
+    """Contexts of more than 256 tokens per call hold q8_0 / q4_0 weights
+    expanded to fp16 at create: every value must be the oracle's fp16(d * code)
+    (the weight the in-register dequantisation forms), in the 16-bit layout,
+    including subnormal and zero scales, q = -128 and padding rows."""
+    rng = np.random.default_rng(64)
+    rows, K = 300, 96
+    nb = K // 32
+    sc = (np.abs(rng.standard_normal((rows, nb))) * 1e-3).astype(np.float16)
+    sc[3, 0] = np.float16(3e-7)                       # subnormal scale
+    sc[4, 1] = np.float16(0.0)
+    sc[5, 2] = np.float16(-0.02)
+    if fmt == "q8_0":
+        codes = rng.integers(-128, 128, size=(rows, K), dtype=np.int8)
+        codes[6, :32] = -128
+        blocks = synth.pack_q8_0(codes, sc)
+        want16 = ref.dequant_q8_0_f16_bits(blocks, rows, K)
+    else:
+        n = rng.integers(0, 16, size=(rows, K)).astype(np.uint8)
+        blocks = synth.pack_q4_0(n, sc)
+        want16 = ref.dequant_q4_0_f16_bits(blocks, rows, K)
+    st, out, _ = kva.kva_debug_pack_weight(blocks, fmt, rows, K, "f16")
+    assert st == kva.KVA_OK
+    got = out.view(np.uint16)
+    r, k = np.meshgrid(np.arange(512), np.arange(K), indexing="ij")
+    bits = np.zeros((512, K), dtype=np.uint16)
+    bits[:rows] = np.asarray(want16, dtype=np.uint16).reshape(rows, K)
+    assert np.array_equal(got[_t32_index(r, k, K)], bits)

@@ -188,6 +188,30 @@ def test_r3_q4_0_ubatch_parity():
     proj.close()
 
 
+@pytest.mark.parametrize("cfg_name", ["r3_q8_0", "r3_q4_0"])
+def test_expanded_fp16_weights_give_the_in_register_bits(cfg_name):
+    """A context of more than 256 tokens per call holds the q8_0 / q4_0
+    weights expanded to fp16 at create (twice the weight bytes); one of at
+    most 256 keeps the code and scale planes and dequantises in registers.
+    Both multiply the same fp16 weights in the same K order (here both split
+    the d-wide GEMMs two ways: max_tokens 2048 and 256), so a call's outputs
+    must be bitwise equal."""
+    cfg = synth.config(cfg_name)
+    w = synth.make_weights(cfg)
+    x = synth.make_input(cfg, n_tokens=200, seed=25)
+    outs, wbytes = [], []
+    for max_tokens in (2048, 256):
+        proj = kva.Projector(cfg, w, max_tokens=max_tokens)
+        outs.append([o.cpu() for o in proj.project(torch.from_numpy(x).cuda())])
+        torch.cuda.synchronize()
+        wbytes.append(kva.kva_get_stats(proj.ctx)["weight_bytes"])
+        proj.close()
+    print(f"{cfg_name}: weight bytes expanded {wbytes[0]}, planes {wbytes[1]}", flush=True)
+    assert wbytes[0] > 1.8 * wbytes[1]
+    for i, (a, b) in enumerate(zip(*outs)):
+        assert torch.equal(a, b), (cfg_name, cfg["heads"][i]["name"])
+
+
 @pytest.mark.parametrize("m", [16, 128])
 def test_r3_q8_0_small_context_parity(m):
     """A context of at most 128 tokens per call splits the GEMMs whose N is
