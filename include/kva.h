@@ -52,7 +52,7 @@ typedef enum {
     KVA_ERR_DTYPE = 3,        /* unsupported storage type                    */
     KVA_ERR_OOM = 4,          /* device or host allocation failed            */
     KVA_ERR_RANGE = 5,        /* a weight does not fit the compute type      */
-    KVA_ERR_UNSUPPORTED = 6,  /* valid request this build does not implement */
+    KVA_ERR_UNSUPPORTED = 6,  /* valid request the library does not implement */
     KVA_ERR_HIP = 7           /* a HIP runtime call or kernel launch failed  */
 } kva_status;
 
