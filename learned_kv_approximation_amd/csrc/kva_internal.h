@@ -122,7 +122,15 @@ enum EpiKind : int {
     EPI_QKV = 2,        // n < n_split: out16[m][n] = fp16(acc); else vt[n - n_split][m] = fp16(acc)
     EPI_SWIGLU = 3,     // gate/up interleaved per 32 columns: out16[tiled32_index(m, f, ld16)] = fp16(silu(g) * u)
     EPI_HEADS = 4,      // bias add, scatter to per-head fp32 outputs
-    EPI_PARTIAL = 5     // split-K partial: out_f32[split * split_stride + m * ld_f32 + n] = acc
+    EPI_PARTIAL = 5,    // split-K partial: out_f32[split * split_stride + m * ld_f32 + n] = acc
+    // The input Linear with its RMSNorm folded in: A is read as fp32 rows
+    // (A = x, lda in floats, 16-byte aligned) and each operand value is
+    // formed in the kernel as fp16(x[m][k] * a_gain[k]); the output is the
+    // split-K partial of EPI_PARTIAL (unnormalised), and the workgroups of
+    // the first N-tile also write each row's sum of squares of x over the
+    // split's K range to ss[split * ss_stride + m].  The row's 1/RMS is then
+    // applied to the summed partials by the fold (launch_fold_rmsnorm).
+    EPI_INPUT = 6
 };
 
 struct EpiArgs {
@@ -150,6 +158,10 @@ struct EpiArgs {
     int8_t kv_slot[kMaxHeads];
     KvPool kv_pool[kMaxAttnHeads];
     KvRope kv_rope;
+    // EPI_INPUT: the input norm's gain [K] and the per-split row sums of squares
+    const float* a_gain = nullptr;
+    float* ss = nullptr;
+    int64_t ss_stride = 0;
 };
 
 // C[M][N] = A[M][K] * B[N][K]^T with 16-bit activations (tiled32 layout)
@@ -254,9 +266,15 @@ hipError_t launch_gemm_heads(GemmOperand opd, const GemmArgs& args, int n_cu, in
 //   out[r][c] = 16-bit(h[r][c] / sqrt(mean_c h[r][c]^2 + eps) * g[c]).
 // P_s = partials + s * pstride, rows of ldp.  out is in the tiled32_index
 // layout (K = cols; cols % 32 == 0).
+// With ss (the partials of an EPI_INPUT GEMM; add is then false), the sum
+// is then scaled by the input row's 1/RMS:
+//   h[r][c] = (P_0[r][c] + P_1[r][c] + ...) * rin[r],
+//   rin[r] = 1 / sqrt((ss_0[r] + ss_1[r] + ...) / ss_cols + eps),
+// ss_s = ss + s * ss_stride (one value per row, `splits` of them).
 hipError_t launch_fold_rmsnorm(float* h, int64_t ldh, bool add, const float* partials, int32_t splits,
                                int64_t pstride, int64_t ldp, const float* g, int32_t rows, int32_t cols,
-                               float eps, uint16_t* out, bool bf16, hipStream_t stream);
+                               float eps, uint16_t* out, bool bf16, hipStream_t stream,
+                               const float* ss = nullptr, int64_t ss_stride = 0, int32_t ss_cols = 0);
 
 // out[tiled32_index(r, c, cols)] = 16-bit(x[r][c]) (fp16 or bf16, nearest
 // even); cols % 32 == 0.

@@ -71,6 +71,15 @@ __global__ void __launch_bounds__(256) cast_tiled(const float* __restrict__ x, i
     }
 }
 
+// 1/RMS of an input row from the per-split sums of squares an EPI_INPUT
+// GEMM wrote (added in split order).
+__device__ __forceinline__ float input_rinv(const float* ss, int64_t ss_stride, int splits, int row, int cols,
+                                            float eps) {
+    float tot = 0.0f;
+    for (int sp = 0; sp < splits; ++sp) tot += ss[sp * ss_stride + row];
+    return 1.0f / sqrtf(tot / (float)cols + eps);
+}
+
 // Split-K fold + RMSNorm: the residual update that follows a split GEMM,
 // fused with the norm that reads the updated residual.  The partials are
 // added in a fixed order, so the result is deterministic and independent of
@@ -81,11 +90,13 @@ __global__ void __launch_bounds__(256) fold_rmsnorm(float* __restrict__ h, int64
                                                     const float* __restrict__ partials, int32_t splits,
                                                     int64_t pstride, int64_t ldp,
                                                     const float* __restrict__ gain, int32_t cols, float eps,
-                                                    uint16_t* __restrict__ out) {
+                                                    uint16_t* __restrict__ out, const float* __restrict__ in_ss,
+                                                    int64_t ss_stride, int32_t ss_cols) {
     __shared__ float part[4];
     const int row = blockIdx.x, tid = threadIdx.x;
     float* hr = h + (int64_t)row * ldh;
     const float* pr = partials + (int64_t)row * ldp;
+    const float rin = in_ss ? input_rinv(in_ss, ss_stride, splits, row, ss_cols, eps) : 1.0f;
     float ss = 0.0f;
     for (int c = tid * 4; c < cols; c += 1024) {
         float4 v = add ? *(const float4*)(hr + c) : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -93,6 +104,7 @@ __global__ void __launch_bounds__(256) fold_rmsnorm(float* __restrict__ h, int64
             const float4 p = *(const float4*)(pr + sp * pstride + c);
             v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
         }
+        if (in_ss) { v.x *= rin; v.y *= rin; v.z *= rin; v.w *= rin; }
         *(float4*)(hr + c) = v;
         ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
     }
@@ -125,11 +137,13 @@ __global__ void __launch_bounds__(1024) fold_rmsnorm_row(float* __restrict__ h, 
                                                          const float* __restrict__ partials, int32_t splits,
                                                          int64_t pstride, int64_t ldp,
                                                          const float* __restrict__ gain, int32_t cols, float eps,
-                                                         uint16_t* __restrict__ out) {
+                                                         uint16_t* __restrict__ out, const float* __restrict__ in_ss,
+                                                         int64_t ss_stride, int32_t ss_cols) {
     __shared__ float part[16];
     const int row = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
     float* hr = h + (int64_t)row * ldh;
     const float* pr = partials + (int64_t)row * ldp;
+    const float rin = in_ss ? input_rinv(in_ss, ss_stride, splits, row, ss_cols, eps) : 1.0f;
     float4 v[V], p[kMaxFoldSplits][V];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
@@ -150,6 +164,7 @@ __global__ void __launch_bounds__(1024) fold_rmsnorm_row(float* __restrict__ h, 
                 if (sp < splits) {
                     v[i].x += p[sp][i].x; v[i].y += p[sp][i].y; v[i].z += p[sp][i].z; v[i].w += p[sp][i].w;
                 }
+            if (in_ss) { v[i].x *= rin; v[i].y *= rin; v[i].z *= rin; v[i].w *= rin; }
             *(float4*)(hr + c) = v[i];
         }
         ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
@@ -420,30 +435,32 @@ hipError_t launch_cast_tiled(const float* x, int64_t ldx, int32_t rows, int32_t 
 
 hipError_t launch_fold_rmsnorm(float* h, int64_t ldh, bool add, const float* partials, int32_t splits,
                                int64_t pstride, int64_t ldp, const float* g, int32_t rows, int32_t cols,
-                               float eps, uint16_t* out, bool bf16, hipStream_t s) {
+                               float eps, uint16_t* out, bool bf16, hipStream_t s, const float* ss,
+                               int64_t ss_stride, int32_t ss_cols) {
     if (rows <= 0) return hipSuccess;
     if (cols % 32 || splits < 1) return hipErrorInvalidValue;
+    if (ss && (add || ss_cols <= 0 || ss_stride < rows)) return hipErrorInvalidValue;
     if (cols <= 4096 && splits <= kMaxFoldSplits) {
         const bool two = cols > 1024;
         const dim3 t(row_threads(cols, two ? 2 : 1));
         if (bf16 && two)
             hipLaunchKernelGGL((fold_rmsnorm_row<true, 2>), dim3(rows), t, 0, s, h, ldh, (int)add, partials,
-                               splits, pstride, ldp, g, cols, eps, out);
+                               splits, pstride, ldp, g, cols, eps, out, ss, ss_stride, ss_cols);
         else if (two)
             hipLaunchKernelGGL((fold_rmsnorm_row<false, 2>), dim3(rows), t, 0, s, h, ldh, (int)add, partials,
-                               splits, pstride, ldp, g, cols, eps, out);
+                               splits, pstride, ldp, g, cols, eps, out, ss, ss_stride, ss_cols);
         else if (bf16)
             hipLaunchKernelGGL((fold_rmsnorm_row<true, 1>), dim3(rows), t, 0, s, h, ldh, (int)add, partials,
-                               splits, pstride, ldp, g, cols, eps, out);
+                               splits, pstride, ldp, g, cols, eps, out, ss, ss_stride, ss_cols);
         else
             hipLaunchKernelGGL((fold_rmsnorm_row<false, 1>), dim3(rows), t, 0, s, h, ldh, (int)add, partials,
-                               splits, pstride, ldp, g, cols, eps, out);
+                               splits, pstride, ldp, g, cols, eps, out, ss, ss_stride, ss_cols);
     } else if (bf16)
         hipLaunchKernelGGL(fold_rmsnorm<true>, dim3(rows), dim3(256), 0, s, h, ldh, (int)add, partials, splits,
-                           pstride, ldp, g, cols, eps, out);
+                           pstride, ldp, g, cols, eps, out, ss, ss_stride, ss_cols);
     else
         hipLaunchKernelGGL(fold_rmsnorm<false>, dim3(rows), dim3(256), 0, s, h, ldh, (int)add, partials, splits,
-                           pstride, ldp, g, cols, eps, out);
+                           pstride, ldp, g, cols, eps, out, ss, ss_stride, ss_cols);
     return hipGetLastError();
 }
 

@@ -275,7 +275,8 @@ struct kva_ctx {
 
     // scratch (device), rows padded to kRowPad
     int64_t m_alloc = 0;
-    uint16_t* u16 = nullptr;    // [m][n_in]   fp16 normed input
+    uint16_t* u16 = nullptr;    // [m][n_in]   fp16 normed input (skinny contexts only)
+    float* ss_in = nullptr;     // [n_split][m] input rows' sums of squares per K split (EPI_INPUT)
     float* h = nullptr;         // [m][d]      fp32 residual stream
     uint16_t* a16 = nullptr;    // [m][d]      fp16 normed activations
     uint16_t* qk16 = nullptr;   // [m][2 hd]   fp16 Q | K
@@ -661,7 +662,12 @@ kva_status create_impl(const kva_config* cfg, const kva_weights* w, int device, 
     // -------- scratch
     const int64_t m = round_up(c.max_tokens, kRowPad);
     ctx->m_alloc = m;
-    HIP_TRY(ctx->alloc(&ctx->u16, (size_t)m * n_in * 2, false));
+    ctx->skinny = c.max_tokens <= kSkinnyTokens;
+    ctx->n_split = ctx->skinny ? kSkinnySplits : split_narrow(d, c.max_tokens, ctx->trunk_opd == OPD_F16);
+    // The input RMSNorm runs inside the input GEMM (EPI_INPUT), except on the
+    // skinny kernel, which reads a normalised fp16 copy
+    if (ctx->skinny) HIP_TRY(ctx->alloc(&ctx->u16, (size_t)m * n_in * 2, false));
+    else HIP_TRY(ctx->alloc(&ctx->ss_in, (size_t)ctx->n_split * m * 4, false));
     HIP_TRY(ctx->alloc(&ctx->h, (size_t)m * d * 4, false));
     HIP_TRY(ctx->alloc(&ctx->a16, (size_t)m * d * 2, false));
     HIP_TRY(ctx->alloc(&ctx->qk16, (size_t)m * 2 * hd * 2, false));
@@ -669,12 +675,10 @@ kva_status create_impl(const kva_config* cfg, const kva_weights* w, int device, 
     HIP_TRY(ctx->alloc(&ctx->o16, (size_t)m * hd * 2, false));
     HIP_TRY(ctx->alloc(&ctx->act16, (size_t)m * F * 2, false));
     HIP_TRY(ctx->alloc(&ctx->z16, (size_t)m * d * 2, false));
-    ctx->skinny = c.max_tokens <= kSkinnyTokens;
-    ctx->n_split = ctx->skinny ? kSkinnySplits : split_narrow(d, c.max_tokens, ctx->trunk_opd == OPD_F16);
     HIP_TRY(ctx->alloc(&ctx->ws, (size_t)ctx->n_split * m * d * 4, false));
     // Scratch rows past n_tokens feed MFMA rows whose results are dropped; zero
     // them once so they always hold finite values.
-    HIP_TRY(hipMemset(ctx->u16, 0, (size_t)m * n_in * 2));
+    if (ctx->u16) HIP_TRY(hipMemset(ctx->u16, 0, (size_t)m * n_in * 2));
     HIP_TRY(hipMemset(ctx->h, 0, (size_t)m * d * 4));
     HIP_TRY(hipMemset(ctx->a16, 0, (size_t)m * d * 2));
     HIP_TRY(hipMemset(ctx->qk16, 0, (size_t)m * 2 * hd * 2));
@@ -937,19 +941,34 @@ kva_status project(kva_ctx* ctx, const float* x, int32_t n, float* const* head_o
         STAGE(stage, gemm(EPI_PARTIAL, g));
         return KVA_OK;
     };
-    auto fold = [&](bool add, const float* gain, uint16_t* out, bool bf16) -> kva_status {
+    // ss: the input GEMM's row sums of squares (the first fold applies the
+    // input norm's 1/RMS to the summed partials)
+    auto fold = [&](bool add, const float* gain, uint16_t* out, bool bf16, const float* ss = nullptr) -> kva_status {
         STAGE(KVA_STAGE_NORM, launch_fold_rmsnorm(ctx->h, d, add, ctx->ws, ctx->n_split, pstride, d, gain, n,
-                                                  (int32_t)d, c.eps, out, bf16, s));
+                                                  (int32_t)d, c.eps, out, bf16, s, ss, ctx->m_alloc, (int32_t)n_in));
         return KVA_OK;
     };
 
-    STAGE(KVA_STAGE_NORM,
-          launch_rmsnorm_cast(x, n_in, ctx->g_in, n, (int32_t)n_in, c.eps, ctx->u16, false, s));
-    KVA_TRY(narrow(ctx->u16, n_in, ctx->w_in, KVA_STAGE_GEMM_IN));
+    if (ctx->skinny) {
+        STAGE(KVA_STAGE_NORM,
+              launch_rmsnorm_cast(x, n_in, ctx->g_in, n, (int32_t)n_in, c.eps, ctx->u16, false, s));
+        KVA_TRY(narrow(ctx->u16, n_in, ctx->w_in, KVA_STAGE_GEMM_IN));
+    } else {
+        // RMSNorm + input Linear in one GEMM: A = fp16(x * g_in), unnormalised
+        // partials, and each row's sum of squares for the fold
+        GemmArgs g;
+        g.A = reinterpret_cast<const uint16_t*>(x); g.lda = n_in; set_b(g, ctx->w_in, n_in);
+        g.M = n; g.N = (int32_t)round_up(d, kColPad); g.K = (int32_t)n_in;
+        g.splits = ctx->n_split; g.split_stride = pstride;
+        g.epi.out_f32 = ctx->ws; g.epi.ld_f32 = d; g.epi.n_real = (int32_t)d;
+        g.epi.a_gain = ctx->g_in; g.epi.ss = ctx->ss_in; g.epi.ss_stride = ctx->m_alloc;
+        STAGE(KVA_STAGE_GEMM_IN,
+              launch_gemm_t32(opd, pick_tile_t32(g.M, g.N, g.splits, opd == OPD_F16), EPI_INPUT, g, s));
+    }
     for (int b = 0; b < c.n_blocks; ++b) {
         const kva_ctx::Blk& B = ctx->blk[b];
         // h = (b == 0 ? 0 : h) + input/down partials; a = attn_norm(h)
-        KVA_TRY(fold(b > 0, B.g_attn, ctx->a16, false));
+        KVA_TRY(fold(b > 0, B.g_attn, ctx->a16, false, (b == 0 && !ctx->skinny) ? ctx->ss_in : nullptr));
         {
             GemmArgs g;
             g.A = ctx->a16; g.lda = d; set_b(g, B.wqkv, d);

@@ -13,7 +13,8 @@ time:
   ------  ------------------------------------------------  ------------------
   w       trunk weights (bf16/fp32 storage -> MFMA operand)  fp16
   wh      head weights                                       bf16 (fp16 for q8_0/q4_0)
-  in      input RMSNorm output u                             fp16
+  in      input times its norm gain, x * g (the row's 1/RMS  fp16
+          then scales the input Linear's output)
   a1      attention-norm output                              fp16
   q       Q times log2(e)/sqrt(128) (scores in base 2; the   fp16
           factor itself as a binary32 constant)
@@ -121,8 +122,14 @@ def project(cfg: dict, weights: dict, x: np.ndarray, points=ALL_POINTS, which=No
 
     z = np.empty((x.shape[0], d), dtype=ar)
     for s, e in ref.block_ranges(x.shape[0], cfg["attn_block"]):
-        u = _r(points, "in", f16, _rmsnorm(x[s:e], g_in, eps))
-        h = u @ w_in.T
+        if "in" in points:
+            # a 16-bit implementation that folds the norm into the GEMM rounds
+            # x * g and applies the row's 1/RMS to the product afterwards
+            xb = x[s:e]
+            rin = 1.0 / np.sqrt(np.mean(xb * xb, axis=-1, keepdims=True) + eps)
+            h = (f16(xb * g_in).astype(ar) @ w_in.T) * rin
+        else:
+            h = _rmsnorm(x[s:e], g_in, eps) @ w_in.T
         for b in blocks:
             a = _r(points, "a1", f16, _rmsnorm(h, b["attn_norm"], eps))
             q2 = (a @ b["wq"].T) * ar.type(Q_SCALE_F32 if "q" in points else Q_SCALE)

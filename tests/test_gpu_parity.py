@@ -7,6 +7,7 @@ dequantisation hook, and determinism.  The KV-cache write must land within
 one bf16 ulp of the oracle's correctly rounded value plus the fp32
 rotation's absolute error (2^-20 of the rotary pair's norm); V bit-exact.
 """
+import concurrent.futures
 import os
 
 import numpy as np
@@ -368,6 +369,23 @@ def _kv_cache(n_logical, n_pages):
     return kp, vp
 
 
+def _check_kv_bf16(gk, gv, k, v, n_rot):
+    """bf16 cache rows (bit patterns) against the oracle's float64 K and V."""
+    assert np.array_equal(gv, ref.f64_to_bf16_bits(v))            # V: a single rounding of fp32 data
+    # K: one bf16 ulp of the correctly rounded value, plus the fp32 rotation's
+    # absolute error (angle, sin/cos and products, relative to the rotary pair's
+    # norm): where a rotated value nearly cancels, that exceeds its own bf16 ulp.
+    dk = np.abs(ref.bf16_bits_to_f64(gk) - ref.bf16_bits_to_f64(ref.f64_to_bf16_bits(k)))
+    ulp = np.ldexp(1.0, np.frexp(np.abs(k))[1] - 8)
+    pair = np.zeros_like(k)
+    half = n_rot // 2
+    pn = np.sqrt(k[..., :half] ** 2 + k[..., half:n_rot] ** 2)
+    pair[..., :half], pair[..., half:n_rot] = pn, pn
+    bound = ulp + 2.0 ** -20 * pair
+    assert np.all(dk <= bound), float(np.max(dk / bound))
+    assert np.mean(dk == 0) > (0.98 if k.shape[0] > 100 else 0.9)
+
+
 @pytest.mark.parametrize("pos0,n,n_rot", [(0, 600, 64), (65536 - 700, 700, 64), (300, 5, 32), (1021, 3, 64),
                                           (4000, 1, 16)])
 def test_kv_write_parity(pos0, n, n_rot):
@@ -386,25 +404,45 @@ def test_kv_write_parity(pos0, n, n_rot):
     vpn = vp.cpu().numpy().view(np.uint16)
     k, v = ref.kv_write_values(kv, gains[0], pos0, n_rot=n_rot)
     pos = pos0 + np.arange(n)
-    gk = kpn[ptab[pos // 256], pos % 256]
-    gv = vpn[ptab[pos // 256], pos % 256]
-    assert np.array_equal(gv, ref.f64_to_bf16_bits(v))            # V: a single rounding of fp32 data
-    # K: one bf16 ulp of the correctly rounded value, plus the fp32 rotation's
-    # absolute error (angle, sin/cos and products, relative to the rotary pair's
-    # norm): where a rotated value nearly cancels, that exceeds its own bf16 ulp.
-    dk = np.abs(ref.bf16_bits_to_f64(gk) - ref.bf16_bits_to_f64(ref.f64_to_bf16_bits(k)))
-    ulp = np.ldexp(1.0, np.frexp(np.abs(k))[1] - 8)
-    pair = np.zeros_like(k)
-    half = n_rot // 2
-    pn = np.sqrt(k[..., :half] ** 2 + k[..., half:n_rot] ** 2)
-    pair[..., :half], pair[..., half:n_rot] = pn, pn
-    bound = ulp + 2.0 ** -20 * pair
-    assert np.all(dk <= bound), float(np.max(dk / bound))
-    assert np.mean(dk == 0) > (0.98 if n > 100 else 0.9)
+    _check_kv_bf16(kpn[ptab[pos // 256], pos % 256], vpn[ptab[pos // 256], pos % 256], k, v, n_rot)
     # slots outside the written range keep the poison
     used = np.zeros((n_pages, 256), dtype=bool)
     used[ptab[pos // 256], pos % 256] = True
     assert np.all(kpn[~used] == 0xFFFF) and np.all(vpn[~used] == 0xFFFF)
+
+
+def test_kv_write_every_position_of_a_65536_token_prompt():
+    """The bf16 paged KV write of a whole 65536-token prompt for 8 attention
+    layers, in the launches the benchmark times (8192 tokens per call): every
+    position of every layer against the oracle, at the bar above, and every
+    slot of every page written."""
+    n_tok, layers, chunk = 65536, 8, 8192
+    gains, ptab, n_pages = synth.make_kv_write_inputs(n_tok, n_layers=layers)
+    ptab_d = torch.from_numpy(ptab).cuda()
+    st = kva.current_stream()
+    for li in range(layers):
+        kv = synth.make_kv_rows(n_tok, seed=40 + li, scale=3.0)
+        kp, vp = _kv_cache((n_tok + 255) // 256, n_pages)
+        cache = kva.kva_paged_kv(kp.data_ptr(), vp.data_ptr(), ptab_d.data_ptr(), 256, n_pages, len(ptab),
+                                 4, 256, 64, 1.0e7, 1e-6)
+        kv_d = torch.from_numpy(kv).cuda()
+        g_d = torch.from_numpy(gains[li]).cuda()
+        for c0 in range(0, n_tok, chunk):
+            kva.kva_attn_kv_write(kv_d[c0].data_ptr(), kv.shape[1], chunk, c0, g_d.data_ptr(), cache, st)
+        torch.cuda.synchronize()
+        kpn = kp.cpu().numpy().view(np.uint16)
+        vpn = vp.cpu().numpy().view(np.uint16)
+        assert not (kpn == 0xFFFF).all(axis=-1).any() and not (vpn == 0xFFFF).all(axis=-1).any()
+        def check(c0, li=li, kv=kv, kpn=kpn, vpn=vpn):
+            k, v = ref.kv_write_values(kv[c0:c0 + chunk], gains[li], c0)
+            pos = c0 + np.arange(chunk)
+            _check_kv_bf16(kpn[ptab[pos // 256], pos % 256], vpn[ptab[pos // 256], pos % 256], k, v, 64)
+
+        # the oracle's chunks in threads (NumPy releases the GIL in its loops)
+        with concurrent.futures.ThreadPoolExecutor(max_workers=8) as pool:
+            list(pool.map(check, range(0, n_tok, chunk)))
+        print(f"kv write layer {li}: all {n_tok} positions match", flush=True)
+        del kv_d, kp, vp
 
 
 def _q8_rows_check(got_rows, want, where):
