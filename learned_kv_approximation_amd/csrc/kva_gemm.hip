@@ -1141,11 +1141,11 @@ hipError_t launch_gemm_t32(GemmOperand opd, GemmTile tile, EpiKind epi, const Ge
     if (a.M <= 0) return hipSuccess;
     if (a.K % 32 != 0 || a.K <= 0) return hipErrorInvalidValue;
     KVA_T32_CASE(OPD_F16, TILE_256x256, EPI_PARTIAL, 256, 256, 2, 4)
-    KVA_T32_CASE(OPD_F16, TILE_256x256, EPI_INPUT, 256, 256, 2, 4)
     KVA_T32_CASE(OPD_F16, TILE_256x256, EPI_QKV, 256, 256, 2, 4)
     KVA_T32_CASE(OPD_F16, TILE_256x256, EPI_SWIGLU, 256, 256, 2, 4)
     KVA_T32_CASE(OPD_F16, TILE_256x128, EPI_PARTIAL, 256, 128, 4, 2)
     KVA_T32_CASE(OPD_F16, TILE_256x128, EPI_INPUT, 256, 128, 4, 2)
+    KVA_T32_CASE(OPD_F16, TILE_128x256, EPI_INPUT, 128, 256, 2, 4)
     KVA_T32_CASE(OPD_F16, TILE_256x128, EPI_QKV, 256, 128, 4, 2)
     KVA_T32_CASE(OPD_F16, TILE_256x128, EPI_SWIGLU, 256, 128, 4, 2)
     KVA_T32_CASE(OPD_F16, TILE_128x128, EPI_PARTIAL, 128, 128, 2, 2)

@@ -242,7 +242,8 @@ __device__ __forceinline__ void q8_0_f16x8(uint32_t c0, uint32_t c1, uint16_t d_
 }
 // 256x256: 8 waves (2 per SIMD); 128x128: 4 waves; 64xN (calls of at most
 // 64 rows): 2 waves of 64 x 32 (N = 64), or of 64 x 64 for SwiGLU (N = 128).
-enum GemmTile : int { TILE_256x256 = 0, TILE_128x128 = 1, TILE_256x128 = 2, TILE_64xN = 3 };
+// TILE_128x256: the input GEMM with 16-bit weights only (EPI_INPUT)
+enum GemmTile : int { TILE_256x256 = 0, TILE_128x128 = 1, TILE_256x128 = 2, TILE_64xN = 3, TILE_128x256 = 4 };
 
 // The GEMM.  A rows are grouped by 256 like the weight rows (rows >= M of
 // the last group are read and dropped).  32-wide K slabs through a ring of
