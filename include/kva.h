@@ -455,8 +455,10 @@ kva_status kva_debug_host_to_f16(const void* src, int32_t src_dtype, int64_t n, 
 
 /* Stages of one projection, for kva_profile_*. */
 typedef enum {
-    KVA_STAGE_NORM = 0,        /* RMSNorm + cast kernels (input, 2 per block, final) */
-    KVA_STAGE_GEMM_IN = 1,     /* Linear n_in -> d                                    */
+    KVA_STAGE_NORM = 0,        /* RMSNorm + cast kernels (2 per block, final; the
+                                  input norm too in contexts of <= 32 tokens per call) */
+    KVA_STAGE_GEMM_IN = 1,     /* input RMSNorm + Linear n_in -> d in one GEMM (the
+                                  row's 1/RMS applied by the first block's norm)      */
     KVA_STAGE_GEMM_QKV = 2,    /* Q|K|V projection                                    */
     KVA_STAGE_ATTN = 3,        /* block-causal attention                               */
     KVA_STAGE_GEMM_O = 4,      /* output projection + residual                         */
