@@ -294,6 +294,25 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[MI][NI
     }
 }
 
+// The input GEMM's operand arithmetic (EPI_INPUT), shared by its two tile
+// kernels so that every tile shape gives the same bits:
+//  - four activations x (one 16-byte chunk of a row, K-values 4c..4c+3) and
+//    their norm gains -> fp16(x * gain), two per dword (whole-vector casts: a
+//    bit cast of one vector element compiled to element 0 for every index);
+//  - the chunk's sum of squares, x0^2 + x1^2 + x2^2 + x3^2 in this order.
+// A row's sum of squares over a K range is then, per chunk position c of the
+// 32-wide slabs, S_c = the slabs' chunk sums added in slab order, and the
+// total ((S0 + S1) + (S2 + S3)) + ((S4 + S5) + (S6 + S7)).
+__device__ __forceinline__ u32x2 input_f16x4(f32x4 x, f32x4 gv) {
+    u32x2 o;
+    o[0] = (uint32_t)to_f16_bits(x[0] * gv[0]) | ((uint32_t)to_f16_bits(x[1] * gv[1]) << 16);
+    o[1] = (uint32_t)to_f16_bits(x[2] * gv[2]) | ((uint32_t)to_f16_bits(x[3] * gv[3]) << 16);
+    return o;
+}
+__device__ __forceinline__ float input_chunk_sq(f32x4 x) {
+    return __builtin_fmaf(x[3], x[3], __builtin_fmaf(x[2], x[2], __builtin_fmaf(x[1], x[1], x[0] * x[0])));
+}
+
 // K is walked in 32-wide slabs through a ring of S LDS stages.
 //  - A slab's A rows and B rows are each one contiguous block in global
 //    memory (the tiled layouts), copied straight into LDS with
@@ -320,25 +339,6 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[MI][NI
 // q8_0 (except SwiGLU, whose gate/up pairs need two 32-column blocks a wave)
 // 1 x 4 waves of 128 x 32, so that each weight fragment is converted by one
 // wave only.
-// The input GEMM's operand arithmetic (EPI_INPUT), shared by its two tile
-// kernels so that every tile shape gives the same bits:
-//  - four activations x (one 16-byte chunk of a row, K-values 4c..4c+3) and
-//    their norm gains -> fp16(x * gain), two per dword (whole-vector casts: a
-//    bit cast of one vector element compiled to element 0 for every index);
-//  - the chunk's sum of squares, x0^2 + x1^2 + x2^2 + x3^2 in this order.
-// A row's sum of squares over a K range is then, per chunk position c of the
-// 32-wide slabs, S_c = the slabs' chunk sums added in slab order, and the
-// total ((S0 + S1) + (S2 + S3)) + ((S4 + S5) + (S6 + S7)).
-__device__ __forceinline__ u32x2 input_f16x4(f32x4 x, f32x4 gv) {
-    u32x2 o;
-    o[0] = (uint32_t)to_f16_bits(x[0] * gv[0]) | ((uint32_t)to_f16_bits(x[1] * gv[1]) << 16);
-    o[1] = (uint32_t)to_f16_bits(x[2] * gv[2]) | ((uint32_t)to_f16_bits(x[3] * gv[3]) << 16);
-    return o;
-}
-__device__ __forceinline__ float input_chunk_sq(f32x4 x) {
-    return __builtin_fmaf(x[3], x[3], __builtin_fmaf(x[2], x[2], __builtin_fmaf(x[1], x[1], x[0] * x[0])));
-}
-
 template <int BM, int BN, int OPD, int EPI>
 struct T32Shape {
     static constexpr bool Q8 = OPD == OPD_Q8;
