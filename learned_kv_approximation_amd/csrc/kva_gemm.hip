@@ -294,8 +294,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[MI][NI
     }
 }
 
-// The input GEMM's operand arithmetic (EPI_INPUT), shared by its two tile
-// kernels so that every tile shape gives the same bits:
+// The input GEMM's operand arithmetic (EPI_INPUT), the same for every tile
+// shape so that a row's bits never depend on the tile a call takes:
 //  - four activations x (one 16-byte chunk of a row, K-values 4c..4c+3) and
 //    their norm gains -> fp16(x * gain), two per dword (whole-vector casts: a
 //    bit cast of one vector element compiled to element 0 for every index);
@@ -344,25 +344,18 @@ struct T32Shape {
     static constexpr bool Q8 = OPD == OPD_Q8;
     static constexpr bool Q4 = OPD == OPD_Q4;
     static constexpr bool QW = Q8 || Q4;                            // block-quantised weights
-    // EPI_INPUT: the activations arrive as fp32 rows (128 bytes a row per
-    // slab) and the slab's 32 input-norm gains ride along
-    static constexpr bool AF = EPI == EPI_INPUT;
     static constexpr int KB = 32;
-    static constexpr int A_BYTES = BM * KB * (AF ? 4 : 2);
+    static constexpr int A_BYTES = BM * KB * 2;
     static constexpr int B_ROW = Q8 ? KB : Q4 ? KB / 2 : KB * 2;    // weight bytes of a row per slab
     static constexpr int B_BYTES = BN * B_ROW;
     static constexpr int S_BYTES = QW ? BN * 2 : 0;                 // fp16 block scales
-    static constexpr int G_BYTES = AF ? KB * 4 : 0;                 // fp32 input-norm gains
-    static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES + G_BYTES;
+    static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
     // the head epilogue stages whole 256-column tiles through LDS (128 KB at
     // a time for a 256-row tile)
     static constexpr bool LDS_EPI = EPI == EPI_HEADS && BN == kHeadTileN;
     // 64-row tiles (calls of at most 64 rows) stream every weight once from
     // few workgroups: a deeper ring keeps more slabs in flight
-    static constexpr int S0 = (LDS_EPI && BM == 256) ? (128 * 1024 + STAGE - 1) / STAGE : (BM == 64 && EPI != EPI_HEADS) ? 8 : 4;
-    // (the fp32 rows of EPI_INPUT take fewer stages where four do not fit
-    // the 160 KB of LDS)
-    static constexpr int S = S0 * STAGE <= 160 * 1024 ? S0 : (160 * 1024) / STAGE;
+    static constexpr int S = (LDS_EPI && BM == 256) ? (128 * 1024 + STAGE - 1) / STAGE : (BM == 64 && EPI != EPI_HEADS) ? 8 : 4;
     static constexpr int BYTES = S * STAGE;
 };
 
@@ -385,7 +378,6 @@ __device__ __forceinline__ void t32_tile(const GemmArgs& g, int tm, int tn, int 
     constexpr bool BF16 = OPD == OPD_BF16;
     constexpr bool Q4 = Sh::Q4;
     constexpr bool QW = Sh::QW;          // block-quantised weights (q8_0 or q4_0)
-    constexpr bool AF = Sh::AF;          // fp32 input rows, converted here (EPI_INPUT)
     constexpr int NW = WGM * WGN, KB = Sh::KB, S = Sh::S;
     constexpr int WM = BM / WGM, WN = BN / WGN, MI = WM / 32, NI = WN / 32;
     // DMA instructions per wave and slab: 16 bytes per lane, or 4 for a
@@ -395,10 +387,7 @@ __device__ __forceinline__ void t32_tile(const GemmArgs& g, int tm, int tn, int 
     // q8_0 scales: every wave copies an equal share of them (SL lanes x 4
     // bytes), so that every wave issues the same number of DMA instructions
     constexpr int SL = Sh::S_BYTES / (4 * NW);
-    // EPI_INPUT gains: 8 pieces of 16 bytes per slab, GL lanes per wave
-    constexpr int GL = AF ? 8 / NW : 0;
-    static_assert(!AF || (GL >= 1 && GL * NW == 8), "gain DMA split");
-    constexpr int L = AI + BI + (QW ? 1 : 0) + (AF ? 1 : 0);
+    constexpr int L = AI + BI + (QW ? 1 : 0);
     static_assert(AI >= 1 && BI >= 1 && AI * 1024 * NW == Sh::A_BYTES && BI * 64 * BSZ * NW == Sh::B_BYTES,
                   "tile too small for the wave grid");
     static_assert(!QW || (SL >= 1 && SL <= 64 && SL * 4 * NW == Sh::S_BYTES), "scale DMA split");
@@ -426,38 +415,13 @@ __device__ __forceinline__ void t32_tile(const GemmArgs& g, int tm, int tn, int 
     constexpr int64_t A_SLAB = (int64_t)kWeightTileRows * KB * 2;              // bytes between slabs
     constexpr int64_t B_SLAB = (int64_t)kWeightTileRows * Sh::B_ROW;
     constexpr int64_t S_SLAB = (int64_t)kWeightTileRows * 2;
-    // EPI_INPUT: DMA instruction i of this wave copies 8 fp32 rows of the
-    // slab (lane: row lane / 8, 16-byte chunk lane % 8).  LDS keeps a row's 8
-    // chunks rotated by the row's low 3 bits (position p holds chunk
-    // p ^ (r & 7)), so a fragment read by 8 consecutive rows covers every
-    // bank once; rows past M read row M - 1 (in bounds, never stored).
-    const float* xsrc[AF ? AI : 1];
-    if constexpr (AF) {
-        const float* X = reinterpret_cast<const float*>(g.A);
-#pragma unroll
-        for (int i = 0; i < AI; ++i) {
-            const int lr = (i * NW + wave) * 8 + (lane >> 3);
-            const int row = min(tm * BM + lr, g.M - 1);
-            xsrc[i] = X + (int64_t)row * g.lda + (int64_t)kb * KB + (((lane & 7) ^ (lr & 7)) * 4);
-        }
-    }
     auto issue = [&](int kt, int st) {
         uint8_t* sa = smem + st * Sh::STAGE;
         uint8_t* sb = sa + Sh::A_BYTES;
-        if constexpr (AF) {
 #pragma unroll
-            for (int i = 0; i < AI; ++i)
-                __builtin_amdgcn_global_load_lds((gbl_ptr_t)(xsrc[i] + kt * KB),
-                                                 (lds_ptr_t)(sa + (i * NW + wave) * 1024), 16, 0, 0);
-            if (lane < GL)
-                __builtin_amdgcn_global_load_lds((gbl_ptr_t)(g.epi.a_gain + (int64_t)(kb + kt) * KB + (wave * GL + lane) * 4),
-                                                 (lds_ptr_t)(sb + Sh::B_BYTES + Sh::S_BYTES + wave * GL * 16), 16, 0, 0);
-        } else {
-#pragma unroll
-            for (int i = 0; i < AI; ++i)
-                __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Ab + kt * A_SLAB + (i * NW + wave) * 1024 + lane * 16),
-                                                 (lds_ptr_t)(sa + (i * NW + wave) * 1024), 16, 0, 0);
-        }
+        for (int i = 0; i < AI; ++i)
+            __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Ab + kt * A_SLAB + (i * NW + wave) * 1024 + lane * 16),
+                                             (lds_ptr_t)(sa + (i * NW + wave) * 1024), 16, 0, 0);
 #pragma unroll
         for (int i = 0; i < BI; ++i) {
             const uint8_t* src = Bb + kt * B_SLAB + (i * NW + wave) * 64 * BSZ + lane * BSZ;
@@ -491,41 +455,18 @@ __device__ __forceinline__ void t32_tile(const GemmArgs& g, int tm, int tn, int 
     const int swq = Q4 ? (frow >> 3) & 3 : (frow >> 2) & 3;   // q4_0 / q8_0 code chunk swizzle
     int aoff[MI], boff[NI];
 #pragma unroll
-    for (int i = 0; i < MI; ++i) aoff[i] = (wm * WM + i * 32 + frow) * KB * (AF ? 4 : 2);
+    for (int i = 0; i < MI; ++i) aoff[i] = (wm * WM + i * 32 + frow) * KB * 2;
 #pragma unroll
     for (int j = 0; j < NI; ++j) boff[j] = Sh::A_BYTES + (wn * WN + j * 32 + frow) * Sh::B_ROW;
     // fragments: fa/fb ready for the MFMA; for q8_0, qc/qs hold the raw codes and scales
     u32x4 fa0[MI], fb0[NI], fa1[MI], fb1[NI];
     u32x2 qc0[NI], qc1[NI];
     uint16_t qs0[NI], qs1[NI];
-    // EPI_INPUT: the raw fp32 activations (8 K-values: two 16-byte chunks)
-    // and their 8 gains, and per 32-row block the running sums of squares of
-    // the lane's four 4-value chunks of a slab (chunks 2 fk + h of step 0 in
-    // ssq[i][h], of step 1 in ssq[i][2 + h]; see input_chunk_sq)
-    constexpr int XM = AF ? MI : 1;
-    u32x4 xa0[XM][2], xa1[XM][2], ga0[2], ga1[2];
-    float ssq[XM][4], sq0[XM][2], sq1[XM][2];     // running sums; one step's chunk sums
-#pragma unroll
-    for (int i = 0; i < XM; ++i)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) ssq[i][c] = 0.0f;
-    auto rd = [&](int st, int ks, u32x4* fa, u32x4* fb, u32x2* qc, uint16_t* qs, u32x4 (*xa)[2], u32x4* ga) {
+    auto rd = [&](int st, int ks, u32x4* fa, u32x4* fb, u32x2* qc, uint16_t* qs) {
         const uint8_t* base = smem + st * Sh::STAGE;
         const int c = ((ks * 2 + fk) ^ sw) << 4;
-        if constexpr (AF) {
-            const int c0 = ks * 4 + fk * 2, swa = frow & 7;
 #pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                xa[i][0] = *(const u32x4*)(base + aoff[i] + ((c0 ^ swa) << 4));
-                xa[i][1] = *(const u32x4*)(base + aoff[i] + (((c0 + 1) ^ swa) << 4));
-            }
-            const uint8_t* gb = base + Sh::A_BYTES + Sh::B_BYTES + Sh::S_BYTES + ks * 64 + fk * 32;
-            ga[0] = *(const u32x4*)gb;
-            ga[1] = *(const u32x4*)(gb + 16);
-        } else {
-#pragma unroll
-            for (int i = 0; i < MI; ++i) fa[i] = *(const u32x4*)(base + aoff[i] + c);
-        }
+        for (int i = 0; i < MI; ++i) fa[i] = *(const u32x4*)(base + aoff[i] + c);
         if constexpr (QW) {
             const int cq = ((ks * 2 + fk) ^ swq) << (Q4 ? 2 : 3);
 #pragma unroll
@@ -545,31 +486,6 @@ __device__ __forceinline__ void t32_tile(const GemmArgs& g, int tm, int tn, int 
             for (int j = 0; j < NI; ++j) fb[j] = q_fragment<Q4>(qc[j], qs[j]);
         }
     };
-    // EPI_INPUT: fa = input_f16x4 (fp16(x * gain)), and sq = the step's two
-    // chunk sums of squares; they join the running sums when the step's MFMAs
-    // are issued (so the stale read after the last slab is never counted)
-    auto cvt_a = [&](u32x4* fa, u32x4 (*xa)[2], const u32x4* ga, float (*sq)[2]) {
-        if constexpr (AF) {
-#pragma unroll
-            for (int i = 0; i < MI; ++i) {
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const u32x2 v = input_f16x4(__builtin_bit_cast(f32x4, xa[i][h]), __builtin_bit_cast(f32x4, ga[h]));
-                    fa[i][2 * h] = v[0];
-                    fa[i][2 * h + 1] = v[1];
-                    sq[i][h] = input_chunk_sq(__builtin_bit_cast(f32x4, xa[i][h]));
-                }
-            }
-        }
-    };
-    auto add_sq = [&](float (*sq)[2], int ks) {
-        if constexpr (AF) {
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) ssq[i][2 * ks + h] += sq[i][h];
-        }
-    };
     auto mm = [&](const u32x4* fa, const u32x4* fb) {
 #pragma unroll
         for (int i = 0; i < MI; ++i)
@@ -584,21 +500,19 @@ __device__ __forceinline__ void t32_tile(const GemmArgs& g, int tm, int tn, int 
     else vm_wait(std::integral_constant<int, 0>{});
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
-    rd(0, 0, fa0, fb0, qc0, qs0, xa0, ga0);
+    rd(0, 0, fa0, fb0, qc0, qs0);
     cvt(fb0, qc0, qs0);
-    cvt_a(fa0, xa0, ga0, sq0);
     lds_wait();
     // Instruction order of one K step: the LDS reads of the next step first,
     // then the current MFMAs (q8_0: with the conversion of the next
     // fragments between their two halves; it waits for the reads, and the
     // first MFMAs cover that latency).
     auto order = [&]() {
-        if constexpr (QW || AF) {
-            constexpr int RD = (AF ? 2 * MI + 2 : MI) + (QW ? 2 * NI : NI);
-            __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);            // LDS reads
+        if constexpr (QW) {
+            __builtin_amdgcn_sched_group_barrier(0x100, MI + 2 * NI, 0);   // LDS reads
             __builtin_amdgcn_sched_group_barrier(0x008, MI * NI / 2, 0);   // MFMAs
             __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);            // VALU: conversion
-            __builtin_amdgcn_sched_group_barrier(0x008, MI * NI - MI * NI / 2, 0);   // MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x008, MI * NI / 2, 0);   // MFMAs
         } else {
             // one LDS read after each of the first MFMAs
 #pragma unroll
@@ -625,12 +539,10 @@ __device__ __forceinline__ void t32_tile(const GemmArgs& g, int tm, int tn, int 
         constexpr bool MORE = decltype(more_c)::value;
         // the stage of slab kt-1 was released by the previous barrier
         if constexpr (MORE) issue(kt + S - 1, (kt + S - 1) % S);
-        rd(kt % S, 1, fa1, fb1, qc1, qs1, xa1, ga1);
+        rd(kt % S, 1, fa1, fb1, qc1, qs1);
         prio(std::integral_constant<int, 1>{});
         mm(fa0, fb0);
-        add_sq(sq0, 0);
         cvt(fb1, qc1, qs1);
-        cvt_a(fa1, xa1, ga1, sq1);
         order();
         prio(std::integral_constant<int, 0>{});
         __builtin_amdgcn_sched_barrier(0);      // the waits below stay after this step's MFMAs
@@ -642,12 +554,10 @@ __device__ __forceinline__ void t32_tile(const GemmArgs& g, int tm, int tn, int 
         __builtin_amdgcn_sched_barrier(0);
         __asm__ volatile("" ::: "memory");
         // after the last slab this reads a stale stage (in bounds); the values are not used
-        rd((kt + 1) % S, 0, fa0, fb0, qc0, qs0, xa0, ga0);
+        rd((kt + 1) % S, 0, fa0, fb0, qc0, qs0);
         prio(std::integral_constant<int, 1>{});
         mm(fa1, fb1);
-        add_sq(sq1, 1);
         cvt(fb0, qc0, qs0);
-        cvt_a(fa0, xa0, ga0, sq0);
         order();
         prio(std::integral_constant<int, 0>{});
         __builtin_amdgcn_sched_barrier(0);
@@ -656,53 +566,48 @@ __device__ __forceinline__ void t32_tile(const GemmArgs& g, int tm, int tn, int 
     int kt = 0;
     for (; kt + S - 1 < nk; ++kt) slab(kt, std::true_type{});
     for (; kt < nk; ++kt) slab(kt, std::false_type{});
-    if constexpr (AF) {
-        // the row sums of squares of this split's K range: the two K-halves
-        // (lanes l and l + 32) added, written once per row by the first N-tile
-        // lane fk holds chunks 2 fk, 2 fk + 1 (step 0) and 4 + 2 fk, 5 + 2 fk
-        // (step 1): ((S0 + S1) + (S2 + S3)) + ((S4 + S5) + (S6 + S7))
-        if (tn == 0 && wn == 0) {
-#pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                const float p1 = ssq[i][0] + ssq[i][1], p2 = ssq[i][2] + ssq[i][3];
-                const float q1 = __shfl_xor(p1, 32), q2 = __shfl_xor(p2, 32);
-                const int row = tm * BM + wm * WM + i * 32 + frow;
-                if (fk == 0 && row < g.M) g.epi.ss[split * g.epi.ss_stride + row] = (p1 + q1) + (p2 + q2);
-            }
-        }
-    }
     if constexpr (Sh::LDS_EPI) __syncthreads();    // the head epilogue reuses LDS
     epilogue<BM, BN, WGM, WGN, EPI, MI, NI, Sh::BYTES>(g, acc, tm, tn, split, reinterpret_cast<uint16_t*>(smem));
 }
 
-// The input GEMM (EPI_INPUT) with 16-bit weights.  The fp32 activation rows
-// and the weight slabs come through registers, three slabs ahead, and are
-// written to LDS by this kernel: the activations already as the fp16 operand
-// fp16(x * gain) in the tiled32 slab layout, so that the MFMA fragment reads
-// are those of the 16-bit GEMM (fp32 rows in LDS would double them).  Per
-// thread and slab: AQ 16-byte chunks of activation rows (8 threads to a
-// row), one chunk of gains, BQ 16-byte pieces of the weight slab (a copy of
-// its contiguous tiled block).  Two LDS stages, one barrier per slab; the
-// MFMA order over K and the fragment layout are those of t32_tile, and the
-// row sums of squares follow input_chunk_sq's order (thread chunk c = t % 8
-// holds S_c), so the bits equal the other input kernel's.
-template <int BM, int BN>
+// The input GEMM (EPI_INPUT: the input RMSNorm folded into the input
+// Linear), on the tiles whose accumulators leave room for its registers
+// (not 256x256: the host maps that choice to 128x256 or 128x128).  The fp32
+// activation rows and the weight slabs come through registers, three slabs
+// ahead, and are written to LDS by this kernel: the activations already as
+// the fp16 operand fp16(x * gain) in the tiled32 slab layout, so that the
+// MFMA fragment reads are those of t32_tile (fp32 rows in LDS would double
+// them).  Per thread
+// and slab: AQ 16-byte chunks of activation rows (8 threads to a row), one
+// chunk of gains, BQ 16-byte pieces of the weight slab and, for code planes,
+// one piece of its block scales (copies of their contiguous tiled blocks;
+// threads past the last piece load it again and do not write it).  Two LDS
+// stages, one barrier per slab; the MFMA order over K, the fragment layout
+// and the dequantisation are those of t32_tile, and the row sums of squares
+// follow input_chunk_sq's order (thread chunk c = t % 8 holds S_c).
+template <int BM, int BN, int OPD>
 struct InputShape {
+    static constexpr bool QW = OPD == OPD_Q8 || OPD == OPD_Q4;
     static constexpr int KB = 32;
-    static constexpr int A_BYTES = BM * KB * 2, B_BYTES = BN * KB * 2;
-    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int B_ROW = OPD == OPD_Q8 ? KB : OPD == OPD_Q4 ? KB / 2 : KB * 2;
+    static constexpr int A_BYTES = BM * KB * 2, B_BYTES = BN * B_ROW, S_BYTES = QW ? BN * 2 : 0;
+    static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
     static constexpr int BYTES = 2 * STAGE;
 };
 
-template <int BM, int BN, int WGM, int WGN>
+template <int BM, int BN, int WGM, int WGN, int OPD>
 __device__ __forceinline__ void t32_tile_input(const GemmArgs& g, int tm, int tn, int split, uint8_t* smem) {
-    using Sh = InputShape<BM, BN>;
+    using Sh = InputShape<BM, BN, OPD>;
+    constexpr bool QW = Sh::QW, Q4 = OPD == OPD_Q4;
     constexpr int NW = WGM * WGN, NT = 64 * NW, KB = Sh::KB;
     constexpr int WM = BM / WGM, WN = BN / WGN, MI = WM / 32, NI = WN / 32;
     constexpr int AQ = BM * KB / 4 / NT;          // activation chunks per thread and slab
-    constexpr int BQ = Sh::B_BYTES / 16 / NT;     // weight pieces per thread and slab
+    constexpr int NBP = Sh::B_BYTES / 16;         // weight pieces per slab
+    constexpr int BQ = (NBP + NT - 1) / NT;       // weight pieces per thread and slab
+    constexpr int NSP = Sh::S_BYTES / 16;         // scale pieces per slab (code planes)
+    constexpr int SQ = QW ? 1 : 0;
     constexpr int RPQ = NT / 8;                   // rows covered by one chunk index q
-    static_assert(AQ >= 1 && AQ * 4 * NT == BM * KB && BQ >= 1 && BQ * 16 * NT == Sh::B_BYTES, "input tile");
+    static_assert(AQ >= 1 && AQ * 4 * NT == BM * KB && NBP * 16 == Sh::B_BYTES && NSP <= NT, "input tile");
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WGN, wn = wave % WGN;
@@ -720,9 +625,16 @@ __device__ __forceinline__ void t32_tile_input(const GemmArgs& g, int tm, int tn
     }
     const float* gs = g.epi.a_gain + (int64_t)kb * KB + c4 * 4;
     const int64_t b_slab0 = (int64_t)(tn * BN / kWeightTileRows) * nk_all + kb;
-    const uint8_t* Bb = reinterpret_cast<const uint8_t*>(g.B) +
-                        (b_slab0 * kWeightTileRows + (tn * BN) % kWeightTileRows) * KB * 2 + tid * 16;
-    constexpr int64_t B_SLAB = (int64_t)kWeightTileRows * KB * 2;
+    const int64_t b_row0 = b_slab0 * kWeightTileRows + (tn * BN) % kWeightTileRows;
+    const uint8_t* Bb = (QW ? reinterpret_cast<const uint8_t*>(g.Bq) : reinterpret_cast<const uint8_t*>(g.B)) +
+                        b_row0 * Sh::B_ROW;
+    const uint8_t* Sb = QW ? reinterpret_cast<const uint8_t*>(g.Bs) + b_row0 * 2 : nullptr;
+    constexpr int64_t B_SLAB = (int64_t)kWeightTileRows * Sh::B_ROW;
+    constexpr int64_t S_SLAB = (int64_t)kWeightTileRows * 2;
+    int bp[BQ];                                    // this thread's weight pieces (clamped)
+#pragma unroll
+    for (int q = 0; q < BQ; ++q) bp[q] = min(q * NT + tid, NBP - 1) * 16;
+    const int sp = QW ? min(tid, NSP - 1) * 16 : 0;
     // LDS byte offset of this thread's fp16 chunk of row r (tiled32 slab
     // layout: 64-byte rows, 16-byte chunk cc at cc ^ swizzle(r), 8 bytes = half)
     int a_dst[AQ];
@@ -735,6 +647,7 @@ __device__ __forceinline__ void t32_tile_input(const GemmArgs& g, int tm, int tn
         f32x4 a[AQ];
         f32x4 gn;
         u32x4 b[BQ];
+        u32x4 sc[SQ > 0 ? SQ : 1];
     };
     Regs R0, R1, R2;
     auto load = [&](Regs& R, int kt) {
@@ -742,7 +655,8 @@ __device__ __forceinline__ void t32_tile_input(const GemmArgs& g, int tm, int tn
         for (int q = 0; q < AQ; ++q) R.a[q] = *(const f32x4*)(xs[q] + kt * KB);
         R.gn = *(const f32x4*)(gs + kt * KB);
 #pragma unroll
-        for (int q = 0; q < BQ; ++q) R.b[q] = *(const u32x4*)(Bb + kt * B_SLAB + q * NT * 16);
+        for (int q = 0; q < BQ; ++q) R.b[q] = *(const u32x4*)(Bb + kt * B_SLAB + bp[q]);
+        if constexpr (QW) R.sc[0] = *(const u32x4*)(Sb + kt * S_SLAB + sp);
     };
     float S[AQ];                                   // running chunk sums of squares
 #pragma unroll
@@ -756,7 +670,10 @@ __device__ __forceinline__ void t32_tile_input(const GemmArgs& g, int tm, int tn
             S[q] += valid ? input_chunk_sq(R.a[q]) : 0.0f;
         }
 #pragma unroll
-        for (int q = 0; q < BQ; ++q) *(u32x4*)(sa + Sh::A_BYTES + (q * NT + tid) * 16) = R.b[q];
+        for (int q = 0; q < BQ; ++q)
+            if (BQ * NT == NBP || q * NT + tid < NBP) *(u32x4*)(sa + Sh::A_BYTES + (q * NT + tid) * 16) = R.b[q];
+        if constexpr (QW)
+            if (tid < NSP) *(u32x4*)(sa + Sh::A_BYTES + Sh::B_BYTES + tid * 16) = R.sc[0];
     };
     f32x16 acc[MI][NI];
 #pragma unroll
@@ -767,19 +684,40 @@ __device__ __forceinline__ void t32_tile_input(const GemmArgs& g, int tm, int tn
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     const int frow = lane & 31, fk = lane >> 5;
     const int sw = tiled32_swizzle(frow);
+    const int swq = Q4 ? (frow >> 3) & 3 : (frow >> 2) & 3;   // q4_0 / q8_0 code chunk swizzle
     int aoff[MI], boff[NI];
 #pragma unroll
     for (int i = 0; i < MI; ++i) aoff[i] = (wm * WM + i * 32 + frow) * KB * 2;
 #pragma unroll
-    for (int j = 0; j < NI; ++j) boff[j] = Sh::A_BYTES + (wn * WN + j * 32 + frow) * KB * 2;
+    for (int j = 0; j < NI; ++j) boff[j] = Sh::A_BYTES + (wn * WN + j * 32 + frow) * Sh::B_ROW;
     u32x4 fa0[MI], fb0[NI], fa1[MI], fb1[NI];
-    auto rd = [&](int st, int ks, u32x4* fa, u32x4* fb) {
+    u32x2 qc0[NI], qc1[NI];
+    uint16_t qs0[NI], qs1[NI];
+    // code planes: the raw codes and scale of a weight fragment, turned into
+    // fp16 weights by cvt after the current step's MFMAs are issued
+    auto rd = [&](int st, int ks, u32x4* fa, u32x4* fb, u32x2* qc, uint16_t* qs) {
         const uint8_t* base = smem + st * Sh::STAGE;
         const int c = ((ks * 2 + fk) ^ sw) << 4;
 #pragma unroll
         for (int i = 0; i < MI; ++i) fa[i] = *(const u32x4*)(base + aoff[i] + c);
+        if constexpr (QW) {
+            const int cq = ((ks * 2 + fk) ^ swq) << (Q4 ? 2 : 3);
 #pragma unroll
-        for (int j = 0; j < NI; ++j) fb[j] = *(const u32x4*)(base + boff[j] + c);
+            for (int j = 0; j < NI; ++j) {
+                if constexpr (Q4) qc[j] = u32x2{*(const uint32_t*)(base + boff[j] + cq), 0u};
+                else qc[j] = *(const u32x2*)(base + boff[j] + cq);
+                qs[j] = *(const uint16_t*)(base + Sh::A_BYTES + Sh::B_BYTES + (wn * WN + j * 32 + frow) * 2);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NI; ++j) fb[j] = *(const u32x4*)(base + boff[j] + c);
+        }
+    };
+    auto cvt = [&](u32x4* fb, const u32x2* qc, const uint16_t* qs) {
+        if constexpr (QW) {
+#pragma unroll
+            for (int j = 0; j < NI; ++j) fb[j] = q_fragment<Q4>(qc[j], qs[j]);
+        }
     };
     auto mm = [&](const u32x4* fa, const u32x4* fb) {
 #pragma unroll
@@ -807,19 +745,22 @@ __device__ __forceinline__ void t32_tile_input(const GemmArgs& g, int tm, int tn
     commit(R0, 0, true);
     load(R0, min(3, last));
     barrier();
-    rd(0, 0, fa0, fb0);
+    rd(0, 0, fa0, fb0, qc0, qs0);
+    cvt(fb0, qc0, qs0);
     // slab kt from stage kt & 1; Rn holds slab kt + 1 (committed to the other
     // stage, whose last reader passed the previous barrier), then reloaded
     // with slab kt + 4: three slabs of loads in flight
     auto step = [&](int kt, Regs& Rn) {
         const int st = kt & 1;
-        rd(st, 1, fa1, fb1);
+        rd(st, 1, fa1, fb1, qc1, qs1);
         mm(fa0, fb0);
+        cvt(fb1, qc1, qs1);
         commit(Rn, st ^ 1, kt + 1 < nk);
         load(Rn, min(kt + 4, last));
         barrier();
-        rd(st ^ 1, 0, fa0, fb0);                   // after the last slab: a stale stage, not used
+        rd(st ^ 1, 0, fa0, fb0, qc0, qs0);         // after the last slab: a stale stage, not used
         mm(fa1, fb1);
+        cvt(fb0, qc0, qs0);
     };
     int kt = 0;
     for (; kt + 3 <= nk; kt += 3) {
@@ -849,9 +790,9 @@ __device__ __forceinline__ void t32_tile_input(const GemmArgs& g, int tm, int tn
 // consecutive tile indices run on one XCD (count: the grid, a multiple of 8).
 __device__ __forceinline__ int xcd_remap(int bid, int count) { return (bid % 8) * (count / 8) + bid / 8; }
 
-// EPI_INPUT with 16-bit weights runs t32_tile_input
+// EPI_INPUT runs t32_tile_input
 template <int BM, int BN, int OPD, int EPI>
-constexpr int kT32Smem = (EPI == EPI_INPUT && OPD == OPD_F16) ? InputShape<BM, BN>::BYTES : T32Shape<BM, BN, OPD, EPI>::BYTES;
+constexpr int kT32Smem = EPI == EPI_INPUT ? InputShape<BM, BN, OPD>::BYTES : T32Shape<BM, BN, OPD, EPI>::BYTES;
 
 template <int BM, int BN, int WGM, int WGN, int OPD, int EPI>
 __global__ void __launch_bounds__(64 * WGM * WGN) gemm_t32(GemmArgs g) {
@@ -866,10 +807,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_t32(GemmArgs g) {
     // the bytes of the weights' rows): M-tiles, then N-tiles, then splits, so
     // that an XCD's tiles read the activation rows of one K range only
     // (about 80 instead of 195 MB of L2 fills at 1024 tokens)
-    if constexpr (EPI == EPI_INPUT && OPD == OPD_F16)
-        t32_tile_input<BM, BN, WGM, WGN>(g, v % mt, (v / mt) % nt, v / (mt * nt), smem);
-    else if constexpr (EPI == EPI_INPUT)
-        t32_tile<BM, BN, WGM, WGN, OPD, EPI>(g, v % mt, (v / mt) % nt, v / (mt * nt), smem);
+    if constexpr (EPI == EPI_INPUT)
+        t32_tile_input<BM, BN, WGM, WGN, OPD>(g, v % mt, (v / mt) % nt, v / (mt * nt), smem);
     else
         t32_tile<BM, BN, WGM, WGN, OPD, EPI>(g, v % mt, v / (mt * g.splits), (v / mt) % g.splits, smem);
 }
@@ -1153,7 +1092,6 @@ hipError_t launch_gemm_t32(GemmOperand opd, GemmTile tile, EpiKind epi, const Ge
     KVA_T32_CASE(OPD_F16, TILE_128x128, EPI_QKV, 128, 128, 2, 2)
     KVA_T32_CASE(OPD_F16, TILE_128x128, EPI_SWIGLU, 128, 128, 2, 2)
     KVA_T32_CASE(OPD_Q8, TILE_256x256, EPI_PARTIAL, 256, 256, 2, 4)
-    KVA_T32_CASE(OPD_Q8, TILE_256x256, EPI_INPUT, 256, 256, 2, 4)
     KVA_T32_CASE(OPD_Q8, TILE_256x256, EPI_QKV, 256, 256, 2, 4)
     KVA_T32_CASE(OPD_Q8, TILE_256x256, EPI_SWIGLU, 256, 256, 2, 4)
     KVA_T32_CASE(OPD_Q8, TILE_128x128, EPI_PARTIAL, 128, 128, 1, 4)
@@ -1161,7 +1099,6 @@ hipError_t launch_gemm_t32(GemmOperand opd, GemmTile tile, EpiKind epi, const Ge
     KVA_T32_CASE(OPD_Q8, TILE_128x128, EPI_QKV, 128, 128, 1, 4)
     KVA_T32_CASE(OPD_Q8, TILE_128x128, EPI_SWIGLU, 128, 128, 2, 2)
     KVA_T32_CASE(OPD_Q4, TILE_256x256, EPI_PARTIAL, 256, 256, 2, 4)
-    KVA_T32_CASE(OPD_Q4, TILE_256x256, EPI_INPUT, 256, 256, 2, 4)
     KVA_T32_CASE(OPD_Q4, TILE_256x256, EPI_QKV, 256, 256, 2, 4)
     KVA_T32_CASE(OPD_Q4, TILE_256x256, EPI_SWIGLU, 256, 256, 2, 4)
     KVA_T32_CASE(OPD_Q4, TILE_128x128, EPI_PARTIAL, 128, 128, 1, 4)

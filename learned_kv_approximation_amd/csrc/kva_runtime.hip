@@ -962,15 +962,17 @@ kva_status project(kva_ctx* ctx, const float* x, int32_t n, float* const* head_o
         g.splits = ctx->n_split; g.split_stride = pstride;
         g.epi.out_f32 = ctx->ws; g.epi.ld_f32 = d; g.epi.n_real = (int32_t)d;
         g.epi.a_gain = ctx->g_in; g.epi.ss = ctx->ss_in; g.epi.ss_stride = ctx->m_alloc;
-        // With 16-bit weights the input kernel keeps three slabs of both
-        // operands in registers (a 256x256 tile's accumulators leave no room
-        // for them: the compiler then waits for every load in flight), and
-        // its time follows the bytes it copies per slab, of which the fp32
-        // rows are most: the 256-row tiles take 128x256 ones instead (32 KB
-        // a slab for the work of a 256x128 tile's 40 KB).  Same bits: one K
-        // order and one sum-of-squares order for every tile.
+        // The input kernel keeps three slabs of both operands in registers
+        // (a 256x256 tile's accumulators leave no room for them: the compiler
+        // then waits for every load in flight), and its time follows the
+        // bytes it copies per slab, of which the fp32 rows are most: with
+        // 16-bit weights the 256-row tiles take 128x256 ones instead (32 KB a
+        // slab for the work of a 256x128 tile's 40 KB); code-plane contexts
+        // (at most 256 tokens per call) take 128x128 for a 256x256 choice.
+        // Same bits: one K order and one sum-of-squares order for every tile.
         GemmTile t = pick_tile_t32(g.M, g.N, g.splits, opd == OPD_F16);
         if (opd == OPD_F16 && (t == TILE_256x256 || t == TILE_256x128) && g.N % 256 == 0) t = TILE_128x256;
+        if (opd != OPD_F16 && t == TILE_256x256) t = TILE_128x128;
         STAGE(KVA_STAGE_GEMM_IN, launch_gemm_t32(opd, t, EPI_INPUT, g, s));
     }
     for (int b = 0; b < c.n_blocks; ++b) {
